@@ -1,0 +1,338 @@
+"""Plain, slow, obviously-correct CPU oracle for SPIN's decode step.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.  It shares no code
+with the HIP library.
+
+Sources (cited by page title and section):
+  * "SPIN: Shadow Predictive Indexer for Sparse Attention" (arXiv 2610.09025),
+    Sec. 2 (indexer score z_t[i] = sum_h w_h ReLU(q_{t,h} . k_{i,h})),
+    Sec. 3.2 Eq. 1 (predicted slot score), Eq. 2 (block max pooling),
+    Algorithm 1 (block budget, block top-m, indexer, top-K, EMA update) and the
+    prose after it (reset, dense first step, sink and newest block always kept),
+    Sec. 3.2.1 (exploration share inside the budget), Sec. 3.2.2 (verifier
+    rows, mask union, deferred in-order EMA replay of prefix-valid rows),
+    Sec. 4.1 (64-slot logical blocks, max pooling).
+  * The project blog "Sparse Attention Still Has a Dense Problem", sections
+    "Score only where history points" and "SPIN works with speculative
+    decoding" (same method, prose form).
+  * Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+    Easy as 1, 2, 3", SC'11 (the counter-based generator used for exploration).
+
+Readings where the pages are silent (each is listed in the design doc):
+  * All positions are compressed-slot coordinates; row r of a step sits at
+    q_pos + r; D is indexed by the offset q - i >= 1.
+  * combine = max (Eq. 1) by default; combine = sum (one fp32 add) is the
+    variant the tiny workload states.
+  * Ties rank the lower index first (blocks and slots).  -0 ranks as +0.
+  * Budget arithmetic in integer basis points: m = min(B, max(ceil(K/b),
+    ceil((10000 - rho_bp) * B / 10000))).
+  * Forced blocks {0, B-1} count toward m; n_e = min(floor(m*gamma_bp/1e4),
+    m - n_f); ranked = top (m - n_f - n_e) of the rest; explored = the n_e
+    smallest Philox priorities (ties: lower block) among blocks neither forced
+    nor ranked.  Priority of block j = first output word of
+    Philox4x32-10(counter=(j, t, layer, req_id), key=(seed_lo, seed_hi)); the
+    counter has no row field, so verifier rows share priorities.
+  * If m < n_f (only possible for B <= 2 blocks budgets), the forced blocks are
+    still all kept.
+  * Step t = 0 after a reset scores every block (dense warm-up).
+  * The indexer score is evaluated in fp64 from the decoded inputs (fp8 keys
+    dequantised as code * scale).  Everything downstream of the score (top-K,
+    EMA) consumes it rounded to fp32, the storage precision of the state.
+  * EMA in fp32 with three roundings: V' = fl(fl(a*V) + fl(b*z)), b = fl(1 - a).
+  * top-K returns min(K, |dom|) slot ids in ascending order, padded with -1.
+  * MTP: each row predicts its own mask; the union is scored for every row;
+    each row's top-K runs over the whole union; after acceptance the first L
+    rows are replayed in row order.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 64
+CODE_SKIP, CODE_FORCED, CODE_RANKED, CODE_EXPLORED, CODE_DENSE = 0, 1, 2, 3, 4
+MASK32 = 0xFFFFFFFF
+
+# --------------------------------------------------------------------------
+# Philox4x32-10 (Salmon et al., SC'11): 10 rounds of the 4x32 S-box with
+# multipliers 0xD2511F53 / 0xCD9E8D57 and Weyl key increments 0x9E3779B9 /
+# 0xBB67AE85.
+# --------------------------------------------------------------------------
+PHILOX_M0, PHILOX_M1 = 0xD2511F53, 0xCD9E8D57
+PHILOX_W0, PHILOX_W1 = 0x9E3779B9, 0xBB67AE85
+
+
+def philox4x32_10(ctr, key):
+    """Vectorised Philox4x32-10.
+
+    ctr: 4 arrays (or ints) of uint32 words (c0, c1, c2, c3); key: (k0, k1).
+    Returns four uint64 arrays holding the 32-bit output words.
+    """
+    c0, c1, c2, c3 = (np.asarray(c, dtype=np.uint64) & MASK32 for c in ctr)
+    k0 = np.uint64(int(key[0]) & MASK32)
+    k1 = np.uint64(int(key[1]) & MASK32)
+    m0, m1 = np.uint64(PHILOX_M0), np.uint64(PHILOX_M1)
+    w0, w1 = np.uint64(PHILOX_W0), np.uint64(PHILOX_W1)
+    mask, sh = np.uint64(MASK32), np.uint64(32)
+    for rnd in range(10):
+        if rnd > 0:
+            k0 = (k0 + w0) & mask
+            k1 = (k1 + w1) & mask
+        p0 = m0 * c0               # < 2^64, exact in uint64
+        p1 = m1 * c2
+        hi0, lo0 = p0 >> sh, p0 & mask
+        hi1, lo1 = p1 >> sh, p1 & mask
+        c0, c1, c2, c3 = (hi1 ^ c1 ^ k0), lo1, (hi0 ^ c3 ^ k1), lo0
+    return c0, c1, c2, c3
+
+
+def block_priority(n_blocks: int, step: int, layer: int, req_id: int, seed: int):
+    """Exploration priority of blocks 0..n_blocks-1 (uint64 holding u32)."""
+    j = np.arange(n_blocks, dtype=np.uint64)
+    z = np.zeros_like(j)
+    out = philox4x32_10((j, z + np.uint64(step & MASK32), z + np.uint64(layer & MASK32),
+                         z + np.uint64(req_id & MASK32)),
+                        (seed & MASK32, (seed >> 32) & MASK32))
+    return out[0]
+
+
+# --------------------------------------------------------------------------
+# number formats (decoded exactly into float64)
+# --------------------------------------------------------------------------
+def decode_e4m3(codes) -> np.ndarray:
+    """OCP FP8 E4M3 (bias 7, no infinities, S.1111.111 = NaN) -> float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    sub = s * (m / 8.0) * 2.0 ** -6
+    nrm = s * (1.0 + m / 8.0) * np.exp2(e - 7.0)
+    out = np.where(e == 0, sub, nrm)
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
+def decode_bf16(codes) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64 (exact: bf16 is the top half of fp32)."""
+    c = np.asarray(codes).astype(np.uint32) << np.uint32(16)
+    return c.view(np.float32).astype(np.float64)
+
+
+def f32(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32)
+
+
+def canon32(x) -> np.ndarray:
+    """Round to fp32 and map -0 to +0 (ranking treats them as equal anyway)."""
+    y = np.asarray(x, dtype=np.float32)
+    return (y + np.float32(0.0)).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Stage 1 -- predicted block scores (Eq. 1, Eq. 2; Algorithm 1 steps 1-3)
+# --------------------------------------------------------------------------
+def n_blocks(n_slots: int, b: int = BLOCK) -> int:
+    return -(-int(n_slots) // b)
+
+
+def predict_block_scores(V, D, n_slots: int, q: int, combine: str = "max", b: int = BLOCK):
+    """S[j] = max_{jb <= i < min((j+1)b, N)} C(V[i], D[q - i]).
+
+    V: fp32 [>= N]; D: fp32 [> q]; q: the query position of this row.
+    C = max (Eq. 1) or an fp32 sum.  Returns fp32 [B].
+    """
+    N = int(n_slots)
+    i = np.arange(N)
+    v = f32(V)[:N]
+    d = f32(D)[q - i]
+    if combine == "max":
+        zhat = np.maximum(v, d)
+    elif combine == "sum":
+        zhat = (v + d).astype(np.float32)
+    else:
+        raise ValueError(combine)
+    B = n_blocks(N, b)
+    S = np.empty(B, dtype=np.float32)
+    for j in range(B):
+        S[j] = zhat[j * b:min((j + 1) * b, N)].max()
+    return canon32(S)
+
+
+# --------------------------------------------------------------------------
+# Stage 2 -- budget and block selection (Algorithm 1 steps 4-5; Sec. 3.2.1)
+# --------------------------------------------------------------------------
+def block_budget(B: int, K: int, sparsity_bp: int, b: int = BLOCK) -> int:
+    keep = -(-(10000 - int(sparsity_bp)) * int(B) // 10000)
+    return min(int(B), max(-(-int(K) // b), keep))
+
+
+def rank_desc(values, candidates):
+    """candidates ordered by (value descending, index ascending)."""
+    cand = np.asarray(candidates, dtype=np.int64)
+    v = np.asarray(values)[cand].astype(np.float64)
+    order = np.lexsort((cand, -v))
+    return cand[order]
+
+
+def select_blocks(S, n_slots: int, K: int, sparsity_bp: int, explore_bp: int, step: int,
+                  layer: int, req_id: int, seed: int, budget=None, b: int = BLOCK):
+    """Reason-coded block mask of one verifier row (uint8 [B]).
+
+    Codes: 0 skip, 1 forced, 2 ranked, 3 explored, 4 dense warm-up.
+    budget: optional override of m (used by per-layer budgets).
+    """
+    B = n_blocks(n_slots, b)
+    code = np.zeros(B, dtype=np.uint8)
+    if step == 0:
+        code[:] = CODE_DENSE
+        return code
+    m = block_budget(B, K, sparsity_bp, b) if budget is None or budget <= 0 \
+        else min(B, int(budget))
+    forced = sorted({0, B - 1})
+    n_f = len(forced)
+    m = max(m, n_f)
+    n_e = min(m * int(explore_bp) // 10000, m - n_f)
+    n_r = m - n_f - n_e
+    code[forced] = CODE_FORCED
+    rest = [j for j in range(B) if code[j] == CODE_SKIP]
+    ranked = rank_desc(S, rest)[:n_r]
+    code[ranked] = CODE_RANKED
+    pool = np.array([j for j in range(B) if code[j] == CODE_SKIP], dtype=np.int64)
+    if n_e > 0 and pool.size:
+        pri = block_priority(B, step, layer, req_id, seed)
+        order = np.lexsort((pool, pri[pool]))      # smallest priority, then lower block
+        code[pool[order[:n_e]]] = CODE_EXPLORED
+    return code
+
+
+def union_blocks(codes_rows):
+    """Ascending list of blocks selected by any verifier row (Sec. 3.2.2)."""
+    any_sel = np.zeros(len(codes_rows[0]), dtype=bool)
+    for c in codes_rows:
+        any_sel |= np.asarray(c) != CODE_SKIP
+    return np.nonzero(any_sel)[0].astype(np.int64)
+
+
+def union_slots(sel_blocks, n_slots: int, b: int = BLOCK):
+    """dom(z): the slots < N of the selected blocks, ascending."""
+    if len(sel_blocks) == 0:
+        return np.zeros(0, dtype=np.int64)
+    s = (np.asarray(sel_blocks, dtype=np.int64)[:, None] * b + np.arange(b)[None, :]).ravel()
+    return s[s < n_slots]
+
+
+# --------------------------------------------------------------------------
+# Stage 3a -- the indexer on the selected slots (Sec. 2)
+# --------------------------------------------------------------------------
+def gather_keys(pages, page_table_row, slots, key_dtype: str, scale=None):
+    """Dequantised keys of the given logical slots of one request (float64 [n, d])."""
+    slots = np.asarray(slots, dtype=np.int64)
+    phys = np.asarray(page_table_row, dtype=np.int64)[slots // BLOCK]
+    off = slots % BLOCK
+    raw = np.asarray(pages)[phys, off]
+    if key_dtype == "f32":
+        k = raw.astype(np.float64)
+    elif key_dtype == "bf16":
+        k = decode_bf16(raw)
+    elif key_dtype == "fp8":
+        k = decode_e4m3(raw) * np.asarray(scale, dtype=np.float64)[phys, off][:, None]
+    else:
+        raise ValueError(key_dtype)
+    return k
+
+
+def decode_q(q, q_dtype: str):
+    if q_dtype == "f32":
+        return np.asarray(q, dtype=np.float64)
+    if q_dtype == "bf16":
+        return decode_bf16(q)
+    raise ValueError(q_dtype)
+
+
+def index_scores(q, w, keys):
+    """z[i] = sum_h w_h * ReLU(q_h . k_i) in float64.
+
+    q: [n_h, d] float64, w: [n_h], keys: [n, d] float64 -> [n].
+    """
+    dots = np.asarray(keys, dtype=np.float64) @ np.asarray(q, dtype=np.float64).T  # [n, n_h]
+    return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Stage 3b -- post-indexer top-K (Algorithm 1 step 7)
+# --------------------------------------------------------------------------
+def topk_slots(z32, slots, K: int):
+    """min(K, n) slot ids with the largest fp32 z (ties: lower slot), ascending, -1 padded."""
+    z = canon32(z32).astype(np.float64)
+    slots = np.asarray(slots, dtype=np.int64)
+    order = np.lexsort((slots, -z))
+    chosen = np.sort(slots[order[:K]])
+    out = np.full(K, -1, dtype=np.int64)
+    out[:chosen.size] = chosen
+    return out
+
+
+# --------------------------------------------------------------------------
+# Stage 4 -- EMA update (Algorithm 1 steps 8-10; Sec. 3.2.2 deferred replay)
+# --------------------------------------------------------------------------
+def ema_update(V, D, z_rows, slots, q_pos: int, n_valid: int, alpha: float):
+    """In-place fp32 EMA update of V and D from rows 0..n_valid-1, in row order.
+
+    z_rows: fp32 [rows, len(slots)]; row r's query sits at q_pos + r.
+    """
+    a = np.float32(alpha)
+    bcoef = np.float32(np.float32(1.0) - a)
+    slots = np.asarray(slots, dtype=np.int64)
+    for r in range(int(n_valid)):
+        z = canon32(z_rows[r])
+        V[slots] = (a * V[slots]).astype(np.float32) + (bcoef * z).astype(np.float32)
+        off = (q_pos + r) - slots
+        D[off] = (a * D[off]).astype(np.float32) + (bcoef * z).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# One decode step of one (request, layer)
+# --------------------------------------------------------------------------
+class RequestState:
+    """V, D and the step counter of one request in one layer (reset: zeros, t = 0)."""
+
+    def __init__(self, n_cap: int, d_cap: int):
+        self.V = np.zeros(n_cap, dtype=np.float32)
+        self.D = np.zeros(d_cap, dtype=np.float32)
+        self.t = 0
+
+    def reset(self):
+        self.V[:] = 0
+        self.D[:] = 0
+        self.t = 0
+
+
+def spin_step(state: RequestState, *, q, q_dtype, w, pages, page_table_row, key_dtype,
+              scale, n_slots: int, q_pos: int, K: int, sparsity_bp: int, explore_bp: int,
+              alpha: float, layer: int, req_id: int, seed: int, combine: str = "max",
+              n_valid=None, budget=None, defer=False):
+    """One SPIN decode step for one request: predict, select, union, score, top-K, EMA.
+
+    q: [rows, n_h, d] (raw f32 or bf16 codes), w: [rows, n_h].
+    Returns a dict with codes [rows, B], sel, slots, z64 [rows, n], z32, topk [rows, K].
+    The EMA update uses rows 0..n_valid-1 (all rows when n_valid is None) unless
+    defer=True, in which case the caller replays later with ema_update.
+    """
+    rows = q.shape[0]
+    qd = decode_q(q, q_dtype)
+    codes = []
+    for r in range(rows):
+        S = predict_block_scores(state.V, state.D, n_slots, q_pos + r, combine)
+        codes.append(select_blocks(S, n_slots, K, sparsity_bp, explore_bp, state.t, layer,
+                                   req_id, seed, budget))
+    codes = np.stack(codes)
+    sel = union_blocks(codes)
+    slots = union_slots(sel, n_slots)
+    keys = gather_keys(pages, page_table_row, slots, key_dtype, scale)
+    z64 = np.stack([index_scores(qd[r], w[r], keys) for r in range(rows)])
+    z32 = canon32(z64)
+    top = np.stack([topk_slots(z32[r], slots, K) for r in range(rows)])
+    if not defer:
+        ema_update(state.V, state.D, z32, slots, q_pos, rows if n_valid is None else n_valid,
+                   alpha)
+        state.t += 1
+    return dict(codes=codes, sel=sel, slots=slots, z64=z64, z32=z32, topk=top)
