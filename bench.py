@@ -1,0 +1,240 @@
+"""Benchmark of the SPIN decode step on one MI355X.
+
+Workload (default): 32 requests x 131,072 compressed slots (~512K tokens at 4x
+compression, 2,048 blocks of 64), fp8 E4M3 keys with per-slot fp32 scales,
+bf16 queries, 64 heads x 128 dims, top-K 2048, 40 % target block sparsity with
+a 5 % exploration share, EMA decay 0.9.  A "step" is one pass of the whole hot
+path: predict -> select -> sparse indexer score -> top-K -> EMA -> advance,
+each launched through the C ABI on the current stream, inputs resident in HBM.
+
+Prints one JSON line.  `value` = indexer keys scored per second of whole-step
+time; `roofline` is the score kernel's algorithmic HBM bytes / its mean launch
+time (HIP events on its stream) against 8 TB/s; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import spin_synth as G  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fp8_128k_b32")
+    ap.add_argument("--sparsity-bp", type=int, default=None)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=8)
+    return ap.parse_args()
+
+
+class Inputs:
+    """Synthetic workload resident on the GPU."""
+
+    def __init__(self, w: G.Workload, n_steps: int, dev="cuda"):
+        self.w = w
+        self.ctx = G.context_lengths(w)
+        self.keys = G.make_keys(w, 0, dev, self.ctx)
+        self.weights = G.make_weights(w, 0, dev)
+        self.pos, self.accept = G.make_schedule(w, self.ctx, n_steps)
+        q = G.make_queries(w, 0, self.keys, self.pos, dev)
+        self.q = G.cast_queries(w, q).contiguous()
+        del q
+        self.accept_dev = self.accept.to(dev)
+        torch.cuda.synchronize()
+
+
+def algorithmic_score_bytes(w: G.Workload, keys_scored_per_row: float, n_blocks_sel: float):
+    """Bytes the score stage must move per launch (skipped blocks not counted)."""
+    kb = {"fp8": 128 + 4, "bf16": 256, "f32": 512}[w.key_dtype]
+    qb = {"bf16": 2, "f32": 4}[w.q_dtype]
+    per_slot = kb + 4 * w.rows                        # key (+ scale) + z writes
+    per_block = 8                                     # sel entry + page-table entry
+    per_req = w.rows * 64 * (128 * qb + 4)            # q and w
+    return keys_scored_per_row * per_slot + n_blocks_sel * per_block + w.batch * per_req
+
+
+def run_gpu(inp: Inputs, sparsity_bp: int, steps: int, warmup: int):
+    from sparse_attention_indexer_spin_amd import SpinLayer, api
+    w = inp.w
+    lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks, d_cap=G.d_capacity(w, steps + warmup),
+                    topk=w.topk, sparsity_bp=sparsity_bp, n_rows=w.rows,
+                    explore_bp=w.explore_bp, ema_alpha=w.alpha, combine=w.combine,
+                    key_dtype={"fp8": torch.uint8, "bf16": torch.bfloat16,
+                               "f32": torch.float32}[w.key_dtype],
+                    q_dtype=torch.bfloat16 if w.q_dtype == "bf16" else torch.float32)
+    lay.set_requests(inp.ctx.cuda(), inp.pos[0].cuda())
+    lay.reset()
+    pages, scale, pt = inp.keys.pages, inp.keys.scale, inp.keys.page_table
+    bt = lay.batch(pages.shape[0])
+    stream = torch.cuda.current_stream()
+    names = ["predict", "select", "score", "topk", "ema", "advance"]
+
+    def one_step(s, ev=None):
+        q = inp.q[s]
+        nv = inp.accept_dev[s] if w.rows > 1 else None
+        marks = [] if ev is None else ev
+        if ev is not None:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+        api.spin_predict_blocks(lay.cfg, bt, lay.V, lay.D, lay.S)
+        if ev is not None:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+        api.spin_select_blocks(lay.cfg, bt, lay.S, lay.row_code, lay.sel, lay.n_sel)
+        if ev is not None:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+        api.spin_sparse_index_score(lay.cfg, bt, q, inp.weights, pages, scale, pt, lay.sel,
+                                    lay.n_sel, lay.z)
+        if ev is not None:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+        api.spin_topk(lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.topk_idx, lay.workspace)
+        if ev is not None:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+        api.spin_ema_update(lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.V, lay.D, n_valid=nv)
+        if ev is not None:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+        api.spin_advance(w.rows, lay.q_pos, lay.step_ctr, n_valid=nv)
+        if ev is not None:
+            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
+
+    for s in range(warmup):
+        one_step(s)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    all_marks = []
+    t0.record(stream)
+    for s in range(warmup, warmup + steps):
+        m = []
+        one_step(s, m)
+        all_marks.append(m)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    stage_ms = np.zeros(len(names))
+    for m in all_marks:
+        for i in range(len(names)):
+            stage_ms[i] += m[i].elapsed_time(m[i + 1])
+    stage_ms /= steps
+    n_sel = lay.n_sel.cpu().numpy().astype(np.int64)
+    ctx = inp.ctx.numpy().astype(np.int64)
+    # scored keys per step: the valid slots of the selected blocks of every row
+    keys = int(np.minimum(n_sel * 64, ctx).sum()) * w.rows
+    assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
+    return dict(total_ms=total_ms, ms_per_step=total_ms / steps,
+                stage_us={n: float(v * 1e3) for n, v in zip(names, stage_ms)},
+                keys_per_step=keys, n_sel=int(n_sel.sum()))
+
+
+def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, n_req: int):
+    """Time the CPU oracle on n_req requests: one dense warm-up step (untimed),
+    then two sparse steps (timed)."""
+    from threadpoolctl import threadpool_info
+    from oracle import spin_oracle as O
+    pt = inp.keys.page_table.cpu().numpy()
+    pages_dev, scale_dev = inp.keys.pages, inp.keys.scale
+    st_keys = 0
+    elapsed = 0.0
+    for r in range(n_req):
+        phys = torch.from_numpy(pt[r]).long().cuda()
+        pages = pages_dev[phys].cpu().numpy()
+        scale = scale_dev[phys].cpu().numpy() if scale_dev is not None else None
+        local_pt = np.arange(w.max_blocks)
+        if w.key_dtype == "bf16":
+            pages = pages_dev[phys].cpu().view(torch.int16).numpy().astype(np.uint16)
+        state = O.RequestState(w.n_slots + 64, G.d_capacity(w, 8))
+        N = int(inp.ctx[r])
+        for s in range(3):
+            q = inp.q[s, r].cpu()
+            qn = q.view(torch.int16).numpy().astype(np.uint16) if q.dtype == torch.bfloat16 \
+                else q.numpy()
+            t = time.perf_counter()
+            res = O.spin_step(state, q=qn, q_dtype=w.q_dtype, w=inp.weights[r].cpu().numpy(),
+                              pages=pages, page_table_row=local_pt, key_dtype=w.key_dtype,
+                              scale=scale, n_slots=N, q_pos=int(inp.pos[s, r]), K=w.topk,
+                              sparsity_bp=sparsity_bp, explore_bp=w.explore_bp, alpha=w.alpha,
+                              layer=0, req_id=r, seed=G.PHILOX_SEED, combine=w.combine)
+            dt = time.perf_counter() - t
+            if s > 0:
+                elapsed += dt
+                st_keys += len(res["slots"]) * w.rows
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": st_keys / elapsed, "unit": "keys/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_req} of {w.batch} requests x 2 sparse steps after a dense warm-up "
+                      f"step ({st_keys} keys scored in {elapsed:.1f} s; numpy fp64 oracle, "
+                      f"host has {os.cpu_count()} logical CPUs)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(requests shard across GPUs with no exchange)"}))
+        sys.exit(2)
+    w = G.WORKLOADS[args.workload]
+    sp = w.sparsity_bp[0] if args.sparsity_bp is None else args.sparsity_bp
+    total_steps = args.steps + args.warmup
+    inp = Inputs(w, total_steps)
+    res = run_gpu(inp, sp, args.steps, args.warmup)
+    score_us = res["stage_us"]["score"]
+    keys_row = res["keys_per_step"]
+    score_bytes = algorithmic_score_bytes(w, keys_row, res["n_sel"] * w.rows)
+    achieved = score_bytes / (score_us * 1e-6) / 1e9
+    value = keys_row / (res["ms_per_step"] * 1e-3)
+    out = {
+        "metric": "indexer keys scored/s + us/decode-step/layer at 512K ctx; % HBM peak",
+        "value": value, "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3 keys, bf16 q, f32 accumulate",
+        "data": "synthetic (seeded generator: Gaussian keys + heavy slots + RoPE, AR(1) queries)",
+        "config": {"workload": w.name, "requests": w.batch, "slots_per_request": w.n_slots,
+                   "layers": 1, "verifier_rows": w.rows, "topk": w.topk,
+                   "sparsity_bp": sp, "explore_bp": w.explore_bp, "key_dtype": w.key_dtype},
+        "us_per_step_layer": res["ms_per_step"] * 1e3,
+        "stage_us": res["stage_us"],
+        "keys_scored_per_step": keys_row,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_score_fp8" if w.key_dtype == "fp8" else "k_score_" + w.key_dtype,
+                     "algorithmic_bytes_per_launch": score_bytes},
+    }
+    if not args.no_sweep and w.rows == 1 and len(w.sparsity_bp) > 1:
+        sweep = {}
+        for s in sorted(set(w.sparsity_bp)):
+            r2 = run_gpu(inp, s, min(args.steps, 20), args.warmup)
+            sweep[s] = r2
+        rho = np.array([1.0 - sweep[s]["n_sel"] / (w.batch * w.max_blocks) for s in sweep])
+        T = np.array([sweep[s]["ms_per_step"] * 1e3 for s in sweep])
+        A = np.stack([1.0 - rho, np.ones_like(rho)], 1)
+        (a, c), *_ = np.linalg.lstsq(A, T, rcond=None)
+        dense = sweep[min(sweep)]["stage_us"]
+        t_dense_indexer = dense["score"] + dense["topk"]
+        out["sparsity_sweep"] = {
+            "us_per_step": {str(s): sweep[s]["ms_per_step"] * 1e3 for s in sweep},
+            "realized_sparsity": {str(s): float(x) for s, x in zip(sweep, rho)},
+            "fit_us": {"a": float(a), "c": float(c)},
+            "dense_indexer_us": t_dense_indexer,
+            "c_over_dense_indexer": float(c / t_dense_indexer)}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, inp, sp, args.cpu_requests)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+/*
+ * spin.h -- C ABI of the SPIN decode-step library for AMD Instinct MI355X (gfx950).
+ *
+ * SPIN ("SPIN: Shadow Predictive Indexer for Sparse Attention", arXiv
+ * 2610.09025) replaces the dense indexer scan of a DSA-style sparse-attention
+ * layer with four stages per decode step:
+ *   1. predict block importance from two EMA states (Sec. 3.2, Eq. 1, Eq. 2);
+ *   2. fill the block budget with top-ranked blocks plus Philox-drawn
+ *      exploration blocks (Algorithm 1 steps 4-5, Sec. 3.2.1);
+ *   3. run the indexer z[i] = sum_h w_h ReLU(q_h . k_i) on the selected blocks
+ *      only and apply top-K (Sec. 2, Algorithm 1 steps 6-7);
+ *   4. update the EMAs, deferred to the prefix-valid verifier rows under
+ *      speculative decoding (Algorithm 1 steps 8-10, Sec. 3.2.2).
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers unless marked "host".  The caller
+ *     owns every buffer; the library never allocates, frees, or retains a
+ *     pointer past the call.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns without synchronising the host.
+ *   - Positions and lengths are in compressed KV slots.  A KV block is 64
+ *     consecutive logical slots and equals one physical page of the key pool
+ *     (Sec. 3.2 and Sec. 4.1: blocks of 64 slots matching the backend's page).
+ *   - Row r (0 <= r < n_rows) of a request is the verifier query at position
+ *     q_pos[req] + r; the EMA offset axis is D[q - i] with q - i >= 1.
+ *   - The return status reports host-visible argument and launch errors only.
+ *     Range errors that depend on device data (ctx_len, q_pos, page ids) set
+ *     bits of the optional device word `spin_batch.err` (SPIN_DERR_*); the
+ *     offending request is then skipped, never read or written out of bounds.
+ *   - Results are deterministic: integer atomics only, fixed-order floating
+ *     point.  Inputs must be finite (NaN/Inf behaviour is unspecified).
+ */
+#ifndef SPIN_H_
+#define SPIN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spin_status {
+  SPIN_OK = 0,
+  SPIN_E_NULL = 1,         /* a required pointer is NULL                    */
+  SPIN_E_SHAPE = 2,        /* a size or range argument is invalid           */
+  SPIN_E_UNSUPPORTED = 3,  /* dtype / head shape combination not built      */
+  SPIN_E_WORKSPACE = 4,    /* workspace missing or smaller than required    */
+  SPIN_E_HIP = 5           /* the HIP runtime rejected a launch             */
+} spin_status;
+
+/* element types */
+enum { SPIN_F32 = 0, SPIN_BF16 = 1, SPIN_FP8_E4M3 = 2 };
+/* how V[i] and D[q-i] combine into a predicted slot score */
+enum { SPIN_COMBINE_MAX = 0, /* Eq. 1 of the paper                       */
+       SPIN_COMBINE_SUM = 1  /* one fp32 add, the "EMA_pos + EMA_off" form */ };
+/* per-row block reason codes written by spin_select_blocks */
+enum { SPIN_CODE_SKIP = 0, SPIN_CODE_FORCED = 1, SPIN_CODE_RANKED = 2,
+       SPIN_CODE_EXPLORED = 3, SPIN_CODE_DENSE = 4 };
+/* device error-word bits (OR-ed into spin_batch.err) */
+enum { SPIN_DERR_CTX = 1,   /* ctx_len < 1, > 64*max_blocks or > v_ld        */
+       SPIN_DERR_QPOS = 2,  /* q_pos < ctx_len or q_pos + n_rows - 1 >= d_ld */
+       SPIN_DERR_PAGE = 4   /* a page-table entry outside [0, n_pages)       */ };
+
+/* limits of this build */
+#define SPIN_BLOCK 64
+#define SPIN_MAX_ROWS 4
+#define SPIN_MAX_BLOCKS 8192  /* per request: up to 524,288 slots */
+#define SPIN_MAX_TOPK 8192
+
+/* Method parameters, passed by host pointer and copied by value. */
+typedef struct spin_config {
+  int32_t n_heads;      /* indexer heads n_h; this build: 64                       */
+  int32_t head_dim;     /* indexer head dim d; this build: 128                     */
+  int32_t block_size;   /* b; must be 64                                           */
+  int32_t topk;         /* K of the post-indexer top-K, 1..SPIN_MAX_TOPK           */
+  int32_t sparsity_bp;  /* target block sparsity rho in basis points, 0..10000     */
+  int32_t explore_bp;   /* exploration share gamma in basis points, 0..10000       */
+  float ema_alpha;      /* EMA decay alpha in [0,1]; beta = 1.0f - alpha in fp32   */
+  int32_t combine;      /* SPIN_COMBINE_*                                          */
+  int32_t key_dtype;    /* SPIN_F32 | SPIN_BF16 | SPIN_FP8_E4M3                    */
+  int32_t q_dtype;      /* SPIN_F32 | SPIN_BF16                                    */
+  int32_t layer;        /* layer id, part of the Philox counter                    */
+  int32_t reserved;     /* must be 0                                               */
+  uint64_t seed;        /* Philox4x32-10 key (lo, hi words)                        */
+} spin_config;
+
+/* One decode step of one layer for a batch of requests (host struct). */
+typedef struct spin_batch {
+  int32_t batch;           /* R >= 1 requests                                      */
+  int32_t n_rows;          /* verifier queries per request, 1..SPIN_MAX_ROWS        */
+  int32_t max_blocks;      /* capacity of per-request block arrays (>= ceil(N/64)) */
+  int32_t n_pages;         /* pages in the key pool (page ids must be < n_pages)   */
+  const int32_t* ctx_len;  /* [R] context length N in slots, 1..64*max_blocks      */
+  const int32_t* q_pos;    /* [R] position of verifier row 0, >= N                 */
+  const int32_t* step;     /* [R] decode steps since the last reset (0 = dense)    */
+  const int32_t* req_id;   /* [R] stable request id (Philox counter word)          */
+  int32_t* err;            /* optional device error word, OR of SPIN_DERR_*        */
+} spin_batch;
+
+/*
+ * Stage 1 (Sec. 3.2, Eq. 1 and Eq. 2; Algorithm 1 steps 1-3).
+ * S[r][row][j] = max over slots i in block j with i < N of C(V[i], D[q_row - i]),
+ * C = max or fp32 sum (cfg->combine), q_row = q_pos[r] + row.
+ *   V: f32 [R][v_ld] (v_ld >= N), D: f32 [R][d_ld] (d_ld > q_pos + n_rows - 1),
+ *   S: f32 [R][n_rows][max_blocks]; entries j >= ceil(N/64) are not written.
+ */
+spin_status spin_predict_blocks(const spin_config* cfg, const spin_batch* bt,
+                                const float* V, int64_t v_ld, const float* D, int64_t d_ld,
+                                float* S, void* stream);
+
+/*
+ * Stage 2 (Algorithm 1 steps 4-5; the sink and newest blocks are always kept
+ * and count toward the budget; Sec. 3.2.1 exploration share; Sec. 3.2.2 union).
+ * Per row: m = min(B, max(ceil(K/64), ceil((10000 - rho_bp) B / 10000))), or
+ * min(B, budget[r]) when budget != NULL and budget[r] > 0; forced = {0, B-1};
+ * n_e = min(floor(m gamma_bp / 10000), m - n_f); ranked = the m - n_f - n_e
+ * remaining blocks with the largest S (ties: lower block); explored = the n_e
+ * blocks neither forced nor ranked with the smallest Philox4x32-10 word 0 of
+ * counter (j, step, layer, req_id) under key (seed lo, seed hi) (ties: lower
+ * block).  step == 0 selects every block (dense warm-up).
+ *   budget:   optional i32 [R]
+ *   row_code: u8 [R][n_rows][max_blocks] (SPIN_CODE_*; entries j >= B not written)
+ *   sel:      i32 [R][max_blocks] ascending union of the rows' masks, -1 padded
+ *   n_sel:    i32 [R] union size
+ */
+spin_status spin_select_blocks(const spin_config* cfg, const spin_batch* bt, const float* S,
+                               const int32_t* budget, uint8_t* row_code, int32_t* sel,
+                               int32_t* n_sel, void* stream);
+
+/*
+ * Stage 3a (Sec. 2): z[r][row][64k + s] = sum_h w[r][row][h] ReLU(q[r][row][h] . key(i))
+ * for slot i = 64 sel[r][k] + s, k < n_sel[r]; key(i) = k_pages[page_table[r][i/64]][i%64]
+ * (times k_scale[page][i%64] for fp8 keys).  Slots i >= N get z = 0.
+ *   q:          [R][n_rows][n_heads][head_dim] of cfg->q_dtype
+ *   w:          f32 [R][n_rows][n_heads]
+ *   k_pages:    [n_pages][64][head_dim] of cfg->key_dtype (fp8 = OCP E4M3 codes)
+ *   k_scale:    f32 [n_pages][64], non-negative; required for fp8 keys, else ignored
+ *   page_table: i32 [R][pt_ld], pt_ld >= max_blocks
+ *   z:          f32 [R][n_rows][z_ld], z_ld >= 64 * max_blocks
+ * Supported (key, q) dtypes: (f32, f32), (bf16, bf16), (fp8, bf16), (fp8, f32).
+ */
+spin_status spin_sparse_index_score(const spin_config* cfg, const spin_batch* bt, const void* q,
+                                    const float* w, const void* k_pages, const float* k_scale,
+                                    const int32_t* page_table, int64_t pt_ld, const int32_t* sel,
+                                    const int32_t* n_sel, float* z, int64_t z_ld, void* stream);
+
+/*
+ * Stage 3b (Algorithm 1 step 7): per row, the min(K, |dom|) slots of dom(z)
+ * (selected slots < N) with the largest z (ties: lower slot), written in
+ * ascending slot order and padded with -1.
+ *   topk_idx: i32 [R][n_rows][K]
+ *   workspace: device scratch of spin_workspace_bytes() bytes (may be NULL when
+ *              that function returns 0)
+ */
+spin_status spin_topk(const spin_config* cfg, const spin_batch* bt, const float* z, int64_t z_ld,
+                      const int32_t* sel, const int32_t* n_sel, int32_t* topk_idx,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 4 (Algorithm 1 steps 8-10; Sec. 3.2.2 deferred in-order replay).
+ * For rows r = 0 .. L-1 in order (L = n_valid[req], or n_rows when n_valid is
+ * NULL) and every slot i of dom(z):
+ *   V[i]         <- (alpha * V[i])         + (beta * z_r[i])
+ *   D[q_r - i]   <- (alpha * D[q_r - i])   + (beta * z_r[i])
+ * each product and the sum rounded to fp32 separately (no fused multiply-add),
+ * beta = 1.0f - alpha rounded to fp32.
+ *   n_valid: optional i32 [R], each in 1..n_rows
+ */
+spin_status spin_ema_update(const spin_config* cfg, const spin_batch* bt, const float* z,
+                            int64_t z_ld, const int32_t* sel, const int32_t* n_sel,
+                            const int32_t* n_valid, float* V, int64_t v_ld, float* D, int64_t d_ld,
+                            void* stream);
+
+/*
+ * Advance the per-request counters after a committed step:
+ * q_pos[r] += n_valid ? n_valid[r] : n_rows; step[r] += 1.
+ */
+spin_status spin_advance(int32_t batch, int32_t n_rows, const int32_t* n_valid, int32_t* q_pos,
+                         int32_t* step, void* stream);
+
+/*
+ * Reset after prefill or at a turn start (prose after Algorithm 1): V[r][0..v_ld),
+ * D[r][0..d_ld) = 0 and step[r] = 0 for every r < batch, so the next step is dense.
+ * Uses fill kernels only (safe inside captured graphs).
+ */
+spin_status spin_reset_state(int32_t batch, float* V, int64_t v_ld, float* D, int64_t d_ld,
+                             int32_t* step, void* stream);
+
+/* Buffers of one whole step (spin_step).  Pointer meanings as above. */
+typedef struct spin_step_io {
+  float* V; int64_t v_ld;               /* EMA state, updated in place        */
+  float* D; int64_t d_ld;
+  const void* q; const float* w;        /* indexer queries and head weights   */
+  const void* k_pages; const float* k_scale;
+  const int32_t* page_table; int64_t pt_ld;
+  const int32_t* budget;                /* optional per-request block budget  */
+  const int32_t* n_valid;               /* optional accepted rows per request */
+  float* S;                             /* f32 [R][n_rows][max_blocks]        */
+  uint8_t* row_code;                    /* u8  [R][n_rows][max_blocks]        */
+  int32_t* sel; int32_t* n_sel;         /* i32 [R][max_blocks], i32 [R]       */
+  float* z; int64_t z_ld;               /* f32 [R][n_rows][z_ld]              */
+  int32_t* topk_idx;                    /* i32 [R][n_rows][K]                 */
+  int32_t* q_pos_mut;                   /* optional: advanced after the EMA   */
+  int32_t* step_mut;                    /* optional: advanced after the EMA   */
+  void* workspace; size_t workspace_bytes;
+} spin_step_io;
+
+/*
+ * One whole decode step on `stream`: predict, select (+union), score, top-K
+ * and, unless defer_ema != 0, the EMA update followed by spin_advance on
+ * q_pos_mut / step_mut when those are non-NULL (they normally alias
+ * bt->q_pos / bt->step).  With defer_ema != 0 the caller runs
+ * spin_ema_update with the acceptance outcome and then spin_advance.
+ */
+spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_step_io* io,
+                      int32_t defer_ema, void* stream);
+
+/* Device workspace bytes spin_topk / spin_step need for this shape (0 = none). */
+size_t spin_workspace_bytes(const spin_config* cfg, int32_t batch, int32_t n_rows,
+                            int32_t max_blocks);
+
+/* Message for the last non-OK status returned on the calling thread (host string). */
+const char* spin_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPIN_H_ */

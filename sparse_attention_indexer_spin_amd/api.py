@@ -1,0 +1,117 @@
+"""Python binding of the SPIN C ABI: same entry points, torch tensors in.
+
+Argument marshalling only -- every stage runs in libspin.so's HIP kernels.
+Tensors must be CUDA (HIP) tensors, contiguous, of the dtypes include/spin.h
+states; torch supplies device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+_KEY = {torch.float32: L.SPIN_F32, torch.bfloat16: L.SPIN_BF16, torch.uint8: L.SPIN_FP8_E4M3,
+        torch.float8_e4m3fn: L.SPIN_FP8_E4M3}
+_Q = {torch.float32: L.SPIN_F32, torch.bfloat16: L.SPIN_BF16}
+
+
+def _p(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("SPIN buffers must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("SPIN buffers must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def config(*, topk: int, sparsity_bp: int, explore_bp: int = 500, ema_alpha: float = 0.9,
+           combine: str = "max", key_dtype: torch.dtype = torch.uint8,
+           q_dtype: torch.dtype = torch.bfloat16, layer: int = 0, seed: int = 0x5350494E,
+           n_heads: int = 64, head_dim: int = 128, block_size: int = 64) -> L.SpinConfig:
+    return L.SpinConfig(n_heads=n_heads, head_dim=head_dim, block_size=block_size, topk=topk,
+                        sparsity_bp=sparsity_bp, explore_bp=explore_bp, ema_alpha=ema_alpha,
+                        combine=L.SPIN_COMBINE_SUM if combine == "sum" else L.SPIN_COMBINE_MAX,
+                        key_dtype=_KEY[key_dtype], q_dtype=_Q[q_dtype], layer=layer, reserved=0,
+                        seed=seed)
+
+
+def batch(*, ctx_len, q_pos, step, req_id, n_rows: int, max_blocks: int, n_pages: int,
+          err: Optional[torch.Tensor] = None) -> L.SpinBatch:
+    for t in (ctx_len, q_pos, step, req_id):
+        assert t.dtype == torch.int32
+    return L.SpinBatch(batch=ctx_len.numel(), n_rows=n_rows, max_blocks=max_blocks,
+                       n_pages=n_pages, ctx_len=_p(ctx_len), q_pos=_p(q_pos), step=_p(step),
+                       req_id=_p(req_id), err=_p(err))
+
+
+def _ld(t: torch.Tensor) -> int:
+    return t.shape[-1]
+
+
+def spin_predict_blocks(cfg, bt, V, D, S, stream=None):
+    L.check(L.load().spin_predict_blocks(C.byref(cfg), C.byref(bt), _p(V), _ld(V), _p(D), _ld(D),
+                                         _p(S), _stream(stream)))
+
+
+def spin_select_blocks(cfg, bt, S, row_code, sel, n_sel, budget=None, stream=None):
+    L.check(L.load().spin_select_blocks(C.byref(cfg), C.byref(bt), _p(S), _p(budget),
+                                        _p(row_code), _p(sel), _p(n_sel), _stream(stream)))
+
+
+def spin_sparse_index_score(cfg, bt, q, w, k_pages, k_scale, page_table, sel, n_sel, z,
+                            stream=None):
+    L.check(L.load().spin_sparse_index_score(
+        C.byref(cfg), C.byref(bt), _p(q), _p(w), _p(k_pages), _p(k_scale), _p(page_table),
+        _ld(page_table), _p(sel), _p(n_sel), _p(z), _ld(z), _stream(stream)))
+
+
+def workspace_bytes(cfg, batch_size: int, n_rows: int, max_blocks: int) -> int:
+    return int(L.load().spin_workspace_bytes(C.byref(cfg), batch_size, n_rows, max_blocks))
+
+
+def spin_topk(cfg, bt, z, sel, n_sel, topk_idx, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    L.check(L.load().spin_topk(C.byref(cfg), C.byref(bt), _p(z), _ld(z), _p(sel), _p(n_sel),
+                               _p(topk_idx), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def spin_ema_update(cfg, bt, z, sel, n_sel, V, D, n_valid=None, stream=None):
+    L.check(L.load().spin_ema_update(C.byref(cfg), C.byref(bt), _p(z), _ld(z), _p(sel),
+                                     _p(n_sel), _p(n_valid), _p(V), _ld(V), _p(D), _ld(D),
+                                     _stream(stream)))
+
+
+def spin_advance(n_rows: int, q_pos, step, n_valid=None, stream=None):
+    L.check(L.load().spin_advance(q_pos.numel(), n_rows, _p(n_valid), _p(q_pos), _p(step),
+                                  _stream(stream)))
+
+
+def spin_reset_state(V, D, step, stream=None):
+    L.check(L.load().spin_reset_state(V.shape[0], _p(V), _ld(V), _p(D), _ld(D), _p(step),
+                                      _stream(stream)))
+
+
+def step_io(*, V, D, q, w, k_pages, k_scale, page_table, S, row_code, sel, n_sel, z, topk_idx,
+            budget=None, n_valid=None, q_pos_mut=None, step_mut=None, workspace=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return L.SpinStepIO(V=_p(V), v_ld=_ld(V), D=_p(D), d_ld=_ld(D), q=_p(q), w=_p(w),
+                        k_pages=_p(k_pages), k_scale=_p(k_scale), page_table=_p(page_table),
+                        pt_ld=_ld(page_table), budget=_p(budget), n_valid=_p(n_valid), S=_p(S),
+                        row_code=_p(row_code), sel=_p(sel), n_sel=_p(n_sel), z=_p(z),
+                        z_ld=_ld(z), topk_idx=_p(topk_idx), q_pos_mut=_p(q_pos_mut),
+                        step_mut=_p(step_mut), workspace=_p(workspace), workspace_bytes=ws_bytes)
+
+
+def spin_step(cfg, bt, io, defer_ema: bool = False, stream=None):
+    L.check(L.load().spin_step(C.byref(cfg), C.byref(bt), C.byref(io), int(bool(defer_ema)),
+                               _stream(stream)))

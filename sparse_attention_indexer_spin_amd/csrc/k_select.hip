@@ -1,0 +1,296 @@
+// Stages 1-2 of the SPIN decode step: predicted block scores, block budget,
+// ranked + Philox-explored block selection, verifier-row union; plus the
+// per-request counter advance and the state reset.
+//
+// Paper: "SPIN: Shadow Predictive Indexer for Sparse Attention", Sec. 3.2
+// (Eq. 1 predicted slot score, Eq. 2 block max pooling, Algorithm 1 steps
+// 1-5 and the reset / dense first step / always-kept sink and newest block
+// described after it), Sec. 3.2.1 (exploration inside the budget) and
+// Sec. 3.2.2 (union of the verifier rows' masks).
+#include "spin_dev.h"
+#include "spin_launch.h"
+
+namespace spin {
+
+// ---------------------------------------------------------------------------
+// Stage 1: S[r][row][j] = max_{i in block j, i < N} C(V[i], D[q_row - i]).
+// One wave per 4 consecutive blocks; lane = slot within the block.  The data
+// is read once with coalesced 256-B rows (V ascending, D descending).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_blocks,
+                                                 const int32_t* __restrict__ ctx,
+                                                 const int32_t* __restrict__ qpos,
+                                                 const float* __restrict__ V, int64_t v_ld,
+                                                 const float* __restrict__ D, int64_t d_ld,
+                                                 float* __restrict__ S, int32_t* err) {
+  const int r = blockIdx.z, row = blockIdx.y;
+  const int N = ctx[r], q0 = qpos[r];
+  const int e = request_error(N, q0, rows, max_blocks, v_ld, d_ld);
+  if (e) {
+    if (row == 0 && blockIdx.x == 0 && threadIdx.x == 0) raise_error(err, e);
+    return;
+  }
+  const int q = q0 + row;
+  const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j0 = (blockIdx.x * 4 + wave) * 4;
+  if (j0 >= B) return;
+  const float* Vr = V + (int64_t)r * v_ld;
+  const float* Dr = D + (int64_t)r * d_ld;
+  float vv[4], dd[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int i = (j0 + b) * SPIN_BLOCK + lane;
+    const bool ok = (j0 + b) < B && i < N;
+    vv[b] = ok ? Vr[i] : 0.0f;
+    dd[b] = ok ? Dr[q - i] : 0.0f;
+  }
+  float* Srow = S + ((int64_t)r * rows + row) * max_blocks;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int j = j0 + b;
+    const int i = j * SPIN_BLOCK + lane;
+    float zhat = combine == SPIN_COMBINE_SUM ? __fadd_rn(vv[b], dd[b]) : fmaxf(vv[b], dd[b]);
+    zhat = (j < B && i < N) ? zhat : -INFINITY;
+    const float m = wave_max_f32(zhat);
+    if (lane == 0 && j < B) Srow[j] = m + 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-level selection of the k largest u32 keys among flagged elements
+// (ties: lower element index).  Thread t owns elements t*EPT .. t*EPT+EPT-1.
+// On return, bit e of the result mask marks the chosen elements.
+// ---------------------------------------------------------------------------
+constexpr int kSelThreads = 1024;
+
+template <int EPT>
+__device__ uint32_t block_select_top(const uint32_t (&key)[EPT], uint32_t elig, int k,
+                                     int* hist, int* sh, uint32_t* tmpu) {
+  if (k <= 0) return 0u;
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (elig >> e & 1u) { mx = max(mx, key[e]); mn = min(mn, key[e]); }
+  mx = block_max_u32<kSelThreads>(mx, tmpu);
+  mn = block_min_u32<kSelThreads>(mn, tmpu);
+  int nb = (mx == mn) ? 0 : 32 - __clz(mx ^ mn);
+  uint64_t prefix = ((uint64_t)mx >> nb) << nb;
+  while (nb > 0) {
+    const int db = nb < 8 ? nb : 8, pos = nb - db;
+    for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if ((elig >> e & 1u) && ((uint64_t)key[e] >> nb) == (prefix >> nb))
+        atomicAdd(&hist[(key[e] >> pos) & ((1u << db) - 1u)], 1);
+    __syncthreads();
+    if (threadIdx.x < 64) radix_pick_digit(hist, k, sh);
+    __syncthreads();
+    const int d = sh[0], cnt = sh[2];
+    k = sh[1];
+    __syncthreads();
+    prefix |= (uint64_t)d << pos;
+    nb = pos;
+    if (cnt == k) break;  // every key of this bin is taken
+  }
+  const uint64_t hp = prefix >> nb;
+  int eq = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if ((elig >> e & 1u) && ((uint64_t)key[e] >> nb) == hp) ++eq;
+  int tot;
+  int rank = block_excl_scan<kSelThreads>(eq, sh + 4, &tot);
+  uint32_t out = 0u;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (!(elig >> e & 1u)) continue;
+    const uint64_t hk = (uint64_t)key[e] >> nb;
+    if (hk > hp) out |= 1u << e;
+    else if (hk == hp) { if (rank < k) out |= 1u << e; ++rank; }
+  }
+  return out;
+}
+
+// Write the ascending list of flagged blocks; pad with -1 to max_blocks.
+template <int EPT>
+__device__ void compact_blocks(uint32_t flag, int max_blocks, int32_t* sel_row, int32_t* n_sel_r,
+                               int* sh) {
+  int tot;
+  int pos = block_excl_scan<kSelThreads>(__popc(flag), sh, &tot);
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (flag >> e & 1u) sel_row[pos++] = threadIdx.x * EPT + e;
+  for (int i = tot + threadIdx.x; i < max_blocks; i += kSelThreads) sel_row[i] = -1;
+  if (threadIdx.x == 0) *n_sel_r = tot;
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2: one workgroup per (request, verifier row).
+// ---------------------------------------------------------------------------
+template <int EPT>
+__global__ __launch_bounds__(kSelThreads) void k_select(
+    int K, int sparsity_bp, int explore_bp, int layer, uint32_t seed_lo, uint32_t seed_hi,
+    int rows, int max_blocks, const int32_t* __restrict__ ctx, const int32_t* __restrict__ qpos,
+    const int32_t* __restrict__ step, const int32_t* __restrict__ req_id,
+    const float* __restrict__ S, const int32_t* __restrict__ budget, uint8_t* __restrict__ code,
+    int32_t* __restrict__ sel, int32_t* __restrict__ n_sel, int compact) {
+  __shared__ int hist[256];
+  __shared__ int sh[32];
+  __shared__ uint32_t tmpu[16];
+  const int row = blockIdx.x, r = blockIdx.y;
+  const int N = ctx[r];
+  const bool bad = request_error(N, qpos[r], rows, max_blocks, 0, 0) != 0;
+  const int B = bad ? 0 : (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  const int t = step[r];
+  const int j0 = threadIdx.x * EPT;
+  uint8_t* crow = code + ((int64_t)r * rows + row) * max_blocks;
+  uint32_t chosen = 0u;
+  uint8_t c[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) c[e] = SPIN_CODE_SKIP;
+
+  if (B > 0 && t == 0) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if (j0 + e < B) { c[e] = SPIN_CODE_DENSE; chosen |= 1u << e; }
+  } else if (B > 0) {
+    const int kb = (K + SPIN_BLOCK - 1) / SPIN_BLOCK;
+    const int keep = (int)(((int64_t)(10000 - sparsity_bp) * B + 9999) / 10000);
+    int m = (budget && budget[r] > 0) ? min(B, (int)budget[r]) : min(B, max(kb, keep));
+    const int n_f = B > 1 ? 2 : 1;
+    m = max(m, n_f);
+    const int n_e = min((int)((int64_t)m * explore_bp / 10000), m - n_f);
+    const int n_r = m - n_f - n_e;
+    const float* Srow = S + ((int64_t)r * rows + row) * max_blocks;
+    uint32_t key[EPT];
+    uint32_t elig = 0u;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int j = j0 + e;
+      key[e] = 0u;
+      if (j < B) {
+        if (j == 0 || j == B - 1) { c[e] = SPIN_CODE_FORCED; chosen |= 1u << e; }
+        else { key[e] = float_key(Srow[j]); elig |= 1u << e; }
+      }
+    }
+    const uint32_t ranked = block_select_top<EPT>(key, elig, n_r, hist, sh, tmpu);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if (ranked >> e & 1u) c[e] = SPIN_CODE_RANKED;
+    chosen |= ranked;
+    elig &= ~ranked;
+    if (n_e > 0) {
+      // smallest Philox priority first == largest complemented priority
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+        key[e] = ~philox_word0((uint32_t)(j0 + e), (uint32_t)t, (uint32_t)layer,
+                               (uint32_t)req_id[r], seed_lo, seed_hi);
+      const uint32_t expl = block_select_top<EPT>(key, elig, n_e, hist, sh, tmpu);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+        if (expl >> e & 1u) c[e] = SPIN_CODE_EXPLORED;
+      chosen |= expl;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (j0 + e < B) crow[j0 + e] = c[e];
+  if (compact) compact_blocks<EPT>(chosen, max_blocks, sel + (int64_t)r * max_blocks, n_sel + r, sh);
+}
+
+// Union of the verifier rows' masks (Sec. 3.2.2), one workgroup per request.
+template <int EPT>
+__global__ __launch_bounds__(kSelThreads) void k_union(int rows, int max_blocks,
+                                                       const int32_t* __restrict__ ctx,
+                                                       const int32_t* __restrict__ qpos,
+                                                       const uint8_t* __restrict__ code,
+                                                       int32_t* __restrict__ sel,
+                                                       int32_t* __restrict__ n_sel) {
+  __shared__ int sh[32];
+  const int r = blockIdx.x;
+  const int N = ctx[r];
+  const bool bad = request_error(N, qpos[r], rows, max_blocks, 0, 0) != 0;
+  const int B = bad ? 0 : (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  const int j0 = threadIdx.x * EPT;
+  uint32_t any = 0u;
+  for (int row = 0; row < rows; ++row) {
+    const uint8_t* crow = code + ((int64_t)r * rows + row) * max_blocks;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if (j0 + e < B && crow[j0 + e] != SPIN_CODE_SKIP) any |= 1u << e;
+  }
+  compact_blocks<EPT>(any, max_blocks, sel + (int64_t)r * max_blocks, n_sel + r, sh);
+}
+
+__global__ void k_advance(int R, int rows, const int32_t* __restrict__ n_valid,
+                          int32_t* __restrict__ qpos, int32_t* __restrict__ step) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  if (qpos) qpos[r] += n_valid ? n_valid[r] : rows;
+  if (step) step[r] += 1;
+}
+
+__global__ void k_fill_zero(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+__global__ void k_zero_i32(int32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
+                          const float* D, int64_t d_ld, float* S, hipStream_t st) {
+  dim3 grid((b.max_blocks + 15) / 16, b.n_rows, b.batch);
+  hipLaunchKernelGGL(k_predict, grid, dim3(256), 0, st, c.combine, b.n_rows, b.max_blocks,
+                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld, S, b.err);
+  return hipGetLastError();
+}
+
+template <int EPT>
+static void select_t(const spin_config& c, const spin_batch& b, const float* S,
+                     const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
+                     hipStream_t st) {
+  const int compact = b.n_rows == 1;
+  hipLaunchKernelGGL(k_select<EPT>, dim3(b.n_rows, b.batch), dim3(kSelThreads), 0, st, c.topk,
+                     c.sparsity_bp, c.explore_bp, c.layer, (uint32_t)(c.seed & 0xFFFFFFFFu),
+                     (uint32_t)(c.seed >> 32), b.n_rows, b.max_blocks, b.ctx_len, b.q_pos,
+                     b.step, b.req_id, S, budget, code, sel, n_sel, compact);
+  if (!compact)
+    hipLaunchKernelGGL(k_union<EPT>, dim3(b.batch), dim3(kSelThreads), 0, st, b.n_rows,
+                       b.max_blocks, b.ctx_len, b.q_pos, code, sel, n_sel);
+}
+
+hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
+                         const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
+                         hipStream_t st) {
+  const int ept = (b.max_blocks + kSelThreads - 1) / kSelThreads;
+  if (ept <= 1) select_t<1>(c, b, S, budget, code, sel, n_sel, st);
+  else if (ept <= 2) select_t<2>(c, b, S, budget, code, sel, n_sel, st);
+  else if (ept <= 4) select_t<4>(c, b, S, budget, code, sel, n_sel, st);
+  else select_t<8>(c, b, S, budget, code, sel, n_sel, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_advance(int R, int rows, const int32_t* n_valid, int32_t* qpos, int32_t* step,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_advance, dim3((R + 255) / 256), dim3(256), 0, st, R, rows, n_valid, qpos,
+                     step);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset(int R, float* V, int64_t v_ld, float* D, int64_t d_ld, int32_t* step,
+                        hipStream_t st) {
+  const int64_t nv = (int64_t)R * v_ld, nd = (int64_t)R * d_ld;
+  if (nv > 0) hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, V, nv);
+  if (nd > 0) hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, D, nd);
+  if (step) hipLaunchKernelGGL(k_zero_i32, dim3((R + 255) / 256), dim3(256), 0, st, step, R);
+  return hipGetLastError();
+}
+
+}  // namespace spin

@@ -1,0 +1,286 @@
+// C ABI of the SPIN decode-step library: argument validation, error
+// reporting, and stream-ordered launches of the stage kernels.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "spin_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+spin_status fail(spin_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+spin_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SPIN_OK;
+  return fail(SPIN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define SPIN_REQUIRE(ptr)                                                 \
+  do {                                                                    \
+    if (!(ptr)) return fail(SPIN_E_NULL, "%s: %s is NULL", fn, #ptr);     \
+  } while (0)
+
+spin_status check_config(const char* fn, const spin_config* c) {
+  if (!c) return fail(SPIN_E_NULL, "%s: cfg is NULL", fn);
+  if (c->block_size != SPIN_BLOCK)
+    return fail(SPIN_E_UNSUPPORTED, "%s: block_size %d (only 64 is supported)", fn, c->block_size);
+  if (c->n_heads != 64 || c->head_dim != 128)
+    return fail(SPIN_E_UNSUPPORTED, "%s: n_heads=%d head_dim=%d (this build: 64 x 128)", fn,
+                c->n_heads, c->head_dim);
+  if (c->topk < 1 || c->topk > SPIN_MAX_TOPK)
+    return fail(SPIN_E_SHAPE, "%s: topk %d outside [1, %d]", fn, c->topk, SPIN_MAX_TOPK);
+  if (c->sparsity_bp < 0 || c->sparsity_bp > 10000 || c->explore_bp < 0 || c->explore_bp > 10000)
+    return fail(SPIN_E_SHAPE, "%s: sparsity_bp/explore_bp outside [0, 10000]", fn);
+  if (!(c->ema_alpha >= 0.0f && c->ema_alpha <= 1.0f))
+    return fail(SPIN_E_SHAPE, "%s: ema_alpha outside [0, 1]", fn);
+  if (c->combine != SPIN_COMBINE_MAX && c->combine != SPIN_COMBINE_SUM)
+    return fail(SPIN_E_SHAPE, "%s: unknown combine %d", fn, c->combine);
+  if (c->key_dtype < SPIN_F32 || c->key_dtype > SPIN_FP8_E4M3 || c->q_dtype < SPIN_F32 ||
+      c->q_dtype > SPIN_BF16)
+    return fail(SPIN_E_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (c->reserved != 0) return fail(SPIN_E_SHAPE, "%s: reserved must be 0", fn);
+  return SPIN_OK;
+}
+
+spin_status check_batch(const char* fn, const spin_batch* b) {
+  if (!b) return fail(SPIN_E_NULL, "%s: batch is NULL", fn);
+  if (b->batch < 0) return fail(SPIN_E_SHAPE, "%s: batch %d < 0", fn, b->batch);
+  if (b->n_rows < 1 || b->n_rows > SPIN_MAX_ROWS)
+    return fail(SPIN_E_SHAPE, "%s: n_rows %d outside [1, %d]", fn, b->n_rows, SPIN_MAX_ROWS);
+  if (b->max_blocks < 1 || b->max_blocks > SPIN_MAX_BLOCKS)
+    return fail(SPIN_E_SHAPE, "%s: max_blocks %d outside [1, %d]", fn, b->max_blocks,
+                SPIN_MAX_BLOCKS);
+  if (b->batch > 0) {
+    SPIN_REQUIRE(b->ctx_len);
+    SPIN_REQUIRE(b->q_pos);
+    SPIN_REQUIRE(b->step);
+    SPIN_REQUIRE(b->req_id);
+  }
+  return SPIN_OK;
+}
+
+#define SPIN_CHECK(expr)                 \
+  do {                                   \
+    spin_status _s = (expr);             \
+    if (_s != SPIN_OK) return _s;        \
+  } while (0)
+
+spin_status check_state(const char* fn, const spin_batch* b, const float* V, int64_t v_ld,
+                        const float* D, int64_t d_ld) {
+  SPIN_REQUIRE(V);
+  SPIN_REQUIRE(D);
+  if (v_ld < 1 || d_ld < 2) return fail(SPIN_E_SHAPE, "%s: v_ld/d_ld too small", fn);
+  (void)b;
+  return SPIN_OK;
+}
+
+spin_status check_z(const char* fn, const spin_batch* b, const float* z, int64_t z_ld) {
+  SPIN_REQUIRE(z);
+  if (z_ld < (int64_t)SPIN_BLOCK * b->max_blocks || (z_ld & 3))
+    return fail(SPIN_E_SHAPE, "%s: z_ld %lld must be >= 64*max_blocks and a multiple of 4", fn,
+                (long long)z_ld);
+  return SPIN_OK;
+}
+
+}  // namespace
+
+namespace spin {
+
+int resident_workgroups(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(dev, kernel);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess ||
+      per < 1)
+    per = 1;
+  const int g = per * cus;
+  cache[key] = g;
+  return g;
+}
+
+}  // namespace spin
+
+extern "C" {
+
+const char* spin_last_error(void) { return g_err; }
+
+size_t spin_workspace_bytes(const spin_config* cfg, int32_t batch, int32_t n_rows,
+                            int32_t max_blocks) {
+  if (!cfg) return 0;
+  return spin::topk_workspace_bytes(*cfg, batch, n_rows, max_blocks);
+}
+
+spin_status spin_predict_blocks(const spin_config* cfg, const spin_batch* bt, const float* V,
+                                int64_t v_ld, const float* D, int64_t d_ld, float* S,
+                                void* stream) {
+  const char* fn = "spin_predict_blocks";
+  SPIN_CHECK(check_config(fn, cfg));
+  SPIN_CHECK(check_batch(fn, bt));
+  SPIN_CHECK(check_state(fn, bt, V, v_ld, D, d_ld));
+  SPIN_REQUIRE(S);
+  if (bt->batch == 0) return SPIN_OK;
+  return hip_status(spin::launch_predict(*cfg, *bt, V, v_ld, D, d_ld, S, (hipStream_t)stream), fn);
+}
+
+spin_status spin_select_blocks(const spin_config* cfg, const spin_batch* bt, const float* S,
+                               const int32_t* budget, uint8_t* row_code, int32_t* sel,
+                               int32_t* n_sel, void* stream) {
+  const char* fn = "spin_select_blocks";
+  SPIN_CHECK(check_config(fn, cfg));
+  SPIN_CHECK(check_batch(fn, bt));
+  SPIN_REQUIRE(S);
+  SPIN_REQUIRE(row_code);
+  SPIN_REQUIRE(sel);
+  SPIN_REQUIRE(n_sel);
+  if (bt->batch == 0) return SPIN_OK;
+  return hip_status(spin::launch_select(*cfg, *bt, S, budget, row_code, sel, n_sel,
+                                        (hipStream_t)stream), fn);
+}
+
+static spin_status check_score_args(const char* fn, const spin_config* cfg, const spin_batch* bt,
+                                    const void* q, const float* w, const void* k_pages,
+                                    const float* k_scale, const int32_t* page_table,
+                                    int64_t pt_ld, const int32_t* sel, const int32_t* n_sel,
+                                    const float* z, int64_t z_ld) {
+  SPIN_REQUIRE(q);
+  SPIN_REQUIRE(w);
+  SPIN_REQUIRE(k_pages);
+  SPIN_REQUIRE(page_table);
+  SPIN_REQUIRE(sel);
+  SPIN_REQUIRE(n_sel);
+  SPIN_CHECK(check_z(fn, bt, z, z_ld));
+  if (pt_ld < bt->max_blocks) return fail(SPIN_E_SHAPE, "%s: pt_ld < max_blocks", fn);
+  if (bt->n_pages < 1) return fail(SPIN_E_SHAPE, "%s: n_pages < 1", fn);
+  const int kd = cfg->key_dtype, qd = cfg->q_dtype;
+  const bool ok = (kd == SPIN_F32 && qd == SPIN_F32) || (kd == SPIN_BF16 && qd == SPIN_BF16) ||
+                  (kd == SPIN_FP8_E4M3 && (qd == SPIN_BF16 || qd == SPIN_F32));
+  if (!ok) return fail(SPIN_E_UNSUPPORTED, "%s: key/query dtype pair (%d, %d) not built", fn, kd, qd);
+  if (kd == SPIN_FP8_E4M3) SPIN_REQUIRE(k_scale);
+  return SPIN_OK;
+}
+
+spin_status spin_sparse_index_score(const spin_config* cfg, const spin_batch* bt, const void* q,
+                                    const float* w, const void* k_pages, const float* k_scale,
+                                    const int32_t* page_table, int64_t pt_ld, const int32_t* sel,
+                                    const int32_t* n_sel, float* z, int64_t z_ld, void* stream) {
+  const char* fn = "spin_sparse_index_score";
+  SPIN_CHECK(check_config(fn, cfg));
+  SPIN_CHECK(check_batch(fn, bt));
+  SPIN_CHECK(check_score_args(fn, cfg, bt, q, w, k_pages, k_scale, page_table, pt_ld, sel, n_sel,
+                              z, z_ld));
+  if (bt->batch == 0) return SPIN_OK;
+  return hip_status(spin::launch_score(*cfg, *bt, q, w, k_pages, k_scale, page_table, pt_ld, sel,
+                                       n_sel, z, z_ld, (hipStream_t)stream), fn);
+}
+
+spin_status spin_topk(const spin_config* cfg, const spin_batch* bt, const float* z, int64_t z_ld,
+                      const int32_t* sel, const int32_t* n_sel, int32_t* topk_idx,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "spin_topk";
+  SPIN_CHECK(check_config(fn, cfg));
+  SPIN_CHECK(check_batch(fn, bt));
+  SPIN_CHECK(check_z(fn, bt, z, z_ld));
+  SPIN_REQUIRE(sel);
+  SPIN_REQUIRE(n_sel);
+  SPIN_REQUIRE(topk_idx);
+  const size_t need = spin::topk_workspace_bytes(*cfg, bt->batch, bt->n_rows, bt->max_blocks);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SPIN_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  if (bt->batch == 0) return SPIN_OK;
+  return hip_status(spin::launch_topk(*cfg, *bt, z, z_ld, sel, n_sel, topk_idx, workspace,
+                                      workspace_bytes, (hipStream_t)stream), fn);
+}
+
+spin_status spin_ema_update(const spin_config* cfg, const spin_batch* bt, const float* z,
+                            int64_t z_ld, const int32_t* sel, const int32_t* n_sel,
+                            const int32_t* n_valid, float* V, int64_t v_ld, float* D, int64_t d_ld,
+                            void* stream) {
+  const char* fn = "spin_ema_update";
+  SPIN_CHECK(check_config(fn, cfg));
+  SPIN_CHECK(check_batch(fn, bt));
+  SPIN_CHECK(check_z(fn, bt, z, z_ld));
+  SPIN_CHECK(check_state(fn, bt, V, v_ld, D, d_ld));
+  SPIN_REQUIRE(sel);
+  SPIN_REQUIRE(n_sel);
+  if (bt->batch == 0) return SPIN_OK;
+  return hip_status(spin::launch_ema(*cfg, *bt, z, z_ld, sel, n_sel, n_valid, V, v_ld, D, d_ld,
+                                     (hipStream_t)stream), fn);
+}
+
+spin_status spin_advance(int32_t batch, int32_t n_rows, const int32_t* n_valid, int32_t* q_pos,
+                         int32_t* step, void* stream) {
+  const char* fn = "spin_advance";
+  if (batch < 0 || n_rows < 1 || n_rows > SPIN_MAX_ROWS)
+    return fail(SPIN_E_SHAPE, "%s: batch %d / n_rows %d invalid", fn, batch, n_rows);
+  if (batch == 0 || (!q_pos && !step)) return SPIN_OK;
+  return hip_status(spin::launch_advance(batch, n_rows, n_valid, q_pos, step, (hipStream_t)stream),
+                    fn);
+}
+
+spin_status spin_reset_state(int32_t batch, float* V, int64_t v_ld, float* D, int64_t d_ld,
+                             int32_t* step, void* stream) {
+  const char* fn = "spin_reset_state";
+  if (batch < 0 || v_ld < 0 || d_ld < 0) return fail(SPIN_E_SHAPE, "%s: negative size", fn);
+  if (batch == 0) return SPIN_OK;
+  if ((v_ld > 0 && !V) || (d_ld > 0 && !D)) return fail(SPIN_E_NULL, "%s: V or D is NULL", fn);
+  return hip_status(spin::launch_reset(batch, V, v_ld, D, d_ld, step, (hipStream_t)stream), fn);
+}
+
+spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_step_io* io,
+                      int32_t defer_ema, void* stream) {
+  const char* fn = "spin_step";
+  SPIN_CHECK(check_config(fn, cfg));
+  SPIN_CHECK(check_batch(fn, bt));
+  SPIN_REQUIRE(io);
+  SPIN_CHECK(check_state(fn, bt, io->V, io->v_ld, io->D, io->d_ld));
+  SPIN_REQUIRE(io->S);
+  SPIN_REQUIRE(io->row_code);
+  SPIN_REQUIRE(io->topk_idx);
+  SPIN_CHECK(check_score_args(fn, cfg, bt, io->q, io->w, io->k_pages, io->k_scale, io->page_table,
+                              io->pt_ld, io->sel, io->n_sel, io->z, io->z_ld));
+  const size_t need = spin::topk_workspace_bytes(*cfg, bt->batch, bt->n_rows, bt->max_blocks);
+  if (need > 0 && (!io->workspace || io->workspace_bytes < need))
+    return fail(SPIN_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  if (bt->batch == 0) return SPIN_OK;
+  hipStream_t st = (hipStream_t)stream;
+  SPIN_CHECK(hip_status(spin::launch_predict(*cfg, *bt, io->V, io->v_ld, io->D, io->d_ld, io->S, st),
+                        "spin_step/predict"));
+  SPIN_CHECK(hip_status(spin::launch_select(*cfg, *bt, io->S, io->budget, io->row_code, io->sel,
+                                            io->n_sel, st), "spin_step/select"));
+  SPIN_CHECK(hip_status(spin::launch_score(*cfg, *bt, io->q, io->w, io->k_pages, io->k_scale,
+                                           io->page_table, io->pt_ld, io->sel, io->n_sel, io->z,
+                                           io->z_ld, st), "spin_step/score"));
+  SPIN_CHECK(hip_status(spin::launch_topk(*cfg, *bt, io->z, io->z_ld, io->sel, io->n_sel,
+                                          io->topk_idx, io->workspace, io->workspace_bytes, st),
+                        "spin_step/topk"));
+  if (defer_ema) return SPIN_OK;
+  SPIN_CHECK(hip_status(spin::launch_ema(*cfg, *bt, io->z, io->z_ld, io->sel, io->n_sel,
+                                         io->n_valid, io->V, io->v_ld, io->D, io->d_ld, st),
+                        "spin_step/ema"));
+  if (io->q_pos_mut || io->step_mut)
+    SPIN_CHECK(hip_status(spin::launch_advance(bt->batch, bt->n_rows, io->n_valid, io->q_pos_mut,
+                                               io->step_mut, st), "spin_step/advance"));
+  return SPIN_OK;
+}
+
+}  // extern "C"

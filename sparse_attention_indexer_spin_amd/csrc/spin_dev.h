@@ -1,0 +1,194 @@
+// Internal device helpers of the SPIN library (gfx950, wave64).  Not part of
+// the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spin.h"
+
+namespace spin {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Order-preserving float -> u32 map.  -0 is folded onto +0 first (x + 0.0f is
+// +0 for x = -0 under round-to-nearest), so equal floats get equal keys and
+// a larger float always gets a larger key.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t float_key(float x) {
+  uint32_t u = __float_as_uint(x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11): ten rounds of the 4x32 S-box with
+// multipliers 0xD2511F53 / 0xCD9E8D57 and Weyl key increments 0x9E3779B9 /
+// 0xBB67AE85.  Only word 0 of the output is needed for block priorities.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+
+// ---------------------------------------------------------------------------
+// Request validity shared by every stage (SPIN_DERR_* bits, 0 = valid).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int request_error(int N, int q, int rows, int max_blocks,
+                                             int64_t v_ld, int64_t d_ld) {
+  int e = 0;
+  if (N < 1 || N > SPIN_BLOCK * max_blocks || (v_ld > 0 && (int64_t)N > v_ld)) e |= SPIN_DERR_CTX;
+  if (q < N || (d_ld > 0 && (int64_t)q + rows - 1 >= d_ld)) e |= SPIN_DERR_QPOS;
+  return e;
+}
+
+// Number of selected blocks of a request, clamped to the block capacity.
+__device__ __forceinline__ int clamp_nsel(int ns, int max_blocks) {
+  return ns < 0 ? 0 : (ns > max_blocks ? max_blocks : ns);
+}
+
+__device__ __forceinline__ void raise_error(int32_t* err, int bits) {
+  if (err && bits) atomicOr(err, bits);
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions and scans
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, kWave));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(v, d, kWave);
+    if (lane >= d) v += y;
+  }
+  return v;
+}
+
+// Block-wide exclusive scan for blockDim.x = NT (multiple of 64, <= 1024).
+// `tmp` must hold 17 ints of LDS.  Returns the exclusive prefix; *total gets
+// the block sum.  Ends with a barrier so `tmp` may be reused immediately.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) tmp[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    const int x = lane < NW ? tmp[lane] : 0;
+    const int xi = wave_incl_scan(x);
+    if (lane < NW) tmp[lane] = xi - x;
+    if (lane == NW - 1) tmp[NW] = xi;
+  }
+  __syncthreads();
+  const int out = incl - v + tmp[wid];
+  *total = tmp[NW];
+  __syncthreads();
+  return out;
+}
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_max_u32(v);
+  if (lane == 0) tmp[wid] = v;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) r = max(r, tmp[i]);
+  __syncthreads();
+  return r;
+}
+template <int NT>
+__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_min_u32(v);
+  if (lane == 0) tmp[wid] = v;
+  __syncthreads();
+  uint32_t r = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) r = min(r, tmp[i]);
+  __syncthreads();
+  return r;
+}
+template <int NT>
+__device__ __forceinline__ int block_sum_i32(int v, int* tmp) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_sum_i32(v);
+  if (lane == 0) tmp[wid] = v;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) r += tmp[i];
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Radix-select support: find, among a set of u32 keys, the threshold for the
+// k largest.  Keys are examined in 8-bit digits, starting below the common
+// prefix of the set's max and min so the first histogram is well spread.
+// The caller provides per-pass histograms; see RadixState.
+// ---------------------------------------------------------------------------
+struct RadixState {
+  uint64_t prefix;  // resolved high bits (bits below `nb` are zero)
+  int nb;           // number of unresolved low bits
+  int k;            // rank still to take among keys whose high part equals prefix
+  int bin_count;    // keys in the last chosen bin (== k: take them all)
+};
+
+// Wave 0 picks the digit: the largest d with (#keys in bins >= d) >= k.
+// hist holds 256 bins; writes {digit, k', count} into out[0..2].
+__device__ __forceinline__ void radix_pick_digit(const int* hist, int k, int* out) {
+  const int lane = threadIdx.x & 63;
+  const int c0 = hist[4 * lane + 0], c1 = hist[4 * lane + 1];
+  const int c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+  const int mine = c0 + c1 + c2 + c3;
+  // inclusive suffix sum over lanes (lane 63 holds the top bins)
+  int suf = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_down(suf, d, kWave);
+    if (lane + d < 64) suf += y;
+  }
+  int above = suf - mine;  // keys in bins of higher lanes
+  const int cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+  for (int b = 3; b >= 0; --b) {
+    if (above < k && above + cs[b] >= k) {
+      out[0] = 4 * lane + b;
+      out[1] = k - above;
+      out[2] = cs[b];
+    }
+    above += cs[b];
+  }
+}
+
+}  // namespace spin

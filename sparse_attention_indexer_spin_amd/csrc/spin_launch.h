@@ -1,0 +1,34 @@
+// Host-side launchers of the SPIN kernels (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "spin.h"
+
+namespace spin {
+
+hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
+                          const float* D, int64_t d_ld, float* S, hipStream_t st);
+hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
+                         const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
+                         hipStream_t st);
+hipError_t launch_score(const spin_config& c, const spin_batch& b, const void* q, const float* w,
+                        const void* kp, const float* ks, const int32_t* pt, int64_t pt_ld,
+                        const int32_t* sel, const int32_t* n_sel, float* z, int64_t z_ld,
+                        hipStream_t st);
+hipError_t launch_topk(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
+                       const int32_t* sel, const int32_t* n_sel, int32_t* out, void* ws,
+                       size_t ws_bytes, hipStream_t st);
+size_t topk_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks);
+hipError_t launch_ema(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
+                      const int32_t* sel, const int32_t* n_sel, const int32_t* n_valid, float* V,
+                      int64_t v_ld, float* D, int64_t d_ld, hipStream_t st);
+hipError_t launch_advance(int R, int rows, const int32_t* n_valid, int32_t* qpos, int32_t* step,
+                          hipStream_t st);
+hipError_t launch_reset(int R, float* V, int64_t v_ld, float* D, int64_t d_ld, int32_t* step,
+                        hipStream_t st);
+
+// Number of workgroups of `threads` threads of `kernel` resident at once on
+// the current device (occupancy x compute units), cached per kernel.
+int resident_workgroups(const void* kernel, int threads);
+
+}  // namespace spin

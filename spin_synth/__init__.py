@@ -175,6 +175,11 @@ def _layer_params(w: Workload, layer: int):
     return hf, hn
 
 
+def d_capacity(w: Workload, n_steps: int) -> int:
+    """Length of the diagonal-state axis: offsets reach q_pos + rows - 1 < N + rows * (steps + 1)."""
+    return w.n_slots + w.rows * (n_steps + 1) + 64
+
+
 def context_lengths(w: Workload) -> torch.Tensor:
     """Per-request context length (slots); uniform in [n_slots_min, n_slots] when ragged."""
     if w.n_slots_min == w.n_slots:

@@ -46,9 +46,7 @@ def build_layer(w: G.Workload, layer: int = 0, integer: bool = False, n_steps=No
     return LayerInputs(w, layer, ctx, keys, weights, pos, acc, q)
 
 
-def d_capacity(w: G.Workload, n_steps: int) -> int:
-    """D is indexed by offset q - i <= q_pos + rows - 1 < N + rows * (steps + 1)."""
-    return w.n_slots + w.rows * (n_steps + 1) + 64
+d_capacity = G.d_capacity
 
 
 def run_oracle(li: LayerInputs, n_steps: int, sparsity_bp: int, reqs=None, seed=G.PHILOX_SEED,

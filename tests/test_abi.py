@@ -1,0 +1,97 @@
+"""The C-ABI library loads on the CPU and exports every entry point that
+include/spin.h declares; host-side argument validation needs no GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "spin.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spin_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_attention_indexer_spin_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_attention_indexer_spin_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ["spin_predict_blocks", "spin_select_blocks", "spin_sparse_index_score",
+                 "spin_topk", "spin_ema_update", "spin_step"]:
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from sparse_attention_indexer_spin_amd import _lib
+    names = declared_functions()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_struct_layouts_match_header():
+    from sparse_attention_indexer_spin_amd import _lib
+    # spin_config: 12 x int32/float + uint64 -> 56 bytes; spin_batch: 4 ints + 5 pointers
+    assert C.sizeof(_lib.SpinConfig) == 56
+    assert C.sizeof(_lib.SpinBatch) == 16 + 5 * 8
+    assert C.sizeof(_lib.SpinStepIO) == 23 * 8
+
+
+def _cfg(**kw):
+    from sparse_attention_indexer_spin_amd import api
+    return api.config(topk=kw.pop("topk", 2048), sparsity_bp=kw.pop("sparsity_bp", 4000), **kw)
+
+
+def test_host_validation_without_gpu(lib):
+    """Argument errors are reported before any HIP call."""
+    from sparse_attention_indexer_spin_amd import _lib
+    cfg = _cfg()
+    bt = _lib.SpinBatch(batch=1, n_rows=1, max_blocks=16, n_pages=16, ctx_len=1, q_pos=1,
+                        step=1, req_id=1, err=None)
+    # NULL state
+    st = lib.spin_predict_blocks(C.byref(cfg), C.byref(bt), None, 64, None, 64, None, None)
+    assert st == 1 and b"NULL" in lib.spin_last_error()
+    # unsupported head shape
+    bad = _cfg(n_heads=32)
+    assert lib.spin_predict_blocks(C.byref(bad), C.byref(bt), 1, 64, 1, 64, 1, None) == 3
+    # block size other than 64
+    bad = _cfg(block_size=32)
+    assert lib.spin_select_blocks(C.byref(bad), C.byref(bt), 1, None, 1, 1, 1, None) == 3
+    # rows out of range
+    bt2 = _lib.SpinBatch(batch=1, n_rows=5, max_blocks=16, n_pages=16, ctx_len=1, q_pos=1,
+                         step=1, req_id=1, err=None)
+    assert lib.spin_select_blocks(C.byref(cfg), C.byref(bt2), 1, None, 1, 1, 1, None) == 2
+    # topk out of range
+    bad = _cfg(topk=0)
+    assert lib.spin_topk(C.byref(bad), C.byref(bt), 1, 1024, 1, 1, 1, None, 0, None) == 2
+    # z_ld too small
+    assert lib.spin_topk(C.byref(cfg), C.byref(bt), 1, 64, 1, 1, 1, None, 0, None) == 2
+    # unsupported dtype pair: bf16 keys with fp32 queries
+    import torch
+    bad = _cfg(key_dtype=torch.bfloat16, q_dtype=torch.float32)
+    st = lib.spin_sparse_index_score(C.byref(bad), C.byref(bt), 1, 1, 1, None, 1, 16, 1, 1, 1,
+                                     1024, None)
+    assert st == 3
+    # fp8 keys need scales
+    st = lib.spin_sparse_index_score(C.byref(cfg), C.byref(bt), 1, 1, 1, None, 1, 16, 1, 1, 1,
+                                     1024, None)
+    assert st == 1
+    # an empty batch is a valid no-op
+    bt0 = _lib.SpinBatch(batch=0, n_rows=1, max_blocks=16, n_pages=16, ctx_len=None,
+                         q_pos=None, step=None, req_id=None, err=None)
+    assert lib.spin_predict_blocks(C.byref(cfg), C.byref(bt0), 1, 64, 1, 64, 1, None) == 0
+    assert lib.spin_advance(0, 1, None, None, None, None) == 0
+    assert lib.spin_advance(1, 9, None, None, None, None) == 2
+    assert lib.spin_workspace_bytes(C.byref(cfg), 32, 1, 2048) >= 0
