@@ -22,6 +22,9 @@ SOURCES = ["spin_api.hip", "k_select.hip", "k_score.hip", "k_topk.hip", "k_ema.h
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
+    # no implicit multiply-add fusion: the EMA and the combine rules are
+    # specified as separately rounded fp32 operations
+    "-ffp-contract=off",
     # packed fp32 (v_pk_*_f32) stays disabled for every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,

@@ -52,6 +52,8 @@ __device__ __forceinline__ void ema_offset(const EmaCtx& e, int s0, float* Dr) {
   if (upd) Dr[o] = d;
 }
 
+constexpr int kEmaBlocksPerWave = 4;
+
 __global__ __launch_bounds__(256) void k_ema(float alpha, int rows, int max_blocks,
                                              const int32_t* __restrict__ ctx,
                                              const int32_t* __restrict__ qpos,
@@ -62,44 +64,72 @@ __global__ __launch_bounds__(256) void k_ema(float alpha, int rows, int max_bloc
                                              float* __restrict__ V, int64_t v_ld,
                                              float* __restrict__ D, int64_t d_ld) {
   const int r = blockIdx.y;
-  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int k0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kEmaBlocksPerWave;
   const int lane = threadIdx.x & 63;
   const int N = ctx[r], q = qpos[r];
   if (request_error(N, q, rows, max_blocks, v_ld, d_ld)) return;
   const int ns = clamp_nsel(n_sel[r], max_blocks);
-  if (k >= ns) return;
+  if (k0 >= ns) return;
   int L = n_valid ? n_valid[r] : rows;
   L = L < 0 ? 0 : (L > rows ? rows : L);
   if (L == 0) return;
   const int32_t* sr = sel + (int64_t)r * max_blocks;
-  EmaCtx e;
-  e.a = alpha;
-  e.b = __fsub_rn(1.0f, alpha);
-  e.L = L; e.N = N; e.q = q; e.k = k; e.ns = ns;
-  e.j = sr[k];
-  if (e.j < 0 || e.j >= max_blocks) return;
-  e.zb = z + (int64_t)r * rows * z_ld;
-  e.z_ld = z_ld;
-  e.sel = sr;
+  const float a = alpha, b = __fsub_rn(1.0f, alpha);
+  const float* zb = z + (int64_t)r * rows * z_ld;
   float* Vr = V + (int64_t)r * v_ld;
   float* Dr = D + (int64_t)r * d_ld;
-  const int i = e.j * 64 + lane;
-  if (i < N) {
-    float v = Vr[i];
-    for (int row = 0; row < L; ++row) v = ema_step(v, e.zb[row * z_ld + k * 64 + lane], e.a, e.b);
-    Vr[i] = v;
+  if (L == 1) {
+    // one observation per slot: V[i] and D[q - i] from row 0, loads batched
+    float vv[kEmaBlocksPerWave], dd[kEmaBlocksPerWave], zz[kEmaBlocksPerWave];
+    int ii[kEmaBlocksPerWave];
+#pragma unroll
+    for (int u = 0; u < kEmaBlocksPerWave; ++u) {
+      const int k = k0 + u;
+      const int j = k < ns ? sr[k] : -1;
+      const int i = j * 64 + lane;
+      const bool ok = k < ns && j >= 0 && j < max_blocks && i < N;
+      ii[u] = ok ? i : -1;
+      vv[u] = ok ? Vr[i] : 0.0f;
+      dd[u] = ok ? Dr[q - i] : 0.0f;
+      zz[u] = ok ? zb[(int64_t)k * 64 + lane] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kEmaBlocksPerWave; ++u) {
+      if (ii[u] < 0) continue;
+      Vr[ii[u]] = ema_step(vv[u], zz[u], a, b);
+      Dr[q - ii[u]] = ema_step(dd[u], zz[u], a, b);
+    }
+    return;
   }
-  ema_offset(e, i, Dr);
-  if (lane < L - 1) {
-    const bool prev_selected = k > 0 && sr[k - 1] == e.j - 1;
-    if (!prev_selected) ema_offset(e, e.j * 64 - 1 - lane, Dr);
+  for (int u = 0; u < kEmaBlocksPerWave; ++u) {
+    const int k = k0 + u;
+    if (k >= ns) break;
+    EmaCtx e;
+    e.a = a; e.b = b;
+    e.L = L; e.N = N; e.q = q; e.k = k; e.ns = ns;
+    e.j = sr[k];
+    if (e.j < 0 || e.j >= max_blocks) continue;
+    e.zb = zb;
+    e.z_ld = z_ld;
+    e.sel = sr;
+    const int i = e.j * 64 + lane;
+    if (i < N) {
+      float v = Vr[i];
+      for (int row = 0; row < L; ++row) v = ema_step(v, zb[row * z_ld + (int64_t)k * 64 + lane], a, b);
+      Vr[i] = v;
+    }
+    ema_offset(e, i, Dr);
+    if (lane < L - 1) {
+      const bool prev_selected = k > 0 && sr[k - 1] == e.j - 1;
+      if (!prev_selected) ema_offset(e, e.j * 64 - 1 - lane, Dr);
+    }
   }
 }
 
 hipError_t launch_ema(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                       const int32_t* sel, const int32_t* n_sel, const int32_t* n_valid, float* V,
                       int64_t v_ld, float* D, int64_t d_ld, hipStream_t st) {
-  dim3 grid((b.max_blocks + 3) / 4, b.batch);
+  dim3 grid((b.max_blocks + 4 * kEmaBlocksPerWave - 1) / (4 * kEmaBlocksPerWave), b.batch);
   hipLaunchKernelGGL(k_ema, grid, dim3(256), 0, st, c.ema_alpha, b.n_rows, b.max_blocks,
                      b.ctx_len, b.q_pos, n_valid, z, z_ld, sel, n_sel, V, v_ld, D, d_ld);
   return hipGetLastError();

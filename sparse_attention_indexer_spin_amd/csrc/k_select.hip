@@ -14,9 +14,13 @@ namespace spin {
 
 // ---------------------------------------------------------------------------
 // Stage 1: S[r][row][j] = max_{i in block j, i < N} C(V[i], D[q_row - i]).
-// One wave per 4 consecutive blocks; lane = slot within the block.  The data
-// is read once with coalesced 256-B rows (V ascending, D descending).
+// One wave per 8 consecutive blocks, lane = slot within the block; all 16
+// loads of a lane are issued before the first reduction so each wave keeps
+// 4 KB in flight.  V rows are read ascending, D rows descending (both as
+// coalesced 256-B wave accesses).
 // ---------------------------------------------------------------------------
+constexpr int kPredBlocksPerWave = 8;
+
 __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_blocks,
                                                  const int32_t* __restrict__ ctx,
                                                  const int32_t* __restrict__ qpos,
@@ -33,96 +37,28 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
   const int q = q0 + row;
   const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j0 = (blockIdx.x * 4 + wave) * 4;
+  const int j0 = (blockIdx.x * 4 + wave) * kPredBlocksPerWave;
   if (j0 >= B) return;
   const float* Vr = V + (int64_t)r * v_ld;
   const float* Dr = D + (int64_t)r * d_ld;
-  float vv[4], dd[4];
+  float vv[kPredBlocksPerWave], dd[kPredBlocksPerWave];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < kPredBlocksPerWave; ++b) {
     const int i = (j0 + b) * SPIN_BLOCK + lane;
-    const bool ok = (j0 + b) < B && i < N;
+    const bool ok = i < N;
     vv[b] = ok ? Vr[i] : 0.0f;
     dd[b] = ok ? Dr[q - i] : 0.0f;
   }
   float* Srow = S + ((int64_t)r * rows + row) * max_blocks;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < kPredBlocksPerWave; ++b) {
     const int j = j0 + b;
     const int i = j * SPIN_BLOCK + lane;
     float zhat = combine == SPIN_COMBINE_SUM ? __fadd_rn(vv[b], dd[b]) : fmaxf(vv[b], dd[b]);
-    zhat = (j < B && i < N) ? zhat : -INFINITY;
+    zhat = i < N ? zhat : -INFINITY;
     const float m = wave_max_f32(zhat);
     if (lane == 0 && j < B) Srow[j] = m + 0.0f;
   }
-}
-
-// ---------------------------------------------------------------------------
-// Block-level selection of the k largest u32 keys among flagged elements
-// (ties: lower element index).  Thread t owns elements t*EPT .. t*EPT+EPT-1.
-// On return, bit e of the result mask marks the chosen elements.
-// ---------------------------------------------------------------------------
-constexpr int kSelThreads = 1024;
-
-template <int EPT>
-__device__ uint32_t block_select_top(const uint32_t (&key)[EPT], uint32_t elig, int k,
-                                     int* hist, int* sh, uint32_t* tmpu) {
-  if (k <= 0) return 0u;
-  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    if (elig >> e & 1u) { mx = max(mx, key[e]); mn = min(mn, key[e]); }
-  mx = block_max_u32<kSelThreads>(mx, tmpu);
-  mn = block_min_u32<kSelThreads>(mn, tmpu);
-  int nb = (mx == mn) ? 0 : 32 - __clz(mx ^ mn);
-  uint64_t prefix = ((uint64_t)mx >> nb) << nb;
-  while (nb > 0) {
-    const int db = nb < 8 ? nb : 8, pos = nb - db;
-    for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < EPT; ++e)
-      if ((elig >> e & 1u) && ((uint64_t)key[e] >> nb) == (prefix >> nb))
-        atomicAdd(&hist[(key[e] >> pos) & ((1u << db) - 1u)], 1);
-    __syncthreads();
-    if (threadIdx.x < 64) radix_pick_digit(hist, k, sh);
-    __syncthreads();
-    const int d = sh[0], cnt = sh[2];
-    k = sh[1];
-    __syncthreads();
-    prefix |= (uint64_t)d << pos;
-    nb = pos;
-    if (cnt == k) break;  // every key of this bin is taken
-  }
-  const uint64_t hp = prefix >> nb;
-  int eq = 0;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    if ((elig >> e & 1u) && ((uint64_t)key[e] >> nb) == hp) ++eq;
-  int tot;
-  int rank = block_excl_scan<kSelThreads>(eq, sh + 4, &tot);
-  uint32_t out = 0u;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    if (!(elig >> e & 1u)) continue;
-    const uint64_t hk = (uint64_t)key[e] >> nb;
-    if (hk > hp) out |= 1u << e;
-    else if (hk == hp) { if (rank < k) out |= 1u << e; ++rank; }
-  }
-  return out;
-}
-
-// Write the ascending list of flagged blocks; pad with -1 to max_blocks.
-template <int EPT>
-__device__ void compact_blocks(uint32_t flag, int max_blocks, int32_t* sel_row, int32_t* n_sel_r,
-                               int* sh) {
-  int tot;
-  int pos = block_excl_scan<kSelThreads>(__popc(flag), sh, &tot);
-#pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    if (flag >> e & 1u) sel_row[pos++] = threadIdx.x * EPT + e;
-  for (int i = tot + threadIdx.x; i < max_blocks; i += kSelThreads) sel_row[i] = -1;
-  if (threadIdx.x == 0) *n_sel_r = tot;
 }
 
 // ---------------------------------------------------------------------------
@@ -246,7 +182,8 @@ __global__ void k_zero_i32(int32_t* __restrict__ p, int n) {
 // ---------------------------------------------------------------------------
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
                           const float* D, int64_t d_ld, float* S, hipStream_t st) {
-  dim3 grid((b.max_blocks + 15) / 16, b.n_rows, b.batch);
+  dim3 grid((b.max_blocks + 4 * kPredBlocksPerWave - 1) / (4 * kPredBlocksPerWave), b.n_rows,
+            b.batch);
   hipLaunchKernelGGL(k_predict, grid, dim3(256), 0, st, c.combine, b.n_rows, b.max_blocks,
                      b.ctx_len, b.q_pos, V, v_ld, D, d_ld, S, b.err);
   return hipGetLastError();

@@ -2,21 +2,126 @@
 // slots ("SPIN: Shadow Predictive Indexer for Sparse Attention", Algorithm 1
 // step 7; Sec. 2 gives K between 512 and 2048 in practice).
 //
-// One 1024-thread workgroup per (request, verifier row).  Scores are mapped to
-// order-preserving u32 keys and the K-th largest is found by radix select in
-// 8-bit digits, starting below the common prefix of the row's max and min so
-// the first histogram spreads well.  Ties at the threshold go to the lower
-// slot; the selected slots are written in ascending slot order (the compact
-// score layout is already in ascending slot order), padded with -1.
+// Scores map to order-preserving u32 keys; the result is the min(K, |dom|)
+// valid slots with the largest keys (ties: lower slot), written in ascending
+// slot order (the compact score layout is already in ascending slot order).
+//
+// Two kernels per call:
+//   1. filter (one workgroup per 4096-slot chunk of a row): keeps the valid
+//      slots whose key is >= a per-row threshold hint, compacted in order.
+//   2. select (one workgroup per row): if the kept count c satisfies
+//      K' <= c <= 8192 (K' = min(K, |dom|)), the exact top-K' is taken among
+//      the kept candidates in LDS.  This is exact for ANY hint: an element
+//      below the hint is outranked by all c >= K' candidates.  Otherwise the
+//      row falls back to a radix select over all of its scores.
+// The hint lives in the caller's workspace and is refreshed every call so
+// that about 2K candidates pass the next step's filter: scores of a layer are
+// strongly correlated from one decode step to the next, the observation the
+// method itself rests on.  Its value only affects speed, never results.
 #include "spin_dev.h"
 #include "spin_launch.h"
 
 namespace spin {
 
-constexpr int kTopThreads = 1024;
-constexpr int kTopEPT = 8;
-constexpr int kTopChunk = kTopThreads * kTopEPT;
+constexpr int kChunk = 4096;              // filter chunk (64 blocks)
+constexpr int kFilterThreads = 256;       // 16 candidates per thread
+constexpr int kCap = kSelThreads * 8;     // candidates the LDS path takes
+constexpr int kTopEPT = 8;                // fallback: candidates per thread per pass
+constexpr int kTopChunk = kSelThreads * kTopEPT;
 
+struct TopkWs {
+  uint32_t* hint;   // [rows_total]
+  int32_t* cnt;     // [rows_total][n_chunks] candidates kept
+  int32_t* valid;   // [rows_total][n_chunks] valid slots
+  uint2* cand;      // [rows_total][n_cap] (key, slot), chunk c at offset c * kChunk
+  int n_chunks;
+  int64_t n_cap;
+};
+
+__host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+__host__ __device__ inline TopkWs carve(void* ws, int rows_total, int max_blocks) {
+  TopkWs w;
+  w.n_cap = (int64_t)max_blocks * 64;
+  w.n_chunks = (int)((w.n_cap + kChunk - 1) / kChunk);
+  char* p = reinterpret_cast<char*>(ws);
+  int64_t off = 0;
+  w.hint = reinterpret_cast<uint32_t*>(p + off);
+  off = align256(off + 4LL * rows_total);
+  w.cnt = reinterpret_cast<int32_t*>(p + off);
+  off = align256(off + 4LL * rows_total * w.n_chunks);
+  w.valid = reinterpret_cast<int32_t*>(p + off);
+  off = align256(off + 4LL * rows_total * w.n_chunks);
+  w.cand = reinterpret_cast<uint2*>(p + off);
+  return w;
+}
+
+static int64_t ws_size(int rows_total, int max_blocks) {
+  const int64_t n_cap = (int64_t)max_blocks * 64;
+  const int64_t n_chunks = (n_cap + kChunk - 1) / kChunk;
+  return align256(4LL * rows_total) + 2 * align256(4LL * rows_total * n_chunks) +
+         8LL * rows_total * n_cap;
+}
+
+__device__ __forceinline__ int row_candidates(int N, int qpos, int rows, int max_blocks,
+                                              const int32_t* n_sel, int r) {
+  if (request_error(N, qpos, rows, max_blocks, 0, 0)) return 0;
+  return clamp_nsel(n_sel[r], max_blocks) * 64;
+}
+
+// ---------------------------------------------------------------------------
+// 1. filter
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kFilterThreads) void k_topk_filter(
+    int rows, int max_blocks, const int32_t* __restrict__ ctx, const int32_t* __restrict__ qpos,
+    const float* __restrict__ z, int64_t z_ld, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ n_sel, TopkWs ws) {
+  __shared__ int sh[32];
+  const int rowid = blockIdx.y, r = rowid / rows, chunk = blockIdx.x;
+  const int N = ctx[r];
+  const int n = row_candidates(N, qpos[r], rows, max_blocks, n_sel, r);
+  const int c0 = chunk * kChunk;
+  if (c0 >= n) return;
+  const uint32_t tau = ws.hint[rowid];
+  const int cb = c0 + threadIdx.x * 16;
+  const float* zr = z + (int64_t)rowid * z_ld;
+  uint32_t key[16];
+  uint32_t pass = 0u, valid = 0u;
+  int slot0 = 0;
+  if (cb < n) {
+    slot0 = sel[(int64_t)r * max_blocks + (cb >> 6)] * 64 + (cb & 63);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float4 x = *reinterpret_cast<const float4*>(zr + cb + 4 * v);
+      key[4 * v + 0] = float_key(x.x);
+      key[4 * v + 1] = float_key(x.y);
+      key[4 * v + 2] = float_key(x.z);
+      key[4 * v + 3] = float_key(x.w);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (slot0 + e < N) {
+        valid |= 1u << e;
+        if (key[e] >= tau) pass |= 1u << e;
+      }
+    }
+  }
+  int total;
+  int pos = block_excl_scan<kFilterThreads>(__popc(pass), sh, &total);
+  uint2* out = ws.cand + (int64_t)rowid * ws.n_cap + c0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (pass >> e & 1u) out[pos++] = make_uint2(key[e], (uint32_t)(slot0 + e));
+  const int nvalid = block_sum_i32<kFilterThreads>(__popc(valid), sh);
+  if (threadIdx.x == 0) {
+    ws.cnt[(int64_t)rowid * ws.n_chunks + chunk] = total;
+    ws.valid[(int64_t)rowid * ws.n_chunks + chunk] = nvalid;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. select -- fallback helpers: radix passes over the whole row in global memory
+// ---------------------------------------------------------------------------
 struct TopkRow {
   const float* z;
   const int32_t* sel;
@@ -24,14 +129,12 @@ struct TopkRow {
   int N;  // context length
 };
 
-// Load this thread's 8 consecutive candidates of chunk `cb`; returns a valid mask.
 __device__ __forceinline__ uint32_t load_keys(const TopkRow& R, int cb, uint32_t (&key)[kTopEPT],
                                               int& slot0) {
   const int c0 = cb + threadIdx.x * kTopEPT;
   slot0 = 0;
   if (c0 >= R.n) return 0u;
-  const int blk = R.sel[c0 >> 6];
-  slot0 = blk * 64 + (c0 & 63);
+  slot0 = R.sel[c0 >> 6] * 64 + (c0 & 63);
   const float4 a = *reinterpret_cast<const float4*>(R.z + c0);
   const float4 b = *reinterpret_cast<const float4*>(R.z + c0 + 4);
   const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -44,24 +147,40 @@ __device__ __forceinline__ uint32_t load_keys(const TopkRow& R, int cb, uint32_t
   return valid;
 }
 
-__global__ __launch_bounds__(kTopThreads) void k_topk(int K, int rows, int max_blocks,
-                                                      const int32_t* __restrict__ ctx,
-                                                      const int32_t* __restrict__ qpos,
-                                                      const float* __restrict__ z, int64_t z_ld,
-                                                      const int32_t* __restrict__ sel,
-                                                      const int32_t* __restrict__ n_sel,
-                                                      int32_t* __restrict__ out) {
-  __shared__ int hist[256];
-  __shared__ int sh[32];
-  __shared__ uint32_t tmpu[16];
-  const int row = blockIdx.x, r = blockIdx.y;
-  int32_t* orow = out + ((int64_t)r * rows + row) * K;
-  const int N = ctx[r];
-  const bool bad = request_error(N, qpos[r], rows, max_blocks, 0, 0) != 0;
-  TopkRow R{z + ((int64_t)r * rows + row) * z_ld, sel + (int64_t)r * max_blocks,
-            bad ? 0 : clamp_nsel(n_sel[r], max_blocks) * 64, N};
+// Threshold of the k largest valid keys of the row: on return, keys whose top
+// (32 - nb) bits exceed prefix's are in, and `k` of those equal to it (lowest
+// slots first) are in too.
+__device__ void radix_threshold(const TopkRow& R, uint32_t mx, uint32_t mn, int& k, int& nb,
+                                uint64_t& prefix, int* hist, int* sh) {
+  nb = (mx == mn) ? 0 : 32 - __clz(mx ^ mn);
+  prefix = ((uint64_t)mx >> nb) << nb;
+  while (nb > 0) {
+    const int db = nb < 8 ? nb : 8, pos = nb - db;
+    for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    for (int cb = 0; cb < R.n; cb += kTopChunk) {
+      uint32_t key[kTopEPT];
+      int s0;
+      const uint32_t v = load_keys(R, cb, key, s0);
+#pragma unroll
+      for (int e = 0; e < kTopEPT; ++e)
+        if ((v >> e & 1u) && ((uint64_t)key[e] >> nb) == (prefix >> nb))
+          atomicAdd(&hist[(key[e] >> pos) & ((1u << db) - 1u)], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) radix_pick_digit(hist, k, sh);
+    __syncthreads();
+    const int d = sh[0], bc = sh[2];
+    k = sh[1];
+    __syncthreads();
+    prefix |= (uint64_t)d << pos;
+    nb = pos;
+    if (bc == k) break;
+  }
+}
 
-  // pass 1: valid count and key range
+__device__ void fallback_row(const TopkRow& R, int K, int32_t* orow, uint32_t* hint, int* hist,
+                             int* sh, uint32_t* tmpu) {
   int cnt = 0;
   uint32_t mx = 0u, mn = 0xFFFFFFFFu;
   for (int cb = 0; cb < R.n; cb += kTopChunk) {
@@ -73,45 +192,15 @@ __global__ __launch_bounds__(kTopThreads) void k_topk(int K, int rows, int max_b
     for (int e = 0; e < kTopEPT; ++e)
       if (v >> e & 1u) { mx = max(mx, key[e]); mn = min(mn, key[e]); }
   }
-  const int nvalid = block_sum_i32<kTopThreads>(cnt, sh);
-  mx = block_max_u32<kTopThreads>(mx, tmpu);
-  mn = block_min_u32<kTopThreads>(mn, tmpu);
+  const int nvalid = block_sum_i32<kSelThreads>(cnt, sh);
+  mx = block_max_u32<kSelThreads>(mx, tmpu);
+  mn = block_min_u32<kSelThreads>(mn, tmpu);
   const int take = min(K, nvalid);
-
-  // radix select of the take-th largest key (skipped when every valid slot is taken)
   int nb = 0, k = take;
   uint64_t prefix = 0;
-  if (take < nvalid && take > 0) {
-    nb = (mx == mn) ? 0 : 32 - __clz(mx ^ mn);
-    prefix = ((uint64_t)mx >> nb) << nb;
-    while (nb > 0) {
-      const int db = nb < 8 ? nb : 8, pos = nb - db;
-      for (int i = threadIdx.x; i < 256; i += kTopThreads) hist[i] = 0;
-      __syncthreads();
-      for (int cb = 0; cb < R.n; cb += kTopChunk) {
-        uint32_t key[kTopEPT];
-        int s0;
-        const uint32_t v = load_keys(R, cb, key, s0);
-#pragma unroll
-        for (int e = 0; e < kTopEPT; ++e)
-          if ((v >> e & 1u) && ((uint64_t)key[e] >> nb) == (prefix >> nb))
-            atomicAdd(&hist[(key[e] >> pos) & ((1u << db) - 1u)], 1);
-      }
-      __syncthreads();
-      if (threadIdx.x < 64) radix_pick_digit(hist, k, sh);
-      __syncthreads();
-      const int d = sh[0], bc = sh[2];
-      k = sh[1];
-      __syncthreads();
-      prefix |= (uint64_t)d << pos;
-      nb = pos;
-      if (bc == k) break;
-    }
-  }
   const bool take_all = take >= nvalid;
+  if (!take_all) radix_threshold(R, mx, mn, k, nb, prefix, hist, sh);
   const uint64_t hp = prefix >> nb;
-
-  // emit in ascending slot order
   int written = 0, eq_before = 0;
   for (int cb = 0; cb < R.n; cb += kTopChunk) {
     uint32_t key[kTopEPT];
@@ -126,29 +215,129 @@ __global__ __launch_bounds__(kTopThreads) void k_topk(int K, int rows, int max_b
       else if (hk == hp) eq |= 1u << e;
     }
     int eq_tot;
-    int eq_rank = eq_before + block_excl_scan<kTopThreads>(__popc(eq), sh, &eq_tot);
+    int eq_rank = eq_before + block_excl_scan<kSelThreads>(__popc(eq), sh, &eq_tot);
     uint32_t chosen = gt;
 #pragma unroll
     for (int e = 0; e < kTopEPT; ++e)
       if (eq >> e & 1u) { if (eq_rank < k) chosen |= 1u << e; ++eq_rank; }
     eq_before += eq_tot;
     int tot;
-    int pos = written + block_excl_scan<kTopThreads>(__popc(chosen), sh, &tot);
+    int pos = written + block_excl_scan<kSelThreads>(__popc(chosen), sh, &tot);
 #pragma unroll
     for (int e = 0; e < kTopEPT; ++e)
       if ((chosen >> e & 1u) && pos < K) orow[pos++] = s0 + e;
     written += tot;
   }
-  for (int i = written + threadIdx.x; i < K; i += kTopThreads) orow[i] = -1;
+  for (int i = written + threadIdx.x; i < K; i += kSelThreads) orow[i] = -1;
+  // next hint: the key of rank min(|dom|, 2 K') so about 2 K' slots pass the filter
+  const int r2 = min(nvalid, 2 * take);
+  if (r2 > 0 && r2 < nvalid) {
+    int k2 = r2, nb2;
+    uint64_t p2;
+    radix_threshold(R, mx, mn, k2, nb2, p2, hist, sh);
+    if (threadIdx.x == 0) *hint = (uint32_t)p2;  // low bits zero: a slightly lower bound
+  } else if (threadIdx.x == 0) {
+    *hint = 0u;
+  }
 }
 
-size_t topk_workspace_bytes(const spin_config&, int, int, int) { return 0; }
+// ---------------------------------------------------------------------------
+// 2. select
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSelThreads) void k_topk_select(
+    int K, int rows, int max_blocks, const int32_t* __restrict__ ctx,
+    const int32_t* __restrict__ qpos, const float* __restrict__ z, int64_t z_ld,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
+    int32_t* __restrict__ out, TopkWs ws) {
+  __shared__ uint32_t lkey[kCap];
+  __shared__ int off[kSelThreads / 4 + 1];
+  __shared__ int hist[256];
+  __shared__ int sh[32];
+  __shared__ uint32_t tmpu[16];
+  const int rowid = blockIdx.x, r = rowid / rows;
+  int32_t* orow = out + (int64_t)rowid * K;
+  const int N = ctx[r];
+  const int n = row_candidates(N, qpos[r], rows, max_blocks, n_sel, r);
+  const int nch = (n + kChunk - 1) / kChunk;
+  // chunk offsets of the kept candidates, and the valid count
+  int c_mine = 0, v_mine = 0;
+  for (int i = threadIdx.x; i < nch; i += kSelThreads) {
+    c_mine += ws.cnt[(int64_t)rowid * ws.n_chunks + i];
+    v_mine += ws.valid[(int64_t)rowid * ws.n_chunks + i];
+  }
+  // nch <= 128 < kSelThreads: one chunk per thread at most
+  int c_tot;
+  const int c_off = block_excl_scan<kSelThreads>(c_mine, sh, &c_tot);
+  if (threadIdx.x < nch) off[threadIdx.x] = c_off;
+  if (threadIdx.x == nch) off[nch] = c_tot;
+  const int nvalid = block_sum_i32<kSelThreads>(v_mine, sh);
+  const int take = min(K, nvalid);
+  __syncthreads();
+  if (take == 0) {
+    for (int i = threadIdx.x; i < K; i += kSelThreads) orow[i] = -1;
+    return;
+  }
+  if (c_tot < take || c_tot > kCap) {
+    TopkRow R{z + (int64_t)rowid * z_ld, sel + (int64_t)r * max_blocks, n, N};
+    fallback_row(R, K, orow, ws.hint + rowid, hist, sh, tmpu);
+    return;
+  }
+  // gather the kept keys (ascending slot order) into LDS
+  const uint2* cand = ws.cand + (int64_t)rowid * ws.n_cap;
+  for (int i = 0; i < nch; ++i) {
+    const int o = off[i], cnt = off[i + 1] - o;
+    for (int e = threadIdx.x; e < cnt; e += kSelThreads) lkey[o + e] = cand[(int64_t)i * kChunk + e].x;
+  }
+  __syncthreads();
+  uint32_t key[8];
+  uint32_t elig = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int p = threadIdx.x * 8 + e;
+    key[e] = p < c_tot ? lkey[p] : 0u;
+    if (p < c_tot) elig |= 1u << e;
+  }
+  const uint32_t chosen = block_select_top<8>(key, elig, take, hist, sh, tmpu);
+  int tot;
+  int pos = block_excl_scan<kSelThreads>(__popc(chosen), sh, &tot);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (!(chosen >> e & 1u)) continue;
+    const int p = threadIdx.x * 8 + e;
+    int lo = 0, hi = nch - 1;  // chunk holding kept candidate p
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    if (pos < K) orow[pos++] = (int32_t)cand[(int64_t)lo * kChunk + (p - off[lo])].y;
+  }
+  for (int i = tot + threadIdx.x; i < K; i += kSelThreads) orow[i] = -1;
+  // keep the hint while it passes a comfortable number of candidates; raise
+  // it to rank 2 K' when too many pass
+  if (c_tot > 4 * take) {
+    const uint32_t top2 = block_select_top<8>(key, elig, 2 * take, hist, sh, tmpu);
+    uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (top2 >> e & 1u) m = min(m, key[e]);
+    m = block_min_u32<kSelThreads>(m, tmpu);
+    if (threadIdx.x == 0) ws.hint[rowid] = m;
+  }
+}
+
+size_t topk_workspace_bytes(const spin_config&, int R, int rows, int max_blocks) {
+  return (size_t)ws_size(R * rows, max_blocks);
+}
 
 hipError_t launch_topk(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
-                       const int32_t* sel, const int32_t* n_sel, int32_t* out, void*, size_t,
+                       const int32_t* sel, const int32_t* n_sel, int32_t* out, void* wsp, size_t,
                        hipStream_t st) {
-  hipLaunchKernelGGL(k_topk, dim3(b.n_rows, b.batch), dim3(kTopThreads), 0, st, c.topk, b.n_rows,
-                     b.max_blocks, b.ctx_len, b.q_pos, z, z_ld, sel, n_sel, out);
+  const int rows_total = b.batch * b.n_rows;
+  const TopkWs ws = carve(wsp, rows_total, b.max_blocks);
+  hipLaunchKernelGGL(k_topk_filter, dim3(ws.n_chunks, rows_total), dim3(kFilterThreads), 0, st,
+                     b.n_rows, b.max_blocks, b.ctx_len, b.q_pos, z, z_ld, sel, n_sel, ws);
+  hipLaunchKernelGGL(k_topk_select, dim3(rows_total), dim3(kSelThreads), 0, st, c.topk, b.n_rows,
+                     b.max_blocks, b.ctx_len, b.q_pos, z, z_ld, sel, n_sel, out, ws);
   return hipGetLastError();
 }
 

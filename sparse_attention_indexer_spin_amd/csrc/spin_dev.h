@@ -191,4 +191,73 @@ __device__ __forceinline__ void radix_pick_digit(const int* hist, int k, int* ou
   }
 }
 
+constexpr int kSelThreads = 1024;
+
+// ---------------------------------------------------------------------------
+// Block-level selection of the k largest u32 keys among flagged elements
+// (ties: lower element index).  Thread t owns elements t*EPT .. t*EPT+EPT-1.
+// On return, bit e of the result mask marks the chosen elements.
+// ---------------------------------------------------------------------------
+
+template <int EPT>
+__device__ uint32_t block_select_top(const uint32_t (&key)[EPT], uint32_t elig, int k,
+                                     int* hist, int* sh, uint32_t* tmpu) {
+  if (k <= 0) return 0u;
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (elig >> e & 1u) { mx = max(mx, key[e]); mn = min(mn, key[e]); }
+  mx = block_max_u32<kSelThreads>(mx, tmpu);
+  mn = block_min_u32<kSelThreads>(mn, tmpu);
+  int nb = (mx == mn) ? 0 : 32 - __clz(mx ^ mn);
+  uint64_t prefix = ((uint64_t)mx >> nb) << nb;
+  while (nb > 0) {
+    const int db = nb < 8 ? nb : 8, pos = nb - db;
+    for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if ((elig >> e & 1u) && ((uint64_t)key[e] >> nb) == (prefix >> nb))
+        atomicAdd(&hist[(key[e] >> pos) & ((1u << db) - 1u)], 1);
+    __syncthreads();
+    if (threadIdx.x < 64) radix_pick_digit(hist, k, sh);
+    __syncthreads();
+    const int d = sh[0], cnt = sh[2];
+    k = sh[1];
+    __syncthreads();
+    prefix |= (uint64_t)d << pos;
+    nb = pos;
+    if (cnt == k) break;  // every key of this bin is taken
+  }
+  const uint64_t hp = prefix >> nb;
+  int eq = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if ((elig >> e & 1u) && ((uint64_t)key[e] >> nb) == hp) ++eq;
+  int tot;
+  int rank = block_excl_scan<kSelThreads>(eq, sh + 4, &tot);
+  uint32_t out = 0u;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (!(elig >> e & 1u)) continue;
+    const uint64_t hk = (uint64_t)key[e] >> nb;
+    if (hk > hp) out |= 1u << e;
+    else if (hk == hp) { if (rank < k) out |= 1u << e; ++rank; }
+  }
+  return out;
+}
+
+// Write the ascending list of flagged blocks; pad with -1 to max_blocks.
+template <int EPT>
+__device__ void compact_blocks(uint32_t flag, int max_blocks, int32_t* sel_row, int32_t* n_sel_r,
+                               int* sh) {
+  int tot;
+  int pos = block_excl_scan<kSelThreads>(__popc(flag), sh, &tot);
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (flag >> e & 1u) sel_row[pos++] = threadIdx.x * EPT + e;
+  for (int i = tot + threadIdx.x; i < max_blocks; i += kSelThreads) sel_row[i] = -1;
+  if (threadIdx.x == 0) *n_sel_r = tot;
+}
+
 }  // namespace spin

@@ -4,7 +4,7 @@ fp32, so every stage must match bit for bit), and the error paths.
 
 Bars: bit-exact for masks, exploration draws, block lists, top-K index sets
 and EMA state; indexer scores within 1e-3 relative (bf16 keys), 2e-2 (fp8
-keys) and 1e-5 (fp32 keys: fp32 accumulation of 128 products and 64 heads),
+keys) and 1e-4 (fp32 keys: fp32 accumulation of 128 products and 64 heads),
 relative to max(|z|, 1e-3 rms(z))."""
 import numpy as np
 import pytest
@@ -17,7 +17,9 @@ from tests.harness import build_layer, run_oracle
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "bf16": 1e-3, "fp8": 2e-2}
+# fp32 keys: a 128-term fp32 dot product carries up to ~128 * 2^-24 of
+# sum|q_c k_c|, a few times |q . k| for these inputs -> 1e-4 relative.
+TOL = {"f32": 1e-4, "bf16": 1e-3, "fp8": 2e-2}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -174,6 +176,9 @@ def test_score_parity(key, q, integer, rows):
 @pytest.mark.parametrize("K", [64, 512, 2048, 100000])
 @pytest.mark.parametrize("ties", [False, True])
 def test_topk_parity(K, ties):
+    """Exact for any threshold hint: zeroed workspace (everything passes the
+    filter), the hint the previous call left (fast path), and a hint above
+    every key (nothing passes: fallback)."""
     banner(f"topk K={K} ties={ties}")
     A = api()
     ctx = [131072, 70001, 4096 + 5, 64]
@@ -183,16 +188,47 @@ def test_topk_parity(K, ties):
     bt, keep = _batch(ctx, [c + 1 for c in ctx], [2] * R, rows, mb)
     Kc = min(K, 8192)
     cfg = A.config(topk=Kc, sparsity_bp=4000)
-    out = torch.full((R, rows, Kc), -9, dtype=torch.int32, device=DEV)
-    A.spin_topk(cfg, bt, zin.to(DEV), sel.to(DEV), n_sel.to(DEV), out)
-    out = out.cpu().numpy()
+    ws = torch.zeros(A.workspace_bytes(cfg, R, rows, mb), dtype=torch.uint8, device=DEV)
+    want = {}
     for r, N in enumerate(ctx):
         blocks = sel[r, :int(n_sel[r])].numpy()
         slots = O.union_slots(blocks, N)
         comp = np.searchsorted(blocks, slots // 64) * 64 + slots % 64
         for row in range(rows):
-            want = O.topk_slots(zin[r, row].numpy()[comp], slots, Kc)
-            assert np.array_equal(out[r, row], want), (r, row)
+            want[r, row] = O.topk_slots(zin[r, row].numpy()[comp], slots, Kc)
+    zd, seld, nsd = zin.to(DEV), sel.to(DEV), n_sel.to(DEV)
+    for attempt in ("zero hint", "carried hint", "carried hint again", "hint above all"):
+        if attempt == "hint above all":
+            ws[: 4 * R * rows] = 0xFF
+        out = torch.full((R, rows, Kc), -9, dtype=torch.int32, device=DEV)
+        A.spin_topk(cfg, bt, zd, seld, nsd, out, workspace=ws)
+        out = out.cpu().numpy()
+        for r in range(R):
+            for row in range(rows):
+                assert np.array_equal(out[r, row], want[r, row]), (attempt, r, row)
+
+
+def test_topk_tracks_drifting_scores():
+    """Scores that drift from call to call (as in decoding): every call exact."""
+    banner("topk drift")
+    A = api()
+    ctx = [131072, 90000]
+    R, mb, rows = 2, 2048, 1
+    sel, n_sel = G.make_selection(R, torch.tensor([O.n_blocks(c) for c in ctx]), mb, 0.6, seed=3)
+    cfg = A.config(topk=2048, sparsity_bp=4000)
+    ws = torch.zeros(A.workspace_bytes(cfg, R, rows, mb), dtype=torch.uint8, device=DEV)
+    bt, keep = _batch(ctx, [c + 1 for c in ctx], [2] * R, rows, mb)
+    base = G.make_scores((R, rows, 64 * mb), seed=77)
+    for step in range(8):
+        zin = base * (1.0 + 0.15 * step) + G.make_scores((R, rows, 64 * mb), seed=step) * 0.3
+        out = torch.full((R, rows, 2048), -9, dtype=torch.int32, device=DEV)
+        A.spin_topk(cfg, bt, zin.to(DEV), sel.to(DEV), n_sel.to(DEV), out, workspace=ws)
+        out = out.cpu().numpy()
+        for r, N in enumerate(ctx):
+            blocks = sel[r, :int(n_sel[r])].numpy()
+            slots = O.union_slots(blocks, N)
+            comp = np.searchsorted(blocks, slots // 64) * 64 + slots % 64
+            assert np.array_equal(out[r, 0], O.topk_slots(zin[r, 0].numpy()[comp], slots, 2048))
 
 
 # ---------------------------------------------------------------------------
