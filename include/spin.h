@@ -64,6 +64,7 @@ enum { SPIN_DERR_CTX = 1,   /* ctx_len < 1, > 64*max_blocks or > v_ld        */
 
 /* limits of this build */
 #define SPIN_BLOCK 64
+#define SPIN_MAX_BATCH 4096   /* requests per call */
 #define SPIN_MAX_ROWS 4
 #define SPIN_MAX_BLOCKS 8192  /* per request: up to 524,288 slots */
 #define SPIN_MAX_TOPK 8192
@@ -87,7 +88,7 @@ typedef struct spin_config {
 
 /* One decode step of one layer for a batch of requests (host struct). */
 typedef struct spin_batch {
-  int32_t batch;           /* R >= 1 requests                                      */
+  int32_t batch;           /* R requests, 0..SPIN_MAX_BATCH (0 = nothing to do)     */
   int32_t n_rows;          /* verifier queries per request, 1..SPIN_MAX_ROWS        */
   int32_t max_blocks;      /* capacity of per-request block arrays (>= ceil(N/64)) */
   int32_t n_pages;         /* pages in the key pool (page ids must be < n_pages)   */

@@ -25,6 +25,8 @@ FLAGS = [
     # no implicit multiply-add fusion: the EMA and the combine rules are
     # specified as separately rounded fp32 operations
     "-ffp-contract=off",
+    # MFMA results straight into VGPRs (no accumulator-register reads in the epilogues)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     # packed fp32 (v_pk_*_f32) stays disabled for every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,

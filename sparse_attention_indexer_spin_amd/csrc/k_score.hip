@@ -3,9 +3,9 @@
 // Sparse Attention", Sec. 2; Algorithm 1 step 6).
 //
 // Per selected 64-slot block the work is a small dense contraction
-// [64 heads x 128] x [128 x 64 slots], so it runs on the matrix cores:
-//   * fp8 keys: v_mfma_scale_f32_16x16x128_f8f6f4 with the keys fed straight
-//     from HBM as OCP E4M3.  The query of each head is scaled by a power of
+// [rows x 64 heads x 128] x [128 x 64 slots], so it runs on the matrix cores:
+//   * fp8 keys: v_mfma_scale_f32_16x16x128_f8f6f4 with the keys used as they
+//     sit in HBM (OCP E4M3).  The query of each head is scaled by a power of
 //     two and written as a sum of E4M3 terms (two reproduce a bf16 query,
 //     three are used for fp32 queries), one MFMA per term, so the keys need
 //     no conversion.  The head scale is folded into w; the per-slot key scale
@@ -13,15 +13,16 @@
 //   * bf16 keys: v_mfma_f32_16x16x32_bf16, fp32 accumulation.
 //   * fp32 keys + fp32 queries: a plain fp32 VALU kernel.
 //
-// Work split: the (request, row, selected block) items are cut into one
-// contiguous chunk per resident wave.  A wave owns a whole block (4 sub-tiles
-// of 16 slots x 64 heads): the ReLU / weight / head-sum epilogue stays in
-// registers (each lane sums 4 heads of each of the 4 head tiles), a 3-step
-// cross-lane reduce-scatter (v_permlane16/32_swap) leaves lane (n, g) with the
-// score of slot 16 g + n, and the block's 64 scores go out as one 256-byte
-// store.  Block descriptors (page, block id, row, position) are fetched 64 at
-// a time, one per lane, so the key loads never wait on a page-table lookup,
-// and the keys of block i+1 are in flight while block i is on the MFMAs.
+// MFMA kernels: a workgroup of 4 waves owns a contiguous run of
+// (request, selected block) items; wave w owns heads 16w..16w+15 of every
+// verifier row, so its query tile stays in registers and each key page is
+// read from HBM once for all rows.  A page is staged global -> VGPR ->
+// LDS (16-byte chunks XOR-swizzled by slot so the MFMA operand reads are
+// bank-conflict free), double-buffered: page i+1 is written to LDS and page
+// i+2 is in flight while page i is on the matrix cores.  Each wave reduces
+// ReLU(qk) * w over its 16 heads in registers (3-step permlane
+// reduce-scatter); the 4 head-tile partials meet in LDS and one wave writes
+// the page's 64 scores per row as one 256-byte store.
 #include "spin_dev.h"
 #include "spin_launch.h"
 
@@ -31,11 +32,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
-// 16-byte streaming load (keys are read once per step: non-temporal)
-__device__ __forceinline__ v4u ld16_nt(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-}
 
 struct ScoreParams {
   const void* q;
@@ -54,56 +50,90 @@ struct ScoreParams {
   int32_t* err;
 };
 
+// Selected blocks of request r (0 for a request with invalid bounds).
 __device__ __forceinline__ int items_of(const ScoreParams& p, int r) {
   const int N = p.ctx[r];
   if (request_error(N, p.qpos[r], p.rows, p.max_blocks, 0, 0)) return 0;
-  return clamp_nsel(p.n_sel[r], p.max_blocks) * p.rows;
+  return clamp_nsel(p.n_sel[r], p.max_blocks);
 }
 
-// This wave's item range [lo, hi).
-__device__ __forceinline__ void wave_range(const ScoreParams& p, int n_waves, int wave, int& lo,
-                                           int& hi) {
-  int T = 0;
-  for (int r = 0; r < p.R; ++r) T += items_of(p, r);
-  const int per = (T + n_waves - 1) / n_waves;
-  lo = min(T, wave * per);
-  hi = min(T, lo + per);
-}
-
-// Descriptor of item g, computed by one lane: page (0 if invalid), block id j,
-// row id (r * rows + row), position k in the request's block list, context N,
-// and a flag for an out-of-range page.
-struct Desc {
-  int page, j, rowid, k, N, bad;
+// Exclusive prefix of the per-request item counts in LDS (all requests'
+// counters loaded in parallel) plus the total.
+struct ItemTable {
+  const int* pre;  // [R + 1]
+  int total;
 };
 
-__device__ __forceinline__ Desc describe(const ScoreParams& p, int g) {
-  Desc d{0, 0, 0, 0, 0, 1};
-  int run = 0;
-  for (int r = 0; r < p.R; ++r) {
-    const int cnt = items_of(p, r);
-    if (g >= run && g < run + cnt) {
-      const int ns = cnt / p.rows, off = g - run;
-      const int row = off / ns, k = off % ns;
-      const int j = p.sel[(int64_t)r * p.max_blocks + k];
-      const int page = (j >= 0 && j < p.max_blocks) ? p.pt[(int64_t)r * p.pt_ld + j] : -1;
-      d.bad = !(page >= 0 && page < p.n_pages);
-      d.page = d.bad ? 0 : page;
-      d.j = j;
-      d.rowid = r * p.rows + row;
-      d.k = k;
-      d.N = p.ctx[r];
-    }
-    run += cnt;
+__device__ __forceinline__ ItemTable build_items(const ScoreParams& p, int* pre, int* tmp) {
+  constexpr int NT = 256;
+  const int per = (p.R + NT - 1) / NT;  // requests per thread (R <= SPIN_MAX_BATCH)
+  const int r0 = threadIdx.x * per;
+  int cnt[SPIN_MAX_BATCH / NT];
+  int mine = 0;
+#pragma unroll
+  for (int u = 0; u < SPIN_MAX_BATCH / NT; ++u) {
+    cnt[u] = (u < per && r0 + u < p.R) ? items_of(p, r0 + u) : 0;
+    mine += cnt[u];
   }
+  int total;
+  int run = block_excl_scan<NT>(mine, tmp, &total);
+#pragma unroll
+  for (int u = 0; u < SPIN_MAX_BATCH / NT; ++u)
+    if (u < per && r0 + u < p.R) { pre[r0 + u] = run; run += cnt[u]; }
+  if (threadIdx.x == 0) pre[p.R] = total;
+  __syncthreads();
+  return ItemTable{pre, total};
+}
+
+// Descriptor of item g (one lane each): page (0 if invalid), block id j,
+// request r, position k in the request's block list, context N, and a flag
+// for an out-of-range page.
+struct Desc {
+  int page, j, r, k, N, bad;
+};
+
+__device__ __forceinline__ Desc describe(const ScoreParams& p, const ItemTable& tb, int g) {
+  Desc d{0, 0, 0, 0, 0, 1};
+  if (g >= tb.total) return d;
+  int lo = 0, hi = p.R - 1;  // last r with pre[r] <= g
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tb.pre[mid] <= g) lo = mid; else hi = mid - 1;
+  }
+  const int r = lo, k = g - tb.pre[r];
+  const int j = p.sel[(int64_t)r * p.max_blocks + k];
+  const int page = (j >= 0 && j < p.max_blocks) ? p.pt[(int64_t)r * p.pt_ld + j] : -1;
+  d.bad = !(page >= 0 && page < p.n_pages);
+  d.page = d.bad ? 0 : page;
+  d.j = j;
+  d.r = r;
+  d.k = k;
+  d.N = p.ctx[r];
   return d;
 }
 
 __device__ __forceinline__ int rl(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
 __device__ __forceinline__ Desc pick(const Desc& m, int i) {
-  return Desc{rl(m.page, i), rl(m.j, i), rl(m.rowid, i), rl(m.k, i), rl(m.N, i), rl(m.bad, i)};
+  return Desc{rl(m.page, i), rl(m.j, i), rl(m.r, i), rl(m.k, i), rl(m.N, i), rl(m.bad, i)};
 }
+
+// Descriptor cursor: 64 items' descriptors per wave, refreshed as it advances.
+struct DescBatch {
+  Desc mine;
+  int base;
+  __device__ __forceinline__ void init(const ScoreParams& p, const ItemTable& tb, int g) {
+    base = g;
+    mine = describe(p, tb, g + (int)(threadIdx.x & 63));
+    // complete the descriptor loads here (once per 64 items) so later code
+    // never has to drain the vector-memory counter to read them
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+  }
+  __device__ __forceinline__ Desc get(const ScoreParams& p, const ItemTable& tb, int g) {
+    if (g - base >= 64) init(p, tb, g);
+    return pick(mine, g - base);
+  }
+};
 
 // Value of lane l ^ 16 / l ^ 32 (VALU lane swaps, no LDS traffic).
 __device__ __forceinline__ float xor16(float v) {
@@ -134,12 +164,10 @@ __device__ __forceinline__ float reduce_scatter4(const float (&p)[4]) {
   return keep + xor32(send);
 }
 
-__device__ __forceinline__ float ld_q(const void* q, int q_bf16, int64_t idx) {
-  if (q_bf16) {
-    const uint16_t b = reinterpret_cast<const uint16_t*>(q)[idx];
-    return __uint_as_float((uint32_t)b << 16);
-  }
-  return reinterpret_cast<const float*>(q)[idx];
+// ReLU of a finite float as one integer max on its bits: negative values
+// (sign bit set, so negative as int32) and -0 map to +0.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
 }
 
 // Pack 4 floats into 4 OCP E4M3 bytes (round to nearest even).
@@ -148,246 +176,514 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
 }
 
-__device__ __forceinline__ void store_block(const ScoreParams& p, const Desc& d, float zv) {
-  const int lane = threadIdx.x & 63;
-  const int slot = d.j * 64 + lane;
-  zv = (slot < d.N && !d.bad) ? zv + 0.0f : 0.0f;
-  p.z[(int64_t)d.rowid * p.z_ld + (int64_t)d.k * 64 + lane] = zv;
-  if (d.bad && lane == 0) raise_error(p.err, SPIN_DERR_PAGE);
+// 32 query values of lane (m, g) of head `head` (row base qrow): dims
+// [16g, 16g+16) and [64+16g, 64+16g+16).
+__device__ __forceinline__ void load_q32(const void* q, int q_bf16, int64_t hb, int g,
+                                         float (&x)[32]) {
+  if (q_bf16) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(q) + hb;
+    const v4u rr[4] = {*reinterpret_cast<const v4u*>(qp + 16 * g),
+                       *reinterpret_cast<const v4u*>(qp + 16 * g + 8),
+                       *reinterpret_cast<const v4u*>(qp + 64 + 16 * g),
+                       *reinterpret_cast<const v4u*>(qp + 64 + 16 * g + 8)};
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        x[8 * v + 2 * c] = __uint_as_float(rr[v][c] << 16);
+        x[8 * v + 2 * c + 1] = __uint_as_float(rr[v][c] & 0xFFFF0000u);
+      }
+  } else {
+    const float* qp = reinterpret_cast<const float*>(q) + hb;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float4 a = *reinterpret_cast<const float4*>(qp + 16 * g + 4 * v);
+      const float4 b = *reinterpret_cast<const float4*>(qp + 64 + 16 * g + 4 * v);
+      x[4 * v] = a.x; x[4 * v + 1] = a.y; x[4 * v + 2] = a.z; x[4 * v + 3] = a.w;
+      x[16 + 4 * v] = b.x; x[16 + 4 * v + 1] = b.y; x[16 + 4 * v + 2] = b.z;
+      x[16 + 4 * v + 3] = b.w;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// fp8 keys.  Lane (n = lane % 16, g = lane / 16).  MFMA B operand: 32 key
-// bytes of slot 16 s + n, dims [16g, 16g+16) and [64+16g, 64+16g+16); the A
-// operand holds the same dims of head 16 t + n, so C = q . k^T over all 128
-// dims.  C lane layout: rows (heads) 4g + i, column (slot) n.
+// Key pages: geometry, staging and the swizzled LDS layout.
+// KT = 0: fp8 rows of 128 B (8 chunks); KT = 1: bf16 rows of 256 B (16 chunks).
+// Chunk c of slot s lives at LDS byte s * row + 16 * (c ^ (s & 7)), so the 8
+// lanes of an MFMA operand read (8 slots, same logical chunk) hit 8
+// different bank groups.
 // ---------------------------------------------------------------------------
-template <int NS>
-struct QFp8 {
-  v8i part[NS][4];
-  float wq[4][4];
+template <int KT>
+struct KGeo {
+  static constexpr int kRow = KT == 0 ? 128 : 256;
+  static constexpr int kBytes = 64 * kRow;
+  static constexpr int kChunksPerRow = kRow / 16;
+  static constexpr int kPerThread = kBytes / 16 / 256;
 };
 
-template <int NS>
-__device__ __forceinline__ void load_q_fp8(const ScoreParams& p, int q_bf16, int rowid,
-                                           QFp8<NS>& Q) {
-  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
-  const int64_t qbase = (int64_t)rowid * 64;
-  const float* wr = p.w + qbase;
+__device__ __forceinline__ int swz(int slot, int chunk, int row_bytes) {
+  return slot * row_bytes + 16 * (chunk ^ (slot & 7));
+}
+
+#define SPIN_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
+
+// Direct global -> LDS copy of one key page (and its fp8 scales) into a ring
+// slot.  Wave w writes LDS bytes [w * kBytes/4, (w+1) * kBytes/4) in 1 KB
+// instructions (lane l -> 16 l within each); each lane fetches the global
+// chunk that the swizzle places there, so every instruction still reads one
+// contiguous 1 KB run of the page.  Returns nothing; completion is tracked
+// with vmcnt by the caller (kDmaOps[w] instructions per page for wave w).
+template <int KT>
+struct Dma {
+  using G = KGeo<KT>;
+  static constexpr int kPerWave = G::kBytes / 4 / 1024;  // 1 KB instructions per wave
+  __device__ static __forceinline__ int ops(int wave) { return kPerWave + (KT == 0 && wave == 0); }
+  __device__ static __forceinline__ void issue(const ScoreParams& p, int page, uint8_t* kslot,
+                                               float* sslot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(p.kp) + (int64_t)page * G::kBytes;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int64_t hb = (qbase + 16 * t + m) * 128;
-    float x[32];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      x[u] = ld_q(p.q, q_bf16, hb + 16 * g + u);
-      x[16 + u] = ld_q(p.q, q_bf16, hb + 64 + 16 * g + u);
+    for (int u = 0; u < kPerWave; ++u) {
+      const int lds_off = (wave * kPerWave + u) * 1024;      // this instruction's 1 KB
+      const int pos = lds_off + 16 * lane;                    // LDS byte this lane fills
+      const int slot = pos / G::kRow, cpos = (pos % G::kRow) / 16;
+      const int c = cpos ^ (slot & 7);                        // global chunk stored there
+      __builtin_amdgcn_global_load_lds(base + slot * G::kRow + 16 * c, SPIN_LDS(kslot + lds_off),
+                                       16, 0, 0);
     }
-    float amax = 0.0f;
+    if (KT == 0 && wave == 0)
+      __builtin_amdgcn_global_load_lds(p.ks + (int64_t)page * 64 + lane, SPIN_LDS(sslot), 4, 0, 0);
+  }
+};
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left at their maxima), n <= 63.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most `later` pages' DMA (issued after the page needed now)
+// are outstanding for this wave.
+template <int KT, int NB>
+__device__ __forceinline__ void wait_pages(int later) {
+  const int wave = threadIdx.x >> 6;
+  const bool w0 = KT == 0 && wave == 0;  // wave 0 also copies the scales
+  constexpr int P = Dma<KT>::kPerWave;
+#define SPIN_WAIT_CASE(k)                                 \
+  case k:                                                 \
+    if (w0) wait_vm<(P + 1) * (k)>(); else wait_vm<P * (k)>(); \
+    break;
+  switch (later < NB - 1 ? later : NB - 1) {
+    SPIN_WAIT_CASE(0) SPIN_WAIT_CASE(1) SPIN_WAIT_CASE(2) SPIN_WAIT_CASE(3)
+    SPIN_WAIT_CASE(4) SPIN_WAIT_CASE(5) SPIN_WAIT_CASE(6) SPIN_WAIT_CASE(7)
+    default: wait_vm<0>();
+  }
+#undef SPIN_WAIT_CASE
+}
+
+// ---------------------------------------------------------------------------
+// Query tiles in registers: wave w holds heads 16w .. 16w+15 of NR rows.
+// ---------------------------------------------------------------------------
+template <int KT, int NS, int NR>
+struct QTile;
+
+// fp8 keys: NS E4M3 terms per value, MFMA A-operand layout (lane (m, g):
+// head 16w + m, the same dims the key operand holds).
+template <int NS, int NR>
+struct QTile<0, NS, NR> {
+  v8i part[NR][NS];
+  float wq[NR][4];  // weights of output heads 16w + 4g + i, over 2^e_head
+
+  __device__ __forceinline__ void load(const ScoreParams& p, int q_bf16, int r) {
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int u = 0; u < 32; ++u) amax = fmaxf(amax, fabsf(x[u]));
-    amax = fmaxf(amax, xor16(amax));
-    amax = fmaxf(amax, xor32(amax));
-    // 2^e * amax lies in [128, 256): inside the E4M3 range (max 448)
-    const int e = amax > 0.0f ? 7 - ilogbf(amax) : 0;
-    int pw[NS][8];
+    for (int row = 0; row < NR; ++row) {
+      if (row >= p.rows) break;
+      const int64_t qbase = ((int64_t)r * p.rows + row) * 64;
+      float x[32];
+      load_q32(p.q, q_bf16, (qbase + 16 * w + m) * 128, g, x);
+      float amax = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      float rem[4];
+      for (int u = 0; u < 32; ++u) amax = fmaxf(amax, fabsf(x[u]));
+      amax = fmaxf(amax, xor16(amax));
+      amax = fmaxf(amax, xor32(amax));
+      // 2^e * amax lies in [128, 256): inside the E4M3 range (max 448)
+      const int e = amax > 0.0f ? 7 - ilogbf(amax) : 0;
+      int pw[NS][8];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) rem[v] = ldexpf(x[4 * u + v], e);
+      for (int u = 0; u < 8; ++u) {
+        float rem[4];
 #pragma unroll
-      for (int sp = 0; sp < NS; ++sp) {
-        const int packed = pack_fp8x4(rem[0], rem[1], rem[2], rem[3]);
-        pw[sp][u] = packed;
-        if (sp + 1 < NS) {
-          rem[0] -= __builtin_amdgcn_cvt_f32_fp8(packed, 0);
-          rem[1] -= __builtin_amdgcn_cvt_f32_fp8(packed, 1);
-          rem[2] -= __builtin_amdgcn_cvt_f32_fp8(packed, 2);
-          rem[3] -= __builtin_amdgcn_cvt_f32_fp8(packed, 3);
+        for (int v = 0; v < 4; ++v) rem[v] = ldexpf(x[4 * u + v], e);
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) {
+          const int packed = pack_fp8x4(rem[0], rem[1], rem[2], rem[3]);
+          pw[sp][u] = packed;
+          if (sp + 1 < NS) {
+            rem[0] -= __builtin_amdgcn_cvt_f32_fp8(packed, 0);
+            rem[1] -= __builtin_amdgcn_cvt_f32_fp8(packed, 1);
+            rem[2] -= __builtin_amdgcn_cvt_f32_fp8(packed, 2);
+            rem[3] -= __builtin_amdgcn_cvt_f32_fp8(packed, 3);
+          }
         }
       }
-    }
-#pragma unroll
-    for (int sp = 0; sp < NS; ++sp)
-      Q.part[sp][t] = v8i{pw[sp][0], pw[sp][1], pw[sp][2], pw[sp][3],
-                          pw[sp][4], pw[sp][5], pw[sp][6], pw[sp][7]};
-    // weights of the output heads 16t + 4g + i, divided by their head scale
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ei = __shfl(e, 4 * g + i, 64);
-      Q.wq[t][i] = ldexpf(wr[16 * t + 4 * g + i], -ei);
-    }
-  }
-}
-
-struct KTileFp8 {
-  v4u a[4], b[4];
-  float sc[4];
-};
-
-__device__ __forceinline__ void issue_fp8(const ScoreParams& p, int page, KTileFp8& t) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.kp) + (int64_t)page * (64 * 128);
-  const float* sb = p.ks + (int64_t)page * 64;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint8_t* rowp = kb + (16 * s + n) * 128;
-    t.a[s] = ld16_nt(rowp + 16 * g);
-    t.b[s] = ld16_nt(rowp + 64 + 16 * g);
-    t.sc[s] = sb[16 * s + n];
-  }
-}
-
-template <int NS>
-__device__ __forceinline__ float consume_fp8(const QFp8<NS>& Q, const KTileFp8& t) {
-  const int g = (threadIdx.x & 63) >> 4;
-  float part[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const v8i kf = v8i{(int)t.a[s].x, (int)t.a[s].y, (int)t.a[s].z, (int)t.a[s].w,
-                       (int)t.b[s].x, (int)t.b[s].y, (int)t.b[s].z, (int)t.b[s].w};
-    float acc_sum = 0.0f;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int sp = 0; sp < NS; ++sp)
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.part[sp][tt], kf, acc, 0, 0, 0,
-                                                               127, 0, 127);
+        part[row][sp] = v8i{pw[sp][0], pw[sp][1], pw[sp][2], pw[sp][3],
+                            pw[sp][4], pw[sp][5], pw[sp][6], pw[sp][7]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc_sum = fmaf(Q.wq[tt][i], fmaxf(acc[i], 0.0f), acc_sum);
+      for (int i = 0; i < 4; ++i) {
+        const int ei = __shfl(e, 4 * g + i, 64);
+        wq[row][i] = ldexpf(p.w[qbase + 16 * w + 4 * g + i], -ei);
+      }
     }
-    part[s] = acc_sum;
   }
-  const float total = reduce_scatter4(part);
-  const float sc = g == 0 ? t.sc[0] : g == 1 ? t.sc[1] : g == 2 ? t.sc[2] : t.sc[3];
-  return total * sc;
-}
 
-template <int Q_BF16>
-__global__ __launch_bounds__(256) void k_score_fp8(ScoreParams p) {
-  constexpr int NS = Q_BF16 ? 2 : 3;
-  const int lane = threadIdx.x & 63;
-  int lo, hi;
-  wave_range(p, gridDim.x * 4, blockIdx.x * 4 + (threadIdx.x >> 6), lo, hi);
-  if (lo >= hi) return;
-  QFp8<NS> Q;
-  int q_rowid = -1;
-  KTileFp8 t0, t1;
-  Desc mine = describe(p, lo + lane);  // descriptors of items base .. base+63
-  int base = lo;
-  issue_fp8(p, rl(mine.page, 0), t0);
-  for (int it = lo; it < hi; it += 2) {
-    if (it - base >= 64) { base = it; mine = describe(p, it + lane); }
-    const Desc d0 = pick(mine, it - base);
-    const bool has1 = it + 1 < hi;
-    Desc d1 = d0;
-    if (has1) {
-      if (it + 1 - base >= 64) { base = it + 1; mine = describe(p, it + 1 + lane); }
-      d1 = pick(mine, it + 1 - base);
-      issue_fp8(p, d1.page, t1);
+  // partial[row][s]: this lane's ReLU-weighted sum over its 4 heads, sub-tile s
+  __device__ __forceinline__ void mul(const uint8_t* kbuf, int rows,
+                                      float (&partial)[NR][4]) const {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int slot = 16 * s + n;
+      const v4u a = *reinterpret_cast<const v4u*>(kbuf + swz(slot, g, 128));
+      const v4u b = *reinterpret_cast<const v4u*>(kbuf + swz(slot, 4 + g, 128));
+      const v8i kf = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w,
+                         (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+#pragma unroll
+      for (int row = 0; row < NR; ++row) {
+        if (row >= rows) break;
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp)
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(part[row][sp], kf, acc, 0, 0, 0,
+                                                                 127, 0, 127);
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t = fmaf(wq[row][i], relu(acc[i]), t);
+        partial[row][s] = t;
+      }
     }
-    if (d0.rowid != q_rowid) { load_q_fp8<NS>(p, Q_BF16, d0.rowid, Q); q_rowid = d0.rowid; }
-    store_block(p, d0, consume_fp8<NS>(Q, t0));
-    if (!has1) break;
-    if (it + 2 < hi) {
-      if (it + 2 - base >= 64) { base = it + 2; mine = describe(p, it + 2 + lane); }
-      issue_fp8(p, rl(mine.page, it + 2 - base), t0);
-    }
-    if (d1.rowid != q_rowid) { load_q_fp8<NS>(p, Q_BF16, d1.rowid, Q); q_rowid = d1.rowid; }
-    store_block(p, d1, consume_fp8<NS>(Q, t1));
   }
-}
-
-// ---------------------------------------------------------------------------
-// bf16 keys.  MFMA 16x16x32: lane (n, g) holds 8 bf16 of slot n per k-step;
-// k-step ks covers dims [32 ks + 8 g, +8), so each load instruction reads 64
-// contiguous bytes of 16 key rows.
-// ---------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ v8bf as_v8bf(T x) {
-  return __builtin_bit_cast(v8bf, x);
-}
-
-struct QBf16 {
-  uint4 qa[4][4];
-  float wq[4][4];
 };
 
-__device__ __forceinline__ void load_q_bf16(const ScoreParams& p, int rowid, QBf16& Q) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
-  const int64_t qbase = (int64_t)rowid * 64;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      Q.qa[t][ks] =
-          *reinterpret_cast<const uint4*>(qp + (qbase + 16 * t + n) * 128 + 32 * ks + 8 * g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Q.wq[t][i] = p.w[qbase + 16 * t + 4 * g + i];
-  }
-}
+// bf16 keys: MFMA 16x16x32, lane (n, g): head 16w + n, k-step ks covering
+// dims [32 ks + 8 g, +8).
+template <int NS, int NR>
+struct QTile<1, NS, NR> {
+  v4u qa[NR][4];
+  float wq[NR][4];
 
-// Half a block (2 sub-tiles of 16 slots) per tile keeps the double buffer small.
-struct KTileBf16 {
-  v4u b[2][4];
-};
-
-__device__ __forceinline__ void issue_bf16(const ScoreParams& p, int page, int half,
-                                           KTileBf16& t) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.kp) + (int64_t)page * (64 * 128);
+  __device__ __forceinline__ void load(const ScoreParams& p, int, int r) {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, w = threadIdx.x >> 6;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      t.b[s][ks] = ld16_nt(kb + (16 * (2 * half + s) + n) * 128 + 32 * ks + 8 * g);
-}
-
-__device__ __forceinline__ void consume_bf16(const QBf16& Q, const KTileBf16& t, float* part) {
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    float acc_sum = 0.0f;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int row = 0; row < NR; ++row) {
+      if (row >= p.rows) break;
+      const int64_t qbase = ((int64_t)r * p.rows + row) * 64;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(Q.qa[tt][ks]), as_v8bf(t.b[s][ks]),
-                                                      acc, 0, 0, 0);
+        qa[row][ks] =
+            *reinterpret_cast<const v4u*>(qp + (qbase + 16 * w + n) * 128 + 32 * ks + 8 * g);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc_sum = fmaf(Q.wq[tt][i], fmaxf(acc[i], 0.0f), acc_sum);
+      for (int i = 0; i < 4; ++i) wq[row][i] = p.w[qbase + 16 * w + 4 * g + i];
     }
-    part[s] = acc_sum;
+  }
+
+  __device__ __forceinline__ void mul(const uint8_t* kbuf, int rows,
+                                      float (&partial)[NR][4]) const {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int slot = 16 * s + n;
+      v4u kb[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kb[ks] = *reinterpret_cast<const v4u*>(kbuf + swz(slot, 4 * ks + g, 256));
+#pragma unroll
+      for (int row = 0; row < NR; ++row) {
+        if (row >= rows) break;
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, qa[row][ks]),
+                                                        __builtin_bit_cast(v8bf, kb[ks]), acc,
+                                                        0, 0, 0);
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t = fmaf(wq[row][i], relu(acc[i]), t);
+        partial[row][s] = t;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// The MFMA score kernel.  NB = ring slots (NB - 1 pages in flight).
+// ---------------------------------------------------------------------------
+template <int KT, int NR, int NB>
+struct ScoreShared {
+  uint8_t kbuf[NB][KGeo<KT>::kBytes] __attribute__((aligned(16)));
+  float sbuf[NB][64];
+  float red[NR][4][64];
+  int tmp[32];
+};
+
+// Occupancy target: 4 waves per SIMD for one verifier row, fewer for more
+// rows (their query tiles need more registers).
+template <int NR>
+struct WavesPerEU {
+  static constexpr int value = NR == 1 ? 4 : (NR == 2 ? 3 : 2);
+};
+
+template <int KT, int NS, int NR, int QB, int NB>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(WavesPerEU<NR>::value, 8))) void k_score_mfma(ScoreParams p) {
+  __shared__ ScoreShared<KT, NR, NB> sm;
+  extern __shared__ int pre_dyn[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const ItemTable tb = build_items(p, pre_dyn, sm.tmp);
+  const int per = (tb.total + gridDim.x - 1) / gridDim.x;
+  const int lo = min(tb.total, (int)blockIdx.x * per), hi = min(tb.total, lo + per);
+  if (lo >= hi) return;
+  QTile<KT, NS, NR> Q;
+  int q_req = -1;
+  DescBatch db, dd;  // cursors of the scoring stream and of the copy stream
+  db.init(p, tb, lo);
+  dd.init(p, tb, lo);
+  // prologue: NB - 1 pages in flight
+  for (int i = 0; i < NB - 1 && lo + i < hi; ++i)
+    Dma<KT>::issue(p, dd.get(p, tb, lo + i).page, sm.kbuf[i], sm.sbuf[i]);
+  for (int it = lo; it < hi; ++it) {
+    const int slot = (it - lo) % NB;
+    const int ahead = it + NB - 1;
+    if (ahead < hi) {
+      const int as = (ahead - lo) % NB;
+      Dma<KT>::issue(p, dd.get(p, tb, ahead).page, sm.kbuf[as], sm.sbuf[as]);
+    }
+    const Desc d = db.get(p, tb, it);
+    if (d.r != q_req) { Q.load(p, QB, d.r); q_req = d.r; }
+    wait_pages<KT, NB>(min(NB - 1, hi - 1 - it));
+    __builtin_amdgcn_s_barrier();  // page `it` is in ring slot `slot` for every wave
+    float partial[NR][4];
+    Q.mul(sm.kbuf[slot], p.rows, partial);
+    const float sc = KT == 0 ? sm.sbuf[slot][lane] : 1.0f;
+#pragma unroll
+    for (int row = 0; row < NR; ++row) {
+      if (row >= p.rows) break;
+      sm.red[row][wave][lane] = reduce_scatter4(partial[row]);
+    }
+    __syncthreads();  // partials in `red`; ring slot `slot` may be refilled
+    if (wave == (it & 3)) {
+      const int s0 = d.j * 64 + lane;
+      const bool ok = s0 < d.N && !d.bad;
+#pragma unroll
+      for (int row = 0; row < NR; ++row) {
+        if (row >= p.rows) break;
+        const float zs = ((sm.red[row][0][lane] + sm.red[row][1][lane]) + sm.red[row][2][lane]) +
+                         sm.red[row][3][lane];
+        const float zv = ok ? (KT == 0 ? zs * sc : zs) + 0.0f : 0.0f;
+        p.z[((int64_t)d.r * p.rows + row) * p.z_ld + (int64_t)d.k * 64 + lane] = zv;
+      }
+      if (d.bad && lane == 0) raise_error(p.err, SPIN_DERR_PAGE);
+    }
   }
 }
 
-__global__ __launch_bounds__(256) void k_score_bf16(ScoreParams p) {
-  const int lane = threadIdx.x & 63;
-  int lo, hi;
-  wave_range(p, gridDim.x * 4, blockIdx.x * 4 + (threadIdx.x >> 6), lo, hi);
-  if (lo >= hi) return;
-  QBf16 Q;
-  int q_rowid = -1;
-  KTileBf16 t0, t1;
-  Desc mine = describe(p, lo + lane);
-  int base = lo;
-  issue_bf16(p, rl(mine.page, 0), 0, t0);
-  for (int it = lo; it < hi; ++it) {
-    if (it - base >= 64) { base = it; mine = describe(p, it + lane); }
-    const Desc d = pick(mine, it - base);
-    float part[4];
-    issue_bf16(p, d.page, 1, t1);  // second half of this block
-    if (d.rowid != q_rowid) { load_q_bf16(p, d.rowid, Q); q_rowid = d.rowid; }
-    consume_bf16(Q, t0, part);
-    if (it + 1 < hi) {  // first half of the next block
-      if (it + 1 - base >= 64) { base = it + 1; mine = describe(p, it + 1 + lane); }
-      issue_bf16(p, rl(mine.page, it + 1 - base), 0, t0);
+// ---------------------------------------------------------------------------
+// Single-row MFMA kernel: wave w owns slots 16w .. 16w+15 of every page and
+// all 64 heads (the whole query tile in registers), so the head sum finishes
+// inside the wave and a page needs one barrier (ring-slot hand-over) only.
+// ---------------------------------------------------------------------------
+template <int KT, int NS>
+struct QFull;
+
+template <int NS>
+struct QFull<0, NS> {  // fp8 keys: NS E4M3 terms per query value
+  v8i part[NS][4];
+  float wq[4][4];
+
+  __device__ __forceinline__ void load(const ScoreParams& p, int q_bf16, int rowid) {
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    const int64_t qbase = (int64_t)rowid * 64;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float x[32];
+      load_q32(p.q, q_bf16, (qbase + 16 * t + m) * 128, g, x);
+      float amax = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) amax = fmaxf(amax, fabsf(x[u]));
+      amax = fmaxf(amax, xor16(amax));
+      amax = fmaxf(amax, xor32(amax));
+      const int e = amax > 0.0f ? 7 - ilogbf(amax) : 0;
+      int pw[NS][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float rem[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) rem[v] = ldexpf(x[4 * u + v], e);
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) {
+          const int packed = pack_fp8x4(rem[0], rem[1], rem[2], rem[3]);
+          pw[sp][u] = packed;
+          if (sp + 1 < NS) {
+            rem[0] -= __builtin_amdgcn_cvt_f32_fp8(packed, 0);
+            rem[1] -= __builtin_amdgcn_cvt_f32_fp8(packed, 1);
+            rem[2] -= __builtin_amdgcn_cvt_f32_fp8(packed, 2);
+            rem[3] -= __builtin_amdgcn_cvt_f32_fp8(packed, 3);
+          }
+        }
+      }
+#pragma unroll
+      for (int sp = 0; sp < NS; ++sp)
+        part[sp][t] = v8i{pw[sp][0], pw[sp][1], pw[sp][2], pw[sp][3],
+                          pw[sp][4], pw[sp][5], pw[sp][6], pw[sp][7]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ei = __shfl(e, 4 * g + i, 64);
+        wq[t][i] = ldexpf(p.w[qbase + 16 * t + 4 * g + i], -ei);
+      }
     }
-    consume_bf16(Q, t1, part + 2);
-    store_block(p, d, reduce_scatter4(part));
+  }
+
+  // this lane's ReLU-weighted sum over its heads for slot `slot` of the page
+  __device__ __forceinline__ float mul(const uint8_t* kbuf, int slot) const {
+    const int g = (threadIdx.x & 63) >> 4;
+    const v4u a = *reinterpret_cast<const v4u*>(kbuf + swz(slot, g, 128));
+    const v4u b = *reinterpret_cast<const v4u*>(kbuf + swz(slot, 4 + g, 128));
+    const v8i kf = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    v4f acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(part[sp][t], kf, acc[t], 0, 0, 0,
+                                                                  127, 0, 127);
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s = fmaf(wq[t][i], relu(acc[t][i]), s);
+    return s;
+  }
+};
+
+template <int NS>
+struct QFull<1, NS> {  // bf16 keys
+  v4u qa[4][4];
+  float wq[4][4];
+
+  __device__ __forceinline__ void load(const ScoreParams& p, int, int rowid) {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
+    const int64_t qbase = (int64_t)rowid * 64;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qa[t][ks] = *reinterpret_cast<const v4u*>(qp + (qbase + 16 * t + n) * 128 + 32 * ks + 8 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wq[t][i] = p.w[qbase + 16 * t + 4 * g + i];
+    }
+  }
+
+  __device__ __forceinline__ float mul(const uint8_t* kbuf, int slot) const {
+    const int g = (threadIdx.x & 63) >> 4;
+    v4u kb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kb[ks] = *reinterpret_cast<const v4u*>(kbuf + swz(slot, 4 * ks + g, 256));
+    v4f acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, qa[t][ks]),
+                                                         __builtin_bit_cast(v8bf, kb[ks]), acc[t],
+                                                         0, 0, 0);
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s = fmaf(wq[t][i], relu(acc[t][i]), s);
+    return s;
+  }
+};
+
+template <int KT, int NB>
+struct SlotShared {
+  uint8_t kbuf[NB][KGeo<KT>::kBytes] __attribute__((aligned(16)));
+  float sbuf[NB][64];
+  int tmp[32];
+};
+
+// G pages per iteration: one barrier, one descriptor step and one wait per
+// group, and G x 8 independent MFMAs per wave between barriers.  The ring
+// holds NB = G * D pages: one group being scored, D - 1 groups in flight.
+template <int KT, int NS, int QB, int G, int D>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(3, 8))) void k_score_slots(ScoreParams p) {
+  constexpr int NB = G * D;
+  __shared__ SlotShared<KT, NB> sm;
+  extern __shared__ int pre_dyn[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
+  const ItemTable tb = build_items(p, pre_dyn, sm.tmp);
+  // whole groups per workgroup (the last group of the grid may be partial)
+  const int n_groups = (tb.total + G - 1) / G;
+  const int per = (n_groups + gridDim.x - 1) / gridDim.x;
+  const int lo = min(tb.total, (int)blockIdx.x * per * G), hi = min(tb.total, lo + per * G);
+  if (lo >= hi) return;
+  QFull<KT, NS> Q;
+  int q_req = -1;
+  DescBatch db, dd;  // cursors of the scoring stream and of the copy stream
+  db.init(p, tb, lo);
+  dd.init(p, tb, lo);
+  for (int i = 0; i < (D - 1) * G && lo + i < hi; ++i)
+    Dma<KT>::issue(p, dd.get(p, tb, lo + i).page, sm.kbuf[i], sm.sbuf[i]);
+  const int my_slot = 16 * wave + (lane & 15);  // page slot this lane scores
+  int ring = 0;                                 // ring slot of group `it`
+  for (int it = lo; it < hi; it += G) {
+    const int cnt = min(G, hi - it);
+    Desc d[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) d[u] = db.get(p, tb, min(it + u, hi - 1));
+    const int issued_end = min(hi, it + (D - 1) * G);   // pages [it, issued_end) in flight
+    wait_pages<KT, NB>(max(0, issued_end - (it + cnt)));
+    __builtin_amdgcn_s_barrier();  // group visible; the previous group is no longer read
+    // refill: the group D - 1 ahead goes where the previous group was
+    const int ahead = it + (D - 1) * G;
+    const int aring = (ring + (D - 1) * G) % NB;
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      if (ahead + u < hi)
+        Dma<KT>::issue(p, dd.get(p, tb, ahead + u).page, sm.kbuf[(aring + u) % NB],
+                       sm.sbuf[(aring + u) % NB]);
+    float sv[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      if (u >= cnt) { sv[u] = 0.0f; continue; }
+      if (d[u].r != q_req) { Q.load(p, QB, d[u].r); q_req = d[u].r; }  // rows == 1
+      sv[u] = Q.mul(sm.kbuf[ring + u], my_slot);
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      if (u >= cnt) break;
+      float s = sv[u];
+      s += xor16(s);
+      s += xor32(s);
+      const float sc = KT == 0 ? sm.sbuf[ring + u][my_slot] : 1.0f;
+      if (g == 0) {
+        const int gslot = d[u].j * 64 + my_slot;
+        const float zv = (gslot < d[u].N && !d[u].bad) ? (KT == 0 ? s * sc : s) + 0.0f : 0.0f;
+        p.z[(int64_t)d[u].r * p.z_ld + (int64_t)d[u].k * 64 + my_slot] = zv;
+      }
+      if (d[u].bad && lane == 0 && wave == 0) raise_error(p.err, SPIN_DERR_PAGE);
+    }
+    ring = (ring + G) % NB;
   }
 }
 
@@ -437,6 +733,31 @@ __global__ __launch_bounds__(64) void k_score_f32(ScoreParams p) {
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
+template <int KT, int NS, int NR, int QB>
+static void launch_mfma(const ScoreParams& p, hipStream_t st) {
+  constexpr int NB = KT == 0 ? 6 : 4;
+  const auto kern = k_score_mfma<KT, NS, NR, QB, NB>;
+  const size_t dyn = sizeof(int) * (p.R + 1);
+  const int g = min(resident_workgroups((const void*)kern, 256, dyn), p.R * p.max_blocks);
+  hipLaunchKernelGGL(kern, dim3(g), dim3(256), dyn, st, p);
+}
+
+template <int KT, int NS, int QB>
+static void launch_slots(const ScoreParams& p, hipStream_t st) {
+  constexpr int G = 2, D = KT == 0 ? 3 : 2;
+  const auto kern = k_score_slots<KT, NS, QB, G, D>;
+  const size_t dyn = sizeof(int) * (p.R + 1);
+  const int g = min(resident_workgroups((const void*)kern, 256, dyn), p.R * p.max_blocks);
+  hipLaunchKernelGGL(kern, dim3(g), dim3(256), dyn, st, p);
+}
+
+template <int KT, int NS, int QB>
+static void launch_rows(const ScoreParams& p, hipStream_t st) {
+  if (p.rows <= 1) launch_slots<KT, NS, QB>(p, st);
+  else if (p.rows <= 2) launch_mfma<KT, NS, 2, QB>(p, st);
+  else launch_mfma<KT, NS, 4, QB>(p, st);
+}
+
 hipError_t launch_score(const spin_config& c, const spin_batch& b, const void* q, const float* w,
                         const void* kp, const float* ks, const int32_t* pt, int64_t pt_ld,
                         const int32_t* sel, const int32_t* n_sel, float* z, int64_t z_ld,
@@ -444,16 +765,10 @@ hipError_t launch_score(const spin_config& c, const spin_batch& b, const void* q
   ScoreParams p{q, w, kp, ks, pt, pt_ld, sel, n_sel, b.ctx_len, b.q_pos, z, z_ld,
                 b.batch, b.n_rows, b.max_blocks, b.n_pages, b.err};
   if (c.key_dtype == SPIN_FP8_E4M3) {
-    if (c.q_dtype == SPIN_BF16) {
-      const int g = resident_workgroups((const void*)k_score_fp8<1>, 256);
-      hipLaunchKernelGGL(k_score_fp8<1>, dim3(g), dim3(256), 0, st, p);
-    } else {
-      const int g = resident_workgroups((const void*)k_score_fp8<0>, 256);
-      hipLaunchKernelGGL(k_score_fp8<0>, dim3(g), dim3(256), 0, st, p);
-    }
+    if (c.q_dtype == SPIN_BF16) launch_rows<0, 2, 1>(p, st);
+    else launch_rows<0, 3, 0>(p, st);
   } else if (c.key_dtype == SPIN_BF16) {
-    const int g = resident_workgroups((const void*)k_score_bf16, 256);
-    hipLaunchKernelGGL(k_score_bf16, dim3(g), dim3(256), 0, st, p);
+    launch_rows<1, 1, 1>(p, st);
   } else {
     hipLaunchKernelGGL(k_score_f32, dim3(b.max_blocks, b.n_rows, b.batch), dim3(64), 0, st, p);
   }

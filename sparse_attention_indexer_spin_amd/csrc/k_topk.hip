@@ -282,11 +282,15 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(
     fallback_row(R, K, orow, ws.hint + rowid, hist, sh, tmpu);
     return;
   }
-  // gather the kept keys (ascending slot order) into LDS
+  // gather the kept keys (ascending slot order) into LDS, all loads in flight
   const uint2* cand = ws.cand + (int64_t)rowid * ws.n_cap;
-  for (int i = 0; i < nch; ++i) {
-    const int o = off[i], cnt = off[i + 1] - o;
-    for (int e = threadIdx.x; e < cnt; e += kSelThreads) lkey[o + e] = cand[(int64_t)i * kChunk + e].x;
+  for (int p = threadIdx.x; p < c_tot; p += kSelThreads) {
+    int lo = 0, hi = nch - 1;  // chunk holding kept candidate p
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    lkey[p] = cand[(int64_t)lo * kChunk + (p - off[lo])].x;
   }
   __syncthreads();
   uint32_t key[8];

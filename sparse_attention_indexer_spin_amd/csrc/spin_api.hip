@@ -55,7 +55,8 @@ spin_status check_config(const char* fn, const spin_config* c) {
 
 spin_status check_batch(const char* fn, const spin_batch* b) {
   if (!b) return fail(SPIN_E_NULL, "%s: batch is NULL", fn);
-  if (b->batch < 0) return fail(SPIN_E_SHAPE, "%s: batch %d < 0", fn, b->batch);
+  if (b->batch < 0 || b->batch > SPIN_MAX_BATCH)
+    return fail(SPIN_E_SHAPE, "%s: batch %d outside [0, %d]", fn, b->batch, SPIN_MAX_BATCH);
   if (b->n_rows < 1 || b->n_rows > SPIN_MAX_ROWS)
     return fail(SPIN_E_SHAPE, "%s: n_rows %d outside [1, %d]", fn, b->n_rows, SPIN_MAX_ROWS);
   if (b->max_blocks < 1 || b->max_blocks > SPIN_MAX_BLOCKS)
@@ -97,20 +98,20 @@ spin_status check_z(const char* fn, const spin_batch* b, const float* z, int64_t
 
 namespace spin {
 
-int resident_workgroups(const void* kernel, int threads) {
+int resident_workgroups(const void* kernel, int threads, size_t dyn_lds) {
   static std::mutex mu;
-  static std::map<std::pair<int, const void*>, int> cache;
+  static std::map<std::pair<std::pair<int, const void*>, size_t>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
   std::lock_guard<std::mutex> lock(mu);
-  auto key = std::make_pair(dev, kernel);
+  auto key = std::make_pair(std::make_pair(dev, kernel), dyn_lds);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus < 1)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, dyn_lds) != hipSuccess ||
       per < 1)
     per = 1;
   const int g = per * cus;
