@@ -8,9 +8,13 @@ path: predict -> select -> sparse indexer score -> top-K -> EMA -> advance,
 each launched through the C ABI on the current stream, inputs resident in HBM.
 
 Prints one JSON line.  `value` = indexer keys scored per second of whole-step
-time; `roofline` is the score kernel's algorithmic HBM bytes / its mean launch
-time (HIP events on its stream) against 8 TB/s; `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+time (one spin_step call per step).  `roofline` is the score kernel's
+algorithmic HBM bytes per launch / its mean launch duration (HIP events around
+back-to-back launches on the step's stream, on the last timed step's
+selection) against 8 TB/s, with `traffic` taken from the committed
+FETCH_SIZE/WRITE_SIZE summary when it was measured on the current kernel
+source.  `cpu_baseline` times the CPU oracle on whole requests of the same
+workload for about 15 s.
 """
 from __future__ import annotations
 
@@ -38,9 +42,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fp8_128k_b32")
     ap.add_argument("--sparsity-bp", type=int, default=None)
-    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the workload's sparsity sweep and fit t = a(1-rho) + c")
+    ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-max-requests", type=int, default=32)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run three plain 1 GiB device-to-device copies (the reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -70,7 +80,23 @@ def algorithmic_score_bytes(w: G.Workload, keys_scored_per_row: float, n_blocks_
     return keys_scored_per_row * per_slot + n_blocks_sel * per_block + w.batch * per_req
 
 
-def run_gpu(inp: Inputs, sparsity_bp: int, steps: int, warmup: int):
+def _timed_us(fn, reps: int, stream) -> float:
+    """Mean duration of `fn` over `reps` back-to-back launches (HIP events on `stream`)."""
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def run_gpu(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_reps: int = 0):
+    """Time `steps` decode steps (one spin_step call each) after `warmup` untimed
+    ones; with stage_reps > 0, then time each stage alone on the last step's inputs."""
     from sparse_attention_indexer_spin_amd import SpinLayer, api
     w = inp.w
     lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks, d_cap=G.d_capacity(w, steps + warmup),
@@ -84,79 +110,69 @@ def run_gpu(inp: Inputs, sparsity_bp: int, steps: int, warmup: int):
     pages, scale, pt = inp.keys.pages, inp.keys.scale, inp.keys.page_table
     bt = lay.batch(pages.shape[0])
     stream = torch.cuda.current_stream()
-    names = ["predict", "select", "score", "topk", "ema", "advance"]
-
-    def one_step(s, ev=None):
-        q = inp.q[s]
-        nv = inp.accept_dev[s] if w.rows > 1 else None
-        marks = [] if ev is None else ev
-        if ev is not None:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
-        api.spin_predict_blocks(lay.cfg, bt, lay.V, lay.D, lay.S)
-        if ev is not None:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
-        api.spin_select_blocks(lay.cfg, bt, lay.S, lay.row_code, lay.sel, lay.n_sel)
-        if ev is not None:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
-        api.spin_sparse_index_score(lay.cfg, bt, q, inp.weights, pages, scale, pt, lay.sel,
-                                    lay.n_sel, lay.z)
-        if ev is not None:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
-        api.spin_topk(lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.topk_idx, lay.workspace)
-        if ev is not None:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
-        api.spin_ema_update(lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.V, lay.D, n_valid=nv)
-        if ev is not None:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
-        api.spin_advance(w.rows, lay.q_pos, lay.step_ctr, n_valid=nv)
-        if ev is not None:
-            marks.append(torch.cuda.Event(enable_timing=True)); marks[-1].record(stream)
-
+    nv = [inp.accept_dev[s] if w.rows > 1 else None for s in range(warmup + steps)]
+    ios = [lay.make_io(inp.q[s], inp.weights, pages, scale, pt, n_valid=nv[s])
+           for s in range(warmup + steps)]
     for s in range(warmup):
-        one_step(s)
+        api.spin_step(lay.cfg, bt, ios[s])
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    all_marks = []
     t0.record(stream)
     for s in range(warmup, warmup + steps):
-        m = []
-        one_step(s, m)
-        all_marks.append(m)
+        api.spin_step(lay.cfg, bt, ios[s])
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    stage_ms = np.zeros(len(names))
-    for m in all_marks:
-        for i in range(len(names)):
-            stage_ms[i] += m[i].elapsed_time(m[i + 1])
-    stage_ms /= steps
+    assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
     n_sel = lay.n_sel.cpu().numpy().astype(np.int64)
-    ctx = inp.ctx.numpy().astype(np.int64)
+    ctx = lay.ctx_len.cpu().numpy().astype(np.int64)
     # scored keys per step: the valid slots of the selected blocks of every row
     keys = int(np.minimum(n_sel * 64, ctx).sum()) * w.rows
-    assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
-    return dict(total_ms=total_ms, ms_per_step=total_ms / steps,
-                stage_us={n: float(v * 1e3) for n, v in zip(names, stage_ms)},
-                keys_per_step=keys, n_sel=int(n_sel.sum()))
+    out = dict(total_ms=total_ms, ms_per_step=total_ms / steps, keys_per_step=keys,
+               n_sel=int(n_sel.sum()))
+    if stage_reps:
+        # the last step's inputs: its selection is in lay.sel / lay.n_sel
+        q = inp.q[warmup + steps - 1]
+        last_nv = nv[-1]
+        st = {
+            "predict": lambda: api.spin_predict_blocks(lay.cfg, bt, lay.V, lay.D, lay.S),
+            "select": lambda: api.spin_select_blocks(lay.cfg, bt, lay.S, lay.row_code, lay.sel,
+                                                     lay.n_sel),
+            "score": lambda: api.spin_sparse_index_score(lay.cfg, bt, q, inp.weights, pages,
+                                                         scale, pt, lay.sel, lay.n_sel, lay.z),
+            "topk": lambda: api.spin_topk(lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.topk_idx,
+                                          lay.workspace),
+            "ema": lambda: api.spin_ema_update(lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.V,
+                                               lay.D, n_valid=last_nv),
+        }
+        out["stage_us"] = {k: _timed_us(f, stage_reps, stream) for k, f in st.items()}
+        assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
+    return out
 
 
-def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, n_req: int):
-    """Time the CPU oracle on n_req requests: one dense warm-up step (untimed),
-    then two sparse steps (timed)."""
+def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, budget_s: float,
+                 max_requests: int):
+    """Time the CPU oracle on whole requests of the workload until about `budget_s`
+    seconds of timed work: per request one dense warm-up step (untimed, t = 0 is
+    dense by definition), then two sparse steps (timed)."""
     from threadpoolctl import threadpool_info
     from oracle import spin_oracle as O
     pt = inp.keys.page_table.cpu().numpy()
     pages_dev, scale_dev = inp.keys.pages, inp.keys.scale
     st_keys = 0
     elapsed = 0.0
-    for r in range(n_req):
+    n_req = 0
+    for r in range(min(w.batch, max_requests)):
+        if elapsed >= budget_s:
+            break
         phys = torch.from_numpy(pt[r]).long().cuda()
-        pages = pages_dev[phys].cpu().numpy()
-        scale = scale_dev[phys].cpu().numpy() if scale_dev is not None else None
-        local_pt = np.arange(w.max_blocks)
         if w.key_dtype == "bf16":
             pages = pages_dev[phys].cpu().view(torch.int16).numpy().astype(np.uint16)
+        else:
+            pages = pages_dev[phys].cpu().numpy()
+        scale = scale_dev[phys].cpu().numpy() if scale_dev is not None else None
+        local_pt = np.arange(w.max_blocks)
         state = O.RequestState(w.n_slots + 64, G.d_capacity(w, 8))
         N = int(inp.ctx[r])
         for s in range(3):
@@ -173,16 +189,60 @@ def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, n_req: int):
             if s > 0:
                 elapsed += dt
                 st_keys += len(res["slots"]) * w.rows
+        n_req += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": st_keys / elapsed, "unit": "keys/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{n_req} of {w.batch} requests x 2 sparse steps after a dense warm-up "
-                      f"step ({st_keys} keys scored in {elapsed:.1f} s; numpy fp64 oracle, "
-                      f"host has {os.cpu_count()} logical CPUs)"}
+            "sample": f"{n_req} of {w.batch} requests x 2 sparse steps after an untimed dense "
+                      f"warm-up step ({st_keys} keys scored in {elapsed:.1f} s; numpy fp64 "
+                      f"oracle, host has {os.cpu_count()} logical CPUs)"}
+
+
+SCORE_SOURCES = ("sparse_attention_indexer_spin_amd/csrc/k_score.hip",
+                 "sparse_attention_indexer_spin_amd/csrc/spin_dev.h", "include/spin.h")
+
+
+def score_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, sparsity_bp: int):
+    """HBM bytes per score launch from the committed counter summary, or None when
+    there is none for this workload or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"k_score_{workload}_rho{sparsity_bp}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != score_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def copy_calibration():
+    n = 256 * 1024 * 1024  # 1 GiB of fp32
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "copies": 3}))
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
                                    "(requests shard across GPUs with no exchange)"}))
@@ -191,7 +251,7 @@ def main():
     sp = w.sparsity_bp[0] if args.sparsity_bp is None else args.sparsity_bp
     total_steps = args.steps + args.warmup
     inp = Inputs(w, total_steps)
-    res = run_gpu(inp, sp, args.steps, args.warmup)
+    res = run_gpu(inp, sp, args.steps, args.warmup, stage_reps=args.stage_reps)
     score_us = res["stage_us"]["score"]
     keys_row = res["keys_per_step"]
     score_bytes = algorithmic_score_bytes(w, keys_row, res["n_sel"] * w.rows)
@@ -201,24 +261,26 @@ def main():
         "metric": "indexer keys scored/s + us/decode-step/layer at 512K ctx; % HBM peak",
         "value": value, "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3 keys, bf16 q, f32 accumulate",
+        "scaling": "weak", "vs_baseline": None, "dtype": w.key_dtype,
         "data": "synthetic (seeded generator: Gaussian keys + heavy slots + RoPE, AR(1) queries)",
         "config": {"workload": w.name, "requests": w.batch, "slots_per_request": w.n_slots,
                    "layers": 1, "verifier_rows": w.rows, "topk": w.topk,
-                   "sparsity_bp": sp, "explore_bp": w.explore_bp, "key_dtype": w.key_dtype},
+                   "sparsity_bp": sp, "explore_bp": w.explore_bp, "key_dtype": w.key_dtype,
+                   "q_dtype": w.q_dtype},
         "us_per_step_layer": res["ms_per_step"] * 1e3,
         "stage_us": res["stage_us"],
         "keys_scored_per_step": keys_row,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "k_score_fp8" if w.key_dtype == "fp8" else "k_score_" + w.key_dtype,
-                     "algorithmic_bytes_per_launch": score_bytes},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name, sp),
+                     "kernel": "spin::k_score_slots" if w.rows == 1 else "spin::k_score_mfma",
+                     "algorithmic_bytes_per_launch": score_bytes,
+                     "launch_us": score_us},
     }
-    if not args.no_sweep and w.rows == 1 and len(w.sparsity_bp) > 1:
+    if args.sweep and w.rows == 1 and len(w.sparsity_bp) > 1:
         sweep = {}
         for s in sorted(set(w.sparsity_bp)):
-            r2 = run_gpu(inp, s, min(args.steps, 20), args.warmup)
-            sweep[s] = r2
+            sweep[s] = run_gpu(inp, s, min(args.steps, 20), args.warmup, stage_reps=10)
         rho = np.array([1.0 - sweep[s]["n_sel"] / (w.batch * w.max_blocks) for s in sweep])
         T = np.array([sweep[s]["ms_per_step"] * 1e3 for s in sweep])
         A = np.stack([1.0 - rho, np.ones_like(rho)], 1)
@@ -227,12 +289,13 @@ def main():
         t_dense_indexer = dense["score"] + dense["topk"]
         out["sparsity_sweep"] = {
             "us_per_step": {str(s): sweep[s]["ms_per_step"] * 1e3 for s in sweep},
+            "score_us": {str(s): sweep[s]["stage_us"]["score"] for s in sweep},
             "realized_sparsity": {str(s): float(x) for s, x in zip(sweep, rho)},
             "fit_us": {"a": float(a), "c": float(c)},
             "dense_indexer_us": t_dense_indexer,
             "c_over_dense_indexer": float(c / t_dense_indexer)}
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, inp, sp, args.cpu_requests)
+        out["cpu_baseline"] = cpu_baseline(w, inp, sp, args.cpu_seconds, args.cpu_max_requests)
     print(json.dumps(out))
 
 
