@@ -64,16 +64,18 @@ struct ItemTable {
   int total;
 };
 
-__device__ __forceinline__ ItemTable build_items(const ScoreParams& p, int* pre, int* tmp) {
+__device__ __forceinline__ ItemTable build_items(const ScoreParams& p, int* pre, int* tmp,
+                                                int* ne_pre = nullptr, int* n_ne = nullptr) {
   constexpr int NT = 256;
   const int per = (p.R + NT - 1) / NT;  // requests per thread (R <= SPIN_MAX_BATCH)
   const int r0 = threadIdx.x * per;
   int cnt[SPIN_MAX_BATCH / NT];
-  int mine = 0;
+  int mine = 0, mine_ne = 0;
 #pragma unroll
   for (int u = 0; u < SPIN_MAX_BATCH / NT; ++u) {
     cnt[u] = (u < per && r0 + u < p.R) ? items_of(p, r0 + u) : 0;
     mine += cnt[u];
+    mine_ne += cnt[u] > 0;
   }
   int total;
   int run = block_excl_scan<NT>(mine, tmp, &total);
@@ -81,8 +83,48 @@ __device__ __forceinline__ ItemTable build_items(const ScoreParams& p, int* pre,
   for (int u = 0; u < SPIN_MAX_BATCH / NT; ++u)
     if (u < per && r0 + u < p.R) { pre[r0 + u] = run; run += cnt[u]; }
   if (threadIdx.x == 0) pre[p.R] = total;
+  if (ne_pre) {  // exclusive prefix count of the requests that have items
+    int tot_ne;
+    int run_ne = block_excl_scan<NT>(mine_ne, tmp, &tot_ne);
+#pragma unroll
+    for (int u = 0; u < SPIN_MAX_BATCH / NT; ++u)
+      if (u < per && r0 + u < p.R) { ne_pre[r0 + u] = run_ne; run_ne += cnt[u] > 0; }
+    *n_ne = tot_ne;
+  }
   __syncthreads();
   return ItemTable{pre, total};
+}
+
+// Item range [lo, hi) of worker bx of gx (a workgroup or a wave), aligned to
+// requests: every request with items gets one worker plus a share of the
+// others in proportion to its items, and splits its groups of G items evenly
+// over them.  A range then lies in one request, so the worker loads one
+// query.  Needs gx >= the number of requests with items (else returns false).
+template <int G>
+__device__ __forceinline__ bool request_range(const ScoreParams& p, const ItemTable& tb,
+                                              const int* ne_pre, int n_ne, int bx, int gx,
+                                              int& lo, int& hi, int& req) {
+  lo = hi = 0;
+  req = -1;
+  if (gx < n_ne) return false;
+  if (tb.total == 0) return true;
+  const auto first_wg = [&](int r) {  // first workgroup of request r; first_wg(R) = gx
+    return ne_pre[r] + (int)((int64_t)(gx - n_ne) * tb.pre[r] / tb.total);
+  };
+  int a = 0, b = p.R - 1;  // last r with first_wg(r) <= bx
+  while (a < b) {
+    const int mid = (a + b + 1) >> 1;
+    if (first_wg(mid) <= bx) a = mid; else b = mid - 1;
+  }
+  const int r = a;
+  req = r;
+  const int w = (r + 1 < p.R ? first_wg(r + 1) : gx) - first_wg(r), part = bx - first_wg(r);
+  const int items = tb.pre[r + 1] - tb.pre[r], groups = (items + G - 1) / G;
+  if (w <= 0 || items <= 0) return true;
+  const int gl = (int)((int64_t)part * groups / w), gh = (int)((int64_t)(part + 1) * groups / w);
+  lo = tb.pre[r] + gl * G;
+  hi = min(tb.pre[r + 1], tb.pre[r] + gh * G);
+  return true;
 }
 
 // Descriptor of item g (one lane each): page (0 if invalid), block id j,
@@ -503,13 +545,48 @@ struct QFull<0, NS> {  // fp8 keys: NS E4M3 terms per query value
   v8i part[NS][4];
   float wq[4][4];
 
+  v4u raw[4][4];  // bf16 queries between fetch() and convert()
+
+  // Issue the loads of a bf16 query (fp32 queries are read by convert()).
+  __device__ __forceinline__ void fetch(const ScoreParams& p, int q_bf16, int rowid) {
+    if (!q_bf16) return;
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    const int64_t qbase = (int64_t)rowid * 64;
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint16_t* qp = q + (qbase + 16 * t + m) * 128;
+      raw[t][0] = *reinterpret_cast<const v4u*>(qp + 16 * g);
+      raw[t][1] = *reinterpret_cast<const v4u*>(qp + 16 * g + 8);
+      raw[t][2] = *reinterpret_cast<const v4u*>(qp + 64 + 16 * g);
+      raw[t][3] = *reinterpret_cast<const v4u*>(qp + 64 + 16 * g + 8);
+    }
+  }
+
   __device__ __forceinline__ void load(const ScoreParams& p, int q_bf16, int rowid) {
+    fetch(p, q_bf16, rowid);
+    convert(p, q_bf16, rowid);
+  }
+
+  // Split the query into NS E4M3 terms per value after a per-head power-of-two
+  // scaling (2^e amax in [128, 256)); 2^-e folds into the head weight.
+  __device__ __forceinline__ void convert(const ScoreParams& p, int q_bf16, int rowid) {
     const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
     const int64_t qbase = (int64_t)rowid * 64;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       float x[32];
-      load_q32(p.q, q_bf16, (qbase + 16 * t + m) * 128, g, x);
+      if (q_bf16) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            x[8 * v + 2 * c] = __uint_as_float(raw[t][v][c] << 16);
+            x[8 * v + 2 * c + 1] = __uint_as_float(raw[t][v][c] & 0xFFFF0000u);
+          }
+      } else {
+        load_q32(p.q, q_bf16, (qbase + 16 * t + m) * 128, g, x);
+      }
       float amax = 0.0f;
 #pragma unroll
       for (int u = 0; u < 32; ++u) amax = fmaxf(amax, fabsf(x[u]));
@@ -546,6 +623,26 @@ struct QFull<0, NS> {  // fp8 keys: NS E4M3 terms per query value
     }
   }
 
+  // this lane's ReLU-weighted sum over its 16 heads for the 16 slots whose
+  // key bytes are in kf (MFMA B operand)
+  __device__ __forceinline__ float dot(const v8i& kf) const {
+    v4f acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(part[sp][t], kf, acc[t], 0, 0, 0,
+                                                                  127, 0, 127);
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s = fmaf(wq[t][i], relu(acc[t][i]), s);
+    return s;
+  }
+
   // this lane's ReLU-weighted sum over its heads for slot `slot` of the page
   __device__ __forceinline__ float mul(const uint8_t* kbuf, int slot) const {
     const int g = (threadIdx.x & 63) >> 4;
@@ -575,7 +672,11 @@ struct QFull<1, NS> {  // bf16 keys
   v4u qa[4][4];
   float wq[4][4];
 
-  __device__ __forceinline__ void load(const ScoreParams& p, int, int rowid) {
+  // bf16 queries feed the bf16 MFMA as they are: fetching is all there is
+  __device__ __forceinline__ void convert(const ScoreParams&, int, int) {}
+  __device__ __forceinline__ void load(const ScoreParams& p, int qb, int rowid) { fetch(p, qb, rowid); }
+
+  __device__ __forceinline__ void fetch(const ScoreParams& p, int, int rowid) {
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
     const int64_t qbase = (int64_t)rowid * 64;
@@ -631,19 +732,31 @@ __attribute__((amdgpu_waves_per_eu(3, 8))) void k_score_slots(ScoreParams p) {
   __shared__ SlotShared<KT, NB> sm;
   extern __shared__ int pre_dyn[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
-  const ItemTable tb = build_items(p, pre_dyn, sm.tmp);
-  // whole groups per workgroup (the last group of the grid may be partial)
-  const int n_groups = (tb.total + G - 1) / G;
-  const int per = (n_groups + gridDim.x - 1) / gridDim.x;
-  const int lo = min(tb.total, (int)blockIdx.x * per * G), hi = min(tb.total, lo + per * G);
+  int n_ne;
+  const ItemTable tb = build_items(p, pre_dyn, sm.tmp, pre_dyn + p.R + 1, &n_ne);
+  int lo, hi, q_req;
+  if (!request_range<G>(p, tb, pre_dyn + p.R + 1, n_ne, blockIdx.x, gridDim.x, lo, hi, q_req)) {
+    // fewer workgroups than requests: contiguous runs of whole groups
+    const int n_groups = (tb.total + G - 1) / G;
+    const int per = (n_groups + gridDim.x - 1) / gridDim.x;
+    lo = min(tb.total, (int)blockIdx.x * per * G);
+    hi = min(tb.total, lo + per * G);
+    q_req = -1;
+  }
   if (lo >= hi) return;
   QFull<KT, NS> Q;
-  int q_req = -1;
-  DescBatch db, dd;  // cursors of the scoring stream and of the copy stream
+  // the first request's query loads fly together with the descriptor loads
+  if (q_req >= 0) Q.fetch(p, QB, q_req);
+  DescBatch db;  // cursor of the scoring stream
   db.init(p, tb, lo);
-  dd.init(p, tb, lo);
+  if (q_req < 0) {
+    q_req = __builtin_amdgcn_readfirstlane(db.mine.r);
+    Q.fetch(p, QB, q_req);
+  }
+  DescBatch dd = db;  // cursor of the copy stream
   for (int i = 0; i < (D - 1) * G && lo + i < hi; ++i)
     Dma<KT>::issue(p, dd.get(p, tb, lo + i).page, sm.kbuf[i], sm.sbuf[i]);
+  Q.convert(p, QB, q_req);  // while the first pages are in flight
   const int my_slot = 16 * wave + (lane & 15);  // page slot this lane scores
   int ring = 0;                                 // ring slot of group `it`
   for (int it = lo; it < hi; it += G) {
@@ -685,6 +798,91 @@ __attribute__((amdgpu_waves_per_eu(3, 8))) void k_score_slots(ScoreParams p) {
     }
     ring = (ring + G) % NB;
   }
+}
+
+
+// ---------------------------------------------------------------------------
+// fp8 keys, one verifier row: every wave scores whole pages on its own.
+// A wave holds the request's whole query (64 heads, NS E4M3 terms), loads
+// each page straight into registers (lane (n, g) holds the key bytes
+// [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16) of slots 16s + n, s = 0..3,
+// the same dims its query registers hold) with P pages in flight, and runs
+// 4 sub-tiles x 4 head tiles x NS MFMAs per page.  A reduce-scatter over the
+// lane groups leaves lane l with slot l's total, which it scales and stores.
+// No LDS staging and no barriers: waves progress independently.
+// ---------------------------------------------------------------------------
+template <int NS, int QB, int P>
+__global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
+  extern __shared__ int pre_dyn[];
+  __shared__ int tmp[32];
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int wave_id = blockIdx.x * 4 + (threadIdx.x >> 6), n_waves = gridDim.x * 4;
+  int n_ne;
+  const ItemTable tb = build_items(p, pre_dyn, tmp, pre_dyn + p.R + 1, &n_ne);
+  int lo, hi, q_req;
+  if (!request_range<1>(p, tb, pre_dyn + p.R + 1, n_ne, wave_id, n_waves, lo, hi, q_req)) {
+    const int per = (tb.total + n_waves - 1) / n_waves;
+    lo = min(tb.total, wave_id * per);
+    hi = min(tb.total, lo + per);
+    q_req = -1;
+  }
+  if (lo >= hi) return;  // no barrier follows
+  QFull<0, NS> Q;
+  if (q_req >= 0) Q.fetch(p, QB, q_req);
+  DescBatch db;
+  db.init(p, tb, lo);
+  if (q_req < 0) {
+    q_req = __builtin_amdgcn_readfirstlane(db.mine.r);
+    Q.fetch(p, QB, q_req);
+  }
+  DescBatch dd = db;
+  const uint8_t* kp = reinterpret_cast<const uint8_t*>(p.kp);
+  // lane's byte offsets inside a page: sub-tile s, halves h
+  const int off0 = n * 128 + 16 * g;
+  v4u kb[P][8];
+  float sc[P];
+  const auto load_page = [&](int page, v4u (&b)[8], float& s) {
+    const uint8_t* base = kp + (int64_t)page * 8192 + off0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      b[2 * t] = *reinterpret_cast<const v4u*>(base + t * 2048);
+      b[2 * t + 1] = *reinterpret_cast<const v4u*>(base + t * 2048 + 64);
+    }
+    s = p.ks[(int64_t)page * 64 + lane];
+  };
+#pragma unroll
+  for (int u = 0; u < P - 1; ++u) load_page(dd.get(p, tb, min(lo + u, hi - 1)).page, kb[u], sc[u]);
+  Q.convert(p, QB, q_req);
+  int bad = 0;
+  for (int it = lo; it < hi; it += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int cur = it + u;
+      if (cur >= hi) break;
+      // refill: page cur + P - 1 (the last page again past the end: an L2 hit)
+      load_page(dd.get(p, tb, min(cur + P - 1, hi - 1)).page, kb[(u + P - 1) % P],
+                sc[(u + P - 1) % P]);
+      const Desc d = db.get(p, tb, cur);
+      if (d.r != q_req) {  // only without request-aligned ranges
+        q_req = d.r;
+        Q.load(p, QB, q_req);
+      }
+      float part[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const v4u a = kb[u][2 * st], b2 = kb[u][2 * st + 1];
+        const v8i kf = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w,
+                           (int)b2.x, (int)b2.y, (int)b2.z, (int)b2.w};
+        part[st] = Q.dot(kf);
+      }
+      const float tot = reduce_scatter4(part);
+      const int slot = d.j * 64 + lane;
+      const float zv = (slot < d.N && !d.bad) ? tot * sc[u] + 0.0f : 0.0f;
+      p.z[(int64_t)d.r * p.z_ld + (int64_t)d.k * 64 + lane] = zv;
+      bad |= d.bad;
+    }
+  }
+  if (bad && lane == 0) raise_error(p.err, SPIN_DERR_PAGE);
 }
 
 // ---------------------------------------------------------------------------
@@ -737,7 +935,7 @@ template <int KT, int NS, int NR, int QB>
 static void launch_mfma(const ScoreParams& p, hipStream_t st) {
   constexpr int NB = KT == 0 ? 6 : 4;
   const auto kern = k_score_mfma<KT, NS, NR, QB, NB>;
-  const size_t dyn = sizeof(int) * (p.R + 1);
+  const size_t dyn = sizeof(int) * 2 * (p.R + 1);
   const int g = min(resident_workgroups((const void*)kern, 256, dyn), p.R * p.max_blocks);
   hipLaunchKernelGGL(kern, dim3(g), dim3(256), dyn, st, p);
 }
@@ -746,14 +944,24 @@ template <int KT, int NS, int QB>
 static void launch_slots(const ScoreParams& p, hipStream_t st) {
   constexpr int G = 2, D = KT == 0 ? 3 : 2;
   const auto kern = k_score_slots<KT, NS, QB, G, D>;
-  const size_t dyn = sizeof(int) * (p.R + 1);
+  const size_t dyn = sizeof(int) * 2 * (p.R + 1);
+  const int g = min(resident_workgroups((const void*)kern, 256, dyn), p.R * p.max_blocks);
+  hipLaunchKernelGGL(kern, dim3(g), dim3(256), dyn, st, p);
+}
+
+template <int NS, int QB>
+static void launch_wave(const ScoreParams& p, hipStream_t st) {
+  constexpr int P = 2;  // 234 VGPRs: two waves per SIMD
+  const auto kern = k_score_wave<NS, QB, P>;
+  const size_t dyn = sizeof(int) * 2 * (p.R + 1);
   const int g = min(resident_workgroups((const void*)kern, 256, dyn), p.R * p.max_blocks);
   hipLaunchKernelGGL(kern, dim3(g), dim3(256), dyn, st, p);
 }
 
 template <int KT, int NS, int QB>
 static void launch_rows(const ScoreParams& p, hipStream_t st) {
-  if (p.rows <= 1) launch_slots<KT, NS, QB>(p, st);
+  if (p.rows <= 1 && KT == 0) launch_wave<NS, QB>(p, st);
+  else if (p.rows <= 1) launch_slots<KT, NS, QB>(p, st);
   else if (p.rows <= 2) launch_mfma<KT, NS, 2, QB>(p, st);
   else launch_mfma<KT, NS, 4, QB>(p, st);
 }
