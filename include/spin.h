@@ -217,7 +217,14 @@ typedef struct spin_step_io {
 spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_step_io* io,
                       int32_t defer_ema, void* stream);
 
-/* Device workspace bytes spin_topk / spin_step need for this shape (0 = none). */
+/*
+ * Device workspace bytes spin_topk / spin_step need for this shape.  The
+ * buffer holds the top-K threshold hints and candidate lists (any initial
+ * contents are valid: a hint only changes speed) followed, for spin_step, by
+ * the step's q_pos snapshot that lets one kernel run the EMA update and the
+ * counter advance together.  One workspace per layer; calls that share a
+ * workspace must not overlap.
+ */
 size_t spin_workspace_bytes(const spin_config* cfg, int32_t batch, int32_t n_rows,
                             int32_t max_blocks);
 

@@ -62,11 +62,18 @@ __global__ __launch_bounds__(256) void k_ema(float alpha, int rows, int max_bloc
                                              const int32_t* __restrict__ sel,
                                              const int32_t* __restrict__ n_sel,
                                              float* __restrict__ V, int64_t v_ld,
-                                             float* __restrict__ D, int64_t d_ld) {
+                                             float* __restrict__ D, int64_t d_ld,
+                                             int32_t* __restrict__ qpos_out,
+                                             int32_t* __restrict__ step_out) {
   const int r = blockIdx.y;
   const int k0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kEmaBlocksPerWave;
   const int lane = threadIdx.x & 63;
   const int N = ctx[r], q = qpos[r];
+  // fused counter advance (qpos is then the step's snapshot, not qpos_out)
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (qpos_out) qpos_out[r] = q + (n_valid ? n_valid[r] : rows);
+    if (step_out) step_out[r] += 1;
+  }
   if (request_error(N, q, rows, max_blocks, v_ld, d_ld)) return;
   const int ns = clamp_nsel(n_sel[r], max_blocks);
   if (k0 >= ns) return;
@@ -128,10 +135,12 @@ __global__ __launch_bounds__(256) void k_ema(float alpha, int rows, int max_bloc
 
 hipError_t launch_ema(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                       const int32_t* sel, const int32_t* n_sel, const int32_t* n_valid, float* V,
-                      int64_t v_ld, float* D, int64_t d_ld, hipStream_t st) {
+                      int64_t v_ld, float* D, int64_t d_ld, hipStream_t st,
+                      const int32_t* qpos_snap, int32_t* qpos_out, int32_t* step_out) {
   dim3 grid((b.max_blocks + 4 * kEmaBlocksPerWave - 1) / (4 * kEmaBlocksPerWave), b.batch);
   hipLaunchKernelGGL(k_ema, grid, dim3(256), 0, st, c.ema_alpha, b.n_rows, b.max_blocks,
-                     b.ctx_len, b.q_pos, n_valid, z, z_ld, sel, n_sel, V, v_ld, D, d_ld);
+                     b.ctx_len, qpos_snap ? qpos_snap : b.q_pos, n_valid, z, z_ld, sel, n_sel, V,
+                     v_ld, D, d_ld, qpos_out, step_out);
   return hipGetLastError();
 }
 

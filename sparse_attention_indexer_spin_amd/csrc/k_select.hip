@@ -26,9 +26,13 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
                                                  const int32_t* __restrict__ qpos,
                                                  const float* __restrict__ V, int64_t v_ld,
                                                  const float* __restrict__ D, int64_t d_ld,
-                                                 float* __restrict__ S, int32_t* err) {
+                                                 float* __restrict__ S, int32_t* err,
+                                                 int32_t* __restrict__ qpos_snap) {
   const int r = blockIdx.z, row = blockIdx.y;
   const int N = ctx[r], q0 = qpos[r];
+  // a whole step keeps the step's query position here for the fused EMA +
+  // counter advance, which then never reads the array it advances
+  if (qpos_snap && blockIdx.x == 0 && row == 0 && threadIdx.x == 0) qpos_snap[r] = q0;
   const int e = request_error(N, q0, rows, max_blocks, v_ld, d_ld);
   if (e) {
     if (row == 0 && blockIdx.x == 0 && threadIdx.x == 0) raise_error(err, e);
@@ -181,11 +185,12 @@ __global__ void k_zero_i32(int32_t* __restrict__ p, int n) {
 // host launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
-                          const float* D, int64_t d_ld, float* S, hipStream_t st) {
+                          const float* D, int64_t d_ld, float* S, hipStream_t st,
+                          int32_t* qpos_snap) {
   dim3 grid((b.max_blocks + 4 * kPredBlocksPerWave - 1) / (4 * kPredBlocksPerWave), b.n_rows,
             b.batch);
   hipLaunchKernelGGL(k_predict, grid, dim3(256), 0, st, c.combine, b.n_rows, b.max_blocks,
-                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld, S, b.err);
+                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld, S, b.err, qpos_snap);
   return hipGetLastError();
 }
 

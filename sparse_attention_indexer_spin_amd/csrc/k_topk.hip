@@ -333,6 +333,11 @@ size_t topk_workspace_bytes(const spin_config&, int R, int rows, int max_blocks)
   return (size_t)ws_size(R * rows, max_blocks);
 }
 
+size_t step_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks) {
+  return (size_t)align256((int64_t)topk_workspace_bytes(c, R, rows, max_blocks)) +
+         (size_t)align256(4LL * R);
+}
+
 hipError_t launch_topk(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                        const int32_t* sel, const int32_t* n_sel, int32_t* out, void* wsp, size_t,
                        hipStream_t st) {

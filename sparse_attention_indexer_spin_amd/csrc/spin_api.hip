@@ -128,7 +128,7 @@ const char* spin_last_error(void) { return g_err; }
 size_t spin_workspace_bytes(const spin_config* cfg, int32_t batch, int32_t n_rows,
                             int32_t max_blocks) {
   if (!cfg) return 0;
-  return spin::topk_workspace_bytes(*cfg, batch, n_rows, max_blocks);
+  return spin::step_workspace_bytes(*cfg, batch, n_rows, max_blocks);
 }
 
 spin_status spin_predict_blocks(const spin_config* cfg, const spin_batch* bt, const float* V,
@@ -259,13 +259,17 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
   SPIN_REQUIRE(io->topk_idx);
   SPIN_CHECK(check_score_args(fn, cfg, bt, io->q, io->w, io->k_pages, io->k_scale, io->page_table,
                               io->pt_ld, io->sel, io->n_sel, io->z, io->z_ld));
-  const size_t need = spin::topk_workspace_bytes(*cfg, bt->batch, bt->n_rows, bt->max_blocks);
-  if (need > 0 && (!io->workspace || io->workspace_bytes < need))
+  const size_t need = spin::step_workspace_bytes(*cfg, bt->batch, bt->n_rows, bt->max_blocks);
+  if (!io->workspace || io->workspace_bytes < need)
     return fail(SPIN_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
   if (bt->batch == 0) return SPIN_OK;
   hipStream_t st = (hipStream_t)stream;
-  SPIN_CHECK(hip_status(spin::launch_predict(*cfg, *bt, io->V, io->v_ld, io->D, io->d_ld, io->S, st),
-                        "spin_step/predict"));
+  // the q_pos snapshot sits after the top-K region (256-B aligned)
+  const size_t topk_bytes = spin::topk_workspace_bytes(*cfg, bt->batch, bt->n_rows, bt->max_blocks);
+  int32_t* qsnap = reinterpret_cast<int32_t*>(static_cast<char*>(io->workspace) +
+                                              ((topk_bytes + 255) & ~size_t(255)));
+  SPIN_CHECK(hip_status(spin::launch_predict(*cfg, *bt, io->V, io->v_ld, io->D, io->d_ld, io->S, st,
+                                             qsnap), "spin_step/predict"));
   SPIN_CHECK(hip_status(spin::launch_select(*cfg, *bt, io->S, io->budget, io->row_code, io->sel,
                                             io->n_sel, st), "spin_step/select"));
   SPIN_CHECK(hip_status(spin::launch_score(*cfg, *bt, io->q, io->w, io->k_pages, io->k_scale,
@@ -275,12 +279,13 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
                                           io->topk_idx, io->workspace, io->workspace_bytes, st),
                         "spin_step/topk"));
   if (defer_ema) return SPIN_OK;
+  // EMA and counter advance in one kernel: it reads q positions from the
+  // snapshot, so advancing q_pos_mut (normally the same array as bt->q_pos)
+  // cannot race with its reads
   SPIN_CHECK(hip_status(spin::launch_ema(*cfg, *bt, io->z, io->z_ld, io->sel, io->n_sel,
-                                         io->n_valid, io->V, io->v_ld, io->D, io->d_ld, st),
-                        "spin_step/ema"));
-  if (io->q_pos_mut || io->step_mut)
-    SPIN_CHECK(hip_status(spin::launch_advance(bt->batch, bt->n_rows, io->n_valid, io->q_pos_mut,
-                                               io->step_mut, st), "spin_step/advance"));
+                                         io->n_valid, io->V, io->v_ld, io->D, io->d_ld, st, qsnap,
+                                         io->q_pos_mut, io->step_mut),
+                        "spin_step/ema+advance"));
   return SPIN_OK;
 }
 

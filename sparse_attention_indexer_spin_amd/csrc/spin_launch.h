@@ -6,8 +6,11 @@
 
 namespace spin {
 
+// qpos_snap (optional, [R]): predict records the step's q_pos there; the
+// fused EMA + advance of a whole step reads it instead of q_pos.
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
-                          const float* D, int64_t d_ld, float* S, hipStream_t st);
+                          const float* D, int64_t d_ld, float* S, hipStream_t st,
+                          int32_t* qpos_snap = nullptr);
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
                          hipStream_t st);
@@ -19,9 +22,15 @@ hipError_t launch_topk(const spin_config& c, const spin_batch& b, const float* z
                        const int32_t* sel, const int32_t* n_sel, int32_t* out, void* ws,
                        size_t ws_bytes, hipStream_t st);
 size_t topk_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks);
+// A whole step's workspace: the top-K region, then the step's q_pos snapshot.
+size_t step_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks);
+// With qpos_snap, q positions come from the snapshot and the kernel also
+// advances qpos_out / step_out (each optional) like launch_advance.
 hipError_t launch_ema(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                       const int32_t* sel, const int32_t* n_sel, const int32_t* n_valid, float* V,
-                      int64_t v_ld, float* D, int64_t d_ld, hipStream_t st);
+                      int64_t v_ld, float* D, int64_t d_ld, hipStream_t st,
+                      const int32_t* qpos_snap = nullptr, int32_t* qpos_out = nullptr,
+                      int32_t* step_out = nullptr);
 hipError_t launch_advance(int R, int rows, const int32_t* n_valid, int32_t* qpos, int32_t* step,
                           hipStream_t st);
 hipError_t launch_reset(int R, float* V, int64_t v_ld, float* D, int64_t d_ld, int32_t* step,
