@@ -48,6 +48,7 @@ struct ScoreParams {
   int64_t z_ld;
   int R, rows, max_blocks, n_pages;
   int32_t* err;
+  CandSink sink;  // sink.hint == nullptr: no candidate output
 };
 
 // Selected blocks of request r (0 for a request with invalid bounds).
@@ -853,6 +854,7 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
 #pragma unroll
   for (int u = 0; u < P - 1; ++u) load_page(dd.get(p, tb, min(lo + u, hi - 1)).page, kb[u], sc[u]);
   Q.convert(p, QB, q_req);
+  uint32_t hint = p.sink.hint ? p.sink.hint[q_req] : 0u;  // one row per request here
   int bad = 0;
   for (int it = lo; it < hi; it += P) {
 #pragma unroll
@@ -866,6 +868,7 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
       if (d.r != q_req) {  // only without request-aligned ranges
         q_req = d.r;
         Q.load(p, QB, q_req);
+        if (p.sink.hint) hint = p.sink.hint[q_req];
       }
       float part[4];
 #pragma unroll
@@ -880,6 +883,17 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
       const float zv = (slot < d.N && !d.bad) ? tot * sc[u] + 0.0f : 0.0f;
       p.z[(int64_t)d.r * p.z_ld + (int64_t)d.k * 64 + lane] = zv;
       bad |= d.bad;
+      if (p.sink.hint) {  // top-K pre-filter: this block's slots at or above the hint
+        const uint32_t key = float_key(zv);
+        const bool pass = slot < d.N && key >= hint;
+        const uint64_t m = __ballot(pass);
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (pass)
+          p.sink.cand[(int64_t)d.r * p.sink.cand_ld + (int64_t)d.k * 64 + pos] =
+              make_uint2(key, (uint32_t)slot);
+        if (lane == 0) p.sink.pcnt[(int64_t)d.r * p.sink.pcnt_ld + d.k] = __popcll(m);
+      }
     }
   }
   if (bad && lane == 0) raise_error(p.err, SPIN_DERR_PAGE);
@@ -966,12 +980,17 @@ static void launch_rows(const ScoreParams& p, hipStream_t st) {
   else launch_mfma<KT, NS, 4, QB>(p, st);
 }
 
+bool score_filters(const spin_config& c, const spin_batch& b) {
+  return c.key_dtype == SPIN_FP8_E4M3 && b.n_rows == 1;  // the per-wave kernel
+}
+
 hipError_t launch_score(const spin_config& c, const spin_batch& b, const void* q, const float* w,
                         const void* kp, const float* ks, const int32_t* pt, int64_t pt_ld,
                         const int32_t* sel, const int32_t* n_sel, float* z, int64_t z_ld,
-                        hipStream_t st) {
+                        hipStream_t st, const CandSink* sink) {
   ScoreParams p{q, w, kp, ks, pt, pt_ld, sel, n_sel, b.ctx_len, b.q_pos, z, z_ld,
-                b.batch, b.n_rows, b.max_blocks, b.n_pages, b.err};
+                b.batch, b.n_rows, b.max_blocks, b.n_pages, b.err, CandSink{}};
+  if (sink && score_filters(c, b)) p.sink = *sink;
   if (c.key_dtype == SPIN_FP8_E4M3) {
     if (c.q_dtype == SPIN_BF16) launch_rows<0, 2, 1>(p, st);
     else launch_rows<0, 3, 0>(p, st);

@@ -75,9 +75,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     const int32_t* __restrict__ step, const int32_t* __restrict__ req_id,
     const float* __restrict__ S, const int32_t* __restrict__ budget, uint8_t* __restrict__ code,
     int32_t* __restrict__ sel, int32_t* __restrict__ n_sel, int compact) {
-  __shared__ int hist[256];
+  __shared__ int hist[512];
   __shared__ int sh[32];
-  __shared__ uint32_t tmpu[16];
+  __shared__ uint32_t tmpu[32];
   const int row = blockIdx.x, r = blockIdx.y;
   const int N = ctx[r];
   const bool bad = request_error(N, qpos[r], rows, max_blocks, 0, 0) != 0;

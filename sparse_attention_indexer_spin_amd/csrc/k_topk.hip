@@ -34,6 +34,7 @@ struct TopkWs {
   int32_t* cnt;     // [rows_total][n_chunks] candidates kept
   int32_t* valid;   // [rows_total][n_chunks] valid slots
   uint2* cand;      // [rows_total][n_cap] (key, slot), chunk c at offset c * kChunk
+  int32_t* pcnt;    // [rows_total][max_blocks] kept per block (filter inside the score kernel)
   int n_chunks;
   int64_t n_cap;
 };
@@ -53,6 +54,8 @@ __host__ __device__ inline TopkWs carve(void* ws, int rows_total, int max_blocks
   w.valid = reinterpret_cast<int32_t*>(p + off);
   off = align256(off + 4LL * rows_total * w.n_chunks);
   w.cand = reinterpret_cast<uint2*>(p + off);
+  off = align256(off + 8LL * rows_total * w.n_cap);
+  w.pcnt = reinterpret_cast<int32_t*>(p + off);
   return w;
 }
 
@@ -60,7 +63,7 @@ static int64_t ws_size(int rows_total, int max_blocks) {
   const int64_t n_cap = (int64_t)max_blocks * 64;
   const int64_t n_chunks = (n_cap + kChunk - 1) / kChunk;
   return align256(4LL * rows_total) + 2 * align256(4LL * rows_total * n_chunks) +
-         8LL * rows_total * n_cap;
+         align256(8LL * rows_total * n_cap) + 4LL * rows_total * max_blocks;
 }
 
 __device__ __forceinline__ int row_candidates(int N, int qpos, int rows, int max_blocks,
@@ -251,9 +254,9 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(
     int32_t* __restrict__ out, TopkWs ws) {
   __shared__ uint32_t lkey[kCap];
   __shared__ int off[kSelThreads / 4 + 1];
-  __shared__ int hist[256];
+  __shared__ int hist[512];
   __shared__ int sh[32];
-  __shared__ uint32_t tmpu[16];
+  __shared__ uint32_t tmpu[32];
   const int rowid = blockIdx.x, r = rowid / rows;
   int32_t* orow = out + (int64_t)rowid * K;
   const int N = ctx[r];
@@ -329,6 +332,105 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// 2'. select after a score kernel that filtered (CandSink): the candidates of
+// selected block k are cand[64 k .. 64 k + pcnt[k]), so concatenating the
+// blocks in list order gives them in ascending slot order.
+// ---------------------------------------------------------------------------
+constexpr int kPagesPerThread = SPIN_MAX_BLOCKS / kSelThreads;
+
+__global__ __launch_bounds__(kSelThreads) void k_topk_select_pages(
+    int K, int rows, int max_blocks, const int32_t* __restrict__ ctx,
+    const int32_t* __restrict__ qpos, const float* __restrict__ z, int64_t z_ld,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
+    int32_t* __restrict__ out, TopkWs ws) {
+  __shared__ uint32_t lkey[kCap];
+  __shared__ int32_t lslot[kCap];
+  __shared__ int32_t lsrc[kCap];  // candidate q sits at cand[lsrc[q]]
+  __shared__ int hist[512];
+  __shared__ int sh[32];
+  __shared__ uint32_t tmpu[32];
+  const int rowid = blockIdx.x, r = rowid / rows;
+  int32_t* orow = out + (int64_t)rowid * K;
+  const int N = ctx[r];
+  const int n = row_candidates(N, qpos[r], rows, max_blocks, n_sel, r);
+  const int ns = n / 64;  // selected blocks
+  const int32_t* srow = sel + (int64_t)r * max_blocks;
+  // per-block kept counts: thread t owns blocks [t * PPT, t * PPT + PPT)
+  constexpr int PPT = kPagesPerThread;
+  const int32_t* prow = ws.pcnt + (int64_t)rowid * max_blocks;
+  int c[PPT];
+  int mine = 0;
+#pragma unroll
+  for (int e = 0; e < PPT; ++e) {
+    const int k = threadIdx.x * PPT + e;
+    c[e] = k < ns ? prow[k] : 0;
+    mine += c[e];
+  }
+  // valid slots: every selected block is full except the one holding slot N - 1
+  const int nvalid = ns == 0 ? 0 : 64 * ns - max(0, 64 * (srow[ns - 1] + 1) - N);
+  const int take = min(K, nvalid);
+  if (take == 0) {
+    for (int i = threadIdx.x; i < K; i += kSelThreads) orow[i] = -1;
+    return;
+  }
+  int c_tot;
+  int off = block_excl_scan<kSelThreads>(mine, sh, &c_tot);
+  if (c_tot < take || c_tot > kCap) {
+    TopkRow R{z + (int64_t)rowid * z_ld, srow, n, N};
+    fallback_row(R, K, orow, ws.hint + rowid, hist, sh, tmpu);
+    return;
+  }
+  // where each candidate comes from (LDS only), then all loads in flight
+#pragma unroll
+  for (int e = 0; e < PPT; ++e) {
+    const int k = threadIdx.x * PPT + e;
+    for (int i = 0; i < c[e]; ++i) lsrc[off + i] = k * 64 + i;
+    off += c[e];
+  }
+  __syncthreads();
+  const uint2* crow = ws.cand + (int64_t)rowid * ws.n_cap;
+  uint2 v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int q = threadIdx.x + e * kSelThreads;
+    v[e] = q < c_tot ? crow[lsrc[q]] : make_uint2(0u, 0u);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int q = threadIdx.x + e * kSelThreads;
+    if (q < c_tot) { lkey[q] = v[e].x; lslot[q] = (int32_t)v[e].y; }
+  }
+  __syncthreads();
+  uint32_t key[8];
+  uint32_t elig = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int q = threadIdx.x * 8 + e;
+    key[e] = q < c_tot ? lkey[q] : 0u;
+    if (q < c_tot) elig |= 1u << e;
+  }
+  const uint32_t chosen = block_select_top<8>(key, elig, take, hist, sh, tmpu);
+  int tot;
+  int pos = block_excl_scan<kSelThreads>(__popc(chosen), sh, &tot);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if ((chosen >> e & 1u) && pos < K) orow[pos++] = lslot[threadIdx.x * 8 + e];
+  for (int i = tot + threadIdx.x; i < K; i += kSelThreads) orow[i] = -1;
+  // keep the hint while it passes a comfortable number of candidates; raise
+  // it to rank 2 K' when too many pass
+  if (c_tot > 4 * take) {
+    const uint32_t top2 = block_select_top<8>(key, elig, 2 * take, hist, sh, tmpu);
+    uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (top2 >> e & 1u) m = min(m, key[e]);
+    m = block_min_u32<kSelThreads>(m, tmpu);
+    if (threadIdx.x == 0) ws.hint[rowid] = m;
+  }
+}
+
 size_t topk_workspace_bytes(const spin_config&, int R, int rows, int max_blocks) {
   return (size_t)ws_size(R * rows, max_blocks);
 }
@@ -338,11 +440,21 @@ size_t step_workspace_bytes(const spin_config& c, int R, int rows, int max_block
          (size_t)align256(4LL * R);
 }
 
+CandSink topk_sink(void* wsp, int R, int rows, int max_blocks) {
+  const TopkWs ws = carve(wsp, R * rows, max_blocks);
+  return CandSink{ws.hint, ws.cand, ws.pcnt, ws.n_cap, max_blocks};
+}
+
 hipError_t launch_topk(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                        const int32_t* sel, const int32_t* n_sel, int32_t* out, void* wsp, size_t,
-                       hipStream_t st) {
+                       hipStream_t st, bool prefiltered) {
   const int rows_total = b.batch * b.n_rows;
   const TopkWs ws = carve(wsp, rows_total, b.max_blocks);
+  if (prefiltered) {
+    hipLaunchKernelGGL(k_topk_select_pages, dim3(rows_total), dim3(kSelThreads), 0, st, c.topk,
+                       b.n_rows, b.max_blocks, b.ctx_len, b.q_pos, z, z_ld, sel, n_sel, out, ws);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_topk_filter, dim3(ws.n_chunks, rows_total), dim3(kFilterThreads), 0, st,
                      b.n_rows, b.max_blocks, b.ctx_len, b.q_pos, z, z_ld, sel, n_sel, ws);
   hipLaunchKernelGGL(k_topk_select, dim3(rows_total), dim3(kSelThreads), 0, st, c.topk, b.n_rows,

@@ -272,12 +272,16 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
                                              qsnap), "spin_step/predict"));
   SPIN_CHECK(hip_status(spin::launch_select(*cfg, *bt, io->S, io->budget, io->row_code, io->sel,
                                             io->n_sel, st), "spin_step/select"));
+  // where the score kernel can, it also applies the top-K threshold filter
+  const bool prefilter = spin::score_filters(*cfg, *bt);
+  const spin::CandSink sink = spin::topk_sink(io->workspace, bt->batch, bt->n_rows, bt->max_blocks);
   SPIN_CHECK(hip_status(spin::launch_score(*cfg, *bt, io->q, io->w, io->k_pages, io->k_scale,
                                            io->page_table, io->pt_ld, io->sel, io->n_sel, io->z,
-                                           io->z_ld, st), "spin_step/score"));
+                                           io->z_ld, st, prefilter ? &sink : nullptr),
+                        "spin_step/score"));
   SPIN_CHECK(hip_status(spin::launch_topk(*cfg, *bt, io->z, io->z_ld, io->sel, io->n_sel,
-                                          io->topk_idx, io->workspace, io->workspace_bytes, st),
-                        "spin_step/topk"));
+                                          io->topk_idx, io->workspace, io->workspace_bytes, st,
+                                          prefilter), "spin_step/topk"));
   if (defer_ema) return SPIN_OK;
   // EMA and counter advance in one kernel: it reads q positions from the
   // snapshot, so advancing q_pos_mut (normally the same array as bt->q_pos)

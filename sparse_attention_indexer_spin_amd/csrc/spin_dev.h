@@ -195,38 +195,52 @@ constexpr int kSelThreads = 1024;
 
 // ---------------------------------------------------------------------------
 // Block-level selection of the k largest u32 keys among flagged elements
-// (ties: lower element index).  Thread t owns elements t*EPT .. t*EPT+EPT-1.
+// (ties: lower element index).  Thread t of NT owns elements t*EPT ..
+// t*EPT+EPT-1 (EPT <= 32).
 // On return, bit e of the result mask marks the chosen elements.
 // ---------------------------------------------------------------------------
 
-template <int EPT>
+template <int EPT, int NT = kSelThreads>
 __device__ uint32_t block_select_top(const uint32_t (&key)[EPT], uint32_t elig, int k,
                                      int* hist, int* sh, uint32_t* tmpu) {
+  // hist: 512 ints (two histograms used in turn), sh: 32 ints, tmpu: 2 NT/64
   if (k <= 0) return 0u;
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   uint32_t mx = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
   for (int e = 0; e < EPT; ++e)
     if (elig >> e & 1u) { mx = max(mx, key[e]); mn = min(mn, key[e]); }
-  mx = block_max_u32<kSelThreads>(mx, tmpu);
-  mn = block_min_u32<kSelThreads>(mn, tmpu);
+  // max and min in one exchange; both histograms cleared under the same barrier
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  if (lane == 0) { tmpu[wid] = mx; tmpu[NW + wid] = mn; }
+  for (int i = threadIdx.x; i < 512; i += NT) hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NW; ++i) { mx = max(mx, tmpu[i]); mn = min(mn, tmpu[NW + i]); }
   int nb = (mx == mn) ? 0 : 32 - __clz(mx ^ mn);
   uint64_t prefix = ((uint64_t)mx >> nb) << nb;
+  int cur = 0;
   while (nb > 0) {
     const int db = nb < 8 ? nb : 8, pos = nb - db;
-    for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
+    int* h = hist + 256 * cur;
 #pragma unroll
     for (int e = 0; e < EPT; ++e)
       if ((elig >> e & 1u) && ((uint64_t)key[e] >> nb) == (prefix >> nb))
-        atomicAdd(&hist[(key[e] >> pos) & ((1u << db) - 1u)], 1);
+        atomicAdd(&h[(key[e] >> pos) & ((1u << db) - 1u)], 1);
     __syncthreads();
-    if (threadIdx.x < 64) radix_pick_digit(hist, k, sh);
+    // wave 0 picks the digit while the others clear the other histogram (its
+    // last reader was the previous pass's pick, before the previous barrier)
+    if (threadIdx.x < 64) radix_pick_digit(h, k, sh + 24 + 4 * cur);
+    else
+      for (int i = threadIdx.x - 64; i < 256; i += NT - 64) hist[256 * (cur ^ 1) + i] = 0;
     __syncthreads();
-    const int d = sh[0], cnt = sh[2];
-    k = sh[1];
-    __syncthreads();
+    const int d = sh[24 + 4 * cur], cnt = sh[26 + 4 * cur];
+    k = sh[25 + 4 * cur];
     prefix |= (uint64_t)d << pos;
     nb = pos;
+    cur ^= 1;
     if (cnt == k) break;  // every key of this bin is taken
   }
   const uint64_t hp = prefix >> nb;
@@ -235,7 +249,7 @@ __device__ uint32_t block_select_top(const uint32_t (&key)[EPT], uint32_t elig, 
   for (int e = 0; e < EPT; ++e)
     if ((elig >> e & 1u) && ((uint64_t)key[e] >> nb) == hp) ++eq;
   int tot;
-  int rank = block_excl_scan<kSelThreads>(eq, sh + 4, &tot);
+  int rank = block_excl_scan<NT>(eq, sh + 4, &tot);
   uint32_t out = 0u;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {

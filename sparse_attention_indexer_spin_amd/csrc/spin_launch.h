@@ -6,6 +6,18 @@
 
 namespace spin {
 
+// Where a score kernel that also filters for the top-K writes its candidates:
+// per (row, selected block k) the slots of that block whose z key is >= the
+// row's hint, compacted at cand[row * cand_ld + 64 k ..] in slot order as
+// (key, slot) pairs, and their count at pcnt[row * pcnt_ld + k].
+struct CandSink {
+  const uint32_t* hint;  // [rows_total]
+  uint2* cand;
+  int32_t* pcnt;
+  int64_t cand_ld;
+  int pcnt_ld;
+};
+
 // qpos_snap (optional, [R]): predict records the step's q_pos there; the
 // fused EMA + advance of a whole step reads it instead of q_pos.
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
@@ -14,13 +26,18 @@ hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
                          hipStream_t st);
+// With a non-null `sink`, kernels that can (score_filters()) also write the
+// top-K candidates; the caller then runs launch_topk with `prefiltered`.
 hipError_t launch_score(const spin_config& c, const spin_batch& b, const void* q, const float* w,
                         const void* kp, const float* ks, const int32_t* pt, int64_t pt_ld,
                         const int32_t* sel, const int32_t* n_sel, float* z, int64_t z_ld,
-                        hipStream_t st);
+                        hipStream_t st, const CandSink* sink = nullptr);
+bool score_filters(const spin_config& c, const spin_batch& b);
 hipError_t launch_topk(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                        const int32_t* sel, const int32_t* n_sel, int32_t* out, void* ws,
-                       size_t ws_bytes, hipStream_t st);
+                       size_t ws_bytes, hipStream_t st, bool prefiltered = false);
+// The candidate sink inside a top-K workspace.
+CandSink topk_sink(void* ws, int R, int rows, int max_blocks);
 size_t topk_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks);
 // A whole step's workspace: the top-K region, then the step's q_pos snapshot.
 size_t step_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks);
