@@ -546,13 +546,19 @@ struct QFull<0, NS> {  // fp8 keys: NS E4M3 terms per query value
   v8i part[NS][4];
   float wq[4][4];
 
-  v4u raw[4][4];  // bf16 queries between fetch() and convert()
+  v4u raw[4][4];    // bf16 queries between fetch() and convert()
+  float wraw[4][4];  // head weights between fetch() and convert()
 
-  // Issue the loads of a bf16 query (fp32 queries are read by convert()).
+  // Issue the loads of the head weights and of a bf16 query (fp32 queries are
+  // read by convert()), so that convert() need not wait for later loads.
   __device__ __forceinline__ void fetch(const ScoreParams& p, int q_bf16, int rowid) {
-    if (!q_bf16) return;
     const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
     const int64_t qbase = (int64_t)rowid * 64;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wraw[t][i] = p.w[qbase + 16 * t + 4 * g + i];
+    if (!q_bf16) return;
     const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -619,7 +625,7 @@ struct QFull<0, NS> {  // fp8 keys: NS E4M3 terms per query value
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ei = __shfl(e, 4 * g + i, 64);
-        wq[t][i] = ldexpf(p.w[qbase + 16 * t + 4 * g + i], -ei);
+        wq[t][i] = ldexpf(wraw[t][i], -ei);
       }
     }
   }
@@ -812,8 +818,12 @@ __attribute__((amdgpu_waves_per_eu(3, 8))) void k_score_slots(ScoreParams p) {
 // lane groups leaves lane l with slot l's total, which it scales and stores.
 // No LDS staging and no barriers: waves progress independently.
 // ---------------------------------------------------------------------------
-template <int NS, int QB, int P>
+template <int NS, int QB, int P, bool Span>
 __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
+  // Span: a wave's range may cross requests (fewer waves than requests), so
+  // the query is reloaded inside the loop; without it (at least one wave per
+  // request, ranges aligned to requests) the loop keeps no reload state and
+  // the kernel fits two waves per SIMD
   extern __shared__ int pre_dyn[];
   __shared__ int tmp[32];
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
@@ -865,7 +875,7 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
       load_page(dd.get(p, tb, min(cur + P - 1, hi - 1)).page, kb[(u + P - 1) % P],
                 sc[(u + P - 1) % P]);
       const Desc d = db.get(p, tb, cur);
-      if (d.r != q_req) {  // only without request-aligned ranges
+      if (Span && d.r != q_req) {
         q_req = d.r;
         Q.load(p, QB, q_req);
         if (p.sink.hint) hint = p.sink.hint[q_req];
@@ -965,11 +975,17 @@ static void launch_slots(const ScoreParams& p, hipStream_t st) {
 
 template <int NS, int QB>
 static void launch_wave(const ScoreParams& p, hipStream_t st) {
-  constexpr int P = 2;  // 234 VGPRs: two waves per SIMD
-  const auto kern = k_score_wave<NS, QB, P>;
+  constexpr int P = 2;  // pages in flight per wave (two waves per SIMD)
   const size_t dyn = sizeof(int) * 2 * (p.R + 1);
-  const int g = min(resident_workgroups((const void*)kern, 256, dyn), p.R * p.max_blocks);
-  hipLaunchKernelGGL(kern, dim3(g), dim3(256), dyn, st, p);
+  const auto aligned = k_score_wave<NS, QB, P, false>;
+  const int g = min(resident_workgroups((const void*)aligned, 256, dyn), p.R * p.max_blocks);
+  if (4 * g >= p.R) {  // a wave per request at least: request-aligned ranges
+    hipLaunchKernelGGL(aligned, dim3(g), dim3(256), dyn, st, p);
+    return;
+  }
+  const auto span = k_score_wave<NS, QB, P, true>;
+  const int g2 = min(resident_workgroups((const void*)span, 256, dyn), p.R * p.max_blocks);
+  hipLaunchKernelGGL(span, dim3(g2), dim3(256), dyn, st, p);
 }
 
 template <int KT, int NS, int QB>

@@ -39,7 +39,7 @@ class SpinLayer:
         self.req_id = torch.arange(batch, **i32)
         self.err = torch.zeros(1, **i32)
         nws = api.workspace_bytes(self.cfg, batch, n_rows, max_blocks)
-        self.workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
+        self.workspace = torch.zeros(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
         self.n_pages = 1
         self._bt = None
 

@@ -170,6 +170,37 @@ def test_score_parity(key, q, integer, rows):
     assert int(keep["err"].item()) == 0
 
 
+def test_score_parity_more_requests_than_waves():
+    """3,000 short requests: more requests than the fp8 kernel has waves, so a
+    wave's range crosses requests and the query is reloaded inside the loop."""
+    banner("score: more requests than waves")
+    A = api()
+    li = _small("fp8", "bf16", N=tuple(64 + (r * 37) % 200 for r in range(3000)))
+    w = li.w
+    R, mb = w.batch, w.max_blocks
+    sel, n_sel = G.make_selection(R, torch.tensor([O.n_blocks(int(c)) for c in li.ctx]), mb,
+                                  0.5, seed=7)
+    pages, scale, pt = device_keys(li)
+    bt, keep = _batch(li.ctx.numpy(), li.pos[0].numpy(), [1] * R, 1, mb, n_pages=pages.shape[0])
+    cfg = A.config(topk=512, sparsity_bp=4000, key_dtype=pages.dtype, q_dtype=torch.bfloat16)
+    z = torch.full((R, 1, 64 * mb), -3.0, device=DEV)
+    A.spin_sparse_index_score(cfg, bt, li.q[1].to(DEV).contiguous(), li.weights.to(DEV), pages,
+                              scale, pt, sel.to(DEV), n_sel.to(DEV), z)
+    z = z.cpu().numpy()
+    np_pages, np_scale = li.np_pages(), li.keys.scale.numpy()
+    q_all = li.np_q(1)
+    for r in range(R):
+        N = int(li.ctx[r])
+        blocks = sel[r, :int(n_sel[r])].numpy()
+        slots = O.union_slots(blocks, N)
+        keys = O.gather_keys(np_pages, li.keys.page_table[r].numpy(), slots, "fp8", np_scale)
+        want = O.index_scores(O.decode_q(q_all[r], "bf16")[0], li.weights[r, 0].numpy(), keys)
+        comp = np.searchsorted(blocks, slots // 64) * 64 + slots % 64
+        ok, worst = z_close(z[r, 0, comp], want, TOL["fp8"])
+        assert ok, (r, worst)
+    assert int(keep["err"].item()) == 0
+
+
 # ---------------------------------------------------------------------------
 # stage 3b: top-K
 # ---------------------------------------------------------------------------
