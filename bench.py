@@ -70,14 +70,16 @@ class Inputs:
         torch.cuda.synchronize()
 
 
-def algorithmic_score_bytes(w: G.Workload, keys_scored_per_row: float, n_blocks_sel: float):
-    """Bytes the score stage must move per launch (skipped blocks not counted)."""
+def algorithmic_score_bytes(w: G.Workload, slots: float, n_blocks_sel: float):
+    """Bytes the score stage must move per launch (skipped blocks not counted):
+    each scored slot's key (+ scale) once, its z once per verifier row, the
+    block list and page-table entries, and every row's query and weights."""
     kb = {"fp8": 128 + 4, "bf16": 256, "f32": 512}[w.key_dtype]
     qb = {"bf16": 2, "f32": 4}[w.q_dtype]
     per_slot = kb + 4 * w.rows                        # key (+ scale) + z writes
     per_block = 8                                     # sel entry + page-table entry
     per_req = w.rows * 64 * (128 * qb + 4)            # q and w
-    return keys_scored_per_row * per_slot + n_blocks_sel * per_block + w.batch * per_req
+    return slots * per_slot + n_blocks_sel * per_block + w.batch * per_req
 
 
 def _timed_us(fn, reps: int, stream) -> float:
@@ -254,7 +256,7 @@ def main():
     res = run_gpu(inp, sp, args.steps, args.warmup, stage_reps=args.stage_reps)
     score_us = res["stage_us"]["score"]
     keys_row = res["keys_per_step"]
-    score_bytes = algorithmic_score_bytes(w, keys_row, res["n_sel"] * w.rows)
+    score_bytes = algorithmic_score_bytes(w, keys_row // w.rows, res["n_sel"])
     achieved = score_bytes / (score_us * 1e-6) / 1e9
     value = keys_row / (res["ms_per_step"] * 1e-3)
     out = {
