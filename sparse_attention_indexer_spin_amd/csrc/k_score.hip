@@ -68,6 +68,19 @@ struct ItemTable {
 __device__ __forceinline__ ItemTable build_items(const ScoreParams& p, int* pre, int* tmp,
                                                 int* ne_pre = nullptr, int* n_ne = nullptr) {
   constexpr int NT = 256;
+  if (p.R <= 64) {  // one wave: one load round and in-wave scans, then one barrier
+    if (threadIdx.x < 64) {
+      const int r = threadIdx.x;
+      const int c = r < p.R ? items_of(p, r) : 0;
+      const int ci = wave_incl_scan(c), ne = wave_incl_scan(c > 0 ? 1 : 0);
+      if (r < p.R) pre[r] = ci - c;
+      if (r == 63) { pre[p.R] = ci; tmp[0] = ne; }
+      if (ne_pre && r < p.R) ne_pre[r] = ne - (c > 0 ? 1 : 0);
+    }
+    __syncthreads();
+    if (n_ne) *n_ne = tmp[0];
+    return ItemTable{pre, pre[p.R]};
+  }
   const int per = (p.R + NT - 1) / NT;  // requests per thread (R <= SPIN_MAX_BATCH)
   const int r0 = threadIdx.x * per;
   int cnt[SPIN_MAX_BATCH / NT];
@@ -495,20 +508,19 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
     q_req = -1;
   }
   if (lo >= hi) return;
-  QFull<KT, NS> Q;
-  if (q_req >= 0) Q.fetch(p, QB, q_req * p.rows + row);
+  // descriptors, then the first page, then the query: the descriptor loads do
+  // not queue behind the query loads, and the query arrives while the page does
   DescBatch db;
   db.init(p, tb, lo);
-  if (q_req < 0) {
-    q_req = __builtin_amdgcn_readfirstlane(db.mine.r);
-    Q.fetch(p, QB, q_req * p.rows + row);
-  }
+  if (q_req < 0) q_req = __builtin_amdgcn_readfirstlane(db.mine.r);
   DescBatch dd = db;
   v4u kb[P][PR::kRegs];
   float sc[P];
 #pragma unroll
   for (int u = 0; u < P - 1; ++u)
     PR::load(p, dd.get(p, tb, min(lo + u, hi - 1)).page, kb[u], sc[u]);
+  QFull<KT, NS> Q;
+  Q.fetch(p, QB, q_req * p.rows + row);
   Q.convert(p, QB, q_req * p.rows + row);
   int rowid = q_req * p.rows + row;
   uint32_t hint = p.sink.hint ? p.sink.hint[rowid] : 0u;
