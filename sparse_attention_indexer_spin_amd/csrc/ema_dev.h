@@ -1,0 +1,138 @@
+// EMA update device code (Algorithm 1 steps 8-10 of "SPIN: Shadow Predictive
+// Indexer for Sparse Attention"; deferred in-order replay of Sec. 3.2.2),
+// shared by the EMA kernel and the kernel that runs it beside the top-K.
+#pragma once
+#include "spin_dev.h"
+
+namespace spin {
+
+struct EmaCtx {
+  float a, b;
+  int L, N, q, j, k, ns;
+  const float* zb;  // z of this request, row 0
+  int64_t z_ld;
+  const int32_t* sel;  // this request's selected blocks
+};
+
+__device__ __forceinline__ float ema_step(float x, float zv, float a, float b) {
+  return __fadd_rn(__fmul_rn(a, x), __fmul_rn(b, zv));
+}
+
+__device__ __forceinline__ void ema_offset(const EmaCtx& e, int s0, float* Dr) {
+  if (s0 >= e.N) return;
+  const int o = e.q - s0;
+  float d = 0.0f;
+  bool upd = false;
+  for (int row = 0; row < e.L; ++row) {
+    const int slot = s0 + row;
+    if (slot < 0 || slot >= e.N) continue;
+    const int blk = slot >> 6;
+    int kk = -1;
+    if (blk == e.j) kk = e.k;
+    else if (blk == e.j + 1 && e.k + 1 < e.ns && e.sel[e.k + 1] == e.j + 1) kk = e.k + 1;
+    if (kk < 0) continue;
+    if (!upd) d = Dr[o];
+    d = ema_step(d, e.zb[row * e.z_ld + kk * 64 + (slot & 63)], e.a, e.b);
+    upd = true;
+  }
+  if (upd) Dr[o] = d;
+}
+
+constexpr int kEmaBlocksPerWave = 4;
+
+struct EmaArgs {
+  float alpha;
+  int rows, max_blocks;
+  const int32_t* ctx;
+  const int32_t* qpos;      // the step's q positions (a snapshot when advancing)
+  const int32_t* n_valid;
+  const float* z;
+  int64_t z_ld;
+  const int32_t* sel;
+  const int32_t* n_sel;
+  float* V;
+  int64_t v_ld;
+  float* D;
+  int64_t d_ld;
+  int32_t* qpos_out;        // optional counter advance
+  int32_t* step_out;
+};
+
+// One wave: the EMA update of selected blocks k0 .. k0 + kEmaBlocksPerWave - 1
+// of request r; `advance`: this thread also advances r's counters.
+__device__ __forceinline__ void ema_wave(const EmaArgs& A, int r, int k0, bool advance) {
+  const int rows = A.rows, max_blocks = A.max_blocks;
+  const int32_t* n_valid = A.n_valid;
+  const float* z = A.z;
+  const int64_t z_ld = A.z_ld, v_ld = A.v_ld, d_ld = A.d_ld;
+  const int32_t* sel = A.sel;
+  float* V = A.V;
+  float* D = A.D;
+  const int lane = threadIdx.x & 63;
+  const int N = A.ctx[r], q = A.qpos[r];
+  if (advance) {
+    if (A.qpos_out) A.qpos_out[r] = q + (n_valid ? n_valid[r] : rows);
+    if (A.step_out) A.step_out[r] += 1;
+  }
+  const float alpha = A.alpha;
+  const int32_t* n_sel = A.n_sel;
+  if (request_error(N, q, rows, max_blocks, v_ld, d_ld)) return;
+  const int ns = clamp_nsel(n_sel[r], max_blocks);
+  if (k0 >= ns) return;
+  int L = n_valid ? n_valid[r] : rows;
+  L = L < 0 ? 0 : (L > rows ? rows : L);
+  if (L == 0) return;
+  const int32_t* sr = sel + (int64_t)r * max_blocks;
+  const float a = alpha, b = __fsub_rn(1.0f, alpha);
+  const float* zb = z + (int64_t)r * rows * z_ld;
+  float* Vr = V + (int64_t)r * v_ld;
+  float* Dr = D + (int64_t)r * d_ld;
+  if (L == 1) {
+    // one observation per slot: V[i] and D[q - i] from row 0, loads batched
+    float vv[kEmaBlocksPerWave], dd[kEmaBlocksPerWave], zz[kEmaBlocksPerWave];
+    int ii[kEmaBlocksPerWave];
+#pragma unroll
+    for (int u = 0; u < kEmaBlocksPerWave; ++u) {
+      const int k = k0 + u;
+      const int j = k < ns ? sr[k] : -1;
+      const int i = j * 64 + lane;
+      const bool ok = k < ns && j >= 0 && j < max_blocks && i < N;
+      ii[u] = ok ? i : -1;
+      vv[u] = ok ? Vr[i] : 0.0f;
+      dd[u] = ok ? Dr[q - i] : 0.0f;
+      zz[u] = ok ? zb[(int64_t)k * 64 + lane] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kEmaBlocksPerWave; ++u) {
+      if (ii[u] < 0) continue;
+      Vr[ii[u]] = ema_step(vv[u], zz[u], a, b);
+      Dr[q - ii[u]] = ema_step(dd[u], zz[u], a, b);
+    }
+    return;
+  }
+  for (int u = 0; u < kEmaBlocksPerWave; ++u) {
+    const int k = k0 + u;
+    if (k >= ns) break;
+    EmaCtx e;
+    e.a = a; e.b = b;
+    e.L = L; e.N = N; e.q = q; e.k = k; e.ns = ns;
+    e.j = sr[k];
+    if (e.j < 0 || e.j >= max_blocks) continue;
+    e.zb = zb;
+    e.z_ld = z_ld;
+    e.sel = sr;
+    const int i = e.j * 64 + lane;
+    if (i < N) {
+      float v = Vr[i];
+      for (int row = 0; row < L; ++row) v = ema_step(v, zb[row * z_ld + (int64_t)k * 64 + lane], a, b);
+      Vr[i] = v;
+    }
+    ema_offset(e, i, Dr);
+    if (lane < L - 1) {
+      const bool prev_selected = k > 0 && sr[k - 1] == e.j - 1;
+      if (!prev_selected) ema_offset(e, e.j * 64 - 1 - lane, Dr);
+    }
+  }
+}
+
+}  // namespace spin

@@ -66,10 +66,14 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2: one workgroup per (request, verifier row).
+// Stage 2: one workgroup per (request, verifier row); kSelectThreads threads
+// (4 waves: the selection is a chain of block-wide steps, each ending in a
+// barrier, which costs less over fewer waves), EPT blocks per thread.
 // ---------------------------------------------------------------------------
+constexpr int kSelectThreads = 256;
+
 template <int EPT>
-__global__ __launch_bounds__(kSelThreads) void k_select(
+__global__ __launch_bounds__(kSelectThreads) void k_select(
     int K, int sparsity_bp, int explore_bp, int layer, uint32_t seed_lo, uint32_t seed_hi,
     int rows, int max_blocks, const int32_t* __restrict__ ctx, const int32_t* __restrict__ qpos,
     const int32_t* __restrict__ step, const int32_t* __restrict__ req_id,
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         else { key[e] = float_key(Srow[j]); elig |= 1u << e; }
       }
     }
-    const uint32_t ranked = block_select_top<EPT>(key, elig, n_r, hist, sh, tmpu);
+    const uint32_t ranked = block_select_top<EPT, kSelectThreads>(key, elig, n_r, hist, sh, tmpu);
 #pragma unroll
     for (int e = 0; e < EPT; ++e)
       if (ranked >> e & 1u) c[e] = SPIN_CODE_RANKED;
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
       for (int e = 0; e < EPT; ++e)
         key[e] = ~philox_word0((uint32_t)(j0 + e), (uint32_t)t, (uint32_t)layer,
                                (uint32_t)req_id[r], seed_lo, seed_hi);
-      const uint32_t expl = block_select_top<EPT>(key, elig, n_e, hist, sh, tmpu);
+      const uint32_t expl = block_select_top<EPT, kSelectThreads>(key, elig, n_e, hist, sh, tmpu);
 #pragma unroll
       for (int e = 0; e < EPT; ++e)
         if (expl >> e & 1u) c[e] = SPIN_CODE_EXPLORED;
@@ -136,7 +140,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
 #pragma unroll
   for (int e = 0; e < EPT; ++e)
     if (j0 + e < B) crow[j0 + e] = c[e];
-  if (compact) compact_blocks<EPT>(chosen, max_blocks, sel + (int64_t)r * max_blocks, n_sel + r, sh);
+  if (compact)
+    compact_blocks<EPT, kSelectThreads>(chosen, max_blocks, sel + (int64_t)r * max_blocks,
+                                        n_sel + r, sh);
 }
 
 // Union of the verifier rows' masks (Sec. 3.2.2), one workgroup per request.
@@ -199,23 +205,37 @@ static void select_t(const spin_config& c, const spin_batch& b, const float* S,
                      const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
                      hipStream_t st) {
   const int compact = b.n_rows == 1;
-  hipLaunchKernelGGL(k_select<EPT>, dim3(b.n_rows, b.batch), dim3(kSelThreads), 0, st, c.topk,
-                     c.sparsity_bp, c.explore_bp, c.layer, (uint32_t)(c.seed & 0xFFFFFFFFu),
-                     (uint32_t)(c.seed >> 32), b.n_rows, b.max_blocks, b.ctx_len, b.q_pos,
-                     b.step, b.req_id, S, budget, code, sel, n_sel, compact);
-  if (!compact)
-    hipLaunchKernelGGL(k_union<EPT>, dim3(b.batch), dim3(kSelThreads), 0, st, b.n_rows,
-                       b.max_blocks, b.ctx_len, b.q_pos, code, sel, n_sel);
+  hipLaunchKernelGGL(k_select<EPT>, dim3(b.n_rows, b.batch), dim3(kSelectThreads), 0, st,
+                     c.topk, c.sparsity_bp, c.explore_bp, c.layer,
+                     (uint32_t)(c.seed & 0xFFFFFFFFu), (uint32_t)(c.seed >> 32), b.n_rows,
+                     b.max_blocks, b.ctx_len, b.q_pos, b.step, b.req_id, S, budget, code, sel,
+                     n_sel, compact);
+}
+
+template <int EPT>
+static void union_t(const spin_batch& b, uint8_t* code, int32_t* sel, int32_t* n_sel,
+                    hipStream_t st) {
+  hipLaunchKernelGGL(k_union<EPT>, dim3(b.batch), dim3(kSelThreads), 0, st, b.n_rows,
+                     b.max_blocks, b.ctx_len, b.q_pos, code, sel, n_sel);
 }
 
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
                          hipStream_t st) {
-  const int ept = (b.max_blocks + kSelThreads - 1) / kSelThreads;
+  const int ept = (b.max_blocks + kSelectThreads - 1) / kSelectThreads;
   if (ept <= 1) select_t<1>(c, b, S, budget, code, sel, n_sel, st);
   else if (ept <= 2) select_t<2>(c, b, S, budget, code, sel, n_sel, st);
   else if (ept <= 4) select_t<4>(c, b, S, budget, code, sel, n_sel, st);
-  else select_t<8>(c, b, S, budget, code, sel, n_sel, st);
+  else if (ept <= 8) select_t<8>(c, b, S, budget, code, sel, n_sel, st);
+  else if (ept <= 16) select_t<16>(c, b, S, budget, code, sel, n_sel, st);
+  else select_t<32>(c, b, S, budget, code, sel, n_sel, st);
+  if (b.n_rows > 1) {  // union of the rows' masks
+    const int eu = (b.max_blocks + kSelThreads - 1) / kSelThreads;
+    if (eu <= 1) union_t<1>(b, code, sel, n_sel, st);
+    else if (eu <= 2) union_t<2>(b, code, sel, n_sel, st);
+    else if (eu <= 4) union_t<4>(b, code, sel, n_sel, st);
+    else union_t<8>(b, code, sel, n_sel, st);
+  }
   return hipGetLastError();
 }
 

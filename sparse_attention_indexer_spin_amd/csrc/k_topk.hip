@@ -18,6 +18,7 @@
 // that about 2K candidates pass the next step's filter: scores of a layer are
 // strongly correlated from one decode step to the next, the observation the
 // method itself rests on.  Its value only affects speed, never results.
+#include "ema_dev.h"
 #include "spin_dev.h"
 #include "spin_launch.h"
 
@@ -340,18 +341,27 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(
 // ---------------------------------------------------------------------------
 constexpr int kPagesPerThread = SPIN_MAX_BLOCKS / kSelThreads;
 
-__global__ __launch_bounds__(kSelThreads) void k_topk_select_pages(
-    int K, int rows, int max_blocks, const int32_t* __restrict__ ctx,
-    const int32_t* __restrict__ qpos, const float* __restrict__ z, int64_t z_ld,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
-    int32_t* __restrict__ out, TopkWs ws) {
-  __shared__ uint32_t lkey[kCap];
-  __shared__ int32_t lslot[kCap];
-  __shared__ int32_t lsrc[kCap];  // candidate q sits at cand[lsrc[q]]
-  __shared__ int hist[512];
-  __shared__ int sh[32];
-  __shared__ uint32_t tmpu[32];
-  const int rowid = blockIdx.x, r = rowid / rows;
+struct PagesShared {
+  uint32_t lkey[kCap];
+  int32_t lslot[kCap];
+  int32_t lsrc[kCap];  // candidate q sits at cand[lsrc[q]]
+  int hist[512];
+  int sh[32];
+  uint32_t tmpu[32];
+};
+
+__device__ void topk_pages_row(int rowid, int K, int rows, int max_blocks,
+                               const int32_t* __restrict__ ctx, const int32_t* __restrict__ qpos,
+                               const float* __restrict__ z, int64_t z_ld,
+                               const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
+                               int32_t* __restrict__ out, const TopkWs& ws, PagesShared& L) {
+  uint32_t* lkey = L.lkey;
+  int32_t* lslot = L.lslot;
+  int32_t* lsrc = L.lsrc;
+  int* hist = L.hist;
+  int* sh = L.sh;
+  uint32_t* tmpu = L.tmpu;
+  const int r = rowid / rows;
   int32_t* orow = out + (int64_t)rowid * K;
   const int N = ctx[r];
   const int n = row_candidates(N, qpos[r], rows, max_blocks, n_sel, r);
@@ -431,6 +441,41 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select_pages(
   }
 }
 
+__global__ __launch_bounds__(kSelThreads) void k_topk_select_pages(
+    int K, int rows, int max_blocks, const int32_t* __restrict__ ctx,
+    const int32_t* __restrict__ qpos, const float* __restrict__ z, int64_t z_ld,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
+    int32_t* __restrict__ out, TopkWs ws) {
+  __shared__ PagesShared L;
+  topk_pages_row(blockIdx.x, K, rows, max_blocks, ctx, qpos, z, z_ld, sel, n_sel, out, ws, L);
+}
+
+// The top-K of a whole step and its EMA update (+ counter advance) in one
+// launch, because neither reads what the other writes: blocks [0, rows_total)
+// run the per-row select (dispatched first), the others the EMA, ema_x of
+// them per request, sized to fill the CUs the few select workgroups leave
+// idle (one workgroup per CU: the select's LDS).
+__global__ __launch_bounds__(kSelThreads) void k_topk_ema(
+    int K, int rows, int max_blocks, const int32_t* __restrict__ ctx,
+    const int32_t* __restrict__ qpos, const float* __restrict__ z, int64_t z_ld,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
+    int32_t* __restrict__ out, TopkWs ws, int rows_total, EmaArgs A, int ema_x) {
+  __shared__ PagesShared L;
+  if ((int)blockIdx.x < rows_total) {
+    topk_pages_row(blockIdx.x, K, rows, max_blocks, ctx, qpos, z, z_ld, sel, n_sel, out, ws, L);
+    return;
+  }
+  // ema_x blocks per request; each wave strides over the request's selected
+  // blocks kEmaBlocksPerWave at a time
+  const int e = blockIdx.x - rows_total, r = e / ema_x, bx = e % ema_x;
+  constexpr int kWaves = kSelThreads / 64;
+  const int stride = ema_x * kWaves * kEmaBlocksPerWave;
+  const int k_end = clamp_nsel(A.n_sel[r], A.max_blocks);
+  int k0 = (bx * kWaves + (int)(threadIdx.x >> 6)) * kEmaBlocksPerWave;
+  ema_wave(A, r, k0, bx == 0 && threadIdx.x == 0);
+  for (k0 += stride; k0 < k_end; k0 += stride) ema_wave(A, r, k0, false);
+}
+
 size_t topk_workspace_bytes(const spin_config&, int R, int rows, int max_blocks) {
   return (size_t)ws_size(R * rows, max_blocks);
 }
@@ -438,6 +483,25 @@ size_t topk_workspace_bytes(const spin_config&, int R, int rows, int max_blocks)
 size_t step_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks) {
   return (size_t)align256((int64_t)topk_workspace_bytes(c, R, rows, max_blocks)) +
          (size_t)align256(4LL * R);
+}
+
+hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const float* z,
+                           int64_t z_ld, const int32_t* sel, const int32_t* n_sel, int32_t* out,
+                           void* wsp, const int32_t* n_valid, float* V, int64_t v_ld, float* D,
+                           int64_t d_ld, const int32_t* qpos_snap, int32_t* qpos_out,
+                           int32_t* step_out, hipStream_t st) {
+  const int rows_total = b.batch * b.n_rows;
+  const TopkWs ws = carve(wsp, rows_total, b.max_blocks);
+  constexpr int per_block = (kSelThreads / 64) * kEmaBlocksPerWave;
+  const int most = (b.max_blocks + per_block - 1) / per_block;
+  const int free_cus = resident_workgroups((const void*)k_topk_ema, kSelThreads) - rows_total;
+  const int ema_x = max(1, min(most, free_cus / max(1, b.batch)));
+  const EmaArgs A{c.ema_alpha, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap, n_valid, z, z_ld,
+                  sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out};
+  hipLaunchKernelGGL(k_topk_ema, dim3(rows_total + ema_x * b.batch), dim3(kSelThreads), 0, st,
+                     c.topk, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap, z, z_ld, sel, n_sel,
+                     out, ws, rows_total, A, ema_x);
+  return hipGetLastError();
 }
 
 CandSink topk_sink(void* wsp, int R, int rows, int max_blocks) {

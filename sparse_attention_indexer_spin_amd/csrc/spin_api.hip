@@ -279,6 +279,14 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
                                            io->page_table, io->pt_ld, io->sel, io->n_sel, io->z,
                                            io->z_ld, st, prefilter ? &sink : nullptr),
                         "spin_step/score"));
+  if (prefilter && !defer_ema) {  // top-K beside the EMA update, one launch
+    SPIN_CHECK(hip_status(spin::launch_topk_ema(*cfg, *bt, io->z, io->z_ld, io->sel, io->n_sel,
+                                                io->topk_idx, io->workspace, io->n_valid, io->V,
+                                                io->v_ld, io->D, io->d_ld, qsnap, io->q_pos_mut,
+                                                io->step_mut, st),
+                          "spin_step/topk+ema"));
+    return SPIN_OK;
+  }
   SPIN_CHECK(hip_status(spin::launch_topk(*cfg, *bt, io->z, io->z_ld, io->sel, io->n_sel,
                                           io->topk_idx, io->workspace, io->workspace_bytes, st,
                                           prefilter), "spin_step/topk"));
