@@ -275,7 +275,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(w.name, sp),
-                     "kernel": "spin::k_score_slots" if w.rows == 1 else "spin::k_score_mfma",
+                     "kernel": "spin::k_score_f32" if w.key_dtype == "f32" else "spin::k_score_wave",
                      "algorithmic_bytes_per_launch": score_bytes,
                      "launch_us": score_us},
     }
