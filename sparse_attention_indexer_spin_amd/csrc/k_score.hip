@@ -191,6 +191,76 @@ struct DescBatch {
   }
 };
 
+// A stream's request-aligned run: blocks [lo, hi) of request r's selected
+// list, with that request's context length.
+struct Run {
+  int r, N, lo, hi;
+};
+
+// request_range() for one wave on its own when there are at most 64
+// requests: lane r loads request r's counters, in-wave scans give the
+// prefixes, and a ballot over the teams' first workers names the request of
+// worker bx.  One load round, no LDS and no barrier.  Needs gx >= the number
+// of requests with items (the caller guarantees gx >= R).
+__device__ __forceinline__ Run wave_run(const ScoreParams& p, int bx, int gx) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < p.R;
+  const int c = in ? items_of(p, lane) : 0;
+  const int n_ctx = in ? p.ctx[lane] : 0;
+  const int ci = wave_incl_scan(c), ne = wave_incl_scan(c > 0 ? 1 : 0);
+  const int total = rl(ci, 63), n_ne = rl(ne, 63);
+  Run run{0, 0, 0, 0};
+  if (total == 0) return run;
+  const int pre = ci - c, ne_pre = ne - (c > 0 ? 1 : 0);
+  // first worker of request r, as in request_range(); gx past the last request
+  const int first = in ? ne_pre + (int)((int64_t)(gx - n_ne) * pre / total) : gx;
+  const uint64_t m = __ballot(first <= bx);  // lanes 0 .. r (first() is non-decreasing)
+  const int r = 63 - __clzll(m);
+  const int f0 = rl(first, r), f1 = r + 1 < p.R ? rl(first, r + 1) : gx;
+  const int items = rl(c, r), w = f1 - f0, part = bx - f0;
+  run.r = r;
+  run.N = rl(n_ctx, r);
+  if (w <= 0 || items <= 0) return run;
+  // uniform results, kept in scalar registers
+  run.lo = __builtin_amdgcn_readfirstlane((int)((int64_t)part * items / w));
+  run.hi = __builtin_amdgcn_readfirstlane((int)((int64_t)(part + 1) * items / w));
+  return run;
+}
+
+// Descriptor cursor over one request's run: lane i describes block
+// base + i of the run (64 at a time); the request and its context length are
+// the run's.
+struct RunCursor {
+  int page, j, bad, base;
+  int r, N, hi;
+  __device__ __forceinline__ void init(const ScoreParams& p, int k) {
+    base = k;
+    const int kk = k + (int)(threadIdx.x & 63);
+    page = 0;
+    j = 0;
+    bad = 1;
+    if (kk < hi) {
+      j = p.sel[(int64_t)r * p.max_blocks + kk];
+      const int pg = (j >= 0 && j < p.max_blocks) ? p.pt[(int64_t)r * p.pt_ld + j] : -1;
+      bad = !(pg >= 0 && pg < p.n_pages);
+      page = bad ? 0 : pg;
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0), as in DescBatch
+  }
+  __device__ __forceinline__ Desc get(const ScoreParams& p, int k) {
+    if (k - base >= 64) init(p, k);
+    const int i = k - base;
+    return Desc{rl(page, i), rl(j, i), r, k, N, rl(bad, i)};
+  }
+};
+
+// Table-based cursor (runs may cross requests).
+struct TableCursor {
+  DescBatch b;
+  ItemTable tb;
+  __device__ __forceinline__ Desc get(const ScoreParams& p, int g) { return b.get(p, tb, g); }
+};
+
 // Value of lane l ^ 16 / l ^ 32 (VALU lane swaps, no LDS traffic).
 __device__ __forceinline__ float xor16(float v) {
   const int lane = threadIdx.x & 63;
@@ -486,39 +556,28 @@ struct PageRegs<1> {
 // selected blocks, and each of its waves loads the run's pages two deep into
 // registers and scores them for its row.  Span: a run may cross requests
 // (fewer streams than requests), so the query is reloaded inside the loop;
-// without it the loop keeps no reload state (two waves per SIMD).
+// without it the loop keeps no reload state (two waves per SIMD).  Mode:
+// kRunWave (at most 64 requests, request-aligned): each wave finds its run by
+// itself (wave_run); kRunTable: the workgroup first builds the item table in
+// LDS and runs stay request-aligned; kRunSpan: the table, and runs may cross
+// requests.
 // ---------------------------------------------------------------------------
-template <int KT, int NS, int QB, int P, bool Span>
-__global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
+
+// The page loop of one worker: blocks [lo, hi) through cursor `db`, query
+// row `row` of request q_req.  The descriptors are loaded first, then the
+// first page, then the query: the descriptor loads do not queue behind the
+// query loads, and the query arrives while the page does.
+template <int KT, int NS, int QB, int P, bool Span, class Cur>
+__device__ __forceinline__ void score_pages(const ScoreParams& p, Cur& db, int lo, int hi,
+                                            int q_req, int row) {
   using PR = PageRegs<KT>;
-  extern __shared__ int pre_dyn[];
-  __shared__ int tmp[32];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int spw = p.rows == 1 ? 4 : (p.rows == 2 ? 2 : 1);  // streams per workgroup
-  const int row = wave % p.rows, stream_id = blockIdx.x * spw + wave / p.rows;
-  const int n_streams = gridDim.x * spw;
-  int n_ne;
-  const ItemTable tb = build_items(p, pre_dyn, tmp, pre_dyn + p.R + 1, &n_ne);
-  if (wave >= spw * p.rows) return;  // the idle wave with 3 rows; no barrier follows
-  int lo, hi, q_req;
-  if (!request_range<1>(p, tb, pre_dyn + p.R + 1, n_ne, stream_id, n_streams, lo, hi, q_req)) {
-    const int per = (tb.total + n_streams - 1) / n_streams;
-    lo = min(tb.total, stream_id * per);
-    hi = min(tb.total, lo + per);
-    q_req = -1;
-  }
-  if (lo >= hi) return;
-  // descriptors, then the first page, then the query: the descriptor loads do
-  // not queue behind the query loads, and the query arrives while the page does
-  DescBatch db;
-  db.init(p, tb, lo);
-  if (q_req < 0) q_req = __builtin_amdgcn_readfirstlane(db.mine.r);
-  DescBatch dd = db;
+  const int lane = threadIdx.x & 63;
+  Cur dd = db;
   v4u kb[P][PR::kRegs];
   float sc[P];
 #pragma unroll
   for (int u = 0; u < P - 1; ++u)
-    PR::load(p, dd.get(p, tb, min(lo + u, hi - 1)).page, kb[u], sc[u]);
+    PR::load(p, dd.get(p, min(lo + u, hi - 1)).page, kb[u], sc[u]);
   QFull<KT, NS> Q;
   Q.fetch(p, QB, q_req * p.rows + row);
   Q.convert(p, QB, q_req * p.rows + row);
@@ -531,9 +590,9 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
       const int cur = it + u;
       if (cur >= hi) break;
       // refill: page cur + P - 1 (the last page again past the end: an L2 hit)
-      PR::load(p, dd.get(p, tb, min(cur + P - 1, hi - 1)).page, kb[(u + P - 1) % P],
+      PR::load(p, dd.get(p, min(cur + P - 1, hi - 1)).page, kb[(u + P - 1) % P],
                sc[(u + P - 1) % P]);
-      const Desc d = db.get(p, tb, cur);
+      const Desc d = db.get(p, cur);
       if (Span && d.r != q_req) {
         q_req = d.r;
         rowid = q_req * p.rows + row;
@@ -562,6 +621,46 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
     }
   }
   if (bad && lane == 0) raise_error(p.err, SPIN_DERR_PAGE);
+}
+
+enum { kRunWave = 0, kRunTable = 1, kRunSpan = 2 };
+
+template <int KT, int NS, int QB, int P, int Mode>
+__global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
+  extern __shared__ int pre_dyn[];
+  __shared__ int tmp[32];
+  const int wave = threadIdx.x >> 6;
+  const int spw = p.rows == 1 ? 4 : (p.rows == 2 ? 2 : 1);  // streams per workgroup
+  const int row = wave % p.rows, stream_id = blockIdx.x * spw + wave / p.rows;
+  const int n_streams = gridDim.x * spw;
+  if constexpr (Mode == kRunWave) {  // every wave finds its own run: no LDS, no barrier
+    if (wave >= spw * p.rows) return;
+    const Run run = wave_run(p, stream_id, n_streams);
+    if (run.lo >= run.hi) return;
+    RunCursor db;
+    db.r = run.r;
+    db.N = run.N;
+    db.hi = run.hi;
+    db.init(p, run.lo);
+    score_pages<KT, NS, QB, P, false>(p, db, run.lo, run.hi, run.r, row);
+  } else {
+    int n_ne;
+    const ItemTable tb = build_items(p, pre_dyn, tmp, pre_dyn + p.R + 1, &n_ne);
+    if (wave >= spw * p.rows) return;  // the idle wave with 3 rows; no barrier follows
+    int lo, hi, q_req;
+    if (!request_range<1>(p, tb, pre_dyn + p.R + 1, n_ne, stream_id, n_streams, lo, hi, q_req)) {
+      const int per = (tb.total + n_streams - 1) / n_streams;
+      lo = min(tb.total, stream_id * per);
+      hi = min(tb.total, lo + per);
+      q_req = -1;
+    }
+    if (lo >= hi) return;
+    TableCursor db;
+    db.tb = tb;
+    db.b.init(p, tb, lo);
+    if (q_req < 0) q_req = __builtin_amdgcn_readfirstlane(db.b.mine.r);
+    score_pages<KT, NS, QB, P, Mode == kRunSpan>(p, db, lo, hi, q_req, row);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -614,14 +713,22 @@ template <int KT, int NS, int QB>
 static void launch_wave(const ScoreParams& p, hipStream_t st) {
   constexpr int P = 2;  // pages in flight per wave
   const int spw = p.rows == 1 ? 4 : (p.rows == 2 ? 2 : 1);
+  if (p.R <= 64) {  // every wave finds its own run
+    const auto wave = k_score_wave<KT, NS, QB, P, kRunWave>;
+    const int g = min(resident_workgroups((const void*)wave, 256, 0), p.R * p.max_blocks);
+    if (spw * g >= p.R) {
+      hipLaunchKernelGGL(wave, dim3(g), dim3(256), 0, st, p);
+      return;
+    }
+  }
   const size_t dyn = sizeof(int) * 2 * (p.R + 1);
-  const auto aligned = k_score_wave<KT, NS, QB, P, false>;
+  const auto aligned = k_score_wave<KT, NS, QB, P, kRunTable>;
   const int g = min(resident_workgroups((const void*)aligned, 256, dyn), p.R * p.max_blocks);
   if (spw * g >= p.R) {  // a stream per request at least: request-aligned runs
     hipLaunchKernelGGL(aligned, dim3(g), dim3(256), dyn, st, p);
     return;
   }
-  const auto span = k_score_wave<KT, NS, QB, P, true>;
+  const auto span = k_score_wave<KT, NS, QB, P, kRunSpan>;
   const int g2 = min(resident_workgroups((const void*)span, 256, dyn), p.R * p.max_blocks);
   hipLaunchKernelGGL(span, dim3(g2), dim3(256), dyn, st, p);
 }
