@@ -373,59 +373,122 @@ struct QFull<0, NS> {  // fp8 keys: NS E4M3 terms per query value
     convert(p, q_bf16, rowid);
   }
 
-  // Split the query into NS E4M3 terms per value after a per-head power-of-two
-  // scaling (2^e amax in [128, 256)); 2^-e folds into the head weight.
-  __device__ __forceinline__ void convert(const ScoreParams& p, int q_bf16, int rowid) {
+  // This lane's 32 values of head tile t (bf16 from raw[t], fp32 loaded here).
+  __device__ __forceinline__ void tile_values(const ScoreParams& p, int q_bf16, int rowid, int t,
+                                              float (&x)[32]) const {
     const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
-    const int64_t qbase = (int64_t)rowid * 64;
+    if (q_bf16) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[8 * v + 2 * c] = __uint_as_float(raw[t][v][c] << 16);
+          x[8 * v + 2 * c + 1] = __uint_as_float(raw[t][v][c] & 0xFFFF0000u);
+        }
+    } else {
+      load_q32(p.q, q_bf16, ((int64_t)rowid * 64 + 16 * t + m) * 128, g, x);
+    }
+  }
+
+  // Split one head tile into NS E4M3 terms per value after a per-head
+  // power-of-two scaling (2^e amax in [128, 256)); returns the lane's head
+  // exponent e (2^-e folds into the head weight).
+  __device__ static __forceinline__ int split_tile(const float (&x)[32], v8i (&out)[NS]) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) amax = fmaxf(amax, fabsf(x[u]));
+    amax = fmaxf(amax, xor16(amax));
+    amax = fmaxf(amax, xor32(amax));
+    const int e = amax > 0.0f ? 7 - ilogbf(amax) : 0;
+    int pw[NS][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float rem[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) rem[v] = ldexpf(x[4 * u + v], e);
+#pragma unroll
+      for (int sp = 0; sp < NS; ++sp) {
+        const int packed = pack_fp8x4(rem[0], rem[1], rem[2], rem[3]);
+        pw[sp][u] = packed;
+        if (sp + 1 < NS) {
+          rem[0] -= __builtin_amdgcn_cvt_f32_fp8(packed, 0);
+          rem[1] -= __builtin_amdgcn_cvt_f32_fp8(packed, 1);
+          rem[2] -= __builtin_amdgcn_cvt_f32_fp8(packed, 2);
+          rem[3] -= __builtin_amdgcn_cvt_f32_fp8(packed, 3);
+        }
+      }
+    }
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp)
+      out[sp] = v8i{pw[sp][0], pw[sp][1], pw[sp][2], pw[sp][3],
+                    pw[sp][4], pw[sp][5], pw[sp][6], pw[sp][7]};
+    return e;
+  }
+
+  __device__ __forceinline__ void convert(const ScoreParams& p, int q_bf16, int rowid) {
+    const int lane = threadIdx.x & 63, g = lane >> 4;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       float x[32];
-      if (q_bf16) {
+      tile_values(p, q_bf16, rowid, t, x);
+      v8i o[NS];
+      const int e = split_tile(x, o);
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            x[8 * v + 2 * c] = __uint_as_float(raw[t][v][c] << 16);
-            x[8 * v + 2 * c + 1] = __uint_as_float(raw[t][v][c] & 0xFFFF0000u);
-          }
-      } else {
-        load_q32(p.q, q_bf16, (qbase + 16 * t + m) * 128, g, x);
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int u = 0; u < 32; ++u) amax = fmaxf(amax, fabsf(x[u]));
-      amax = fmaxf(amax, xor16(amax));
-      amax = fmaxf(amax, xor32(amax));
-      const int e = amax > 0.0f ? 7 - ilogbf(amax) : 0;
-      int pw[NS][8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        float rem[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) rem[v] = ldexpf(x[4 * u + v], e);
-#pragma unroll
-        for (int sp = 0; sp < NS; ++sp) {
-          const int packed = pack_fp8x4(rem[0], rem[1], rem[2], rem[3]);
-          pw[sp][u] = packed;
-          if (sp + 1 < NS) {
-            rem[0] -= __builtin_amdgcn_cvt_f32_fp8(packed, 0);
-            rem[1] -= __builtin_amdgcn_cvt_f32_fp8(packed, 1);
-            rem[2] -= __builtin_amdgcn_cvt_f32_fp8(packed, 2);
-            rem[3] -= __builtin_amdgcn_cvt_f32_fp8(packed, 3);
-          }
-        }
-      }
-#pragma unroll
-      for (int sp = 0; sp < NS; ++sp)
-        part[sp][t] = v8i{pw[sp][0], pw[sp][1], pw[sp][2], pw[sp][3],
-                          pw[sp][4], pw[sp][5], pw[sp][6], pw[sp][7]};
+      for (int sp = 0; sp < NS; ++sp) part[sp][t] = o[sp];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ei = __shfl(e, 4 * g + i, 64);
         wq[t][i] = ldexpf(wraw[t][i], -ei);
       }
     }
+  }
+
+  // Workgroup-shared query: LDS bytes per verifier row (the head weights go
+  // to a separate 64-float array per row).
+  static constexpr int kStageBytes = NS * 4 * 64 * 32;
+
+  // Convert head tile t of query row rowid into the LDS stage of `slot`: the
+  // MFMA operands of every lane, then the scaled head weights.
+  __device__ __forceinline__ void stage(const ScoreParams& p, int q_bf16, int rowid, int t,
+                                        unsigned char* lds, float* ws, int slot) {
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    float x[32];
+    if (q_bf16) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)rowid * 64 + 16 * t + m) * 128;
+      raw[t][0] = *reinterpret_cast<const v4u*>(qp + 16 * g);
+      raw[t][1] = *reinterpret_cast<const v4u*>(qp + 16 * g + 8);
+      raw[t][2] = *reinterpret_cast<const v4u*>(qp + 64 + 16 * g);
+      raw[t][3] = *reinterpret_cast<const v4u*>(qp + 64 + 16 * g + 8);
+    }
+    const float w = lane < 16 ? p.w[(int64_t)rowid * 64 + 16 * t + m] : 0.0f;
+    tile_values(p, q_bf16, rowid, t, x);
+    v8i o[NS];
+    const int e = split_tile(x, o);
+    v4u* qs = reinterpret_cast<v4u*>(lds + slot * kStageBytes);
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) {
+      qs[((sp * 4 + t) * 2 + 0) * 64 + lane] = v4u{(unsigned)o[sp][0], (unsigned)o[sp][1],
+                                                   (unsigned)o[sp][2], (unsigned)o[sp][3]};
+      qs[((sp * 4 + t) * 2 + 1) * 64 + lane] = v4u{(unsigned)o[sp][4], (unsigned)o[sp][5],
+                                                   (unsigned)o[sp][6], (unsigned)o[sp][7]};
+    }
+    if (lane < 16) ws[64 * slot + 16 * t + m] = ldexpf(w, -e);
+  }
+
+  __device__ __forceinline__ void from_lds(const unsigned char* lds, const float* ws, int slot) {
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    const v4u* qs = reinterpret_cast<const v4u*>(lds + slot * kStageBytes);
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const v4u a = qs[((sp * 4 + t) * 2 + 0) * 64 + lane], b = qs[((sp * 4 + t) * 2 + 1) * 64 + lane];
+        part[sp][t] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+      }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wq[t][i] = ws[64 * slot + 16 * t + 4 * g + i];
   }
 
   // this lane's ReLU-weighted sum over its 16 heads for the 16 slots whose
@@ -470,6 +533,36 @@ struct QFull<1, NS> {  // bf16 keys
 #pragma unroll
       for (int i = 0; i < 4; ++i) wq[t][i] = p.w[qbase + 16 * t + 4 * g + i];
     }
+  }
+
+  static constexpr int kStageBytes = 4 * 4 * 64 * 16;
+
+  // Copy head tile t of query row rowid into the LDS stage of `slot`.
+  __device__ __forceinline__ void stage(const ScoreParams& p, int, int rowid, int t,
+                                        unsigned char* lds, float* ws, int slot) {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)rowid * 64 + 16 * t + n) * 128;
+    v4u a[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const v4u*>(qp + 32 * ks + 8 * g);
+    const float w = lane < 16 ? p.w[(int64_t)rowid * 64 + 16 * t + n] : 0.0f;
+    v4u* qs = reinterpret_cast<v4u*>(lds + slot * kStageBytes);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qs[(t * 4 + ks) * 64 + lane] = a[ks];
+    if (lane < 16) ws[64 * slot + 16 * t + n] = w;
+  }
+
+  __device__ __forceinline__ void from_lds(const unsigned char* lds, const float* ws, int slot) {
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    const v4u* qs = reinterpret_cast<const v4u*>(lds + slot * kStageBytes);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qa[t][ks] = qs[(t * 4 + ks) * 64 + lane];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wq[t][i] = ws[64 * slot + 16 * t + 4 * g + i];
   }
 
   // this lane's ReLU-weighted sum over its 16 heads for the 16 slots of
@@ -563,24 +656,15 @@ struct PageRegs<1> {
 // requests.
 // ---------------------------------------------------------------------------
 
-// The page loop of one worker: blocks [lo, hi) through cursor `db`, query
-// row `row` of request q_req.  The descriptors are loaded first, then the
-// first page, then the query: the descriptor loads do not queue behind the
-// query loads, and the query arrives while the page does.
+// The page loop of one worker: blocks [lo, hi) through cursors `db` (the
+// block being scored) and `dd` (the block being loaded, P - 1 ahead, whose
+// first pages are already in kb), query row `row` of request q_req in Q.
 template <int KT, int NS, int QB, int P, bool Span, class Cur>
-__device__ __forceinline__ void score_pages(const ScoreParams& p, Cur& db, int lo, int hi,
-                                            int q_req, int row) {
+__device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd,
+                                          v4u (&kb)[P][PageRegs<KT>::kRegs], float (&sc)[P],
+                                          QFull<KT, NS>& Q, int lo, int hi, int q_req, int row) {
   using PR = PageRegs<KT>;
   const int lane = threadIdx.x & 63;
-  Cur dd = db;
-  v4u kb[P][PR::kRegs];
-  float sc[P];
-#pragma unroll
-  for (int u = 0; u < P - 1; ++u)
-    PR::load(p, dd.get(p, min(lo + u, hi - 1)).page, kb[u], sc[u]);
-  QFull<KT, NS> Q;
-  Q.fetch(p, QB, q_req * p.rows + row);
-  Q.convert(p, QB, q_req * p.rows + row);
   int rowid = q_req * p.rows + row;
   uint32_t hint = p.sink.hint ? p.sink.hint[rowid] : 0u;
   int bad = 0;
@@ -623,6 +707,32 @@ __device__ __forceinline__ void score_pages(const ScoreParams& p, Cur& db, int l
   if (bad && lane == 0) raise_error(p.err, SPIN_DERR_PAGE);
 }
 
+
+template <int KT, int P, class Cur>
+__device__ __forceinline__ void first_pages(const ScoreParams& p, Cur& dd,
+                                            v4u (&kb)[P][PageRegs<KT>::kRegs], float (&sc)[P],
+                                            int lo, int hi) {
+#pragma unroll
+  for (int u = 0; u < P - 1; ++u)
+    PageRegs<KT>::load(p, dd.get(p, min(lo + u, hi - 1)).page, kb[u], sc[u]);
+}
+
+// One worker with its own query: descriptors first, then the first page, then
+// the query, so that the descriptor loads do not queue behind the query loads
+// and the query arrives while the page does.
+template <int KT, int NS, int QB, int P, bool Span, class Cur>
+__device__ __forceinline__ void score_pages(const ScoreParams& p, Cur& db, int lo, int hi,
+                                            int q_req, int row) {
+  Cur dd = db;
+  v4u kb[P][PageRegs<KT>::kRegs];
+  float sc[P];
+  first_pages<KT, P>(p, dd, kb, sc, lo, hi);
+  QFull<KT, NS> Q;
+  Q.fetch(p, QB, q_req * p.rows + row);
+  Q.convert(p, QB, q_req * p.rows + row);
+  page_loop<KT, NS, QB, P, Span>(p, db, dd, kb, sc, Q, lo, hi, q_req, row);
+}
+
 enum { kRunWave = 0, kRunTable = 1, kRunSpan = 2 };
 
 template <int KT, int NS, int QB, int P, int Mode>
@@ -633,16 +743,39 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
   const int spw = p.rows == 1 ? 4 : (p.rows == 2 ? 2 : 1);  // streams per workgroup
   const int row = wave % p.rows, stream_id = blockIdx.x * spw + wave / p.rows;
   const int n_streams = gridDim.x * spw;
-  if constexpr (Mode == kRunWave) {  // every wave finds its own run: no LDS, no barrier
-    if (wave >= spw * p.rows) return;
-    const Run run = wave_run(p, stream_id, n_streams);
-    if (run.lo >= run.hi) return;
-    RunCursor db;
-    db.r = run.r;
-    db.N = run.N;
-    db.hi = run.hi;
-    db.init(p, run.lo);
-    score_pages<KT, NS, QB, P, false>(p, db, run.lo, run.hi, run.r, row);
+  if constexpr (Mode == kRunWave) {
+    // Teams of workgroups: a workgroup's streams split its request-aligned
+    // run, found by each wave on its own (no table), and share the request's
+    // query rows through LDS, each wave converting rows of the 16-head tiles.
+    const Run run = wave_run(p, blockIdx.x, gridDim.x);
+    if (run.lo >= run.hi) return;  // the whole workgroup: no barrier follows
+    const int s = wave / p.rows, nb = run.hi - run.lo;
+    const int lo = __builtin_amdgcn_readfirstlane(run.lo + s * nb / spw);
+    const int hi = __builtin_amdgcn_readfirstlane(run.lo + (s + 1) * nb / spw);
+    const bool active = wave < spw * p.rows && lo < hi;
+    unsigned char* lds = reinterpret_cast<unsigned char*>(pre_dyn);
+    __shared__ float wstage[SPIN_MAX_ROWS * 64];  // head weights of each row
+    RunCursor db, dd;
+    v4u kb[P][PageRegs<KT>::kRegs];
+    float sc[P];
+    if (active) {  // descriptors and the first pages before the query
+      db.r = run.r;
+      db.N = run.N;
+      db.hi = hi;
+      db.init(p, lo);
+      dd = db;
+      first_pages<KT, P>(p, dd, kb, sc, lo, hi);
+    }
+    {
+      QFull<KT, NS> S;
+      for (int u = wave; u < 4 * p.rows; u += 4)
+        S.stage(p, QB, run.r * p.rows + (u >> 2), u & 3, lds, wstage, u >> 2);
+    }
+    __syncthreads();
+    if (!active) return;
+    QFull<KT, NS> Q;
+    Q.from_lds(lds, wstage, row);
+    page_loop<KT, NS, QB, P, false>(p, db, dd, kb, sc, Q, lo, hi, run.r, row);
   } else {
     int n_ne;
     const ItemTable tb = build_items(p, pre_dyn, tmp, pre_dyn + p.R + 1, &n_ne);
@@ -713,11 +846,12 @@ template <int KT, int NS, int QB>
 static void launch_wave(const ScoreParams& p, hipStream_t st) {
   constexpr int P = 2;  // pages in flight per wave
   const int spw = p.rows == 1 ? 4 : (p.rows == 2 ? 2 : 1);
-  if (p.R <= 64) {  // every wave finds its own run
+  if (p.R <= 64) {  // teams of workgroups, each wave finds its own run
+    const size_t stage = (size_t)p.rows * QFull<KT, NS>::kStageBytes;
     const auto wave = k_score_wave<KT, NS, QB, P, kRunWave>;
-    const int g = min(resident_workgroups((const void*)wave, 256, 0), p.R * p.max_blocks);
-    if (spw * g >= p.R) {
-      hipLaunchKernelGGL(wave, dim3(g), dim3(256), 0, st, p);
+    const int g = min(resident_workgroups((const void*)wave, 256, stage), p.R * p.max_blocks);
+    if (g >= p.R && lds_fits((const void*)wave, stage)) {
+      hipLaunchKernelGGL(wave, dim3(g), dim3(256), stage, st, p);
       return;
     }
   }

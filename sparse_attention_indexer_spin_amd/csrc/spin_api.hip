@@ -119,6 +119,27 @@ int resident_workgroups(const void* kernel, int threads, size_t dyn_lds) {
   return g;
 }
 
+bool lds_fits(const void* kernel, size_t dyn_lds) {
+  static std::mutex mu;
+  static std::map<std::pair<std::pair<int, const void*>, size_t>, bool> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(std::make_pair(dev, kernel), dyn_lds);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int max_lds = 0;
+  hipFuncAttributes fa{};
+  const bool ok =
+      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
+          hipSuccess &&
+      hipFuncGetAttributes(&fa, kernel) == hipSuccess &&
+      dyn_lds + fa.sharedSizeBytes <= (size_t)max_lds &&
+      (fa.maxDynamicSharedSizeBytes <= 0 || dyn_lds <= (size_t)fa.maxDynamicSharedSizeBytes);
+  cache[key] = ok;
+  return ok;
+}
+
 }  // namespace spin
 
 extern "C" {

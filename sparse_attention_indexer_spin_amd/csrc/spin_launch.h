@@ -64,5 +64,8 @@ hipError_t launch_reset(int R, float* V, int64_t v_ld, float* D, int64_t d_ld, i
 // Number of workgroups of `threads` threads of `kernel` resident at once on
 // the current device (occupancy x compute units), cached per kernel.
 int resident_workgroups(const void* kernel, int threads, size_t dyn_lds = 0);
+// Whether `kernel` may be launched with dyn_lds bytes of dynamic LDS on the
+// current device.
+bool lds_fits(const void* kernel, size_t dyn_lds);
 
 }  // namespace spin
