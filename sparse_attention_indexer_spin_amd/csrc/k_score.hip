@@ -447,21 +447,55 @@ struct QFull<0, NS> {  // fp8 keys: NS E4M3 terms per query value
   // to a separate 64-float array per row).
   static constexpr int kStageBytes = NS * 4 * 64 * 32;
 
-  // Convert head tile t of query row rowid into the LDS stage of `slot`: the
-  // MFMA operands of every lane, then the scaled head weights.
-  __device__ __forceinline__ void stage(const ScoreParams& p, int q_bf16, int rowid, int t,
-                                        unsigned char* lds, float* ws, int slot) {
+  v4u sraw[SPIN_MAX_ROWS][8];  // tiles between stage_fetch() and stage_put()
+  float sw[SPIN_MAX_ROWS];
+
+  // LDS staging, step 1: issue the loads of head tile t of query row rowid,
+  // the k-th tile this wave stages (bf16: 4 registers, fp32: 8).
+  __device__ __forceinline__ void stage_fetch(const ScoreParams& p, int q_bf16, int rowid, int t,
+                                              int k) {
     const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    const int64_t hb = ((int64_t)rowid * 64 + 16 * t + m) * 128;
+    if (q_bf16) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + hb;
+      sraw[k][0] = *reinterpret_cast<const v4u*>(qp + 16 * g);
+      sraw[k][1] = *reinterpret_cast<const v4u*>(qp + 16 * g + 8);
+      sraw[k][2] = *reinterpret_cast<const v4u*>(qp + 64 + 16 * g);
+      sraw[k][3] = *reinterpret_cast<const v4u*>(qp + 64 + 16 * g + 8);
+    } else {
+      const float* qp = reinterpret_cast<const float*>(p.q) + hb;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        sraw[k][v] = *reinterpret_cast<const v4u*>(qp + 16 * g + 4 * v);
+        sraw[k][4 + v] = *reinterpret_cast<const v4u*>(qp + 64 + 16 * g + 4 * v);
+      }
+    }
+    sw[k] = lane < 16 ? p.w[(int64_t)rowid * 64 + 16 * t + m] : 0.0f;
+  }
+
+  // Step 2: convert the k-th staged tile (head tile t) into the LDS stage of
+  // `slot`: the MFMA operands of every lane, then the scaled head weights.
+  __device__ __forceinline__ void stage_put(int q_bf16, int t, int k, unsigned char* lds,
+                                            float* ws, int slot) {
+    const int lane = threadIdx.x & 63, m = lane & 15;
     float x[32];
     if (q_bf16) {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)rowid * 64 + 16 * t + m) * 128;
-      raw[t][0] = *reinterpret_cast<const v4u*>(qp + 16 * g);
-      raw[t][1] = *reinterpret_cast<const v4u*>(qp + 16 * g + 8);
-      raw[t][2] = *reinterpret_cast<const v4u*>(qp + 64 + 16 * g);
-      raw[t][3] = *reinterpret_cast<const v4u*>(qp + 64 + 16 * g + 8);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[8 * v + 2 * c] = __uint_as_float(sraw[k][v][c] << 16);
+          x[8 * v + 2 * c + 1] = __uint_as_float(sraw[k][v][c] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[4 * v + c] = __uint_as_float(sraw[k][v][c]);
+          x[16 + 4 * v + c] = __uint_as_float(sraw[k][4 + v][c]);
+        }
     }
-    const float w = lane < 16 ? p.w[(int64_t)rowid * 64 + 16 * t + m] : 0.0f;
-    tile_values(p, q_bf16, rowid, t, x);
     v8i o[NS];
     const int e = split_tile(x, o);
     v4u* qs = reinterpret_cast<v4u*>(lds + slot * kStageBytes);
@@ -472,7 +506,7 @@ struct QFull<0, NS> {  // fp8 keys: NS E4M3 terms per query value
       qs[((sp * 4 + t) * 2 + 1) * 64 + lane] = v4u{(unsigned)o[sp][4], (unsigned)o[sp][5],
                                                    (unsigned)o[sp][6], (unsigned)o[sp][7]};
     }
-    if (lane < 16) ws[64 * slot + 16 * t + m] = ldexpf(w, -e);
+    if (lane < 16) ws[64 * slot + 16 * t + m] = ldexpf(sw[k], -e);
   }
 
   __device__ __forceinline__ void from_lds(const unsigned char* lds, const float* ws, int slot) {
@@ -537,19 +571,27 @@ struct QFull<1, NS> {  // bf16 keys
 
   static constexpr int kStageBytes = 4 * 4 * 64 * 16;
 
-  // Copy head tile t of query row rowid into the LDS stage of `slot`.
-  __device__ __forceinline__ void stage(const ScoreParams& p, int, int rowid, int t,
-                                        unsigned char* lds, float* ws, int slot) {
+  v4u sraw[SPIN_MAX_ROWS][4];  // tiles between stage_fetch() and stage_put()
+  float sw[SPIN_MAX_ROWS];
+
+  // LDS staging, step 1: issue the loads of head tile t of query row rowid,
+  // the k-th tile this wave stages.
+  __device__ __forceinline__ void stage_fetch(const ScoreParams& p, int, int rowid, int t, int k) {
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)rowid * 64 + 16 * t + n) * 128;
-    v4u a[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const v4u*>(qp + 32 * ks + 8 * g);
-    const float w = lane < 16 ? p.w[(int64_t)rowid * 64 + 16 * t + n] : 0.0f;
+    for (int ks = 0; ks < 4; ++ks) sraw[k][ks] = *reinterpret_cast<const v4u*>(qp + 32 * ks + 8 * g);
+    sw[k] = lane < 16 ? p.w[(int64_t)rowid * 64 + 16 * t + n] : 0.0f;
+  }
+
+  // Step 2: the k-th staged tile (head tile t) into the LDS stage of `slot`.
+  __device__ __forceinline__ void stage_put(int, int t, int k, unsigned char* lds, float* ws,
+                                            int slot) {
+    const int lane = threadIdx.x & 63, n = lane & 15;
     v4u* qs = reinterpret_cast<v4u*>(lds + slot * kStageBytes);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qs[(t * 4 + ks) * 64 + lane] = a[ks];
-    if (lane < 16) ws[64 * slot + 16 * t + n] = w;
+    for (int ks = 0; ks < 4; ++ks) qs[(t * 4 + ks) * 64 + lane] = sraw[k][ks];
+    if (lane < 16) ws[64 * slot + 16 * t + n] = sw[k];
   }
 
   __device__ __forceinline__ void from_lds(const unsigned char* lds, const float* ws, int slot) {
@@ -656,6 +698,37 @@ struct PageRegs<1> {
 // requests.
 // ---------------------------------------------------------------------------
 
+// The row's top-K threshold hint (0 without a sink), as a scalar: reading
+// it into an SGPR completes its load here, so the page loop does not wait
+// for every outstanding load (the pages in flight) at its first use.
+__device__ __forceinline__ uint32_t row_hint(const ScoreParams& p, int rowid) {
+  return p.sink.hint ? __builtin_amdgcn_readfirstlane(p.sink.hint[rowid]) : 0u;
+}
+
+// A scored page: the 4 lane groups' partial sums become slot l's total in
+// lane l (times the key scale), one 256-byte store of z, and with a sink the
+// block's candidates at or above the row's hint plus their count.
+__device__ __forceinline__ void emit_page(const ScoreParams& p, const float (&part)[4], float sc,
+                                          const Desc& d, int rowid, uint32_t hint, int& bad) {
+  const int lane = threadIdx.x & 63;
+  const float tot = reduce_scatter4(part);
+  const int slot = d.j * 64 + lane;
+  const float zv = (slot < d.N && !d.bad) ? tot * sc + 0.0f : 0.0f;
+  p.z[(int64_t)rowid * p.z_ld + (int64_t)d.k * 64 + lane] = zv;
+  bad |= d.bad;
+  if (p.sink.hint) {  // top-K pre-filter: this block's slots at or above the hint
+    const uint32_t key = float_key(zv);
+    const bool pass = slot < d.N && key >= hint;
+    const uint64_t m = __ballot(pass);
+    const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+    if (pass)
+      p.sink.cand[(int64_t)rowid * p.sink.cand_ld + (int64_t)d.k * 64 + pos] =
+          make_uint2(key, (uint32_t)slot);
+    if (lane == 0) p.sink.pcnt[(int64_t)rowid * p.sink.pcnt_ld + d.k] = __popcll(m);
+  }
+}
+
 // The page loop of one worker: blocks [lo, hi) through cursors `db` (the
 // block being scored) and `dd` (the block being loaded, P - 1 ahead, whose
 // first pages are already in kb), query row `row` of request q_req in Q.
@@ -666,7 +739,7 @@ __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd
   using PR = PageRegs<KT>;
   const int lane = threadIdx.x & 63;
   int rowid = q_req * p.rows + row;
-  uint32_t hint = p.sink.hint ? p.sink.hint[rowid] : 0u;
+  uint32_t hint = row_hint(p, rowid);
   int bad = 0;
   for (int it = lo; it < hi; it += P) {
 #pragma unroll
@@ -681,32 +754,16 @@ __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd
         q_req = d.r;
         rowid = q_req * p.rows + row;
         Q.load(p, QB, rowid);
-        if (p.sink.hint) hint = p.sink.hint[rowid];
+        hint = row_hint(p, rowid);
       }
       float part[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) part[st] = PR::tile(Q, kb[u], st);
-      const float tot = reduce_scatter4(part);
-      const int slot = d.j * 64 + lane;
-      const float zv = (slot < d.N && !d.bad) ? (KT == 0 ? tot * sc[u] : tot) + 0.0f : 0.0f;
-      p.z[(int64_t)rowid * p.z_ld + (int64_t)d.k * 64 + lane] = zv;
-      bad |= d.bad;
-      if (p.sink.hint) {  // top-K pre-filter: this block's slots at or above the hint
-        const uint32_t key = float_key(zv);
-        const bool pass = slot < d.N && key >= hint;
-        const uint64_t m = __ballot(pass);
-        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (pass)
-          p.sink.cand[(int64_t)rowid * p.sink.cand_ld + (int64_t)d.k * 64 + pos] =
-              make_uint2(key, (uint32_t)slot);
-        if (lane == 0) p.sink.pcnt[(int64_t)rowid * p.sink.pcnt_ld + d.k] = __popcll(m);
-      }
+      emit_page(p, part, KT == 0 ? sc[u] : 1.0f, d, rowid, hint, bad);
     }
   }
   if (bad && lane == 0) raise_error(p.err, SPIN_DERR_PAGE);
 }
-
 
 template <int KT, int P, class Cur>
 __device__ __forceinline__ void first_pages(const ScoreParams& p, Cur& dd,
@@ -755,10 +812,17 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
     const bool active = wave < spw * p.rows && lo < hi;
     unsigned char* lds = reinterpret_cast<unsigned char*>(pre_dyn);
     __shared__ float wstage[SPIN_MAX_ROWS * 64];  // head weights of each row
+    // wave w stages head tile w of every row k: the query loads go out first
+    // (the descriptor wait covers them), the first page next, and the
+    // conversion then runs while the page is in flight
+    QFull<KT, NS> S;
+#pragma unroll
+    for (int k = 0; k < SPIN_MAX_ROWS; ++k)
+      if (k < p.rows) S.stage_fetch(p, QB, run.r * p.rows + k, wave, k);
     RunCursor db, dd;
     v4u kb[P][PageRegs<KT>::kRegs];
     float sc[P];
-    if (active) {  // descriptors and the first pages before the query
+    if (active) {
       db.r = run.r;
       db.N = run.N;
       db.hi = hi;
@@ -766,11 +830,9 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
       dd = db;
       first_pages<KT, P>(p, dd, kb, sc, lo, hi);
     }
-    {
-      QFull<KT, NS> S;
-      for (int u = wave; u < 4 * p.rows; u += 4)
-        S.stage(p, QB, run.r * p.rows + (u >> 2), u & 3, lds, wstage, u >> 2);
-    }
+#pragma unroll
+    for (int k = 0; k < SPIN_MAX_ROWS; ++k)
+      if (k < p.rows) S.stage_put(QB, wave, k, lds, wstage, k);
     __syncthreads();
     if (!active) return;
     QFull<KT, NS> Q;
