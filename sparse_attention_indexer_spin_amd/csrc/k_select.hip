@@ -19,6 +19,25 @@ namespace spin {
 // 4 KB in flight.  V rows are read ascending, D rows descending (both as
 // coalesced 256-B wave accesses).
 // ---------------------------------------------------------------------------
+// Exploration key of block j: the complement of Philox4x32-10 word 0 of
+// counter (j, t, layer, req_id) under key (seed lo, seed hi), so that the
+// smallest priority is the largest key (Sec. 3.2.1).
+__device__ __forceinline__ uint32_t explore_key(int j, int t, int layer, int req_id,
+                                                uint32_t seed_lo, uint32_t seed_hi) {
+  return ~philox_word0((uint32_t)j, (uint32_t)t, (uint32_t)layer, (uint32_t)req_id, seed_lo,
+                       seed_hi);
+}
+
+// Where predict writes the exploration keys for the select of the same step
+// (out == nullptr: select computes them itself).
+struct ExploreKeys {
+  uint32_t* out;  // [R][max_blocks]
+  const int32_t* step;
+  const int32_t* req_id;
+  int layer;
+  uint32_t seed_lo, seed_hi;
+};
+
 constexpr int kPredBlocksPerWave = 8;
 
 __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_blocks,
@@ -27,7 +46,7 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
                                                  const float* __restrict__ V, int64_t v_ld,
                                                  const float* __restrict__ D, int64_t d_ld,
                                                  float* __restrict__ S, int32_t* err,
-                                                 int32_t* __restrict__ qpos_snap) {
+                                                 int32_t* __restrict__ qpos_snap, ExploreKeys xk) {
   const int r = blockIdx.z, row = blockIdx.y;
   const int N = ctx[r], q0 = qpos[r];
   // a whole step keeps the step's query position here for the fused EMA +
@@ -43,6 +62,13 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j0 = (blockIdx.x * 4 + wave) * kPredBlocksPerWave;
   if (j0 >= B) return;
+  // the exploration keys of these blocks (row 0 only; the rows share them)
+  if (xk.out && row == 0 && lane < kPredBlocksPerWave && j0 + lane < B) {
+    const int t = xk.step[r];
+    if (t > 0)
+      xk.out[(int64_t)r * max_blocks + j0 + lane] =
+          explore_key(j0 + lane, t, xk.layer, xk.req_id[r], xk.seed_lo, xk.seed_hi);
+  }
   const float* Vr = V + (int64_t)r * v_ld;
   const float* Dr = D + (int64_t)r * d_ld;
   float vv[kPredBlocksPerWave], dd[kPredBlocksPerWave];
@@ -78,7 +104,8 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     int rows, int max_blocks, const int32_t* __restrict__ ctx, const int32_t* __restrict__ qpos,
     const int32_t* __restrict__ step, const int32_t* __restrict__ req_id,
     const float* __restrict__ S, const int32_t* __restrict__ budget, uint8_t* __restrict__ code,
-    int32_t* __restrict__ sel, int32_t* __restrict__ n_sel, int compact) {
+    int32_t* __restrict__ sel, int32_t* __restrict__ n_sel, int compact,
+    const uint32_t* __restrict__ xkeys) {
   __shared__ int hist[512];
   __shared__ int sh[32];
   __shared__ uint32_t tmpu[32];
@@ -107,6 +134,18 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     const int n_e = min((int)((int64_t)m * explore_bp / 10000), m - n_f);
     const int n_r = m - n_f - n_e;
     const float* Srow = S + ((int64_t)r * rows + row) * max_blocks;
+    float sv[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) sv[e] = j0 + e < B ? Srow[j0 + e] : 0.0f;
+    // exploration keys: precomputed by predict inside a whole step, else here
+    uint32_t pk[EPT];
+    if (n_e > 0) {
+      const uint32_t* xrow = xkeys ? xkeys + (int64_t)r * max_blocks : nullptr;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+        pk[e] = xrow ? (j0 + e < B ? xrow[j0 + e] : 0u)
+                     : explore_key(j0 + e, t, layer, req_id[r], seed_lo, seed_hi);
+    }
     uint32_t key[EPT];
     uint32_t elig = 0u;
 #pragma unroll
@@ -115,7 +154,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
       key[e] = 0u;
       if (j < B) {
         if (j == 0 || j == B - 1) { c[e] = SPIN_CODE_FORCED; chosen |= 1u << e; }
-        else { key[e] = float_key(Srow[j]); elig |= 1u << e; }
+        else { key[e] = float_key(sv[e]); elig |= 1u << e; }
       }
     }
     const uint32_t ranked = block_select_top<EPT, kSelectThreads>(key, elig, n_r, hist, sh, tmpu);
@@ -125,12 +164,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     chosen |= ranked;
     elig &= ~ranked;
     if (n_e > 0) {
-      // smallest Philox priority first == largest complemented priority
-#pragma unroll
-      for (int e = 0; e < EPT; ++e)
-        key[e] = ~philox_word0((uint32_t)(j0 + e), (uint32_t)t, (uint32_t)layer,
-                               (uint32_t)req_id[r], seed_lo, seed_hi);
-      const uint32_t expl = block_select_top<EPT, kSelectThreads>(key, elig, n_e, hist, sh, tmpu);
+      const uint32_t expl = block_select_top<EPT, kSelectThreads>(pk, elig, n_e, hist, sh, tmpu);
 #pragma unroll
       for (int e = 0; e < EPT; ++e)
         if (expl >> e & 1u) c[e] = SPIN_CODE_EXPLORED;
@@ -192,24 +226,26 @@ __global__ void k_zero_i32(int32_t* __restrict__ p, int n) {
 // ---------------------------------------------------------------------------
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
                           const float* D, int64_t d_ld, float* S, hipStream_t st,
-                          int32_t* qpos_snap) {
+                          int32_t* qpos_snap, uint32_t* xkeys) {
   dim3 grid((b.max_blocks + 4 * kPredBlocksPerWave - 1) / (4 * kPredBlocksPerWave), b.n_rows,
             b.batch);
+  const ExploreKeys xk{xkeys, b.step, b.req_id, c.layer, (uint32_t)(c.seed & 0xFFFFFFFFu),
+                       (uint32_t)(c.seed >> 32)};
   hipLaunchKernelGGL(k_predict, grid, dim3(256), 0, st, c.combine, b.n_rows, b.max_blocks,
-                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld, S, b.err, qpos_snap);
+                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld, S, b.err, qpos_snap, xk);
   return hipGetLastError();
 }
 
 template <int EPT>
 static void select_t(const spin_config& c, const spin_batch& b, const float* S,
                      const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                     hipStream_t st) {
+                     hipStream_t st, const uint32_t* xkeys) {
   const int compact = b.n_rows == 1;
   hipLaunchKernelGGL(k_select<EPT>, dim3(b.n_rows, b.batch), dim3(kSelectThreads), 0, st,
                      c.topk, c.sparsity_bp, c.explore_bp, c.layer,
                      (uint32_t)(c.seed & 0xFFFFFFFFu), (uint32_t)(c.seed >> 32), b.n_rows,
                      b.max_blocks, b.ctx_len, b.q_pos, b.step, b.req_id, S, budget, code, sel,
-                     n_sel, compact);
+                     n_sel, compact, xkeys);
 }
 
 template <int EPT>
@@ -221,14 +257,14 @@ static void union_t(const spin_batch& b, uint8_t* code, int32_t* sel, int32_t* n
 
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                         hipStream_t st) {
+                         hipStream_t st, const uint32_t* xkeys) {
   const int ept = (b.max_blocks + kSelectThreads - 1) / kSelectThreads;
-  if (ept <= 1) select_t<1>(c, b, S, budget, code, sel, n_sel, st);
-  else if (ept <= 2) select_t<2>(c, b, S, budget, code, sel, n_sel, st);
-  else if (ept <= 4) select_t<4>(c, b, S, budget, code, sel, n_sel, st);
-  else if (ept <= 8) select_t<8>(c, b, S, budget, code, sel, n_sel, st);
-  else if (ept <= 16) select_t<16>(c, b, S, budget, code, sel, n_sel, st);
-  else select_t<32>(c, b, S, budget, code, sel, n_sel, st);
+  if (ept <= 1) select_t<1>(c, b, S, budget, code, sel, n_sel, st, xkeys);
+  else if (ept <= 2) select_t<2>(c, b, S, budget, code, sel, n_sel, st, xkeys);
+  else if (ept <= 4) select_t<4>(c, b, S, budget, code, sel, n_sel, st, xkeys);
+  else if (ept <= 8) select_t<8>(c, b, S, budget, code, sel, n_sel, st, xkeys);
+  else if (ept <= 16) select_t<16>(c, b, S, budget, code, sel, n_sel, st, xkeys);
+  else select_t<32>(c, b, S, budget, code, sel, n_sel, st, xkeys);
   if (b.n_rows > 1) {  // union of the rows' masks
     const int eu = (b.max_blocks + kSelThreads - 1) / kSelThreads;
     if (eu <= 1) union_t<1>(b, code, sel, n_sel, st);

@@ -59,36 +59,48 @@ __device__ __forceinline__ void raise_error(int32_t* err, int bits) {
 }
 
 // ---------------------------------------------------------------------------
-// wave64 reductions and scans
+// wave64 reductions and scans on DPP lane moves (no LDS crossbar round trips):
+// a Hillis-Steele scan inside each row of 16 lanes (row_shr 1, 2, 4, 8), then
+// row_bcast:15 carries each even row's total into the next row and
+// row_bcast:31 carries lanes 0-31's total into rows 2-3.  Lanes whose DPP
+// source is outside the row, or whose row is masked off, take the identity.
+// A reduction is the inclusive scan's lane 63, read into a scalar.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, kWave));
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_move(int identity, int v) {
+  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+template <class Op>
+__device__ __forceinline__ int dpp_incl_scan(int v, int identity, Op op) {
+  v = op(v, dpp_move<0x111>(identity, v));  // row_shr:1
+  v = op(v, dpp_move<0x112>(identity, v));  // row_shr:2
+  v = op(v, dpp_move<0x114>(identity, v));  // row_shr:4
+  v = op(v, dpp_move<0x118>(identity, v));  // row_shr:8
+  v = op(v, dpp_move<0x142, 0xA>(identity, v));  // row_bcast:15 into rows 1, 3
+  v = op(v, dpp_move<0x143, 0xC>(identity, v));  // row_bcast:31 into rows 2, 3
   return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  const int s = dpp_incl_scan((int)v, 0, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
+  return (uint32_t)__builtin_amdgcn_readlane(s, 63);
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d, kWave));
-  return v;
+  const int s = dpp_incl_scan((int)v, -1, [](int a, int b) { return (int)min((uint32_t)a, (uint32_t)b); });
+  return (uint32_t)__builtin_amdgcn_readlane(s, 63);
 }
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
-  return v;
+  const int s = dpp_incl_scan(__float_as_int(v), __float_as_int(-INFINITY), [](int a, int b) {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  });
+  return __int_as_float(__builtin_amdgcn_readlane(s, 63));
 }
 __device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
+  return __builtin_amdgcn_readlane(dpp_incl_scan(v, 0, [](int a, int b) { return a + b; }), 63);
 }
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(v, d, kWave);
-    if (lane >= d) v += y;
-  }
-  return v;
+  return dpp_incl_scan(v, 0, [](int a, int b) { return a + b; });
 }
 
 // Block-wide exclusive scan for blockDim.x = NT (multiple of 64, <= 1024).
@@ -171,14 +183,9 @@ __device__ __forceinline__ void radix_pick_digit(const int* hist, int k, int* ou
   const int c0 = hist[4 * lane + 0], c1 = hist[4 * lane + 1];
   const int c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
   const int mine = c0 + c1 + c2 + c3;
-  // inclusive suffix sum over lanes (lane 63 holds the top bins)
-  int suf = mine;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_down(suf, d, kWave);
-    if (lane + d < 64) suf += y;
-  }
-  int above = suf - mine;  // keys in bins of higher lanes
+  // keys in the bins of higher lanes (lane 63 holds the top bins)
+  const int incl = wave_incl_scan(mine);
+  int above = __builtin_amdgcn_readlane(incl, 63) - incl;
   const int cs[4] = {c0, c1, c2, c3};
 #pragma unroll
   for (int b = 3; b >= 0; --b) {
