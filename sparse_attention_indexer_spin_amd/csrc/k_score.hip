@@ -705,11 +705,23 @@ __device__ __forceinline__ uint32_t row_hint(const ScoreParams& p, int rowid) {
   return p.sink.hint ? __builtin_amdgcn_readfirstlane(p.sink.hint[rowid]) : 0u;
 }
 
+// The worker's current candidate run (see CandSink): row, first block, the
+// block expected next and the candidates so far (wave-uniform).
+struct CandRun {
+  int rowid = -1, k0 = 0, knext = 0, cnt = 0;
+};
+
+__device__ __forceinline__ void run_flush(const ScoreParams& p, const CandRun& rs) {
+  if (p.sink.hint && rs.rowid >= 0 && (threadIdx.x & 63) == 0)
+    p.sink.pcnt[(int64_t)rs.rowid * p.sink.pcnt_ld + rs.k0] = rs.cnt;
+}
+
 // A scored page: the 4 lane groups' partial sums become slot l's total in
 // lane l (times the key scale), one 256-byte store of z, and with a sink the
-// block's candidates at or above the row's hint plus their count.
+// block's candidates at or above the row's hint appended to the run.
 __device__ __forceinline__ void emit_page(const ScoreParams& p, const float (&part)[4], float sc,
-                                          const Desc& d, int rowid, uint32_t hint, int& bad) {
+                                          const Desc& d, int rowid, uint32_t hint, int& bad,
+                                          CandRun& rs) {
   const int lane = threadIdx.x & 63;
   const float tot = reduce_scatter4(part);
   const int slot = d.j * 64 + lane;
@@ -722,10 +734,18 @@ __device__ __forceinline__ void emit_page(const ScoreParams& p, const float (&pa
     const uint64_t m = __ballot(pass);
     const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+    if (rowid != rs.rowid || d.k != rs.knext) {  // a new run
+      run_flush(p, rs);
+      rs.rowid = rowid;
+      rs.k0 = d.k;
+      rs.cnt = 0;
+    }
+    rs.knext = d.k + 1;
     if (pass)
-      p.sink.cand[(int64_t)rowid * p.sink.cand_ld + (int64_t)d.k * 64 + pos] =
+      p.sink.cand[(int64_t)rowid * p.sink.cand_ld + (int64_t)rs.k0 * 64 + rs.cnt + pos] =
           make_uint2(key, (uint32_t)slot);
-    if (lane == 0) p.sink.pcnt[(int64_t)rowid * p.sink.pcnt_ld + d.k] = __popcll(m);
+    if (lane == 0 && d.k != rs.k0) p.sink.pcnt[(int64_t)rowid * p.sink.pcnt_ld + d.k] = 0;
+    rs.cnt += __popcll(m);
   }
 }
 
@@ -741,6 +761,7 @@ __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd
   int rowid = q_req * p.rows + row;
   uint32_t hint = row_hint(p, rowid);
   int bad = 0;
+  CandRun rs;
   for (int it = lo; it < hi; it += P) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
@@ -759,9 +780,10 @@ __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd
       float part[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) part[st] = PR::tile(Q, kb[u], st);
-      emit_page(p, part, KT == 0 ? sc[u] : 1.0f, d, rowid, hint, bad);
+      emit_page(p, part, KT == 0 ? sc[u] : 1.0f, d, rowid, hint, bad, rs);
     }
   }
+  run_flush(p, rs);
   if (bad && lane == 0) raise_error(p.err, SPIN_DERR_PAGE);
 }
 

@@ -344,7 +344,7 @@ constexpr int kPagesPerThread = SPIN_MAX_BLOCKS / kSelThreads;
 struct PagesShared {
   uint32_t lkey[kCap];
   int32_t lslot[kCap];
-  int32_t lsrc[kCap];  // candidate q sits at cand[lsrc[q]]
+  int32_t lsrc[kCap];  // first candidate of each selected block (boff)
   int hist[512];
   int sh[32];
   uint32_t tmpu[32];
@@ -392,11 +392,14 @@ __device__ void topk_pages_row(int rowid, int K, int rows, int max_blocks,
     fallback_row(R, K, orow, ws.hint + rowid, hist, sh, tmpu);
     return;
   }
-  // where each candidate comes from (LDS only), then all loads in flight
+  // candidate q comes from block k = the last with boff[k] <= q (the
+  // candidates of block k sit at cand[64 k ..], a worker's run at its first
+  // block), at cand[64 k + q - boff[k]]; the loads of a run are contiguous
+  int* boff = lsrc;
 #pragma unroll
   for (int e = 0; e < PPT; ++e) {
     const int k = threadIdx.x * PPT + e;
-    for (int i = 0; i < c[e]; ++i) lsrc[off + i] = k * 64 + i;
+    if (k < ns) boff[k] = off;
     off += c[e];
   }
   __syncthreads();
@@ -405,7 +408,15 @@ __device__ void topk_pages_row(int rowid, int K, int rows, int max_blocks,
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int q = threadIdx.x + e * kSelThreads;
-    v[e] = q < c_tot ? crow[lsrc[q]] : make_uint2(0u, 0u);
+    v[e] = make_uint2(0u, 0u);
+    if (q < c_tot) {
+      int a = 0, b = ns - 1;
+      while (a < b) {
+        const int mid = (a + b + 1) >> 1;
+        if (boff[mid] <= q) a = mid; else b = mid - 1;
+      }
+      v[e] = crow[(int64_t)a * 64 + q - boff[a]];
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {

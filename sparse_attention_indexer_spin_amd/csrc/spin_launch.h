@@ -7,9 +7,11 @@
 namespace spin {
 
 // Where a score kernel that also filters for the top-K writes its candidates:
-// per (row, selected block k) the slots of that block whose z key is >= the
-// row's hint, compacted at cand[row * cand_ld + 64 k ..] in slot order as
-// (key, slot) pairs, and their count at pcnt[row * pcnt_ld + k].
+// the slots whose z key is >= the row's hint, as (key, slot) pairs in slot
+// order.  A worker appends the candidates of its run of consecutive selected
+// blocks k0 .. k1 of a row at cand[row * cand_ld + 64 k0 ..] and writes their
+// count to pcnt[row * pcnt_ld + k0], and 0 for the run's other blocks: for
+// every k, pcnt[k] candidates sit at cand[64 k ..].
 struct CandSink {
   const uint32_t* hint;  // [rows_total]
   uint2* cand;
