@@ -58,9 +58,11 @@ struct EmaArgs {
   int32_t* step_out;
 };
 
-// One wave: the EMA update of selected blocks k0 .. k0 + kEmaBlocksPerWave - 1
-// of request r; `advance`: this thread also advances r's counters.
-__device__ __forceinline__ void ema_wave(const EmaArgs& A, int r, int k0, bool advance) {
+// One wave: the EMA update of selected blocks [k0, k1) of request r, CH
+// blocks' loads at a time with one row; `advance`: this thread also advances
+// r's counters.
+template <int CH>
+__device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int k1, bool advance) {
   const int rows = A.rows, max_blocks = A.max_blocks;
   const int32_t* n_valid = A.n_valid;
   const float* z = A.z;
@@ -78,7 +80,8 @@ __device__ __forceinline__ void ema_wave(const EmaArgs& A, int r, int k0, bool a
   const int32_t* n_sel = A.n_sel;
   if (request_error(N, q, rows, max_blocks, v_ld, d_ld)) return;
   const int ns = clamp_nsel(n_sel[r], max_blocks);
-  if (k0 >= ns) return;
+  k1 = min(k1, ns);
+  if (k0 >= k1) return;
   int L = n_valid ? n_valid[r] : rows;
   L = L < 0 ? 0 : (L > rows ? rows : L);
   if (L == 0) return;
@@ -89,30 +92,30 @@ __device__ __forceinline__ void ema_wave(const EmaArgs& A, int r, int k0, bool a
   float* Dr = D + (int64_t)r * d_ld;
   if (L == 1) {
     // one observation per slot: V[i] and D[q - i] from row 0, loads batched
-    float vv[kEmaBlocksPerWave], dd[kEmaBlocksPerWave], zz[kEmaBlocksPerWave];
-    int ii[kEmaBlocksPerWave];
+    for (int kb = k0; kb < k1; kb += CH) {
+      float vv[CH], dd[CH], zz[CH];
+      int ii[CH];
 #pragma unroll
-    for (int u = 0; u < kEmaBlocksPerWave; ++u) {
-      const int k = k0 + u;
-      const int j = k < ns ? sr[k] : -1;
-      const int i = j * 64 + lane;
-      const bool ok = k < ns && j >= 0 && j < max_blocks && i < N;
-      ii[u] = ok ? i : -1;
-      vv[u] = ok ? Vr[i] : 0.0f;
-      dd[u] = ok ? Dr[q - i] : 0.0f;
-      zz[u] = ok ? zb[(int64_t)k * 64 + lane] : 0.0f;
-    }
+      for (int u = 0; u < CH; ++u) {
+        const int k = kb + u;
+        const int j = k < k1 ? sr[k] : -1;
+        const int i = j * 64 + lane;
+        const bool ok = k < k1 && j >= 0 && j < max_blocks && i < N;
+        ii[u] = ok ? i : -1;
+        vv[u] = ok ? Vr[i] : 0.0f;
+        dd[u] = ok ? Dr[q - i] : 0.0f;
+        zz[u] = ok ? zb[(int64_t)k * 64 + lane] : 0.0f;
+      }
 #pragma unroll
-    for (int u = 0; u < kEmaBlocksPerWave; ++u) {
-      if (ii[u] < 0) continue;
-      Vr[ii[u]] = ema_step(vv[u], zz[u], a, b);
-      Dr[q - ii[u]] = ema_step(dd[u], zz[u], a, b);
+      for (int u = 0; u < CH; ++u) {
+        if (ii[u] < 0) continue;
+        Vr[ii[u]] = ema_step(vv[u], zz[u], a, b);
+        Dr[q - ii[u]] = ema_step(dd[u], zz[u], a, b);
+      }
     }
     return;
   }
-  for (int u = 0; u < kEmaBlocksPerWave; ++u) {
-    const int k = k0 + u;
-    if (k >= ns) break;
+  for (int k = k0; k < k1; ++k) {
     EmaCtx e;
     e.a = a; e.b = b;
     e.L = L; e.N = N; e.q = q; e.k = k; e.ns = ns;
@@ -133,6 +136,11 @@ __device__ __forceinline__ void ema_wave(const EmaArgs& A, int r, int k0, bool a
       if (!prev_selected) ema_offset(e, e.j * 64 - 1 - lane, Dr);
     }
   }
+}
+
+// One wave: selected blocks k0 .. k0 + kEmaBlocksPerWave - 1 of request r.
+__device__ __forceinline__ void ema_wave(const EmaArgs& A, int r, int k0, bool advance) {
+  ema_blocks<kEmaBlocksPerWave>(A, r, k0, k0 + kEmaBlocksPerWave, advance);
 }
 
 }  // namespace spin

@@ -466,6 +466,8 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select_pages(
 // run the per-row select (dispatched first), the others the EMA, ema_x of
 // them per request, sized to fill the CUs the few select workgroups leave
 // idle (one workgroup per CU: the select's LDS).
+constexpr int kEmaChunk = 16;  // blocks whose loads an EMA wave issues together
+
 __global__ __launch_bounds__(kSelThreads) void k_topk_ema(
     int K, int rows, int max_blocks, const int32_t* __restrict__ ctx,
     const int32_t* __restrict__ qpos, const float* __restrict__ z, int64_t z_ld,
@@ -476,15 +478,14 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_ema(
     topk_pages_row(blockIdx.x, K, rows, max_blocks, ctx, qpos, z, z_ld, sel, n_sel, out, ws, L);
     return;
   }
-  // ema_x blocks per request; each wave strides over the request's selected
-  // blocks kEmaBlocksPerWave at a time
+  // ema_x blocks per request; wave w of the request's team takes an even
+  // share of its selected blocks, all of one share's loads issued together
   const int e = blockIdx.x - rows_total, r = e / ema_x, bx = e % ema_x;
   constexpr int kWaves = kSelThreads / 64;
-  const int stride = ema_x * kWaves * kEmaBlocksPerWave;
-  const int k_end = clamp_nsel(A.n_sel[r], A.max_blocks);
-  int k0 = (bx * kWaves + (int)(threadIdx.x >> 6)) * kEmaBlocksPerWave;
-  ema_wave(A, r, k0, bx == 0 && threadIdx.x == 0);
-  for (k0 += stride; k0 < k_end; k0 += stride) ema_wave(A, r, k0, false);
+  const int n_waves = ema_x * kWaves, w = bx * kWaves + (int)(threadIdx.x >> 6);
+  const int ns = clamp_nsel(A.n_sel[r], A.max_blocks);
+  const int k0 = (int)((int64_t)w * ns / n_waves), k1 = (int)((int64_t)(w + 1) * ns / n_waves);
+  ema_blocks<kEmaChunk>(A, r, k0, k1, w == 0 && threadIdx.x == 0);
 }
 
 size_t topk_workspace_bytes(const spin_config&, int R, int rows, int max_blocks) {
@@ -503,7 +504,7 @@ hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const floa
                            int32_t* step_out, hipStream_t st) {
   const int rows_total = b.batch * b.n_rows;
   const TopkWs ws = carve(wsp, rows_total, b.max_blocks);
-  constexpr int per_block = (kSelThreads / 64) * kEmaBlocksPerWave;
+  constexpr int per_block = (kSelThreads / 64) * kEmaChunk;
   const int most = (b.max_blocks + per_block - 1) / per_block;
   const int free_cus = resident_workgroups((const void*)k_topk_ema, kSelThreads) - rows_total;
   const int ema_x = max(1, min(most, free_cus / max(1, b.batch)));
