@@ -138,7 +138,8 @@ def run_gpu(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_reps: 
         q = inp.q[warmup + steps - 1]
         last_nv = nv[-1]
         st = {
-            "predict": lambda: api.spin_predict_blocks(lay.cfg, bt, lay.V, lay.D, lay.S),
+            "predict": lambda: api.spin_predict_blocks(lay.cfg, bt, lay.V, lay.D, lay.S,
+                                                       v_max=lay.v_max),
             "select": lambda: api.spin_select_blocks(lay.cfg, bt, lay.S, lay.row_code, lay.sel,
                                                      lay.n_sel),
             "score": lambda: api.spin_sparse_index_score(lay.cfg, bt, q, inp.weights, pages,
@@ -146,7 +147,7 @@ def run_gpu(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_reps: 
             "topk": lambda: api.spin_topk(lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.topk_idx,
                                           lay.workspace),
             "ema": lambda: api.spin_ema_update(lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.V,
-                                               lay.D, n_valid=last_nv),
+                                               lay.D, n_valid=last_nv, v_max=lay.v_max),
         }
         out["stage_us"] = {k: _timed_us(f, stage_reps, stream) for k, f in st.items()}
         assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"

@@ -104,11 +104,17 @@ typedef struct spin_batch {
  * S[r][row][j] = max over slots i in block j with i < N of C(V[i], D[q_row - i]),
  * C = max or fp32 sum (cfg->combine), q_row = q_pos[r] + row.
  *   V: f32 [R][v_ld] (v_ld >= N), D: f32 [R][d_ld] (d_ld > q_pos + n_rows - 1),
+ *   v_max: optional f32 [R][max_blocks], the block maxima of V.  With C = max,
+ *          max_i max(V[i], D[q - i]) = max(max_i V[i], max_i D[q - i]), so every
+ *          block but the last one then reads v_max[r][j] instead of V.  Entry j
+ *          must hold the max of V over all 64 slots of block j (slots >= N hold
+ *          V = 0); spin_reset_state, spin_ema_update and spin_step keep it so
+ *          when given it.  ctx_len must not shrink between resets.
  *   S: f32 [R][n_rows][max_blocks]; entries j >= ceil(N/64) are not written.
  */
 spin_status spin_predict_blocks(const spin_config* cfg, const spin_batch* bt,
                                 const float* V, int64_t v_ld, const float* D, int64_t d_ld,
-                                float* S, void* stream);
+                                const float* v_max, float* S, void* stream);
 
 /*
  * Stage 2 (Algorithm 1 steps 4-5; the sink and newest blocks are always kept
@@ -167,11 +173,13 @@ spin_status spin_topk(const spin_config* cfg, const spin_batch* bt, const float*
  * each product and the sum rounded to fp32 separately (no fused multiply-add),
  * beta = 1.0f - alpha rounded to fp32.
  *   n_valid: optional i32 [R], each in 1..n_rows
+ *   v_max:   optional f32 [R][max_blocks]: the updated blocks' V maxima are
+ *            refreshed (see spin_predict_blocks)
  */
 spin_status spin_ema_update(const spin_config* cfg, const spin_batch* bt, const float* z,
                             int64_t z_ld, const int32_t* sel, const int32_t* n_sel,
                             const int32_t* n_valid, float* V, int64_t v_ld, float* D, int64_t d_ld,
-                            void* stream);
+                            float* v_max, void* stream);
 
 /*
  * Advance the per-request counters after a committed step:
@@ -182,16 +190,18 @@ spin_status spin_advance(int32_t batch, int32_t n_rows, const int32_t* n_valid, 
 
 /*
  * Reset after prefill or at a turn start (prose after Algorithm 1): V[r][0..v_ld),
- * D[r][0..d_ld) = 0 and step[r] = 0 for every r < batch, so the next step is dense.
+ * D[r][0..d_ld) = 0, v_max[r][0..vmax_ld) = 0 (when v_max != NULL) and step[r] = 0
+ * for every r < batch, so the next step is dense.
  * Uses fill kernels only (safe inside captured graphs).
  */
 spin_status spin_reset_state(int32_t batch, float* V, int64_t v_ld, float* D, int64_t d_ld,
-                             int32_t* step, void* stream);
+                             float* v_max, int64_t vmax_ld, int32_t* step, void* stream);
 
 /* Buffers of one whole step (spin_step).  Pointer meanings as above. */
 typedef struct spin_step_io {
   float* V; int64_t v_ld;               /* EMA state, updated in place        */
   float* D; int64_t d_ld;
+  float* v_max;                         /* optional V block maxima [R][max_blocks] */
   const void* q; const float* w;        /* indexer queries and head weights   */
   const void* k_pages; const float* k_scale;
   const int32_t* page_table; int64_t pt_ld;

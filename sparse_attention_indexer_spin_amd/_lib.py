@@ -41,7 +41,7 @@ class SpinBatch(C.Structure):
 
 class SpinStepIO(C.Structure):
     _fields_ = [("V", C.c_void_p), ("v_ld", C.c_int64), ("D", C.c_void_p), ("d_ld", C.c_int64),
-                ("q", C.c_void_p), ("w", C.c_void_p), ("k_pages", C.c_void_p),
+                ("v_max", C.c_void_p), ("q", C.c_void_p), ("w", C.c_void_p), ("k_pages", C.c_void_p),
                 ("k_scale", C.c_void_p), ("page_table", C.c_void_p), ("pt_ld", C.c_int64),
                 ("budget", C.c_void_p), ("n_valid", C.c_void_p), ("S", C.c_void_p),
                 ("row_code", C.c_void_p), ("sel", C.c_void_p), ("n_sel", C.c_void_p),
@@ -65,13 +65,13 @@ def load() -> C.CDLL:
     P, I32, I64, SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
     cfg, bt = C.POINTER(SpinConfig), C.POINTER(SpinBatch)
     sig = {
-        "spin_predict_blocks": [cfg, bt, P, I64, P, I64, P, P],
+        "spin_predict_blocks": [cfg, bt, P, I64, P, I64, P, P, P],
         "spin_select_blocks": [cfg, bt, P, P, P, P, P, P],
         "spin_sparse_index_score": [cfg, bt, P, P, P, P, P, I64, P, P, P, I64, P],
         "spin_topk": [cfg, bt, P, I64, P, P, P, P, SZ, P],
-        "spin_ema_update": [cfg, bt, P, I64, P, P, P, P, I64, P, I64, P],
+        "spin_ema_update": [cfg, bt, P, I64, P, P, P, P, I64, P, I64, P, P],
         "spin_advance": [I32, I32, P, P, P, P],
-        "spin_reset_state": [I32, P, I64, P, I64, P, P],
+        "spin_reset_state": [I32, P, I64, P, I64, P, I64, P, P],
         "spin_step": [cfg, bt, C.POINTER(SpinStepIO), I32, P],
     }
     for name, args in sig.items():

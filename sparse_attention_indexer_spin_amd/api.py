@@ -58,8 +58,9 @@ def _ld(t: torch.Tensor) -> int:
     return t.shape[-1]
 
 
-def spin_predict_blocks(cfg, bt, V, D, S, stream=None):
+def spin_predict_blocks(cfg, bt, V, D, S, stream=None, v_max=None):
     L.check(L.load().spin_predict_blocks(C.byref(cfg), C.byref(bt), _p(V), _ld(V), _p(D), _ld(D),
+                                         _p(v_max),
                                          _p(S), _stream(stream)))
 
 
@@ -85,10 +86,10 @@ def spin_topk(cfg, bt, z, sel, n_sel, topk_idx, workspace=None, stream=None):
                                _p(topk_idx), _p(workspace), ws_bytes, _stream(stream)))
 
 
-def spin_ema_update(cfg, bt, z, sel, n_sel, V, D, n_valid=None, stream=None):
+def spin_ema_update(cfg, bt, z, sel, n_sel, V, D, n_valid=None, stream=None, v_max=None):
     L.check(L.load().spin_ema_update(C.byref(cfg), C.byref(bt), _p(z), _ld(z), _p(sel),
                                      _p(n_sel), _p(n_valid), _p(V), _ld(V), _p(D), _ld(D),
-                                     _stream(stream)))
+                                     _p(v_max), _stream(stream)))
 
 
 def spin_advance(n_rows: int, q_pos, step, n_valid=None, stream=None):
@@ -96,15 +97,18 @@ def spin_advance(n_rows: int, q_pos, step, n_valid=None, stream=None):
                                   _stream(stream)))
 
 
-def spin_reset_state(V, D, step, stream=None):
-    L.check(L.load().spin_reset_state(V.shape[0], _p(V), _ld(V), _p(D), _ld(D), _p(step),
+def spin_reset_state(V, D, step, stream=None, v_max=None):
+    L.check(L.load().spin_reset_state(V.shape[0], _p(V), _ld(V), _p(D), _ld(D), _p(v_max),
+                                      0 if v_max is None else _ld(v_max), _p(step),
                                       _stream(stream)))
 
 
 def step_io(*, V, D, q, w, k_pages, k_scale, page_table, S, row_code, sel, n_sel, z, topk_idx,
-            budget=None, n_valid=None, q_pos_mut=None, step_mut=None, workspace=None):
+            budget=None, n_valid=None, q_pos_mut=None, step_mut=None, workspace=None,
+            v_max=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    return L.SpinStepIO(V=_p(V), v_ld=_ld(V), D=_p(D), d_ld=_ld(D), q=_p(q), w=_p(w),
+    return L.SpinStepIO(V=_p(V), v_ld=_ld(V), D=_p(D), d_ld=_ld(D), v_max=_p(v_max), q=_p(q),
+                        w=_p(w),
                         k_pages=_p(k_pages), k_scale=_p(k_scale), page_table=_p(page_table),
                         pt_ld=_ld(page_table), budget=_p(budget), n_valid=_p(n_valid), S=_p(S),
                         row_code=_p(row_code), sel=_p(sel), n_sel=_p(n_sel), z=_p(z),

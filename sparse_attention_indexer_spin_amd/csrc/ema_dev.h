@@ -56,7 +56,15 @@ struct EmaArgs {
   int64_t d_ld;
   int32_t* qpos_out;        // optional counter advance
   int32_t* step_out;
+  float* vmax;              // optional V block maxima [R][max_blocks]
 };
+
+// After block j's V update: its max over all 64 slots (slots >= N hold 0),
+// `v` being lane i's new V[i] where i < N.
+__device__ __forceinline__ void ema_vmax(const EmaArgs& A, int r, int j, bool in, float v) {
+  const float m = wave_max_f32(in ? v : 0.0f);
+  if (A.vmax && (threadIdx.x & 63) == 0) A.vmax[(int64_t)r * A.max_blocks + j] = m;
+}
 
 // One wave: the EMA update of selected blocks [k0, k1) of request r, CH
 // blocks' loads at a time with one row; `advance`: this thread also advances
@@ -108,9 +116,15 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
       }
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
-        if (ii[u] < 0) continue;
-        Vr[ii[u]] = ema_step(vv[u], zz[u], a, b);
-        Dr[q - ii[u]] = ema_step(dd[u], zz[u], a, b);
+        const float vn = ema_step(vv[u], zz[u], a, b);
+        if (ii[u] >= 0) {
+          Vr[ii[u]] = vn;
+          Dr[q - ii[u]] = ema_step(dd[u], zz[u], a, b);
+        }
+        if (A.vmax && kb + u < k1) {
+          const int j = sr[kb + u];
+          if (j >= 0 && j < max_blocks) ema_vmax(A, r, j, ii[u] >= 0, vn);
+        }
       }
     }
     return;
@@ -125,11 +139,13 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
     e.z_ld = z_ld;
     e.sel = sr;
     const int i = e.j * 64 + lane;
+    float v = 0.0f;
     if (i < N) {
-      float v = Vr[i];
+      v = Vr[i];
       for (int row = 0; row < L; ++row) v = ema_step(v, zb[row * z_ld + (int64_t)k * 64 + lane], a, b);
       Vr[i] = v;
     }
+    if (A.vmax) ema_vmax(A, r, e.j, i < N, v);
     ema_offset(e, i, Dr);
     if (lane < L - 1) {
       const bool prev_selected = k > 0 && sr[k - 1] == e.j - 1;

@@ -28,11 +28,11 @@ __global__ __launch_bounds__(256) void k_ema(EmaArgs A) {
 
 hipError_t launch_ema(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                       const int32_t* sel, const int32_t* n_sel, const int32_t* n_valid, float* V,
-                      int64_t v_ld, float* D, int64_t d_ld, hipStream_t st,
+                      int64_t v_ld, float* D, int64_t d_ld, float* vmax, hipStream_t st,
                       const int32_t* qpos_snap, int32_t* qpos_out, int32_t* step_out) {
   dim3 grid((b.max_blocks + 4 * kEmaBlocksPerWave - 1) / (4 * kEmaBlocksPerWave), b.batch);
   const EmaArgs A{c.ema_alpha, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap ? qpos_snap : b.q_pos,
-                  n_valid, z, z_ld, sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out};
+                  n_valid, z, z_ld, sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out, vmax};
   hipLaunchKernelGGL(k_ema, grid, dim3(256), 0, st, A);
   return hipGetLastError();
 }

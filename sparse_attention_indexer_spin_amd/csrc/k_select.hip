@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
                                                  const int32_t* __restrict__ qpos,
                                                  const float* __restrict__ V, int64_t v_ld,
                                                  const float* __restrict__ D, int64_t d_ld,
+                                                 const float* __restrict__ vmax,
                                                  float* __restrict__ S, int32_t* err,
                                                  int32_t* __restrict__ qpos_snap, ExploreKeys xk) {
   const int r = blockIdx.z, row = blockIdx.y;
@@ -71,12 +72,18 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
   }
   const float* Vr = V + (int64_t)r * v_ld;
   const float* Dr = D + (int64_t)r * d_ld;
+  // with the V block maxima (max combine), every block but the last reads
+  // its V max (lane b holds block j0 + b's) instead of its 64 V values
+  const float vm = vmax && lane < kPredBlocksPerWave && j0 + lane < B - 1
+                       ? vmax[(int64_t)r * max_blocks + j0 + lane]
+                       : -INFINITY;
   float vv[kPredBlocksPerWave], dd[kPredBlocksPerWave];
 #pragma unroll
   for (int b = 0; b < kPredBlocksPerWave; ++b) {
     const int i = (j0 + b) * SPIN_BLOCK + lane;
     const bool ok = i < N;
-    vv[b] = ok ? Vr[i] : 0.0f;
+    const bool cached = vmax && j0 + b < B - 1;
+    vv[b] = ok && !cached ? Vr[i] : -INFINITY;
     dd[b] = ok ? Dr[q - i] : 0.0f;
   }
   float* Srow = S + ((int64_t)r * rows + row) * max_blocks;
@@ -86,7 +93,8 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
     const int i = j * SPIN_BLOCK + lane;
     float zhat = combine == SPIN_COMBINE_SUM ? __fadd_rn(vv[b], dd[b]) : fmaxf(vv[b], dd[b]);
     zhat = i < N ? zhat : -INFINITY;
-    const float m = wave_max_f32(zhat);
+    const float m =
+        fmaxf(wave_max_f32(zhat), __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vm), b)));
     if (lane == 0 && j < B) Srow[j] = m + 0.0f;
   }
 }
@@ -225,14 +233,15 @@ __global__ void k_zero_i32(int32_t* __restrict__ p, int n) {
 // host launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
-                          const float* D, int64_t d_ld, float* S, hipStream_t st,
-                          int32_t* qpos_snap, uint32_t* xkeys) {
+                          const float* D, int64_t d_ld, const float* vmax, float* S,
+                          hipStream_t st, int32_t* qpos_snap, uint32_t* xkeys) {
   dim3 grid((b.max_blocks + 4 * kPredBlocksPerWave - 1) / (4 * kPredBlocksPerWave), b.n_rows,
             b.batch);
   const ExploreKeys xk{xkeys, b.step, b.req_id, c.layer, (uint32_t)(c.seed & 0xFFFFFFFFu),
                        (uint32_t)(c.seed >> 32)};
   hipLaunchKernelGGL(k_predict, grid, dim3(256), 0, st, c.combine, b.n_rows, b.max_blocks,
-                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld, S, b.err, qpos_snap, xk);
+                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld,
+                     c.combine == SPIN_COMBINE_MAX ? vmax : nullptr, S, b.err, qpos_snap, xk);
   return hipGetLastError();
 }
 
@@ -282,11 +291,12 @@ hipError_t launch_advance(int R, int rows, const int32_t* n_valid, int32_t* qpos
   return hipGetLastError();
 }
 
-hipError_t launch_reset(int R, float* V, int64_t v_ld, float* D, int64_t d_ld, int32_t* step,
-                        hipStream_t st) {
-  const int64_t nv = (int64_t)R * v_ld, nd = (int64_t)R * d_ld;
+hipError_t launch_reset(int R, float* V, int64_t v_ld, float* D, int64_t d_ld, int64_t vmax_ld,
+                        float* vmax, int32_t* step, hipStream_t st) {
+  const int64_t nv = (int64_t)R * v_ld, nd = (int64_t)R * d_ld, nm = (int64_t)R * vmax_ld;
   if (nv > 0) hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, V, nv);
   if (nd > 0) hipLaunchKernelGGL(k_fill_zero, dim3(1024), dim3(256), 0, st, D, nd);
+  if (vmax && nm > 0) hipLaunchKernelGGL(k_fill_zero, dim3(256), dim3(256), 0, st, vmax, nm);
   if (step) hipLaunchKernelGGL(k_zero_i32, dim3((R + 255) / 256), dim3(256), 0, st, step, R);
   return hipGetLastError();
 }

@@ -500,8 +500,8 @@ size_t step_workspace_bytes(const spin_config& c, int R, int rows, int max_block
 hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const float* z,
                            int64_t z_ld, const int32_t* sel, const int32_t* n_sel, int32_t* out,
                            void* wsp, const int32_t* n_valid, float* V, int64_t v_ld, float* D,
-                           int64_t d_ld, const int32_t* qpos_snap, int32_t* qpos_out,
-                           int32_t* step_out, hipStream_t st) {
+                           int64_t d_ld, float* vmax, const int32_t* qpos_snap,
+                           int32_t* qpos_out, int32_t* step_out, hipStream_t st) {
   const int rows_total = b.batch * b.n_rows;
   const TopkWs ws = carve(wsp, rows_total, b.max_blocks);
   constexpr int per_block = (kSelThreads / 64) * kEmaChunk;
@@ -509,7 +509,7 @@ hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const floa
   const int free_cus = resident_workgroups((const void*)k_topk_ema, kSelThreads) - rows_total;
   const int ema_x = max(1, min(most, free_cus / max(1, b.batch)));
   const EmaArgs A{c.ema_alpha, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap, n_valid, z, z_ld,
-                  sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out};
+                  sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out, vmax};
   hipLaunchKernelGGL(k_topk_ema, dim3(rows_total + ema_x * b.batch), dim3(kSelThreads), 0, st,
                      c.topk, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap, z, z_ld, sel, n_sel,
                      out, ws, rows_total, A, ema_x);

@@ -153,15 +153,16 @@ size_t spin_workspace_bytes(const spin_config* cfg, int32_t batch, int32_t n_row
 }
 
 spin_status spin_predict_blocks(const spin_config* cfg, const spin_batch* bt, const float* V,
-                                int64_t v_ld, const float* D, int64_t d_ld, float* S,
-                                void* stream) {
+                                int64_t v_ld, const float* D, int64_t d_ld, const float* v_max,
+                                float* S, void* stream) {
   const char* fn = "spin_predict_blocks";
   SPIN_CHECK(check_config(fn, cfg));
   SPIN_CHECK(check_batch(fn, bt));
   SPIN_CHECK(check_state(fn, bt, V, v_ld, D, d_ld));
   SPIN_REQUIRE(S);
   if (bt->batch == 0) return SPIN_OK;
-  return hip_status(spin::launch_predict(*cfg, *bt, V, v_ld, D, d_ld, S, (hipStream_t)stream), fn);
+  return hip_status(spin::launch_predict(*cfg, *bt, V, v_ld, D, d_ld, v_max, S, (hipStream_t)stream),
+                    fn);
 }
 
 spin_status spin_select_blocks(const spin_config* cfg, const spin_batch* bt, const float* S,
@@ -236,7 +237,7 @@ spin_status spin_topk(const spin_config* cfg, const spin_batch* bt, const float*
 spin_status spin_ema_update(const spin_config* cfg, const spin_batch* bt, const float* z,
                             int64_t z_ld, const int32_t* sel, const int32_t* n_sel,
                             const int32_t* n_valid, float* V, int64_t v_ld, float* D, int64_t d_ld,
-                            void* stream) {
+                            float* v_max, void* stream) {
   const char* fn = "spin_ema_update";
   SPIN_CHECK(check_config(fn, cfg));
   SPIN_CHECK(check_batch(fn, bt));
@@ -246,7 +247,7 @@ spin_status spin_ema_update(const spin_config* cfg, const spin_batch* bt, const 
   SPIN_REQUIRE(n_sel);
   if (bt->batch == 0) return SPIN_OK;
   return hip_status(spin::launch_ema(*cfg, *bt, z, z_ld, sel, n_sel, n_valid, V, v_ld, D, d_ld,
-                                     (hipStream_t)stream), fn);
+                                     v_max, (hipStream_t)stream), fn);
 }
 
 spin_status spin_advance(int32_t batch, int32_t n_rows, const int32_t* n_valid, int32_t* q_pos,
@@ -260,12 +261,14 @@ spin_status spin_advance(int32_t batch, int32_t n_rows, const int32_t* n_valid, 
 }
 
 spin_status spin_reset_state(int32_t batch, float* V, int64_t v_ld, float* D, int64_t d_ld,
-                             int32_t* step, void* stream) {
+                             float* v_max, int64_t vmax_ld, int32_t* step, void* stream) {
   const char* fn = "spin_reset_state";
-  if (batch < 0 || v_ld < 0 || d_ld < 0) return fail(SPIN_E_SHAPE, "%s: negative size", fn);
+  if (batch < 0 || v_ld < 0 || d_ld < 0 || vmax_ld < 0)
+    return fail(SPIN_E_SHAPE, "%s: negative size", fn);
   if (batch == 0) return SPIN_OK;
   if ((v_ld > 0 && !V) || (d_ld > 0 && !D)) return fail(SPIN_E_NULL, "%s: V or D is NULL", fn);
-  return hip_status(spin::launch_reset(batch, V, v_ld, D, d_ld, step, (hipStream_t)stream), fn);
+  return hip_status(spin::launch_reset(batch, V, v_ld, D, d_ld, v_max ? vmax_ld : 0, v_max, step,
+                                       (hipStream_t)stream), fn);
 }
 
 spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_step_io* io,
@@ -292,8 +295,9 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
   int32_t* qsnap = reinterpret_cast<int32_t*>(static_cast<char*>(io->workspace) + qsnap_off);
   uint32_t* xkeys = reinterpret_cast<uint32_t*>(static_cast<char*>(io->workspace) + qsnap_off +
                                                 ((4 * (size_t)bt->batch + 255) & ~size_t(255)));
-  SPIN_CHECK(hip_status(spin::launch_predict(*cfg, *bt, io->V, io->v_ld, io->D, io->d_ld, io->S, st,
-                                             qsnap, xkeys), "spin_step/predict"));
+  SPIN_CHECK(hip_status(spin::launch_predict(*cfg, *bt, io->V, io->v_ld, io->D, io->d_ld,
+                                             io->v_max, io->S, st, qsnap, xkeys),
+                        "spin_step/predict"));
   SPIN_CHECK(hip_status(spin::launch_select(*cfg, *bt, io->S, io->budget, io->row_code, io->sel,
                                             io->n_sel, st, xkeys), "spin_step/select"));
   // where the score kernel can, it also applies the top-K threshold filter
@@ -306,8 +310,8 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
   if (prefilter && !defer_ema) {  // top-K beside the EMA update, one launch
     SPIN_CHECK(hip_status(spin::launch_topk_ema(*cfg, *bt, io->z, io->z_ld, io->sel, io->n_sel,
                                                 io->topk_idx, io->workspace, io->n_valid, io->V,
-                                                io->v_ld, io->D, io->d_ld, qsnap, io->q_pos_mut,
-                                                io->step_mut, st),
+                                                io->v_ld, io->D, io->d_ld, io->v_max, qsnap,
+                                                io->q_pos_mut, io->step_mut, st),
                           "spin_step/topk+ema"));
     return SPIN_OK;
   }
@@ -319,8 +323,8 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
   // snapshot, so advancing q_pos_mut (normally the same array as bt->q_pos)
   // cannot race with its reads
   SPIN_CHECK(hip_status(spin::launch_ema(*cfg, *bt, io->z, io->z_ld, io->sel, io->n_sel,
-                                         io->n_valid, io->V, io->v_ld, io->D, io->d_ld, st, qsnap,
-                                         io->q_pos_mut, io->step_mut),
+                                         io->n_valid, io->V, io->v_ld, io->D, io->d_ld, io->v_max,
+                                         st, qsnap, io->q_pos_mut, io->step_mut),
                         "spin_step/ema+advance"));
   return SPIN_OK;
 }

@@ -24,9 +24,11 @@ struct CandSink {
 // fused EMA + advance of a whole step reads it instead of q_pos.
 // xkeys (optional, [R][max_blocks]): predict also writes the step's
 // exploration keys there, and select reads them instead of computing them.
+// vmax (optional, [R][max_blocks]): the V block maxima (max combine only).
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
-                          const float* D, int64_t d_ld, float* S, hipStream_t st,
-                          int32_t* qpos_snap = nullptr, uint32_t* xkeys = nullptr);
+                          const float* D, int64_t d_ld, const float* vmax, float* S,
+                          hipStream_t st, int32_t* qpos_snap = nullptr,
+                          uint32_t* xkeys = nullptr);
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
                          hipStream_t st, const uint32_t* xkeys = nullptr);
@@ -46,8 +48,8 @@ hipError_t launch_topk(const spin_config& c, const spin_batch& b, const float* z
 hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const float* z,
                            int64_t z_ld, const int32_t* sel, const int32_t* n_sel, int32_t* out,
                            void* ws, const int32_t* n_valid, float* V, int64_t v_ld, float* D,
-                           int64_t d_ld, const int32_t* qpos_snap, int32_t* qpos_out,
-                           int32_t* step_out, hipStream_t st);
+                           int64_t d_ld, float* vmax, const int32_t* qpos_snap,
+                           int32_t* qpos_out, int32_t* step_out, hipStream_t st);
 // The candidate sink inside a top-K workspace.
 CandSink topk_sink(void* ws, int R, int rows, int max_blocks);
 size_t topk_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks);
@@ -57,13 +59,13 @@ size_t step_workspace_bytes(const spin_config& c, int R, int rows, int max_block
 // advances qpos_out / step_out (each optional) like launch_advance.
 hipError_t launch_ema(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                       const int32_t* sel, const int32_t* n_sel, const int32_t* n_valid, float* V,
-                      int64_t v_ld, float* D, int64_t d_ld, hipStream_t st,
+                      int64_t v_ld, float* D, int64_t d_ld, float* vmax, hipStream_t st,
                       const int32_t* qpos_snap = nullptr, int32_t* qpos_out = nullptr,
                       int32_t* step_out = nullptr);
 hipError_t launch_advance(int R, int rows, const int32_t* n_valid, int32_t* qpos, int32_t* step,
                           hipStream_t st);
-hipError_t launch_reset(int R, float* V, int64_t v_ld, float* D, int64_t d_ld, int32_t* step,
-                        hipStream_t st);
+hipError_t launch_reset(int R, float* V, int64_t v_ld, float* D, int64_t d_ld, int64_t vmax_ld,
+                        float* vmax, int32_t* step, hipStream_t st);
 
 // Number of workgroups of `threads` threads of `kernel` resident at once on
 // the current device (occupancy x compute units), cached per kernel.

@@ -17,7 +17,7 @@ class SpinLayer:
     def __init__(self, *, batch: int, max_blocks: int, d_cap: int, topk: int, sparsity_bp: int,
                  n_rows: int = 1, explore_bp: int = 500, ema_alpha: float = 0.9,
                  combine: str = "max", key_dtype=torch.uint8, q_dtype=torch.bfloat16,
-                 layer: int = 0, seed: int = 0x5350494E, device="cuda"):
+                 layer: int = 0, seed: int = 0x5350494E, device="cuda", vmax_cache: bool = True):
         self.R, self.rows, self.max_blocks, self.K = batch, n_rows, max_blocks, topk
         self.cfg = api.config(topk=topk, sparsity_bp=sparsity_bp, explore_bp=explore_bp,
                               ema_alpha=ema_alpha, combine=combine, key_dtype=key_dtype,
@@ -27,6 +27,10 @@ class SpinLayer:
         n_cap = 64 * max_blocks
         self.V = torch.zeros(batch, n_cap, dtype=torch.float32, device=dev)
         self.D = torch.zeros(batch, d_cap, dtype=torch.float32, device=dev)
+        # block maxima of V: predict then reads one float per block instead of
+        # 64 (max combine); kept by reset, the EMA update and every step
+        self.v_max = torch.zeros(batch, max_blocks, dtype=torch.float32, device=dev) \
+            if vmax_cache else None
         self.S = torch.zeros(batch, n_rows, max_blocks, dtype=torch.float32, device=dev)
         self.row_code = torch.zeros(batch, n_rows, max_blocks, dtype=torch.uint8, device=dev)
         self.sel = torch.full((batch, max_blocks), -1, **i32)
@@ -53,7 +57,7 @@ class SpinLayer:
         self._bt = None
 
     def reset(self, stream=None):
-        api.spin_reset_state(self.V, self.D, self.step_ctr, stream=stream)
+        api.spin_reset_state(self.V, self.D, self.step_ctr, stream=stream, v_max=self.v_max)
 
     def batch(self, n_pages: int):
         if self._bt is None or self.n_pages != n_pages:
@@ -69,7 +73,7 @@ class SpinLayer:
                            page_table=page_table, S=self.S, row_code=self.row_code, sel=self.sel,
                            n_sel=self.n_sel, z=self.z, topk_idx=self.topk_idx, budget=budget,
                            n_valid=n_valid, q_pos_mut=self.q_pos, step_mut=self.step_ctr,
-                           workspace=self.workspace)
+                           workspace=self.workspace, v_max=self.v_max)
 
     def step(self, q, w, k_pages, k_scale, page_table, n_valid=None, budget=None,
              defer_ema: bool = False, stream=None):
@@ -82,5 +86,5 @@ class SpinLayer:
         """Deferred EMA replay of the first n_valid rows, then advance the counters."""
         bt = self.batch(self.n_pages)
         api.spin_ema_update(self.cfg, bt, self.z, self.sel, self.n_sel, self.V, self.D,
-                            n_valid=n_valid, stream=stream)
+                            n_valid=n_valid, stream=stream, v_max=self.v_max)
         api.spin_advance(self.rows, self.q_pos, self.step_ctr, n_valid=n_valid, stream=stream)

@@ -41,12 +41,37 @@ def test_every_declared_symbol_is_exported(lib):
     assert sorted(_lib.EXPORTS) == names
 
 
-def test_struct_layouts_match_header():
+def test_struct_layouts_match_header(tmp_path):
+    """ctypes layouts equal the C compiler's: size and every field offset of the
+    three structs, from a host program built against include/spin.h."""
+    import shutil
+    import subprocess
     from sparse_attention_indexer_spin_amd import _lib
-    # spin_config: 12 x int32/float + uint64 -> 56 bytes; spin_batch: 4 ints + 5 pointers
-    assert C.sizeof(_lib.SpinConfig) == 56
-    assert C.sizeof(_lib.SpinBatch) == 16 + 5 * 8
-    assert C.sizeof(_lib.SpinStepIO) == 23 * 8
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"spin_config": _lib.SpinConfig, "spin_batch": _lib.SpinBatch,
+               "spin_step_io": _lib.SpinStepIO}
+    lines = ['#include "spin.h"', "#include <stdio.h>", "#include <stddef.h>", "int main(void) {"]
+    for cname, ct in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in ct._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-I", inc, "-o", str(exe), str(src)], check=True)
+    got = dict()
+    for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                               text=True).stdout.splitlines():
+        cname, what, val = line.split()
+        got[(cname, what)] = int(val)
+    for cname, ct in structs.items():
+        assert got[(cname, "size")] == C.sizeof(ct), cname
+        for fname, _ in ct._fields_:
+            assert got[(cname, fname)] == getattr(ct, fname).offset, (cname, fname)
 
 
 def _cfg(**kw):
@@ -61,11 +86,11 @@ def test_host_validation_without_gpu(lib):
     bt = _lib.SpinBatch(batch=1, n_rows=1, max_blocks=16, n_pages=16, ctx_len=1, q_pos=1,
                         step=1, req_id=1, err=None)
     # NULL state
-    st = lib.spin_predict_blocks(C.byref(cfg), C.byref(bt), None, 64, None, 64, None, None)
+    st = lib.spin_predict_blocks(C.byref(cfg), C.byref(bt), None, 64, None, 64, None, None, None)
     assert st == 1 and b"NULL" in lib.spin_last_error()
     # unsupported head shape
     bad = _cfg(n_heads=32)
-    assert lib.spin_predict_blocks(C.byref(bad), C.byref(bt), 1, 64, 1, 64, 1, None) == 3
+    assert lib.spin_predict_blocks(C.byref(bad), C.byref(bt), 1, 64, 1, 64, None, 1, None) == 3
     # block size other than 64
     bad = _cfg(block_size=32)
     assert lib.spin_select_blocks(C.byref(bad), C.byref(bt), 1, None, 1, 1, 1, None) == 3
@@ -91,7 +116,9 @@ def test_host_validation_without_gpu(lib):
     # an empty batch is a valid no-op
     bt0 = _lib.SpinBatch(batch=0, n_rows=1, max_blocks=16, n_pages=16, ctx_len=None,
                          q_pos=None, step=None, req_id=None, err=None)
-    assert lib.spin_predict_blocks(C.byref(cfg), C.byref(bt0), 1, 64, 1, 64, 1, None) == 0
+    assert lib.spin_predict_blocks(C.byref(cfg), C.byref(bt0), 1, 64, 1, 64, None, 1, None) == 0
+    assert lib.spin_reset_state(0, None, 0, None, 0, None, 0, None, None) == 0
+    assert lib.spin_reset_state(1, None, -1, None, 0, None, 0, None, None) == 2
     assert lib.spin_advance(0, 1, None, None, None, None) == 0
     assert lib.spin_advance(1, 9, None, None, None, None) == 2
     assert lib.spin_workspace_bytes(C.byref(cfg), 32, 1, 2048) >= 0

@@ -73,6 +73,66 @@ def test_predict_parity(rows, combine):
     assert int(keep["err"].item()) == 0
 
 
+def _signed_state(ctx, mb, d_cap, seed):
+    """V of mixed sign (every third request all negative) with V = 0 past each
+    context end, D non-negative, and the V block maxima over all 64 slots."""
+    V, D = G.make_ema_state(len(ctx), 64 * mb, d_cap, seed=seed, ties=True, zero_frac=0.2)
+    for r, N in enumerate(ctx):
+        if r % 3 == 0:
+            V[r] = -V[r] - 1.0
+        V[r, N:] = 0.0
+    vmax = V.view(len(ctx), mb, 64).amax(dim=2)
+    return V, D, vmax
+
+
+@pytest.mark.parametrize("rows", [1, 4])
+@pytest.mark.parametrize("combine", ["max", "sum"])
+def test_predict_parity_vmax(rows, combine):
+    """With the V block maxima (max combine: one float per block instead of 64
+    V values, the last block read in full) S still equals the oracle's."""
+    banner(f"predict vmax rows={rows} combine={combine}")
+    A = api()
+    ctx = [4096, 4000, 130, 64, 1, 4095]
+    mb = 64
+    qpos = [c + 7 for c in ctx]
+    V, D, vmax = _signed_state(ctx, mb, 4096 + 64, seed=31)
+    bt, keep = _batch(ctx, qpos, [3] * len(ctx), rows, mb)
+    cfg = A.config(topk=512, sparsity_bp=4000, combine=combine)
+    S = torch.full((len(ctx), rows, mb), -7.0, device=DEV)
+    A.spin_predict_blocks(cfg, bt, V.to(DEV), D.to(DEV), S, v_max=vmax.to(DEV))
+    S = S.cpu().numpy()
+    for r, N in enumerate(ctx):
+        B = O.n_blocks(N)
+        for row in range(rows):
+            want = O.predict_block_scores(V[r].numpy(), D[r].numpy(), N, qpos[r] + row, combine)
+            assert np.array_equal(S[r, row, :B], want), (r, row)
+    assert int(keep["err"].item()) == 0
+
+
+@pytest.mark.parametrize("rows", [1, 4])
+def test_ema_keeps_vmax(rows):
+    """The EMA update refreshes the block maxima of the blocks it updates: after
+    it, every block's entry equals the max of V over its 64 slots."""
+    banner(f"ema vmax rows={rows}")
+    A = api()
+    ctx = [131072, 9000, 4096 + 33, 64, 1]
+    R, mb = len(ctx), 2048
+    V, D, vmax = _signed_state(ctx, mb, 131072 + 64, seed=41)
+    sel, n_sel = G.make_selection(R, torch.tensor([O.n_blocks(c) for c in ctx]), mb, 0.5, seed=6)
+    zin = G.make_scores((R, rows, 64 * mb), seed=42, signed=True)
+    g = torch.Generator().manual_seed(7)
+    n_valid = torch.randint(1, rows + 1, (R,), generator=g, dtype=torch.int32)
+    bt, keep = _batch(ctx, [c + 11 for c in ctx], [4] * R, rows, mb)
+    cfg = A.config(topk=2048, sparsity_bp=4000, ema_alpha=0.9)
+    Vd, Dd, Md = V.to(DEV), D.to(DEV), vmax.to(DEV)
+    A.spin_ema_update(cfg, bt, zin.to(DEV), sel.to(DEV), n_sel.to(DEV), Vd, Dd,
+                      n_valid=n_valid.to(DEV), v_max=Md)
+    want = Vd.view(R, mb, 64).amax(dim=2)
+    assert torch.equal(Md, want)
+    assert not torch.equal(Md, vmax.to(DEV))  # the update did move some maxima
+    assert int(keep["err"].item()) == 0
+
+
 # ---------------------------------------------------------------------------
 # stage 2: select (+ union)
 # ---------------------------------------------------------------------------
