@@ -102,13 +102,14 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
     // one observation per slot: V[i] and D[q - i] from row 0, loads batched
     for (int kb = k0; kb < k1; kb += CH) {
       float vv[CH], dd[CH], zz[CH];
-      int ii[CH];
+      int ii[CH], jj[CH];
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
         const int k = kb + u;
         const int j = k < k1 ? sr[k] : -1;
         const int i = j * 64 + lane;
         const bool ok = k < k1 && j >= 0 && j < max_blocks && i < N;
+        jj[u] = k < k1 && j >= 0 && j < max_blocks ? j : -1;
         ii[u] = ok ? i : -1;
         vv[u] = ok ? Vr[i] : 0.0f;
         dd[u] = ok ? Dr[q - i] : 0.0f;
@@ -121,10 +122,9 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
           Vr[ii[u]] = vn;
           Dr[q - ii[u]] = ema_step(dd[u], zz[u], a, b);
         }
-        if (A.vmax && kb + u < k1) {
-          const int j = sr[kb + u];
-          if (j >= 0 && j < max_blocks) ema_vmax(A, r, j, ii[u] >= 0, vn);
-        }
+        // (the block id from before the stores: sel may alias V or D for all
+        // the compiler knows, and a reload would wait for them)
+        if (A.vmax && jj[u] >= 0) ema_vmax(A, r, jj[u], ii[u] >= 0, vn);
       }
     }
     return;

@@ -100,11 +100,12 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2: one workgroup per (request, verifier row); kSelectThreads threads
-// (4 waves: the selection is a chain of block-wide steps, each ending in a
-// barrier, which costs less over fewer waves), EPT blocks per thread.
+// Stage 2: one workgroup per (request, verifier row); kSelectThreads threads,
+// EPT blocks per thread.  The selection is a chain of block-wide radix steps
+// whose wave scans run on DPP moves, so wide workgroups (few keys per thread
+// per histogram pass) beat narrow ones despite their larger barriers.
 // ---------------------------------------------------------------------------
-constexpr int kSelectThreads = 256;
+constexpr int kSelectThreads = 1024;
 
 template <int EPT>
 __global__ __launch_bounds__(kSelectThreads) void k_select(

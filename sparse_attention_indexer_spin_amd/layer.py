@@ -17,7 +17,7 @@ class SpinLayer:
     def __init__(self, *, batch: int, max_blocks: int, d_cap: int, topk: int, sparsity_bp: int,
                  n_rows: int = 1, explore_bp: int = 500, ema_alpha: float = 0.9,
                  combine: str = "max", key_dtype=torch.uint8, q_dtype=torch.bfloat16,
-                 layer: int = 0, seed: int = 0x5350494E, device="cuda", vmax_cache: bool = True):
+                 layer: int = 0, seed: int = 0x5350494E, device="cuda", vmax_cache: bool = False):
         self.R, self.rows, self.max_blocks, self.K = batch, n_rows, max_blocks, topk
         self.cfg = api.config(topk=topk, sparsity_bp=sparsity_bp, explore_bp=explore_bp,
                               ema_alpha=ema_alpha, combine=combine, key_dtype=key_dtype,
@@ -27,8 +27,10 @@ class SpinLayer:
         n_cap = 64 * max_blocks
         self.V = torch.zeros(batch, n_cap, dtype=torch.float32, device=dev)
         self.D = torch.zeros(batch, d_cap, dtype=torch.float32, device=dev)
-        # block maxima of V: predict then reads one float per block instead of
-        # 64 (max combine); kept by reset, the EMA update and every step
+        # optional block maxima of V: predict then reads one float per block
+        # instead of 64 (max combine), kept by reset, the EMA update and every
+        # step.  Off by default: the predict kernel is latency-bound, so the
+        # bytes it saves buy less than the upkeep costs the EMA update.
         self.v_max = torch.zeros(batch, max_blocks, dtype=torch.float32, device=dev) \
             if vmax_cache else None
         self.S = torch.zeros(batch, n_rows, max_blocks, dtype=torch.float32, device=dev)

@@ -24,14 +24,15 @@ def device_keys(li: LayerInputs):
     return pages, scale, li.keys.page_table.to(DEV)
 
 
-def make_layer(li: LayerInputs, sparsity_bp: int, seed=G.PHILOX_SEED, combine=None):
+def make_layer(li: LayerInputs, sparsity_bp: int, seed=G.PHILOX_SEED, combine=None,
+               vmax_cache: bool = False):
     from sparse_attention_indexer_spin_amd import SpinLayer
     w = li.w
     lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks, d_cap=d_capacity(w, w.steps),
                     topk=w.topk, sparsity_bp=sparsity_bp, n_rows=w.rows,
                     explore_bp=w.explore_bp, ema_alpha=w.alpha, combine=combine or w.combine,
                     key_dtype=KEY_TORCH[w.key_dtype], q_dtype=Q_TORCH[w.q_dtype],
-                    layer=li.layer, seed=seed, device=DEV)
+                    layer=li.layer, seed=seed, device=DEV, vmax_cache=vmax_cache)
     lay.set_requests(li.ctx.to(DEV), li.pos[0].to(DEV))
     lay.reset()
     return lay

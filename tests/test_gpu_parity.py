@@ -370,15 +370,17 @@ CLOSED = {
 }
 
 
-@pytest.mark.parametrize("name", list(CLOSED))
+@pytest.mark.parametrize("name,vmax", [(n, False) for n in CLOSED] + [("fp8", True),
+                                                                      ("fp8_mtp", True)])
 @pytest.mark.parametrize("deferred", [False, True])
-def test_closed_loop_exact(name, deferred):
-    banner(f"closed loop {name} deferred={deferred}")
+def test_closed_loop_exact(name, vmax, deferred):
+    """vmax: the layer keeps the V block maxima and predict reads them."""
+    banner(f"closed loop {name} vmax={vmax} deferred={deferred}")
     w = CLOSED[name]
     li = build_layer(w, integer=True)
     sp = w.sparsity_bp[0]
     ref, _ = run_oracle(li, w.steps, sp)
-    lay = make_layer(li, sp)
+    lay = make_layer(li, sp, vmax_cache=vmax)
     pages, scale, pt = device_keys(li)
     W = li.weights.to(DEV)
     for s in range(w.steps):
