@@ -8,13 +8,17 @@ path: predict -> select -> sparse indexer score -> top-K -> EMA -> advance,
 each launched through the C ABI on the current stream, inputs resident in HBM.
 
 Prints one JSON line.  `value` = indexer keys scored per second of whole-step
-time (one spin_step call per step).  `roofline` is the score kernel's
-algorithmic HBM bytes per launch / its mean launch duration (HIP events around
-back-to-back launches on the step's stream, on the last timed step's
-selection) against 8 TB/s, with `traffic` taken from the committed
-FETCH_SIZE/WRITE_SIZE summary when it was measured on the current kernel
-source.  `cpu_baseline` times the CPU oracle on whole requests of the same
-workload for about 15 s.
+time (one spin_step call per step).  By default every timed step (and every
+timed stage launch) starts with cold caches: a 1 GiB read streams through the
+L2s and the 256 MB MALL just before it, as when a model's other layers run
+between two steps of this layer, so no key page is served from a cache warmed
+by the previous step; `warm` repeats the step timing back to back for
+reference.  `roofline` is the score kernel's algorithmic HBM bytes per launch /
+its mean launch duration (HIP events around each launch on the step's stream,
+on the last timed step's selection) against 8 TB/s, with `traffic` taken from
+the committed FETCH_SIZE/WRITE_SIZE summary when it was measured on the
+current kernel source.  `cpu_baseline` times the CPU oracle on whole requests
+of the same workload for about 15 s.
 """
 from __future__ import annotations
 
@@ -45,6 +49,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="also time the workload's sparsity sweep and fit t = a(1-rho) + c")
     ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--cache", choices=["cold", "warm"], default="cold",
+                    help="cold: evict the caches before every timed step and stage launch")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-max-requests", type=int, default=32)
@@ -82,23 +88,47 @@ def algorithmic_score_bytes(w: G.Workload, slots: float, n_blocks_sel: float):
     return slots * per_slot + n_blocks_sel * per_block + w.batch * per_req
 
 
-def _timed_us(fn, reps: int, stream) -> float:
-    """Mean duration of `fn` over `reps` back-to-back launches (HIP events on `stream`)."""
+class Evictor:
+    """Reads a 1 GiB buffer: afterwards the L2s and the 256 MB MALL hold clean,
+    unrelated lines, as after the other layers of a model ran."""
+
+    def __init__(self, dev="cuda"):
+        self.buf = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.buf.sum()
+
+
+def _timed_us(fn, reps: int, stream, evict=None) -> float:
+    """Mean duration of `fn` over `reps` launches (HIP events on `stream`):
+    back to back, or each one after `evict` (outside its events)."""
     fn()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
+    if evict is None:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        evict()
+        a.record(stream)
         fn()
-    e1.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps * 1e3
+    return sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
 
 
-def run_gpu(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_reps: int = 0):
+def run_gpu(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_reps: int = 0,
+            evict=None):
     """Time `steps` decode steps (one spin_step call each) after `warmup` untimed
-    ones; with stage_reps > 0, then time each stage alone on the last step's inputs."""
+    ones; with stage_reps > 0, then time each stage alone on the last step's inputs.
+    With `evict`, every timed step and stage launch runs after it (cold caches)."""
     from sparse_attention_indexer_spin_amd import SpinLayer, api
     w = inp.w
     lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks, d_cap=G.d_capacity(w, steps + warmup),
@@ -118,14 +148,25 @@ def run_gpu(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_reps: 
     for s in range(warmup):
         api.spin_step(lay.cfg, bt, ios[s])
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for s in range(warmup, warmup + steps):
-        api.spin_step(lay.cfg, bt, ios[s])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
+    if evict is None:
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for s in range(warmup, warmup + steps):
+            api.spin_step(lay.cfg, bt, ios[s])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t0.elapsed_time(t1)
+    else:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for k, s in enumerate(range(warmup, warmup + steps)):
+            evict()
+            ev[k][0].record(stream)
+            api.spin_step(lay.cfg, bt, ios[s])
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        total_ms = sum(a.elapsed_time(b) for a, b in ev)
     assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
     n_sel = lay.n_sel.cpu().numpy().astype(np.int64)
     ctx = lay.ctx_len.cpu().numpy().astype(np.int64)
@@ -149,7 +190,7 @@ def run_gpu(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_reps: 
             "ema": lambda: api.spin_ema_update(lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.V,
                                                lay.D, n_valid=last_nv, v_max=lay.v_max),
         }
-        out["stage_us"] = {k: _timed_us(f, stage_reps, stream) for k, f in st.items()}
+        out["stage_us"] = {k: _timed_us(f, stage_reps, stream, evict) for k, f in st.items()}
         assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
     return out
 
@@ -254,7 +295,10 @@ def main():
     sp = w.sparsity_bp[0] if args.sparsity_bp is None else args.sparsity_bp
     total_steps = args.steps + args.warmup
     inp = Inputs(w, total_steps)
-    res = run_gpu(inp, sp, args.steps, args.warmup, stage_reps=args.stage_reps)
+    evict = Evictor() if args.cache == "cold" else None
+    # back-to-back steps first, for reference; then the timed protocol
+    warm = run_gpu(inp, sp, args.steps, args.warmup) if evict is not None else None
+    res = run_gpu(inp, sp, args.steps, args.warmup, stage_reps=args.stage_reps, evict=evict)
     score_us = res["stage_us"]["score"]
     keys_row = res["keys_per_step"]
     score_bytes = algorithmic_score_bytes(w, keys_row // w.rows, res["n_sel"])
@@ -271,6 +315,10 @@ def main():
                    "sparsity_bp": sp, "explore_bp": w.explore_bp, "key_dtype": w.key_dtype,
                    "q_dtype": w.q_dtype},
         "us_per_step_layer": res["ms_per_step"] * 1e3,
+        "cache": {"mode": args.cache,
+                  "how": "1 GiB read before each timed step and stage launch" if evict is not None
+                  else "steps back to back",
+                  "warm_us_per_step_layer": None if warm is None else warm["ms_per_step"] * 1e3},
         "stage_us": res["stage_us"],
         "keys_scored_per_step": keys_row,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -283,7 +331,8 @@ def main():
     if args.sweep and w.rows == 1 and len(w.sparsity_bp) > 1:
         sweep = {}
         for s in sorted(set(w.sparsity_bp)):
-            sweep[s] = run_gpu(inp, s, min(args.steps, 20), args.warmup, stage_reps=10)
+            sweep[s] = run_gpu(inp, s, min(args.steps, 20), args.warmup, stage_reps=10,
+                               evict=evict)
         rho = np.array([1.0 - sweep[s]["n_sel"] / (w.batch * w.max_blocks) for s in sweep])
         T = np.array([sweep[s]["ms_per_step"] * 1e3 for s in sweep])
         A = np.stack([1.0 - rho, np.ones_like(rho)], 1)
