@@ -39,6 +39,7 @@ __device__ __forceinline__ void ema_offset(const EmaCtx& e, int s0, float* Dr) {
 }
 
 constexpr int kEmaBlocksPerWave = 4;
+constexpr int kEmaChunkRows = 3;  // blocks whose loads a several-row EMA wave issues together
 
 struct EmaArgs {
   float alpha;
@@ -106,7 +107,7 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
         const int k = kb + u;
-        const int j = k < k1 ? sr[k] : -1;
+        const int j = k < k1 ? __builtin_amdgcn_readfirstlane(sr[k]) : -1;  // uniform
         const int i = j * 64 + lane;
         const bool ok = k < k1 && j >= 0 && j < max_blocks && i < N;
         jj[u] = k < k1 && j >= 0 && j < max_blocks ? j : -1;
@@ -129,27 +130,100 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
     }
     return;
   }
-  for (int k = k0; k < k1; ++k) {
-    EmaCtx e;
-    e.a = a; e.b = b;
-    e.L = L; e.N = N; e.q = q; e.k = k; e.ns = ns;
-    e.j = sr[k];
-    if (e.j < 0 || e.j >= max_blocks) continue;
-    e.zb = zb;
-    e.z_ld = z_ld;
-    e.sel = sr;
-    const int i = e.j * 64 + lane;
-    float v = 0.0f;
-    if (i < N) {
-      v = Vr[i];
-      for (int row = 0; row < L; ++row) v = ema_step(v, zb[row * z_ld + (int64_t)k * 64 + lane], a, b);
-      Vr[i] = v;
+  // several rows: kEmaChunkRows blocks at a time, every load of the chunk
+  // (V, the rows' z, the D offsets the lanes own and the z values that reach
+  // them) issued before any update.  The blocks of a chunk touch disjoint V
+  // and D elements, so no load can depend on a store of the same chunk.
+  constexpr int CR = kEmaChunkRows;
+  // the block ids of 64 of the wave's blocks and of their neighbours in the
+  // list, one lane each, loaded ahead of the chunks that use them
+  int lb = k0, s_cur = -1, s_next = -1, s_prev = -1;
+  const auto load_ids = [&](int base) {
+    lb = base;
+    const int k = base + lane;
+    s_cur = k < k1 ? sr[k] : -1;
+    s_next = k + 1 < ns ? sr[k + 1] : -1;
+    s_prev = k > 0 && k - 1 < ns ? sr[k - 1] : -1;
+  };
+  load_ids(k0);
+  for (int kb = k0; kb < k1; kb += CR) {
+    if (kb + CR - 1 - lb >= 64) load_ids(kb);
+    int jj[CR], kn[CR];
+    bool pe[CR];
+    float vV[CR], zV[CR][SPIN_MAX_ROWS];
+    float dM[CR], zM[CR][SPIN_MAX_ROWS];
+    float dE[CR], zE[CR][SPIN_MAX_ROWS];
+    uint32_t mM[CR], mE[CR];  // bit row: that row updates the offset
+#pragma unroll
+    for (int u = 0; u < CR; ++u) {
+      const int k = kb + u;
+      const int j = k < k1 ? __builtin_amdgcn_readlane(s_cur, k - lb) : -1;  // uniform
+      jj[u] = (j >= 0 && j < max_blocks) ? j : -1;
+      // block j + 1 selected (rows past the block's end land there) and
+      // block j - 1 not selected (this block then owns the offsets of the up
+      // to L - 1 slots left of it)
+      const bool next_sel =
+          jj[u] >= 0 && k + 1 < ns && __builtin_amdgcn_readlane(s_next, k - lb) == j + 1;
+      pe[u] = jj[u] >= 0 && !(k > 0 && __builtin_amdgcn_readlane(s_prev, k - lb) == j - 1) &&
+              lane < L - 1;
+      kn[u] = next_sel ? k + 1 : -1;
+      const int i = j * 64 + lane;
+      vV[u] = 0.0f;
+      dM[u] = 0.0f;
+      dE[u] = 0.0f;
+      mM[u] = 0u;
+      mE[u] = 0u;
+#pragma unroll
+      for (int row = 0; row < SPIN_MAX_ROWS; ++row) {
+        zV[u][row] = 0.0f;
+        zM[u][row] = 0.0f;
+        zE[u][row] = 0.0f;
+      }
+      if (jj[u] < 0) continue;
+      if (i < N) {
+        vV[u] = Vr[i];
+        dM[u] = Dr[q - i];
+      }
+#pragma unroll
+      for (int row = 0; row < SPIN_MAX_ROWS; ++row) {
+        if (row >= L) break;
+        if (i < N) zV[u][row] = zb[row * z_ld + (int64_t)k * 64 + lane];
+        // offset q - i, row `row`: slot i + row, in block j or (if selected) j + 1
+        const int sm = i + row;
+        if (i < N && sm < N) {
+          const int kk = (sm >> 6) == j ? k : kn[u];
+          if (kk >= 0) {
+            zM[u][row] = zb[row * z_ld + (int64_t)kk * 64 + (sm & 63)];
+            mM[u] |= 1u << row;
+          }
+        }
+        // extension offset q - s0, s0 = 64 j - 1 - lane: slot s0 + row in block j
+        const int se = j * 64 - 1 - lane + row;
+        if (pe[u] && se >= j * 64 && se < N) {
+          zE[u][row] = zb[row * z_ld + (int64_t)k * 64 + (se & 63)];
+          mE[u] |= 1u << row;
+        }
+      }
+      if (mE[u]) dE[u] = Dr[q - (j * 64 - 1 - lane)];
     }
-    if (A.vmax) ema_vmax(A, r, e.j, i < N, v);
-    ema_offset(e, i, Dr);
-    if (lane < L - 1) {
-      const bool prev_selected = k > 0 && sr[k - 1] == e.j - 1;
-      if (!prev_selected) ema_offset(e, e.j * 64 - 1 - lane, Dr);
+#pragma unroll
+    for (int u = 0; u < CR; ++u) {
+      if (jj[u] < 0) continue;
+      const int i = jj[u] * 64 + lane;
+      float v = vV[u], d = dM[u], de = dE[u];
+#pragma unroll
+      for (int row = 0; row < SPIN_MAX_ROWS; ++row) {
+        if (row >= L) break;
+        v = ema_step(v, zV[u][row], a, b);
+        if (mM[u] >> row & 1u) d = ema_step(d, zM[u][row], a, b);
+        if (mE[u] >> row & 1u) de = ema_step(de, zE[u][row], a, b);
+      }
+      if (i < N) {
+        Vr[i] = v;
+        Dr[q - i] = d;
+      }
+      if (mE[u]) Dr[q - (jj[u] * 64 - 1 - lane)] = de;
+      if (A.vmax) ema_vmax(A, r, jj[u], i < N, v);
     }
   }
 }
