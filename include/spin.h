@@ -232,8 +232,7 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
  * buffer holds the top-K threshold hints and candidate lists (any initial
  * contents are valid: a hint only changes speed) followed, for spin_step, by
  * the step's q_pos snapshot that lets one kernel run the EMA update and the
- * counter advance together, and the step's exploration keys, which predict
- * computes for select.  One workspace per layer; calls that share a
+ * counter advance together.  One workspace per layer; calls that share a
  * workspace must not overlap.
  */
 size_t spin_workspace_bytes(const spin_config* cfg, int32_t batch, int32_t n_rows,

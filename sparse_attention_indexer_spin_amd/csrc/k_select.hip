@@ -28,65 +28,28 @@ __device__ __forceinline__ uint32_t explore_key(int j, int t, int layer, int req
                        seed_hi);
 }
 
-// Where predict writes the exploration keys for the select of the same step
-// (out == nullptr: select computes them itself).
-struct ExploreKeys {
-  uint32_t* out;  // [R][max_blocks]
-  const int32_t* step;
-  const int32_t* req_id;
-  int layer;
-  uint32_t seed_lo, seed_hi;
-};
-
 constexpr int kPredBlocksPerWave = 8;
 
-__global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_blocks,
-                                                 const int32_t* __restrict__ ctx,
-                                                 const int32_t* __restrict__ qpos,
-                                                 const float* __restrict__ V, int64_t v_ld,
-                                                 const float* __restrict__ D, int64_t d_ld,
-                                                 const float* __restrict__ vmax,
-                                                 float* __restrict__ S, int32_t* err,
-                                                 int32_t* __restrict__ qpos_snap, ExploreKeys xk) {
-  const int r = blockIdx.z, row = blockIdx.y;
-  const int N = ctx[r], q0 = qpos[r];
-  // a whole step keeps the step's query position here for the fused EMA +
-  // counter advance, which then never reads the array it advances
-  if (qpos_snap && blockIdx.x == 0 && row == 0 && threadIdx.x == 0) qpos_snap[r] = q0;
-  const int e = request_error(N, q0, rows, max_blocks, v_ld, d_ld);
-  if (e) {
-    if (row == 0 && blockIdx.x == 0 && threadIdx.x == 0) raise_error(err, e);
-    return;
-  }
-  const int q = q0 + row;
-  const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j0 = (blockIdx.x * 4 + wave) * kPredBlocksPerWave;
-  if (j0 >= B) return;
-  // the exploration keys of these blocks (row 0 only; the rows share them)
-  if (xk.out && row == 0 && lane < kPredBlocksPerWave && j0 + lane < B) {
-    const int t = xk.step[r];
-    if (t > 0)
-      xk.out[(int64_t)r * max_blocks + j0 + lane] =
-          explore_key(j0 + lane, t, xk.layer, xk.req_id[r], xk.seed_lo, xk.seed_hi);
-  }
-  const float* Vr = V + (int64_t)r * v_ld;
-  const float* Dr = D + (int64_t)r * d_ld;
+// One wave's 8 blocks j0 .. j0+7 (j0 < B) of one (request, row).
+__device__ __forceinline__ void predict_wave(int combine, int N, int B, int q, int j0,
+                                             const float* __restrict__ Vr,
+                                             const float* __restrict__ Dr,
+                                             const float* __restrict__ vmax_r,
+                                             float* __restrict__ Srow) {
+  const int lane = threadIdx.x & 63;
   // with the V block maxima (max combine), every block but the last reads
   // its V max (lane b holds block j0 + b's) instead of its 64 V values
-  const float vm = vmax && lane < kPredBlocksPerWave && j0 + lane < B - 1
-                       ? vmax[(int64_t)r * max_blocks + j0 + lane]
-                       : -INFINITY;
+  const float vm = vmax_r && lane < kPredBlocksPerWave && j0 + lane < B - 1 ? vmax_r[j0 + lane]
+                                                                             : -INFINITY;
   float vv[kPredBlocksPerWave], dd[kPredBlocksPerWave];
 #pragma unroll
   for (int b = 0; b < kPredBlocksPerWave; ++b) {
     const int i = (j0 + b) * SPIN_BLOCK + lane;
     const bool ok = i < N;
-    const bool cached = vmax && j0 + b < B - 1;
+    const bool cached = vmax_r && j0 + b < B - 1;
     vv[b] = ok && !cached ? Vr[i] : -INFINITY;
     dd[b] = ok ? Dr[q - i] : 0.0f;
   }
-  float* Srow = S + ((int64_t)r * rows + row) * max_blocks;
 #pragma unroll
   for (int b = 0; b < kPredBlocksPerWave; ++b) {
     const int j = j0 + b;
@@ -99,6 +62,32 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
   }
 }
 
+__global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_blocks,
+                                                 const int32_t* __restrict__ ctx,
+                                                 const int32_t* __restrict__ qpos,
+                                                 const float* __restrict__ V, int64_t v_ld,
+                                                 const float* __restrict__ D, int64_t d_ld,
+                                                 const float* __restrict__ vmax,
+                                                 float* __restrict__ S, int32_t* err,
+                                                 int32_t* __restrict__ qpos_snap) {
+  const int r = blockIdx.z, row = blockIdx.y;
+  const int N = ctx[r], q0 = qpos[r];
+  // a whole step keeps the step's query position here for the fused EMA +
+  // counter advance, which then never reads the array it advances
+  if (qpos_snap && blockIdx.x == 0 && row == 0 && threadIdx.x == 0) qpos_snap[r] = q0;
+  const int e = request_error(N, q0, rows, max_blocks, v_ld, d_ld);
+  if (e) {
+    if (row == 0 && blockIdx.x == 0 && threadIdx.x == 0) raise_error(err, e);
+    return;
+  }
+  const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  const int j0 = (blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * kPredBlocksPerWave;
+  if (j0 >= B) return;
+  predict_wave(combine, N, B, q0 + row, j0, V + (int64_t)r * v_ld, D + (int64_t)r * d_ld,
+               vmax ? vmax + (int64_t)r * max_blocks : nullptr,
+               S + ((int64_t)r * rows + row) * max_blocks);
+}
+
 // ---------------------------------------------------------------------------
 // Stage 2: one workgroup per (request, verifier row); kSelectThreads threads,
 // EPT blocks per thread.  The selection is a chain of block-wide radix steps
@@ -107,24 +96,31 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
 // ---------------------------------------------------------------------------
 constexpr int kSelectThreads = 1024;
 
+struct SelectArgs {
+  int K, sparsity_bp, explore_bp, layer;
+  uint32_t seed_lo, seed_hi;
+  int rows, max_blocks;
+  uint8_t* code;   // [R][rows][max_blocks]
+  int32_t* sel;    // [R][max_blocks]
+  int32_t* n_sel;  // [R]
+};
+
+struct SelectLds {
+  int hist[512];
+  int sh[32];
+  uint32_t tmpu[32];
+};
+
+// Block budget, forced / ranked / explored blocks and (compact) the block
+// list of request r, row `row`: B blocks (0 when the request is invalid), t
+// steps since reset, rid the request id, bud a budget override (<= 0: none).
+// Every thread of the workgroup calls it.
 template <int EPT>
-__global__ __launch_bounds__(kSelectThreads) void k_select(
-    int K, int sparsity_bp, int explore_bp, int layer, uint32_t seed_lo, uint32_t seed_hi,
-    int rows, int max_blocks, const int32_t* __restrict__ ctx, const int32_t* __restrict__ qpos,
-    const int32_t* __restrict__ step, const int32_t* __restrict__ req_id,
-    const float* __restrict__ S, const int32_t* __restrict__ budget, uint8_t* __restrict__ code,
-    int32_t* __restrict__ sel, int32_t* __restrict__ n_sel, int compact,
-    const uint32_t* __restrict__ xkeys) {
-  __shared__ int hist[512];
-  __shared__ int sh[32];
-  __shared__ uint32_t tmpu[32];
-  const int row = blockIdx.x, r = blockIdx.y;
-  const int N = ctx[r];
-  const bool bad = request_error(N, qpos[r], rows, max_blocks, 0, 0) != 0;
-  const int B = bad ? 0 : (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
-  const int t = step[r];
+__device__ __forceinline__ void select_row(const SelectArgs& a, int r, int row, int B, int t,
+                                           int rid, int bud, const float* __restrict__ Srow,
+                                           bool compact, SelectLds& L) {
   const int j0 = threadIdx.x * EPT;
-  uint8_t* crow = code + ((int64_t)r * rows + row) * max_blocks;
+  uint8_t* crow = a.code + ((int64_t)r * a.rows + row) * a.max_blocks;
   uint32_t chosen = 0u;
   uint8_t c[EPT];
 #pragma unroll
@@ -135,26 +131,16 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     for (int e = 0; e < EPT; ++e)
       if (j0 + e < B) { c[e] = SPIN_CODE_DENSE; chosen |= 1u << e; }
   } else if (B > 0) {
-    const int kb = (K + SPIN_BLOCK - 1) / SPIN_BLOCK;
-    const int keep = (int)(((int64_t)(10000 - sparsity_bp) * B + 9999) / 10000);
-    int m = (budget && budget[r] > 0) ? min(B, (int)budget[r]) : min(B, max(kb, keep));
+    const int kb = (a.K + SPIN_BLOCK - 1) / SPIN_BLOCK;
+    const int keep = (int)(((int64_t)(10000 - a.sparsity_bp) * B + 9999) / 10000);
+    int m = bud > 0 ? min(B, bud) : min(B, max(kb, keep));
     const int n_f = B > 1 ? 2 : 1;
     m = max(m, n_f);
-    const int n_e = min((int)((int64_t)m * explore_bp / 10000), m - n_f);
+    const int n_e = min((int)((int64_t)m * a.explore_bp / 10000), m - n_f);
     const int n_r = m - n_f - n_e;
-    const float* Srow = S + ((int64_t)r * rows + row) * max_blocks;
     float sv[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) sv[e] = j0 + e < B ? Srow[j0 + e] : 0.0f;
-    // exploration keys: precomputed by predict inside a whole step, else here
-    uint32_t pk[EPT];
-    if (n_e > 0) {
-      const uint32_t* xrow = xkeys ? xkeys + (int64_t)r * max_blocks : nullptr;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e)
-        pk[e] = xrow ? (j0 + e < B ? xrow[j0 + e] : 0u)
-                     : explore_key(j0 + e, t, layer, req_id[r], seed_lo, seed_hi);
-    }
     uint32_t key[EPT];
     uint32_t elig = 0u;
 #pragma unroll
@@ -166,14 +152,22 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
         else { key[e] = float_key(sv[e]); elig |= 1u << e; }
       }
     }
-    const uint32_t ranked = block_select_top<EPT, kSelectThreads>(key, elig, n_r, hist, sh, tmpu);
+    const uint32_t ranked =
+        block_select_top<EPT, kSelectThreads>(key, elig, n_r, L.hist, L.sh, L.tmpu);
 #pragma unroll
     for (int e = 0; e < EPT; ++e)
       if (ranked >> e & 1u) c[e] = SPIN_CODE_RANKED;
     chosen |= ranked;
     elig &= ~ranked;
     if (n_e > 0) {
-      const uint32_t expl = block_select_top<EPT, kSelectThreads>(pk, elig, n_e, hist, sh, tmpu);
+      // exploration priorities in registers; the rows share them (the
+      // counter carries no row)
+      uint32_t pk[EPT];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+        pk[e] = explore_key(j0 + e, t, a.layer, rid, a.seed_lo, a.seed_hi);
+      const uint32_t expl =
+          block_select_top<EPT, kSelectThreads>(pk, elig, n_e, L.hist, L.sh, L.tmpu);
 #pragma unroll
       for (int e = 0; e < EPT; ++e)
         if (expl >> e & 1u) c[e] = SPIN_CODE_EXPLORED;
@@ -184,8 +178,39 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
   for (int e = 0; e < EPT; ++e)
     if (j0 + e < B) crow[j0 + e] = c[e];
   if (compact)
-    compact_blocks<EPT, kSelectThreads>(chosen, max_blocks, sel + (int64_t)r * max_blocks,
-                                        n_sel + r, sh);
+    compact_blocks<EPT, kSelectThreads>(chosen, a.max_blocks, a.sel + (int64_t)r * a.max_blocks,
+                                        a.n_sel + r, L.sh);
+}
+
+// Union of request r's row masks (Sec. 3.2.2), compacted to its block list.
+template <int EPT>
+__device__ __forceinline__ void union_row(int rows, int max_blocks, int r, int B,
+                                          const uint8_t* __restrict__ code,
+                                          int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
+                                          int* sh) {
+  const int j0 = threadIdx.x * EPT;
+  uint32_t any = 0u;
+  for (int row = 0; row < rows; ++row) {
+    const uint8_t* crow = code + ((int64_t)r * rows + row) * max_blocks;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if (j0 + e < B && crow[j0 + e] != SPIN_CODE_SKIP) any |= 1u << e;
+  }
+  compact_blocks<EPT>(any, max_blocks, sel + (int64_t)r * max_blocks, n_sel + r, sh);
+}
+
+template <int EPT>
+__global__ __launch_bounds__(kSelectThreads) void k_select(
+    SelectArgs a, const int32_t* __restrict__ ctx, const int32_t* __restrict__ qpos,
+    const int32_t* __restrict__ step, const int32_t* __restrict__ req_id,
+    const float* __restrict__ S, const int32_t* __restrict__ budget, int compact) {
+  __shared__ SelectLds L;
+  const int row = blockIdx.x, r = blockIdx.y;
+  const int N = ctx[r];
+  const bool bad = request_error(N, qpos[r], a.rows, a.max_blocks, 0, 0) != 0;
+  const int B = bad ? 0 : (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  select_row<EPT>(a, r, row, B, step[r], req_id[r], budget ? budget[r] : 0,
+                  S + ((int64_t)r * a.rows + row) * a.max_blocks, compact != 0, L);
 }
 
 // Union of the verifier rows' masks (Sec. 3.2.2), one workgroup per request.
@@ -201,15 +226,7 @@ __global__ __launch_bounds__(kSelThreads) void k_union(int rows, int max_blocks,
   const int N = ctx[r];
   const bool bad = request_error(N, qpos[r], rows, max_blocks, 0, 0) != 0;
   const int B = bad ? 0 : (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
-  const int j0 = threadIdx.x * EPT;
-  uint32_t any = 0u;
-  for (int row = 0; row < rows; ++row) {
-    const uint8_t* crow = code + ((int64_t)r * rows + row) * max_blocks;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e)
-      if (j0 + e < B && crow[j0 + e] != SPIN_CODE_SKIP) any |= 1u << e;
-  }
-  compact_blocks<EPT>(any, max_blocks, sel + (int64_t)r * max_blocks, n_sel + r, sh);
+  union_row<EPT>(rows, max_blocks, r, B, code, sel, n_sel, sh);
 }
 
 __global__ void k_advance(int R, int rows, const int32_t* __restrict__ n_valid,
@@ -235,27 +252,36 @@ __global__ void k_zero_i32(int32_t* __restrict__ p, int n) {
 // ---------------------------------------------------------------------------
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
                           const float* D, int64_t d_ld, const float* vmax, float* S,
-                          hipStream_t st, int32_t* qpos_snap, uint32_t* xkeys) {
+                          hipStream_t st, int32_t* qpos_snap) {
   dim3 grid((b.max_blocks + 4 * kPredBlocksPerWave - 1) / (4 * kPredBlocksPerWave), b.n_rows,
             b.batch);
-  const ExploreKeys xk{xkeys, b.step, b.req_id, c.layer, (uint32_t)(c.seed & 0xFFFFFFFFu),
-                       (uint32_t)(c.seed >> 32)};
   hipLaunchKernelGGL(k_predict, grid, dim3(256), 0, st, c.combine, b.n_rows, b.max_blocks,
                      b.ctx_len, b.q_pos, V, v_ld, D, d_ld,
-                     c.combine == SPIN_COMBINE_MAX ? vmax : nullptr, S, b.err, qpos_snap, xk);
+                     c.combine == SPIN_COMBINE_MAX ? vmax : nullptr, S, b.err, qpos_snap);
   return hipGetLastError();
+}
+
+static SelectArgs select_args(const spin_config& c, const spin_batch& b, uint8_t* code,
+                              int32_t* sel, int32_t* n_sel) {
+  return SelectArgs{c.topk, c.sparsity_bp, c.explore_bp, c.layer,
+                    (uint32_t)(c.seed & 0xFFFFFFFFu), (uint32_t)(c.seed >> 32), b.n_rows,
+                    b.max_blocks, code, sel, n_sel};
+}
+
+// blocks per thread of the 1,024-thread selection (max_blocks <= 8,192)
+static int select_ept(int max_blocks) {
+  const int ept = (max_blocks + kSelectThreads - 1) / kSelectThreads;
+  return ept <= 1 ? 1 : ept <= 2 ? 2 : ept <= 4 ? 4 : 8;
 }
 
 template <int EPT>
 static void select_t(const spin_config& c, const spin_batch& b, const float* S,
                      const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                     hipStream_t st, const uint32_t* xkeys) {
+                     hipStream_t st) {
   const int compact = b.n_rows == 1;
   hipLaunchKernelGGL(k_select<EPT>, dim3(b.n_rows, b.batch), dim3(kSelectThreads), 0, st,
-                     c.topk, c.sparsity_bp, c.explore_bp, c.layer,
-                     (uint32_t)(c.seed & 0xFFFFFFFFu), (uint32_t)(c.seed >> 32), b.n_rows,
-                     b.max_blocks, b.ctx_len, b.q_pos, b.step, b.req_id, S, budget, code, sel,
-                     n_sel, compact, xkeys);
+                     select_args(c, b, code, sel, n_sel), b.ctx_len, b.q_pos, b.step, b.req_id,
+                     S, budget, compact);
 }
 
 template <int EPT>
@@ -267,14 +293,13 @@ static void union_t(const spin_batch& b, uint8_t* code, int32_t* sel, int32_t* n
 
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                         hipStream_t st, const uint32_t* xkeys) {
-  const int ept = (b.max_blocks + kSelectThreads - 1) / kSelectThreads;
-  if (ept <= 1) select_t<1>(c, b, S, budget, code, sel, n_sel, st, xkeys);
-  else if (ept <= 2) select_t<2>(c, b, S, budget, code, sel, n_sel, st, xkeys);
-  else if (ept <= 4) select_t<4>(c, b, S, budget, code, sel, n_sel, st, xkeys);
-  else if (ept <= 8) select_t<8>(c, b, S, budget, code, sel, n_sel, st, xkeys);
-  else if (ept <= 16) select_t<16>(c, b, S, budget, code, sel, n_sel, st, xkeys);
-  else select_t<32>(c, b, S, budget, code, sel, n_sel, st, xkeys);
+                         hipStream_t st) {
+  switch (select_ept(b.max_blocks)) {
+    case 1: select_t<1>(c, b, S, budget, code, sel, n_sel, st); break;
+    case 2: select_t<2>(c, b, S, budget, code, sel, n_sel, st); break;
+    case 4: select_t<4>(c, b, S, budget, code, sel, n_sel, st); break;
+    default: select_t<8>(c, b, S, budget, code, sel, n_sel, st); break;
+  }
   if (b.n_rows > 1) {  // union of the rows' masks
     const int eu = (b.max_blocks + kSelThreads - 1) / kSelThreads;
     if (eu <= 1) union_t<1>(b, code, sel, n_sel, st);

@@ -494,7 +494,7 @@ size_t topk_workspace_bytes(const spin_config&, int R, int rows, int max_blocks)
 
 size_t step_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks) {
   return (size_t)align256((int64_t)topk_workspace_bytes(c, R, rows, max_blocks)) +
-         (size_t)align256(4LL * R) + (size_t)align256(4LL * R * max_blocks);
+         (size_t)align256(4LL * R);
 }
 
 hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const float* z,

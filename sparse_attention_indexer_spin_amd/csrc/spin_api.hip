@@ -288,18 +288,14 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
     return fail(SPIN_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
   if (bt->batch == 0) return SPIN_OK;
   hipStream_t st = (hipStream_t)stream;
-  // after the top-K region (256-B aligned): the q_pos snapshot, then the
-  // exploration keys
+  // after the top-K region (256-B aligned): the step's q_pos snapshot
   const size_t topk_bytes = spin::topk_workspace_bytes(*cfg, bt->batch, bt->n_rows, bt->max_blocks);
-  const size_t qsnap_off = (topk_bytes + 255) & ~size_t(255);
-  int32_t* qsnap = reinterpret_cast<int32_t*>(static_cast<char*>(io->workspace) + qsnap_off);
-  uint32_t* xkeys = reinterpret_cast<uint32_t*>(static_cast<char*>(io->workspace) + qsnap_off +
-                                                ((4 * (size_t)bt->batch + 255) & ~size_t(255)));
+  int32_t* qsnap = reinterpret_cast<int32_t*>(static_cast<char*>(io->workspace) +
+                                              ((topk_bytes + 255) & ~size_t(255)));
   SPIN_CHECK(hip_status(spin::launch_predict(*cfg, *bt, io->V, io->v_ld, io->D, io->d_ld,
-                                             io->v_max, io->S, st, qsnap, xkeys),
-                        "spin_step/predict"));
+                                             io->v_max, io->S, st, qsnap), "spin_step/predict"));
   SPIN_CHECK(hip_status(spin::launch_select(*cfg, *bt, io->S, io->budget, io->row_code, io->sel,
-                                            io->n_sel, st, xkeys), "spin_step/select"));
+                                            io->n_sel, st), "spin_step/select"));
   // where the score kernel can, it also applies the top-K threshold filter
   const bool prefilter = spin::score_filters(*cfg, *bt);
   const spin::CandSink sink = spin::topk_sink(io->workspace, bt->batch, bt->n_rows, bt->max_blocks);

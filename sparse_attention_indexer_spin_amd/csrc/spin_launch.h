@@ -20,18 +20,15 @@ struct CandSink {
   int pcnt_ld;
 };
 
+// vmax (optional, [R][max_blocks]): the V block maxima (max combine only).
 // qpos_snap (optional, [R]): predict records the step's q_pos there; the
 // fused EMA + advance of a whole step reads it instead of q_pos.
-// xkeys (optional, [R][max_blocks]): predict also writes the step's
-// exploration keys there, and select reads them instead of computing them.
-// vmax (optional, [R][max_blocks]): the V block maxima (max combine only).
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
                           const float* D, int64_t d_ld, const float* vmax, float* S,
-                          hipStream_t st, int32_t* qpos_snap = nullptr,
-                          uint32_t* xkeys = nullptr);
+                          hipStream_t st, int32_t* qpos_snap = nullptr);
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                         hipStream_t st, const uint32_t* xkeys = nullptr);
+                         hipStream_t st);
 // With a non-null `sink`, kernels that can (score_filters()) also write the
 // top-K candidates; the caller then runs launch_topk with `prefiltered`.
 hipError_t launch_score(const spin_config& c, const spin_batch& b, const void* q, const float* w,
