@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-max-requests", type=int, default=32)
+    ap.add_argument("--stack", action="store_true",
+                    help="multi-layer workloads: time whole decode steps of every layer, one "
+                         "spin_step per layer on one stream and the spin_stack schedule (plans "
+                         "on a side stream)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 1 GiB device-to-device copies (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -195,6 +199,108 @@ def run_gpu(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_reps: 
     return out
 
 
+class StackInputs:
+    """Per-layer synthetic inputs of a multi-layer workload, resident on the GPU."""
+
+    def __init__(self, w: G.Workload, n_steps: int, dev="cuda"):
+        self.w = w
+        self.ctx = G.context_lengths(w)
+        self.pos, self.accept = G.make_schedule(w, self.ctx, n_steps)
+        self.keys, self.weights, self.q = [], [], []
+        for l in range(w.layers):
+            k = G.make_keys(w, l, dev, self.ctx)
+            self.keys.append(k)
+            self.weights.append(G.make_weights(w, l, dev))
+            q = G.make_queries(w, l, k, self.pos, dev)
+            self.q.append(G.cast_queries(w, q).contiguous())
+            del q
+        torch.cuda.synchronize()
+
+
+def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict=None):
+    """Whole decode steps of every layer: (a) one spin_step per layer in layer
+    order on the current stream, (b) one spin_stack_step (plans on a side
+    stream).  Each mode on its own layer states from the same reset; each timed
+    step after `evict` when given.  Both modes must agree bit for bit."""
+    from sparse_attention_indexer_spin_amd import SpinLayer, SpinStack
+    w = inp.w
+
+    def layers():
+        out = []
+        for l in range(w.layers):
+            lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks,
+                            d_cap=G.d_capacity(w, steps + warmup), topk=w.topk,
+                            sparsity_bp=sparsity_bp, n_rows=w.rows, explore_bp=w.explore_bp,
+                            ema_alpha=w.alpha, combine=w.combine, key_dtype=torch.uint8,
+                            q_dtype=torch.bfloat16, layer=l)
+            lay.set_requests(inp.ctx.cuda(), inp.pos[0].cuda())
+            lay.reset()
+            out.append(lay)
+        return out
+
+    pages = [k.pages for k in inp.keys]
+    scales = [k.scale for k in inp.keys]
+    pts = [k.page_table for k in inp.keys]
+    stream = torch.cuda.current_stream()
+
+    def timed(step_fn):
+        for s in range(warmup):
+            step_fn(s)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for k, s in enumerate(range(warmup, warmup + steps)):
+            if evict is not None:
+                evict()
+            ev[k][0].record(stream)
+            step_fn(s)
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+    seq = layers()
+
+    def seq_step(s):
+        for l, lay in enumerate(seq):
+            lay.step(inp.q[l][s], inp.weights[l], pages[l], scales[l], pts[l])
+
+    ms_seq = timed(seq_step)
+    stk_layers = layers()
+    stack = SpinStack(stk_layers)
+
+    def stack_step(s):
+        if evict is not None:
+            # the plans may not start before the timed region (they would run
+            # beside the eviction read): order the side stream after main
+            stack.inputs_changed()
+        stack.step([inp.q[l][s] for l in range(w.layers)], inp.weights, pages, scales, pts)
+
+    ms_stack = timed(stack_step)
+    stack.side.synchronize()
+    for a, b in zip(seq, stk_layers):
+        assert torch.equal(a.topk_idx, b.topk_idx) and torch.equal(a.V, b.V), \
+            "stack and sequential steps disagree"
+        assert int(a.err.item()) == 0 and int(b.err.item()) == 0
+    keys = 0
+    ctx = inp.ctx.numpy().astype(np.int64)
+    n_sel = 0
+    for lay in stk_layers:
+        ns = lay.n_sel.cpu().numpy().astype(np.int64)
+        keys += int(np.minimum(ns * 64, ctx).sum()) * w.rows
+        n_sel += int(ns.sum())
+    # the score launch of layer 0 alone on its last selection, for the roofline
+    lay = stk_layers[0]
+    bt = lay.batch(pages[0].shape[0])
+    from sparse_attention_indexer_spin_amd import api
+    score_us = _timed_us(lambda: api.spin_sparse_index_score(
+        lay.cfg, bt, inp.q[0][warmup + steps - 1], inp.weights[0], pages[0], scales[0], pts[0],
+        lay.sel, lay.n_sel, lay.z), 20, stream, evict)
+    ns0 = lay.n_sel.cpu().numpy().astype(np.int64)
+    keys0 = int(np.minimum(ns0 * 64, ctx).sum()) * w.rows
+    return dict(ms_seq=ms_seq, ms_stack=ms_stack, keys_per_step=keys, n_sel=n_sel,
+                score_us_layer0=score_us, keys_layer0=keys0, n_sel_layer0=int(ns0.sum()))
+
+
 def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, budget_s: float,
                  max_requests: int):
     """Time the CPU oracle on whole requests of the workload until about `budget_s`
@@ -294,6 +400,9 @@ def main():
     w = G.WORKLOADS[args.workload]
     sp = w.sparsity_bp[0] if args.sparsity_bp is None else args.sparsity_bp
     total_steps = args.steps + args.warmup
+    if args.stack:
+        main_stack(args, w, sp)
+        return
     inp = Inputs(w, total_steps)
     evict = Evictor() if args.cache == "cold" else None
     # back-to-back steps first, for reference; then the timed protocol
@@ -348,6 +457,45 @@ def main():
             "c_over_dense_indexer": float(c / t_dense_indexer)}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp, sp, args.cpu_seconds, args.cpu_max_requests)
+    print(json.dumps(out))
+
+
+def main_stack(args, w: G.Workload, sp: int):
+    """The multi-layer bench line: whole decode steps of every layer."""
+    if w.layers < 2 or w.key_dtype != "fp8" or w.rows != 1:
+        print(json.dumps({"error": "--stack needs a multi-layer fp8 workload with one row"}))
+        sys.exit(2)
+    inp = StackInputs(w, args.steps + args.warmup)
+    evict = Evictor() if args.cache == "cold" else None
+    res = run_stack(inp, sp, args.steps, args.warmup, evict)
+    score_bytes = algorithmic_score_bytes(w, res["keys_layer0"], res["n_sel_layer0"])
+    achieved = score_bytes / (res["score_us_layer0"] * 1e-6) / 1e9
+    out = {
+        "metric": "indexer keys scored/s + us/decode-step/layer at 512K ctx; % HBM peak",
+        "value": res["keys_per_step"] / (res["ms_stack"] * 1e-3), "unit": "keys/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_stack"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.key_dtype,
+        "data": "synthetic (seeded generator: Gaussian keys + heavy slots + RoPE, AR(1) queries;"
+                " per-layer heavy fraction and direction norm)",
+        "config": {"workload": w.name, "requests": w.batch, "slots_per_request":
+                   [int(inp.ctx.min()), int(inp.ctx.max())], "layers": w.layers,
+                   "verifier_rows": w.rows, "topk": w.topk, "sparsity_bp": sp,
+                   "explore_bp": w.explore_bp, "key_dtype": w.key_dtype, "q_dtype": w.q_dtype},
+        "us_per_step_layer": res["ms_stack"] * 1e3 / w.layers,
+        "cache": {"mode": args.cache,
+                  "how": "1 GiB read before each timed whole step" if evict is not None
+                  else "steps back to back (the layers' own pages evict each other)"},
+        "stack": {"sequential_us_per_step": res["ms_seq"] * 1e3,
+                  "overlapped_us_per_step": res["ms_stack"] * 1e3,
+                  "sequential_us_per_step_layer": res["ms_seq"] * 1e3 / w.layers,
+                  "overlapped_us_per_step_layer": res["ms_stack"] * 1e3 / w.layers},
+        "keys_scored_per_step": res["keys_per_step"],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "spin::k_score_wave (layer 0)",
+                     "algorithmic_bytes_per_launch": score_bytes,
+                     "launch_us": res["score_us_layer0"]},
+    }
     print(json.dumps(out))
 
 

@@ -68,6 +68,7 @@ enum { SPIN_DERR_CTX = 1,   /* ctx_len < 1, > 64*max_blocks or > v_ld        */
 #define SPIN_MAX_ROWS 4
 #define SPIN_MAX_BLOCKS 8192  /* per request: up to 524,288 slots */
 #define SPIN_MAX_TOPK 8192
+#define SPIN_MAX_LAYERS 256  /* layers of one spin_stack */
 
 /* Method parameters, passed by host pointer and copied by value. */
 typedef struct spin_config {
@@ -226,6 +227,59 @@ typedef struct spin_step_io {
  */
 spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_step_io* io,
                       int32_t defer_ema, void* stream);
+
+/*
+ * The two halves of spin_step, for callers that overlap them.  Block
+ * prediction needs only the EMA state, not the current query, so it can be
+ * scheduled off the critical path (paper Sec. 3.2, after Eq. 2; blog, "Score
+ * only where history points").
+ * spin_step_plan: predict and select (+ union) into io->S, row_code, sel,
+ *   n_sel, and the step's q_pos snapshot in the workspace.  Reads V, D,
+ *   v_max, budget and the bt counters; never q, w or the key pages.
+ * spin_step_finish: score, top-K and (defer_ema == 0) the EMA update +
+ *   counter advance, exactly as the rest of spin_step.  It must run after
+ *   the same step's spin_step_plan (same io), ordered by stream or event.
+ * spin_step_plan then spin_step_finish on one stream is spin_step.
+ */
+spin_status spin_step_plan(const spin_config* cfg, const spin_batch* bt, const spin_step_io* io,
+                           void* stream);
+spin_status spin_step_finish(const spin_config* cfg, const spin_batch* bt,
+                             const spin_step_io* io, int32_t defer_ema, void* stream);
+
+/*
+ * Multi-layer decode step with the plan of every layer on a side stream,
+ * overlapped with the scoring of other layers (paper Sec. 3.2, after Eq. 2:
+ * prediction and EMA upkeep may run asynchronously beside the other layers'
+ * forward pass).  A spin_stack holds a few host events; it is created once
+ * per model and reused every decode step.
+ * spin_stack_step(stack, n, cfgs, bts, ios, order_after_main, main, side)
+ * runs one decode step of layers 0 .. n-1 (each with its own EMA state,
+ * counters, buffers and workspace).  The layers form two groups, A = [0, h)
+ * and B = [h, n) with h = ceil(n / 2):
+ *   side: after the previous call's finishes of group A, the plans of A;
+ *         after all of the previous call's finishes, the plans of B
+ *   main: after the plans of A, the finishes of A (score, top-K, EMA);
+ *         after the plans of B, the finishes of B
+ * so group A's plans run beside the previous step's group-B scoring and
+ * group B's beside this step's group-A scoring, with two cross-stream waits
+ * on main per step.  Every layer sees the same results as n spin_step calls
+ * in layer order.  The plans also read the caller's ctx_len, req_id and
+ * budget: when the caller has written any of them on `main` since the
+ * previous call (or reset a layer there), it passes order_after_main != 0,
+ * and the side stream first waits for all work issued on `main` before this
+ * call.  main and side must be different streams of the stack's device; the
+ * call returns without waiting.  The caller's later work on `main` is ordered
+ * after everything this call issued.  Deferred EMA is not available here.
+ * Errors: SPIN_E_SHAPE when n is < 1 or exceeds the stack's layers, or
+ * main == side; each layer's arguments are validated as for spin_step before
+ * anything is issued.
+ */
+typedef struct spin_stack spin_stack;
+spin_status spin_stack_create(int32_t n_layers, spin_stack** out);
+void spin_stack_destroy(spin_stack* stack);
+spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
+                            const spin_batch* bts, const spin_step_io* ios,
+                            int32_t order_after_main, void* main_stream, void* side_stream);
 
 /*
  * Device workspace bytes spin_topk / spin_step need for this shape.  The

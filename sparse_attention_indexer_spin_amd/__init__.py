@@ -5,6 +5,7 @@ include/spin.h); this package only marshals torch tensors into that ABI.
 """
 from . import _lib  # noqa: F401
 from .api import (batch, config, spin_advance, spin_ema_update, spin_predict_blocks,  # noqa: F401
-                  spin_reset_state, spin_select_blocks, spin_sparse_index_score, spin_step,
-                  spin_topk, step_io, workspace_bytes)
-from .layer import SpinLayer  # noqa: F401
+                  spin_reset_state, spin_select_blocks, spin_sparse_index_score, spin_stack_step,
+                  spin_step, spin_step_finish, spin_step_plan, spin_topk, step_io,
+                  workspace_bytes, Stack)
+from .layer import SpinLayer, SpinStack  # noqa: F401

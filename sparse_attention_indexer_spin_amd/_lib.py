@@ -18,11 +18,12 @@ SPIN_F32, SPIN_BF16, SPIN_FP8_E4M3 = 0, 1, 2
 SPIN_COMBINE_MAX, SPIN_COMBINE_SUM = 0, 1
 SPIN_CODE_SKIP, SPIN_CODE_FORCED, SPIN_CODE_RANKED, SPIN_CODE_EXPLORED, SPIN_CODE_DENSE = range(5)
 SPIN_DERR_CTX, SPIN_DERR_QPOS, SPIN_DERR_PAGE = 1, 2, 4
-SPIN_MAX_ROWS, SPIN_MAX_BLOCKS, SPIN_MAX_TOPK = 4, 8192, 8192
+SPIN_MAX_ROWS, SPIN_MAX_BLOCKS, SPIN_MAX_TOPK, SPIN_MAX_LAYERS = 4, 8192, 8192, 256
 
 EXPORTS = ["spin_predict_blocks", "spin_select_blocks", "spin_sparse_index_score", "spin_topk",
            "spin_ema_update", "spin_advance", "spin_reset_state", "spin_step",
-           "spin_workspace_bytes", "spin_last_error"]
+           "spin_workspace_bytes", "spin_last_error", "spin_step_plan", "spin_step_finish",
+           "spin_stack_create", "spin_stack_destroy", "spin_stack_step"]
 
 
 class SpinConfig(C.Structure):
@@ -73,11 +74,17 @@ def load() -> C.CDLL:
         "spin_advance": [I32, I32, P, P, P, P],
         "spin_reset_state": [I32, P, I64, P, I64, P, I64, P, P],
         "spin_step": [cfg, bt, C.POINTER(SpinStepIO), I32, P],
+        "spin_step_plan": [cfg, bt, C.POINTER(SpinStepIO), P],
+        "spin_step_finish": [cfg, bt, C.POINTER(SpinStepIO), I32, P],
+        "spin_stack_create": [I32, C.POINTER(P)],
+        "spin_stack_step": [P, I32, cfg, bt, C.POINTER(SpinStepIO), I32, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = C.c_int
+    lib.spin_stack_destroy.argtypes = [P]
+    lib.spin_stack_destroy.restype = None
     lib.spin_workspace_bytes.argtypes = [cfg, I32, I32, I32]
     lib.spin_workspace_bytes.restype = SZ
     lib.spin_last_error.argtypes = []

@@ -119,3 +119,45 @@ def step_io(*, V, D, q, w, k_pages, k_scale, page_table, S, row_code, sel, n_sel
 def spin_step(cfg, bt, io, defer_ema: bool = False, stream=None):
     L.check(L.load().spin_step(C.byref(cfg), C.byref(bt), C.byref(io), int(bool(defer_ema)),
                                _stream(stream)))
+
+
+def spin_step_plan(cfg, bt, io, stream=None):
+    L.check(L.load().spin_step_plan(C.byref(cfg), C.byref(bt), C.byref(io), _stream(stream)))
+
+
+def spin_step_finish(cfg, bt, io, defer_ema: bool = False, stream=None):
+    L.check(L.load().spin_step_finish(C.byref(cfg), C.byref(bt), C.byref(io),
+                                      int(bool(defer_ema)), _stream(stream)))
+
+
+class Stack:
+    """Handle of a spin_stack (host events of the multi-layer schedule)."""
+
+    def __init__(self, n_layers: int):
+        h = C.c_void_p()
+        L.check(L.load().spin_stack_create(n_layers, C.byref(h)))
+        self.handle, self.n_layers = h, n_layers
+
+    def close(self):
+        if self.handle:
+            L.load().spin_stack_destroy(self.handle)
+            self.handle = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def spin_stack_step(stack: Stack, cfgs, bts, ios, order_after_main: bool = False,
+                    main_stream=None, side_stream=None):
+    """One decode step of len(cfgs) layers: plans on side_stream, finishes on
+    main_stream (default: the current stream)."""
+    n = len(cfgs)
+    assert len(bts) == n and len(ios) == n and side_stream is not None
+    ca = (L.SpinConfig * n)(*cfgs)
+    ba = (L.SpinBatch * n)(*bts)
+    ia = (L.SpinStepIO * n)(*ios)
+    L.check(L.load().spin_stack_step(stack.handle, n, ca, ba, ia, int(bool(order_after_main)),
+                                     _stream(main_stream), side_stream.cuda_stream))

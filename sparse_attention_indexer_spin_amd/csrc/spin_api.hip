@@ -4,8 +4,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "spin_launch.h"
 
@@ -271,9 +273,12 @@ spin_status spin_reset_state(int32_t batch, float* V, int64_t v_ld, float* D, in
                                        (hipStream_t)stream), fn);
 }
 
-spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_step_io* io,
-                      int32_t defer_ema, void* stream) {
-  const char* fn = "spin_step";
+}  // extern "C"
+
+namespace {
+
+spin_status check_step(const char* fn, const spin_config* cfg, const spin_batch* bt,
+                       const spin_step_io* io) {
   SPIN_CHECK(check_config(fn, cfg));
   SPIN_CHECK(check_batch(fn, bt));
   SPIN_REQUIRE(io);
@@ -286,42 +291,180 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
   const size_t need = spin::step_workspace_bytes(*cfg, bt->batch, bt->n_rows, bt->max_blocks);
   if (!io->workspace || io->workspace_bytes < need)
     return fail(SPIN_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
-  if (bt->batch == 0) return SPIN_OK;
-  hipStream_t st = (hipStream_t)stream;
-  // after the top-K region (256-B aligned): the step's q_pos snapshot
-  const size_t topk_bytes = spin::topk_workspace_bytes(*cfg, bt->batch, bt->n_rows, bt->max_blocks);
-  int32_t* qsnap = reinterpret_cast<int32_t*>(static_cast<char*>(io->workspace) +
-                                              ((topk_bytes + 255) & ~size_t(255)));
-  SPIN_CHECK(hip_status(spin::launch_predict(*cfg, *bt, io->V, io->v_ld, io->D, io->d_ld,
-                                             io->v_max, io->S, st, qsnap), "spin_step/predict"));
-  SPIN_CHECK(hip_status(spin::launch_select(*cfg, *bt, io->S, io->budget, io->row_code, io->sel,
-                                            io->n_sel, st), "spin_step/select"));
+  return SPIN_OK;
+}
+
+// The step's q_pos snapshot: after the top-K region of the workspace (256-B aligned).
+int32_t* step_qsnap(const spin_config& c, const spin_batch& b, const spin_step_io& io) {
+  const size_t topk_bytes = spin::topk_workspace_bytes(c, b.batch, b.n_rows, b.max_blocks);
+  return reinterpret_cast<int32_t*>(static_cast<char*>(io.workspace) +
+                                    ((topk_bytes + 255) & ~size_t(255)));
+}
+
+// Predict + select (+ union), arguments already checked.
+spin_status issue_plan(const spin_config& c, const spin_batch& b, const spin_step_io& io,
+                       hipStream_t st) {
+  SPIN_CHECK(hip_status(spin::launch_predict(c, b, io.V, io.v_ld, io.D, io.d_ld, io.v_max, io.S,
+                                             st, step_qsnap(c, b, io)),
+                        "spin_step/predict"));
+  return hip_status(spin::launch_select(c, b, io.S, io.budget, io.row_code, io.sel, io.n_sel, st),
+                    "spin_step/select");
+}
+
+// Score, top-K and (unless deferred) the EMA update + counter advance.
+spin_status issue_finish(const spin_config& c, const spin_batch& b, const spin_step_io& io,
+                         int32_t defer_ema, hipStream_t st) {
+  int32_t* qsnap = step_qsnap(c, b, io);
   // where the score kernel can, it also applies the top-K threshold filter
-  const bool prefilter = spin::score_filters(*cfg, *bt);
-  const spin::CandSink sink = spin::topk_sink(io->workspace, bt->batch, bt->n_rows, bt->max_blocks);
-  SPIN_CHECK(hip_status(spin::launch_score(*cfg, *bt, io->q, io->w, io->k_pages, io->k_scale,
-                                           io->page_table, io->pt_ld, io->sel, io->n_sel, io->z,
-                                           io->z_ld, st, prefilter ? &sink : nullptr),
+  const bool prefilter = spin::score_filters(c, b);
+  const spin::CandSink sink = spin::topk_sink(io.workspace, b.batch, b.n_rows, b.max_blocks);
+  SPIN_CHECK(hip_status(spin::launch_score(c, b, io.q, io.w, io.k_pages, io.k_scale,
+                                           io.page_table, io.pt_ld, io.sel, io.n_sel, io.z,
+                                           io.z_ld, st, prefilter ? &sink : nullptr),
                         "spin_step/score"));
-  if (prefilter && !defer_ema) {  // top-K beside the EMA update, one launch
-    SPIN_CHECK(hip_status(spin::launch_topk_ema(*cfg, *bt, io->z, io->z_ld, io->sel, io->n_sel,
-                                                io->topk_idx, io->workspace, io->n_valid, io->V,
-                                                io->v_ld, io->D, io->d_ld, io->v_max, qsnap,
-                                                io->q_pos_mut, io->step_mut, st),
-                          "spin_step/topk+ema"));
-    return SPIN_OK;
-  }
-  SPIN_CHECK(hip_status(spin::launch_topk(*cfg, *bt, io->z, io->z_ld, io->sel, io->n_sel,
-                                          io->topk_idx, io->workspace, io->workspace_bytes, st,
-                                          prefilter), "spin_step/topk"));
+  if (prefilter && !defer_ema)  // top-K beside the EMA update, one launch
+    return hip_status(spin::launch_topk_ema(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.topk_idx,
+                                            io.workspace, io.n_valid, io.V, io.v_ld, io.D,
+                                            io.d_ld, io.v_max, qsnap, io.q_pos_mut, io.step_mut,
+                                            st),
+                      "spin_step/topk+ema");
+  SPIN_CHECK(hip_status(spin::launch_topk(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.topk_idx,
+                                          io.workspace, io.workspace_bytes, st, prefilter),
+                        "spin_step/topk"));
   if (defer_ema) return SPIN_OK;
   // EMA and counter advance in one kernel: it reads q positions from the
-  // snapshot, so advancing q_pos_mut (normally the same array as bt->q_pos)
+  // snapshot, so advancing q_pos_mut (normally the same array as b.q_pos)
   // cannot race with its reads
-  SPIN_CHECK(hip_status(spin::launch_ema(*cfg, *bt, io->z, io->z_ld, io->sel, io->n_sel,
-                                         io->n_valid, io->V, io->v_ld, io->D, io->d_ld, io->v_max,
-                                         st, qsnap, io->q_pos_mut, io->step_mut),
-                        "spin_step/ema+advance"));
+  return hip_status(spin::launch_ema(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.n_valid, io.V,
+                                     io.v_ld, io.D, io.d_ld, io.v_max, st, qsnap, io.q_pos_mut,
+                                     io.step_mut),
+                    "spin_step/ema+advance");
+}
+
+}  // namespace
+
+// Host-side scheduler state of a multi-layer step.  The layers split into
+// two groups, A = [0, h) and B = [h, n), h = ceil(n / 2); per group, the
+// event of its last plans (side stream) and of its last finishes (main).
+// Each cross-stream wait costs the waiting queue several microseconds even
+// when the event has long completed, so main waits twice per step, not once
+// per layer.
+struct spin_stack {
+  int32_t n_layers = 0;
+  int device = 0;
+  int32_t prev_h = 0;            // group split of the previous call
+  hipEvent_t plan_done[2] = {nullptr, nullptr};
+  hipEvent_t finish_done[2] = {nullptr, nullptr};
+  hipEvent_t entry = nullptr;    // main at the call, for order_after_main
+};
+
+extern "C" {
+
+spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_step_io* io,
+                      int32_t defer_ema, void* stream) {
+  SPIN_CHECK(check_step("spin_step", cfg, bt, io));
+  if (bt->batch == 0) return SPIN_OK;
+  SPIN_CHECK(issue_plan(*cfg, *bt, *io, (hipStream_t)stream));
+  return issue_finish(*cfg, *bt, *io, defer_ema, (hipStream_t)stream);
+}
+
+spin_status spin_step_plan(const spin_config* cfg, const spin_batch* bt, const spin_step_io* io,
+                           void* stream) {
+  SPIN_CHECK(check_step("spin_step_plan", cfg, bt, io));
+  if (bt->batch == 0) return SPIN_OK;
+  return issue_plan(*cfg, *bt, *io, (hipStream_t)stream);
+}
+
+spin_status spin_step_finish(const spin_config* cfg, const spin_batch* bt,
+                             const spin_step_io* io, int32_t defer_ema, void* stream) {
+  SPIN_CHECK(check_step("spin_step_finish", cfg, bt, io));
+  if (bt->batch == 0) return SPIN_OK;
+  return issue_finish(*cfg, *bt, *io, defer_ema, (hipStream_t)stream);
+}
+
+spin_status spin_stack_create(int32_t n_layers, spin_stack** out) {
+  const char* fn = "spin_stack_create";
+  if (!out) return fail(SPIN_E_NULL, "%s: out is NULL", fn);
+  *out = nullptr;
+  if (n_layers < 1 || n_layers > SPIN_MAX_LAYERS)
+    return fail(SPIN_E_SHAPE, "%s: n_layers %d outside [1, %d]", fn, n_layers, SPIN_MAX_LAYERS);
+  std::unique_ptr<spin_stack> st(new spin_stack);
+  st->n_layers = n_layers;
+  SPIN_CHECK(hip_status(hipGetDevice(&st->device), fn));
+  hipEvent_t* evs[5] = {&st->plan_done[0], &st->plan_done[1], &st->finish_done[0],
+                        &st->finish_done[1], &st->entry};
+  for (hipEvent_t* e : evs) {
+    const hipError_t r = hipEventCreateWithFlags(e, hipEventDisableTiming);
+    if (r != hipSuccess) {
+      spin_stack_destroy(st.release());
+      return hip_status(r, fn);
+    }
+  }
+  *out = st.release();
+  return SPIN_OK;
+}
+
+void spin_stack_destroy(spin_stack* stack) {
+  if (!stack) return;
+  for (hipEvent_t e : {stack->plan_done[0], stack->plan_done[1], stack->finish_done[0],
+                       stack->finish_done[1], stack->entry})
+    if (e) (void)hipEventDestroy(e);
+  delete stack;
+}
+
+spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
+                            const spin_batch* bts, const spin_step_io* ios,
+                            int32_t order_after_main, void* main_stream, void* side_stream) {
+  const char* fn = "spin_stack_step";
+  if (!stack || !cfgs || !bts || !ios) return fail(SPIN_E_NULL, "%s: NULL argument", fn);
+  if (n_layers < 1 || n_layers > stack->n_layers)
+    return fail(SPIN_E_SHAPE, "%s: n_layers %d outside [1, %d]", fn, n_layers, stack->n_layers);
+  if (main_stream == side_stream)
+    return fail(SPIN_E_SHAPE, "%s: main and side must be different streams", fn);
+  int dev = -1;
+  SPIN_CHECK(hip_status(hipGetDevice(&dev), fn));
+  if (dev != stack->device)
+    return fail(SPIN_E_SHAPE, "%s: stack created on device %d, current device %d", fn,
+                stack->device, dev);
+  for (int l = 0; l < n_layers; ++l) {
+    char lfn[64];
+    std::snprintf(lfn, sizeof(lfn), "%s[layer %d]", fn, l);
+    SPIN_CHECK(check_step(lfn, &cfgs[l], &bts[l], &ios[l]));
+  }
+  hipStream_t mst = (hipStream_t)main_stream, sst = (hipStream_t)side_stream;
+  auto wait = [&](hipStream_t st, hipEvent_t e) {
+    return hip_status(hipStreamWaitEvent(st, e, 0), fn);
+  };
+  auto record = [&](hipEvent_t e, hipStream_t st) { return hip_status(hipEventRecord(e, st), fn); };
+  if (order_after_main) {  // plan inputs the caller wrote on main
+    SPIN_CHECK(record(stack->entry, mst));
+    SPIN_CHECK(wait(sst, stack->entry));
+  }
+  const int h = (n_layers + 1) / 2;
+  const int lo[2] = {0, h}, hi[2] = {h, n_layers};
+  // side: every plan(l) after the previous call's finish(l).  Group A's
+  // finishes were recorded as a group when the split was the same or wider;
+  // otherwise the previous call's last record covers every layer.
+  for (int g = 0; g < 2; ++g) {
+    if (lo[g] == hi[g]) continue;
+    const bool a_covers = g == 0 && h <= stack->prev_h;
+    SPIN_CHECK(wait(sst, stack->finish_done[a_covers ? 0 : 1]));
+    for (int l = lo[g]; l < hi[g]; ++l)
+      if (bts[l].batch > 0) SPIN_CHECK(issue_plan(cfgs[l], bts[l], ios[l], sst));
+    SPIN_CHECK(record(stack->plan_done[g], sst));
+  }
+  // main: each group's finishes after the group's plans
+  for (int g = 0; g < 2; ++g) {
+    if (lo[g] == hi[g]) continue;
+    SPIN_CHECK(wait(mst, stack->plan_done[g]));
+    for (int l = lo[g]; l < hi[g]; ++l)
+      if (bts[l].batch > 0) SPIN_CHECK(issue_finish(cfgs[l], bts[l], ios[l], 0, mst));
+    SPIN_CHECK(record(stack->finish_done[g], mst));
+  }
+  // with a single group, finish_done[1] (what the next call's group-A plans
+  // may wait for when the split widens) must also cover this call
+  if (lo[1] == hi[1]) SPIN_CHECK(record(stack->finish_done[1], mst));
+  stack->prev_h = h;
   return SPIN_OK;
 }
 

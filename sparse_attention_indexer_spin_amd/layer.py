@@ -90,3 +90,41 @@ class SpinLayer:
         api.spin_ema_update(self.cfg, bt, self.z, self.sel, self.n_sel, self.V, self.D,
                             n_valid=n_valid, stream=stream, v_max=self.v_max)
         api.spin_advance(self.rows, self.q_pos, self.step_ctr, n_valid=n_valid, stream=stream)
+
+
+class SpinStack:
+    """The SPIN state of several layers and the multi-layer schedule: every
+    layer's plan (predict + select) runs on a side stream, overlapped with the
+    score / top-K / EMA of other layers on the main stream (spin_stack_step).
+
+    `layers` are SpinLayer objects (own EMA state, counters and buffers each).
+    step() takes per-layer queries, weights and key caches."""
+
+    def __init__(self, layers, device="cuda"):
+        self.layers = list(layers)
+        self.stack = api.Stack(len(self.layers))
+        # default priority (a side stream of another priority is not used)
+        self.side = torch.cuda.Stream(device=device)
+        self._order_next = True
+
+    def inputs_changed(self):
+        """Call after writing a layer's plan inputs on the main stream since
+        the last step (set_requests, reset, budgets): the next step's plans
+        then wait for the main stream first."""
+        self._order_next = True
+
+    def step(self, qs, ws, k_pages, k_scales, page_tables, n_valid=None, budgets=None,
+             stream=None, n_layers=None):
+        """One decode step of the first n_layers layers (default: all)."""
+        n = len(self.layers) if n_layers is None else n_layers
+        cfgs, bts, ios = [], [], []
+        for l, lay in enumerate(self.layers[:n]):
+            bts.append(lay.batch(k_pages[l].shape[0]))
+            cfgs.append(lay.cfg)
+            ios.append(lay.make_io(qs[l], ws[l], k_pages[l], k_scales[l], page_tables[l],
+                                   None if n_valid is None else n_valid[l],
+                                   None if budgets is None else budgets[l]))
+        api.spin_stack_step(self.stack, cfgs, bts, ios, order_after_main=self._order_next,
+                            main_stream=stream, side_stream=self.side)
+        self._order_next = False
+        return [lay.topk_idx for lay in self.layers]

@@ -122,3 +122,13 @@ def test_host_validation_without_gpu(lib):
     assert lib.spin_advance(0, 1, None, None, None, None) == 0
     assert lib.spin_advance(1, 9, None, None, None, None) == 2
     assert lib.spin_workspace_bytes(C.byref(cfg), 32, 1, 2048) >= 0
+
+
+def test_stack_host_validation_without_gpu(lib):
+    """spin_stack argument errors come back before any HIP call."""
+    h = C.c_void_p()
+    assert lib.spin_stack_create(0, C.byref(h)) == 2 and not h.value
+    assert lib.spin_stack_create(257, C.byref(h)) == 2 and not h.value
+    assert lib.spin_stack_create(4, None) == 1
+    assert lib.spin_stack_step(None, 1, None, None, None, 0, None, None) == 1
+    lib.spin_stack_destroy(None)  # a no-op

@@ -1,0 +1,108 @@
+"""Multi-layer decode steps through spin_stack_step (plans on a side stream,
+score / top-K / EMA on the main stream): every layer's outputs and EMA state
+must be bit-identical to the same layers stepped one after another with
+spin_step on one stream, and to spin_step_plan + spin_step_finish; on
+integer-valued inputs (every score exact in fp32) also to the CPU oracle,
+closed loop."""
+import numpy as np
+import pytest
+import torch
+
+import spin_synth as G
+from tests.gpu_util import DEV, banner, device_keys, make_layer
+from tests.harness import build_layer, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_attention_indexer_spin_amd import _lib
+    return _lib.load()
+
+
+def _workload(layers, steps=6):
+    # ragged requests, per-layer heavy-slot fraction and direction norm
+    return G.WORKLOADS["fp8_256k_ragged_8l"].scaled(batch=5, layers=layers, n_slots=64 * 150 + 9,
+                                                    n_slots_min=3000, steps=steps, topk=256)
+
+
+def _state(lay):
+    return [t.clone() for t in (lay.topk_idx, lay.V, lay.D, lay.z, lay.row_code, lay.sel,
+                                lay.n_sel, lay.q_pos, lay.step_ctr)]
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_stack_matches_sequential_steps(integer):
+    banner(f"stack vs sequential integer={integer}")
+    from sparse_attention_indexer_spin_amd import SpinStack, api as A
+    n_layers = 3
+    w = _workload(n_layers)
+    lis = [build_layer(w, layer=l, integer=integer) for l in range(n_layers)]
+    keys = [device_keys(li) for li in lis]
+    seq = [make_layer(li, 4000) for li in lis]
+    stk_layers = [make_layer(li, 4000) for li in lis]
+    split = [make_layer(li, 4000) for li in lis]
+    stack = SpinStack(stk_layers)
+    torch.cuda.synchronize()
+    for s in range(w.steps):
+        qs = [li.q[s].to(DEV).contiguous() for li in lis]
+        ws = [li.weights.to(DEV) for li in lis]
+        for l in range(n_layers):
+            seq[l].step(qs[l], ws[l], *keys[l])
+            lay = split[l]
+            bt = lay.batch(keys[l][0].shape[0])
+            io = lay.make_io(qs[l], ws[l], *keys[l])
+            A.spin_step_plan(lay.cfg, bt, io)
+            A.spin_step_finish(lay.cfg, bt, io)
+        stack.step(qs, ws, [k[0] for k in keys], [k[1] for k in keys], [k[2] for k in keys])
+        torch.cuda.synchronize()
+        for l in range(n_layers):
+            a, b, c = _state(seq[l]), _state(stk_layers[l]), _state(split[l])
+            for x, y, z in zip(a, b, c):
+                assert torch.equal(x, y), f"stack differs from spin_step: step {s} layer {l}"
+                assert torch.equal(x, z), f"plan+finish differs from spin_step: step {s} layer {l}"
+    for lay in stk_layers + seq + split:
+        assert int(lay.err.item()) == 0
+    if not integer:
+        return
+    # integer inputs: every layer against the closed-loop oracle
+    for l in range(n_layers):
+        ref, states = run_oracle(lis[l], w.steps, 4000)
+        top = stk_layers[l].topk_idx.cpu().numpy()
+        for r in range(w.batch):
+            assert np.array_equal(top[r], ref[w.steps - 1][r]["topk"]), (l, r)
+            N = int(lis[l].ctx[r])
+            assert np.array_equal(stk_layers[l].V.cpu().numpy()[r, :N], states[r].V[:N]), (l, r)
+
+
+def test_stack_reuse_after_reset_and_fewer_layers():
+    """A reset between steps (announced with inputs_changed) and a step over a
+    prefix of the layers: still identical to sequential spin_step calls."""
+    banner("stack reset / layer prefix")
+    from sparse_attention_indexer_spin_amd import SpinStack
+    n_layers = 4
+    w = _workload(n_layers, steps=5)
+    lis = [build_layer(w, layer=l) for l in range(n_layers)]
+    keys = [device_keys(li) for li in lis]
+    seq = [make_layer(li, 3000) for li in lis]
+    stk_layers = [make_layer(li, 3000) for li in lis]
+    stack = SpinStack(stk_layers)
+    for s in range(w.steps):
+        qs = [li.q[s].to(DEV).contiguous() for li in lis]
+        ws = [li.weights.to(DEV) for li in lis]
+        if s == 3:
+            for lay in seq + stk_layers:
+                lay.reset()
+            stack.inputs_changed()
+        use = n_layers if s != 2 else 2            # step 2 runs layers 0-1 only
+        for l in range(use):
+            seq[l].step(qs[l], ws[l], *keys[l])
+        stack.step(qs, ws, [k[0] for k in keys], [k[1] for k in keys], [k[2] for k in keys],
+                   n_layers=use)
+        torch.cuda.synchronize()
+        for l in range(n_layers):
+            for x, y in zip(_state(seq[l]), _state(stk_layers[l])):
+                assert torch.equal(x, y), f"step {s} layer {l}"
