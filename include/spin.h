@@ -282,6 +282,49 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
                             int32_t order_after_main, void* main_stream, void* side_stream);
 
 /*
+ * Per-layer block budgets (blog "Sparse Attention Still Has a Dense Problem",
+ * section "Per-layer block budgets": every P steps a dense probe step measures
+ * each layer's miss curve -- the share of the dense top-K slots that fall in
+ * skipped blocks, at each budget -- and the budgets are re-sized per layer at
+ * a fixed total, minimising the worst layer's miss rate, into a device-side
+ * table).  A budget is a level g in 0 .. levels (levels divides 10000): the
+ * blocks the selection keeps at target sparsity 10000 - (10000/levels) g bp,
+ * at least ceil(K/64) and at most B.
+ *
+ * spin_miss_curve: after a dense step (every block selected, e.g. budget B),
+ *   from that step's predicted scores S (f32 [R][n_rows][max_blocks], as the
+ *   plan left them) and dense top-K (i32 [R][n_rows][K], -1 padded):
+ *   covered[r][row][g] = top-K slots inside the blocks kept at level g
+ *   without exploration (the forced blocks and the first m - n_f - n_e
+ *   others by S desc, lower block first), g = 0 .. levels;
+ *   kprime[r][row] = valid top-K slots.  Device buffers; max_blocks <= 8192.
+ * spin_budget_fill: budget[r] (i32 [R], the selection's budget override) =
+ *   the blocks of level level_table[0] (device i32) for request r.  Reading
+ *   the level on the device keeps the table usable from captured graphs.
+ * spin_budget_allocate (host only, no device work): per-layer levels from
+ *   covered / total (i64 [L][levels + 1] and [L], summed over a layer's
+ *   requests and rows) with sum_l level_l = L * target_level:
+ *   SPIN_BUDGET_MINIMAX raises, one level at a time, the layer with the
+ *   largest miss rate (1 - covered/total at its level; ties: lower layer)
+ *   from all-zero levels; SPIN_BUDGET_PROPORTIONAL shares the levels in
+ *   proportion to running_miss[l] + 1e-3 (f64 [L]), clamped to [0, levels],
+ *   integer parts plus one level to the largest fractional parts (ties: lower
+ *   layer).  covered/total may be NULL for the proportional rule,
+ *   running_miss for minimax.
+ */
+enum { SPIN_BUDGET_MINIMAX = 0, SPIN_BUDGET_PROPORTIONAL = 1 };
+spin_status spin_miss_curve(const spin_config* cfg, const spin_batch* bt, const float* S,
+                            const int32_t* topk_idx, int32_t levels, int32_t* covered,
+                            int32_t* kprime, void* stream);
+spin_status spin_budget_fill(const spin_config* cfg, const spin_batch* bt,
+                             const int32_t* level_table, int32_t levels, int32_t* budget,
+                             void* stream);
+spin_status spin_budget_allocate(int32_t policy, int32_t n_layers, int32_t levels,
+                                 int32_t target_level, const int64_t* covered,
+                                 const int64_t* total, const double* running_miss,
+                                 int32_t* level_out);
+
+/*
  * Device workspace bytes spin_topk / spin_step need for this shape.  The
  * buffer holds the top-K threshold hints and candidate lists (any initial
  * contents are valid: a hint only changes speed) followed, for spin_step, by

@@ -23,7 +23,9 @@ SPIN_MAX_ROWS, SPIN_MAX_BLOCKS, SPIN_MAX_TOPK, SPIN_MAX_LAYERS = 4, 8192, 8192, 
 EXPORTS = ["spin_predict_blocks", "spin_select_blocks", "spin_sparse_index_score", "spin_topk",
            "spin_ema_update", "spin_advance", "spin_reset_state", "spin_step",
            "spin_workspace_bytes", "spin_last_error", "spin_step_plan", "spin_step_finish",
-           "spin_stack_create", "spin_stack_destroy", "spin_stack_step"]
+           "spin_stack_create", "spin_stack_destroy", "spin_stack_step", "spin_miss_curve",
+           "spin_budget_fill", "spin_budget_allocate"]
+SPIN_BUDGET_MINIMAX, SPIN_BUDGET_PROPORTIONAL = 0, 1
 
 
 class SpinConfig(C.Structure):
@@ -78,6 +80,9 @@ def load() -> C.CDLL:
         "spin_step_finish": [cfg, bt, C.POINTER(SpinStepIO), I32, P],
         "spin_stack_create": [I32, C.POINTER(P)],
         "spin_stack_step": [P, I32, cfg, bt, C.POINTER(SpinStepIO), I32, P, P],
+        "spin_miss_curve": [cfg, bt, P, P, I32, P, P, P],
+        "spin_budget_fill": [cfg, bt, P, I32, P, P],
+        "spin_budget_allocate": [I32, I32, I32, I32, P, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)

@@ -161,3 +161,35 @@ def spin_stack_step(stack: Stack, cfgs, bts, ios, order_after_main: bool = False
     ia = (L.SpinStepIO * n)(*ios)
     L.check(L.load().spin_stack_step(stack.handle, n, ca, ba, ia, int(bool(order_after_main)),
                                      _stream(main_stream), side_stream.cuda_stream))
+
+
+def spin_miss_curve(cfg, bt, S, topk_idx, levels: int, covered, kprime, stream=None):
+    L.check(L.load().spin_miss_curve(C.byref(cfg), C.byref(bt), _p(S), _p(topk_idx), levels,
+                                     _p(covered), _p(kprime), _stream(stream)))
+
+
+def spin_budget_fill(cfg, bt, level_table, levels: int, budget, stream=None):
+    L.check(L.load().spin_budget_fill(C.byref(cfg), C.byref(bt), _p(level_table), levels,
+                                      _p(budget), _stream(stream)))
+
+
+def spin_budget_allocate(policy: str, levels: int, target_level: int, covered=None, total=None,
+                         running_miss=None):
+    """Host-only allocation of per-layer levels (numpy in, list of ints out)."""
+    import numpy as np
+    if policy == "minimax":
+        cov = np.ascontiguousarray(covered, dtype=np.int64)
+        tot = np.ascontiguousarray(total, dtype=np.int64)
+        n = tot.shape[0]
+        assert cov.shape == (n, levels + 1)
+        args = (L.SPIN_BUDGET_MINIMAX, cov.ctypes.data, tot.ctypes.data, None)
+    elif policy == "proportional":
+        miss = np.ascontiguousarray(running_miss, dtype=np.float64)
+        n = miss.shape[0]
+        args = (L.SPIN_BUDGET_PROPORTIONAL, None, None, miss.ctypes.data)
+    else:
+        raise ValueError(f"unknown budget policy {policy!r}")
+    out = np.zeros(n, dtype=np.int32)
+    L.check(L.load().spin_budget_allocate(args[0], n, levels, target_level, args[1], args[2],
+                                          args[3], out.ctypes.data))
+    return out.tolist()

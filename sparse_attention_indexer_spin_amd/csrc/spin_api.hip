@@ -360,6 +360,78 @@ struct spin_stack {
 
 extern "C" {
 
+static spin_status check_levels(const char* fn, int32_t levels) {
+  if (levels < 1 || levels > 10000 || 10000 % levels != 0)
+    return fail(SPIN_E_SHAPE, "%s: levels %d must divide 10000", fn, levels);
+  return SPIN_OK;
+}
+
+spin_status spin_miss_curve(const spin_config* cfg, const spin_batch* bt, const float* S,
+                            const int32_t* topk_idx, int32_t levels, int32_t* covered,
+                            int32_t* kprime, void* stream) {
+  const char* fn = "spin_miss_curve";
+  SPIN_CHECK(check_config(fn, cfg));
+  SPIN_CHECK(check_batch(fn, bt));
+  SPIN_CHECK(check_levels(fn, levels));
+  SPIN_REQUIRE(S);
+  SPIN_REQUIRE(topk_idx);
+  SPIN_REQUIRE(covered);
+  SPIN_REQUIRE(kprime);
+  if (bt->batch == 0) return SPIN_OK;
+  return hip_status(spin::launch_miss_curve(*cfg, *bt, S, topk_idx, levels, covered, kprime,
+                                            (hipStream_t)stream), fn);
+}
+
+spin_status spin_budget_fill(const spin_config* cfg, const spin_batch* bt,
+                             const int32_t* level_table, int32_t levels, int32_t* budget,
+                             void* stream) {
+  const char* fn = "spin_budget_fill";
+  SPIN_CHECK(check_config(fn, cfg));
+  SPIN_CHECK(check_batch(fn, bt));
+  SPIN_CHECK(check_levels(fn, levels));
+  SPIN_REQUIRE(level_table);
+  SPIN_REQUIRE(budget);
+  if (bt->batch == 0) return SPIN_OK;
+  return hip_status(spin::launch_budget_fill(*cfg, *bt, level_table, levels, budget,
+                                             (hipStream_t)stream), fn);
+}
+
+spin_status spin_budget_allocate(int32_t policy, int32_t n_layers, int32_t levels,
+                                 int32_t target_level, const int64_t* covered,
+                                 const int64_t* total, const double* running_miss,
+                                 int32_t* level_out) {
+  const char* fn = "spin_budget_allocate";
+  SPIN_CHECK(check_levels(fn, levels));
+  if (n_layers < 1 || n_layers > SPIN_MAX_LAYERS)
+    return fail(SPIN_E_SHAPE, "%s: n_layers %d outside [1, %d]", fn, n_layers, SPIN_MAX_LAYERS);
+  if (target_level < 0 || target_level > levels)
+    return fail(SPIN_E_SHAPE, "%s: target_level %d outside [0, %d]", fn, target_level, levels);
+  SPIN_REQUIRE(level_out);
+  if (policy == SPIN_BUDGET_MINIMAX) {
+    SPIN_REQUIRE(covered);
+    SPIN_REQUIRE(total);
+    for (int l = 0; l < n_layers; ++l) {
+      if (total[l] < 0) return fail(SPIN_E_SHAPE, "%s: total[%d] < 0", fn, l);
+      for (int g = 0; g <= levels; ++g) {
+        const int64_t c = covered[(int64_t)l * (levels + 1) + g];
+        if (c < 0 || c > total[l])
+          return fail(SPIN_E_SHAPE, "%s: covered[%d][%d] outside [0, total]", fn, l, g);
+      }
+    }
+    spin::allocate_minimax(n_layers, levels, target_level, covered, total, level_out);
+    return SPIN_OK;
+  }
+  if (policy == SPIN_BUDGET_PROPORTIONAL) {
+    SPIN_REQUIRE(running_miss);
+    for (int l = 0; l < n_layers; ++l)
+      if (!(running_miss[l] >= 0.0 && running_miss[l] <= 1.0))
+        return fail(SPIN_E_SHAPE, "%s: running_miss[%d] outside [0, 1]", fn, l);
+    spin::allocate_proportional(n_layers, levels, target_level, running_miss, level_out);
+    return SPIN_OK;
+  }
+  return fail(SPIN_E_SHAPE, "%s: unknown policy %d", fn, policy);
+}
+
 spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_step_io* io,
                       int32_t defer_ema, void* stream) {
   SPIN_CHECK(check_step("spin_step", cfg, bt, io));

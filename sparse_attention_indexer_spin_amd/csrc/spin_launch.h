@@ -64,6 +64,17 @@ hipError_t launch_advance(int R, int rows, const int32_t* n_valid, int32_t* qpos
 hipError_t launch_reset(int R, float* V, int64_t v_ld, float* D, int64_t d_ld, int64_t vmax_ld,
                         float* vmax, int32_t* step, hipStream_t st);
 
+// Per-layer budgets: the miss curve of a dense probe step, the budget table
+// fill, and the host allocation between layers.
+hipError_t launch_miss_curve(const spin_config& c, const spin_batch& b, const float* S,
+                             const int32_t* topk, int levels, int32_t* covered, int32_t* kprime,
+                             hipStream_t st);
+hipError_t launch_budget_fill(const spin_config& c, const spin_batch& b, const int32_t* level,
+                              int levels, int32_t* budget, hipStream_t st);
+void allocate_minimax(int L, int levels, int target, const int64_t* covered,
+                      const int64_t* total, int32_t* out);
+void allocate_proportional(int L, int levels, int target, const double* miss, int32_t* out);
+
 // Number of workgroups of `threads` threads of `kernel` resident at once on
 // the current device (occupancy x compute units), cached per kernel.
 int resident_workgroups(const void* kernel, int threads, size_t dyn_lds = 0);

@@ -98,14 +98,96 @@ class SpinStack:
     score / top-K / EMA of other layers on the main stream (spin_stack_step).
 
     `layers` are SpinLayer objects (own EMA state, counters and buffers each).
-    step() takes per-layer queries, weights and key caches."""
+    step() takes per-layer queries, weights and key caches.
 
-    def __init__(self, layers, device="cuda"):
+    Per-layer block budgets (optional, `budget_policy` "minimax" or
+    "proportional"): every `probe_period` steps (t = P, 2P, ... after a reset)
+    a probe step selects every block of every layer; its miss curves
+    (spin_miss_curve) go to the host, which re-sizes the layers' budget levels
+    (spin_budget_allocate: the level sum stays n_layers x the target level of
+    the layers' sparsity) and publishes them to the device-side level table;
+    the budgets apply from the second step after the probe on.  Until the
+    first probe every layer runs at the target level."""
+
+    def __init__(self, layers, device="cuda", budget_policy=None, probe_period: int = 8,
+                 levels: int = 100):
         self.layers = list(layers)
         self.stack = api.Stack(len(self.layers))
         # default priority (a side stream of another priority is not used)
         self.side = torch.cuda.Stream(device=device)
         self._order_next = True
+        self.policy = budget_policy
+        if budget_policy is not None:
+            assert budget_policy in ("minimax", "proportional")
+            L, R = len(self.layers), self.layers[0].R
+            sp = {lay.cfg.sparsity_bp for lay in self.layers}
+            assert len(sp) == 1 and 10000 % levels == 0 and (10000 - sp.pop()) % (10000 // levels) == 0
+            self.levels, self.P = levels, probe_period
+            self.target = (10000 - self.layers[0].cfg.sparsity_bp) // (10000 // levels)
+            dev = torch.device(device)
+            i32 = dict(dtype=torch.int32, device=dev)
+            self.level_table = torch.full((L,), self.target, **i32)
+            self.probe_table = torch.full((1,), levels, **i32)
+            self.budget = torch.zeros(L, R, **i32)
+            self.probe_budget = torch.zeros(L, R, **i32)
+            rows = self.layers[0].rows
+            self.covered = torch.zeros(L, R, rows, levels + 1, **i32)
+            self.kprime = torch.zeros(L, R, rows, **i32)
+            self.covered_host = torch.zeros(L, R, rows, levels + 1, dtype=torch.int32,
+                                            pin_memory=True)
+            self.kprime_host = torch.zeros(L, R, rows, dtype=torch.int32, pin_memory=True)
+            self.level_host = torch.zeros(L, dtype=torch.int32, pin_memory=True)
+            self.probe_event = torch.cuda.Event()
+            self.publish_event = torch.cuda.Event()
+            self.reset_budgets()
+
+    # -- budgets -------------------------------------------------------------
+    def reset_budgets(self):
+        """Uniform target levels, no probe history: call with a reset of the
+        layers, and after set_requests (the budgets follow the contexts)."""
+        self.t = 0
+        self.levels_now = [self.target] * len(self.layers)
+        self.level_history = []            # (step, levels) of every allocation
+        self.miss_sum = [0.0] * len(self.layers)
+        self.n_probes = 0
+        self._pending = None               # step of a probe whose curves are not applied yet
+        self._publish(self.levels_now, fill_probe=True)
+
+    def _publish(self, levels, fill_probe=False):
+        """Level table -> per-layer budgets, on the side stream (before its plans).
+        The fill reads the layers' ctx_len, written on the main stream."""
+        self.publish_event.synchronize()       # the previous copy out of level_host ran
+        self.level_host.copy_(torch.tensor(levels, dtype=torch.int32))
+        self.side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(self.side):
+            self.level_table.copy_(self.level_host, non_blocking=True)
+            for l, lay in enumerate(self.layers):
+                bt = lay.batch(lay.n_pages)
+                api.spin_budget_fill(lay.cfg, bt, self.level_table[l:l + 1], self.levels,
+                                     self.budget[l], stream=self.side)
+                if fill_probe:
+                    api.spin_budget_fill(lay.cfg, bt, self.probe_table, self.levels,
+                                         self.probe_budget[l], stream=self.side)
+        self.publish_event.record(self.side)
+
+    def _apply_probe(self):
+        """Host side of a probe: miss curves -> new levels (see class docstring)."""
+        self.probe_event.synchronize()
+        cov = self.covered_host.to(torch.int64).sum(dim=(1, 2)).numpy()     # [L, levels+1]
+        tot = self.kprime_host.to(torch.int64).sum(dim=(1, 2)).numpy()      # [L]
+        if self.policy == "minimax":
+            new = api.spin_budget_allocate("minimax", self.levels, self.target, covered=cov,
+                                           total=tot)
+        else:
+            for l in range(len(self.layers)):
+                g = self.levels_now[l]
+                self.miss_sum[l] += 0.0 if tot[l] == 0 else float(tot[l] - cov[l][g]) / float(tot[l])
+            self.n_probes += 1
+            new = api.spin_budget_allocate("proportional", self.levels, self.target,
+                                           running_miss=[m / self.n_probes for m in self.miss_sum])
+        self.levels_now = list(new)
+        self.level_history.append((self.t, list(new)))
+        self._publish(self.levels_now)
 
     def inputs_changed(self):
         """Call after writing a layer's plan inputs on the main stream since
@@ -117,6 +199,15 @@ class SpinStack:
              stream=None, n_layers=None):
         """One decode step of the first n_layers layers (default: all)."""
         n = len(self.layers) if n_layers is None else n_layers
+        probe = False
+        if self.policy is not None:
+            assert budgets is None and n == len(self.layers)
+            if self._pending is not None and self.t >= self._pending + 2:
+                self._apply_probe()
+                self._pending = None
+            probe = self.t > 0 and self.t % self.P == 0
+            src = self.probe_budget if probe else self.budget
+            budgets = [src[l] for l in range(n)]
         cfgs, bts, ios = [], [], []
         for l, lay in enumerate(self.layers[:n]):
             bts.append(lay.batch(k_pages[l].shape[0]))
@@ -127,4 +218,18 @@ class SpinStack:
         api.spin_stack_step(self.stack, cfgs, bts, ios, order_after_main=self._order_next,
                             main_stream=stream, side_stream=self.side)
         self._order_next = False
-        return [lay.topk_idx for lay in self.layers]
+        if probe:
+            st = torch.cuda.current_stream() if stream is None else stream
+            for l, lay in enumerate(self.layers):
+                api.spin_miss_curve(lay.cfg, bts[l], lay.S, lay.topk_idx, self.levels,
+                                    self.covered[l], self.kprime[l], stream=st)
+            with torch.cuda.stream(st):
+                self.covered_host.copy_(self.covered, non_blocking=True)
+                self.kprime_host.copy_(self.kprime, non_blocking=True)
+            self.probe_event.record(st)
+            self._pending = self.t
+            # the next plans overwrite S: order them after the curves
+            self._order_next = True
+        if self.policy is not None:
+            self.t += 1
+        return [lay.topk_idx for lay in self.layers[:n]]

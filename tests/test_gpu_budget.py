@@ -1,0 +1,151 @@
+"""Per-layer block budgets on the GPU: the miss-curve kernel and the budget
+table fill against the oracle (exact integers), and multi-layer runs with
+probes in which every step's outputs, every probe's miss curves and every
+re-allocation match a reference driven by the oracle's budget functions."""
+import numpy as np
+import pytest
+import torch
+
+import spin_synth as G
+from oracle import spin_budget as OB
+from oracle import spin_oracle as O
+from tests.gpu_util import DEV, banner, device_keys, make_layer
+from tests.harness import build_layer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_attention_indexer_spin_amd import _lib
+    return _lib.load()
+
+
+def _batch(ctx, rows, mb):
+    from sparse_attention_indexer_spin_amd import api as A
+    t = lambda x: torch.as_tensor(np.asarray(x), dtype=torch.int32, device=DEV)
+    keep = dict(ctx=t(ctx), qpos=t([c + 3 for c in ctx]), step=t([5] * len(ctx)),
+                req=t(np.arange(len(ctx))))
+    bt = A.batch(ctx_len=keep["ctx"], q_pos=keep["qpos"], step=keep["step"], req_id=keep["req"],
+                 n_rows=rows, max_blocks=mb, n_pages=1)
+    return bt, keep
+
+
+@pytest.mark.parametrize("mb,ctx", [(64, [4096, 4000, 130, 64]), (2048, [131072, 70001, 200]),
+                                    (4096, [262144, 190000]), (8192, [524288, 300001])])
+@pytest.mark.parametrize("levels,explore", [(4, 0), (100, 500), (100, 3000)])
+@pytest.mark.parametrize("rows", [1, 2])
+def test_miss_curve_parity(mb, ctx, levels, explore, rows):
+    banner(f"miss curve mb={mb} levels={levels} explore={explore} rows={rows}")
+    from sparse_attention_indexer_spin_amd import api as A
+    R, K = len(ctx), 2048 if mb > 64 else 512
+    ctx = list(ctx) + [64 * mb + 5]                       # plus one invalid request
+    R += 1
+    S = G.make_scores((R, rows, mb), seed=7 + mb + rows, ties=True)
+    rng = np.random.default_rng(mb + levels + rows)
+    topk = -np.ones((R, rows, K), dtype=np.int32)
+    for r in range(R - 1):
+        for row in range(rows):
+            n = int(rng.integers(0, min(K, ctx[r]) + 1))
+            topk[r, row, :n] = np.sort(rng.choice(ctx[r], n, replace=False))
+    bt, keep = _batch(ctx, rows, mb)
+    cfg = A.config(topk=K, sparsity_bp=4000, explore_bp=explore)
+    cov = torch.full((R, rows, levels + 1), -3, dtype=torch.int32, device=DEV)
+    kp = torch.full((R, rows), -3, dtype=torch.int32, device=DEV)
+    A.spin_miss_curve(cfg, bt, S.to(DEV), torch.from_numpy(topk).to(DEV), levels, cov, kp)
+    cov, kp = cov.cpu().numpy(), kp.cpu().numpy()
+    for r in range(R - 1):
+        for row in range(rows):
+            want, wk = OB.miss_curve(S[r, row, :O.n_blocks(ctx[r])].numpy(), topk[r, row],
+                                     ctx[r], K, explore, levels)
+            assert cov[r, row].tolist() == want, (r, row)
+            assert kp[r, row] == wk
+    assert (cov[R - 1] == 0).all() and (kp[R - 1] == 0).all()
+
+
+def test_budget_fill_parity():
+    banner("budget fill")
+    from sparse_attention_indexer_spin_amd import api as A
+    ctx = [131072, 70001, 200, 64, 1]
+    bt, keep = _batch(ctx, 1, 2048)
+    cfg = A.config(topk=2048, sparsity_bp=4000)
+    for levels in (4, 100):
+        for g in sorted({0, 1, levels // 3, levels - 1, levels}):
+            out = torch.full((len(ctx),), -1, dtype=torch.int32, device=DEV)
+            A.spin_budget_fill(cfg, bt, torch.tensor([g], dtype=torch.int32, device=DEV), levels,
+                               out)
+            want = [OB.level_budget(O.n_blocks(c), 2048, g, levels) for c in ctx]
+            assert out.cpu().tolist() == want, (levels, g)
+
+
+@pytest.mark.parametrize("policy", ["minimax", "proportional"])
+def test_stack_budgets_match_oracle_reference(policy):
+    """SpinStack with probes every 3 steps against sequential spin_step layers
+    whose budgets come from the oracle: oracle miss curves of the same probe
+    outputs, oracle allocation, applied from the second step after the probe."""
+    banner(f"stack budgets {policy}")
+    from sparse_attention_indexer_spin_amd import SpinStack
+    L, P, levels, sp = 3, 3, 100, 4000
+    w = G.WORKLOADS["fp8_256k_ragged_8l"].scaled(batch=4, layers=L, n_slots=64 * 120 + 9,
+                                                 n_slots_min=3000, steps=11, topk=256)
+    lis = [build_layer(w, layer=l) for l in range(L)]
+    keys = [device_keys(li) for li in lis]
+    seq = [make_layer(li, sp) for li in lis]
+    stk = [make_layer(li, sp) for li in lis]
+    stack = SpinStack(stk, budget_policy=policy, probe_period=P, levels=levels)
+    target = (10000 - sp) // 100
+    ref_levels, history, pending, miss_sum, n_probes = [target] * L, [], None, [0.0] * L, 0
+    Bs = [O.n_blocks(int(c)) for c in lis[0].ctx]
+    ref_cov = None
+    for s in range(w.steps):
+        if pending is not None and s >= pending + 2:
+            cov, tot = ref_cov
+            if policy == "minimax":
+                ref_levels = OB.allocate_minimax(cov, tot, target, levels)
+            else:
+                for l in range(L):
+                    miss_sum[l] += 0.0 if tot[l] == 0 else (tot[l] - cov[l][ref_levels[l]]) / tot[l]
+                n_probes += 1
+                ref_levels = OB.allocate_proportional([m / n_probes for m in miss_sum], target,
+                                                      levels)
+            history.append((s, list(ref_levels)))
+            pending = None
+        probe = s > 0 and s % P == 0
+        qs = [li.q[s].to(DEV).contiguous() for li in lis]
+        ws = [li.weights.to(DEV) for li in lis]
+        for l in range(L):
+            bud = [B if probe else OB.level_budget(B, w.topk, ref_levels[l], levels) for B in Bs]
+            seq[l].step(qs[l], ws[l], *keys[l],
+                        budget=torch.tensor(bud, dtype=torch.int32, device=DEV))
+        stack.step(qs, ws, [k[0] for k in keys], [k[1] for k in keys], [k[2] for k in keys])
+        torch.cuda.synchronize()
+        stack.side.synchronize()
+        for l in range(L):
+            for a, b in ((seq[l].topk_idx, stk[l].topk_idx), (seq[l].V, stk[l].V),
+                         (seq[l].D, stk[l].D), (seq[l].row_code, stk[l].row_code)):
+                assert torch.equal(a, b), f"step {s} layer {l}"
+        if probe:
+            cov, tot = [], []
+            for l in range(L):
+                S, top = seq[l].S.cpu().numpy(), seq[l].topk_idx.cpu().numpy()
+                c_l, t_l = np.zeros(levels + 1, dtype=np.int64), 0
+                for r in range(w.batch):
+                    c, k = OB.miss_curve(S[r, 0, :Bs[r]], top[r, 0], int(lis[l].ctx[r]), w.topk,
+                                         w.explore_bp, levels)
+                    c_l += np.asarray(c)
+                    t_l += k
+                    assert stk_cov_row(stack, l, r) == c, (s, l, r)
+                cov.append(c_l.tolist())
+                tot.append(t_l)
+            ref_cov, pending = (cov, tot), s
+    assert [h[1] for h in stack.level_history] == [h[1] for h in history]
+    assert [h[0] for h in stack.level_history] == [h[0] for h in history]
+    assert len(history) >= 2
+    for lay in seq + stk:
+        assert int(lay.err.item()) == 0
+
+
+def stk_cov_row(stack, l, r):
+    return stack.covered[l, r, 0].cpu().tolist()
