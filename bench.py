@@ -58,6 +58,12 @@ def parse():
                     help="multi-layer workloads: time whole decode steps of every layer, one "
                          "spin_step per layer on one stream and the spin_stack schedule (plans "
                          "on a side stream)")
+    ap.add_argument("--budget-policy", choices=["none", "proportional", "minimax"],
+                    default="proportional",
+                    help="--stack: per-layer block budgets re-sized from a dense probe every "
+                         "--probe-period steps (the multi-layer workload states the "
+                         "proportional rule), timed beside the uniform runs")
+    ap.add_argument("--probe-period", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 1 GiB device-to-device copies (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -217,7 +223,8 @@ class StackInputs:
         torch.cuda.synchronize()
 
 
-def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict=None):
+def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict=None,
+              policy: str = "none", probe_period: int = 8):
     """Whole decode steps of every layer: (a) one spin_step per layer in layer
     order on the current stream, (b) one spin_stack_step (plans on a side
     stream).  Each mode on its own layer states from the same reset; each timed
@@ -277,6 +284,43 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
 
     ms_stack = timed(stack_step)
     stack.side.synchronize()
+    budget = None
+    if policy != "none":
+        # the same schedule with per-layer budgets and dense probe steps; the
+        # effective sparsity counts every selected block of every step
+        bud_layers = layers()
+        bstack = SpinStack(bud_layers, budget_policy=policy, probe_period=probe_period)
+        sel_blocks = []
+
+        def budget_step(s):
+            if evict is not None:
+                bstack.inputs_changed()
+            bstack.step([inp.q[l][s] for l in range(w.layers)], inp.weights, pages, scales, pts)
+
+        for s in range(warmup):
+            budget_step(s)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for k, s in enumerate(range(warmup, warmup + steps)):
+            if evict is not None:
+                evict()
+            ev[k][0].record(stream)
+            budget_step(s)
+            ev[k][1].record(stream)
+            sel_blocks.append(torch.stack([lay.n_sel for lay in bud_layers]).sum())
+        torch.cuda.synchronize()
+        ms_budget = sum(a.elapsed_time(b) for a, b in ev) / steps
+        total_blocks = w.layers * int(sum(-(-int(c) // 64) for c in inp.ctx))
+        chosen = float(torch.stack(sel_blocks).sum().item()) / steps
+        budget = {"policy": policy, "probe_period": probe_period,
+                  "us_per_step": ms_budget * 1e3,
+                  "us_per_step_layer": ms_budget * 1e3 / w.layers,
+                  "effective_block_sparsity": 1.0 - chosen / total_blocks,
+                  "levels": [h[1] for h in bstack.level_history],
+                  "allocated_at_steps": [h[0] for h in bstack.level_history]}
+        for lay in bud_layers:
+            assert int(lay.err.item()) == 0
     for a, b in zip(seq, stk_layers):
         assert torch.equal(a.topk_idx, b.topk_idx) and torch.equal(a.V, b.V), \
             "stack and sequential steps disagree"
@@ -298,7 +342,8 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
     ns0 = lay.n_sel.cpu().numpy().astype(np.int64)
     keys0 = int(np.minimum(ns0 * 64, ctx).sum()) * w.rows
     return dict(ms_seq=ms_seq, ms_stack=ms_stack, keys_per_step=keys, n_sel=n_sel,
-                score_us_layer0=score_us, keys_layer0=keys0, n_sel_layer0=int(ns0.sum()))
+                score_us_layer0=score_us, keys_layer0=keys0, n_sel_layer0=int(ns0.sum()),
+                budget=budget)
 
 
 def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, budget_s: float,
@@ -467,7 +512,8 @@ def main_stack(args, w: G.Workload, sp: int):
         sys.exit(2)
     inp = StackInputs(w, args.steps + args.warmup)
     evict = Evictor() if args.cache == "cold" else None
-    res = run_stack(inp, sp, args.steps, args.warmup, evict)
+    res = run_stack(inp, sp, args.steps, args.warmup, evict, args.budget_policy,
+                    args.probe_period)
     score_bytes = algorithmic_score_bytes(w, res["keys_layer0"], res["n_sel_layer0"])
     achieved = score_bytes / (res["score_us_layer0"] * 1e-6) / 1e9
     out = {
@@ -488,7 +534,8 @@ def main_stack(args, w: G.Workload, sp: int):
         "stack": {"sequential_us_per_step": res["ms_seq"] * 1e3,
                   "overlapped_us_per_step": res["ms_stack"] * 1e3,
                   "sequential_us_per_step_layer": res["ms_seq"] * 1e3 / w.layers,
-                  "overlapped_us_per_step_layer": res["ms_stack"] * 1e3 / w.layers},
+                  "overlapped_us_per_step_layer": res["ms_stack"] * 1e3 / w.layers,
+                  "per_layer_budgets": res["budget"]},
         "keys_scored_per_step": res["keys_per_step"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
