@@ -8,17 +8,21 @@ path: predict -> select -> sparse indexer score -> top-K -> EMA -> advance,
 each launched through the C ABI on the current stream, inputs resident in HBM.
 
 Prints one JSON line.  `value` = indexer keys scored per second of whole-step
-time (one spin_step call per step).  By default every timed step (and every
-timed stage launch) starts with cold caches: a 1 GiB read streams through the
-L2s and the 256 MB MALL just before it, as when a model's other layers run
-between two steps of this layer, so no key page is served from a cache warmed
-by the previous step; `warm` repeats the step timing back to back for
-reference.  `roofline` is the score kernel's algorithmic HBM bytes per launch /
-its mean launch duration (HIP events around each launch on the step's stream,
-on the last timed step's selection) against 8 TB/s, with `traffic` taken from
-the committed FETCH_SIZE/WRITE_SIZE summary when it was measured on the
-current kernel source.  `cpu_baseline` times the CPU oracle on whole requests
-of the same workload for about 15 s.
+time (one spin_step call per step).  By default (`--cache rotate`) the bench
+steps 4 independent copies of the workload (own key pages, EMA state and
+buffers; the same data) round robin back to back, as the layers of a model
+run: when a copy steps again, the other copies have streamed 3 x its pages
+(~1 GB) through the L2s and the 256 MB MALL, so its pages come from HBM, and
+no host sync or event sits between steps.  The two other protocols are
+reported beside it: `cold` times each step alone after a 1 GiB read (adds the
+event and launch latency of an isolated step), `warm` steps one copy back to
+back (the MALL keeps part of the previous step's pages).  `roofline` is the
+score kernel's algorithmic HBM bytes per launch / its mean launch duration
+(the stage launched round robin over the copies between two HIP events on
+the step's stream, on the last timed step's selection) against 8 TB/s, with
+`traffic` taken from the committed FETCH_SIZE/WRITE_SIZE summary when it was
+measured on the current kernel source.  `cpu_baseline` times the CPU oracle
+on whole requests of the same workload for about 15 s.
 """
 from __future__ import annotations
 
@@ -49,8 +53,12 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="also time the workload's sparsity sweep and fit t = a(1-rho) + c")
     ap.add_argument("--stage-reps", type=int, default=20)
-    ap.add_argument("--cache", choices=["cold", "warm"], default="cold",
-                    help="cold: evict the caches before every timed step and stage launch")
+    ap.add_argument("--cache", choices=["rotate", "cold", "warm"], default="rotate",
+                    help="rotate: step --copies independent copies of the workload round robin "
+                         "back to back (each step's pages were evicted by the others, as between "
+                         "the layers of a model); cold: a 1 GiB read before every timed step and "
+                         "stage launch, each timed alone; warm: one copy back to back")
+    ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-max-requests", type=int, default=32)
@@ -346,6 +354,88 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
                 budget=budget)
 
 
+def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_reps: int,
+               copies: int):
+    """`copies` independent copies of the workload -- own key pages (same data),
+    EMA state and buffers -- stepped round robin back to back, as the layers of
+    a model run: by the time a copy steps again, the others have streamed
+    (copies - 1) x its pages through the L2s and the 256 MB MALL, and no host
+    sync or event sits between two steps.  Per-step time = total / (steps x
+    copies).  Stage timing likewise: each stage launched round robin over the
+    copies, reps x copies launches between two events."""
+    from sparse_attention_indexer_spin_amd import SpinLayer, api
+    w = inp.w
+    pages = [inp.keys.pages] + [inp.keys.pages.clone() for _ in range(copies - 1)]
+    scales = [inp.keys.scale] + [None if inp.keys.scale is None else inp.keys.scale.clone()
+                                 for _ in range(copies - 1)]
+    pt = inp.keys.page_table
+    lays = []
+    for c in range(copies):
+        lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks,
+                        d_cap=G.d_capacity(w, steps + warmup), topk=w.topk,
+                        sparsity_bp=sparsity_bp, n_rows=w.rows, explore_bp=w.explore_bp,
+                        ema_alpha=w.alpha, combine=w.combine,
+                        key_dtype={"fp8": torch.uint8, "bf16": torch.bfloat16,
+                                   "f32": torch.float32}[w.key_dtype],
+                        q_dtype=torch.bfloat16 if w.q_dtype == "bf16" else torch.float32)
+        lay.set_requests(inp.ctx.cuda(), inp.pos[0].cuda())
+        lay.reset()
+        lays.append(lay)
+    bts = [lay.batch(pages[c].shape[0]) for c, lay in enumerate(lays)]
+    nv = [inp.accept_dev[s] if w.rows > 1 else None for s in range(warmup + steps)]
+    ios = [[lay.make_io(inp.q[s], inp.weights, pages[c], scales[c], pt, n_valid=nv[s])
+            for s in range(warmup + steps)] for c, lay in enumerate(lays)]
+    stream = torch.cuda.current_stream()
+    for s in range(warmup):
+        for c in range(copies):
+            api.spin_step(lays[c].cfg, bts[c], ios[c][s])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s in range(warmup, warmup + steps):
+        for c in range(copies):
+            api.spin_step(lays[c].cfg, bts[c], ios[c][s])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    for lay in lays:
+        assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
+    for lay in lays[1:]:
+        assert torch.equal(lay.topk_idx, lays[0].topk_idx), "copies disagree"
+    n_sel = lays[0].n_sel.cpu().numpy().astype(np.int64)
+    ctx = lays[0].ctx_len.cpu().numpy().astype(np.int64)
+    keys = int(np.minimum(n_sel * 64, ctx).sum()) * w.rows
+    out = dict(total_ms=total_ms, ms_per_step=total_ms / (steps * copies), keys_per_step=keys,
+               n_sel=int(n_sel.sum()))
+    if stage_reps:
+        q = inp.q[warmup + steps - 1]
+        last_nv = nv[-1]
+
+        def per_copy(make):
+            fns = [make(c, lays[c], bts[c]) for c in range(copies)]
+            return lambda: [f() for f in fns]
+
+        st = {
+            "predict": per_copy(lambda c, lay, bt: lambda: api.spin_predict_blocks(
+                lay.cfg, bt, lay.V, lay.D, lay.S, v_max=lay.v_max)),
+            "select": per_copy(lambda c, lay, bt: lambda: api.spin_select_blocks(
+                lay.cfg, bt, lay.S, lay.row_code, lay.sel, lay.n_sel)),
+            "score": per_copy(lambda c, lay, bt: lambda: api.spin_sparse_index_score(
+                lay.cfg, bt, q, inp.weights, pages[c], scales[c], pt, lay.sel, lay.n_sel,
+                lay.z)),
+            "topk": per_copy(lambda c, lay, bt: lambda: api.spin_topk(
+                lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.topk_idx, lay.workspace)),
+            "ema": per_copy(lambda c, lay, bt: lambda: api.spin_ema_update(
+                lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.V, lay.D, n_valid=last_nv,
+                v_max=lay.v_max)),
+        }
+        out["stage_us"] = {k: _timed_us(f, stage_reps, stream) / copies for k, f in st.items()}
+        for lay in lays:
+            assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
+    return out
+
+
 def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, budget_s: float,
                  max_requests: int):
     """Time the CPU oracle on whole requests of the workload until about `budget_s`
@@ -449,10 +539,19 @@ def main():
         main_stack(args, w, sp)
         return
     inp = Inputs(w, total_steps)
-    evict = Evictor() if args.cache == "cold" else None
-    # back-to-back steps first, for reference; then the timed protocol
-    warm = run_gpu(inp, sp, args.steps, args.warmup) if evict is not None else None
-    res = run_gpu(inp, sp, args.steps, args.warmup, stage_reps=args.stage_reps, evict=evict)
+    evictor = Evictor()
+    # the two other protocols first, for reference; then the reported one
+    refs = {}
+    if args.cache != "warm":
+        refs["warm"] = run_gpu(inp, sp, args.steps, args.warmup)
+    if args.cache != "cold":
+        refs["cold"] = run_gpu(inp, sp, args.steps, args.warmup, evict=evictor)
+    if args.cache == "rotate":
+        res = run_rotate(inp, sp, args.steps, args.warmup, args.stage_reps, args.copies)
+    else:
+        res = run_gpu(inp, sp, args.steps, args.warmup, stage_reps=args.stage_reps,
+                      evict=evictor if args.cache == "cold" else None)
+    evict = evictor if args.cache == "cold" else None
     score_us = res["stage_us"]["score"]
     keys_row = res["keys_per_step"]
     score_bytes = algorithmic_score_bytes(w, keys_row // w.rows, res["n_sel"])
@@ -470,9 +569,11 @@ def main():
                    "q_dtype": w.q_dtype},
         "us_per_step_layer": res["ms_per_step"] * 1e3,
         "cache": {"mode": args.cache,
-                  "how": "1 GiB read before each timed step and stage launch" if evict is not None
-                  else "steps back to back",
-                  "warm_us_per_step_layer": None if warm is None else warm["ms_per_step"] * 1e3},
+                  "how": {"rotate": f"{args.copies} independent copies of the workload (own "
+                                    "pages and state) stepped round robin back to back",
+                          "cold": "1 GiB read before each timed step and stage launch",
+                          "warm": "one copy, steps back to back"}[args.cache],
+                  **{f"{k}_us_per_step_layer": v["ms_per_step"] * 1e3 for k, v in refs.items()}},
         "stage_us": res["stage_us"],
         "keys_scored_per_step": keys_row,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -485,8 +586,11 @@ def main():
     if args.sweep and w.rows == 1 and len(w.sparsity_bp) > 1:
         sweep = {}
         for s in sorted(set(w.sparsity_bp)):
-            sweep[s] = run_gpu(inp, s, min(args.steps, 20), args.warmup, stage_reps=10,
-                               evict=evict)
+            if args.cache == "rotate":
+                sweep[s] = run_rotate(inp, s, min(args.steps, 20), args.warmup, 10, args.copies)
+            else:
+                sweep[s] = run_gpu(inp, s, min(args.steps, 20), args.warmup, stage_reps=10,
+                                   evict=evict)
         rho = np.array([1.0 - sweep[s]["n_sel"] / (w.batch * w.max_blocks) for s in sweep])
         T = np.array([sweep[s]["ms_per_step"] * 1e3 for s in sweep])
         A = np.stack([1.0 - rho, np.ones_like(rho)], 1)

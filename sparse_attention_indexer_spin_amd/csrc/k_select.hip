@@ -111,6 +111,21 @@ struct SelectLds {
   uint32_t tmpu[32];
 };
 
+// The row's budget m (Algorithm 1 step 4; the forced blocks count toward it,
+// Sec. 3.2.1 caps the exploration share by what is left).
+struct RowBudget {
+  int n_f, n_e, n_r;
+};
+__device__ __forceinline__ RowBudget row_budget(const SelectArgs& a, int B, int bud) {
+  const int kb = (a.K + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  const int keep = (int)(((int64_t)(10000 - a.sparsity_bp) * B + 9999) / 10000);
+  int m = bud > 0 ? min(B, bud) : min(B, max(kb, keep));
+  const int n_f = B > 1 ? 2 : 1;
+  m = max(m, n_f);
+  const int n_e = min((int)((int64_t)m * a.explore_bp / 10000), m - n_f);
+  return RowBudget{n_f, n_e, m - n_f - n_e};
+}
+
 // Block budget, forced / ranked / explored blocks and (compact) the block
 // list of request r, row `row`: B blocks (0 when the request is invalid), t
 // steps since reset, rid the request id, bud a budget override (<= 0: none).
@@ -131,13 +146,8 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int r, int row, 
     for (int e = 0; e < EPT; ++e)
       if (j0 + e < B) { c[e] = SPIN_CODE_DENSE; chosen |= 1u << e; }
   } else if (B > 0) {
-    const int kb = (a.K + SPIN_BLOCK - 1) / SPIN_BLOCK;
-    const int keep = (int)(((int64_t)(10000 - a.sparsity_bp) * B + 9999) / 10000);
-    int m = bud > 0 ? min(B, bud) : min(B, max(kb, keep));
-    const int n_f = B > 1 ? 2 : 1;
-    m = max(m, n_f);
-    const int n_e = min((int)((int64_t)m * a.explore_bp / 10000), m - n_f);
-    const int n_r = m - n_f - n_e;
+    const RowBudget rb = row_budget(a, B, bud);
+    const int n_e = rb.n_e, n_r = rb.n_r;
     float sv[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) sv[e] = j0 + e < B ? Srow[j0 + e] : 0.0f;

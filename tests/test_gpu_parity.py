@@ -136,8 +136,17 @@ def test_ema_keeps_vmax(rows):
 # ---------------------------------------------------------------------------
 # stage 2: select (+ union)
 # ---------------------------------------------------------------------------
+# block capacities from 1 to 8,192: every blocks-per-thread instantiation of
+# the selection, full and ragged contexts, 1-4 rows
 @pytest.mark.parametrize("rows,mb,ctx", [(1, 64, [4096, 4000, 130, 64, 1]),
                                          (4, 64, [4096, 2000, 65]),
+                                         (1, 1, [64, 1, 30]),
+                                         (2, 100, [6400, 6000, 129]),
+                                         (1, 250, [16000, 15999, 4000]),
+                                         (3, 500, [32000, 31000, 64 * 7]),
+                                         (1, 1000, [64000, 40001]),
+                                         (1, 2048, [131072, 131000, 70001, 200]),
+                                         (4, 2048, [131072, 99999]),
                                          (1, 4096, [262144, 70000]),
                                          (2, 8192, [524288, 300001])])
 @pytest.mark.parametrize("step", [0, 1, 9])
