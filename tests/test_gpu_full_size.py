@@ -123,3 +123,75 @@ def test_full_size_sampled_parity(name):
         assert np.array_equal(V1[r], Vr), (name, r)
         assert np.array_equal(D1[r], Dr), (name, r)
     banner(f"full size {name}: requests {_sample_requests(w.batch)} checked")
+
+
+def test_full_size_stack_with_budgets():
+    """The 8-layer ragged workload at full size through SpinStack with per-layer
+    budgets (proportional rule, a probe every 2 steps): every step bit-identical
+    to sequential spin_step layers given the same budgets; the probe's miss
+    curves of sampled requests equal the oracle's; the allocation equals the
+    oracle's on the summed curves."""
+    from oracle import spin_budget as OB
+    from sparse_attention_indexer_spin_amd import SpinLayer, SpinStack
+    banner("full size stack + budgets fp8_256k_ragged_8l")
+    w = G.WORKLOADS["fp8_256k_ragged_8l"]
+    n_steps, sp, P, levels = 5, w.sparsity_bp[0], 2, 100
+    ctx = G.context_lengths(w)
+    pos, _ = G.make_schedule(w, ctx, n_steps)
+    keys, W, Q = [], [], []
+    for l in range(w.layers):
+        k = G.make_keys(w, l, DEV, ctx)
+        keys.append(k)
+        W.append(G.make_weights(w, l, DEV))
+        Q.append(G.cast_queries(w, G.make_queries(w, l, k, pos, DEV)).contiguous())
+
+    def layers():
+        out = []
+        for l in range(w.layers):
+            lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks,
+                            d_cap=G.d_capacity(w, n_steps), topk=w.topk, sparsity_bp=sp,
+                            explore_bp=w.explore_bp, ema_alpha=w.alpha, layer=l, device=DEV)
+            lay.set_requests(ctx.to(DEV), pos[0].to(DEV))
+            lay.reset()
+            out.append(lay)
+        return out
+
+    seq, stk = layers(), layers()
+    stack = SpinStack(stk, budget_policy="proportional", probe_period=P, levels=levels)
+    target = (10000 - sp) // 100
+    Bs = [O.n_blocks(int(c)) for c in ctx]
+    levels_now = [target] * w.layers
+    want_levels = None                       # allocation from the first probe's curves
+    for s in range(n_steps):
+        if stack.level_history and stack.level_history[-1][0] == s:
+            levels_now = stack.level_history[-1][1]
+        probe = s > 0 and s % P == 0
+        for l in range(w.layers):
+            bud = [B if probe else OB.level_budget(B, w.topk, levels_now[l], levels) for B in Bs]
+            seq[l].step(Q[l][s], W[l], keys[l].pages, keys[l].scale, keys[l].page_table,
+                        budget=torch.tensor(bud, dtype=torch.int32, device=DEV))
+        stack.step([Q[l][s] for l in range(w.layers)], W, [k.pages for k in keys],
+                   [k.scale for k in keys], [k.page_table for k in keys])
+        torch.cuda.synchronize()
+        stack.side.synchronize()
+        for l in range(w.layers):
+            for a, b in ((seq[l].topk_idx, stk[l].topk_idx), (seq[l].V, stk[l].V),
+                         (seq[l].D, stk[l].D), (seq[l].sel, stk[l].sel)):
+                assert torch.equal(a, b), f"step {s} layer {l}"
+        if probe and want_levels is None:
+            cov = stack.covered.cpu().numpy()
+            kp = stack.kprime.cpu().numpy()
+            for l in (0, w.layers - 1):
+                S, top = stk[l].S.cpu().numpy(), stk[l].topk_idx.cpu().numpy()
+                for r in _sample_requests(w.batch):
+                    want, wk = OB.miss_curve(S[r, 0, :Bs[r]], top[r, 0], int(ctx[r]), w.topk,
+                                             w.explore_bp, levels)
+                    assert cov[l, r, 0].tolist() == want and kp[l, r, 0] == wk, (s, l, r)
+            tot = kp.astype(np.int64).sum(axis=(1, 2))
+            c = cov.astype(np.int64).sum(axis=(1, 2))
+            miss = [0.0 if tot[l] == 0 else float(tot[l] - c[l][levels_now[l]]) / float(tot[l])
+                    for l in range(w.layers)]
+            want_levels = OB.allocate_proportional(miss, target, levels)
+    assert stack.level_history[0] == (P + 2, want_levels)
+    for lay in seq + stk:
+        assert int(lay.err.item()) == 0
