@@ -258,7 +258,9 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
     pts = [k.page_table for k in inp.keys]
     stream = torch.cuda.current_stream()
 
-    def timed(step_fn):
+    def timed(step_fn, join=None):
+        """Mean step time; `join` (if given) orders the main stream after work
+        the step left on other streams, before the last end event."""
         for s in range(warmup):
             step_fn(s)
         torch.cuda.synchronize()
@@ -269,6 +271,8 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
                 evict()
             ev[k][0].record(stream)
             step_fn(s)
+            if join is not None and (evict is not None or k == steps - 1):
+                join()
             ev[k][1].record(stream)
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in ev) / steps
@@ -280,18 +284,23 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
             lay.step(inp.q[l][s], inp.weights[l], pages[l], scales[l], pts[l])
 
     ms_seq = timed(seq_step)
-    stk_layers = layers()
-    stack = SpinStack(stk_layers)
+    def run_stack_mode(ema_stream):
+        lays = layers()
+        stack = SpinStack(lays, ema_stream=ema_stream)
 
-    def stack_step(s):
-        if evict is not None:
-            # the plans may not start before the timed region (they would run
-            # beside the eviction read): order the side stream after main
-            stack.inputs_changed()
-        stack.step([inp.q[l][s] for l in range(w.layers)], inp.weights, pages, scales, pts)
+        def stack_step(s):
+            if evict is not None:
+                # the plans may not start before the timed region (they would
+                # run beside the eviction read): order the side stream after main
+                stack.inputs_changed()
+            stack.step([inp.q[l][s] for l in range(w.layers)], inp.weights, pages, scales, pts)
 
-    ms_stack = timed(stack_step)
-    stack.side.synchronize()
+        ms = timed(stack_step, join=stack.join)
+        torch.cuda.synchronize()
+        return ms, lays
+
+    ms_stack, stk_layers = run_stack_mode(False)
+    ms_stack_ema_stream, lays_ema_stream = run_stack_mode(True)
     budget = None
     if policy != "none":
         # the same schedule with per-layer budgets and dense probe steps; the
@@ -315,6 +324,8 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
                 evict()
             ev[k][0].record(stream)
             budget_step(s)
+            if evict is not None or k == steps - 1:
+                bstack.join()
             ev[k][1].record(stream)
             sel_blocks.append(torch.stack([lay.n_sel for lay in bud_layers]).sum())
         torch.cuda.synchronize()
@@ -329,10 +340,11 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
                   "allocated_at_steps": [h[0] for h in bstack.level_history]}
         for lay in bud_layers:
             assert int(lay.err.item()) == 0
-    for a, b in zip(seq, stk_layers):
-        assert torch.equal(a.topk_idx, b.topk_idx) and torch.equal(a.V, b.V), \
+    for a, b, c in zip(seq, stk_layers, lays_ema_stream):
+        assert torch.equal(a.topk_idx, b.topk_idx) and torch.equal(a.V, b.V) and \
+            torch.equal(a.topk_idx, c.topk_idx) and torch.equal(a.V, c.V), \
             "stack and sequential steps disagree"
-        assert int(a.err.item()) == 0 and int(b.err.item()) == 0
+        assert int(a.err.item()) == 0 and int(b.err.item()) == 0 and int(c.err.item()) == 0
     keys = 0
     ctx = inp.ctx.numpy().astype(np.int64)
     n_sel = 0
@@ -349,7 +361,8 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
         lay.sel, lay.n_sel, lay.z), 20, stream, evict)
     ns0 = lay.n_sel.cpu().numpy().astype(np.int64)
     keys0 = int(np.minimum(ns0 * 64, ctx).sum()) * w.rows
-    return dict(ms_seq=ms_seq, ms_stack=ms_stack, keys_per_step=keys, n_sel=n_sel,
+    return dict(ms_seq=ms_seq, ms_stack=ms_stack, ms_stack_ema_stream=ms_stack_ema_stream,
+                keys_per_step=keys, n_sel=n_sel,
                 score_us_layer0=score_us, keys_layer0=keys0, n_sel_layer0=int(ns0.sum()),
                 budget=budget)
 
@@ -639,6 +652,8 @@ def main_stack(args, w: G.Workload, sp: int):
                   "overlapped_us_per_step": res["ms_stack"] * 1e3,
                   "sequential_us_per_step_layer": res["ms_seq"] * 1e3 / w.layers,
                   "overlapped_us_per_step_layer": res["ms_stack"] * 1e3 / w.layers,
+                  "overlapped_ema_stream_us_per_step_layer":
+                      res["ms_stack_ema_stream"] * 1e3 / w.layers,
                   "per_layer_budgets": res["budget"]},
         "keys_scored_per_step": res["keys_per_step"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

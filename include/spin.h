@@ -262,24 +262,30 @@ spin_status spin_step_finish(const spin_config* cfg, const spin_batch* bt,
  *         after the plans of B, the finishes of B
  * so group A's plans run beside the previous step's group-B scoring and
  * group B's beside this step's group-A scoring, with two cross-stream waits
- * on main per step.  Every layer sees the same results as n spin_step calls
- * in layer order.  The plans also read the caller's ctx_len, req_id and
- * budget: when the caller has written any of them on `main` since the
- * previous call (or reset a layer there), it passes order_after_main != 0,
- * and the side stream first waits for all work issued on `main` before this
- * call.  main and side must be different streams of the stack's device; the
- * call returns without waiting.  The caller's later work on `main` is ordered
- * after everything this call issued.  Deferred EMA is not available here.
- * Errors: SPIN_E_SHAPE when n is < 1 or exceeds the stack's layers, or
- * main == side; each layer's arguments are validated as for spin_step before
- * anything is issued.
+ * on main per step.  With ema_stream != NULL the finishes on main are score +
+ * top-K only, and each group's EMA updates + counter advances run on
+ * ema_stream after the group's finishes; the plans then wait for the
+ * previous call's EMA of their group instead of its finishes.  Every layer
+ * sees the same results as n spin_step calls in layer order.  The plans also
+ * read the caller's ctx_len, req_id and budget: when the caller has written
+ * any of them on `main` since the previous call (or reset a layer there), it
+ * passes order_after_main != 0, and the side stream first waits for all work
+ * issued on `main` before this call.  The streams must differ and belong to
+ * the stack's device; the call returns without waiting.  The caller's later
+ * work on `main` is ordered after every layer's top-K; without ema_stream
+ * also after every EMA update, with it the caller makes `main` wait for
+ * ema_stream before it reads or writes a layer's EMA state or counters.
+ * Deferred EMA is not available here.  Errors: SPIN_E_SHAPE when n is < 1 or
+ * exceeds the stack's layers, or two streams are the same; each layer's
+ * arguments are validated as for spin_step before anything is issued.
  */
 typedef struct spin_stack spin_stack;
 spin_status spin_stack_create(int32_t n_layers, spin_stack** out);
 void spin_stack_destroy(spin_stack* stack);
 spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
                             const spin_batch* bts, const spin_step_io* ios,
-                            int32_t order_after_main, void* main_stream, void* side_stream);
+                            int32_t order_after_main, void* main_stream, void* side_stream,
+                            void* ema_stream);
 
 /*
  * Per-layer block budgets (blog "Sparse Attention Still Has a Dense Problem",

@@ -79,7 +79,7 @@ def load() -> C.CDLL:
         "spin_step_plan": [cfg, bt, C.POINTER(SpinStepIO), P],
         "spin_step_finish": [cfg, bt, C.POINTER(SpinStepIO), I32, P],
         "spin_stack_create": [I32, C.POINTER(P)],
-        "spin_stack_step": [P, I32, cfg, bt, C.POINTER(SpinStepIO), I32, P, P],
+        "spin_stack_step": [P, I32, cfg, bt, C.POINTER(SpinStepIO), I32, P, P, P],
         "spin_miss_curve": [cfg, bt, P, P, I32, P, P, P],
         "spin_budget_fill": [cfg, bt, P, I32, P, P],
         "spin_budget_allocate": [I32, I32, I32, I32, P, P, P, P],

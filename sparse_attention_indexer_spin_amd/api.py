@@ -151,16 +151,18 @@ class Stack:
 
 
 def spin_stack_step(stack: Stack, cfgs, bts, ios, order_after_main: bool = False,
-                    main_stream=None, side_stream=None):
+                    main_stream=None, side_stream=None, ema_stream=None):
     """One decode step of len(cfgs) layers: plans on side_stream, finishes on
-    main_stream (default: the current stream)."""
+    main_stream (default: the current stream), EMA updates on ema_stream when
+    given (else inside the finishes)."""
     n = len(cfgs)
     assert len(bts) == n and len(ios) == n and side_stream is not None
     ca = (L.SpinConfig * n)(*cfgs)
     ba = (L.SpinBatch * n)(*bts)
     ia = (L.SpinStepIO * n)(*ios)
     L.check(L.load().spin_stack_step(stack.handle, n, ca, ba, ia, int(bool(order_after_main)),
-                                     _stream(main_stream), side_stream.cuda_stream))
+                                     _stream(main_stream), side_stream.cuda_stream,
+                                     None if ema_stream is None else ema_stream.cuda_stream))
 
 
 def spin_miss_curve(cfg, bt, S, topk_idx, levels: int, covered, kprime, stream=None):

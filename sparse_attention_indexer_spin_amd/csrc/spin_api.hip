@@ -341,6 +341,16 @@ spin_status issue_finish(const spin_config& c, const spin_batch& b, const spin_s
                     "spin_step/ema+advance");
 }
 
+// The EMA update + counter advance of a finished step (after a finish with
+// defer_ema): q positions from the step's snapshot.
+spin_status issue_ema(const spin_config& c, const spin_batch& b, const spin_step_io& io,
+                      hipStream_t st) {
+  return hip_status(spin::launch_ema(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.n_valid, io.V,
+                                     io.v_ld, io.D, io.d_ld, io.v_max, st, step_qsnap(c, b, io),
+                                     io.q_pos_mut, io.step_mut),
+                    "spin_stack_step/ema+advance");
+}
+
 }  // namespace
 
 // Host-side scheduler state of a multi-layer step.  The layers split into
@@ -355,6 +365,7 @@ struct spin_stack {
   int32_t prev_h = 0;            // group split of the previous call
   hipEvent_t plan_done[2] = {nullptr, nullptr};
   hipEvent_t finish_done[2] = {nullptr, nullptr};
+  hipEvent_t ema_done[2] = {nullptr, nullptr};   // with an EMA stream
   hipEvent_t entry = nullptr;    // main at the call, for order_after_main
 };
 
@@ -463,8 +474,9 @@ spin_status spin_stack_create(int32_t n_layers, spin_stack** out) {
   std::unique_ptr<spin_stack> st(new spin_stack);
   st->n_layers = n_layers;
   SPIN_CHECK(hip_status(hipGetDevice(&st->device), fn));
-  hipEvent_t* evs[5] = {&st->plan_done[0], &st->plan_done[1], &st->finish_done[0],
-                        &st->finish_done[1], &st->entry};
+  hipEvent_t* evs[7] = {&st->plan_done[0], &st->plan_done[1], &st->finish_done[0],
+                        &st->finish_done[1], &st->ema_done[0], &st->ema_done[1],
+                        &st->entry};
   for (hipEvent_t* e : evs) {
     const hipError_t r = hipEventCreateWithFlags(e, hipEventDisableTiming);
     if (r != hipSuccess) {
@@ -479,20 +491,23 @@ spin_status spin_stack_create(int32_t n_layers, spin_stack** out) {
 void spin_stack_destroy(spin_stack* stack) {
   if (!stack) return;
   for (hipEvent_t e : {stack->plan_done[0], stack->plan_done[1], stack->finish_done[0],
-                       stack->finish_done[1], stack->entry})
+                       stack->finish_done[1], stack->ema_done[0], stack->ema_done[1],
+                       stack->entry})
     if (e) (void)hipEventDestroy(e);
   delete stack;
 }
 
 spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
                             const spin_batch* bts, const spin_step_io* ios,
-                            int32_t order_after_main, void* main_stream, void* side_stream) {
+                            int32_t order_after_main, void* main_stream, void* side_stream,
+                            void* ema_stream) {
   const char* fn = "spin_stack_step";
   if (!stack || !cfgs || !bts || !ios) return fail(SPIN_E_NULL, "%s: NULL argument", fn);
   if (n_layers < 1 || n_layers > stack->n_layers)
     return fail(SPIN_E_SHAPE, "%s: n_layers %d outside [1, %d]", fn, n_layers, stack->n_layers);
-  if (main_stream == side_stream)
-    return fail(SPIN_E_SHAPE, "%s: main and side must be different streams", fn);
+  if (main_stream == side_stream || (ema_stream && (ema_stream == main_stream ||
+                                                     ema_stream == side_stream)))
+    return fail(SPIN_E_SHAPE, "%s: main, side and ema must be different streams", fn);
   int dev = -1;
   SPIN_CHECK(hip_status(hipGetDevice(&dev), fn));
   if (dev != stack->device)
@@ -514,28 +529,42 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
   }
   const int h = (n_layers + 1) / 2;
   const int lo[2] = {0, h}, hi[2] = {h, n_layers};
-  // side: every plan(l) after the previous call's finish(l).  Group A's
-  // finishes were recorded as a group when the split was the same or wider;
-  // otherwise the previous call's last record covers every layer.
+  hipStream_t est = (hipStream_t)ema_stream;
+  // side: every plan(l) after the previous call's update of layer l (its
+  // finish, or with an EMA stream its EMA).  Group A's were recorded as a
+  // group when the split was the same or wider; otherwise the previous
+  // call's last record covers every layer.
+  hipEvent_t* prev_done = est ? stack->ema_done : stack->finish_done;
   for (int g = 0; g < 2; ++g) {
     if (lo[g] == hi[g]) continue;
     const bool a_covers = g == 0 && h <= stack->prev_h;
-    SPIN_CHECK(wait(sst, stack->finish_done[a_covers ? 0 : 1]));
+    SPIN_CHECK(wait(sst, prev_done[a_covers ? 0 : 1]));
     for (int l = lo[g]; l < hi[g]; ++l)
       if (bts[l].batch > 0) SPIN_CHECK(issue_plan(cfgs[l], bts[l], ios[l], sst));
     SPIN_CHECK(record(stack->plan_done[g], sst));
   }
-  // main: each group's finishes after the group's plans
+  // main: each group's finishes after the group's plans; with an EMA stream
+  // the finishes are score + top-K and the group's EMA updates + counter
+  // advances follow there
   for (int g = 0; g < 2; ++g) {
     if (lo[g] == hi[g]) continue;
     SPIN_CHECK(wait(mst, stack->plan_done[g]));
     for (int l = lo[g]; l < hi[g]; ++l)
-      if (bts[l].batch > 0) SPIN_CHECK(issue_finish(cfgs[l], bts[l], ios[l], 0, mst));
+      if (bts[l].batch > 0) SPIN_CHECK(issue_finish(cfgs[l], bts[l], ios[l], est ? 1 : 0, mst));
     SPIN_CHECK(record(stack->finish_done[g], mst));
+    if (est) {
+      SPIN_CHECK(wait(est, stack->finish_done[g]));
+      for (int l = lo[g]; l < hi[g]; ++l)
+        if (bts[l].batch > 0) SPIN_CHECK(issue_ema(cfgs[l], bts[l], ios[l], est));
+      SPIN_CHECK(record(stack->ema_done[g], est));
+    }
   }
-  // with a single group, finish_done[1] (what the next call's group-A plans
+  // with a single group, the [1] records (what the next call's group-A plans
   // may wait for when the split widens) must also cover this call
-  if (lo[1] == hi[1]) SPIN_CHECK(record(stack->finish_done[1], mst));
+  if (lo[1] == hi[1]) {
+    SPIN_CHECK(record(stack->finish_done[1], mst));
+    if (est) SPIN_CHECK(record(stack->ema_done[1], est));
+  }
   stack->prev_h = h;
   return SPIN_OK;
 }

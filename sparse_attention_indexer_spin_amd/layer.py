@@ -110,11 +110,16 @@ class SpinStack:
     first probe every layer runs at the target level."""
 
     def __init__(self, layers, device="cuda", budget_policy=None, probe_period: int = 8,
-                 levels: int = 100):
+                 levels: int = 100, ema_stream: bool = False):
         self.layers = list(layers)
         self.stack = api.Stack(len(self.layers))
-        # default priority (a side stream of another priority is not used)
+        # default priority (streams of another priority are not used)
         self.side = torch.cuda.Stream(device=device)
+        # optionally the EMA updates on a third stream, off the main stream
+        # (see join()).  Off by default: the update is bandwidth-bound like
+        # the score kernel beside it, so running them together slows both;
+        # fused with the latency-bound top-K on the main stream it is free.
+        self.ema = torch.cuda.Stream(device=device) if ema_stream else None
         self._order_next = True
         self.policy = budget_policy
         if budget_policy is not None:
@@ -189,6 +194,25 @@ class SpinStack:
         self.level_history.append((self.t, list(new)))
         self._publish(self.levels_now)
 
+    def join(self, stream=None):
+        """Order `stream` (default: the current one) after everything the stack
+        issued; needed before reading or writing a layer's EMA state or
+        counters there when the EMA runs on its own stream."""
+        st = torch.cuda.current_stream() if stream is None else stream
+        st.wait_stream(self.side)
+        if self.ema is not None:
+            st.wait_stream(self.ema)
+
+    def reset(self):
+        """Reset every layer (EMA state to zero, next step dense), on the
+        current stream after the stack's pending work."""
+        self.join()
+        for lay in self.layers:
+            lay.reset()
+        if self.policy is not None:
+            self.reset_budgets()
+        self.inputs_changed()
+
     def inputs_changed(self):
         """Call after writing a layer's plan inputs on the main stream since
         the last step (set_requests, reset, budgets): the next step's plans
@@ -216,7 +240,7 @@ class SpinStack:
                                    None if n_valid is None else n_valid[l],
                                    None if budgets is None else budgets[l]))
         api.spin_stack_step(self.stack, cfgs, bts, ios, order_after_main=self._order_next,
-                            main_stream=stream, side_stream=self.side)
+                            main_stream=stream, side_stream=self.side, ema_stream=self.ema)
         self._order_next = False
         if probe:
             st = torch.cuda.current_stream() if stream is None else stream

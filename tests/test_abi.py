@@ -130,5 +130,5 @@ def test_stack_host_validation_without_gpu(lib):
     assert lib.spin_stack_create(0, C.byref(h)) == 2 and not h.value
     assert lib.spin_stack_create(257, C.byref(h)) == 2 and not h.value
     assert lib.spin_stack_create(4, None) == 1
-    assert lib.spin_stack_step(None, 1, None, None, None, 0, None, None) == 1
+    assert lib.spin_stack_step(None, 1, None, None, None, 0, None, None, None) == 1
     lib.spin_stack_destroy(None)  # a no-op

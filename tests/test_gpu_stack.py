@@ -35,8 +35,9 @@ def _state(lay):
 
 
 @pytest.mark.parametrize("integer", [False, True])
-def test_stack_matches_sequential_steps(integer):
-    banner(f"stack vs sequential integer={integer}")
+@pytest.mark.parametrize("ema_stream", [True, False])
+def test_stack_matches_sequential_steps(integer, ema_stream):
+    banner(f"stack vs sequential integer={integer} ema_stream={ema_stream}")
     from sparse_attention_indexer_spin_amd import SpinStack, api as A
     n_layers = 3
     w = _workload(n_layers)
@@ -45,7 +46,7 @@ def test_stack_matches_sequential_steps(integer):
     seq = [make_layer(li, 4000) for li in lis]
     stk_layers = [make_layer(li, 4000) for li in lis]
     split = [make_layer(li, 4000) for li in lis]
-    stack = SpinStack(stk_layers)
+    stack = SpinStack(stk_layers, ema_stream=ema_stream)
     torch.cuda.synchronize()
     for s in range(w.steps):
         qs = [li.q[s].to(DEV).contiguous() for li in lis]
@@ -93,15 +94,17 @@ def test_stack_reuse_after_reset_and_fewer_layers():
     for s in range(w.steps):
         qs = [li.q[s].to(DEV).contiguous() for li in lis]
         ws = [li.weights.to(DEV) for li in lis]
-        if s == 3:
-            for lay in seq + stk_layers:
+        if s == 3:                                 # no host sync before the reset
+            for lay in seq:
                 lay.reset()
-            stack.inputs_changed()
+            stack.reset()
         use = n_layers if s != 2 else 2            # step 2 runs layers 0-1 only
         for l in range(use):
             seq[l].step(qs[l], ws[l], *keys[l])
         stack.step(qs, ws, [k[0] for k in keys], [k[1] for k in keys], [k[2] for k in keys],
                    n_layers=use)
+        if s == 2:
+            continue                               # step 3's reset follows without a host sync
         torch.cuda.synchronize()
         for l in range(n_layers):
             for x, y in zip(_state(seq[l]), _state(stk_layers[l])):
