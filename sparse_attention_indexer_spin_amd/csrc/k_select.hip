@@ -62,6 +62,79 @@ __device__ __forceinline__ void predict_wave(int combine, int N, int B, int q, i
   }
 }
 
+// Several verifier rows: one wave computes every row of its 8 blocks from
+// one load of V and D.  Row r needs D[q0 + r - i] = the value row 0 loads
+// for slot i - r, so lane l takes it from lane l - r of the same block's
+// vector, or of the previous block's for l < r (the wave's first block
+// loads the few previous offsets it needs, q0 + 1 .. q0 + rows - 1 at most).
+template <int ROWS>
+__device__ __forceinline__ void predict_wave_rows(int combine, int N, int B, int q0, int j0,
+                                                  const float* __restrict__ Vr,
+                                                  const float* __restrict__ Dr,
+                                                  const float* __restrict__ vmax_r,
+                                                  float* __restrict__ S0, int max_blocks) {
+  const int lane = threadIdx.x & 63;
+  const float vm = vmax_r && lane < kPredBlocksPerWave && j0 + lane < B - 1 ? vmax_r[j0 + lane]
+                                                                             : -INFINITY;
+  float vv[kPredBlocksPerWave], dd[kPredBlocksPerWave];
+  // slot 64 j0 - 64 + lane: only lanes >= 64 - (ROWS - 1) are read by the shifts
+  const int ip = j0 * SPIN_BLOCK - SPIN_BLOCK + lane;
+  const float dprev = lane >= SPIN_BLOCK - (ROWS - 1) && ip < N ? Dr[q0 - ip] : 0.0f;
+#pragma unroll
+  for (int b = 0; b < kPredBlocksPerWave; ++b) {
+    const int i = (j0 + b) * SPIN_BLOCK + lane;
+    const bool ok = i < N;
+    const bool cached = vmax_r && j0 + b < B - 1;
+    vv[b] = ok && !cached ? Vr[i] : -INFINITY;
+    dd[b] = ok ? Dr[q0 - i] : 0.0f;
+  }
+#pragma unroll
+  for (int b = 0; b < kPredBlocksPerWave; ++b) {
+    const int j = j0 + b;
+    const int i = j * SPIN_BLOCK + lane;
+    const float before = b == 0 ? dprev : dd[b > 0 ? b - 1 : 0];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      float d = dd[b];
+      if (r > 0) {
+        const int src = (lane - r) & 63;
+        const float x = __shfl(dd[b], src), y = __shfl(before, src);
+        d = lane >= r ? x : y;
+      }
+      float zhat = combine == SPIN_COMBINE_SUM ? __fadd_rn(vv[b], d) : fmaxf(vv[b], d);
+      zhat = i < N ? zhat : -INFINITY;
+      const float m = fmaxf(wave_max_f32(zhat),
+                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vm), b)));
+      if (lane == 0 && j < B) S0[(int64_t)r * max_blocks + j] = m + 0.0f;
+    }
+  }
+}
+
+template <int ROWS>
+__global__ __launch_bounds__(256) void k_predict_rows(int combine, int max_blocks,
+                                                      const int32_t* __restrict__ ctx,
+                                                      const int32_t* __restrict__ qpos,
+                                                      const float* __restrict__ V, int64_t v_ld,
+                                                      const float* __restrict__ D, int64_t d_ld,
+                                                      const float* __restrict__ vmax,
+                                                      float* __restrict__ S, int32_t* err,
+                                                      int32_t* __restrict__ qpos_snap) {
+  const int r = blockIdx.z;
+  const int N = ctx[r], q0 = qpos[r];
+  if (qpos_snap && blockIdx.x == 0 && threadIdx.x == 0) qpos_snap[r] = q0;
+  const int e = request_error(N, q0, ROWS, max_blocks, v_ld, d_ld);
+  if (e) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) raise_error(err, e);
+    return;
+  }
+  const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  const int j0 = (blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * kPredBlocksPerWave;
+  if (j0 >= B) return;
+  predict_wave_rows<ROWS>(combine, N, B, q0, j0, V + (int64_t)r * v_ld, D + (int64_t)r * d_ld,
+                          vmax ? vmax + (int64_t)r * max_blocks : nullptr,
+                          S + (int64_t)r * ROWS * max_blocks, max_blocks);
+}
+
 __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_blocks,
                                                  const int32_t* __restrict__ ctx,
                                                  const int32_t* __restrict__ qpos,
@@ -260,9 +333,27 @@ __global__ void k_zero_i32(int32_t* __restrict__ p, int n) {
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+template <int ROWS>
+static void predict_rows_t(const spin_config& c, const spin_batch& b, const float* V,
+                           int64_t v_ld, const float* D, int64_t d_ld, const float* vmax,
+                           float* S, hipStream_t st, int32_t* qpos_snap) {
+  dim3 grid((b.max_blocks + 4 * kPredBlocksPerWave - 1) / (4 * kPredBlocksPerWave), 1, b.batch);
+  hipLaunchKernelGGL(k_predict_rows<ROWS>, grid, dim3(256), 0, st, c.combine, b.max_blocks,
+                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld,
+                     c.combine == SPIN_COMBINE_MAX ? vmax : nullptr, S, b.err, qpos_snap);
+}
+
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
                           const float* D, int64_t d_ld, const float* vmax, float* S,
                           hipStream_t st, int32_t* qpos_snap) {
+  if (b.n_rows > 1) {  // every row from one load of V and D
+    switch (b.n_rows) {
+      case 2: predict_rows_t<2>(c, b, V, v_ld, D, d_ld, vmax, S, st, qpos_snap); break;
+      case 3: predict_rows_t<3>(c, b, V, v_ld, D, d_ld, vmax, S, st, qpos_snap); break;
+      default: predict_rows_t<4>(c, b, V, v_ld, D, d_ld, vmax, S, st, qpos_snap); break;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((b.max_blocks + 4 * kPredBlocksPerWave - 1) / (4 * kPredBlocksPerWave), b.n_rows,
             b.batch);
   hipLaunchKernelGGL(k_predict, grid, dim3(256), 0, st, c.combine, b.n_rows, b.max_blocks,

@@ -50,7 +50,7 @@ def _batch(ctx, qpos, step, rows, max_blocks, n_pages=1, req=None):
 # ---------------------------------------------------------------------------
 # stage 1: predict
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("rows", [1, 4])
+@pytest.mark.parametrize("rows", [1, 2, 3, 4])
 @pytest.mark.parametrize("combine", ["max", "sum"])
 def test_predict_parity(rows, combine):
     banner(f"predict rows={rows} combine={combine}")
@@ -85,7 +85,7 @@ def _signed_state(ctx, mb, d_cap, seed):
     return V, D, vmax
 
 
-@pytest.mark.parametrize("rows", [1, 4])
+@pytest.mark.parametrize("rows", [1, 2, 3, 4])
 @pytest.mark.parametrize("combine", ["max", "sum"])
 def test_predict_parity_vmax(rows, combine):
     """With the V block maxima (max combine: one float per block instead of 64
