@@ -27,6 +27,7 @@ on whole requests of the same workload for about 15 s.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -73,6 +74,8 @@ def parse():
                          "--probe-period steps (the multi-layer workload states the "
                          "proportional rule), timed beside the uniform runs")
     ap.add_argument("--probe-period", type=int, default=8)
+    ap.add_argument("--stack-layers", type=int, default=8,
+                    help="--stack on a one-layer workload: that many independent layers of it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 1 GiB device-to-device copies (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -233,7 +236,8 @@ class StackInputs:
 
 
 def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict=None,
-              policy: str = "none", probe_period: int = 8):
+              policy: str = "none", probe_period: int = 8,
+              modes=("seq", "stack", "ema_stream")):
     """Whole decode steps of every layer: (a) one spin_step per layer in layer
     order on the current stream, (b) one spin_stack_step (plans on a side
     stream).  Each mode on its own layer states from the same reset; each timed
@@ -278,13 +282,15 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in ev) / steps
 
-    seq = layers()
+    seq, ms_seq = None, None
+    if "seq" in modes:
+        seq = layers()
 
-    def seq_step(s):
-        for l, lay in enumerate(seq):
-            lay.step(inp.q[l][s], inp.weights[l], pages[l], scales[l], pts[l])
+        def seq_step(s):
+            for l, lay in enumerate(seq):
+                lay.step(inp.q[l][s], inp.weights[l], pages[l], scales[l], pts[l])
 
-    ms_seq = timed(seq_step)
+        ms_seq = timed(seq_step)
     def run_stack_mode(ema_stream):
         lays = layers()
         stack = SpinStack(lays, ema_stream=ema_stream)
@@ -301,7 +307,8 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
         return ms, lays
 
     ms_stack, stk_layers = run_stack_mode(False)
-    ms_stack_ema_stream, lays_ema_stream = run_stack_mode(True)
+    ms_stack_ema_stream, lays_ema_stream = (run_stack_mode(True) if "ema_stream" in modes
+                                            else (None, None))
     budget = None
     if policy != "none":
         # the same schedule with per-layer budgets and dense probe steps; the
@@ -341,11 +348,15 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
                   "allocated_at_steps": [h[0] for h in bstack.level_history]}
         for lay in bud_layers:
             assert int(lay.err.item()) == 0
-    for a, b, c in zip(seq, stk_layers, lays_ema_stream):
-        assert torch.equal(a.topk_idx, b.topk_idx) and torch.equal(a.V, b.V) and \
-            torch.equal(a.topk_idx, c.topk_idx) and torch.equal(a.V, c.V), \
-            "stack and sequential steps disagree"
-        assert int(a.err.item()) == 0 and int(b.err.item()) == 0 and int(c.err.item()) == 0
+    for other in (seq, lays_ema_stream):
+        if other is None:
+            continue
+        for a, b in zip(other, stk_layers):
+            assert torch.equal(a.topk_idx, b.topk_idx) and torch.equal(a.V, b.V), \
+                "stack and sequential steps disagree"
+            assert int(a.err.item()) == 0
+    for b in stk_layers:
+        assert int(b.err.item()) == 0
     keys = 0
     ctx = inp.ctx.numpy().astype(np.int64)
     n_sel = 0
@@ -641,13 +652,42 @@ def main():
     print(json.dumps(out))
 
 
+def stack_sweep(inp: StackInputs, steps: int, warmup: int, evict=None):
+    """Per-layer step time over the workload's sparsity sweep, one spin_step per
+    layer on one stream and with the stack schedule, with the fit
+    t = a (1 - rho) + c of each."""
+    w = inp.w
+    out = {"us_per_step_layer": {}, "realized_sparsity": {}}
+    rho, t_seq, t_stk = [], [], []
+    for sp in sorted(set(w.sparsity_bp)):
+        res = run_stack(inp, sp, steps, warmup, evict, modes=("seq", "stack"))
+        total_blocks = w.layers * int(sum(-(-int(c) // 64) for c in inp.ctx))
+        r = 1.0 - res["n_sel"] / total_blocks
+        rho.append(r)
+        t_seq.append(res["ms_seq"] * 1e3 / w.layers)
+        t_stk.append(res["ms_stack"] * 1e3 / w.layers)
+        out["us_per_step_layer"][str(sp)] = {"sequential": t_seq[-1], "stack": t_stk[-1]}
+        out["realized_sparsity"][str(sp)] = r
+    A = np.stack([1.0 - np.array(rho), np.ones(len(rho))], 1)
+    for name, T in (("sequential", t_seq), ("stack", t_stk)):
+        (a, c), *_ = np.linalg.lstsq(A, np.array(T), rcond=None)
+        out[f"fit_{name}_us"] = {"a": float(a), "c": float(c)}
+    return out
+
+
 def main_stack(args, w: G.Workload, sp: int):
     """The multi-layer bench line: whole decode steps of every layer."""
-    if w.layers < 2 or w.key_dtype != "fp8" or w.rows != 1:
-        print(json.dumps({"error": "--stack needs a multi-layer fp8 workload with one row"}))
+    if w.layers < 2:
+        w = dataclasses.replace(w, layers=args.stack_layers, name=f"{w.name}_x{args.stack_layers}")
+    if w.key_dtype != "fp8" or w.rows != 1:
+        print(json.dumps({"error": "--stack needs an fp8 workload with one row"}))
         sys.exit(2)
     inp = StackInputs(w, args.steps + args.warmup)
     evict = Evictor() if args.cache == "cold" else None
+    if args.sweep and len(w.sparsity_bp) > 1:
+        sw = stack_sweep(inp, min(args.steps, 20), args.warmup, evict)
+        print(json.dumps({"workload": w.name, "cache": args.cache, "stack_sweep": sw}))
+        return
     res = run_stack(inp, sp, args.steps, args.warmup, evict, args.budget_policy,
                     args.probe_period)
     score_bytes = algorithmic_score_bytes(w, res["keys_layer0"], res["n_sel_layer0"])

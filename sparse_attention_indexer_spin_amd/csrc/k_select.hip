@@ -179,7 +179,7 @@ struct SelectArgs {
 };
 
 struct SelectLds {
-  int hist[512];
+  int hist[kRadixHist];
   int sh[32];
   uint32_t tmpu[32];
 };

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(
     int32_t* __restrict__ out, TopkWs ws) {
   __shared__ uint32_t lkey[kCap];
   __shared__ int off[kSelThreads / 4 + 1];
-  __shared__ int hist[512];
+  __shared__ int hist[kRadixHist];
   __shared__ int sh[32];
   __shared__ uint32_t tmpu[32];
   const int rowid = blockIdx.x, r = rowid / rows;
@@ -345,7 +345,7 @@ struct PagesShared {
   uint32_t lkey[kCap];
   int32_t lslot[kCap];
   int32_t lsrc[kCap];  // first candidate of each selected block (boff)
-  int hist[512];
+  int hist[kRadixHist];
   int sh[32];
   uint32_t tmpu[32];
 };

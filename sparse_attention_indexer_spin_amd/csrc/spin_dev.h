@@ -205,12 +205,41 @@ constexpr int kSelThreads = 1024;
 // (ties: lower element index).  Thread t of NT owns elements t*EPT ..
 // t*EPT+EPT-1 (EPT <= 32).
 // On return, bit e of the result mask marks the chosen elements.
+//
+// Each 8-bit radix pass costs one barrier: every wave reads the pass's
+// histogram and picks the digit itself, and three histograms rotate -- pass
+// i fills H[i % 3] and clears H[(i + 1) % 3], whose last readers (the picks
+// of pass i - 2) finished before the previous barrier and whose next writers
+// (pass i + 1) start after this pass's barrier.  When the last pass takes
+// every key of its bin, the keys at or above the threshold are exactly the
+// k largest and no rank among equal keys is needed.
 // ---------------------------------------------------------------------------
+constexpr int kRadixHist = 3 * 256;  // ints of LDS block_select_top needs for `hist`
+
+// The largest digit d with (keys in bins >= d) >= k, in every lane of the
+// calling wave: {d, k - keys in bins above d, keys in bin d}.
+__device__ __forceinline__ int3 radix_pick_digit_wave(const int* h, int k) {
+  const int lane = threadIdx.x & 63;
+  const int4 cb = reinterpret_cast<const int4*>(h)[lane];
+  const int cs[4] = {cb.x, cb.y, cb.z, cb.w};
+  const int incl = wave_incl_scan(cb.x + cb.y + cb.z + cb.w);
+  int above = __builtin_amdgcn_readlane(incl, 63) - incl;  // keys in the higher lanes' bins
+  int d = 0, kk = 0, cnt = 0;
+  bool found = false;
+#pragma unroll
+  for (int b = 3; b >= 0; --b) {
+    if (above < k && above + cs[b] >= k) { d = 4 * lane + b; kk = k - above; cnt = cs[b]; found = true; }
+    above += cs[b];
+  }
+  const int src = __builtin_ctzll(__ballot(found));
+  return make_int3(__builtin_amdgcn_readlane(d, src), __builtin_amdgcn_readlane(kk, src),
+                   __builtin_amdgcn_readlane(cnt, src));
+}
 
 template <int EPT, int NT = kSelThreads>
 __device__ uint32_t block_select_top(const uint32_t (&key)[EPT], uint32_t elig, int k,
                                      int* hist, int* sh, uint32_t* tmpu) {
-  // hist: 512 ints (two histograms used in turn), sh: 32 ints, tmpu: 2 NT/64
+  // hist: kRadixHist ints, sh: 32 ints, tmpu: 2 NT/64
   if (k <= 0) return 0u;
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -218,46 +247,51 @@ __device__ uint32_t block_select_top(const uint32_t (&key)[EPT], uint32_t elig, 
 #pragma unroll
   for (int e = 0; e < EPT; ++e)
     if (elig >> e & 1u) { mx = max(mx, key[e]); mn = min(mn, key[e]); }
-  // max and min in one exchange; both histograms cleared under the same barrier
+  // max and min in one exchange; the first histogram cleared under the same barrier
   mx = wave_max_u32(mx);
   mn = wave_min_u32(mn);
   if (lane == 0) { tmpu[wid] = mx; tmpu[NW + wid] = mn; }
-  for (int i = threadIdx.x; i < 512; i += NT) hist[i] = 0;
+  for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < NW; ++i) { mx = max(mx, tmpu[i]); mn = min(mn, tmpu[NW + i]); }
   int nb = (mx == mn) ? 0 : 32 - __clz(mx ^ mn);
   uint64_t prefix = ((uint64_t)mx >> nb) << nb;
   int cur = 0;
+  bool whole_bin = false;
   while (nb > 0) {
     const int db = nb < 8 ? nb : 8, pos = nb - db;
     int* h = hist + 256 * cur;
+    int* hn = hist + 256 * (cur == 2 ? 0 : cur + 1);
+    for (int i = threadIdx.x; i < 256; i += NT) hn[i] = 0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e)
       if ((elig >> e & 1u) && ((uint64_t)key[e] >> nb) == (prefix >> nb))
         atomicAdd(&h[(key[e] >> pos) & ((1u << db) - 1u)], 1);
     __syncthreads();
-    // wave 0 picks the digit while the others clear the other histogram (its
-    // last reader was the previous pass's pick, before the previous barrier)
-    if (threadIdx.x < 64) radix_pick_digit(h, k, sh + 24 + 4 * cur);
-    else
-      for (int i = threadIdx.x - 64; i < 256; i += NT - 64) hist[256 * (cur ^ 1) + i] = 0;
-    __syncthreads();
-    const int d = sh[24 + 4 * cur], cnt = sh[26 + 4 * cur];
-    k = sh[25 + 4 * cur];
-    prefix |= (uint64_t)d << pos;
+    const int3 pick = radix_pick_digit_wave(h, k);
+    k = pick.y;
+    prefix |= (uint64_t)pick.x << pos;
     nb = pos;
-    cur ^= 1;
-    if (cnt == k) break;  // every key of this bin is taken
+    cur = cur == 2 ? 0 : cur + 1;
+    if (pick.z == k) { whole_bin = true; break; }  // every key of this bin is taken
   }
   const uint64_t hp = prefix >> nb;
+  uint32_t out = 0u;
+  if (whole_bin) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if ((elig >> e & 1u) && ((uint64_t)key[e] >> nb) >= hp) out |= 1u << e;
+    // the next call clears histograms this call's slowest wave may still read
+    __syncthreads();
+    return out;
+  }
   int eq = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e)
     if ((elig >> e & 1u) && ((uint64_t)key[e] >> nb) == hp) ++eq;
   int tot;
   int rank = block_excl_scan<NT>(eq, sh + 4, &tot);
-  uint32_t out = 0u;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     if (!(elig >> e & 1u)) continue;
