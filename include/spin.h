@@ -70,6 +70,32 @@ enum { SPIN_DERR_CTX = 1,   /* ctx_len < 1, > 64*max_blocks or > v_ld        */
 #define SPIN_MAX_TOPK 8192
 #define SPIN_MAX_LAYERS 256  /* layers of one spin_stack */
 
+/*
+ * spin_config.flags: the design choices the paper ablates, as variants; 0
+ * selects the paper's defaults throughout.
+ *  - Block pooling of the predicted slot scores (Sec. 4.6, "Block reduction",
+ *    variant A1), bits 0-1: SPIN_POOL_MAX (default): the largest; SPIN_POOL_TOP4:
+ *    the mean of the up to four largest, summed largest first, divided by
+ *    their count; SPIN_POOL_MEAN: the mean over the block's valid slots, the
+ *    64 slot values (0 past the context) summed as a balanced pairwise tree
+ *    ((s0 + s1) + (s2 + s3)) + ... in fp32, divided by the valid count.  The
+ *    V block maxima (v_max) apply to SPIN_POOL_MAX only and are ignored
+ *    otherwise.
+ *  - SPIN_MTP_ROW0_MASK (Sec. 4.5, "Offline policy ablation", row-0 sharing):
+ *    the scored union is row 0's mask alone, not the union of every row's.
+ *  - SPIN_MTP_ROW0_UPDATE (same passage, row-0 update): the EMA takes row 0's
+ *    scores only, whatever the acceptance outcome, instead of replaying the
+ *    prefix-valid rows; q positions still advance by the accepted rows.
+ *  - SPIN_EXPLORE_PER_ROW: each verifier row draws its own exploration
+ *    priorities, with counter (j, step, layer + 65536 row, req_id) (layer
+ *    < 65536), instead of sharing row 0's.
+ */
+enum {
+  SPIN_POOL_MAX = 0, SPIN_POOL_TOP4 = 1, SPIN_POOL_MEAN = 2, SPIN_POOL_MASK = 3,
+  SPIN_MTP_ROW0_MASK = 4, SPIN_MTP_ROW0_UPDATE = 8, SPIN_EXPLORE_PER_ROW = 16,
+  SPIN_FLAGS_ALL = 31
+};
+
 /* Method parameters, passed by host pointer and copied by value. */
 typedef struct spin_config {
   int32_t n_heads;      /* indexer heads n_h; this build: 64                       */
@@ -83,7 +109,7 @@ typedef struct spin_config {
   int32_t key_dtype;    /* SPIN_F32 | SPIN_BF16 | SPIN_FP8_E4M3                    */
   int32_t q_dtype;      /* SPIN_F32 | SPIN_BF16                                    */
   int32_t layer;        /* layer id, part of the Philox counter                    */
-  int32_t reserved;     /* must be 0                                               */
+  int32_t flags;        /* SPIN_POOL_* | SPIN_MTP_* | SPIN_EXPLORE_*; 0 = defaults  */
   uint64_t seed;        /* Philox4x32-10 key (lo, hi words)                        */
 } spin_config;
 

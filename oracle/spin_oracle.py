@@ -134,11 +134,41 @@ def n_blocks(n_slots: int, b: int = BLOCK) -> int:
     return -(-int(n_slots) // b)
 
 
-def predict_block_scores(V, D, n_slots: int, q: int, combine: str = "max", b: int = BLOCK):
-    """S[j] = max_{jb <= i < min((j+1)b, N)} C(V[i], D[q - i]).
+def pool_block(vals, pooling: str = "max"):
+    """Pool one block's predicted slot scores (fp32, the valid slots in slot
+    order) into its block score (paper Sec. 4.6, "Block reduction", A1):
+      max  -- the largest (Eq. 2, the default);
+      top4 -- the up to four largest, summed largest first in fp32, divided
+              by their count;
+      mean -- the 64 slot values (0 past the context) summed as a balanced
+              pairwise tree in fp32, ((s0 + s1) + (s2 + s3)) + ..., divided by
+              the number of valid slots."""
+    vals = np.asarray(vals, dtype=np.float32)
+    n = len(vals)
+    if pooling == "max":
+        return np.float32(vals.max())
+    if pooling == "top4":
+        top = np.sort(vals)[::-1][:min(4, n)]
+        s = np.float32(top[0])
+        for x in top[1:]:
+            s = np.float32(s + x)
+        return np.float32(s / np.float32(len(top)))
+    if pooling == "mean":
+        v = np.zeros(BLOCK, dtype=np.float32)
+        v[:n] = vals
+        while len(v) > 1:
+            v = (v[0::2] + v[1::2]).astype(np.float32)
+        return np.float32(v[0] / np.float32(n))
+    raise ValueError(pooling)
+
+
+def predict_block_scores(V, D, n_slots: int, q: int, combine: str = "max", b: int = BLOCK,
+                         pooling: str = "max"):
+    """S[j] = pool over jb <= i < min((j+1)b, N) of C(V[i], D[q - i]).
 
     V: fp32 [>= N]; D: fp32 [> q]; q: the query position of this row.
-    C = max (Eq. 1) or an fp32 sum.  Returns fp32 [B].
+    C = max (Eq. 1) or an fp32 sum; pool = max (Eq. 2) or a variant of
+    pool_block.  Returns fp32 [B].
     """
     N = int(n_slots)
     i = np.arange(N)
@@ -153,7 +183,7 @@ def predict_block_scores(V, D, n_slots: int, q: int, combine: str = "max", b: in
     B = n_blocks(N, b)
     S = np.empty(B, dtype=np.float32)
     for j in range(B):
-        S[j] = zhat[j * b:min((j + 1) * b, N)].max()
+        S[j] = pool_block(zhat[j * b:min((j + 1) * b, N)], pooling)
     return canon32(S)
 
 
@@ -309,30 +339,38 @@ class RequestState:
 def spin_step(state: RequestState, *, q, q_dtype, w, pages, page_table_row, key_dtype,
               scale, n_slots: int, q_pos: int, K: int, sparsity_bp: int, explore_bp: int,
               alpha: float, layer: int, req_id: int, seed: int, combine: str = "max",
-              n_valid=None, budget=None, defer=False):
+              n_valid=None, budget=None, defer=False, pooling: str = "max",
+              mtp_row0_mask: bool = False, mtp_row0_update: bool = False,
+              explore_per_row: bool = False):
     """One SPIN decode step for one request: predict, select, union, score, top-K, EMA.
 
     q: [rows, n_h, d] (raw f32 or bf16 codes), w: [rows, n_h].
     Returns a dict with codes [rows, B], sel, slots, z64 [rows, n], z32, topk [rows, K].
     The EMA update uses rows 0..n_valid-1 (all rows when n_valid is None) unless
     defer=True, in which case the caller replays later with ema_update.
+    Variants (the paper's ablations, Sec. 4.5 and 4.6; defaults = the method):
+    `pooling` (pool_block); mtp_row0_mask: score row 0's mask alone (row-0
+    sharing); mtp_row0_update: the EMA takes row 0 only (row-0 update);
+    explore_per_row: row r's exploration priorities come from the counter
+    (j, t, layer + 65536 r, req_id).
     """
     rows = q.shape[0]
     qd = decode_q(q, q_dtype)
     codes = []
     for r in range(rows):
-        S = predict_block_scores(state.V, state.D, n_slots, q_pos + r, combine)
-        codes.append(select_blocks(S, n_slots, K, sparsity_bp, explore_bp, state.t, layer,
+        S = predict_block_scores(state.V, state.D, n_slots, q_pos + r, combine, pooling=pooling)
+        lay = layer + 65536 * r if explore_per_row else layer
+        codes.append(select_blocks(S, n_slots, K, sparsity_bp, explore_bp, state.t, lay,
                                    req_id, seed, budget))
     codes = np.stack(codes)
-    sel = union_blocks(codes)
+    sel = union_blocks(codes[:1] if mtp_row0_mask else codes)
     slots = union_slots(sel, n_slots)
     keys = gather_keys(pages, page_table_row, slots, key_dtype, scale)
     z64 = np.stack([index_scores(qd[r], w[r], keys) for r in range(rows)])
     z32 = canon32(z64)
     top = np.stack([topk_slots(z32[r], slots, K) for r in range(rows)])
     if not defer:
-        ema_update(state.V, state.D, z32, slots, q_pos, rows if n_valid is None else n_valid,
-                   alpha)
+        ema_update(state.V, state.D, z32, slots, q_pos,
+                   1 if mtp_row0_update else (rows if n_valid is None else n_valid), alpha)
         state.t += 1
     return dict(codes=codes, sel=sel, slots=slots, z64=z64, z32=z32, topk=top)

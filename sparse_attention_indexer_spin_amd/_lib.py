@@ -26,13 +26,15 @@ EXPORTS = ["spin_predict_blocks", "spin_select_blocks", "spin_sparse_index_score
            "spin_stack_create", "spin_stack_destroy", "spin_stack_step", "spin_miss_curve",
            "spin_budget_fill", "spin_budget_allocate"]
 SPIN_BUDGET_MINIMAX, SPIN_BUDGET_PROPORTIONAL = 0, 1
+SPIN_POOL_MAX, SPIN_POOL_TOP4, SPIN_POOL_MEAN = 0, 1, 2
+SPIN_MTP_ROW0_MASK, SPIN_MTP_ROW0_UPDATE, SPIN_EXPLORE_PER_ROW = 4, 8, 16
 
 
 class SpinConfig(C.Structure):
     _fields_ = [("n_heads", C.c_int32), ("head_dim", C.c_int32), ("block_size", C.c_int32),
                 ("topk", C.c_int32), ("sparsity_bp", C.c_int32), ("explore_bp", C.c_int32),
                 ("ema_alpha", C.c_float), ("combine", C.c_int32), ("key_dtype", C.c_int32),
-                ("q_dtype", C.c_int32), ("layer", C.c_int32), ("reserved", C.c_int32),
+                ("q_dtype", C.c_int32), ("layer", C.c_int32), ("flags", C.c_int32),
                 ("seed", C.c_uint64)]
 
 

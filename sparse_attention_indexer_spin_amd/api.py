@@ -34,14 +34,23 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+_POOL = {"max": L.SPIN_POOL_MAX, "top4": L.SPIN_POOL_TOP4, "mean": L.SPIN_POOL_MEAN}
+
+
 def config(*, topk: int, sparsity_bp: int, explore_bp: int = 500, ema_alpha: float = 0.9,
            combine: str = "max", key_dtype: torch.dtype = torch.uint8,
            q_dtype: torch.dtype = torch.bfloat16, layer: int = 0, seed: int = 0x5350494E,
-           n_heads: int = 64, head_dim: int = 128, block_size: int = 64) -> L.SpinConfig:
+           n_heads: int = 64, head_dim: int = 128, block_size: int = 64, pooling: str = "max",
+           mtp_row0_mask: bool = False, mtp_row0_update: bool = False,
+           explore_per_row: bool = False) -> L.SpinConfig:
+    """spin_config; the keyword variants map to spin_config.flags (defaults: the paper's)."""
+    flags = (_POOL[pooling] | (L.SPIN_MTP_ROW0_MASK if mtp_row0_mask else 0)
+             | (L.SPIN_MTP_ROW0_UPDATE if mtp_row0_update else 0)
+             | (L.SPIN_EXPLORE_PER_ROW if explore_per_row else 0))
     return L.SpinConfig(n_heads=n_heads, head_dim=head_dim, block_size=block_size, topk=topk,
                         sparsity_bp=sparsity_bp, explore_bp=explore_bp, ema_alpha=ema_alpha,
                         combine=L.SPIN_COMBINE_SUM if combine == "sum" else L.SPIN_COMBINE_MAX,
-                        key_dtype=_KEY[key_dtype], q_dtype=_Q[q_dtype], layer=layer, reserved=0,
+                        key_dtype=_KEY[key_dtype], q_dtype=_Q[q_dtype], layer=layer, flags=flags,
                         seed=seed)
 
 

@@ -51,7 +51,10 @@ spin_status check_config(const char* fn, const spin_config* c) {
   if (c->key_dtype < SPIN_F32 || c->key_dtype > SPIN_FP8_E4M3 || c->q_dtype < SPIN_F32 ||
       c->q_dtype > SPIN_BF16)
     return fail(SPIN_E_UNSUPPORTED, "%s: unknown dtype", fn);
-  if (c->reserved != 0) return fail(SPIN_E_SHAPE, "%s: reserved must be 0", fn);
+  if ((c->flags & ~SPIN_FLAGS_ALL) != 0 || (c->flags & SPIN_POOL_MASK) == SPIN_POOL_MASK)
+    return fail(SPIN_E_SHAPE, "%s: unknown flags 0x%x", fn, c->flags);
+  if ((c->flags & SPIN_EXPLORE_PER_ROW) && (c->layer < 0 || c->layer >= 65536))
+    return fail(SPIN_E_SHAPE, "%s: per-row exploration needs 0 <= layer < 65536", fn);
   return SPIN_OK;
 }
 

@@ -17,11 +17,14 @@ class SpinLayer:
     def __init__(self, *, batch: int, max_blocks: int, d_cap: int, topk: int, sparsity_bp: int,
                  n_rows: int = 1, explore_bp: int = 500, ema_alpha: float = 0.9,
                  combine: str = "max", key_dtype=torch.uint8, q_dtype=torch.bfloat16,
-                 layer: int = 0, seed: int = 0x5350494E, device="cuda", vmax_cache: bool = False):
+                 layer: int = 0, seed: int = 0x5350494E, device="cuda", vmax_cache: bool = False,
+                 **variants):
+        """`variants`: the design variants of api.config (pooling, mtp_row0_mask,
+        mtp_row0_update, explore_per_row); the paper's defaults without them."""
         self.R, self.rows, self.max_blocks, self.K = batch, n_rows, max_blocks, topk
         self.cfg = api.config(topk=topk, sparsity_bp=sparsity_bp, explore_bp=explore_bp,
                               ema_alpha=ema_alpha, combine=combine, key_dtype=key_dtype,
-                              q_dtype=q_dtype, layer=layer, seed=seed)
+                              q_dtype=q_dtype, layer=layer, seed=seed, **variants)
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         n_cap = 64 * max_blocks
