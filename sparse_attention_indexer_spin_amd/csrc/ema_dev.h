@@ -58,6 +58,7 @@ struct EmaArgs {
   int32_t* qpos_out;        // optional counter advance
   int32_t* step_out;
   float* vmax;              // optional V block maxima [R][max_blocks]
+  int row0_only;            // SPIN_MTP_ROW0_UPDATE: the EMA takes row 0 alone
 };
 
 // After block j's V update: its max over all 64 slots (slots >= N hold 0),
@@ -91,7 +92,7 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
   const int ns = clamp_nsel(n_sel[r], max_blocks);
   k1 = min(k1, ns);
   if (k0 >= k1) return;
-  int L = n_valid ? n_valid[r] : rows;
+  int L = A.row0_only ? 1 : (n_valid ? n_valid[r] : rows);
   L = L < 0 ? 0 : (L > rows ? rows : L);
   if (L == 0) return;
   const int32_t* sr = sel + (int64_t)r * max_blocks;

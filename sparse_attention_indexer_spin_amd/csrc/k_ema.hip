@@ -32,7 +32,8 @@ hipError_t launch_ema(const spin_config& c, const spin_batch& b, const float* z,
                       const int32_t* qpos_snap, int32_t* qpos_out, int32_t* step_out) {
   dim3 grid((b.max_blocks + 4 * kEmaBlocksPerWave - 1) / (4 * kEmaBlocksPerWave), b.batch);
   const EmaArgs A{c.ema_alpha, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap ? qpos_snap : b.q_pos,
-                  n_valid, z, z_ld, sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out, vmax};
+                  n_valid, z, z_ld, sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out, vmax,
+                  (c.flags & SPIN_MTP_ROW0_UPDATE) != 0};
   hipLaunchKernelGGL(k_ema, grid, dim3(256), 0, st, A);
   return hipGetLastError();
 }

@@ -30,9 +30,36 @@ __device__ __forceinline__ uint32_t explore_key(int j, int t, int layer, int req
 
 constexpr int kPredBlocksPerWave = 8;
 
+// Pool block j's predicted slot scores, one per lane (`valid`: the slot lies
+// in the context, n_valid of them), per spin_config.flags: the max (Eq. 2),
+// the mean of the up to four largest (largest first), or the mean over the
+// valid slots with the 64 values (0 past the context) summed as a balanced
+// pairwise tree -- the xor butterfly below adds lane pairs, then pairs of
+// pairs, in exactly that order, and fp32 addition is commutative.
+__device__ __forceinline__ float pool_block_wave(float zhat, bool valid, int n_valid,
+                                                 int pooling) {
+  if (pooling == SPIN_POOL_MEAN) {
+    float v = valid ? zhat : 0.0f;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v = v + __shfl_xor(v, m);
+    return v / (float)n_valid;
+  }
+  float v = valid ? zhat : -INFINITY;
+  if (pooling != SPIN_POOL_TOP4) return wave_max_f32(v);
+  const int cnt = min(4, n_valid);
+  float s = 0.0f;
+  for (int it = 0; it < cnt; ++it) {
+    const float m = wave_max_f32(v);
+    s = it == 0 ? m : s + m;
+    const uint64_t at = __ballot(v == m);  // one lane holding the max leaves the set
+    if ((int)(threadIdx.x & 63) == __builtin_ctzll(at)) v = -INFINITY;
+  }
+  return s / (float)cnt;
+}
+
 // One wave's 8 blocks j0 .. j0+7 (j0 < B) of one (request, row).
-__device__ __forceinline__ void predict_wave(int combine, int N, int B, int q, int j0,
-                                             const float* __restrict__ Vr,
+__device__ __forceinline__ void predict_wave(int combine, int pooling, int N, int B, int q,
+                                             int j0, const float* __restrict__ Vr,
                                              const float* __restrict__ Dr,
                                              const float* __restrict__ vmax_r,
                                              float* __restrict__ Srow) {
@@ -54,10 +81,13 @@ __device__ __forceinline__ void predict_wave(int combine, int N, int B, int q, i
   for (int b = 0; b < kPredBlocksPerWave; ++b) {
     const int j = j0 + b;
     const int i = j * SPIN_BLOCK + lane;
-    float zhat = combine == SPIN_COMBINE_SUM ? __fadd_rn(vv[b], dd[b]) : fmaxf(vv[b], dd[b]);
-    zhat = i < N ? zhat : -INFINITY;
+    const float zhat =
+        combine == SPIN_COMBINE_SUM ? __fadd_rn(vv[b], dd[b]) : fmaxf(vv[b], dd[b]);
     const float m =
-        fmaxf(wave_max_f32(zhat), __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vm), b)));
+        pooling == SPIN_POOL_MAX
+            ? fmaxf(wave_max_f32(i < N ? zhat : -INFINITY),
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vm), b)))
+            : pool_block_wave(zhat, i < N, min(SPIN_BLOCK, N - j * SPIN_BLOCK), pooling);
     if (lane == 0 && j < B) Srow[j] = m + 0.0f;
   }
 }
@@ -68,7 +98,8 @@ __device__ __forceinline__ void predict_wave(int combine, int N, int B, int q, i
 // vector, or of the previous block's for l < r (the wave's first block
 // loads the few previous offsets it needs, q0 + 1 .. q0 + rows - 1 at most).
 template <int ROWS>
-__device__ __forceinline__ void predict_wave_rows(int combine, int N, int B, int q0, int j0,
+__device__ __forceinline__ void predict_wave_rows(int combine, int pooling, int N, int B, int q0,
+                                                  int j0,
                                                   const float* __restrict__ Vr,
                                                   const float* __restrict__ Dr,
                                                   const float* __restrict__ vmax_r,
@@ -101,17 +132,19 @@ __device__ __forceinline__ void predict_wave_rows(int combine, int N, int B, int
         const float x = __shfl(dd[b], src), y = __shfl(before, src);
         d = lane >= r ? x : y;
       }
-      float zhat = combine == SPIN_COMBINE_SUM ? __fadd_rn(vv[b], d) : fmaxf(vv[b], d);
-      zhat = i < N ? zhat : -INFINITY;
-      const float m = fmaxf(wave_max_f32(zhat),
-                            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vm), b)));
+      const float zhat = combine == SPIN_COMBINE_SUM ? __fadd_rn(vv[b], d) : fmaxf(vv[b], d);
+      const float m =
+          pooling == SPIN_POOL_MAX
+              ? fmaxf(wave_max_f32(i < N ? zhat : -INFINITY),
+                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vm), b)))
+              : pool_block_wave(zhat, i < N, min(SPIN_BLOCK, N - j * SPIN_BLOCK), pooling);
       if (lane == 0 && j < B) S0[(int64_t)r * max_blocks + j] = m + 0.0f;
     }
   }
 }
 
 template <int ROWS>
-__global__ __launch_bounds__(256) void k_predict_rows(int combine, int max_blocks,
+__global__ __launch_bounds__(256) void k_predict_rows(int combine, int pooling, int max_blocks,
                                                       const int32_t* __restrict__ ctx,
                                                       const int32_t* __restrict__ qpos,
                                                       const float* __restrict__ V, int64_t v_ld,
@@ -130,12 +163,14 @@ __global__ __launch_bounds__(256) void k_predict_rows(int combine, int max_block
   const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
   const int j0 = (blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * kPredBlocksPerWave;
   if (j0 >= B) return;
-  predict_wave_rows<ROWS>(combine, N, B, q0, j0, V + (int64_t)r * v_ld, D + (int64_t)r * d_ld,
+  predict_wave_rows<ROWS>(combine, pooling, N, B, q0, j0, V + (int64_t)r * v_ld,
+                          D + (int64_t)r * d_ld,
                           vmax ? vmax + (int64_t)r * max_blocks : nullptr,
                           S + (int64_t)r * ROWS * max_blocks, max_blocks);
 }
 
-__global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_blocks,
+__global__ __launch_bounds__(256) void k_predict(int combine, int pooling, int rows,
+                                                 int max_blocks,
                                                  const int32_t* __restrict__ ctx,
                                                  const int32_t* __restrict__ qpos,
                                                  const float* __restrict__ V, int64_t v_ld,
@@ -156,7 +191,8 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
   const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
   const int j0 = (blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * kPredBlocksPerWave;
   if (j0 >= B) return;
-  predict_wave(combine, N, B, q0 + row, j0, V + (int64_t)r * v_ld, D + (int64_t)r * d_ld,
+  predict_wave(combine, pooling, N, B, q0 + row, j0, V + (int64_t)r * v_ld,
+               D + (int64_t)r * d_ld,
                vmax ? vmax + (int64_t)r * max_blocks : nullptr,
                S + ((int64_t)r * rows + row) * max_blocks);
 }
@@ -170,7 +206,7 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int rows, int max_
 constexpr int kSelectThreads = 1024;
 
 struct SelectArgs {
-  int K, sparsity_bp, explore_bp, layer;
+  int K, sparsity_bp, explore_bp, layer, per_row;  // per_row: SPIN_EXPLORE_PER_ROW
   uint32_t seed_lo, seed_hi;
   int rows, max_blocks;
   uint8_t* code;   // [R][rows][max_blocks]
@@ -244,11 +280,12 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int r, int row, 
     elig &= ~ranked;
     if (n_e > 0) {
       // exploration priorities in registers; the rows share them (the
-      // counter carries no row)
+      // counter carries no row) unless each row draws its own
       uint32_t pk[EPT];
 #pragma unroll
       for (int e = 0; e < EPT; ++e)
-        pk[e] = explore_key(j0 + e, t, a.layer, rid, a.seed_lo, a.seed_hi);
+        pk[e] = explore_key(j0 + e, t, a.layer + (a.per_row ? 65536 * row : 0), rid, a.seed_lo,
+                            a.seed_hi);
       const uint32_t expl =
           block_select_top<EPT, kSelectThreads>(pk, elig, n_e, L.hist, L.sh, L.tmpu);
 #pragma unroll
@@ -267,13 +304,13 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int r, int row, 
 
 // Union of request r's row masks (Sec. 3.2.2), compacted to its block list.
 template <int EPT>
-__device__ __forceinline__ void union_row(int rows, int max_blocks, int r, int B,
+__device__ __forceinline__ void union_row(int rows, int n_use, int max_blocks, int r, int B,
                                           const uint8_t* __restrict__ code,
                                           int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
                                           int* sh) {
   const int j0 = threadIdx.x * EPT;
   uint32_t any = 0u;
-  for (int row = 0; row < rows; ++row) {
+  for (int row = 0; row < n_use; ++row) {  // the first n_use rows' masks
     const uint8_t* crow = code + ((int64_t)r * rows + row) * max_blocks;
 #pragma unroll
     for (int e = 0; e < EPT; ++e)
@@ -298,7 +335,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
 
 // Union of the verifier rows' masks (Sec. 3.2.2), one workgroup per request.
 template <int EPT>
-__global__ __launch_bounds__(kSelThreads) void k_union(int rows, int max_blocks,
+__global__ __launch_bounds__(kSelThreads) void k_union(int rows, int n_use, int max_blocks,
                                                        const int32_t* __restrict__ ctx,
                                                        const int32_t* __restrict__ qpos,
                                                        const uint8_t* __restrict__ code,
@@ -309,7 +346,7 @@ __global__ __launch_bounds__(kSelThreads) void k_union(int rows, int max_blocks,
   const int N = ctx[r];
   const bool bad = request_error(N, qpos[r], rows, max_blocks, 0, 0) != 0;
   const int B = bad ? 0 : (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
-  union_row<EPT>(rows, max_blocks, r, B, code, sel, n_sel, sh);
+  union_row<EPT>(rows, n_use, max_blocks, r, B, code, sel, n_sel, sh);
 }
 
 __global__ void k_advance(int R, int rows, const int32_t* __restrict__ n_valid,
@@ -333,14 +370,20 @@ __global__ void k_zero_i32(int32_t* __restrict__ p, int n) {
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+// The V block maxima stand in for V only under the max combine and max pooling.
+static bool vmax_usable(const spin_config& c) {
+  return c.combine == SPIN_COMBINE_MAX && (c.flags & SPIN_POOL_MASK) == SPIN_POOL_MAX;
+}
+
 template <int ROWS>
 static void predict_rows_t(const spin_config& c, const spin_batch& b, const float* V,
                            int64_t v_ld, const float* D, int64_t d_ld, const float* vmax,
                            float* S, hipStream_t st, int32_t* qpos_snap) {
   dim3 grid((b.max_blocks + 4 * kPredBlocksPerWave - 1) / (4 * kPredBlocksPerWave), 1, b.batch);
-  hipLaunchKernelGGL(k_predict_rows<ROWS>, grid, dim3(256), 0, st, c.combine, b.max_blocks,
-                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld,
-                     c.combine == SPIN_COMBINE_MAX ? vmax : nullptr, S, b.err, qpos_snap);
+  const int pooling = c.flags & SPIN_POOL_MASK;
+  hipLaunchKernelGGL(k_predict_rows<ROWS>, grid, dim3(256), 0, st, c.combine, pooling,
+                     b.max_blocks, b.ctx_len, b.q_pos, V, v_ld, D, d_ld,
+                     vmax_usable(c) ? vmax : nullptr, S, b.err, qpos_snap);
 }
 
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
@@ -356,15 +399,16 @@ hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float
   }
   dim3 grid((b.max_blocks + 4 * kPredBlocksPerWave - 1) / (4 * kPredBlocksPerWave), b.n_rows,
             b.batch);
-  hipLaunchKernelGGL(k_predict, grid, dim3(256), 0, st, c.combine, b.n_rows, b.max_blocks,
-                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld,
-                     c.combine == SPIN_COMBINE_MAX ? vmax : nullptr, S, b.err, qpos_snap);
+  hipLaunchKernelGGL(k_predict, grid, dim3(256), 0, st, c.combine, c.flags & SPIN_POOL_MASK,
+                     b.n_rows, b.max_blocks, b.ctx_len, b.q_pos, V, v_ld, D, d_ld,
+                     vmax_usable(c) ? vmax : nullptr, S, b.err, qpos_snap);
   return hipGetLastError();
 }
 
 static SelectArgs select_args(const spin_config& c, const spin_batch& b, uint8_t* code,
                               int32_t* sel, int32_t* n_sel) {
   return SelectArgs{c.topk, c.sparsity_bp, c.explore_bp, c.layer,
+                    (c.flags & SPIN_EXPLORE_PER_ROW) != 0,
                     (uint32_t)(c.seed & 0xFFFFFFFFu), (uint32_t)(c.seed >> 32), b.n_rows,
                     b.max_blocks, code, sel, n_sel};
 }
@@ -386,9 +430,11 @@ static void select_t(const spin_config& c, const spin_batch& b, const float* S,
 }
 
 template <int EPT>
-static void union_t(const spin_batch& b, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                    hipStream_t st) {
-  hipLaunchKernelGGL(k_union<EPT>, dim3(b.batch), dim3(kSelThreads), 0, st, b.n_rows,
+static void union_t(const spin_config& c, const spin_batch& b, uint8_t* code, int32_t* sel,
+                    int32_t* n_sel, hipStream_t st) {
+  // row-0 sharing scores row 0's mask alone
+  const int n_use = (c.flags & SPIN_MTP_ROW0_MASK) ? 1 : b.n_rows;
+  hipLaunchKernelGGL(k_union<EPT>, dim3(b.batch), dim3(kSelThreads), 0, st, b.n_rows, n_use,
                      b.max_blocks, b.ctx_len, b.q_pos, code, sel, n_sel);
 }
 
@@ -403,10 +449,10 @@ hipError_t launch_select(const spin_config& c, const spin_batch& b, const float*
   }
   if (b.n_rows > 1) {  // union of the rows' masks
     const int eu = (b.max_blocks + kSelThreads - 1) / kSelThreads;
-    if (eu <= 1) union_t<1>(b, code, sel, n_sel, st);
-    else if (eu <= 2) union_t<2>(b, code, sel, n_sel, st);
-    else if (eu <= 4) union_t<4>(b, code, sel, n_sel, st);
-    else union_t<8>(b, code, sel, n_sel, st);
+    if (eu <= 1) union_t<1>(c, b, code, sel, n_sel, st);
+    else if (eu <= 2) union_t<2>(c, b, code, sel, n_sel, st);
+    else if (eu <= 4) union_t<4>(c, b, code, sel, n_sel, st);
+    else union_t<8>(c, b, code, sel, n_sel, st);
   }
   return hipGetLastError();
 }

@@ -509,7 +509,8 @@ hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const floa
   const int free_cus = resident_workgroups((const void*)k_topk_ema, kSelThreads) - rows_total;
   const int ema_x = max(1, min(most, free_cus / max(1, b.batch)));
   const EmaArgs A{c.ema_alpha, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap, n_valid, z, z_ld,
-                  sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out, vmax};
+                  sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out, vmax,
+                  (c.flags & SPIN_MTP_ROW0_UPDATE) != 0};
   hipLaunchKernelGGL(k_topk_ema, dim3(rows_total + ema_x * b.batch), dim3(kSelThreads), 0, st,
                      c.topk, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap, z, z_ld, sel, n_sel,
                      out, ws, rows_total, A, ema_x);

@@ -25,14 +25,14 @@ def device_keys(li: LayerInputs):
 
 
 def make_layer(li: LayerInputs, sparsity_bp: int, seed=G.PHILOX_SEED, combine=None,
-               vmax_cache: bool = False):
+               vmax_cache: bool = False, **variants):
     from sparse_attention_indexer_spin_amd import SpinLayer
     w = li.w
     lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks, d_cap=d_capacity(w, w.steps),
                     topk=w.topk, sparsity_bp=sparsity_bp, n_rows=w.rows,
                     explore_bp=w.explore_bp, ema_alpha=w.alpha, combine=combine or w.combine,
                     key_dtype=KEY_TORCH[w.key_dtype], q_dtype=Q_TORCH[w.q_dtype],
-                    layer=li.layer, seed=seed, device=DEV, vmax_cache=vmax_cache)
+                    layer=li.layer, seed=seed, device=DEV, vmax_cache=vmax_cache, **variants)
     lay.set_requests(li.ctx.to(DEV), li.pos[0].to(DEV))
     lay.reset()
     return lay

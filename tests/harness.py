@@ -50,7 +50,7 @@ d_capacity = G.d_capacity
 
 
 def run_oracle(li: LayerInputs, n_steps: int, sparsity_bp: int, reqs=None, seed=G.PHILOX_SEED,
-               combine=None, states=None):
+               combine=None, states=None, **variants):
     """Closed-loop oracle over n_steps; returns per-step lists of per-request results."""
     w = li.w
     reqs = range(w.batch) if reqs is None else reqs
@@ -71,7 +71,7 @@ def run_oracle(li: LayerInputs, n_steps: int, sparsity_bp: int, reqs=None, seed=
                               q_pos=int(li.pos[s, r]), K=w.topk, sparsity_bp=sparsity_bp,
                               explore_bp=w.explore_bp, alpha=w.alpha, layer=li.layer,
                               req_id=r, seed=seed, combine=combine or w.combine,
-                              n_valid=int(li.accept[s, r]))
+                              n_valid=int(li.accept[s, r]), **variants)
             step_res[r] = res
         out.append(step_res)
     return out, states
