@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--probe-period", type=int, default=8)
     ap.add_argument("--stack-layers", type=int, default=8,
                     help="--stack on a one-layer workload: that many independent layers of it")
+    ap.add_argument("--miss-eval", action="store_true",
+                    help="top-K miss rate (share of the dense top-K slots outside the scored "
+                         "blocks) of the method's design variants, closed loop on the workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 1 GiB device-to-device copies (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -466,6 +469,57 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
     return out
 
 
+def miss_eval(inp: Inputs, sparsity_bp: int, steps: int, variants: dict):
+    """Closed loop of one variant; after every sparse step, the dense top-K of
+    the same queries (every block scored through the library) and the share
+    of its slots that fall in blocks the step did not score.  Returns the
+    per-(step, request, row) miss rates and the realized block sparsity."""
+    from sparse_attention_indexer_spin_amd import SpinLayer, api
+    w = inp.w
+    kd = {"fp8": torch.uint8, "bf16": torch.bfloat16, "f32": torch.float32}[w.key_dtype]
+    qd = torch.bfloat16 if w.q_dtype == "bf16" else torch.float32
+    lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks, d_cap=G.d_capacity(w, steps),
+                    topk=w.topk, sparsity_bp=sparsity_bp, n_rows=w.rows,
+                    explore_bp=w.explore_bp, ema_alpha=w.alpha, combine=w.combine,
+                    key_dtype=kd, q_dtype=qd, **variants)
+    lay.set_requests(inp.ctx.cuda(), inp.pos[0].cuda())
+    lay.reset()
+    pages, scale, pt = inp.keys.pages, inp.keys.scale, inp.keys.page_table
+    bt = lay.batch(pages.shape[0])
+    dev = pages.device
+    B = (inp.ctx.to(dev).long() + 63) // 64
+    ar = torch.arange(w.max_blocks, device=dev)
+    sel_all = torch.where(ar[None, :] < B[:, None], ar[None, :], torch.full_like(ar, -1)[None, :])
+    sel_all = sel_all.to(torch.int32).contiguous()
+    n_all = B.to(torch.int32).contiguous()
+    z_d = torch.zeros_like(lay.z)
+    top_d = torch.full_like(lay.topk_idx, -1)
+    ws_d = torch.zeros_like(lay.workspace)
+    misses, sparsity = [], []
+    for s in range(steps):
+        nv = inp.accept_dev[s] if w.rows > 1 else None
+        # the dense reference first: it reads the counters the step advances
+        api.spin_sparse_index_score(lay.cfg, bt, inp.q[s], inp.weights, pages, scale, pt,
+                                    sel_all, n_all, z_d)
+        api.spin_topk(lay.cfg, bt, z_d, sel_all, n_all, top_d, ws_d)
+        lay.step(inp.q[s], inp.weights, pages, scale, pt, n_valid=nv)
+        if s == 0:
+            continue                                   # the dense warm-up step
+        mask = torch.zeros(w.batch, w.max_blocks + 1, dtype=torch.bool, device=dev)
+        ns = lay.n_sel.long()
+        for r in range(w.batch):
+            mask[r, lay.sel[r, :int(ns[r])].long()] = True
+        blk = torch.where(top_d >= 0, top_d // 64, torch.full_like(top_d, w.max_blocks)).long()
+        valid = top_d >= 0
+        hit = torch.gather(mask[:, None, :].expand(-1, w.rows, -1), 2, blk) & valid
+        m = 1.0 - hit.sum(-1).float() / valid.sum(-1).clamp(min=1).float()
+        misses.append(m.flatten().cpu())
+        sparsity.append(float(1.0 - ns.sum().item() / B.sum().item()))
+    torch.cuda.synchronize()
+    assert int(lay.err.item()) == 0
+    return torch.cat(misses).numpy(), float(np.mean(sparsity))
+
+
 def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, budget_s: float,
                  max_requests: int):
     """Time the CPU oracle on whole requests of the workload until about `budget_s`
@@ -569,6 +623,25 @@ def main():
         main_stack(args, w, sp)
         return
     inp = Inputs(w, total_steps)
+    if args.miss_eval:
+        variants = [("A1-max (default)", {}), ("A1-top4", {"pooling": "top4"}),
+                    ("A1-mean", {"pooling": "mean"})]
+        if w.rows > 1:
+            variants += [("row-0 mask", {"mtp_row0_mask": True}),
+                         ("row-0 update", {"mtp_row0_update": True}),
+                         ("row-0 mask + row-0 update", {"mtp_row0_mask": True,
+                                                        "mtp_row0_update": True}),
+                         ("per-row exploration", {"explore_per_row": True})]
+        res = {}
+        for spb in sorted(set(w.sparsity_bp) | {sp}):
+            for name, v in variants:
+                m, rs = miss_eval(inp, spb, total_steps, v)
+                res.setdefault(str(spb), {})[name] = {
+                    "mean_miss": float(m.mean()), "p99_miss": float(np.quantile(m, 0.99)),
+                    "realized_sparsity": rs}
+        print(json.dumps({"workload": w.name, "steps": total_steps, "miss_eval": res,
+                          "data": "synthetic (seeded generator)"}))
+        return
     evictor = Evictor()
     # the two other protocols first, for reference; then the reported one
     refs = {}
