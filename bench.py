@@ -441,6 +441,35 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
     keys = int(np.minimum(n_sel * 64, ctx).sum()) * w.rows
     out = dict(total_ms=total_ms, ms_per_step=total_ms / (steps * copies), keys_per_step=keys,
                n_sel=int(n_sel.sum()))
+    # the same copies as the layers of one model through the multi-layer
+    # schedule (plans on a side stream), from fresh state: per-layer step time
+    from sparse_attention_indexer_spin_amd import SpinStack
+    slays = []
+    for c in range(copies):
+        lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks,
+                        d_cap=G.d_capacity(w, steps + warmup), topk=w.topk,
+                        sparsity_bp=sparsity_bp, n_rows=w.rows, explore_bp=w.explore_bp,
+                        ema_alpha=w.alpha, combine=w.combine,
+                        key_dtype={"fp8": torch.uint8, "bf16": torch.bfloat16,
+                                   "f32": torch.float32}[w.key_dtype],
+                        q_dtype=torch.bfloat16 if w.q_dtype == "bf16" else torch.float32)
+        lay.set_requests(inp.ctx.cuda(), inp.pos[0].cuda())
+        lay.reset()
+        slays.append(lay)
+    stack = SpinStack(slays)
+    if w.rows == 1:
+        for s in range(warmup):
+            stack.step([inp.q[s]] * copies, [inp.weights] * copies, pages, scales, [pt] * copies)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for s in range(warmup, warmup + steps):
+            stack.step([inp.q[s]] * copies, [inp.weights] * copies, pages, scales, [pt] * copies)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        for lay in slays:
+            assert torch.equal(lay.topk_idx, lays[0].topk_idx), "stack and spin_step disagree"
+        out["stack_ms_per_step"] = t0.elapsed_time(t1) / (steps * copies)
+    del slays, stack
     if stage_reps:
         q = inp.q[warmup + steps - 1]
         last_nv = nv[-1]
@@ -677,6 +706,8 @@ def main():
                           "cold": "1 GiB read before each timed step and stage launch",
                           "warm": "one copy, steps back to back"}[args.cache],
                   **{f"{k}_us_per_step_layer": v["ms_per_step"] * 1e3 for k, v in refs.items()}},
+        "stack_us_per_step_layer": (res["stack_ms_per_step"] * 1e3
+                                    if "stack_ms_per_step" in res else None),
         "stage_us": res["stage_us"],
         "keys_scored_per_step": keys_row,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
