@@ -635,7 +635,41 @@ struct QFull<1, NS> {  // bf16 keys
 // 16 st + n (the dims its fp8 query registers hold), plus slot l's scale.
 // bf16 (KT = 1): for sub-tile st and k-step ks, dims 32 ks + 8 g .. + 8 of
 // slot 16 st + n.
+//
+// Loaded in that layout, one instruction touches half of each of 16 128-byte
+// lines.  With one verifier row (WL) every load instruction instead reads 8
+// whole lines (one kilobyte of the page, each line by 8 lanes), and a
+// register pair is then brought into the MFMA layout by exchanging lane bit
+// 3 with the pair's register bit (swap_pair: one row rotation by 8 lanes and
+// a select per dword).  Whole-line loads can be marked non-temporal
+// (streamed through the caches); half-line loads cannot, as the second half
+// of a line would miss again.  With several rows the waves of a stream read
+// each page in turn and the L2 must keep it, and the rows' epilogues already
+// fill the VALU, so they keep the plain half-line loads.  In lane l (l3 =
+// bit 3 of l, n' = l & 7) the pair members x (register bit 0) and y (bit 1)
+// hold, as loaded, slots n' and 8 + n' of the sub-tile, both at the 16-byte
+// chunk c(l3); after the swap both hold slot l & 15, x at chunk c(0) and y at
+// chunk c(1), c(b) being the chunk the MFMA layout gives register b of lane l.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void swap_pair(v4u& x, v4u& y) {
+  const bool hi = (threadIdx.x & 8) != 0;
+  v4u nx, ny;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    // row_ror:8 -- lane l reads lane l ^ 8 of its 16-lane row
+    const unsigned ty = __builtin_amdgcn_update_dpp(0u, y[c], 0x128, 0xF, 0xF, false);
+    const unsigned tx = __builtin_amdgcn_update_dpp(0u, x[c], 0x128, 0xF, 0xF, false);
+    nx[c] = hi ? ty : x[c];
+    ny[c] = hi ? y[c] : tx;
+  }
+  x = nx;
+  y = ny;
+}
+
+__device__ __forceinline__ v4u load16_nt(const uint8_t* a) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(a));
+}
+
 template <int KT>
 struct PageRegs;
 
@@ -643,20 +677,29 @@ template <>
 struct PageRegs<0> {
   static constexpr int kRegs = 8;
   static constexpr int64_t kBytes = 8192;
+  // WL: register 2 st + b holds slots 16 st + 8 b + (l & 7), chunk (l >> 4) + 4 l3
+  template <bool WL>
   __device__ static __forceinline__ void load(const ScoreParams& p, int page, v4u (&b)[8],
                                               float& sc) {
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(p.kp) + (int64_t)page * kBytes +
-                          n * 128 + 16 * g;
+    const uint8_t* page_base = reinterpret_cast<const uint8_t*>(p.kp) + (int64_t)page * kBytes;
+    if constexpr (WL) {
+      const uint8_t* base = page_base + (lane & 7) * 128 + ((lane >> 3) & 1) * 64 + g * 16;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      b[2 * st] = *reinterpret_cast<const v4u*>(base + st * 2048);
-      b[2 * st + 1] = *reinterpret_cast<const v4u*>(base + st * 2048 + 64);
+      for (int i = 0; i < 8; ++i) b[i] = load16_nt(base + i * 1024);
+    } else {
+      const uint8_t* base = page_base + n * 128 + 16 * g;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        b[2 * st] = *reinterpret_cast<const v4u*>(base + st * 2048);
+        b[2 * st + 1] = *reinterpret_cast<const v4u*>(base + st * 2048 + 64);
+      }
     }
     sc = p.ks[(int64_t)page * 64 + lane];
   }
-  template <class Q>
-  __device__ static __forceinline__ float tile(const Q& q, const v4u (&b)[8], int st) {
+  template <bool WL, class Q>
+  __device__ static __forceinline__ float tile(const Q& q, v4u (&b)[8], int st) {
+    if constexpr (WL) swap_pair(b[2 * st], b[2 * st + 1]);
     const v4u a = b[2 * st], c = b[2 * st + 1];
     return q.dot(v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z,
                      (int)c.w});
@@ -667,20 +710,34 @@ template <>
 struct PageRegs<1> {
   static constexpr int kRegs = 16;
   static constexpr int64_t kBytes = 16384;
+  // WL: register 4 st + 2 k1 + b holds slots 16 st + 8 b + (l & 7), bytes
+  // 128 k1 + 64 l3 + 16 (l >> 4) of the slot (after the swap: k-step 2 k1 + b)
+  template <bool WL>
   __device__ static __forceinline__ void load(const ScoreParams& p, int page, v4u (&b)[16],
                                               float& sc) {
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(p.kp) + (int64_t)page * kBytes +
-                          n * 256 + 16 * g;
+    const uint8_t* page_base = reinterpret_cast<const uint8_t*>(p.kp) + (int64_t)page * kBytes;
+    if constexpr (WL) {
+      const uint8_t* base = page_base + (lane & 7) * 256 + ((lane >> 3) & 1) * 64 + g * 16;
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+      for (int i = 0; i < 16; ++i)
+        b[i] = load16_nt(base + (i >> 2) * 4096 + (i & 1) * 2048 + ((i >> 1) & 1) * 128);
+    } else {
+      const uint8_t* base = page_base + n * 256 + 16 * g;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        b[4 * st + ks] = *reinterpret_cast<const v4u*>(base + st * 4096 + ks * 64);
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          b[4 * st + ks] = *reinterpret_cast<const v4u*>(base + st * 4096 + ks * 64);
+    }
     sc = 1.0f;
   }
-  template <class Q>
-  __device__ static __forceinline__ float tile(const Q& q, const v4u (&b)[16], int st) {
+  template <bool WL, class Q>
+  __device__ static __forceinline__ float tile(const Q& q, v4u (&b)[16], int st) {
+    if constexpr (WL) {
+      swap_pair(b[4 * st], b[4 * st + 1]);
+      swap_pair(b[4 * st + 2], b[4 * st + 3]);
+    }
     return q.dot(b, st);
   }
 };
@@ -752,7 +809,7 @@ __device__ __forceinline__ void emit_page(const ScoreParams& p, const float (&pa
 // The page loop of one worker: blocks [lo, hi) through cursors `db` (the
 // block being scored) and `dd` (the block being loaded, P - 1 ahead, whose
 // first pages are already in kb), query row `row` of request q_req in Q.
-template <int KT, int NS, int QB, int P, bool Span, class Cur>
+template <int KT, int NS, int QB, int P, bool Span, bool WL, class Cur>
 __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd,
                                           v4u (&kb)[P][PageRegs<KT>::kRegs], float (&sc)[P],
                                           QFull<KT, NS>& Q, int lo, int hi, int q_req, int row) {
@@ -768,8 +825,8 @@ __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd
       const int cur = it + u;
       if (cur >= hi) break;
       // refill: page cur + P - 1 (the last page again past the end: an L2 hit)
-      PR::load(p, dd.get(p, min(cur + P - 1, hi - 1)).page, kb[(u + P - 1) % P],
-               sc[(u + P - 1) % P]);
+      PR::template load<WL>(p, dd.get(p, min(cur + P - 1, hi - 1)).page,
+                            kb[(u + P - 1) % P], sc[(u + P - 1) % P]);
       const Desc d = db.get(p, cur);
       if (Span && d.r != q_req) {
         q_req = d.r;
@@ -779,7 +836,7 @@ __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd
       }
       float part[4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) part[st] = PR::tile(Q, kb[u], st);
+      for (int st = 0; st < 4; ++st) part[st] = PR::template tile<WL>(Q, kb[u], st);
       emit_page(p, part, KT == 0 ? sc[u] : 1.0f, d, rowid, hint, bad, rs);
     }
   }
@@ -787,34 +844,35 @@ __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd
   if (bad && lane == 0) raise_error(p.err, SPIN_DERR_PAGE);
 }
 
-template <int KT, int P, class Cur>
+template <int KT, int P, bool WL, class Cur>
 __device__ __forceinline__ void first_pages(const ScoreParams& p, Cur& dd,
                                             v4u (&kb)[P][PageRegs<KT>::kRegs], float (&sc)[P],
                                             int lo, int hi) {
 #pragma unroll
   for (int u = 0; u < P - 1; ++u)
-    PageRegs<KT>::load(p, dd.get(p, min(lo + u, hi - 1)).page, kb[u], sc[u]);
+    PageRegs<KT>::template load<WL>(p, dd.get(p, min(lo + u, hi - 1)).page, kb[u], sc[u]);
 }
 
 // One worker with its own query: descriptors first, then the first page, then
 // the query, so that the descriptor loads do not queue behind the query loads
 // and the query arrives while the page does.
-template <int KT, int NS, int QB, int P, bool Span, class Cur>
+template <int KT, int NS, int QB, int P, bool Span, bool WL, class Cur>
 __device__ __forceinline__ void score_pages(const ScoreParams& p, Cur& db, int lo, int hi,
                                             int q_req, int row) {
   Cur dd = db;
   v4u kb[P][PageRegs<KT>::kRegs];
   float sc[P];
-  first_pages<KT, P>(p, dd, kb, sc, lo, hi);
+  first_pages<KT, P, WL>(p, dd, kb, sc, lo, hi);
   QFull<KT, NS> Q;
   Q.fetch(p, QB, q_req * p.rows + row);
   Q.convert(p, QB, q_req * p.rows + row);
-  page_loop<KT, NS, QB, P, Span>(p, db, dd, kb, sc, Q, lo, hi, q_req, row);
+  page_loop<KT, NS, QB, P, Span, WL>(p, db, dd, kb, sc, Q, lo, hi, q_req, row);
 }
 
 enum { kRunWave = 0, kRunTable = 1, kRunSpan = 2 };
 
-template <int KT, int NS, int QB, int P, int Mode>
+// WL: whole-line page loads (one verifier row; see PageRegs)
+template <int KT, int NS, int QB, int P, int Mode, bool WL>
 __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
   extern __shared__ int pre_dyn[];
   __shared__ int tmp[32];
@@ -850,7 +908,7 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
       db.hi = hi;
       db.init(p, lo);
       dd = db;
-      first_pages<KT, P>(p, dd, kb, sc, lo, hi);
+      first_pages<KT, P, WL>(p, dd, kb, sc, lo, hi);
     }
 #pragma unroll
     for (int k = 0; k < SPIN_MAX_ROWS; ++k)
@@ -859,7 +917,7 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
     if (!active) return;
     QFull<KT, NS> Q;
     Q.from_lds(lds, wstage, row);
-    page_loop<KT, NS, QB, P, false>(p, db, dd, kb, sc, Q, lo, hi, run.r, row);
+    page_loop<KT, NS, QB, P, false, WL>(p, db, dd, kb, sc, Q, lo, hi, run.r, row);
   } else {
     int n_ne;
     const ItemTable tb = build_items(p, pre_dyn, tmp, pre_dyn + p.R + 1, &n_ne);
@@ -876,7 +934,7 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
     db.tb = tb;
     db.b.init(p, tb, lo);
     if (q_req < 0) q_req = __builtin_amdgcn_readfirstlane(db.b.mine.r);
-    score_pages<KT, NS, QB, P, Mode == kRunSpan>(p, db, lo, hi, q_req, row);
+    score_pages<KT, NS, QB, P, Mode == kRunSpan, WL>(p, db, lo, hi, q_req, row);
   }
 }
 
@@ -926,13 +984,13 @@ __global__ __launch_bounds__(64) void k_score_f32(ScoreParams p) {
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
-template <int KT, int NS, int QB>
-static void launch_wave(const ScoreParams& p, hipStream_t st) {
+template <int KT, int NS, int QB, bool WL>
+static void launch_wave_l(const ScoreParams& p, hipStream_t st) {
   constexpr int P = 2;  // pages in flight per wave
   const int spw = p.rows == 1 ? 4 : (p.rows == 2 ? 2 : 1);
   if (p.R <= 64) {  // teams of workgroups, each wave finds its own run
     const size_t stage = (size_t)p.rows * QFull<KT, NS>::kStageBytes;
-    const auto wave = k_score_wave<KT, NS, QB, P, kRunWave>;
+    const auto wave = k_score_wave<KT, NS, QB, P, kRunWave, WL>;
     const int g = min(resident_workgroups((const void*)wave, 256, stage), p.R * p.max_blocks);
     if (g >= p.R && lds_fits((const void*)wave, stage)) {
       hipLaunchKernelGGL(wave, dim3(g), dim3(256), stage, st, p);
@@ -940,15 +998,21 @@ static void launch_wave(const ScoreParams& p, hipStream_t st) {
     }
   }
   const size_t dyn = sizeof(int) * 2 * (p.R + 1);
-  const auto aligned = k_score_wave<KT, NS, QB, P, kRunTable>;
+  const auto aligned = k_score_wave<KT, NS, QB, P, kRunTable, WL>;
   const int g = min(resident_workgroups((const void*)aligned, 256, dyn), p.R * p.max_blocks);
   if (spw * g >= p.R) {  // a stream per request at least: request-aligned runs
     hipLaunchKernelGGL(aligned, dim3(g), dim3(256), dyn, st, p);
     return;
   }
-  const auto span = k_score_wave<KT, NS, QB, P, kRunSpan>;
+  const auto span = k_score_wave<KT, NS, QB, P, kRunSpan, WL>;
   const int g2 = min(resident_workgroups((const void*)span, 256, dyn), p.R * p.max_blocks);
   hipLaunchKernelGGL(span, dim3(g2), dim3(256), dyn, st, p);
+}
+
+template <int KT, int NS, int QB>
+static void launch_wave(const ScoreParams& p, hipStream_t st) {
+  if (p.rows == 1) launch_wave_l<KT, NS, QB, true>(p, st);
+  else launch_wave_l<KT, NS, QB, false>(p, st);
 }
 
 bool score_filters(const spin_config& c, const spin_batch&) {
