@@ -778,12 +778,13 @@ __device__ __forceinline__ void run_flush(const ScoreParams& p, const CandRun& r
 // block's candidates at or above the row's hint appended to the run.
 __device__ __forceinline__ void emit_page(const ScoreParams& p, const float (&part)[4], float sc,
                                           const Desc& d, int rowid, uint32_t hint, int& bad,
-                                          CandRun& rs) {
+                                          CandRun& rs, float* zout = nullptr) {
   const int lane = threadIdx.x & 63;
   const float tot = reduce_scatter4(part);
   const int slot = d.j * 64 + lane;
   const float zv = (slot < d.N && !d.bad) ? tot * sc + 0.0f : 0.0f;
-  p.z[(int64_t)rowid * p.z_ld + (int64_t)d.k * 64 + lane] = zv;
+  if (zout) *zout = zv;  // the caller stores it later (ZQueue)
+  else p.z[(int64_t)rowid * p.z_ld + (int64_t)d.k * 64 + lane] = zv;
   bad |= d.bad;
   if (p.sink.hint) {  // top-K pre-filter: this block's slots at or above the hint
     const uint32_t key = float_key(zv);
@@ -806,6 +807,39 @@ __device__ __forceinline__ void emit_page(const ScoreParams& p, const float (&pa
   }
 }
 
+// The z rows of the last (up to) kZQueue pages a wave scored, held in
+// registers (lane l: slot l of each page) while the pages are consecutive
+// blocks of one row, and stored together when the queue is full, the next
+// page does not continue the run, or the loop ends.  Stored page by page,
+// the z lines cost ~8 us of a 67 us launch although they are 3 % of its
+// bytes (the same stores kept on a few L2-resident lines cost ~1 us, so it
+// is their way to HBM amid the page stream, not the instructions); stored
+// in bursts of 16 pages they cost ~3 us.
+constexpr int kZQueue = 16;
+
+struct ZQueue {
+  float q[kZQueue];
+  int n = 0, k = 0, rowid = 0;  // pages held; block index and row of the newest (uniform)
+
+  __device__ __forceinline__ void flush(const ScoreParams& p) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kZQueue; ++i)
+      if (i >= kZQueue - n)
+        p.z[(int64_t)rowid * p.z_ld + (int64_t)(k - (kZQueue - 1 - i)) * 64 + lane] = q[i];
+    n = 0;
+  }
+  __device__ __forceinline__ void push(const ScoreParams& p, float zv, int rid, int kk) {
+    if (n > 0 && (n == kZQueue || kk != k + 1 || rid != rowid)) flush(p);
+#pragma unroll
+    for (int i = 0; i < kZQueue - 1; ++i) q[i] = q[i + 1];
+    q[kZQueue - 1] = zv;
+    k = kk;
+    rowid = rid;
+    ++n;
+  }
+};
+
 // The page loop of one worker: blocks [lo, hi) through cursors `db` (the
 // block being scored) and `dd` (the block being loaded, P - 1 ahead, whose
 // first pages are already in kb), query row `row` of request q_req in Q.
@@ -819,6 +853,7 @@ __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd
   uint32_t hint = row_hint(p, rowid);
   int bad = 0;
   CandRun rs;
+  ZQueue zq;  // one row, runs inside one request: z stores queued
   for (int it = lo; it < hi; it += P) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
@@ -837,9 +872,17 @@ __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd
       float part[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) part[st] = PR::template tile<WL>(Q, kb[u], st);
-      emit_page(p, part, KT == 0 ? sc[u] : 1.0f, d, rowid, hint, bad, rs);
+      if constexpr (WL && !Span) {
+        float zv;
+        emit_page(p, part, KT == 0 ? sc[u] : 1.0f, d, rowid, hint, bad, rs, &zv);
+        zq.push(p, zv, rowid, d.k);
+      } else {
+        emit_page(p, part, KT == 0 ? sc[u] : 1.0f, d, rowid, hint, bad, rs);
+      }
     }
   }
+  if constexpr (WL && !Span)
+    if (zq.n > 0) zq.flush(p);
   run_flush(p, rs);
   if (bad && lane == 0) raise_error(p.err, SPIN_DERR_PAGE);
 }
