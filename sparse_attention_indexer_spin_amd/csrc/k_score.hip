@@ -15,11 +15,14 @@
 //
 // MFMA kernels: every wave scores whole pages on its own, with the query of
 // one verifier row (all 64 heads) in registers.  It loads each page straight
-// from HBM into registers, two pages deep, in the operand layout of the MFMA
-// (the dims a lane holds are the same for query and key), runs the 16-slot x
-// 16-head tiles, applies ReLU and the head weights in registers and leaves
-// lane l with slot l's total after a permlane reduce-scatter, so a page's 64
-// scores go out as one 256-byte store.  No LDS staging, no barriers.  With
+// from HBM into registers, two pages deep, and brings it into the operand
+// layout of the MFMA (the dims a lane holds are the same for query and key):
+// with one row by whole-line non-temporal loads and a lane swap, with several
+// rows by loading in that layout (PageRegs).  It runs the 16-slot x 16-head
+// tiles, applies ReLU and the head weights in registers and leaves lane l
+// with slot l's total after a permlane reduce-scatter, so a page's 64 scores
+// are one 256-byte row of z (with one row, queued and stored 16 pages at a
+// time: ZQueue).  No LDS staging of keys, no barriers in the page loop.  With
 // several verifier rows, a stream of `rows` waves walks the same pages (one
 // row each); the page comes from HBM once and from L2 for the others.
 // Work is split into request-aligned contiguous runs of selected blocks.

@@ -37,12 +37,22 @@ def _sample_requests(R: int):
     return sorted({0, 1, R // 2, R - 1})
 
 
+# More than 64 requests: the score kernel builds its item table in LDS, and
+# with ~30 pages per wave its z queue fills and flushes mid-run.
+_MANY_REQUESTS = {
+    "fp8_72req_64k": lambda: G.WORKLOADS["fp8_128k_b32"].scaled(batch=72, n_slots=65536,
+                                                                n_slots_min=40001),
+    "bf16_72req_64k": lambda: G.WORKLOADS["bf16_64k_b16"].scaled(batch=72, n_slots=65536,
+                                                                 n_slots_min=40001),
+}
+
+
 @pytest.mark.parametrize("name", ["fp8_128k_b32", "bf16_64k_b16", "fp8_128k_b32_mtp4",
-                                  "fp8_256k_ragged_8l"])
+                                  "fp8_256k_ragged_8l", "fp8_72req_64k", "bf16_72req_64k"])
 def test_full_size_sampled_parity(name):
     from sparse_attention_indexer_spin_amd import SpinLayer
     banner(f"full size {name}")
-    w = G.WORKLOADS[name]
+    w = _MANY_REQUESTS[name]() if name in _MANY_REQUESTS else G.WORKLOADS[name]
     n_steps = 3
     sp = w.sparsity_bp[0]  # the workload's headline sparsity (40 %)
     layer = 0
