@@ -935,30 +935,39 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
     const int s = wave / p.rows, nb = run.hi - run.lo;
     const int lo = __builtin_amdgcn_readfirstlane(run.lo + s * nb / spw);
     const int hi = __builtin_amdgcn_readfirstlane(run.lo + (s + 1) * nb / spw);
-    const bool active = wave < spw * p.rows && lo < hi;
+    // (uniform: a scalar branch below, so each path's load waits are known where they join)
+    const bool active = __builtin_amdgcn_readfirstlane(wave < spw * p.rows && lo < hi ? 1 : 0) != 0;
     unsigned char* lds = reinterpret_cast<unsigned char*>(pre_dyn);
     __shared__ float wstage[SPIN_MAX_ROWS * 64];  // head weights of each row
     // wave w stages head tile w of every row k: the query loads go out first
     // (the descriptor wait covers them), the first page next, and the
     // conversion then runs while the page is in flight
     QFull<KT, NS> S;
+    constexpr int kRowsMax = WL ? 1 : SPIN_MAX_ROWS;  // WL: one row
 #pragma unroll
-    for (int k = 0; k < SPIN_MAX_ROWS; ++k)
+    for (int k = 0; k < kRowsMax; ++k)
       if (k < p.rows) S.stage_fetch(p, QB, run.r * p.rows + k, wave, k);
     RunCursor db, dd;
     v4u kb[P][PageRegs<KT>::kRegs];
     float sc[P];
+    // The conversion runs on each path after the query loads are known to be
+    // complete: placed after the two paths join, it made the compiler wait
+    // for every load, the first pages' too, and so held up the barrier.
     if (active) {
       db.r = run.r;
       db.N = run.N;
       db.hi = hi;
-      db.init(p, lo);
+      db.init(p, lo);  // its wait completes the query loads too
       dd = db;
       first_pages<KT, P, WL>(p, dd, kb, sc, lo, hi);
-    }
 #pragma unroll
-    for (int k = 0; k < SPIN_MAX_ROWS; ++k)
-      if (k < p.rows) S.stage_put(QB, wave, k, lds, wstage, k);
+      for (int k = 0; k < kRowsMax; ++k)
+        if (k < p.rows) S.stage_put(QB, wave, k, lds, wstage, k);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kRowsMax; ++k)
+        if (k < p.rows) S.stage_put(QB, wave, k, lds, wstage, k);
+    }
     __syncthreads();
     if (!active) return;
     QFull<KT, NS> Q;
