@@ -101,33 +101,49 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
   float* Vr = V + (int64_t)r * v_ld;
   float* Dr = D + (int64_t)r * d_ld;
   if (L == 1) {
-    // one observation per slot: V[i] and D[q - i] from row 0, loads batched
-    for (int kb = k0; kb < k1; kb += CH) {
+    // one observation per slot: V[i] and D[q - i] from row 0, CH blocks'
+    // loads at a time, two chunks in flight: chunk c + 1's loads go out
+    // before chunk c's stores, so a wave's writes overlap its next reads
+    // (different blocks touch disjoint V and D elements)
+    struct Chunk {
       float vv[CH], dd[CH], zz[CH];
       int ii[CH], jj[CH];
+    };
+    const auto load = [&](Chunk& C, int kb) {
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
         const int k = kb + u;
         const int j = k < k1 ? __builtin_amdgcn_readfirstlane(sr[k]) : -1;  // uniform
         const int i = j * 64 + lane;
         const bool ok = k < k1 && j >= 0 && j < max_blocks && i < N;
-        jj[u] = k < k1 && j >= 0 && j < max_blocks ? j : -1;
-        ii[u] = ok ? i : -1;
-        vv[u] = ok ? Vr[i] : 0.0f;
-        dd[u] = ok ? Dr[q - i] : 0.0f;
-        zz[u] = ok ? zb[(int64_t)k * 64 + lane] : 0.0f;
+        C.jj[u] = k < k1 && j >= 0 && j < max_blocks ? j : -1;
+        C.ii[u] = ok ? i : -1;
+        C.vv[u] = ok ? Vr[i] : 0.0f;
+        C.dd[u] = ok ? Dr[q - i] : 0.0f;
+        C.zz[u] = ok ? zb[(int64_t)k * 64 + lane] : 0.0f;
       }
+    };
+    const auto finish = [&](const Chunk& C) {
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
-        const float vn = ema_step(vv[u], zz[u], a, b);
-        if (ii[u] >= 0) {
-          Vr[ii[u]] = vn;
-          Dr[q - ii[u]] = ema_step(dd[u], zz[u], a, b);
+        const float vn = ema_step(C.vv[u], C.zz[u], a, b);
+        if (C.ii[u] >= 0) {
+          Vr[C.ii[u]] = vn;
+          Dr[q - C.ii[u]] = ema_step(C.dd[u], C.zz[u], a, b);
         }
         // (the block id from before the stores: sel may alias V or D for all
         // the compiler knows, and a reload would wait for them)
-        if (A.vmax && jj[u] >= 0) ema_vmax(A, r, jj[u], ii[u] >= 0, vn);
+        if (A.vmax && C.jj[u] >= 0) ema_vmax(A, r, C.jj[u], C.ii[u] >= 0, vn);
       }
+    };
+    Chunk c0, c1;
+    load(c0, k0);
+    for (int kb = k0; kb < k1; kb += 2 * CH) {
+      if (kb + CH < k1) load(c1, kb + CH);
+      finish(c0);
+      if (kb + CH >= k1) break;
+      if (kb + 2 * CH < k1) load(c0, kb + 2 * CH);
+      finish(c1);
     }
     return;
   }

@@ -466,7 +466,9 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select_pages(
 // run the per-row select (dispatched first), the others the EMA, ema_x of
 // them per request, sized to fill the CUs the few select workgroups leave
 // idle (one workgroup per CU: the select's LDS).
-constexpr int kEmaChunk = 16;  // blocks whose loads an EMA wave issues together
+// blocks whose loads an EMA wave issues together (two such chunks are in
+// flight; 16 made the 1,024-thread kernel spill)
+constexpr int kEmaChunk = 6;
 
 __global__ __launch_bounds__(kSelThreads) void k_topk_ema(
     int K, int rows, int max_blocks, const int32_t* __restrict__ ctx,
