@@ -240,7 +240,7 @@ class StackInputs:
 
 def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict=None,
               policy: str = "none", probe_period: int = 8,
-              modes=("seq", "stack", "ema_stream")):
+              modes=("seq", "stack", "ema_stream", "one_stream")):
     """Whole decode steps of every layer: (a) one spin_step per layer in layer
     order on the current stream, (b) one spin_stack_step (plans on a side
     stream).  Each mode on its own layer states from the same reset; each timed
@@ -294,9 +294,9 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
                 lay.step(inp.q[l][s], inp.weights[l], pages[l], scales[l], pts[l])
 
         ms_seq = timed(seq_step)
-    def run_stack_mode(ema_stream):
+    def run_stack_mode(ema_stream, one_stream=False):
         lays = layers()
-        stack = SpinStack(lays, ema_stream=ema_stream)
+        stack = SpinStack(lays, ema_stream=ema_stream, one_stream=one_stream)
 
         def stack_step(s):
             if evict is not None:
@@ -312,6 +312,8 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
     ms_stack, stk_layers = run_stack_mode(False)
     ms_stack_ema_stream, lays_ema_stream = (run_stack_mode(True) if "ema_stream" in modes
                                             else (None, None))
+    ms_one_stream, lays_one_stream = (run_stack_mode(False, one_stream=True)
+                                      if "one_stream" in modes else (None, None))
     budget = None
     if policy != "none":
         # the same schedule with per-layer budgets and dense probe steps; the
@@ -351,7 +353,7 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
                   "allocated_at_steps": [h[0] for h in bstack.level_history]}
         for lay in bud_layers:
             assert int(lay.err.item()) == 0
-    for other in (seq, lays_ema_stream):
+    for other in (seq, lays_ema_stream, lays_one_stream):
         if other is None:
             continue
         for a, b in zip(other, stk_layers):
@@ -382,6 +384,7 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
     keys0 = keys // w.layers
     n_sel0 = n_sel // w.layers
     return dict(ms_seq=ms_seq, ms_stack=ms_stack, ms_stack_ema_stream=ms_stack_ema_stream,
+                ms_one_stream=ms_one_stream,
                 keys_per_step=keys, n_sel=n_sel,
                 score_us_layer0=score_us, keys_layer0=keys0, n_sel_layer0=n_sel0,
                 budget=budget)
@@ -762,18 +765,20 @@ def stack_sweep(inp: StackInputs, steps: int, warmup: int, evict=None):
     t = a (1 - rho) + c of each."""
     w = inp.w
     out = {"us_per_step_layer": {}, "realized_sparsity": {}}
-    rho, t_seq, t_stk = [], [], []
+    rho, t_seq, t_stk, t_one = [], [], [], []
     for sp in sorted(set(w.sparsity_bp)):
-        res = run_stack(inp, sp, steps, warmup, evict, modes=("seq", "stack"))
+        res = run_stack(inp, sp, steps, warmup, evict, modes=("seq", "stack", "one_stream"))
         total_blocks = w.layers * int(sum(-(-int(c) // 64) for c in inp.ctx))
         r = 1.0 - res["n_sel"] / total_blocks
         rho.append(r)
         t_seq.append(res["ms_seq"] * 1e3 / w.layers)
         t_stk.append(res["ms_stack"] * 1e3 / w.layers)
-        out["us_per_step_layer"][str(sp)] = {"sequential": t_seq[-1], "stack": t_stk[-1]}
+        t_one.append(res["ms_one_stream"] * 1e3 / w.layers)
+        out["us_per_step_layer"][str(sp)] = {"sequential": t_seq[-1], "stack": t_stk[-1],
+                                             "one_stream": t_one[-1]}
         out["realized_sparsity"][str(sp)] = r
     A = np.stack([1.0 - np.array(rho), np.ones(len(rho))], 1)
-    for name, T in (("sequential", t_seq), ("stack", t_stk)):
+    for name, T in (("sequential", t_seq), ("stack", t_stk), ("one_stream", t_one)):
         (a, c), *_ = np.linalg.lstsq(A, np.array(T), rcond=None)
         out[f"fit_{name}_us"] = {"a": float(a), "c": float(c)}
     return out
@@ -817,6 +822,7 @@ def main_stack(args, w: G.Workload, sp: int):
                   "overlapped_us_per_step_layer": res["ms_stack"] * 1e3 / w.layers,
                   "overlapped_ema_stream_us_per_step_layer":
                       res["ms_stack_ema_stream"] * 1e3 / w.layers,
+                  "one_stream_us_per_step_layer": res["ms_one_stream"] * 1e3 / w.layers,
                   "per_layer_budgets": res["budget"]},
         "keys_scored_per_step": res["keys_per_step"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

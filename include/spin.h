@@ -301,9 +301,20 @@ spin_status spin_step_finish(const spin_config* cfg, const spin_batch* bt,
  * work on `main` is ordered after every layer's top-K; without ema_stream
  * also after every EMA update, with it the caller makes `main` wait for
  * ema_stream before it reads or writes a layer's EMA state or counters.
- * Deferred EMA is not available here.  Errors: SPIN_E_SHAPE when n is < 1 or
- * exceeds the stack's layers, or two streams are the same; each layer's
- * arguments are validated as for spin_step before anything is issued.
+ * Deferred EMA is not available here.
+ * With side_stream == NULL (and ema_stream == NULL) everything runs on `main`
+ * in layer order, with no events: layer l + 1's plan runs inside layer l's
+ * two launches -- its prediction in the last workgroups of the score launch,
+ * which start as the scoring workgroups leave their CUs, its selection in
+ * the last workgroups of the top-K + EMA launch -- when layer l's keys are
+ * fp8 or bf16 (its score kernel filters the top-K candidates) and layer l + 1
+ * has one verifier row; otherwise layer l + 1's plan is issued on its own
+ * before its finish.  Layer 0's plan always is.  order_after_main is then
+ * moot.  A stack may alternate between the two forms from call to call.
+ * Errors: SPIN_E_SHAPE when n is < 1 or exceeds the stack's layers, two
+ * streams are the same, or ema_stream is given without side_stream; each
+ * layer's arguments are validated as for spin_step before anything is
+ * issued.
  */
 typedef struct spin_stack spin_stack;
 spin_status spin_stack_create(int32_t n_layers, spin_stack** out);

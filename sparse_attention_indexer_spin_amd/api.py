@@ -163,14 +163,16 @@ def spin_stack_step(stack: Stack, cfgs, bts, ios, order_after_main: bool = False
                     main_stream=None, side_stream=None, ema_stream=None):
     """One decode step of len(cfgs) layers: plans on side_stream, finishes on
     main_stream (default: the current stream), EMA updates on ema_stream when
-    given (else inside the finishes)."""
+    given (else inside the finishes).  side_stream None: one stream, each
+    layer's plan inside the previous layer's launches where possible."""
     n = len(cfgs)
-    assert len(bts) == n and len(ios) == n and side_stream is not None
+    assert len(bts) == n and len(ios) == n
     ca = (L.SpinConfig * n)(*cfgs)
     ba = (L.SpinBatch * n)(*bts)
     ia = (L.SpinStepIO * n)(*ios)
     L.check(L.load().spin_stack_step(stack.handle, n, ca, ba, ia, int(bool(order_after_main)),
-                                     _stream(main_stream), side_stream.cuda_stream,
+                                     _stream(main_stream),
+                                     None if side_stream is None else side_stream.cuda_stream,
                                      None if ema_stream is None else ema_stream.cuda_stream))
 
 

@@ -26,7 +26,7 @@
 // several verifier rows, a stream of `rows` waves walks the same pages (one
 // row each); the page comes from HBM once and from L2 for the others.
 // Work is split into request-aligned contiguous runs of selected blocks.
-#include "spin_dev.h"
+#include "plan_dev.h"
 #include "spin_launch.h"
 
 namespace spin {
@@ -52,6 +52,10 @@ struct ScoreParams {
   int R, rows, max_blocks, n_pages;
   int32_t* err;
   CandSink sink;  // sink.hint == nullptr: no candidate output
+  // another layer's prediction run by the last plan_wgs workgroups of the
+  // launch, after the scoring workgroups (dispatched first) leave their CUs
+  PredictArgs plan;
+  int plan_wgs;
 };
 
 // Selected blocks of request r (0 for a request with invalid bounds).
@@ -922,15 +926,20 @@ template <int KT, int NS, int QB, int P, int Mode, bool WL>
 __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
   extern __shared__ int pre_dyn[];
   __shared__ int tmp[32];
+  const int gx = (int)gridDim.x - p.plan_wgs;  // scoring workgroups
+  if ((int)blockIdx.x >= gx) {  // the plan role: no barrier, no LDS
+    predict_wg(p.plan, (int)blockIdx.x - gx);
+    return;
+  }
   const int wave = threadIdx.x >> 6;
   const int spw = p.rows == 1 ? 4 : (p.rows == 2 ? 2 : 1);  // streams per workgroup
   const int row = wave % p.rows, stream_id = blockIdx.x * spw + wave / p.rows;
-  const int n_streams = gridDim.x * spw;
+  const int n_streams = gx * spw;
   if constexpr (Mode == kRunWave) {
     // Teams of workgroups: a workgroup's streams split its request-aligned
     // run, found by each wave on its own (no table), and share the request's
     // query rows through LDS, each wave converting rows of the 16-head tiles.
-    const Run run = wave_run(p, blockIdx.x, gridDim.x);
+    const Run run = wave_run(p, blockIdx.x, gx);
     if (run.lo >= run.hi) return;  // the whole workgroup: no barrier follows
     const int s = wave / p.rows, nb = run.hi - run.lo;
     const int lo = __builtin_amdgcn_readfirstlane(run.lo + s * nb / spw);
@@ -1048,7 +1057,7 @@ static void launch_wave_l(const ScoreParams& p, hipStream_t st) {
     const auto wave = k_score_wave<KT, NS, QB, P, kRunWave, WL>;
     const int g = min(resident_workgroups((const void*)wave, 256, stage), p.R * p.max_blocks);
     if (g >= p.R && lds_fits((const void*)wave, stage)) {
-      hipLaunchKernelGGL(wave, dim3(g), dim3(256), stage, st, p);
+      hipLaunchKernelGGL(wave, dim3(g + p.plan_wgs), dim3(256), stage, st, p);
       return;
     }
   }
@@ -1056,12 +1065,12 @@ static void launch_wave_l(const ScoreParams& p, hipStream_t st) {
   const auto aligned = k_score_wave<KT, NS, QB, P, kRunTable, WL>;
   const int g = min(resident_workgroups((const void*)aligned, 256, dyn), p.R * p.max_blocks);
   if (spw * g >= p.R) {  // a stream per request at least: request-aligned runs
-    hipLaunchKernelGGL(aligned, dim3(g), dim3(256), dyn, st, p);
+    hipLaunchKernelGGL(aligned, dim3(g + p.plan_wgs), dim3(256), dyn, st, p);
     return;
   }
   const auto span = k_score_wave<KT, NS, QB, P, kRunSpan, WL>;
   const int g2 = min(resident_workgroups((const void*)span, 256, dyn), p.R * p.max_blocks);
-  hipLaunchKernelGGL(span, dim3(g2), dim3(256), dyn, st, p);
+  hipLaunchKernelGGL(span, dim3(g2 + p.plan_wgs), dim3(256), dyn, st, p);
 }
 
 template <int KT, int NS, int QB>
@@ -1077,10 +1086,15 @@ bool score_filters(const spin_config& c, const spin_batch&) {
 hipError_t launch_score(const spin_config& c, const spin_batch& b, const void* q, const float* w,
                         const void* kp, const float* ks, const int32_t* pt, int64_t pt_ld,
                         const int32_t* sel, const int32_t* n_sel, float* z, int64_t z_ld,
-                        hipStream_t st, const CandSink* sink) {
+                        hipStream_t st, const CandSink* sink, const PredictPlan* plan) {
   ScoreParams p{q, w, kp, ks, pt, pt_ld, sel, n_sel, b.ctx_len, b.q_pos, z, z_ld,
                 b.batch, b.n_rows, b.max_blocks, b.n_pages, b.err, CandSink{}};
   if (sink && score_filters(c, b)) p.sink = *sink;
+  if (plan) {
+    if (!score_filters(c, b)) return hipErrorInvalidValue;  // MFMA kernels only
+    p.plan = plan->args;
+    p.plan_wgs = plan->wgs;
+  }
   if (c.key_dtype == SPIN_FP8_E4M3) {
     if (c.q_dtype == SPIN_BF16) launch_wave<0, 2, 1>(p, st);
     else launch_wave<0, 3, 0>(p, st);

@@ -470,12 +470,24 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select_pages(
 // flight; 16 made the 1,024-thread kernel spill)
 constexpr int kEmaChunk = 6;
 
+// SEPT > 0: the last `sel_wgs` workgroups select the blocks of another layer
+// (one verifier row, SEPT blocks per thread), one request each.
+template <int SEPT>
 __global__ __launch_bounds__(kSelThreads) void k_topk_ema(
     int K, int rows, int max_blocks, const int32_t* __restrict__ ctx,
     const int32_t* __restrict__ qpos, const float* __restrict__ z, int64_t z_ld,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
-    int32_t* __restrict__ out, TopkWs ws, int rows_total, EmaArgs A, int ema_x) {
-  __shared__ PagesShared L;
+    int32_t* __restrict__ out, TopkWs ws, int rows_total, EmaArgs A, int ema_x,
+    SelectArgs sa, SelectInputs si, int sel_wgs) {
+  __shared__ __align__(16) PagesShared L;
+  if constexpr (SEPT > 0) {
+    const int s0 = (int)gridDim.x - sel_wgs;
+    if ((int)blockIdx.x >= s0) {
+      static_assert(sizeof(SelectLds) <= sizeof(PagesShared), "LDS");
+      select_request<SEPT>(sa, si, (int)blockIdx.x - s0, *reinterpret_cast<SelectLds*>(&L));
+      return;
+    }
+  }
   if ((int)blockIdx.x < rows_total) {
     topk_pages_row(blockIdx.x, K, rows, max_blocks, ctx, qpos, z, z_ld, sel, n_sel, out, ws, L);
     return;
@@ -499,23 +511,45 @@ size_t step_workspace_bytes(const spin_config& c, int R, int rows, int max_block
          (size_t)align256(4LL * R);
 }
 
+template <int SEPT>
+static void topk_ema_t(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
+                       const int32_t* sel, const int32_t* n_sel, int32_t* out, const TopkWs& ws,
+                       const EmaArgs& A, const SelectArgs& sa, const SelectInputs& si,
+                       int sel_wgs, hipStream_t st) {
+  const int rows_total = b.batch * b.n_rows;
+  constexpr int per_block = (kSelThreads / 64) * kEmaChunk;
+  const int most = (b.max_blocks + per_block - 1) / per_block;
+  const int free_cus =
+      resident_workgroups((const void*)k_topk_ema<SEPT>, kSelThreads) - rows_total - sel_wgs;
+  const int ema_x = max(1, min(most, free_cus / max(1, b.batch)));
+  hipLaunchKernelGGL(k_topk_ema<SEPT>, dim3(rows_total + ema_x * b.batch + sel_wgs),
+                     dim3(kSelThreads), 0, st, c.topk, b.n_rows, b.max_blocks, b.ctx_len,
+                     A.qpos, z, z_ld, sel, n_sel, out, ws, rows_total, A, ema_x, sa, si,
+                     sel_wgs);
+}
+
 hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const float* z,
                            int64_t z_ld, const int32_t* sel, const int32_t* n_sel, int32_t* out,
                            void* wsp, const int32_t* n_valid, float* V, int64_t v_ld, float* D,
                            int64_t d_ld, float* vmax, const int32_t* qpos_snap,
-                           int32_t* qpos_out, int32_t* step_out, hipStream_t st) {
+                           int32_t* qpos_out, int32_t* step_out, hipStream_t st,
+                           const SelectPlan* next) {
   const int rows_total = b.batch * b.n_rows;
   const TopkWs ws = carve(wsp, rows_total, b.max_blocks);
-  constexpr int per_block = (kSelThreads / 64) * kEmaChunk;
-  const int most = (b.max_blocks + per_block - 1) / per_block;
-  const int free_cus = resident_workgroups((const void*)k_topk_ema, kSelThreads) - rows_total;
-  const int ema_x = max(1, min(most, free_cus / max(1, b.batch)));
   const EmaArgs A{c.ema_alpha, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap, n_valid, z, z_ld,
                   sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out, vmax,
                   (c.flags & SPIN_MTP_ROW0_UPDATE) != 0};
-  hipLaunchKernelGGL(k_topk_ema, dim3(rows_total + ema_x * b.batch), dim3(kSelThreads), 0, st,
-                     c.topk, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap, z, z_ld, sel, n_sel,
-                     out, ws, rows_total, A, ema_x);
+  if (!next) {
+    topk_ema_t<0>(c, b, z, z_ld, sel, n_sel, out, ws, A, SelectArgs{}, SelectInputs{}, 0, st);
+  } else {
+    const int n = next->requests;
+    switch (next->ept) {
+      case 1: topk_ema_t<1>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st); break;
+      case 2: topk_ema_t<2>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st); break;
+      case 4: topk_ema_t<4>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st); break;
+      default: topk_ema_t<8>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st); break;
+    }
+  }
   return hipGetLastError();
 }
 

@@ -344,6 +344,31 @@ spin_status issue_finish(const spin_config& c, const spin_batch& b, const spin_s
                     "spin_step/ema+advance");
 }
 
+// Score, top-K and the EMA update + counter advance of one layer (its
+// score kernel filters the top-K candidates), with the plan of layer `n`
+// (one verifier row) run inside the same two launches: its prediction by the
+// score launch's last workgroups, its selection by the top-K + EMA launch's.
+// The two layers share no data.
+spin_status issue_finish_with_plan(const spin_config& c, const spin_batch& b,
+                                   const spin_step_io& io, const spin_config& nc,
+                                   const spin_batch& nb, const spin_step_io& nio,
+                                   hipStream_t st) {
+  const spin::CandSink sink = spin::topk_sink(io.workspace, b.batch, b.n_rows, b.max_blocks);
+  const spin::PredictPlan pp = spin::predict_plan(nc, nb, nio.V, nio.v_ld, nio.D, nio.d_ld,
+                                                  nio.v_max, nio.S, step_qsnap(nc, nb, nio));
+  const spin::SelectPlan sp = spin::select_plan(nc, nb, nio.S, nio.budget, nio.row_code,
+                                                nio.sel, nio.n_sel);
+  SPIN_CHECK(hip_status(spin::launch_score(c, b, io.q, io.w, io.k_pages, io.k_scale,
+                                           io.page_table, io.pt_ld, io.sel, io.n_sel, io.z,
+                                           io.z_ld, st, &sink, &pp),
+                        "spin_stack_step/score+predict"));
+  return hip_status(spin::launch_topk_ema(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.topk_idx,
+                                          io.workspace, io.n_valid, io.V, io.v_ld, io.D,
+                                          io.d_ld, io.v_max, step_qsnap(c, b, io),
+                                          io.q_pos_mut, io.step_mut, st, &sp),
+                    "spin_stack_step/topk+ema+select");
+}
+
 // The EMA update + counter advance of a finished step (after a finish with
 // defer_ema): q positions from the step's snapshot.
 spin_status issue_ema(const spin_config& c, const spin_batch& b, const spin_step_io& io,
@@ -366,6 +391,7 @@ struct spin_stack {
   int32_t n_layers = 0;
   int device = 0;
   int32_t prev_h = 0;            // group split of the previous call
+  bool one_stream_last = false;  // the previous call ran on one stream
   hipEvent_t plan_done[2] = {nullptr, nullptr};
   hipEvent_t finish_done[2] = {nullptr, nullptr};
   hipEvent_t ema_done[2] = {nullptr, nullptr};   // with an EMA stream
@@ -508,8 +534,10 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
   if (!stack || !cfgs || !bts || !ios) return fail(SPIN_E_NULL, "%s: NULL argument", fn);
   if (n_layers < 1 || n_layers > stack->n_layers)
     return fail(SPIN_E_SHAPE, "%s: n_layers %d outside [1, %d]", fn, n_layers, stack->n_layers);
-  if (main_stream == side_stream || (ema_stream && (ema_stream == main_stream ||
-                                                     ema_stream == side_stream)))
+  if (!side_stream && ema_stream)
+    return fail(SPIN_E_SHAPE, "%s: an EMA stream needs a side stream", fn);
+  if (side_stream && (main_stream == side_stream ||
+                      (ema_stream && (ema_stream == main_stream || ema_stream == side_stream))))
     return fail(SPIN_E_SHAPE, "%s: main, side and ema must be different streams", fn);
   int dev = -1;
   SPIN_CHECK(hip_status(hipGetDevice(&dev), fn));
@@ -522,11 +550,36 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
     SPIN_CHECK(check_step(lfn, &cfgs[l], &bts[l], &ios[l]));
   }
   hipStream_t mst = (hipStream_t)main_stream, sst = (hipStream_t)side_stream;
+  if (!sst) {
+    // one stream: layer l + 1's plan inside layer l's score and top-K + EMA
+    // launches where both allow it (layer l's score kernel filters, layer
+    // l + 1 has one verifier row), else on its own before its finish
+    bool planned = false;  // this layer's plan was issued inside the previous launches
+    for (int l = 0; l < n_layers; ++l) {
+      if (bts[l].batch <= 0) {
+        planned = false;
+        continue;
+      }
+      if (!planned) SPIN_CHECK(issue_plan(cfgs[l], bts[l], ios[l], mst));
+      const int m = l + 1;
+      const bool fuse = m < n_layers && bts[m].batch > 0 && bts[m].n_rows == 1 &&
+                        spin::score_filters(cfgs[l], bts[l]);
+      if (fuse)
+        SPIN_CHECK(issue_finish_with_plan(cfgs[l], bts[l], ios[l], cfgs[m], bts[m], ios[m], mst));
+      else
+        SPIN_CHECK(issue_finish(cfgs[l], bts[l], ios[l], 0, mst));
+      planned = fuse;
+    }
+    stack->one_stream_last = true;
+    return SPIN_OK;
+  }
   auto wait = [&](hipStream_t st, hipEvent_t e) {
     return hip_status(hipStreamWaitEvent(st, e, 0), fn);
   };
   auto record = [&](hipEvent_t e, hipStream_t st) { return hip_status(hipEventRecord(e, st), fn); };
-  if (order_after_main) {  // plan inputs the caller wrote on main
+  // after a one-stream call the stack's events describe an older call: the
+  // side stream then starts after everything issued on main
+  if (order_after_main || stack->one_stream_last) {  // or plan inputs the caller wrote on main
     SPIN_CHECK(record(stack->entry, mst));
     SPIN_CHECK(wait(sst, stack->entry));
   }
@@ -569,6 +622,7 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
     if (est) SPIN_CHECK(record(stack->ema_done[1], est));
   }
   stack->prev_h = h;
+  stack->one_stream_last = false;
   return SPIN_OK;
 }
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include "spin.h"
+#include "plan_dev.h"
 
 namespace spin {
 
@@ -26,6 +27,23 @@ struct CandSink {
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
                           const float* D, int64_t d_ld, const float* vmax, float* S,
                           hipStream_t st, int32_t* qpos_snap = nullptr);
+// A layer's plan (one verifier row) run inside another layer's launches:
+// its prediction by the last workgroups of a score launch, its selection by
+// the last workgroups of a top-K + EMA launch.
+struct PredictPlan {
+  PredictArgs args;
+  int wgs;
+};
+struct SelectPlan {
+  SelectArgs args;
+  SelectInputs in;
+  int requests, ept;
+};
+PredictPlan predict_plan(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
+                         const float* D, int64_t d_ld, const float* vmax, float* S,
+                         int32_t* qpos_snap);
+SelectPlan select_plan(const spin_config& c, const spin_batch& b, const float* S,
+                       const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel);
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
                          hipStream_t st);
@@ -34,7 +52,8 @@ hipError_t launch_select(const spin_config& c, const spin_batch& b, const float*
 hipError_t launch_score(const spin_config& c, const spin_batch& b, const void* q, const float* w,
                         const void* kp, const float* ks, const int32_t* pt, int64_t pt_ld,
                         const int32_t* sel, const int32_t* n_sel, float* z, int64_t z_ld,
-                        hipStream_t st, const CandSink* sink = nullptr);
+                        hipStream_t st, const CandSink* sink = nullptr,
+                        const PredictPlan* plan = nullptr);
 bool score_filters(const spin_config& c, const spin_batch& b);
 hipError_t launch_topk(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                        const int32_t* sel, const int32_t* n_sel, int32_t* out, void* ws,
@@ -46,7 +65,8 @@ hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const floa
                            int64_t z_ld, const int32_t* sel, const int32_t* n_sel, int32_t* out,
                            void* ws, const int32_t* n_valid, float* V, int64_t v_ld, float* D,
                            int64_t d_ld, float* vmax, const int32_t* qpos_snap,
-                           int32_t* qpos_out, int32_t* step_out, hipStream_t st);
+                           int32_t* qpos_out, int32_t* step_out, hipStream_t st,
+                           const SelectPlan* next = nullptr);
 // The candidate sink inside a top-K workspace.
 CandSink topk_sink(void* ws, int R, int rows, int max_blocks);
 size_t topk_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks);

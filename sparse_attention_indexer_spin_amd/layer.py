@@ -113,8 +113,12 @@ class SpinStack:
     first probe every layer runs at the target level."""
 
     def __init__(self, layers, device="cuda", budget_policy=None, probe_period: int = 8,
-                 levels: int = 100, ema_stream: bool = False):
+                 levels: int = 100, ema_stream: bool = False, one_stream: bool = False):
         self.layers = list(layers)
+        # one_stream: every layer's plan inside the previous layer's score and
+        # top-K + EMA launches on the main stream (no side stream, no events)
+        assert not (one_stream and ema_stream)
+        self.one_stream = one_stream
         self.stack = api.Stack(len(self.layers))
         # default priority (streams of another priority are not used)
         self.side = torch.cuda.Stream(device=device)
@@ -243,7 +247,9 @@ class SpinStack:
                                    None if n_valid is None else n_valid[l],
                                    None if budgets is None else budgets[l]))
         api.spin_stack_step(self.stack, cfgs, bts, ios, order_after_main=self._order_next,
-                            main_stream=stream, side_stream=self.side, ema_stream=self.ema)
+                            main_stream=stream,
+                            side_stream=None if self.one_stream else self.side,
+                            ema_stream=self.ema)
         self._order_next = False
         if probe:
             st = torch.cuda.current_stream() if stream is None else stream

@@ -80,8 +80,9 @@ def test_budget_fill_parity():
             assert out.cpu().tolist() == want, (levels, g)
 
 
-@pytest.mark.parametrize("policy", ["minimax", "proportional"])
-def test_stack_budgets_match_oracle_reference(policy):
+@pytest.mark.parametrize("policy,one_stream", [("minimax", False), ("proportional", False),
+                                               ("proportional", True)])
+def test_stack_budgets_match_oracle_reference(policy, one_stream):
     """SpinStack with probes every 3 steps against sequential spin_step layers
     whose budgets come from the oracle: oracle miss curves of the same probe
     outputs, oracle allocation, applied from the second step after the probe."""
@@ -94,7 +95,8 @@ def test_stack_budgets_match_oracle_reference(policy):
     keys = [device_keys(li) for li in lis]
     seq = [make_layer(li, sp) for li in lis]
     stk = [make_layer(li, sp) for li in lis]
-    stack = SpinStack(stk, budget_policy=policy, probe_period=P, levels=levels)
+    stack = SpinStack(stk, budget_policy=policy, probe_period=P, levels=levels,
+                      one_stream=one_stream)
     target = (10000 - sp) // 100
     ref_levels, history, pending, miss_sum, n_probes = [target] * L, [], None, [0.0] * L, 0
     Bs = [O.n_blocks(int(c)) for c in lis[0].ctx]

@@ -35,9 +35,10 @@ def _state(lay):
 
 
 @pytest.mark.parametrize("integer", [False, True])
-@pytest.mark.parametrize("ema_stream", [True, False])
-def test_stack_matches_sequential_steps(integer, ema_stream):
-    banner(f"stack vs sequential integer={integer} ema_stream={ema_stream}")
+@pytest.mark.parametrize("mode", ["side", "side+ema", "one_stream"])
+def test_stack_matches_sequential_steps(integer, mode):
+    banner(f"stack vs sequential integer={integer} mode={mode}")
+    ema_stream, one_stream = mode == "side+ema", mode == "one_stream"
     from sparse_attention_indexer_spin_amd import SpinStack, api as A
     n_layers = 3
     w = _workload(n_layers)
@@ -46,7 +47,7 @@ def test_stack_matches_sequential_steps(integer, ema_stream):
     seq = [make_layer(li, 4000) for li in lis]
     stk_layers = [make_layer(li, 4000) for li in lis]
     split = [make_layer(li, 4000) for li in lis]
-    stack = SpinStack(stk_layers, ema_stream=ema_stream)
+    stack = SpinStack(stk_layers, ema_stream=ema_stream, one_stream=one_stream)
     torch.cuda.synchronize()
     for s in range(w.steps):
         qs = [li.q[s].to(DEV).contiguous() for li in lis]
@@ -79,10 +80,11 @@ def test_stack_matches_sequential_steps(integer, ema_stream):
             assert np.array_equal(stk_layers[l].V.cpu().numpy()[r, :N], states[r].V[:N]), (l, r)
 
 
-def test_stack_reuse_after_reset_and_fewer_layers():
+@pytest.mark.parametrize("one_stream", [False, True])
+def test_stack_reuse_after_reset_and_fewer_layers(one_stream):
     """A reset between steps (announced with inputs_changed) and a step over a
     prefix of the layers: still identical to sequential spin_step calls."""
-    banner("stack reset / layer prefix")
+    banner(f"stack reset / layer prefix one_stream={one_stream}")
     from sparse_attention_indexer_spin_amd import SpinStack
     n_layers = 4
     w = _workload(n_layers, steps=5)
@@ -90,7 +92,7 @@ def test_stack_reuse_after_reset_and_fewer_layers():
     keys = [device_keys(li) for li in lis]
     seq = [make_layer(li, 3000) for li in lis]
     stk_layers = [make_layer(li, 3000) for li in lis]
-    stack = SpinStack(stk_layers)
+    stack = SpinStack(stk_layers, one_stream=one_stream)
     for s in range(w.steps):
         qs = [li.q[s].to(DEV).contiguous() for li in lis]
         ws = [li.weights.to(DEV) for li in lis]
@@ -109,3 +111,29 @@ def test_stack_reuse_after_reset_and_fewer_layers():
         for l in range(n_layers):
             for x, y in zip(_state(seq[l]), _state(stk_layers[l])):
                 assert torch.equal(x, y), f"step {s} layer {l}"
+
+
+def test_stack_switches_between_one_and_two_streams():
+    """Steps alternating the one-stream and the side-stream schedules on one
+    stack: identical to sequential spin_step calls (a two-stream call after a
+    one-stream call orders its plans after everything issued on main)."""
+    banner("stack mode switch")
+    from sparse_attention_indexer_spin_amd import SpinStack
+    n_layers = 3
+    w = _workload(n_layers, steps=6)
+    lis = [build_layer(w, layer=l) for l in range(n_layers)]
+    keys = [device_keys(li) for li in lis]
+    seq = [make_layer(li, 4000) for li in lis]
+    stk_layers = [make_layer(li, 4000) for li in lis]
+    stack = SpinStack(stk_layers)
+    for s in range(w.steps):
+        stack.one_stream = s % 2 == 0
+        qs = [li.q[s].to(DEV).contiguous() for li in lis]
+        ws = [li.weights.to(DEV) for li in lis]
+        for l in range(n_layers):
+            seq[l].step(qs[l], ws[l], *keys[l])
+        stack.step(qs, ws, [k[0] for k in keys], [k[1] for k in keys], [k[2] for k in keys])
+    torch.cuda.synchronize()
+    for l in range(n_layers):
+        for x, y in zip(_state(seq[l]), _state(stk_layers[l])):
+            assert torch.equal(x, y), f"layer {l}"
