@@ -600,7 +600,8 @@ def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, budget_s: float,
 
 
 SCORE_SOURCES = ("sparse_attention_indexer_spin_amd/csrc/k_score.hip",
-                 "sparse_attention_indexer_spin_amd/csrc/spin_dev.h", "include/spin.h")
+                 "sparse_attention_indexer_spin_amd/csrc/spin_dev.h",
+                 "sparse_attention_indexer_spin_amd/csrc/plan_dev.h", "include/spin.h")
 
 
 def score_source_hash() -> str:

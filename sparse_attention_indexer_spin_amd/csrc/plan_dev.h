@@ -200,8 +200,10 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int r, int row, 
 // top-K + EMA launch), one verifier row.
 // ---------------------------------------------------------------------------
 // Prediction: workgroup w of n covers request w / per_req, blocks
-// [128 (w % per_req), + 128): 4 waves x kPredGroups groups of 8 blocks.
-constexpr int kPredGroups = 4;
+// [32 kPredGroups (w % per_req), + 32 kPredGroups): 4 waves x kPredGroups
+// groups of 8 blocks.  One group per workgroup (as k_predict) beat 2 and 4:
+// the many small workgroups fill the CUs the scoring workgroups leave.
+constexpr int kPredGroups = 1;
 constexpr int kPredBlocksPerWg = 4 * kPredGroups * kPredBlocksPerWave;
 
 struct PredictArgs {
