@@ -36,9 +36,13 @@ Readings where the pages are silent (each is listed in the design doc):
   * If m < n_f (only possible for B <= 2 blocks budgets), the forced blocks are
     still all kept.
   * Step t = 0 after a reset scores every block (dense warm-up).
-  * The indexer score is evaluated in fp64 from the decoded inputs (fp8 keys
-    dequantised as code * scale).  Everything downstream of the score (top-K,
-    EMA) consumes it rounded to fp32, the storage precision of the state.
+  * With bf16 or fp8 keys the indexer score is evaluated in fp64 from the
+    decoded inputs (fp8 keys dequantised as code * scale).  Everything
+    downstream of the score (top-K, EMA) consumes it rounded to fp32, the
+    storage precision of the state.
+  * With fp32 keys and fp32 queries (the exact mode) the score is one
+    canonical fp32 evaluation: per head a sequential fmaf chain over the 128
+    dims, ReLU, then a sequential fmaf chain over the heads (score_f32.c).
   * EMA in fp32 with three roundings: V' = fl(fl(a*V) + fl(b*z)), b = fl(1 - a).
   * top-K returns min(K, |dom|) slot ids in ascending order, padded with -1.
   * MTP: each row predicts its own mask; the union is scored for every row;
@@ -278,6 +282,14 @@ def decode_q(q, q_dtype: str):
     raise ValueError(q_dtype)
 
 
+def index_scores_exact_f32(q, w, keys):
+    """z[i] = sum_h w_h * ReLU(q_h . k_i) in the canonical fp32 order (exact
+    mode, fp32 keys and queries): see oracle/score_f32.c.  Returns fp32 [n]."""
+    from .score_f32 import index_scores_f32
+    return index_scores_f32(np.asarray(q, dtype=np.float32), np.asarray(w, dtype=np.float32),
+                            np.asarray(keys, dtype=np.float32))
+
+
 def index_scores(q, w, keys):
     """z[i] = sum_h w_h * ReLU(q_h . k_i) in float64.
 
@@ -341,11 +353,14 @@ def spin_step(state: RequestState, *, q, q_dtype, w, pages, page_table_row, key_
               alpha: float, layer: int, req_id: int, seed: int, combine: str = "max",
               n_valid=None, budget=None, defer=False, pooling: str = "max",
               mtp_row0_mask: bool = False, mtp_row0_update: bool = False,
-              explore_per_row: bool = False):
+              explore_per_row: bool = False, exact_f32: bool = True):
     """One SPIN decode step for one request: predict, select, union, score, top-K, EMA.
 
     q: [rows, n_h, d] (raw f32 or bf16 codes), w: [rows, n_h].
     Returns a dict with codes [rows, B], sel, slots, z64 [rows, n], z32, topk [rows, K].
+    z32 is what top-K and the EMA consume: the fp64 score rounded to fp32, or,
+    with fp32 keys and queries and exact_f32 (the default), the canonical fp32
+    evaluation of index_scores_exact_f32.
     The EMA update uses rows 0..n_valid-1 (all rows when n_valid is None) unless
     defer=True, in which case the caller replays later with ema_update.
     Variants (the paper's ablations, Sec. 4.5 and 4.6; defaults = the method):
@@ -367,7 +382,10 @@ def spin_step(state: RequestState, *, q, q_dtype, w, pages, page_table_row, key_
     slots = union_slots(sel, n_slots)
     keys = gather_keys(pages, page_table_row, slots, key_dtype, scale)
     z64 = np.stack([index_scores(qd[r], w[r], keys) for r in range(rows)])
-    z32 = canon32(z64)
+    if key_dtype == "f32" and q_dtype == "f32" and exact_f32:
+        z32 = np.stack([index_scores_exact_f32(qd[r], w[r], keys) for r in range(rows)])
+    else:
+        z32 = canon32(z64)
     top = np.stack([topk_slots(z32[r], slots, K) for r in range(rows)])
     if not defer:
         ema_update(state.V, state.D, z32, slots, q_pos,

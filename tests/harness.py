@@ -50,8 +50,10 @@ d_capacity = G.d_capacity
 
 
 def run_oracle(li: LayerInputs, n_steps: int, sparsity_bp: int, reqs=None, seed=G.PHILOX_SEED,
-               combine=None, states=None, **variants):
-    """Closed-loop oracle over n_steps; returns per-step lists of per-request results."""
+               combine=None, states=None, keep_state_history=False, **variants):
+    """Closed-loop oracle over n_steps; returns per-step lists of per-request results.
+    keep_state_history: each result also holds "state_after", copies of the
+    request's (V, D) after the step."""
     w = li.w
     reqs = range(w.batch) if reqs is None else reqs
     pages = li.np_pages()
@@ -72,6 +74,8 @@ def run_oracle(li: LayerInputs, n_steps: int, sparsity_bp: int, reqs=None, seed=
                               explore_bp=w.explore_bp, alpha=w.alpha, layer=li.layer,
                               req_id=r, seed=seed, combine=combine or w.combine,
                               n_valid=int(li.accept[s, r]), **variants)
+            if keep_state_history:
+                res["state_after"] = (states[r].V.copy(), states[r].D.copy())
             step_res[r] = res
         out.append(step_res)
     return out, states

@@ -4,6 +4,7 @@ forms, invariants, or an independent library routine).  CPU only."""
 import os
 import shutil
 import subprocess
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -253,6 +254,112 @@ def test_score_structure():
     d = k @ q[5]
     assert np.array_equal(O.index_scores(q2, w1, k) - z1,
                           w1[5] * (np.maximum(-d, 0) - np.maximum(d, 0)))
+
+
+# --- exact fp32 mode: the canonical fp32 order (oracle/score_f32.c) -------
+def _round_f32(x: Fraction) -> float:
+    """Round an exact rational to the nearest fp32 (ties to even), written
+    from the definition of IEEE-754 binary32 (24-bit significand, emin -126,
+    subnormal quantum 2^-149); no float arithmetic is involved."""
+    if x == 0:
+        return 0.0
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    quantum = Fraction(2) ** (e - 23)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = fl * quantum
+    assert v < Fraction(2) ** 128, "overflow"
+    return sign * float(v)           # v is an fp32 value: exact in a Python float
+
+
+def _exact_chain_z(q, w, k):
+    """z of one slot in the canonical order, each fma rounded from the exact
+    rational a*b + c (the definition of a fused multiply-add)."""
+    z = Fraction(0)
+    for h in range(q.shape[0]):
+        s = Fraction(0)
+        for c in range(q.shape[1]):
+            s = Fraction(_round_f32(Fraction(float(q[h, c])) * Fraction(float(k[c])) + s))
+        r = s if s > 0 else Fraction(0)
+        z = Fraction(_round_f32(Fraction(float(w[h])) * r + z))
+    return np.float32(float(z))
+
+
+def test_fmaf_rounds_once():
+    from oracle.score_f32 import fmaf
+    a = np.float32(1 + 2.0 ** -12)
+    # a*a = 1 + 2^-11 + 2^-24 is halfway between two fp32 neighbours; a tiny
+    # addend decides the direction.  A product and sum rounded to fp64 first
+    # would lose it and round the tie to even instead.
+    up, down = np.float32(1 + 2.0 ** -11 + 2.0 ** -23), np.float32(1 + 2.0 ** -11)
+    assert fmaf(a, a, np.float32(2.0 ** -60)) == up
+    assert fmaf(a, a, np.float32(-(2.0 ** -60))) == down
+    assert np.float32(np.float64(a) * np.float64(a) + 2.0 ** -60) == down  # double rounding
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        x, y, c = (np.float32(v) for v in rng.standard_normal(3) * 2.0 ** rng.integers(-8, 8, 3))
+        want = _round_f32(Fraction(float(x)) * Fraction(float(y)) + Fraction(float(c)))
+        assert fmaf(x, y, c) == np.float32(want)
+
+
+def test_exact_f32_score_matches_rational_chain():
+    """Gaussian inputs of the tiny workload's shape: the C oracle's canonical
+    fp32 chain equals the chain evaluated with exact rationals and rounded per
+    the fp32 definition, bit for bit."""
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((64, 128)).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, 64).astype(np.float32)
+    k = rng.standard_normal((6, 128)).astype(np.float32)
+    z = O.index_scores_exact_f32(q, w, k)
+    for i in range(k.shape[0]):
+        assert z[i] == _exact_chain_z(q, w, k[i]), i
+
+
+def test_exact_f32_score_hand_and_integer_inputs():
+    g = read_golden("score_hand.txt")
+    q = np.array(g["q"], dtype=np.float32).reshape(2, 2)
+    w = np.array(g["w"], dtype=np.float32)
+    k = np.array(g["k"], dtype=np.float32).reshape(3, 2)
+    assert np.array_equal(O.index_scores_exact_f32(q, w, k), np.array(g["z"], dtype=np.float32))
+    # small integers: every partial sum is exact in fp32, so the chain equals
+    # the fp64 definition exactly
+    rng = np.random.default_rng(13)
+    q = rng.integers(-4, 5, (64, 128)).astype(np.float32)
+    k = rng.integers(-4, 5, (200, 128)).astype(np.float32)
+    w = (rng.integers(1, 5, 64) * 0.5).astype(np.float32)
+    assert np.array_equal(O.index_scores_exact_f32(q, w, k),
+                          O.index_scores(q, w, k).astype(np.float32))
+
+
+def test_exact_f32_score_within_fp32_error_bound():
+    """|z32 - z| within the standard bound for recursive summation with fma
+    (gamma_n = n u / (1 - n u), u = 2^-24): per head gamma_128 sum_c |q_c k_c|,
+    then the head sum adds gamma_64 sum_h w_h |r_h| and scales the head errors
+    by (1 + gamma_64)."""
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((64, 128)).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, 64).astype(np.float32)
+    k = rng.standard_normal((500, 128)).astype(np.float32)
+    u = 2.0 ** -24
+    g = lambda n: n * u / (1 - n * u)
+    qd, kd, wd = q.astype(np.float64), k.astype(np.float64), w.astype(np.float64)
+    z64 = O.index_scores(qd, wd, kd)
+    absdot = np.abs(kd) @ np.abs(qd).T                      # [n, n_h]
+    r = np.maximum(kd @ qd.T, 0)
+    bound = (1 + g(64)) * g(128) * (absdot @ wd) + g(64) * (r @ wd)
+    err = np.abs(O.index_scores_exact_f32(q, w, k).astype(np.float64) - z64)
+    assert np.all(err <= bound)
+    assert err.max() > 0                    # the fp32 chain is not the fp64 value
 
 
 def test_fp8_scale_pulls_out_of_relu():
