@@ -255,6 +255,24 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
                       int32_t defer_ema, void* stream);
 
 /*
+ * spin_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same step, bit for bit, with io->workspace and io->workspace_bytes ignored.
+ * Its workspace is a static device array of SPIN_NOALLOC_WORKSPACE_BYTES
+ * inside the library, one per GPU, held until the process ends; the call
+ * itself allocates and frees nothing.  Shapes whose spin_workspace_bytes()
+ * exceeds that size return SPIN_E_WORKSPACE.  Every call on a GPU shares that
+ * GPU's array and its contents carry over between calls (only top-K
+ * threshold hints, which change speed, not results), so calls that may
+ * overlap on one GPU -- on different streams, or from different threads --
+ * race and must not be issued; issue them on one stream, or use spin_step
+ * with a workspace per caller.
+ */
+#define SPIN_NOALLOC_WORKSPACE_BYTES (160u * 1024u * 1024u)
+spin_status spin_step_noalloc(const spin_config* cfg, const spin_batch* bt,
+                              const spin_step_io* io, int32_t defer_ema, void* stream);
+
+/*
  * The two halves of spin_step, for callers that overlap them.  Block
  * prediction needs only the EMA state, not the current query, so it can be
  * scheduled off the critical path (paper Sec. 3.2, after Eq. 2; blog, "Score

@@ -24,7 +24,8 @@ EXPORTS = ["spin_predict_blocks", "spin_select_blocks", "spin_sparse_index_score
            "spin_ema_update", "spin_advance", "spin_reset_state", "spin_step",
            "spin_workspace_bytes", "spin_last_error", "spin_step_plan", "spin_step_finish",
            "spin_stack_create", "spin_stack_destroy", "spin_stack_step", "spin_miss_curve",
-           "spin_budget_fill", "spin_budget_allocate"]
+           "spin_budget_fill", "spin_budget_allocate", "spin_step_noalloc"]
+SPIN_NOALLOC_WORKSPACE_BYTES = 160 * 1024 * 1024
 SPIN_BUDGET_MINIMAX, SPIN_BUDGET_PROPORTIONAL = 0, 1
 SPIN_POOL_MAX, SPIN_POOL_TOP4, SPIN_POOL_MEAN = 0, 1, 2
 SPIN_MTP_ROW0_MASK, SPIN_MTP_ROW0_UPDATE, SPIN_EXPLORE_PER_ROW = 4, 8, 16
@@ -78,6 +79,7 @@ def load() -> C.CDLL:
         "spin_advance": [I32, I32, P, P, P, P],
         "spin_reset_state": [I32, P, I64, P, I64, P, I64, P, P],
         "spin_step": [cfg, bt, C.POINTER(SpinStepIO), I32, P],
+        "spin_step_noalloc": [cfg, bt, C.POINTER(SpinStepIO), I32, P],
         "spin_step_plan": [cfg, bt, C.POINTER(SpinStepIO), P],
         "spin_step_finish": [cfg, bt, C.POINTER(SpinStepIO), I32, P],
         "spin_stack_create": [I32, C.POINTER(P)],

@@ -130,6 +130,12 @@ def spin_step(cfg, bt, io, defer_ema: bool = False, stream=None):
                                _stream(stream)))
 
 
+def spin_step_noalloc(cfg, bt, io, defer_ema: bool = False, stream=None):
+    """spin_step on the library's static scratch (io's workspace is ignored)."""
+    L.check(L.load().spin_step_noalloc(C.byref(cfg), C.byref(bt), C.byref(io),
+                                       int(bool(defer_ema)), _stream(stream)))
+
+
 def spin_step_plan(cfg, bt, io, stream=None):
     L.check(L.load().spin_step_plan(C.byref(cfg), C.byref(bt), C.byref(io), _stream(stream)))
 

@@ -480,6 +480,65 @@ spin_status spin_step(const spin_config* cfg, const spin_batch* bt, const spin_s
   return issue_finish(*cfg, *bt, *io, defer_ema, (hipStream_t)stream);
 }
 
+}  // extern "C"
+
+// Device scratch of spin_step_noalloc: the workspace of a whole step for
+// callers that cannot allocate device memory.  One copy per GPU, held until
+// the process ends; host code uses only the address hipGetSymbolAddress
+// returns for the current device, never this name.
+static __device__ __align__(256) unsigned char scratch[SPIN_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices] = {};
+hipError_t g_scratch_err[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device (with
+// that device current) on the first call made on it.
+spin_status scratch_of_current_device(const char* fn, void** out) {
+  int dev = -1;
+  SPIN_CHECK(hip_status(hipGetDevice(&dev), fn));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SPIN_E_UNSUPPORTED, "%s: device %d beyond the %d this build tracks", fn, dev,
+                kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_status(g_scratch_err[dev], fn);
+  if (!g_scratch_ptr[dev]) return fail(SPIN_E_HIP, "%s: no scratch address on device %d", fn, dev);
+  *out = g_scratch_ptr[dev];
+  return SPIN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+spin_status spin_step_noalloc(const spin_config* cfg, const spin_batch* bt,
+                              const spin_step_io* io, int32_t defer_ema, void* stream) {
+  const char* fn = "spin_step_noalloc";
+  SPIN_CHECK(check_config(fn, cfg));
+  SPIN_CHECK(check_batch(fn, bt));
+  SPIN_REQUIRE(io);
+  const size_t need = spin::step_workspace_bytes(*cfg, bt->batch, bt->n_rows, bt->max_blocks);
+  if (need > (size_t)SPIN_NOALLOC_WORKSPACE_BYTES)
+    return fail(SPIN_E_WORKSPACE,
+                "%s: this shape needs %zu bytes of workspace, above the %zu bytes of the "
+                "library's static scratch (use spin_step with a caller workspace)",
+                fn, need, (size_t)SPIN_NOALLOC_WORKSPACE_BYTES);
+  void* ws = nullptr;
+  SPIN_CHECK(scratch_of_current_device(fn, &ws));
+  spin_step_io own = *io;
+  own.workspace = ws;
+  own.workspace_bytes = SPIN_NOALLOC_WORKSPACE_BYTES;
+  SPIN_CHECK(check_step(fn, cfg, bt, &own));
+  if (bt->batch == 0) return SPIN_OK;
+  SPIN_CHECK(issue_plan(*cfg, *bt, own, (hipStream_t)stream));
+  return issue_finish(*cfg, *bt, own, defer_ema, (hipStream_t)stream);
+}
+
 spin_status spin_step_plan(const spin_config* cfg, const spin_batch* bt, const spin_step_io* io,
                            void* stream) {
   SPIN_CHECK(check_step("spin_step_plan", cfg, bt, io));
