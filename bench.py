@@ -53,7 +53,10 @@ def parse():
     ap.add_argument("--workload", default="fp8_128k_b32")
     ap.add_argument("--sparsity-bp", type=int, default=None)
     ap.add_argument("--sweep", action="store_true",
-                    help="also time the workload's sparsity sweep and fit t = a(1-rho) + c")
+                    help="--stack: time the workload's sparsity sweep and fit t = a(1-rho) + c")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the fixed-cost section (the sparsity sweep with its fits)")
+    ap.add_argument("--sweep-runs", type=int, default=3)
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--cache", choices=["rotate", "cold", "warm"], default="rotate",
                     help="rotate: step --copies independent copies of the workload round robin "
@@ -62,7 +65,7 @@ def parse():
                          "stage launch, each timed alone; warm: one copy back to back")
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-max-requests", type=int, default=32)
     ap.add_argument("--stack", action="store_true",
                     help="multi-layer workloads: time whole decode steps of every layer, one "
@@ -473,6 +476,41 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
             assert torch.equal(lay.topk_idx, lays[0].topk_idx), "stack and spin_step disagree"
         out["stack_ms_per_step"] = t0.elapsed_time(t1) / (steps * copies)
     del slays, stack
+    if w.rows == 1:
+        # one spin_step per copy captured in a HIP graph, replayed round robin
+        gl = []
+        for c in range(copies):
+            lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks,
+                            d_cap=G.d_capacity(w, steps + warmup + 1), topk=w.topk,
+                            sparsity_bp=sparsity_bp, n_rows=1, explore_bp=w.explore_bp,
+                            ema_alpha=w.alpha, combine=w.combine,
+                            key_dtype={"fp8": torch.uint8, "bf16": torch.bfloat16,
+                                       "f32": torch.float32}[w.key_dtype],
+                            q_dtype=torch.bfloat16 if w.q_dtype == "bf16" else torch.float32)
+            lay.set_requests(inp.ctx.cuda(), inp.pos[0].cuda())
+            lay.reset()
+            gl.append(lay)
+        for s in range(warmup):
+            for c in range(copies):
+                gl[c].step(inp.q[s], inp.weights, pages[c], scales[c], pt)
+        torch.cuda.synchronize()
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                gl[c].step(inp.q[warmup], inp.weights, pages[c], scales[c], pt)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for s in range(steps):
+            for g in graphs:
+                g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        for lay in gl:
+            assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
+        out["graph_ms_per_step"] = t0.elapsed_time(t1) / (steps * copies)
+        del graphs, gl
     if stage_reps:
         q = inp.q[warmup + steps - 1]
         last_nv = nv[-1]
@@ -486,7 +524,11 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
                 lay.cfg, bt, lay.V, lay.D, lay.S, v_max=lay.v_max)),
             "select": per_copy(lambda c, lay, bt: lambda: api.spin_select_blocks(
                 lay.cfg, bt, lay.S, lay.row_code, lay.sel, lay.n_sel)),
+            # the kernel spin_step runs (it also filters the top-K candidates)
             "score": per_copy(lambda c, lay, bt: lambda: api.spin_sparse_index_score(
+                lay.cfg, bt, q, inp.weights, pages[c], scales[c], pt, lay.sel, lay.n_sel,
+                lay.z, workspace=lay.workspace)),
+            "score_no_filter": per_copy(lambda c, lay, bt: lambda: api.spin_sparse_index_score(
                 lay.cfg, bt, q, inp.weights, pages[c], scales[c], pt, lay.sel, lay.n_sel,
                 lay.z)),
             "topk": per_copy(lambda c, lay, bt: lambda: api.spin_topk(
@@ -498,6 +540,132 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
         out["stage_us"] = {k: _timed_us(f, stage_reps, stream) / copies for k, f in st.items()}
         for lay in lays:
             assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
+    return out
+
+
+def _copies_of(inp: Inputs, copies: int):
+    pages = [inp.keys.pages] + [inp.keys.pages.clone() for _ in range(copies - 1)]
+    scales = [inp.keys.scale] + [None if inp.keys.scale is None else inp.keys.scale.clone()
+                                 for _ in range(copies - 1)]
+    return pages, scales
+
+
+def sweep_point(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, pages, scales,
+                dense: bool):
+    """One point of the sparsity sweep on len(pages) copies of the workload:
+    per-layer step time of (a) spin_step on each copy round robin and (b) the
+    copies as the layers of one spin_stack_step on one stream (each layer's
+    plan inside the previous layer's launches), each from a reset, steps back
+    to back.  With `dense` (0 % sparsity), also the dense indexer: score +
+    top-K over every block (spin_step_finish without the EMA) round robin."""
+    from sparse_attention_indexer_spin_amd import SpinLayer, SpinStack, api
+    w = inp.w
+    copies = len(pages)
+    pt = inp.keys.page_table
+    lays = []
+    for c in range(copies):
+        lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks,
+                        d_cap=G.d_capacity(w, steps + warmup), topk=w.topk,
+                        sparsity_bp=sparsity_bp, n_rows=1, explore_bp=w.explore_bp,
+                        ema_alpha=w.alpha, combine=w.combine, layer=c,
+                        key_dtype={"fp8": torch.uint8, "bf16": torch.bfloat16}[w.key_dtype],
+                        q_dtype=torch.bfloat16 if w.q_dtype == "bf16" else torch.float32)
+        lays.append(lay)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def reset():
+        for lay in lays:
+            lay.set_requests(inp.ctx.cuda(), inp.pos[0].cuda())
+            lay.reset()
+
+    def timed(step):
+        reset()
+        for s in range(warmup):
+            step(s)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(warmup, warmup + steps):
+            step(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (steps * copies)
+
+    def seq(s):
+        for c, lay in enumerate(lays):
+            lay.step(inp.q[s], inp.weights, pages[c], scales[c], pt)
+
+    out = {"spin_step": timed(seq)}
+    n_sel = int(sum(int(lay.n_sel.sum()) for lay in lays)) / copies
+    stack = SpinStack(lays, one_stream=True)
+
+    def stk(s):
+        stack.step([inp.q[s]] * copies, [inp.weights] * copies, pages, scales, [pt] * copies)
+
+    out["one_stream_stack"] = timed(stk)
+    for lay in lays:
+        assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
+    out["realized_sparsity"] = 1.0 - n_sel / float(sum(-(-int(c) // 64) for c in inp.ctx))
+    if dense:
+        bts = [lay.batch(pages[c].shape[0]) for c, lay in enumerate(lays)]
+        ios = [lay.make_io(inp.q[warmup], inp.weights, pages[c], scales[c], pt)
+               for c, lay in enumerate(lays)]
+        for c, lay in enumerate(lays):
+            api.spin_step_plan(lay.cfg, bts[c], ios[c])   # every block (0 % sparsity)
+
+        def finish():
+            for c, lay in enumerate(lays):
+                api.spin_step_finish(lay.cfg, bts[c], ios[c], defer_ema=True)
+
+        out["dense_indexer"] = _timed_us(finish, 10, stream) / copies
+    del stack, lays
+    return out
+
+
+def fixed_cost(inp: Inputs, sparsities, steps: int, warmup: int, copies: int, runs: int):
+    """The step time over the sparsity sweep, `runs` times: per run and mode,
+    the least-squares fit T = a (1 - rho) + c and, with the slope pinned to the
+    dense indexer time T_d (score + top-K over every block, same protocol),
+    the overhead T(rho) - (1 - rho) T_d at each point and its mean.  Medians
+    over the runs, with their spread."""
+    pages, scales = _copies_of(inp, copies)
+    per_run = []
+    for _ in range(runs):
+        pts = {sp: sweep_point(inp, sp, steps, warmup, pages, scales, dense=(sp == 0))
+               for sp in sorted(set(sparsities) | {0})}
+        td = pts[0]["dense_indexer"]
+        rho = np.array([pts[sp]["realized_sparsity"] for sp in sorted(pts)])
+        run = {"dense_indexer_us": td, "rho": rho.tolist()}
+        for mode in ("spin_step", "one_stream_stack"):
+            T = np.array([pts[sp][mode] for sp in sorted(pts)])
+            A = np.stack([1.0 - rho, np.ones_like(rho)], 1)
+            (a, c), *_ = np.linalg.lstsq(A, T, rcond=None)
+            over = T - (1.0 - rho) * td
+            run[mode] = {"T_us": T.tolist(), "a_us": float(a), "c_us": float(c),
+                         "overhead_pinned_us": over.tolist(),
+                         "c_pinned_us": float(over.mean())}
+        per_run.append(run)
+    med = lambda xs: float(np.median(xs))
+    spread = lambda xs: [float(min(xs)), float(max(xs))]
+    sp_list = sorted(set(sparsities) | {0})
+    td = [r["dense_indexer_us"] for r in per_run]
+    out = {"sparsity_bp": sp_list, "runs": runs,
+           "realized_sparsity": per_run[0]["rho"],
+           "dense_indexer_us": med(td), "dense_indexer_us_spread": spread(td)}
+    for mode in ("spin_step", "one_stream_stack"):
+        rs = [r[mode] for r in per_run]
+        c, cp = [r["c_us"] for r in rs], [r["c_pinned_us"] for r in rs]
+        out[mode] = {
+            "us_per_step_layer": {str(sp): med([r["T_us"][i] for r in rs])
+                                  for i, sp in enumerate(sp_list)},
+            "fit_free": {"a_us": med([r["a_us"] for r in rs]), "c_us": med(c),
+                         "c_us_spread": spread(c),
+                         "c_over_dense_indexer": med(c) / med(td)},
+            "fit_slope_pinned_to_dense": {
+                "overhead_us": {str(sp): med([r["overhead_pinned_us"][i] for r in rs])
+                                for i, sp in enumerate(sp_list)},
+                "c_us": med(cp), "c_us_spread": spread(cp),
+                "c_over_dense_indexer": med(cp) / med(td)}}
     return out
 
 
@@ -552,12 +720,22 @@ def miss_eval(inp: Inputs, sparsity_bp: int, steps: int, variants: dict):
     return torch.cat(misses).numpy(), float(np.mean(sparsity))
 
 
-def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, budget_s: float,
-                 max_requests: int):
-    """Time the CPU oracle on whole requests of the workload until about `budget_s`
-    seconds of timed work: per request one dense warm-up step (untimed, t = 0 is
-    dense by definition), then two sparse steps (timed)."""
-    from threadpoolctl import threadpool_info
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_keys_per_s(w: G.Workload, inp: Inputs, sparsity_bp: int, budget_s: float,
+                       max_requests: int):
+    """The CPU oracle on whole requests of the workload until about `budget_s`
+    seconds of timed work: per request one dense warm-up step (untimed, t = 0
+    is dense by definition), then two sparse steps (timed)."""
     from oracle import spin_oracle as O
     pt = inp.keys.page_table.cpu().numpy()
     pages_dev, scale_dev = inp.keys.pages, inp.keys.scale
@@ -591,12 +769,31 @@ def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, budget_s: float,
                 elapsed += dt
                 st_keys += len(res["slots"]) * w.rows
         n_req += 1
+    return st_keys / elapsed, n_req, st_keys, elapsed
+
+
+def cpu_baseline(w: G.Workload, inp: Inputs, sparsity_bp: int, budget_s: float,
+                 max_requests: int):
+    """The oracle as it stands, on the host's cores (its scores are fp64
+    matrix products, threaded by the BLAS), and on one thread; budget_s seconds
+    of timed work each."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    v, n_req, keys, el = _oracle_keys_per_s(w, inp, sparsity_bp, budget_s, max_requests)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": st_keys / elapsed, "unit": "keys/s", "cores": int(threads),
-            "kind": "oracle",
+    with threadpool_limits(limits=1):
+        v1, n1, k1, e1 = _oracle_keys_per_s(w, inp, sparsity_bp, budget_s, max_requests)
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"value": v, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n_req} of {w.batch} requests x 2 sparse steps after an untimed dense "
-                      f"warm-up step ({st_keys} keys scored in {elapsed:.1f} s; numpy fp64 "
-                      f"oracle, host has {os.cpu_count()} logical CPUs)"}
+                      f"warm-up step ({keys} keys scored in {el:.1f} s; numpy fp64 oracle, "
+                      f"BLAS on {threads} threads)",
+            "single_thread": {"value": v1, "unit": "keys/s", "cores": 1,
+                              "sample": f"{n1} requests x 2 sparse steps ({k1} keys in "
+                                        f"{e1:.1f} s)"},
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "usable_cpus": usable}
 
 
 SCORE_SOURCES = ("sparse_attention_indexer_spin_amd/csrc/k_score.hip",
@@ -712,6 +909,8 @@ def main():
                   **{f"{k}_us_per_step_layer": v["ms_per_step"] * 1e3 for k, v in refs.items()}},
         "stack_us_per_step_layer": (res["stack_ms_per_step"] * 1e3
                                     if "stack_ms_per_step" in res else None),
+        "graph_us_per_step_layer": (res["graph_ms_per_step"] * 1e3
+                                    if "graph_ms_per_step" in res else None),
         "stage_us": res["stage_us"],
         "keys_scored_per_step": keys_row,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -734,27 +933,9 @@ def main():
                            "algorithmic_flops_per_launch": flops,
                            "algorithmic_bytes_per_launch": score_bytes, "launch_us": score_us,
                            "hbm_achieved_gbs": achieved, "hbm_frac": achieved / HBM_PEAK_GBS}
-    if args.sweep and w.rows == 1 and len(w.sparsity_bp) > 1:
-        sweep = {}
-        for s in sorted(set(w.sparsity_bp)):
-            if args.cache == "rotate":
-                sweep[s] = run_rotate(inp, s, min(args.steps, 20), args.warmup, 10, args.copies)
-            else:
-                sweep[s] = run_gpu(inp, s, min(args.steps, 20), args.warmup, stage_reps=10,
-                                   evict=evict)
-        rho = np.array([1.0 - sweep[s]["n_sel"] / (w.batch * w.max_blocks) for s in sweep])
-        T = np.array([sweep[s]["ms_per_step"] * 1e3 for s in sweep])
-        A = np.stack([1.0 - rho, np.ones_like(rho)], 1)
-        (a, c), *_ = np.linalg.lstsq(A, T, rcond=None)
-        dense = sweep[min(sweep)]["stage_us"]
-        t_dense_indexer = dense["score"] + dense["topk"]
-        out["sparsity_sweep"] = {
-            "us_per_step": {str(s): sweep[s]["ms_per_step"] * 1e3 for s in sweep},
-            "score_us": {str(s): sweep[s]["stage_us"]["score"] for s in sweep},
-            "realized_sparsity": {str(s): float(x) for s, x in zip(sweep, rho)},
-            "fit_us": {"a": float(a), "c": float(c)},
-            "dense_indexer_us": t_dense_indexer,
-            "c_over_dense_indexer": float(c / t_dense_indexer)}
+    if not args.no_sweep and w.rows == 1 and len(w.sparsity_bp) > 1 and args.cache == "rotate":
+        out["fixed_cost"] = fixed_cost(inp, w.sparsity_bp, min(args.steps, 20), args.warmup,
+                                       args.copies, args.sweep_runs)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp, sp, args.cpu_seconds, args.cpu_max_requests)
     print(json.dumps(out))

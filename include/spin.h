@@ -172,12 +172,17 @@ spin_status spin_select_blocks(const spin_config* cfg, const spin_batch* bt, con
  *   k_scale:    f32 [n_pages][64], non-negative; required for fp8 keys, else ignored
  *   page_table: i32 [R][pt_ld], pt_ld >= max_blocks
  *   z:          f32 [R][n_rows][z_ld], z_ld >= 64 * max_blocks
+ *   workspace:  optional, the layer's top-K workspace (spin_workspace_bytes()).
+ *               With it the call runs the kernel spin_step runs, which also
+ *               writes the slots at or above each row's top-K threshold hint
+ *               into the workspace's candidate lists; z is the same either way.
  * Supported (key, q) dtypes: (f32, f32), (bf16, bf16), (fp8, bf16), (fp8, f32).
  */
 spin_status spin_sparse_index_score(const spin_config* cfg, const spin_batch* bt, const void* q,
                                     const float* w, const void* k_pages, const float* k_scale,
                                     const int32_t* page_table, int64_t pt_ld, const int32_t* sel,
-                                    const int32_t* n_sel, float* z, int64_t z_ld, void* stream);
+                                    const int32_t* n_sel, float* z, int64_t z_ld, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * Stage 3b (Algorithm 1 step 7): per row, the min(K, |dom|) slots of dom(z)
@@ -319,7 +324,11 @@ spin_status spin_step_finish(const spin_config* cfg, const spin_batch* bt,
  * work on `main` is ordered after every layer's top-K; without ema_stream
  * also after every EMA update, with it the caller makes `main` wait for
  * ema_stream before it reads or writes a layer's EMA state or counters.
- * Deferred EMA is not available here.
+ * With defer_ema != 0 (speculative decoding, paper Sec. 3.2.2: the updates
+ * wait for the verification outcome) the finishes are score + top-K only and
+ * the caller then calls spin_stack_commit once the accepted rows are known
+ * (ios[l].n_valid); the next spin_stack_step is refused until it has.  Not
+ * with ema_stream.
  * With side_stream == NULL (and ema_stream == NULL) everything runs on `main`
  * in layer order, with no events: layer l + 1's plan runs inside layer l's
  * two launches -- its prediction in the last workgroups of the score launch,
@@ -328,7 +337,10 @@ spin_status spin_step_finish(const spin_config* cfg, const spin_batch* bt,
  * fp8 or bf16 (its score kernel filters the top-K candidates) and layer l + 1
  * has one verifier row; otherwise layer l + 1's plan is issued on its own
  * before its finish.  Layer 0's plan always is.  order_after_main is then
- * moot.  A stack may alternate between the two forms from call to call.
+ * moot.  A stack may alternate between the forms from call to call (a
+ * one-stream call after one with an EMA stream first waits for those EMA
+ * updates).  The one-stream form issues kernels only (no events), so a
+ * caller may capture it in a HIP graph.
  * Errors: SPIN_E_SHAPE when n is < 1 or exceeds the stack's layers, two
  * streams are the same, or ema_stream is given without side_stream; each
  * layer's arguments are validated as for spin_step before anything is
@@ -339,8 +351,20 @@ spin_status spin_stack_create(int32_t n_layers, spin_stack** out);
 void spin_stack_destroy(spin_stack* stack);
 spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
                             const spin_batch* bts, const spin_step_io* ios,
-                            int32_t order_after_main, void* main_stream, void* side_stream,
-                            void* ema_stream);
+                            int32_t order_after_main, int32_t defer_ema, void* main_stream,
+                            void* side_stream, void* ema_stream);
+/*
+ * The deferred EMA updates of the last spin_stack_step (defer_ema != 0), on
+ * main_stream, in layer order: each layer replays its rows 0 .. n_valid - 1
+ * in row order (ios[l].n_valid, or every row when NULL) and advances its
+ * counters, exactly as spin_ema_update + spin_advance after that layer's
+ * deferred spin_step (paper Sec. 3.2.2).  n_layers and the ios must be the
+ * step's (the q positions come from the step's snapshot in each workspace).
+ * Errors: SPIN_E_SHAPE when the last step did not defer, or n_layers differs.
+ */
+spin_status spin_stack_commit(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
+                              const spin_batch* bts, const spin_step_io* ios,
+                              void* main_stream);
 
 /*
  * Per-layer block budgets (blog "Sparse Attention Still Has a Dense Problem",

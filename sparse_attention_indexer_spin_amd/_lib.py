@@ -24,7 +24,7 @@ EXPORTS = ["spin_predict_blocks", "spin_select_blocks", "spin_sparse_index_score
            "spin_ema_update", "spin_advance", "spin_reset_state", "spin_step",
            "spin_workspace_bytes", "spin_last_error", "spin_step_plan", "spin_step_finish",
            "spin_stack_create", "spin_stack_destroy", "spin_stack_step", "spin_miss_curve",
-           "spin_budget_fill", "spin_budget_allocate", "spin_step_noalloc"]
+           "spin_budget_fill", "spin_budget_allocate", "spin_step_noalloc", "spin_stack_commit"]
 SPIN_NOALLOC_WORKSPACE_BYTES = 160 * 1024 * 1024
 SPIN_BUDGET_MINIMAX, SPIN_BUDGET_PROPORTIONAL = 0, 1
 SPIN_POOL_MAX, SPIN_POOL_TOP4, SPIN_POOL_MEAN = 0, 1, 2
@@ -73,7 +73,7 @@ def load() -> C.CDLL:
     sig = {
         "spin_predict_blocks": [cfg, bt, P, I64, P, I64, P, P, P],
         "spin_select_blocks": [cfg, bt, P, P, P, P, P, P],
-        "spin_sparse_index_score": [cfg, bt, P, P, P, P, P, I64, P, P, P, I64, P],
+        "spin_sparse_index_score": [cfg, bt, P, P, P, P, P, I64, P, P, P, I64, P, SZ, P],
         "spin_topk": [cfg, bt, P, I64, P, P, P, P, SZ, P],
         "spin_ema_update": [cfg, bt, P, I64, P, P, P, P, I64, P, I64, P, P],
         "spin_advance": [I32, I32, P, P, P, P],
@@ -83,7 +83,8 @@ def load() -> C.CDLL:
         "spin_step_plan": [cfg, bt, C.POINTER(SpinStepIO), P],
         "spin_step_finish": [cfg, bt, C.POINTER(SpinStepIO), I32, P],
         "spin_stack_create": [I32, C.POINTER(P)],
-        "spin_stack_step": [P, I32, cfg, bt, C.POINTER(SpinStepIO), I32, P, P, P],
+        "spin_stack_step": [P, I32, cfg, bt, C.POINTER(SpinStepIO), I32, I32, P, P, P],
+        "spin_stack_commit": [P, I32, cfg, bt, C.POINTER(SpinStepIO), P],
         "spin_miss_curve": [cfg, bt, P, P, I32, P, P, P],
         "spin_budget_fill": [cfg, bt, P, I32, P, P],
         "spin_budget_allocate": [I32, I32, I32, I32, P, P, P, P],

@@ -79,10 +79,14 @@ def spin_select_blocks(cfg, bt, S, row_code, sel, n_sel, budget=None, stream=Non
 
 
 def spin_sparse_index_score(cfg, bt, q, w, k_pages, k_scale, page_table, sel, n_sel, z,
-                            stream=None):
+                            stream=None, workspace=None):
+    """workspace (optional): the layer's workspace; the call then runs the kernel
+    spin_step runs (with the top-K candidate filter)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     L.check(L.load().spin_sparse_index_score(
         C.byref(cfg), C.byref(bt), _p(q), _p(w), _p(k_pages), _p(k_scale), _p(page_table),
-        _ld(page_table), _p(sel), _p(n_sel), _p(z), _ld(z), _stream(stream)))
+        _ld(page_table), _p(sel), _p(n_sel), _p(z), _ld(z), _p(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def workspace_bytes(cfg, batch_size: int, n_rows: int, max_blocks: int) -> int:
@@ -165,21 +169,30 @@ class Stack:
             pass
 
 
+def _layer_arrays(cfgs, bts, ios):
+    n = len(cfgs)
+    assert len(bts) == n and len(ios) == n
+    return n, (L.SpinConfig * n)(*cfgs), (L.SpinBatch * n)(*bts), (L.SpinStepIO * n)(*ios)
+
+
 def spin_stack_step(stack: Stack, cfgs, bts, ios, order_after_main: bool = False,
-                    main_stream=None, side_stream=None, ema_stream=None):
+                    main_stream=None, side_stream=None, ema_stream=None, defer_ema=False):
     """One decode step of len(cfgs) layers: plans on side_stream, finishes on
     main_stream (default: the current stream), EMA updates on ema_stream when
     given (else inside the finishes).  side_stream None: one stream, each
-    layer's plan inside the previous layer's launches where possible."""
-    n = len(cfgs)
-    assert len(bts) == n and len(ios) == n
-    ca = (L.SpinConfig * n)(*cfgs)
-    ba = (L.SpinBatch * n)(*bts)
-    ia = (L.SpinStepIO * n)(*ios)
+    layer's plan inside the previous layer's launches where possible.
+    defer_ema: the EMA updates wait for spin_stack_commit."""
+    n, ca, ba, ia = _layer_arrays(cfgs, bts, ios)
     L.check(L.load().spin_stack_step(stack.handle, n, ca, ba, ia, int(bool(order_after_main)),
-                                     _stream(main_stream),
+                                     int(bool(defer_ema)), _stream(main_stream),
                                      None if side_stream is None else side_stream.cuda_stream,
                                      None if ema_stream is None else ema_stream.cuda_stream))
+
+
+def spin_stack_commit(stack: Stack, cfgs, bts, ios, main_stream=None):
+    """The deferred EMA updates (ios[l].n_valid rows) of the last stack step."""
+    n, ca, ba, ia = _layer_arrays(cfgs, bts, ios)
+    L.check(L.load().spin_stack_commit(stack.handle, n, ca, ba, ia, _stream(main_stream)))
 
 
 def spin_miss_curve(cfg, bt, S, topk_idx, levels: int, covered, kprime, stream=None):

@@ -515,13 +515,15 @@ template <int SEPT>
 static void topk_ema_t(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                        const int32_t* sel, const int32_t* n_sel, int32_t* out, const TopkWs& ws,
                        const EmaArgs& A, const SelectArgs& sa, const SelectInputs& si,
-                       int sel_wgs, hipStream_t st) {
+                       int sel_wgs, hipStream_t st, bool ema) {
   const int rows_total = b.batch * b.n_rows;
   constexpr int per_block = (kSelThreads / 64) * kEmaChunk;
   const int most = (b.max_blocks + per_block - 1) / per_block;
   const int free_cus =
       resident_workgroups((const void*)k_topk_ema<SEPT>, kSelThreads) - rows_total - sel_wgs;
-  const int ema_x = max(1, min(most, free_cus / max(1, b.batch)));
+  // no EMA workgroups when the update is deferred (the launch is then the
+  // top-K and, with SEPT > 0, the next layer's selection)
+  const int ema_x = ema ? max(1, min(most, free_cus / max(1, b.batch))) : 0;
   hipLaunchKernelGGL(k_topk_ema<SEPT>, dim3(rows_total + ema_x * b.batch + sel_wgs),
                      dim3(kSelThreads), 0, st, c.topk, b.n_rows, b.max_blocks, b.ctx_len,
                      A.qpos, z, z_ld, sel, n_sel, out, ws, rows_total, A, ema_x, sa, si,
@@ -533,21 +535,22 @@ hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const floa
                            void* wsp, const int32_t* n_valid, float* V, int64_t v_ld, float* D,
                            int64_t d_ld, float* vmax, const int32_t* qpos_snap,
                            int32_t* qpos_out, int32_t* step_out, hipStream_t st,
-                           const SelectPlan* next) {
+                           const SelectPlan* next, bool ema) {
   const int rows_total = b.batch * b.n_rows;
   const TopkWs ws = carve(wsp, rows_total, b.max_blocks);
   const EmaArgs A{c.ema_alpha, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap, n_valid, z, z_ld,
                   sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out, vmax,
                   (c.flags & SPIN_MTP_ROW0_UPDATE) != 0};
   if (!next) {
-    topk_ema_t<0>(c, b, z, z_ld, sel, n_sel, out, ws, A, SelectArgs{}, SelectInputs{}, 0, st);
+    topk_ema_t<0>(c, b, z, z_ld, sel, n_sel, out, ws, A, SelectArgs{}, SelectInputs{}, 0, st,
+                  true);
   } else {
     const int n = next->requests;
     switch (next->ept) {
-      case 1: topk_ema_t<1>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st); break;
-      case 2: topk_ema_t<2>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st); break;
-      case 4: topk_ema_t<4>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st); break;
-      default: topk_ema_t<8>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st); break;
+      case 1: topk_ema_t<1>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st, ema); break;
+      case 2: topk_ema_t<2>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st, ema); break;
+      case 4: topk_ema_t<4>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st, ema); break;
+      default: topk_ema_t<8>(c, b, z, z_ld, sel, n_sel, out, ws, A, next->args, next->in, n, st, ema); break;
     }
   }
   return hipGetLastError();

@@ -210,15 +210,28 @@ static spin_status check_score_args(const char* fn, const spin_config* cfg, cons
 spin_status spin_sparse_index_score(const spin_config* cfg, const spin_batch* bt, const void* q,
                                     const float* w, const void* k_pages, const float* k_scale,
                                     const int32_t* page_table, int64_t pt_ld, const int32_t* sel,
-                                    const int32_t* n_sel, float* z, int64_t z_ld, void* stream) {
+                                    const int32_t* n_sel, float* z, int64_t z_ld, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   const char* fn = "spin_sparse_index_score";
   SPIN_CHECK(check_config(fn, cfg));
   SPIN_CHECK(check_batch(fn, bt));
   SPIN_CHECK(check_score_args(fn, cfg, bt, q, w, k_pages, k_scale, page_table, pt_ld, sel, n_sel,
                               z, z_ld));
+  if (workspace) {
+    const size_t need = spin::topk_workspace_bytes(*cfg, bt->batch, bt->n_rows, bt->max_blocks);
+    if (workspace_bytes < need)
+      return fail(SPIN_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  }
   if (bt->batch == 0) return SPIN_OK;
+  // with a workspace: the kernel spin_step runs, which also filters the
+  // top-K candidates into it
+  const spin::CandSink sink =
+      workspace ? spin::topk_sink(workspace, bt->batch, bt->n_rows, bt->max_blocks)
+                : spin::CandSink{};
   return hip_status(spin::launch_score(*cfg, *bt, q, w, k_pages, k_scale, page_table, pt_ld, sel,
-                                       n_sel, z, z_ld, (hipStream_t)stream), fn);
+                                       n_sel, z, z_ld, (hipStream_t)stream,
+                                       workspace ? &sink : nullptr),
+                    fn);
 }
 
 spin_status spin_topk(const spin_config* cfg, const spin_batch* bt, const float* z, int64_t z_ld,
@@ -352,7 +365,7 @@ spin_status issue_finish(const spin_config& c, const spin_batch& b, const spin_s
 spin_status issue_finish_with_plan(const spin_config& c, const spin_batch& b,
                                    const spin_step_io& io, const spin_config& nc,
                                    const spin_batch& nb, const spin_step_io& nio,
-                                   hipStream_t st) {
+                                   int32_t defer_ema, hipStream_t st) {
   const spin::CandSink sink = spin::topk_sink(io.workspace, b.batch, b.n_rows, b.max_blocks);
   const spin::PredictPlan pp = spin::predict_plan(nc, nb, nio.V, nio.v_ld, nio.D, nio.d_ld,
                                                   nio.v_max, nio.S, step_qsnap(nc, nb, nio));
@@ -365,7 +378,7 @@ spin_status issue_finish_with_plan(const spin_config& c, const spin_batch& b,
   return hip_status(spin::launch_topk_ema(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.topk_idx,
                                           io.workspace, io.n_valid, io.V, io.v_ld, io.D,
                                           io.d_ld, io.v_max, step_qsnap(c, b, io),
-                                          io.q_pos_mut, io.step_mut, st, &sp),
+                                          io.q_pos_mut, io.step_mut, st, &sp, !defer_ema),
                     "spin_stack_step/topk+ema+select");
 }
 
@@ -392,6 +405,9 @@ struct spin_stack {
   int device = 0;
   int32_t prev_h = 0;            // group split of the previous call
   bool one_stream_last = false;  // the previous call ran on one stream
+  bool ema_stream_last = false;  // the previous call ran the EMA updates on an EMA stream
+  bool commit_pending = false;   // the previous call deferred its EMA updates
+  int32_t committed_layers = 0;  // layers of the previous call
   hipEvent_t plan_done[2] = {nullptr, nullptr};
   hipEvent_t finish_done[2] = {nullptr, nullptr};
   hipEvent_t ema_done[2] = {nullptr, nullptr};   // with an EMA stream
@@ -587,14 +603,20 @@ void spin_stack_destroy(spin_stack* stack) {
 
 spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
                             const spin_batch* bts, const spin_step_io* ios,
-                            int32_t order_after_main, void* main_stream, void* side_stream,
-                            void* ema_stream) {
+                            int32_t order_after_main, int32_t defer_ema, void* main_stream,
+                            void* side_stream, void* ema_stream) {
   const char* fn = "spin_stack_step";
   if (!stack || !cfgs || !bts || !ios) return fail(SPIN_E_NULL, "%s: NULL argument", fn);
   if (n_layers < 1 || n_layers > stack->n_layers)
     return fail(SPIN_E_SHAPE, "%s: n_layers %d outside [1, %d]", fn, n_layers, stack->n_layers);
   if (!side_stream && ema_stream)
     return fail(SPIN_E_SHAPE, "%s: an EMA stream needs a side stream", fn);
+  if (defer_ema && ema_stream)
+    return fail(SPIN_E_SHAPE, "%s: a deferred EMA update runs in spin_stack_commit, not on an "
+                "EMA stream", fn);
+  if (stack->commit_pending)
+    return fail(SPIN_E_SHAPE, "%s: the previous step deferred its EMA updates; call "
+                "spin_stack_commit first", fn);
   if (side_stream && (main_stream == side_stream ||
                       (ema_stream && (ema_stream == main_stream || ema_stream == side_stream))))
     return fail(SPIN_E_SHAPE, "%s: main, side and ema must be different streams", fn);
@@ -610,6 +632,12 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
   }
   hipStream_t mst = (hipStream_t)main_stream, sst = (hipStream_t)side_stream;
   if (!sst) {
+    // the previous call's EMA updates may still run on its EMA stream: main
+    // waits for them before any plan reads the EMA state
+    if (stack->ema_stream_last) {
+      SPIN_CHECK(hip_status(hipStreamWaitEvent(mst, stack->ema_done[0], 0), fn));
+      SPIN_CHECK(hip_status(hipStreamWaitEvent(mst, stack->ema_done[1], 0), fn));
+    }
     // one stream: layer l + 1's plan inside layer l's score and top-K + EMA
     // launches where both allow it (layer l's score kernel filters, layer
     // l + 1 has one verifier row), else on its own before its finish
@@ -624,12 +652,16 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
       const bool fuse = m < n_layers && bts[m].batch > 0 && bts[m].n_rows == 1 &&
                         spin::score_filters(cfgs[l], bts[l]);
       if (fuse)
-        SPIN_CHECK(issue_finish_with_plan(cfgs[l], bts[l], ios[l], cfgs[m], bts[m], ios[m], mst));
+        SPIN_CHECK(issue_finish_with_plan(cfgs[l], bts[l], ios[l], cfgs[m], bts[m], ios[m],
+                                          defer_ema, mst));
       else
-        SPIN_CHECK(issue_finish(cfgs[l], bts[l], ios[l], 0, mst));
+        SPIN_CHECK(issue_finish(cfgs[l], bts[l], ios[l], defer_ema, mst));
       planned = fuse;
     }
     stack->one_stream_last = true;
+    stack->ema_stream_last = false;
+    stack->commit_pending = defer_ema != 0;
+    stack->committed_layers = n_layers;
     return SPIN_OK;
   }
   auto wait = [&](hipStream_t st, hipEvent_t e) {
@@ -665,7 +697,8 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
     if (lo[g] == hi[g]) continue;
     SPIN_CHECK(wait(mst, stack->plan_done[g]));
     for (int l = lo[g]; l < hi[g]; ++l)
-      if (bts[l].batch > 0) SPIN_CHECK(issue_finish(cfgs[l], bts[l], ios[l], est ? 1 : 0, mst));
+      if (bts[l].batch > 0)
+        SPIN_CHECK(issue_finish(cfgs[l], bts[l], ios[l], (est || defer_ema) ? 1 : 0, mst));
     SPIN_CHECK(record(stack->finish_done[g], mst));
     if (est) {
       SPIN_CHECK(wait(est, stack->finish_done[g]));
@@ -682,6 +715,43 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
   }
   stack->prev_h = h;
   stack->one_stream_last = false;
+  stack->ema_stream_last = est != nullptr;
+  stack->commit_pending = defer_ema != 0;
+  stack->committed_layers = n_layers;
+  return SPIN_OK;
+}
+
+spin_status spin_stack_commit(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
+                              const spin_batch* bts, const spin_step_io* ios,
+                              void* main_stream) {
+  const char* fn = "spin_stack_commit";
+  if (!stack || !cfgs || !bts || !ios) return fail(SPIN_E_NULL, "%s: NULL argument", fn);
+  if (!stack->commit_pending)
+    return fail(SPIN_E_SHAPE, "%s: the previous step did not defer its EMA updates", fn);
+  if (n_layers != stack->committed_layers)
+    return fail(SPIN_E_SHAPE, "%s: n_layers %d, but the deferred step ran %d", fn, n_layers,
+                stack->committed_layers);
+  int dev = -1;
+  SPIN_CHECK(hip_status(hipGetDevice(&dev), fn));
+  if (dev != stack->device)
+    return fail(SPIN_E_SHAPE, "%s: stack created on device %d, current device %d", fn,
+                stack->device, dev);
+  for (int l = 0; l < n_layers; ++l) {
+    char lfn[64];
+    std::snprintf(lfn, sizeof(lfn), "%s[layer %d]", fn, l);
+    SPIN_CHECK(check_step(lfn, &cfgs[l], &bts[l], &ios[l]));
+  }
+  hipStream_t mst = (hipStream_t)main_stream;
+  // in layer order, each layer's replay of its prefix-valid rows (io.n_valid)
+  // and counter advance, q positions from the step's snapshot
+  for (int l = 0; l < n_layers; ++l)
+    if (bts[l].batch > 0) SPIN_CHECK(issue_ema(cfgs[l], bts[l], ios[l], mst));
+  // the next two-stream call's plans wait for these updates
+  if (!stack->one_stream_last) {
+    SPIN_CHECK(hip_status(hipEventRecord(stack->finish_done[0], mst), fn));
+    SPIN_CHECK(hip_status(hipEventRecord(stack->finish_done[1], mst), fn));
+  }
+  stack->commit_pending = false;
   return SPIN_OK;
 }
 

@@ -60,13 +60,14 @@ hipError_t launch_topk(const spin_config& c, const spin_batch& b, const float* z
                        size_t ws_bytes, hipStream_t st, bool prefiltered = false);
 // After a filtering score kernel, the top-K and the EMA update + counter
 // advance of a whole step in one launch (they share no outputs).  Both read
-// q positions from the step's snapshot.
+// q positions from the step's snapshot.  ema == false (deferred update; only
+// with `next`): the top-K and the next layer's selection alone.
 hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const float* z,
                            int64_t z_ld, const int32_t* sel, const int32_t* n_sel, int32_t* out,
                            void* ws, const int32_t* n_valid, float* V, int64_t v_ld, float* D,
                            int64_t d_ld, float* vmax, const int32_t* qpos_snap,
                            int32_t* qpos_out, int32_t* step_out, hipStream_t st,
-                           const SelectPlan* next = nullptr);
+                           const SelectPlan* next = nullptr, bool ema = true);
 // The candidate sink inside a top-K workspace.
 CandSink topk_sink(void* ws, int R, int rows, int max_blocks);
 size_t topk_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks);

@@ -128,6 +128,7 @@ class SpinStack:
         # fused with the latency-bound top-K on the main stream it is free.
         self.ema = torch.cuda.Stream(device=device) if ema_stream else None
         self._order_next = True
+        self._deferred = None
         self.policy = budget_policy
         if budget_policy is not None:
             assert budget_policy in ("minimax", "proportional")
@@ -201,6 +202,15 @@ class SpinStack:
         self.level_history.append((self.t, list(new)))
         self._publish(self.levels_now)
 
+    def commit(self, n_valid=None, stream=None):
+        """The deferred EMA updates of the last step: layer l replays its rows
+        0 .. n_valid[l] - 1 (every row when None) and advances its counters."""
+        cfgs, bts, ios = self._deferred
+        for l, io in enumerate(ios):
+            io.n_valid = None if n_valid is None else api._p(n_valid[l])
+        api.spin_stack_commit(self.stack, cfgs, bts, ios, main_stream=stream)
+        self._deferred = None
+
     def join(self, stream=None):
         """Order `stream` (default: the current one) after everything the stack
         issued; needed before reading or writing a layer's EMA state or
@@ -227,11 +237,13 @@ class SpinStack:
         self._order_next = True
 
     def step(self, qs, ws, k_pages, k_scales, page_tables, n_valid=None, budgets=None,
-             stream=None, n_layers=None):
-        """One decode step of the first n_layers layers (default: all)."""
+             stream=None, n_layers=None, defer_ema: bool = False):
+        """One decode step of the first n_layers layers (default: all).
+        defer_ema: the EMA updates wait for commit() (speculative decoding)."""
         n = len(self.layers) if n_layers is None else n_layers
         probe = False
         if self.policy is not None:
+            assert not defer_ema
             assert budgets is None and n == len(self.layers)
             if self._pending is not None and self.t >= self._pending + 2:
                 self._apply_probe()
@@ -239,6 +251,10 @@ class SpinStack:
             probe = self.t > 0 and self.t % self.P == 0
             src = self.probe_budget if probe else self.budget
             budgets = [src[l] for l in range(n)]
+        if self.policy is not None and self.one_stream:
+            # the budget table is written on the side stream; on one stream
+            # the plans run on main and must see it
+            (torch.cuda.current_stream() if stream is None else stream).wait_stream(self.side)
         cfgs, bts, ios = [], [], []
         for l, lay in enumerate(self.layers[:n]):
             bts.append(lay.batch(k_pages[l].shape[0]))
@@ -249,8 +265,10 @@ class SpinStack:
         api.spin_stack_step(self.stack, cfgs, bts, ios, order_after_main=self._order_next,
                             main_stream=stream,
                             side_stream=None if self.one_stream else self.side,
-                            ema_stream=self.ema)
+                            ema_stream=self.ema, defer_ema=defer_ema)
         self._order_next = False
+        if defer_ema:
+            self._deferred = (cfgs, bts, ios)
         if probe:
             st = torch.cuda.current_stream() if stream is None else stream
             for l, lay in enumerate(self.layers):

@@ -107,12 +107,16 @@ def test_host_validation_without_gpu(lib):
     import torch
     bad = _cfg(key_dtype=torch.bfloat16, q_dtype=torch.float32)
     st = lib.spin_sparse_index_score(C.byref(bad), C.byref(bt), 1, 1, 1, None, 1, 16, 1, 1, 1,
-                                     1024, None)
+                                     1024, None, 0, None)
     assert st == 3
     # fp8 keys need scales
     st = lib.spin_sparse_index_score(C.byref(cfg), C.byref(bt), 1, 1, 1, None, 1, 16, 1, 1, 1,
-                                     1024, None)
+                                     1024, None, 0, None)
     assert st == 1
+    # a workspace smaller than the top-K region
+    st = lib.spin_sparse_index_score(C.byref(cfg), C.byref(bt), 1, 1, 1, 1, 1, 16, 1, 1, 1,
+                                     1024, 1, 64, None)
+    assert st == 4
     # an empty batch is a valid no-op
     bt0 = _lib.SpinBatch(batch=0, n_rows=1, max_blocks=16, n_pages=16, ctx_len=None,
                          q_pos=None, step=None, req_id=None, err=None)
@@ -130,5 +134,6 @@ def test_stack_host_validation_without_gpu(lib):
     assert lib.spin_stack_create(0, C.byref(h)) == 2 and not h.value
     assert lib.spin_stack_create(257, C.byref(h)) == 2 and not h.value
     assert lib.spin_stack_create(4, None) == 1
-    assert lib.spin_stack_step(None, 1, None, None, None, 0, None, None, None) == 1
+    assert lib.spin_stack_step(None, 1, None, None, None, 0, 0, None, None, None) == 1
+    assert lib.spin_stack_commit(None, 1, None, None, None, None) == 1
     lib.spin_stack_destroy(None)  # a no-op

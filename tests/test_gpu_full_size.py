@@ -153,7 +153,8 @@ def test_full_size_sampled_parity(name, sparsity):
            f"{n_steps} steps checked; worst |dz| / bound = {worst_bound:.3f}")
 
 
-def test_full_size_stack_with_budgets():
+@pytest.mark.parametrize("one_stream", [False, True])
+def test_full_size_stack_with_budgets(one_stream):
     """The 8-layer ragged workload at full size through SpinStack with per-layer
     budgets (proportional rule, a probe every 2 steps): every step bit-identical
     to sequential spin_step layers given the same budgets; the probe's miss
@@ -161,7 +162,7 @@ def test_full_size_stack_with_budgets():
     oracle's on the summed curves."""
     from oracle import spin_budget as OB
     from sparse_attention_indexer_spin_amd import SpinLayer, SpinStack
-    banner("full size stack + budgets fp8_256k_ragged_8l")
+    banner(f"full size stack + budgets fp8_256k_ragged_8l one_stream={one_stream}")
     w = G.WORKLOADS["fp8_256k_ragged_8l"]
     n_steps, sp, P, levels = 5, w.sparsity_bp[0], 2, 100
     ctx = G.context_lengths(w)
@@ -185,7 +186,8 @@ def test_full_size_stack_with_budgets():
         return out
 
     seq, stk = layers(), layers()
-    stack = SpinStack(stk, budget_policy="proportional", probe_period=P, levels=levels)
+    stack = SpinStack(stk, budget_policy="proportional", probe_period=P, levels=levels,
+                      one_stream=one_stream)
     target = (10000 - sp) // 100
     Bs = [O.n_blocks(int(c)) for c in ctx]
     levels_now = [target] * w.layers
