@@ -207,12 +207,37 @@ def rank_desc(values, candidates):
     return cand[order]
 
 
+def exploration_order(pool, S, step: int, layer: int, req_id: int, seed: int,
+                      explore: str = "random", last_obs=None):
+    """The blocks of `pool` in the order exploration takes them (paper Sec. 3.2.1
+    and Sec. 4.6, "Staleness mitigation"; ties: lower block):
+      random    -- smallest Philox priority first (the method);
+      age       -- least recently observed first: smallest last_obs[j], the
+                   step at which block j was last scored;
+      staleness -- predicted importance weighted by staleness first: largest
+                   S[j] * (step - last_obs[j]), one fp32 product."""
+    pool = np.asarray(pool, dtype=np.int64)
+    if explore == "random":
+        pri = block_priority(int(pool.max()) + 1 if pool.size else 0, step, layer, req_id, seed)
+        return pool[np.lexsort((pool, pri[pool]))]
+    obs = np.asarray(last_obs, dtype=np.int64)[pool]
+    if explore == "age":
+        return pool[np.lexsort((pool, obs))]
+    if explore == "staleness":
+        age = (np.int64(step) - obs).astype(np.float32)
+        score = canon32((f32(S)[pool] * age).astype(np.float32)).astype(np.float64)
+        return pool[np.lexsort((pool, -score))]
+    raise ValueError(explore)
+
+
 def select_blocks(S, n_slots: int, K: int, sparsity_bp: int, explore_bp: int, step: int,
-                  layer: int, req_id: int, seed: int, budget=None, b: int = BLOCK):
+                  layer: int, req_id: int, seed: int, budget=None, b: int = BLOCK,
+                  explore: str = "random", last_obs=None):
     """Reason-coded block mask of one verifier row (uint8 [B]).
 
     Codes: 0 skip, 1 forced, 2 ranked, 3 explored, 4 dense warm-up.
     budget: optional override of m (used by per-layer budgets).
+    explore / last_obs: the exploration policy (exploration_order).
     """
     B = n_blocks(n_slots, b)
     code = np.zeros(B, dtype=np.uint8)
@@ -232,10 +257,90 @@ def select_blocks(S, n_slots: int, K: int, sparsity_bp: int, explore_bp: int, st
     code[ranked] = CODE_RANKED
     pool = np.array([j for j in range(B) if code[j] == CODE_SKIP], dtype=np.int64)
     if n_e > 0 and pool.size:
-        pri = block_priority(B, step, layer, req_id, seed)
-        order = np.lexsort((pool, pri[pool]))      # smallest priority, then lower block
-        code[pool[order[:n_e]]] = CODE_EXPLORED
+        order = exploration_order(pool, S, step, layer, req_id, seed, explore, last_obs)
+        code[order[:n_e]] = CODE_EXPLORED
     return code
+
+
+def a0_select(zhat, n_slots: int, K: int, explore_bp: int, step: int, layer: int, req_id: int,
+              seed: int, S=None, explore: str = "random", last_obs=None, b: int = BLOCK):
+    """Block mask of one verifier row under block reduction A0 (paper Sec. 4.6,
+    "Block reduction"): the K slots with the largest predicted slot score
+    zhat (fp32 [N]; ties: lower slot; K the post-indexer top-K size), then
+    every block holding one of them (code 2), with the sink and newest blocks
+    (code 1) and floor(|mask| gamma) exploration blocks (code 3) from the
+    rest, |mask| the forced and expanded blocks.  The budget does not bound
+    A0: its realized sparsity follows from how the K slots spread."""
+    N = int(n_slots)
+    B = n_blocks(N, b)
+    code = np.zeros(B, dtype=np.uint8)
+    if step == 0:
+        code[:] = CODE_DENSE
+        return code
+    z = canon32(np.asarray(zhat, dtype=np.float32)[:N]).astype(np.float64)
+    slots = np.arange(N)
+    top = slots[np.lexsort((slots, -z))[:min(int(K), N)]]
+    code[np.unique(top // b)] = CODE_RANKED
+    code[sorted({0, B - 1})] = CODE_FORCED
+    m = int((code != CODE_SKIP).sum())
+    n_e = m * int(explore_bp) // 10000
+    pool = np.array([j for j in range(B) if code[j] == CODE_SKIP], dtype=np.int64)
+    if n_e > 0 and pool.size:
+        order = exploration_order(pool, S, step, layer, req_id, seed, explore, last_obs)
+        code[order[:n_e]] = CODE_EXPLORED
+    return code
+
+
+def predicted_slot_scores(V, D, n_slots: int, q: int, combine: str = "max"):
+    """zhat[i] = C(V[i], D[q - i]) for i < N (Eq. 1), fp32."""
+    N = int(n_slots)
+    i = np.arange(N)
+    v, d = f32(V)[:N], f32(D)[q - i]
+    return (np.maximum(v, d) if combine == "max" else (v + d).astype(np.float32)).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Block reduction A2 (paper Sec. 4.6, "Block reduction"): block-level V / D
+# EMA states updated from pooled indexer scores, predicting block scores
+# directly.  Vb[j] per block, Db[floor(q / b) - j] per block offset.
+# --------------------------------------------------------------------------
+def predict_block_scores_a2(Vb, Db, n_slots: int, q: int, combine: str = "max", b: int = BLOCK):
+    """S[j] = C(Vb[j], Db[floor(q / b) - j]) for j < B, fp32."""
+    B = n_blocks(n_slots, b)
+    j = np.arange(B)
+    v, d = f32(Vb)[:B], f32(Db)[q // b - j]
+    S = np.maximum(v, d) if combine == "max" else (v + d).astype(np.float32)
+    return canon32(S)
+
+
+def pool_scores(z32, sel_blocks, n_slots: int, pooling: str = "max", b: int = BLOCK):
+    """The pooled indexer score of each selected block (pool_block over its
+    valid slots' fp32 scores, in slot order)."""
+    z32 = np.asarray(z32, dtype=np.float32)
+    N = int(n_slots)
+    out = np.empty(len(sel_blocks), dtype=np.float32)
+    pos = 0
+    for k, j in enumerate(sel_blocks):
+        n = min(b, N - int(j) * b)
+        out[k] = pool_block(canon32(z32[pos:pos + n]), pooling)
+        pos += n
+    return canon32(out)
+
+
+def ema_update_a2(Vb, Db, z_rows, sel_blocks, n_slots: int, q_pos: int, n_valid: int,
+                  alpha: float, pooling: str = "max", b: int = BLOCK):
+    """In-place block-level EMA of rows 0..n_valid-1 in row order: for each
+    selected block j, with zb its pooled score of that row,
+      Vb[j] <- (a Vb[j]) + (be zb),  Db[floor((q + r) / b) - j] <- likewise,
+    three fp32 roundings each, be = fl(1 - a)."""
+    a = np.float32(alpha)
+    bcoef = np.float32(np.float32(1.0) - a)
+    blocks = np.asarray(sel_blocks, dtype=np.int64)
+    for r in range(int(n_valid)):
+        zb = pool_scores(z_rows[r], blocks, n_slots, pooling, b)
+        Vb[blocks] = (a * Vb[blocks]).astype(np.float32) + (bcoef * zb).astype(np.float32)
+        off = (q_pos + r) // b - blocks
+        Db[off] = (a * Db[off]).astype(np.float32) + (bcoef * zb).astype(np.float32)
 
 
 def union_blocks(codes_rows):
@@ -340,11 +445,14 @@ class RequestState:
     def __init__(self, n_cap: int, d_cap: int):
         self.V = np.zeros(n_cap, dtype=np.float32)
         self.D = np.zeros(d_cap, dtype=np.float32)
+        # the step at which each block was last scored (block age / staleness)
+        self.last_obs = np.zeros(n_blocks(n_cap), dtype=np.int64)
         self.t = 0
 
     def reset(self):
         self.V[:] = 0
         self.D[:] = 0
+        self.last_obs[:] = 0
         self.t = 0
 
 
@@ -353,7 +461,8 @@ def spin_step(state: RequestState, *, q, q_dtype, w, pages, page_table_row, key_
               alpha: float, layer: int, req_id: int, seed: int, combine: str = "max",
               n_valid=None, budget=None, defer=False, pooling: str = "max",
               mtp_row0_mask: bool = False, mtp_row0_update: bool = False,
-              explore_per_row: bool = False, exact_f32: bool = True):
+              explore_per_row: bool = False, exact_f32: bool = True,
+              explore: str = "random", reduction: str = "A1"):
     """One SPIN decode step for one request: predict, select, union, score, top-K, EMA.
 
     q: [rows, n_h, d] (raw f32 or bf16 codes), w: [rows, n_h].
@@ -367,18 +476,34 @@ def spin_step(state: RequestState, *, q, q_dtype, w, pages, page_table_row, key_
     `pooling` (pool_block); mtp_row0_mask: score row 0's mask alone (row-0
     sharing); mtp_row0_update: the EMA takes row 0 only (row-0 update);
     explore_per_row: row r's exploration priorities come from the counter
-    (j, t, layer + 65536 r, req_id).
+    (j, t, layer + 65536 r, req_id); explore: the exploration policy
+    (exploration_order: random, age, staleness); reduction: where slot
+    signals become blocks (Sec. 4.6): A1 pools predicted slot scores (the
+    method), A0 expands the predicted top-K slots (a0_select), A2 keeps
+    block-level V / D (state.V, state.D indexed by block and block offset).
+    Every block of the scored union is recorded as observed at step t.
     """
     rows = q.shape[0]
     qd = decode_q(q, q_dtype)
     codes = []
     for r in range(rows):
-        S = predict_block_scores(state.V, state.D, n_slots, q_pos + r, combine, pooling=pooling)
+        q = q_pos + r
+        if reduction == "A2":
+            S = predict_block_scores_a2(state.V, state.D, n_slots, q, combine)
+        else:
+            S = predict_block_scores(state.V, state.D, n_slots, q, combine, pooling=pooling)
         lay = layer + 65536 * r if explore_per_row else layer
-        codes.append(select_blocks(S, n_slots, K, sparsity_bp, explore_bp, state.t, lay,
-                                   req_id, seed, budget))
+        if reduction == "A0":
+            zhat = predicted_slot_scores(state.V, state.D, n_slots, q, combine)
+            codes.append(a0_select(zhat, n_slots, K, explore_bp, state.t, lay, req_id, seed,
+                                   S=S, explore=explore, last_obs=state.last_obs))
+        else:
+            codes.append(select_blocks(S, n_slots, K, sparsity_bp, explore_bp, state.t, lay,
+                                       req_id, seed, budget, explore=explore,
+                                       last_obs=state.last_obs))
     codes = np.stack(codes)
     sel = union_blocks(codes[:1] if mtp_row0_mask else codes)
+    state.last_obs[sel] = state.t
     slots = union_slots(sel, n_slots)
     keys = gather_keys(pages, page_table_row, slots, key_dtype, scale)
     z64 = np.stack([index_scores(qd[r], w[r], keys) for r in range(rows)])
@@ -388,7 +513,10 @@ def spin_step(state: RequestState, *, q, q_dtype, w, pages, page_table_row, key_
         z32 = canon32(z64)
     top = np.stack([topk_slots(z32[r], slots, K) for r in range(rows)])
     if not defer:
-        ema_update(state.V, state.D, z32, slots, q_pos,
-                   1 if mtp_row0_update else (rows if n_valid is None else n_valid), alpha)
+        nv = 1 if mtp_row0_update else (rows if n_valid is None else n_valid)
+        if reduction == "A2":
+            ema_update_a2(state.V, state.D, z32, sel, n_slots, q_pos, nv, alpha, pooling)
+        else:
+            ema_update(state.V, state.D, z32, slots, q_pos, nv, alpha)
         state.t += 1
     return dict(codes=codes, sel=sel, slots=slots, z64=z64, z32=z32, topk=top)
