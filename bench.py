@@ -678,9 +678,11 @@ def miss_eval(inp: Inputs, sparsity_bp: int, steps: int, variants: dict):
     w = inp.w
     kd = {"fp8": torch.uint8, "bf16": torch.bfloat16, "f32": torch.float32}[w.key_dtype]
     qd = torch.bfloat16 if w.q_dtype == "bf16" else torch.float32
+    variants = dict(variants)
+    explore_bp = variants.pop("explore_bp", w.explore_bp)
     lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks, d_cap=G.d_capacity(w, steps),
                     topk=w.topk, sparsity_bp=sparsity_bp, n_rows=w.rows,
-                    explore_bp=w.explore_bp, ema_alpha=w.alpha, combine=w.combine,
+                    explore_bp=explore_bp, ema_alpha=w.alpha, combine=w.combine,
                     key_dtype=kd, q_dtype=qd, **variants)
     lay.set_requests(inp.ctx.cuda(), inp.pos[0].cuda())
     lay.reset()
@@ -855,7 +857,14 @@ def main():
     inp = Inputs(w, total_steps)
     if args.miss_eval:
         variants = [("A1-max (default)", {}), ("A1-top4", {"pooling": "top4"}),
-                    ("A1-mean", {"pooling": "mean"})]
+                    ("A1-mean", {"pooling": "mean"}),
+                    ("A0 (top-K predicted slots expanded)", {"reduction": "A0"}),
+                    ("A2-max (block-level EMA)", {"reduction": "A2"}),
+                    ("A2-top4", {"reduction": "A2", "pooling": "top4"}),
+                    ("A2-mean", {"reduction": "A2", "pooling": "mean"}),
+                    ("no exploration", {"explore_bp": 0}),
+                    ("block-age exploration", {"explore": "age"}),
+                    ("staleness-score exploration", {"explore": "staleness"})]
         if w.rows > 1:
             variants += [("row-0 mask", {"mtp_row0_mask": True}),
                          ("row-0 update", {"mtp_row0_update": True}),

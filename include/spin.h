@@ -89,11 +89,35 @@ enum { SPIN_DERR_CTX = 1,   /* ctx_len < 1, > 64*max_blocks or > v_ld        */
  *  - SPIN_EXPLORE_PER_ROW: each verifier row draws its own exploration
  *    priorities, with counter (j, step, layer + 65536 row, req_id) (layer
  *    < 65536), instead of sharing row 0's.
+ *  - Exploration policy (Sec. 4.6, "Staleness mitigation"), bits 5-6; each
+ *    picks the n_e explored blocks among those neither forced nor ranked
+ *    (ties: lower block).  Random (0, default): the smallest Philox words.
+ *    SPIN_EXPLORE_AGE: the least recently observed first, i.e. the smallest
+ *    last_obs[j], the step at which block j was last in the scored union.
+ *    SPIN_EXPLORE_STALENESS: predicted importance weighted by staleness
+ *    first, the largest S[j] * (float)(step - last_obs[j]) (one fp32
+ *    product).  Both need the last_obs array (below).
+ *  - Block reduction (Sec. 4.6, "Block reduction"), bits 7-8.  A1 (0,
+ *    default): pool the predicted slot scores into block scores.
+ *    SPIN_REDUCE_A0: the K slots with the largest predicted slot score (K =
+ *    topk; ties: lower slot) expanded to every block holding one (code
+ *    RANKED), plus the forced blocks, plus floor(|mask| * explore_bp / 10000)
+ *    explored blocks from the rest; sparsity_bp and the budget override do
+ *    not apply (the realized sparsity follows from how the slots spread).  A0
+ *    runs in spin_step / spin_step_plan only (it reads the slot-level state).
+ *    SPIN_REDUCE_A2: block-level EMA states in the same V and D arrays, V[j]
+ *    per block and D[floor(q / 64) - j] per block offset (floor(q / 64) <
+ *    d_ld), updated from each scored block's pooled indexer score (the
+ *    pooling flag's rule over its valid slots), three fp32 roundings per
+ *    update, rows replayed in order; prediction S[j] = C(V[j], D[floor(q /
+ *    64) - j]).  v_max does not apply.
  */
 enum {
   SPIN_POOL_MAX = 0, SPIN_POOL_TOP4 = 1, SPIN_POOL_MEAN = 2, SPIN_POOL_MASK = 3,
   SPIN_MTP_ROW0_MASK = 4, SPIN_MTP_ROW0_UPDATE = 8, SPIN_EXPLORE_PER_ROW = 16,
-  SPIN_FLAGS_ALL = 31
+  SPIN_EXPLORE_AGE = 32, SPIN_EXPLORE_STALENESS = 64, SPIN_EXPLORE_POLICY_MASK = 96,
+  SPIN_REDUCE_A0 = 128, SPIN_REDUCE_A2 = 256, SPIN_REDUCE_MASK = 384,
+  SPIN_FLAGS_ALL = 511
 };
 
 /* Method parameters, passed by host pointer and copied by value. */
@@ -138,6 +162,8 @@ typedef struct spin_batch {
  *          V = 0); spin_reset_state, spin_ema_update and spin_step keep it so
  *          when given it.  ctx_len must not shrink between resets.
  *   S: f32 [R][n_rows][max_blocks]; entries j >= ceil(N/64) are not written.
+ * With SPIN_REDUCE_A2 the states are block-level (see spin_config.flags):
+ * S[r][row][j] = C(V[j], D[floor(q_row / 64) - j]); v_max is ignored.
  */
 spin_status spin_predict_blocks(const spin_config* cfg, const spin_batch* bt,
                                 const float* V, int64_t v_ld, const float* D, int64_t d_ld,
@@ -154,13 +180,19 @@ spin_status spin_predict_blocks(const spin_config* cfg, const spin_batch* bt,
  * counter (j, step, layer, req_id) under key (seed lo, seed hi) (ties: lower
  * block).  step == 0 selects every block (dense warm-up).
  *   budget:   optional i32 [R]
+ *   last_obs: optional i32 [R][max_blocks], the step at which each block was
+ *             last in the scored union (all 0 after a reset: the dense first
+ *             step observes every block); required by the age and staleness
+ *             exploration policies.  When given, every block of this step's
+ *             union gets step[r].
  *   row_code: u8 [R][n_rows][max_blocks] (SPIN_CODE_*; entries j >= B not written)
  *   sel:      i32 [R][max_blocks] ascending union of the rows' masks, -1 padded
  *   n_sel:    i32 [R] union size
+ * Block reduction A0 is refused here (SPIN_E_UNSUPPORTED): it runs in spin_step.
  */
 spin_status spin_select_blocks(const spin_config* cfg, const spin_batch* bt, const float* S,
-                               const int32_t* budget, uint8_t* row_code, int32_t* sel,
-                               int32_t* n_sel, void* stream);
+                               const int32_t* budget, int32_t* last_obs, uint8_t* row_code,
+                               int32_t* sel, int32_t* n_sel, void* stream);
 
 /*
  * Stage 3a (Sec. 2): z[r][row][64k + s] = sum_h w[r][row][h] ReLU(q[r][row][h] . key(i))
@@ -207,6 +239,10 @@ spin_status spin_topk(const spin_config* cfg, const spin_batch* bt, const float*
  *   n_valid: optional i32 [R], each in 1..n_rows
  *   v_max:   optional f32 [R][max_blocks]: the updated blocks' V maxima are
  *            refreshed (see spin_predict_blocks)
+ * With SPIN_REDUCE_A2 the update is block-level: for each selected block j
+ * and row r in order, with p the pooled z of its valid slots (the pooling
+ * flag's rule), V[j] <- (alpha V[j]) + (beta p) and D[floor(q_r / 64) - j]
+ * likewise.
  */
 spin_status spin_ema_update(const spin_config* cfg, const spin_batch* bt, const float* z,
                             int64_t z_ld, const int32_t* sel, const int32_t* n_sel,
@@ -247,6 +283,8 @@ typedef struct spin_step_io {
   int32_t* q_pos_mut;                   /* optional: advanced after the EMA   */
   int32_t* step_mut;                    /* optional: advanced after the EMA   */
   void* workspace; size_t workspace_bytes;
+  int32_t* last_obs;                    /* optional i32 [R][max_blocks]: see
+                                           spin_select_blocks                 */
 } spin_step_io;
 
 /*

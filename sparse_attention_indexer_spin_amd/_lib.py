@@ -29,6 +29,8 @@ SPIN_NOALLOC_WORKSPACE_BYTES = 160 * 1024 * 1024
 SPIN_BUDGET_MINIMAX, SPIN_BUDGET_PROPORTIONAL = 0, 1
 SPIN_POOL_MAX, SPIN_POOL_TOP4, SPIN_POOL_MEAN = 0, 1, 2
 SPIN_MTP_ROW0_MASK, SPIN_MTP_ROW0_UPDATE, SPIN_EXPLORE_PER_ROW = 4, 8, 16
+SPIN_EXPLORE_AGE, SPIN_EXPLORE_STALENESS = 32, 64
+SPIN_REDUCE_A0, SPIN_REDUCE_A2 = 128, 256
 
 
 class SpinConfig(C.Structure):
@@ -53,7 +55,7 @@ class SpinStepIO(C.Structure):
                 ("row_code", C.c_void_p), ("sel", C.c_void_p), ("n_sel", C.c_void_p),
                 ("z", C.c_void_p), ("z_ld", C.c_int64), ("topk_idx", C.c_void_p),
                 ("q_pos_mut", C.c_void_p), ("step_mut", C.c_void_p), ("workspace", C.c_void_p),
-                ("workspace_bytes", C.c_size_t)]
+                ("workspace_bytes", C.c_size_t), ("last_obs", C.c_void_p)]
 
 
 _lib = None
@@ -72,7 +74,7 @@ def load() -> C.CDLL:
     cfg, bt = C.POINTER(SpinConfig), C.POINTER(SpinBatch)
     sig = {
         "spin_predict_blocks": [cfg, bt, P, I64, P, I64, P, P, P],
-        "spin_select_blocks": [cfg, bt, P, P, P, P, P, P],
+        "spin_select_blocks": [cfg, bt, P, P, P, P, P, P, P],
         "spin_sparse_index_score": [cfg, bt, P, P, P, P, P, I64, P, P, P, I64, P, SZ, P],
         "spin_topk": [cfg, bt, P, I64, P, P, P, P, SZ, P],
         "spin_ema_update": [cfg, bt, P, I64, P, P, P, P, I64, P, I64, P, P],

@@ -35,6 +35,8 @@ def _stream(stream) -> Optional[int]:
 
 
 _POOL = {"max": L.SPIN_POOL_MAX, "top4": L.SPIN_POOL_TOP4, "mean": L.SPIN_POOL_MEAN}
+_EXPLORE = {"random": 0, "age": L.SPIN_EXPLORE_AGE, "staleness": L.SPIN_EXPLORE_STALENESS}
+_REDUCE = {"A1": 0, "A0": L.SPIN_REDUCE_A0, "A2": L.SPIN_REDUCE_A2}
 
 
 def config(*, topk: int, sparsity_bp: int, explore_bp: int = 500, ema_alpha: float = 0.9,
@@ -42,11 +44,13 @@ def config(*, topk: int, sparsity_bp: int, explore_bp: int = 500, ema_alpha: flo
            q_dtype: torch.dtype = torch.bfloat16, layer: int = 0, seed: int = 0x5350494E,
            n_heads: int = 64, head_dim: int = 128, block_size: int = 64, pooling: str = "max",
            mtp_row0_mask: bool = False, mtp_row0_update: bool = False,
-           explore_per_row: bool = False) -> L.SpinConfig:
+           explore_per_row: bool = False, explore: str = "random",
+           reduction: str = "A1") -> L.SpinConfig:
     """spin_config; the keyword variants map to spin_config.flags (defaults: the paper's)."""
     flags = (_POOL[pooling] | (L.SPIN_MTP_ROW0_MASK if mtp_row0_mask else 0)
              | (L.SPIN_MTP_ROW0_UPDATE if mtp_row0_update else 0)
-             | (L.SPIN_EXPLORE_PER_ROW if explore_per_row else 0))
+             | (L.SPIN_EXPLORE_PER_ROW if explore_per_row else 0)
+             | _EXPLORE[explore] | _REDUCE[reduction])
     return L.SpinConfig(n_heads=n_heads, head_dim=head_dim, block_size=block_size, topk=topk,
                         sparsity_bp=sparsity_bp, explore_bp=explore_bp, ema_alpha=ema_alpha,
                         combine=L.SPIN_COMBINE_SUM if combine == "sum" else L.SPIN_COMBINE_MAX,
@@ -73,9 +77,11 @@ def spin_predict_blocks(cfg, bt, V, D, S, stream=None, v_max=None):
                                          _p(S), _stream(stream)))
 
 
-def spin_select_blocks(cfg, bt, S, row_code, sel, n_sel, budget=None, stream=None):
+def spin_select_blocks(cfg, bt, S, row_code, sel, n_sel, budget=None, stream=None,
+                       last_obs=None):
     L.check(L.load().spin_select_blocks(C.byref(cfg), C.byref(bt), _p(S), _p(budget),
-                                        _p(row_code), _p(sel), _p(n_sel), _stream(stream)))
+                                        _p(last_obs), _p(row_code), _p(sel), _p(n_sel),
+                                        _stream(stream)))
 
 
 def spin_sparse_index_score(cfg, bt, q, w, k_pages, k_scale, page_table, sel, n_sel, z,
@@ -118,7 +124,7 @@ def spin_reset_state(V, D, step, stream=None, v_max=None):
 
 def step_io(*, V, D, q, w, k_pages, k_scale, page_table, S, row_code, sel, n_sel, z, topk_idx,
             budget=None, n_valid=None, q_pos_mut=None, step_mut=None, workspace=None,
-            v_max=None):
+            v_max=None, last_obs=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return L.SpinStepIO(V=_p(V), v_ld=_ld(V), D=_p(D), d_ld=_ld(D), v_max=_p(v_max), q=_p(q),
                         w=_p(w),
@@ -126,7 +132,8 @@ def step_io(*, V, D, q, w, k_pages, k_scale, page_table, S, row_code, sel, n_sel
                         pt_ld=_ld(page_table), budget=_p(budget), n_valid=_p(n_valid), S=_p(S),
                         row_code=_p(row_code), sel=_p(sel), n_sel=_p(n_sel), z=_p(z),
                         z_ld=_ld(z), topk_idx=_p(topk_idx), q_pos_mut=_p(q_pos_mut),
-                        step_mut=_p(step_mut), workspace=_p(workspace), workspace_bytes=ws_bytes)
+                        step_mut=_p(step_mut), workspace=_p(workspace), workspace_bytes=ws_bytes,
+                        last_obs=_p(last_obs))
 
 
 def spin_step(cfg, bt, io, defer_ema: bool = False, stream=None):

@@ -122,7 +122,7 @@ template <int EPT>
 __device__ __forceinline__ void union_row(int rows, int n_use, int max_blocks, int r, int B,
                                           const uint8_t* __restrict__ code,
                                           int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
-                                          int* sh) {
+                                          int* sh, int32_t* last_obs, int t) {
   const int j0 = threadIdx.x * EPT;
   uint32_t any = 0u;
   for (int row = 0; row < n_use; ++row) {  // the first n_use rows' masks
@@ -132,6 +132,7 @@ __device__ __forceinline__ void union_row(int rows, int n_use, int max_blocks, i
       if (j0 + e < B && crow[j0 + e] != SPIN_CODE_SKIP) any |= 1u << e;
   }
   compact_blocks<EPT>(any, max_blocks, sel + (int64_t)r * max_blocks, n_sel + r, sh);
+  record_observed<EPT>(last_obs ? last_obs + (int64_t)r * max_blocks : nullptr, j0, B, any, t);
 }
 
 template <int EPT>
@@ -153,15 +154,149 @@ template <int EPT>
 __global__ __launch_bounds__(kSelThreads) void k_union(int rows, int n_use, int max_blocks,
                                                        const int32_t* __restrict__ ctx,
                                                        const int32_t* __restrict__ qpos,
+                                                       const int32_t* __restrict__ step,
                                                        const uint8_t* __restrict__ code,
                                                        int32_t* __restrict__ sel,
-                                                       int32_t* __restrict__ n_sel) {
+                                                       int32_t* __restrict__ n_sel,
+                                                       int32_t* last_obs) {
   __shared__ int sh[32];
   const int r = blockIdx.x;
   const int N = ctx[r];
   const bool bad = request_error(N, qpos[r], rows, max_blocks, 0, 0) != 0;
   const int B = bad ? 0 : (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
-  union_row<EPT>(rows, n_use, max_blocks, r, B, code, sel, n_sel, sh);
+  union_row<EPT>(rows, n_use, max_blocks, r, B, code, sel, n_sel, sh, last_obs, step[r]);
+}
+
+// ---------------------------------------------------------------------------
+// Block reduction A2 (Sec. 4.6): block scores straight from block-level
+// states, S[r][row][j] = C(V[j], D[floor(q_row / 64) - j]).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_predict_a2(int combine, int rows, int max_blocks,
+                                                    const int32_t* __restrict__ ctx,
+                                                    const int32_t* __restrict__ qpos,
+                                                    const float* __restrict__ V, int64_t v_ld,
+                                                    const float* __restrict__ D, int64_t d_ld,
+                                                    float* __restrict__ S, int32_t* err,
+                                                    int32_t* __restrict__ qpos_snap) {
+  const int r = blockIdx.z, row = blockIdx.y;
+  const int N = ctx[r], q0 = qpos[r];
+  if (qpos_snap && blockIdx.x == 0 && row == 0 && threadIdx.x == 0) qpos_snap[r] = q0;
+  const int e = request_error(N, q0, rows, max_blocks, v_ld, d_ld);
+  if (e) {
+    if (row == 0 && blockIdx.x == 0 && threadIdx.x == 0) raise_error(err, e);
+    return;
+  }
+  const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= B) return;
+  const int bq = (q0 + row) / SPIN_BLOCK;
+  const float v = V[(int64_t)r * v_ld + j], d = D[(int64_t)r * d_ld + (bq - j)];
+  const float m = combine == SPIN_COMBINE_SUM ? __fadd_rn(v, d) : fmaxf(v, d);
+  S[((int64_t)r * rows + row) * max_blocks + j] = m + 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Block reduction A0 (Sec. 4.6): the predicted slot scores of every slot,
+// C(V[i], D[q_row - i]), written where the indexer scores go (z, block j at
+// [64 j, 64 j + 64)) with every block listed in sel, so the top-K kernels
+// can pick each row's K largest; then the blocks holding them.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_predict_slots(int combine, int rows, int max_blocks,
+                                                       const int32_t* __restrict__ ctx,
+                                                       const int32_t* __restrict__ qpos,
+                                                       const float* __restrict__ V, int64_t v_ld,
+                                                       const float* __restrict__ D, int64_t d_ld,
+                                                       float* __restrict__ z, int64_t z_ld,
+                                                       int32_t* __restrict__ sel,
+                                                       int32_t* __restrict__ n_sel) {
+  const int r = blockIdx.z, row = blockIdx.y;
+  const int N = ctx[r], q0 = qpos[r];
+  const bool bad = request_error(N, q0, rows, max_blocks, v_ld, d_ld) != 0;
+  const int B = bad ? 0 : (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row == 0 && i == 0) n_sel[r] = B;
+  if (row == 0 && i < max_blocks) sel[(int64_t)r * max_blocks + i] = i < B ? i : -1;
+  if (i >= SPIN_BLOCK * B) return;
+  const int q = q0 + row;
+  float zhat = 0.0f;
+  if (i < N) {
+    const float v = V[(int64_t)r * v_ld + i], d = D[(int64_t)r * d_ld + (q - i)];
+    zhat = combine == SPIN_COMBINE_SUM ? __fadd_rn(v, d) : fmaxf(v, d);
+  }
+  z[((int64_t)r * rows + row) * z_ld + i] = zhat + 0.0f;
+}
+
+// The row's A0 mask from its top-K predicted slots (topk: ascending slot ids,
+// -1 padded): every block holding one, the forced blocks, then
+// floor(|mask| gamma) explored blocks from the rest under the policy.
+template <int EPT>
+__global__ __launch_bounds__(kSelectThreads) void k_a0_select(
+    SelectArgs a, const int32_t* __restrict__ ctx, const int32_t* __restrict__ qpos,
+    const int32_t* __restrict__ step, const int32_t* __restrict__ req_id,
+    const float* __restrict__ S, const int32_t* __restrict__ topk, int compact) {
+  __shared__ SelectLds L;
+  __shared__ uint8_t hit[SPIN_MAX_BLOCKS];
+  const int row = blockIdx.x, r = blockIdx.y;
+  const int N = ctx[r];
+  const bool bad = request_error(N, qpos[r], a.rows, a.max_blocks, 0, 0) != 0;
+  const int B = bad ? 0 : (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  const int t = step[r];
+  const int j0 = threadIdx.x * EPT;
+  for (int j = threadIdx.x; j < a.max_blocks; j += kSelectThreads) hit[j] = 0;
+  __syncthreads();
+  if (B > 0 && t > 0) {
+    const int32_t* trow = topk + ((int64_t)r * a.rows + row) * a.K;
+    for (int k = threadIdx.x; k < a.K; k += kSelectThreads) {
+      const int s = trow[k];
+      if (s >= 0 && s < N) hit[s >> 6] = 1;
+    }
+  }
+  __syncthreads();
+  uint8_t* crow = a.code + ((int64_t)r * a.rows + row) * a.max_blocks;
+  uint8_t c[EPT];
+  uint32_t chosen = 0u, elig = 0u;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int j = j0 + e;
+    c[e] = SPIN_CODE_SKIP;
+    if (j >= B) continue;
+    if (t == 0) c[e] = SPIN_CODE_DENSE;
+    else if (j == 0 || j == B - 1) c[e] = SPIN_CODE_FORCED;
+    else if (hit[j]) c[e] = SPIN_CODE_RANKED;
+    if (c[e] != SPIN_CODE_SKIP) chosen |= 1u << e;
+    else elig |= 1u << e;
+  }
+  const int m = block_sum_i32<kSelectThreads>(__popc(chosen), L.sh);
+  // at most the blocks left outside the mask
+  const int n_e = t > 0 ? min((int)((int64_t)m * a.explore_bp / 10000), B - m) : 0;
+  if (n_e > 0) {
+    const int32_t* orow = a.last_obs ? a.last_obs + (int64_t)r * a.max_blocks : nullptr;
+    const float* Srow = S + ((int64_t)r * a.rows + row) * a.max_blocks;
+    uint32_t pk[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int j = j0 + e;
+      const bool in = j < B;
+      const int obs = a.policy != kExploreRandom && orow && in ? orow[j] : 0;
+      const float sv = a.policy == kExploreStaleness && in ? Srow[j] : 0.0f;
+      pk[e] = policy_key(a, j, t, row, req_id[r], sv, obs);
+    }
+    const uint32_t expl = block_select_top<EPT, kSelectThreads>(pk, elig, n_e, L.hist, L.sh,
+                                                                L.tmpu);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if (expl >> e & 1u) c[e] = SPIN_CODE_EXPLORED;
+    chosen |= expl;
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (j0 + e < B) crow[j0 + e] = c[e];
+  if (compact) {
+    compact_blocks<EPT, kSelectThreads>(chosen, a.max_blocks, a.sel + (int64_t)r * a.max_blocks,
+                                        a.n_sel + r, L.sh);
+    record_observed<EPT>(a.last_obs ? a.last_obs + (int64_t)r * a.max_blocks : nullptr, j0, B,
+                         chosen, t);
+  }
 }
 
 __global__ void k_advance(int R, int rows, const int32_t* __restrict__ n_valid,
@@ -221,11 +356,16 @@ hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float
 }
 
 static SelectArgs select_args(const spin_config& c, const spin_batch& b, uint8_t* code,
-                              int32_t* sel, int32_t* n_sel) {
+                              int32_t* sel, int32_t* n_sel, int32_t* last_obs) {
+  const int pol = c.flags & SPIN_EXPLORE_POLICY_MASK;
   return SelectArgs{c.topk, c.sparsity_bp, c.explore_bp, c.layer,
                     (c.flags & SPIN_EXPLORE_PER_ROW) != 0,
                     (uint32_t)(c.seed & 0xFFFFFFFFu), (uint32_t)(c.seed >> 32), b.n_rows,
-                    b.max_blocks, code, sel, n_sel};
+                    b.max_blocks, code, sel, n_sel,
+                    pol == SPIN_EXPLORE_AGE ? kExploreAge
+                                            : pol == SPIN_EXPLORE_STALENESS ? kExploreStaleness
+                                                                            : kExploreRandom,
+                    last_obs};
 }
 
 PredictPlan predict_plan(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
@@ -247,45 +387,90 @@ static int select_ept(int max_blocks) {
 template <int EPT>
 static void select_t(const spin_config& c, const spin_batch& b, const float* S,
                      const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                     hipStream_t st) {
+                     int32_t* last_obs, hipStream_t st) {
   const int compact = b.n_rows == 1;
   hipLaunchKernelGGL(k_select<EPT>, dim3(b.n_rows, b.batch), dim3(kSelectThreads), 0, st,
-                     select_args(c, b, code, sel, n_sel), b.ctx_len, b.q_pos, b.step, b.req_id,
-                     S, budget, compact);
+                     select_args(c, b, code, sel, n_sel, last_obs), b.ctx_len, b.q_pos, b.step,
+                     b.req_id, S, budget, compact);
+}
+
+template <int EPT>
+static void a0_select_t(const spin_config& c, const spin_batch& b, const float* S,
+                        const int32_t* topk, uint8_t* code, int32_t* sel, int32_t* n_sel,
+                        int32_t* last_obs, hipStream_t st) {
+  const int compact = b.n_rows == 1;
+  hipLaunchKernelGGL(k_a0_select<EPT>, dim3(b.n_rows, b.batch), dim3(kSelectThreads), 0, st,
+                     select_args(c, b, code, sel, n_sel, last_obs), b.ctx_len, b.q_pos, b.step,
+                     b.req_id, S, topk, compact);
 }
 
 template <int EPT>
 static void union_t(const spin_config& c, const spin_batch& b, uint8_t* code, int32_t* sel,
-                    int32_t* n_sel, hipStream_t st) {
+                    int32_t* n_sel, int32_t* last_obs, hipStream_t st) {
   // row-0 sharing scores row 0's mask alone
   const int n_use = (c.flags & SPIN_MTP_ROW0_MASK) ? 1 : b.n_rows;
   hipLaunchKernelGGL(k_union<EPT>, dim3(b.batch), dim3(kSelThreads), 0, st, b.n_rows, n_use,
-                     b.max_blocks, b.ctx_len, b.q_pos, code, sel, n_sel);
+                     b.max_blocks, b.ctx_len, b.q_pos, b.step, code, sel, n_sel, last_obs);
+}
+
+static void launch_union(const spin_config& c, const spin_batch& b, uint8_t* code, int32_t* sel,
+                         int32_t* n_sel, int32_t* last_obs, hipStream_t st) {
+  const int eu = (b.max_blocks + kSelThreads - 1) / kSelThreads;
+  if (eu <= 1) union_t<1>(c, b, code, sel, n_sel, last_obs, st);
+  else if (eu <= 2) union_t<2>(c, b, code, sel, n_sel, last_obs, st);
+  else if (eu <= 4) union_t<4>(c, b, code, sel, n_sel, last_obs, st);
+  else union_t<8>(c, b, code, sel, n_sel, last_obs, st);
 }
 
 SelectPlan select_plan(const spin_config& c, const spin_batch& b, const float* S,
-                       const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel) {
-  return SelectPlan{select_args(c, b, code, sel, n_sel),
+                       const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
+                       int32_t* last_obs) {
+  return SelectPlan{select_args(c, b, code, sel, n_sel, last_obs),
                     SelectInputs{b.ctx_len, b.q_pos, b.step, b.req_id, S, budget}, b.batch,
                     select_ept(b.max_blocks)};
 }
 
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                         hipStream_t st) {
+                         int32_t* last_obs, hipStream_t st) {
   switch (select_ept(b.max_blocks)) {
-    case 1: select_t<1>(c, b, S, budget, code, sel, n_sel, st); break;
-    case 2: select_t<2>(c, b, S, budget, code, sel, n_sel, st); break;
-    case 4: select_t<4>(c, b, S, budget, code, sel, n_sel, st); break;
-    default: select_t<8>(c, b, S, budget, code, sel, n_sel, st); break;
+    case 1: select_t<1>(c, b, S, budget, code, sel, n_sel, last_obs, st); break;
+    case 2: select_t<2>(c, b, S, budget, code, sel, n_sel, last_obs, st); break;
+    case 4: select_t<4>(c, b, S, budget, code, sel, n_sel, last_obs, st); break;
+    default: select_t<8>(c, b, S, budget, code, sel, n_sel, last_obs, st); break;
   }
-  if (b.n_rows > 1) {  // union of the rows' masks
-    const int eu = (b.max_blocks + kSelThreads - 1) / kSelThreads;
-    if (eu <= 1) union_t<1>(c, b, code, sel, n_sel, st);
-    else if (eu <= 2) union_t<2>(c, b, code, sel, n_sel, st);
-    else if (eu <= 4) union_t<4>(c, b, code, sel, n_sel, st);
-    else union_t<8>(c, b, code, sel, n_sel, st);
+  if (b.n_rows > 1) launch_union(c, b, code, sel, n_sel, last_obs, st);  // the rows' masks
+  return hipGetLastError();
+}
+
+hipError_t launch_predict_a2(const spin_config& c, const spin_batch& b, const float* V,
+                             int64_t v_ld, const float* D, int64_t d_ld, float* S,
+                             hipStream_t st, int32_t* qpos_snap) {
+  dim3 grid((b.max_blocks + 255) / 256, b.n_rows, b.batch);
+  hipLaunchKernelGGL(k_predict_a2, grid, dim3(256), 0, st, c.combine, b.n_rows, b.max_blocks,
+                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld, S, b.err, qpos_snap);
+  return hipGetLastError();
+}
+
+hipError_t launch_predict_slots(const spin_config& c, const spin_batch& b, const float* V,
+                                int64_t v_ld, const float* D, int64_t d_ld, float* z,
+                                int64_t z_ld, int32_t* sel, int32_t* n_sel, hipStream_t st) {
+  dim3 grid((SPIN_BLOCK * b.max_blocks + 255) / 256, b.n_rows, b.batch);
+  hipLaunchKernelGGL(k_predict_slots, grid, dim3(256), 0, st, c.combine, b.n_rows, b.max_blocks,
+                     b.ctx_len, b.q_pos, V, v_ld, D, d_ld, z, z_ld, sel, n_sel);
+  return hipGetLastError();
+}
+
+hipError_t launch_a0_select(const spin_config& c, const spin_batch& b, const float* S,
+                            const int32_t* topk, uint8_t* code, int32_t* sel, int32_t* n_sel,
+                            int32_t* last_obs, hipStream_t st) {
+  switch (select_ept(b.max_blocks)) {
+    case 1: a0_select_t<1>(c, b, S, topk, code, sel, n_sel, last_obs, st); break;
+    case 2: a0_select_t<2>(c, b, S, topk, code, sel, n_sel, last_obs, st); break;
+    case 4: a0_select_t<4>(c, b, S, topk, code, sel, n_sel, last_obs, st); break;
+    default: a0_select_t<8>(c, b, S, topk, code, sel, n_sel, last_obs, st); break;
   }
+  if (b.n_rows > 1) launch_union(c, b, code, sel, n_sel, last_obs, st);
   return hipGetLastError();
 }
 

@@ -98,6 +98,8 @@ __device__ __forceinline__ void predict_wave(int combine, int pooling, int N, in
 // ---------------------------------------------------------------------------
 constexpr int kSelectThreads = 1024;
 
+enum { kExploreRandom = 0, kExploreAge = 1, kExploreStaleness = 2 };
+
 struct SelectArgs {
   int K, sparsity_bp, explore_bp, layer, per_row;  // per_row: SPIN_EXPLORE_PER_ROW
   uint32_t seed_lo, seed_hi;
@@ -105,7 +107,28 @@ struct SelectArgs {
   uint8_t* code;   // [R][rows][max_blocks]
   int32_t* sel;    // [R][max_blocks]
   int32_t* n_sel;  // [R]
+  int policy;          // kExplore*
+  int32_t* last_obs;   // optional [R][max_blocks]: step of each block's last observation
 };
+
+// Exploration key of block j (larger = taken first; ties: lower block) under
+// the row's policy (Sec. 3.2.1; Sec. 4.6, "Staleness mitigation").
+__device__ __forceinline__ uint32_t policy_key(const SelectArgs& a, int j, int t, int row,
+                                               int rid, float s, int obs) {
+  if (a.policy == kExploreAge) return ~(uint32_t)obs;  // smallest last_obs first
+  if (a.policy == kExploreStaleness) return float_key(s * (float)(t - obs));
+  return explore_key(j, t, a.layer + (a.per_row ? 65536 * row : 0), rid, a.seed_lo, a.seed_hi);
+}
+
+// Record step t for the chosen blocks of this thread (the union of a step).
+template <int EPT>
+__device__ __forceinline__ void record_observed(int32_t* last_obs_r, int j0, int B,
+                                                uint32_t chosen, int t) {
+  if (!last_obs_r) return;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if ((chosen >> e & 1u) && j0 + e < B) last_obs_r[j0 + e] = t;
+}
 
 struct SelectLds {
   int hist[kRadixHist];
@@ -172,13 +195,15 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int r, int row, 
     chosen |= ranked;
     elig &= ~ranked;
     if (n_e > 0) {
-      // exploration priorities in registers; the rows share them (the
-      // counter carries no row) unless each row draws its own
+      // exploration keys in registers; random priorities are shared by the
+      // rows (the counter carries no row) unless each row draws its own
+      const int32_t* orow = a.last_obs ? a.last_obs + (int64_t)r * a.max_blocks : nullptr;
       uint32_t pk[EPT];
 #pragma unroll
-      for (int e = 0; e < EPT; ++e)
-        pk[e] = explore_key(j0 + e, t, a.layer + (a.per_row ? 65536 * row : 0), rid, a.seed_lo,
-                            a.seed_hi);
+      for (int e = 0; e < EPT; ++e) {
+        const int obs = a.policy != kExploreRandom && orow && j0 + e < B ? orow[j0 + e] : 0;
+        pk[e] = policy_key(a, j0 + e, t, row, rid, sv[e], obs);
+      }
       const uint32_t expl =
           block_select_top<EPT, kSelectThreads>(pk, elig, n_e, L.hist, L.sh, L.tmpu);
 #pragma unroll
@@ -190,9 +215,13 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int r, int row, 
 #pragma unroll
   for (int e = 0; e < EPT; ++e)
     if (j0 + e < B) crow[j0 + e] = c[e];
-  if (compact)
+  if (compact) {
     compact_blocks<EPT, kSelectThreads>(chosen, a.max_blocks, a.sel + (int64_t)r * a.max_blocks,
                                         a.n_sel + r, L.sh);
+    // the union is this row's mask: its blocks are observed at step t
+    record_observed<EPT>(a.last_obs ? a.last_obs + (int64_t)r * a.max_blocks : nullptr, j0, B,
+                         chosen, t);
+  }
 }
 
 // ---------------------------------------------------------------------------

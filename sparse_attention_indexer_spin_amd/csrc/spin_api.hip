@@ -51,7 +51,9 @@ spin_status check_config(const char* fn, const spin_config* c) {
   if (c->key_dtype < SPIN_F32 || c->key_dtype > SPIN_FP8_E4M3 || c->q_dtype < SPIN_F32 ||
       c->q_dtype > SPIN_BF16)
     return fail(SPIN_E_UNSUPPORTED, "%s: unknown dtype", fn);
-  if ((c->flags & ~SPIN_FLAGS_ALL) != 0 || (c->flags & SPIN_POOL_MASK) == SPIN_POOL_MASK)
+  if ((c->flags & ~SPIN_FLAGS_ALL) != 0 || (c->flags & SPIN_POOL_MASK) == SPIN_POOL_MASK ||
+      (c->flags & SPIN_EXPLORE_POLICY_MASK) == SPIN_EXPLORE_POLICY_MASK ||
+      (c->flags & SPIN_REDUCE_MASK) == SPIN_REDUCE_MASK)
     return fail(SPIN_E_SHAPE, "%s: unknown flags 0x%x", fn, c->flags);
   if ((c->flags & SPIN_EXPLORE_PER_ROW) && (c->layer < 0 || c->layer >= 65536))
     return fail(SPIN_E_SHAPE, "%s: per-row exploration needs 0 <= layer < 65536", fn);
@@ -97,6 +99,12 @@ spin_status check_z(const char* fn, const spin_batch* b, const float* z, int64_t
     return fail(SPIN_E_SHAPE, "%s: z_ld %lld must be >= 64*max_blocks and a multiple of 4", fn,
                 (long long)z_ld);
   return SPIN_OK;
+}
+
+bool reduce_a0(const spin_config& c) { return (c.flags & SPIN_REDUCE_MASK) == SPIN_REDUCE_A0; }
+bool reduce_a2(const spin_config& c) { return (c.flags & SPIN_REDUCE_MASK) == SPIN_REDUCE_A2; }
+bool explore_needs_obs(const spin_config& c) {
+  return (c.flags & SPIN_EXPLORE_POLICY_MASK) != 0;
 }
 
 }  // namespace
@@ -166,13 +174,16 @@ spin_status spin_predict_blocks(const spin_config* cfg, const spin_batch* bt, co
   SPIN_CHECK(check_state(fn, bt, V, v_ld, D, d_ld));
   SPIN_REQUIRE(S);
   if (bt->batch == 0) return SPIN_OK;
+  if (reduce_a2(*cfg))
+    return hip_status(spin::launch_predict_a2(*cfg, *bt, V, v_ld, D, d_ld, S,
+                                              (hipStream_t)stream), fn);
   return hip_status(spin::launch_predict(*cfg, *bt, V, v_ld, D, d_ld, v_max, S, (hipStream_t)stream),
                     fn);
 }
 
 spin_status spin_select_blocks(const spin_config* cfg, const spin_batch* bt, const float* S,
-                               const int32_t* budget, uint8_t* row_code, int32_t* sel,
-                               int32_t* n_sel, void* stream) {
+                               const int32_t* budget, int32_t* last_obs, uint8_t* row_code,
+                               int32_t* sel, int32_t* n_sel, void* stream) {
   const char* fn = "spin_select_blocks";
   SPIN_CHECK(check_config(fn, cfg));
   SPIN_CHECK(check_batch(fn, bt));
@@ -180,8 +191,12 @@ spin_status spin_select_blocks(const spin_config* cfg, const spin_batch* bt, con
   SPIN_REQUIRE(row_code);
   SPIN_REQUIRE(sel);
   SPIN_REQUIRE(n_sel);
+  if (reduce_a0(*cfg))
+    return fail(SPIN_E_UNSUPPORTED, "%s: block reduction A0 selects from predicted slot scores; "
+                "it runs in spin_step / spin_step_plan", fn);
+  if (explore_needs_obs(*cfg)) SPIN_REQUIRE(last_obs);
   if (bt->batch == 0) return SPIN_OK;
-  return hip_status(spin::launch_select(*cfg, *bt, S, budget, row_code, sel, n_sel,
+  return hip_status(spin::launch_select(*cfg, *bt, S, budget, row_code, sel, n_sel, last_obs,
                                         (hipStream_t)stream), fn);
 }
 
@@ -264,6 +279,9 @@ spin_status spin_ema_update(const spin_config* cfg, const spin_batch* bt, const 
   SPIN_REQUIRE(sel);
   SPIN_REQUIRE(n_sel);
   if (bt->batch == 0) return SPIN_OK;
+  if (reduce_a2(*cfg))
+    return hip_status(spin::launch_ema_a2(*cfg, *bt, z, z_ld, sel, n_sel, n_valid, V, v_ld, D,
+                                          d_ld, (hipStream_t)stream), fn);
   return hip_status(spin::launch_ema(*cfg, *bt, z, z_ld, sel, n_sel, n_valid, V, v_ld, D, d_ld,
                                      v_max, (hipStream_t)stream), fn);
 }
@@ -307,6 +325,7 @@ spin_status check_step(const char* fn, const spin_config* cfg, const spin_batch*
   const size_t need = spin::step_workspace_bytes(*cfg, bt->batch, bt->n_rows, bt->max_blocks);
   if (!io->workspace || io->workspace_bytes < need)
     return fail(SPIN_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  if (explore_needs_obs(*cfg)) SPIN_REQUIRE(io->last_obs);
   return SPIN_OK;
 }
 
@@ -320,10 +339,30 @@ int32_t* step_qsnap(const spin_config& c, const spin_batch& b, const spin_step_i
 // Predict + select (+ union), arguments already checked.
 spin_status issue_plan(const spin_config& c, const spin_batch& b, const spin_step_io& io,
                        hipStream_t st) {
-  SPIN_CHECK(hip_status(spin::launch_predict(c, b, io.V, io.v_ld, io.D, io.d_ld, io.v_max, io.S,
-                                             st, step_qsnap(c, b, io)),
-                        "spin_step/predict"));
-  return hip_status(spin::launch_select(c, b, io.S, io.budget, io.row_code, io.sel, io.n_sel, st),
+  if (reduce_a2(c)) {
+    SPIN_CHECK(hip_status(spin::launch_predict_a2(c, b, io.V, io.v_ld, io.D, io.d_ld, io.S, st,
+                                                  step_qsnap(c, b, io)),
+                          "spin_step/predict(A2)"));
+  } else {
+    SPIN_CHECK(hip_status(spin::launch_predict(c, b, io.V, io.v_ld, io.D, io.d_ld, io.v_max,
+                                               io.S, st, step_qsnap(c, b, io)),
+                          "spin_step/predict"));
+  }
+  if (reduce_a0(c)) {
+    // A0: every slot's predicted score into z (all blocks listed), each
+    // row's top-K of it into topk_idx, then the blocks holding them
+    SPIN_CHECK(hip_status(spin::launch_predict_slots(c, b, io.V, io.v_ld, io.D, io.d_ld, io.z,
+                                                     io.z_ld, io.sel, io.n_sel, st),
+                          "spin_step/predict slots(A0)"));
+    SPIN_CHECK(hip_status(spin::launch_topk(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.topk_idx,
+                                            io.workspace, io.workspace_bytes, st, false),
+                          "spin_step/slot top-K(A0)"));
+    return hip_status(spin::launch_a0_select(c, b, io.S, io.topk_idx, io.row_code, io.sel,
+                                             io.n_sel, io.last_obs, st),
+                      "spin_step/select(A0)");
+  }
+  return hip_status(spin::launch_select(c, b, io.S, io.budget, io.row_code, io.sel, io.n_sel,
+                                        io.last_obs, st),
                     "spin_step/select");
 }
 
@@ -338,6 +377,16 @@ spin_status issue_finish(const spin_config& c, const spin_batch& b, const spin_s
                                            io.page_table, io.pt_ld, io.sel, io.n_sel, io.z,
                                            io.z_ld, st, prefilter ? &sink : nullptr),
                         "spin_step/score"));
+  if (reduce_a2(c)) {  // top-K, then the block-level EMA update + counter advance
+    SPIN_CHECK(hip_status(spin::launch_topk(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.topk_idx,
+                                            io.workspace, io.workspace_bytes, st, prefilter),
+                          "spin_step/topk"));
+    if (defer_ema) return SPIN_OK;
+    return hip_status(spin::launch_ema_a2(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.n_valid, io.V,
+                                          io.v_ld, io.D, io.d_ld, st, qsnap, io.q_pos_mut,
+                                          io.step_mut),
+                      "spin_step/ema+advance(A2)");
+  }
   if (prefilter && !defer_ema)  // top-K beside the EMA update, one launch
     return hip_status(spin::launch_topk_ema(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.topk_idx,
                                             io.workspace, io.n_valid, io.V, io.v_ld, io.D,
@@ -370,7 +419,7 @@ spin_status issue_finish_with_plan(const spin_config& c, const spin_batch& b,
   const spin::PredictPlan pp = spin::predict_plan(nc, nb, nio.V, nio.v_ld, nio.D, nio.d_ld,
                                                   nio.v_max, nio.S, step_qsnap(nc, nb, nio));
   const spin::SelectPlan sp = spin::select_plan(nc, nb, nio.S, nio.budget, nio.row_code,
-                                                nio.sel, nio.n_sel);
+                                                nio.sel, nio.n_sel, nio.last_obs);
   SPIN_CHECK(hip_status(spin::launch_score(c, b, io.q, io.w, io.k_pages, io.k_scale,
                                            io.page_table, io.pt_ld, io.sel, io.n_sel, io.z,
                                            io.z_ld, st, &sink, &pp),
@@ -386,6 +435,11 @@ spin_status issue_finish_with_plan(const spin_config& c, const spin_batch& b,
 // defer_ema): q positions from the step's snapshot.
 spin_status issue_ema(const spin_config& c, const spin_batch& b, const spin_step_io& io,
                       hipStream_t st) {
+  if (reduce_a2(c))
+    return hip_status(spin::launch_ema_a2(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.n_valid, io.V,
+                                          io.v_ld, io.D, io.d_ld, st, step_qsnap(c, b, io),
+                                          io.q_pos_mut, io.step_mut),
+                      "spin_stack_step/ema+advance(A2)");
   return hip_status(spin::launch_ema(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.n_valid, io.V,
                                      io.v_ld, io.D, io.d_ld, io.v_max, st, step_qsnap(c, b, io),
                                      io.q_pos_mut, io.step_mut),
@@ -649,8 +703,11 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
       }
       if (!planned) SPIN_CHECK(issue_plan(cfgs[l], bts[l], ios[l], mst));
       const int m = l + 1;
+      // (the fused launches run the method's block reduction, A1)
       const bool fuse = m < n_layers && bts[m].batch > 0 && bts[m].n_rows == 1 &&
-                        spin::score_filters(cfgs[l], bts[l]);
+                        spin::score_filters(cfgs[l], bts[l]) &&
+                        (cfgs[l].flags & SPIN_REDUCE_MASK) == 0 &&
+                        (cfgs[m].flags & SPIN_REDUCE_MASK) == 0;
       if (fuse)
         SPIN_CHECK(issue_finish_with_plan(cfgs[l], bts[l], ios[l], cfgs[m], bts[m], ios[m],
                                           defer_ema, mst));

@@ -42,11 +42,33 @@ struct SelectPlan {
 PredictPlan predict_plan(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
                          const float* D, int64_t d_ld, const float* vmax, float* S,
                          int32_t* qpos_snap);
+// last_obs (optional, [R][max_blocks]): the step of each block's last
+// observation, read by the age / staleness exploration policies and set to
+// the step for every block of the union.
 SelectPlan select_plan(const spin_config& c, const spin_batch& b, const float* S,
-                       const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel);
+                       const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
+                       int32_t* last_obs);
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                         hipStream_t st);
+                         int32_t* last_obs, hipStream_t st);
+// Block reduction A2: block scores from block-level states.
+hipError_t launch_predict_a2(const spin_config& c, const spin_batch& b, const float* V,
+                             int64_t v_ld, const float* D, int64_t d_ld, float* S,
+                             hipStream_t st, int32_t* qpos_snap = nullptr);
+// Block reduction A0: every slot's predicted score into z (all blocks listed
+// in sel), then, from the rows' top-K of it, the masks.
+hipError_t launch_predict_slots(const spin_config& c, const spin_batch& b, const float* V,
+                                int64_t v_ld, const float* D, int64_t d_ld, float* z,
+                                int64_t z_ld, int32_t* sel, int32_t* n_sel, hipStream_t st);
+hipError_t launch_a0_select(const spin_config& c, const spin_batch& b, const float* S,
+                            const int32_t* topk, uint8_t* code, int32_t* sel, int32_t* n_sel,
+                            int32_t* last_obs, hipStream_t st);
+// Block reduction A2's EMA update (+ counter advance with qpos_snap, as launch_ema).
+hipError_t launch_ema_a2(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
+                         const int32_t* sel, const int32_t* n_sel, const int32_t* n_valid,
+                         float* V, int64_t v_ld, float* D, int64_t d_ld, hipStream_t st,
+                         const int32_t* qpos_snap = nullptr, int32_t* qpos_out = nullptr,
+                         int32_t* step_out = nullptr);
 // With a non-null `sink`, kernels that can (score_filters()) also write the
 // top-K candidates; the caller then runs launch_topk with `prefiltered`.
 hipError_t launch_score(const spin_config& c, const spin_batch& b, const void* q, const float* w,

@@ -20,7 +20,8 @@ class SpinLayer:
                  layer: int = 0, seed: int = 0x5350494E, device="cuda", vmax_cache: bool = False,
                  **variants):
         """`variants`: the design variants of api.config (pooling, mtp_row0_mask,
-        mtp_row0_update, explore_per_row); the paper's defaults without them."""
+        mtp_row0_update, explore_per_row, explore, reduction); the paper's
+        defaults without them."""
         self.R, self.rows, self.max_blocks, self.K = batch, n_rows, max_blocks, topk
         self.cfg = api.config(topk=topk, sparsity_bp=sparsity_bp, explore_bp=explore_bp,
                               ema_alpha=ema_alpha, combine=combine, key_dtype=key_dtype,
@@ -37,6 +38,9 @@ class SpinLayer:
         self.v_max = torch.zeros(batch, max_blocks, dtype=torch.float32, device=dev) \
             if vmax_cache else None
         self.S = torch.zeros(batch, n_rows, max_blocks, dtype=torch.float32, device=dev)
+        # the step at which each block was last scored (exploration by block
+        # age / staleness), kept by every step's selection
+        self.last_obs = torch.zeros(batch, max_blocks, **i32)
         self.row_code = torch.zeros(batch, n_rows, max_blocks, dtype=torch.uint8, device=dev)
         self.sel = torch.full((batch, max_blocks), -1, **i32)
         self.n_sel = torch.zeros(batch, **i32)
@@ -63,6 +67,9 @@ class SpinLayer:
 
     def reset(self, stream=None):
         api.spin_reset_state(self.V, self.D, self.step_ctr, stream=stream, v_max=self.v_max)
+        st = torch.cuda.current_stream() if stream is None else stream
+        with torch.cuda.stream(st):
+            self.last_obs.zero_()
 
     def batch(self, n_pages: int):
         if self._bt is None or self.n_pages != n_pages:
@@ -78,7 +85,7 @@ class SpinLayer:
                            page_table=page_table, S=self.S, row_code=self.row_code, sel=self.sel,
                            n_sel=self.n_sel, z=self.z, topk_idx=self.topk_idx, budget=budget,
                            n_valid=n_valid, q_pos_mut=self.q_pos, step_mut=self.step_ctr,
-                           workspace=self.workspace, v_max=self.v_max)
+                           workspace=self.workspace, v_max=self.v_max, last_obs=self.last_obs)
 
     def step(self, q, w, k_pages, k_scale, page_table, n_valid=None, budget=None,
              defer_ema: bool = False, stream=None):

@@ -93,11 +93,23 @@ def test_host_validation_without_gpu(lib):
     assert lib.spin_predict_blocks(C.byref(bad), C.byref(bt), 1, 64, 1, 64, None, 1, None) == 3
     # block size other than 64
     bad = _cfg(block_size=32)
-    assert lib.spin_select_blocks(C.byref(bad), C.byref(bt), 1, None, 1, 1, 1, None) == 3
+    assert lib.spin_select_blocks(C.byref(bad), C.byref(bt), 1, None, None, 1, 1, 1, None) == 3
     # rows out of range
     bt2 = _lib.SpinBatch(batch=1, n_rows=5, max_blocks=16, n_pages=16, ctx_len=1, q_pos=1,
                          step=1, req_id=1, err=None)
-    assert lib.spin_select_blocks(C.byref(cfg), C.byref(bt2), 1, None, 1, 1, 1, None) == 2
+    assert lib.spin_select_blocks(C.byref(cfg), C.byref(bt2), 1, None, None, 1, 1, 1, None) == 2
+    # exploration by block age or staleness needs the last-observed steps
+    for pol in ("age", "staleness"):
+        assert lib.spin_select_blocks(C.byref(_cfg(explore=pol)), C.byref(bt), 1, None, None, 1,
+                                      1, 1, None) == 1
+    # A0 selects inside spin_step only; both policy bits or both reductions: unknown flags
+    assert lib.spin_select_blocks(C.byref(_cfg(reduction="A0")), C.byref(bt), 1, None, 1, 1, 1,
+                                  1, None) == 3
+    both = _cfg()
+    both.flags = _lib.SPIN_EXPLORE_AGE | _lib.SPIN_EXPLORE_STALENESS
+    assert lib.spin_select_blocks(C.byref(both), C.byref(bt), 1, None, 1, 1, 1, 1, None) == 2
+    both.flags = _lib.SPIN_REDUCE_A0 | _lib.SPIN_REDUCE_A2
+    assert lib.spin_select_blocks(C.byref(both), C.byref(bt), 1, None, 1, 1, 1, 1, None) == 2
     # topk out of range
     bad = _cfg(topk=0)
     assert lib.spin_topk(C.byref(bad), C.byref(bt), 1, 1024, 1, 1, 1, None, 0, None) == 2
