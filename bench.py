@@ -352,8 +352,8 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
                   "us_per_step": ms_budget * 1e3,
                   "us_per_step_layer": ms_budget * 1e3 / w.layers,
                   "effective_block_sparsity": 1.0 - chosen / total_blocks,
-                  "levels": [h[1] for h in bstack.level_history],
-                  "allocated_at_steps": [h[0] for h in bstack.level_history]}
+                  "levels_after_last_probe": bstack.levels_now(),
+                  "probe_steps": [t for t in range(1, warmup + steps) if t % probe_period == 0]}
         for lay in bud_layers:
             assert int(lay.err.item()) == 0
     for other in (seq, lays_ema_stream, lays_one_stream):

@@ -448,6 +448,65 @@ spin_status spin_budget_allocate(int32_t policy, int32_t n_layers, int32_t level
                                  int32_t* level_out);
 
 /*
+ * The per-layer budget policy run by a spin_stack itself (blog, "Per-layer
+ * block budgets": a dense probe every P steps measures each layer's miss
+ * curve, and the budgets are re-sized at a fixed total and published to a
+ * device-side table).  With a policy set, spin_stack_step
+ *   - counts its calls since spin_stack_reset_budgets; call t = P, 2P, ... is
+ *     a probe: every layer selects every block (probe_budget);
+ *   - otherwise layer l selects with budget[l] (its level in level_table[l],
+ *     filled by spin_budget_fill); the ios' own budget pointers are ignored;
+ *   - after a probe call's finishes, on the main stream: each layer's miss
+ *     curve (spin_miss_curve into covered / kprime), then one device kernel
+ *     that sums the curves over requests and rows, updates the running miss
+ *     rates (state) and writes the new levels into level_table -- the same
+ *     arithmetic as spin_budget_allocate -- then each layer's budget fill.
+ *     The next call selects with them; nothing waits for the host.
+ * Every layer of the stack takes part (n_layers of the stack), with the same
+ * batch and n_rows; defer_ema is not available with a policy.  Buffers are
+ * device memory owned by the caller:
+ *   level_table i32 [n_layers]; budget i32 [n_layers][batch];
+ *   probe_budget i32 [batch]; covered i32 [n_layers][batch][n_rows][levels + 1];
+ *   kprime i32 [n_layers][batch][n_rows]; state: spin_budget_state_bytes().
+ * spin_stack_set_budget_policy copies the struct (NULL: no policy).
+ * spin_stack_reset_budgets (with the layers' reset, and after their contexts
+ * change) sets every level to target_level, clears the probe history and
+ * fills the budgets, on main_stream.
+ */
+typedef struct spin_budget_policy {
+  int32_t policy;        /* SPIN_BUDGET_MINIMAX | SPIN_BUDGET_PROPORTIONAL          */
+  int32_t probe_period;  /* P >= 1                                                  */
+  int32_t levels;        /* divides 10000                                           */
+  int32_t target_level;  /* 0 .. levels; the level sum is n_layers * target_level  */
+  int32_t* level_table;
+  int32_t* budget;
+  int32_t* probe_budget;
+  int32_t* covered;
+  int32_t* kprime;
+  void* state;
+} spin_budget_policy;
+size_t spin_budget_state_bytes(int32_t n_layers, int32_t levels);
+/*
+ * The device step of the policy on its own, for callers with their own
+ * schedule: from the curves of one probe (covered i32 [n_layers][rows_total]
+ * [levels + 1], kprime i32 [n_layers][rows_total], rows_total = batch x
+ * n_rows), on `stream`: per layer the sums over its rows, then
+ *   SPIN_BUDGET_MINIMAX: the greedy minimax allocation of spin_budget_allocate;
+ *   SPIN_BUDGET_PROPORTIONAL: each layer's miss rate at its current level
+ *     (level_table on entry) added to its running sum in `state`, the probe
+ *     count incremented, and the proportional allocation of the running means;
+ * new levels into level_table.  state (spin_budget_state_bytes()) must be
+ * zero before the first probe.  No host synchronisation.
+ */
+spin_status spin_budget_update(int32_t policy, int32_t n_layers, int32_t levels,
+                               int32_t target_level, int32_t rows_total, const int32_t* covered,
+                               const int32_t* kprime, void* state, int32_t* level_table,
+                               void* stream);
+spin_status spin_stack_set_budget_policy(spin_stack* stack, const spin_budget_policy* policy);
+spin_status spin_stack_reset_budgets(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
+                                     const spin_batch* bts, void* main_stream);
+
+/*
  * Device workspace bytes spin_topk / spin_step need for this shape.  The
  * buffer holds the top-K threshold hints and candidate lists (any initial
  * contents are valid: a hint only changes speed) followed, for spin_step, by

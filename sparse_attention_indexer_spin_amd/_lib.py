@@ -24,7 +24,9 @@ EXPORTS = ["spin_predict_blocks", "spin_select_blocks", "spin_sparse_index_score
            "spin_ema_update", "spin_advance", "spin_reset_state", "spin_step",
            "spin_workspace_bytes", "spin_last_error", "spin_step_plan", "spin_step_finish",
            "spin_stack_create", "spin_stack_destroy", "spin_stack_step", "spin_miss_curve",
-           "spin_budget_fill", "spin_budget_allocate", "spin_step_noalloc", "spin_stack_commit"]
+           "spin_budget_fill", "spin_budget_allocate", "spin_step_noalloc", "spin_stack_commit",
+           "spin_budget_state_bytes", "spin_stack_set_budget_policy", "spin_stack_reset_budgets",
+           "spin_budget_update"]
 SPIN_NOALLOC_WORKSPACE_BYTES = 160 * 1024 * 1024
 SPIN_BUDGET_MINIMAX, SPIN_BUDGET_PROPORTIONAL = 0, 1
 SPIN_POOL_MAX, SPIN_POOL_TOP4, SPIN_POOL_MEAN = 0, 1, 2
@@ -56,6 +58,13 @@ class SpinStepIO(C.Structure):
                 ("z", C.c_void_p), ("z_ld", C.c_int64), ("topk_idx", C.c_void_p),
                 ("q_pos_mut", C.c_void_p), ("step_mut", C.c_void_p), ("workspace", C.c_void_p),
                 ("workspace_bytes", C.c_size_t), ("last_obs", C.c_void_p)]
+
+
+class SpinBudgetPolicy(C.Structure):
+    _fields_ = [("policy", C.c_int32), ("probe_period", C.c_int32), ("levels", C.c_int32),
+                ("target_level", C.c_int32), ("level_table", C.c_void_p), ("budget", C.c_void_p),
+                ("probe_budget", C.c_void_p), ("covered", C.c_void_p), ("kprime", C.c_void_p),
+                ("state", C.c_void_p)]
 
 
 _lib = None
@@ -90,6 +99,9 @@ def load() -> C.CDLL:
         "spin_miss_curve": [cfg, bt, P, P, I32, P, P, P],
         "spin_budget_fill": [cfg, bt, P, I32, P, P],
         "spin_budget_allocate": [I32, I32, I32, I32, P, P, P, P],
+        "spin_stack_set_budget_policy": [P, C.POINTER(SpinBudgetPolicy)],
+        "spin_stack_reset_budgets": [P, I32, cfg, bt, P],
+        "spin_budget_update": [I32, I32, I32, I32, I32, P, P, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -99,6 +111,8 @@ def load() -> C.CDLL:
     lib.spin_stack_destroy.restype = None
     lib.spin_workspace_bytes.argtypes = [cfg, I32, I32, I32]
     lib.spin_workspace_bytes.restype = SZ
+    lib.spin_budget_state_bytes.argtypes = [I32, I32]
+    lib.spin_budget_state_bytes.restype = SZ
     lib.spin_last_error.argtypes = []
     lib.spin_last_error.restype = C.c_char_p
     _lib = lib

@@ -170,6 +170,200 @@ hipError_t launch_budget_fill(const spin_config& c, const spin_batch& b, const i
 }
 
 // ---------------------------------------------------------------------------
+// The allocation on the device, after a probe step (one workgroup): sum each
+// layer's curves over its requests and rows, update the running miss rates
+// (proportional rule), re-size the layers' levels into the level table.  The
+// same arithmetic as the host allocation below, so both give the same levels.
+// State (caller-owned, budget_state_bytes()): f64 miss sums [L], f64 probe
+// count, i64 curve sums [L][levels + 1], i64 valid top-K totals [L].
+// ---------------------------------------------------------------------------
+struct BudgetState {
+  double* miss_sum;
+  double* n_probes;
+  int64_t* cov;
+  int64_t* tot;
+};
+
+__host__ __device__ inline BudgetState budget_state(void* p, int L, int levels) {
+  char* b = static_cast<char*>(p);
+  BudgetState s;
+  s.miss_sum = reinterpret_cast<double*>(b);
+  s.n_probes = s.miss_sum + L;
+  s.cov = reinterpret_cast<int64_t*>(s.n_probes + 1);
+  s.tot = s.cov + (int64_t)L * (levels + 1);
+  return s;
+}
+
+size_t budget_state_bytes(int L, int levels) {
+  const size_t n = 8 * ((size_t)L + 1 + (size_t)L * (levels + 1) + (size_t)L);
+  return (n + 255) & ~size_t(255);
+}
+
+// lane-held (miss numerator, denominator, layer) candidates; the wave's
+// largest miss rate, ties to the lower layer, exactly (products < 2^63)
+__device__ __forceinline__ bool cand_better(int64_t na, int64_t da, int la, int64_t nb, int64_t db,
+                                            int lb) {
+  if (la < 0) return false;
+  if (lb < 0) return true;
+  const int64_t x = na * db, y = nb * da;
+  return x > y || (x == y && la < lb);
+}
+
+__device__ __forceinline__ int64_t shfl_xor_i64(int64_t v, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)v, m), hi = __shfl_xor((int)(v >> 32), m);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+constexpr int kBudgetLanes = 64;
+constexpr int kBudgetMaxPerLane = (SPIN_MAX_LAYERS + kBudgetLanes - 1) / kBudgetLanes;
+
+__global__ __launch_bounds__(256) void k_budget_update(int policy, int L, int levels, int target,
+                                                       int RR, const int32_t* __restrict__ cov,
+                                                       const int32_t* __restrict__ kp,
+                                                       void* state, int32_t* level_table) {
+  const BudgetState st = budget_state(state, L, levels);
+  const int W = levels + 1;
+  for (int i = threadIdx.x; i < L * W; i += blockDim.x) {
+    const int l = i / W, g = i % W;
+    int64_t s = 0;
+    for (int k = 0; k < RR; ++k) s += cov[((int64_t)l * RR + k) * W + g];
+    st.cov[i] = s;
+  }
+  for (int l = threadIdx.x; l < L; l += blockDim.x) {
+    int64_t s = 0;
+    for (int k = 0; k < RR; ++k) s += kp[(int64_t)l * RR + k];
+    st.tot[l] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x >= kBudgetLanes) return;
+  const int lane = threadIdx.x;
+  if (policy == SPIN_BUDGET_MINIMAX) {
+    // raise the layer of the largest miss rate by one level, from all zero
+    int g[kBudgetMaxPerLane];
+#pragma unroll
+    for (int u = 0; u < kBudgetMaxPerLane; ++u) g[u] = 0;
+    const int64_t budget = (int64_t)L * target;
+    for (int64_t it = 0; it < budget; ++it) {
+      int64_t bn = 0, bd = 1;
+      int bl = -1;
+#pragma unroll
+      for (int u = 0; u < kBudgetMaxPerLane; ++u) {
+        const int l = lane + kBudgetLanes * u;
+        if (l >= L || g[u] >= levels) continue;
+        const int64_t t = st.tot[l], c = st.cov[(int64_t)l * W + g[u]];
+        const int64_t n = t == 0 ? 0 : t - c, d = t == 0 ? 1 : t;
+        if (cand_better(n, d, l, bn, bd, bl)) {
+          bn = n;
+          bd = d;
+          bl = l;
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < kBudgetLanes; m <<= 1) {
+        const int64_t on = shfl_xor_i64(bn, m), od = shfl_xor_i64(bd, m);
+        const int ol = __shfl_xor(bl, m);
+        if (cand_better(on, od, ol, bn, bd, bl)) {
+          bn = on;
+          bd = od;
+          bl = ol;
+        }
+      }
+      if (bl < 0) break;  // every layer at the top level
+      if (bl % kBudgetLanes == lane) g[bl / kBudgetLanes] += 1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBudgetMaxPerLane; ++u) {
+      const int l = lane + kBudgetLanes * u;
+      if (l < L) level_table[l] = g[u];
+    }
+    return;
+  }
+  // proportional (lane 0): the running mean of each layer's miss rate at the
+  // level it ran at, then shares of L * target in proportion to miss + 1e-3
+  __shared__ double w[SPIN_MAX_LAYERS], share[SPIN_MAX_LAYERS];
+  __shared__ int fixed[SPIN_MAX_LAYERS], gl[SPIN_MAX_LAYERS];
+  __shared__ bool used[SPIN_MAX_LAYERS];
+  if (lane != 0) return;
+  const double np = *st.n_probes + 1.0;
+  *st.n_probes = np;
+  for (int l = 0; l < L; ++l) {
+    const int64_t t = st.tot[l], c = st.cov[(int64_t)l * W + level_table[l]];
+    st.miss_sum[l] += t == 0 ? 0.0 : (double)(t - c) / (double)t;
+    w[l] = st.miss_sum[l] / np + 1e-3;
+    fixed[l] = -1;
+    share[l] = 0.0;
+  }
+  const int64_t T = (int64_t)L * target;
+  for (;;) {
+    int64_t rem = T;
+    double ws = 0.0;
+    for (int l = 0; l < L; ++l) {
+      if (fixed[l] >= 0) rem -= fixed[l];
+      else ws += w[l];
+    }
+    bool changed = false;
+    for (int l = 0; l < L; ++l)
+      if (fixed[l] < 0) share[l] = (double)rem * w[l] / ws;
+    for (int l = 0; l < L; ++l) {
+      if (fixed[l] >= 0) continue;
+      if (share[l] > levels) { fixed[l] = levels; changed = true; }
+      else if (share[l] < 0) { fixed[l] = 0; changed = true; }
+    }
+    if (!changed) break;
+  }
+  int64_t sum = 0;
+  for (int l = 0; l < L; ++l) {
+    gl[l] = fixed[l] >= 0 ? fixed[l] : (int)floor(share[l]);
+    sum += gl[l];
+  }
+  // one more level to the largest fractional parts (ties: lower layer), in
+  // that order, skipping layers at the top
+  int64_t left = T - sum;
+  for (int l = 0; l < L; ++l) used[l] = fixed[l] >= 0;
+  while (left > 0) {
+    int best = -1;
+    double bf = 0.0;
+    for (int l = 0; l < L; ++l) {
+      if (used[l]) continue;
+      const double f = share[l] - gl[l];
+      if (best < 0 || f > bf) { best = l; bf = f; }
+    }
+    if (best < 0) break;
+    used[best] = true;
+    if (gl[best] < levels) { ++gl[best]; --left; }
+  }
+  for (int l = 0; l < L; ++l) level_table[l] = gl[l];
+}
+
+hipError_t launch_budget_update(int policy, int L, int levels, int target, int RR,
+                                const int32_t* covered, const int32_t* kprime, void* state,
+                                int32_t* level_table, hipStream_t st) {
+  hipLaunchKernelGGL(k_budget_update, dim3(1), dim3(256), 0, st, policy, L, levels, target, RR,
+                     covered, kprime, state, level_table);
+  return hipGetLastError();
+}
+
+// Start of a policy: every layer at the target level, no probe history,
+// the probe budget (every block) in place.
+__global__ void k_budget_reset(int L, int levels, int target, int R, void* state,
+                               int32_t* level_table, int32_t* probe_budget) {
+  const BudgetState st = budget_state(state, L, levels);
+  for (int i = threadIdx.x; i < L; i += blockDim.x) {
+    level_table[i] = target;
+    st.miss_sum[i] = 0.0;
+  }
+  for (int i = threadIdx.x; i < R; i += blockDim.x) probe_budget[i] = SPIN_MAX_BLOCKS;
+  if (threadIdx.x == 0) *st.n_probes = 0.0;
+}
+
+hipError_t launch_budget_reset(int L, int levels, int target, int R, void* state,
+                               int32_t* level_table, int32_t* probe_budget, hipStream_t st) {
+  hipLaunchKernelGGL(k_budget_reset, dim3(1), dim3(256), 0, st, L, levels, target, R, state,
+                     level_table, probe_budget);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Host allocation between layers (no device work).
 // ---------------------------------------------------------------------------
 namespace {

@@ -462,6 +462,11 @@ struct spin_stack {
   bool ema_stream_last = false;  // the previous call ran the EMA updates on an EMA stream
   bool commit_pending = false;   // the previous call deferred its EMA updates
   int32_t committed_layers = 0;  // layers of the previous call
+  // per-layer budgets run by the stack (spin_stack_set_budget_policy)
+  bool has_policy = false;
+  spin_budget_policy policy{};
+  int64_t budget_t = 0;          // calls since spin_stack_reset_budgets
+  bool order_side = false;       // the last call wrote budgets on main after its finishes
   hipEvent_t plan_done[2] = {nullptr, nullptr};
   hipEvent_t finish_done[2] = {nullptr, nullptr};
   hipEvent_t ema_done[2] = {nullptr, nullptr};   // with an EMA stream
@@ -655,10 +660,141 @@ void spin_stack_destroy(spin_stack* stack) {
   delete stack;
 }
 
+static spin_status stack_step_impl(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
+                                   const spin_batch* bts, const spin_step_io* ios,
+                                   int32_t order_after_main, int32_t defer_ema,
+                                   void* main_stream, void* side_stream, void* ema_stream);
+
 spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
                             const spin_batch* bts, const spin_step_io* ios,
                             int32_t order_after_main, int32_t defer_ema, void* main_stream,
                             void* side_stream, void* ema_stream) {
+  const char* fn = "spin_stack_step";
+  if (!stack || !cfgs || !bts || !ios) return fail(SPIN_E_NULL, "%s: NULL argument", fn);
+  if (!stack->has_policy)
+    return stack_step_impl(stack, n_layers, cfgs, bts, ios, order_after_main, defer_ema,
+                           main_stream, side_stream, ema_stream);
+  const spin_budget_policy& P = stack->policy;
+  if (n_layers != stack->n_layers)
+    return fail(SPIN_E_SHAPE, "%s: with a budget policy every layer (%d) takes part", fn,
+                stack->n_layers);
+  if (defer_ema)
+    return fail(SPIN_E_SHAPE, "%s: deferred EMA updates are not available with a budget policy",
+                fn);
+  for (int l = 1; l < n_layers; ++l)
+    if (bts[l].batch != bts[0].batch || bts[l].n_rows != bts[0].n_rows)
+      return fail(SPIN_E_SHAPE, "%s: a budget policy needs the same batch and rows in every "
+                  "layer", fn);
+  const int R = bts[0].batch, rows = bts[0].n_rows, W = P.levels + 1;
+  const bool probe = stack->budget_t > 0 && stack->budget_t % P.probe_period == 0;
+  std::vector<spin_step_io> own(ios, ios + n_layers);
+  for (int l = 0; l < n_layers; ++l)
+    own[l].budget = probe ? P.probe_budget : P.budget + (int64_t)l * R;
+  SPIN_CHECK(stack_step_impl(stack, n_layers, cfgs, bts, own.data(),
+                             order_after_main || stack->order_side, 0, main_stream, side_stream,
+                             ema_stream));
+  stack->order_side = false;
+  ++stack->budget_t;
+  if (!probe || R == 0) return SPIN_OK;
+  // the probe's curves, the allocation and the new budgets, on main after
+  // every layer's finish (the next call's plans are ordered after them)
+  hipStream_t mst = (hipStream_t)main_stream;
+  for (int l = 0; l < n_layers; ++l)
+    SPIN_CHECK(hip_status(spin::launch_miss_curve(cfgs[l], bts[l], own[l].S, own[l].topk_idx,
+                                                  P.levels,
+                                                  P.covered + (int64_t)l * R * rows * W,
+                                                  P.kprime + (int64_t)l * R * rows, mst),
+                          "spin_stack_step/miss curve"));
+  SPIN_CHECK(spin_budget_update(P.policy, n_layers, P.levels, P.target_level, R * rows,
+                                P.covered, P.kprime, P.state, P.level_table, mst));
+  for (int l = 0; l < n_layers; ++l)
+    SPIN_CHECK(hip_status(spin::launch_budget_fill(cfgs[l], bts[l], P.level_table + l, P.levels,
+                                                   P.budget + (int64_t)l * R, mst),
+                          "spin_stack_step/budget fill"));
+  stack->order_side = true;
+  return SPIN_OK;
+}
+
+spin_status spin_budget_update(int32_t policy, int32_t n_layers, int32_t levels,
+                               int32_t target_level, int32_t rows_total, const int32_t* covered,
+                               const int32_t* kprime, void* state, int32_t* level_table,
+                               void* stream) {
+  const char* fn = "spin_budget_update";
+  SPIN_CHECK(check_levels(fn, levels));
+  if (policy != SPIN_BUDGET_MINIMAX && policy != SPIN_BUDGET_PROPORTIONAL)
+    return fail(SPIN_E_SHAPE, "%s: unknown policy %d", fn, policy);
+  if (n_layers < 1 || n_layers > SPIN_MAX_LAYERS)
+    return fail(SPIN_E_SHAPE, "%s: n_layers %d outside [1, %d]", fn, n_layers, SPIN_MAX_LAYERS);
+  if (target_level < 0 || target_level > levels)
+    return fail(SPIN_E_SHAPE, "%s: target_level %d outside [0, %d]", fn, target_level, levels);
+  if (rows_total < 0 || rows_total > SPIN_MAX_BATCH * SPIN_MAX_ROWS)
+    return fail(SPIN_E_SHAPE, "%s: rows_total %d", fn, rows_total);
+  SPIN_REQUIRE(covered);
+  SPIN_REQUIRE(kprime);
+  SPIN_REQUIRE(state);
+  SPIN_REQUIRE(level_table);
+  return hip_status(spin::launch_budget_update(policy, n_layers, levels, target_level, rows_total,
+                                               covered, kprime, state, level_table,
+                                               (hipStream_t)stream), fn);
+}
+
+size_t spin_budget_state_bytes(int32_t n_layers, int32_t levels) {
+  if (n_layers < 1 || levels < 1) return 0;
+  return spin::budget_state_bytes(n_layers, levels);
+}
+
+spin_status spin_stack_set_budget_policy(spin_stack* stack, const spin_budget_policy* policy) {
+  const char* fn = "spin_stack_set_budget_policy";
+  if (!stack) return fail(SPIN_E_NULL, "%s: stack is NULL", fn);
+  if (!policy) {
+    stack->has_policy = false;
+    return SPIN_OK;
+  }
+  const spin_budget_policy& P = *policy;
+  if (P.policy != SPIN_BUDGET_MINIMAX && P.policy != SPIN_BUDGET_PROPORTIONAL)
+    return fail(SPIN_E_SHAPE, "%s: unknown policy %d", fn, P.policy);
+  SPIN_CHECK(check_levels(fn, P.levels));
+  if (P.probe_period < 1) return fail(SPIN_E_SHAPE, "%s: probe_period < 1", fn);
+  if (P.target_level < 0 || P.target_level > P.levels)
+    return fail(SPIN_E_SHAPE, "%s: target_level outside [0, levels]", fn);
+  if (!P.level_table || !P.budget || !P.probe_budget || !P.covered || !P.kprime || !P.state)
+    return fail(SPIN_E_NULL, "%s: a policy buffer is NULL", fn);
+  stack->policy = P;
+  stack->has_policy = true;
+  stack->budget_t = 0;
+  return SPIN_OK;
+}
+
+spin_status spin_stack_reset_budgets(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
+                                     const spin_batch* bts, void* main_stream) {
+  const char* fn = "spin_stack_reset_budgets";
+  if (!stack || !cfgs || !bts) return fail(SPIN_E_NULL, "%s: NULL argument", fn);
+  if (!stack->has_policy) return fail(SPIN_E_SHAPE, "%s: no budget policy set", fn);
+  if (n_layers != stack->n_layers)
+    return fail(SPIN_E_SHAPE, "%s: n_layers %d, the stack has %d", fn, n_layers, stack->n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    SPIN_CHECK(check_config(fn, &cfgs[l]));
+    SPIN_CHECK(check_batch(fn, &bts[l]));
+  }
+  const spin_budget_policy& P = stack->policy;
+  hipStream_t mst = (hipStream_t)main_stream;
+  const int R = bts[0].batch;
+  SPIN_CHECK(hip_status(spin::launch_budget_reset(n_layers, P.levels, P.target_level, R, P.state,
+                                                  P.level_table, P.probe_budget, mst), fn));
+  for (int l = 0; l < n_layers; ++l)
+    if (bts[l].batch > 0)
+      SPIN_CHECK(hip_status(spin::launch_budget_fill(cfgs[l], bts[l], P.level_table + l,
+                                                     P.levels, P.budget + (int64_t)l * R, mst),
+                            fn));
+  stack->budget_t = 0;
+  stack->order_side = true;
+  return SPIN_OK;
+}
+
+static spin_status stack_step_impl(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
+                                   const spin_batch* bts, const spin_step_io* ios,
+                                   int32_t order_after_main, int32_t defer_ema,
+                                   void* main_stream, void* side_stream, void* ema_stream) {
   const char* fn = "spin_stack_step";
   if (!stack || !cfgs || !bts || !ios) return fail(SPIN_E_NULL, "%s: NULL argument", fn);
   if (n_layers < 1 || n_layers > stack->n_layers)

@@ -114,6 +114,14 @@ hipError_t launch_miss_curve(const spin_config& c, const spin_batch& b, const fl
                              hipStream_t st);
 hipError_t launch_budget_fill(const spin_config& c, const spin_batch& b, const int32_t* level,
                               int levels, int32_t* budget, hipStream_t st);
+// After a probe step: the layers' curves summed, the running miss rates and
+// the new levels, all on the device (state: budget_state_bytes()).
+hipError_t launch_budget_update(int policy, int L, int levels, int target, int RR,
+                                const int32_t* covered, const int32_t* kprime, void* state,
+                                int32_t* level_table, hipStream_t st);
+hipError_t launch_budget_reset(int L, int levels, int target, int R, void* state,
+                               int32_t* level_table, int32_t* probe_budget, hipStream_t st);
+size_t budget_state_bytes(int L, int levels);
 void allocate_minimax(int L, int levels, int target, const int64_t* covered,
                       const int64_t* total, int32_t* out);
 void allocate_proportional(int L, int levels, int target, const double* miss, int32_t* out);

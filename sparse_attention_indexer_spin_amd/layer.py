@@ -105,19 +105,20 @@ class SpinLayer:
 class SpinStack:
     """The SPIN state of several layers and the multi-layer schedule: every
     layer's plan (predict + select) runs on a side stream, overlapped with the
-    score / top-K / EMA of other layers on the main stream (spin_stack_step).
+    score / top-K / EMA of other layers on the main stream (spin_stack_step),
+    or with one_stream inside the previous layer's launches.
 
     `layers` are SpinLayer objects (own EMA state, counters and buffers each).
     step() takes per-layer queries, weights and key caches.
 
     Per-layer block budgets (optional, `budget_policy` "minimax" or
-    "proportional"): every `probe_period` steps (t = P, 2P, ... after a reset)
-    a probe step selects every block of every layer; its miss curves
-    (spin_miss_curve) go to the host, which re-sizes the layers' budget levels
-    (spin_budget_allocate: the level sum stays n_layers x the target level of
-    the layers' sparsity) and publishes them to the device-side level table;
-    the budgets apply from the second step after the probe on.  Until the
-    first probe every layer runs at the target level."""
+    "proportional"): the stack runs them in the library
+    (spin_stack_set_budget_policy): every `probe_period` steps after a reset a
+    dense probe step measures the layers' miss curves, and a device kernel
+    re-sizes the levels (their sum stays n_layers x the target level of the
+    layers' sparsity) into the device-side level table and the layers'
+    budgets, used from the next step on.  This object only owns the buffers.
+    Until the first probe every layer runs at the target level."""
 
     def __init__(self, layers, device="cuda", budget_policy=None, probe_period: int = 8,
                  levels: int = 100, ema_stream: bool = False, one_stream: bool = False):
@@ -140,6 +141,7 @@ class SpinStack:
         if budget_policy is not None:
             assert budget_policy in ("minimax", "proportional")
             L, R = len(self.layers), self.layers[0].R
+            rows = self.layers[0].rows
             sp = {lay.cfg.sparsity_bp for lay in self.layers}
             assert len(sp) == 1 and 10000 % levels == 0 and (10000 - sp.pop()) % (10000 // levels) == 0
             self.levels, self.P = levels, probe_period
@@ -147,67 +149,32 @@ class SpinStack:
             dev = torch.device(device)
             i32 = dict(dtype=torch.int32, device=dev)
             self.level_table = torch.full((L,), self.target, **i32)
-            self.probe_table = torch.full((1,), levels, **i32)
             self.budget = torch.zeros(L, R, **i32)
-            self.probe_budget = torch.zeros(L, R, **i32)
-            rows = self.layers[0].rows
+            self.probe_budget = torch.zeros(R, **i32)
             self.covered = torch.zeros(L, R, rows, levels + 1, **i32)
             self.kprime = torch.zeros(L, R, rows, **i32)
-            self.covered_host = torch.zeros(L, R, rows, levels + 1, dtype=torch.int32,
-                                            pin_memory=True)
-            self.kprime_host = torch.zeros(L, R, rows, dtype=torch.int32, pin_memory=True)
-            self.level_host = torch.zeros(L, dtype=torch.int32, pin_memory=True)
-            self.probe_event = torch.cuda.Event()
-            self.publish_event = torch.cuda.Event()
+            self.state = torch.zeros(api.spin_budget_state_bytes(L, levels), dtype=torch.uint8,
+                                     device=dev)
+            api.spin_stack_set_budget_policy(
+                self.stack, budget_policy, probe_period=probe_period, levels=levels,
+                target_level=self.target, level_table=self.level_table, budget=self.budget,
+                probe_budget=self.probe_budget, covered=self.covered, kprime=self.kprime,
+                state=self.state)
             self.reset_budgets()
 
     # -- budgets -------------------------------------------------------------
-    def reset_budgets(self):
-        """Uniform target levels, no probe history: call with a reset of the
-        layers, and after set_requests (the budgets follow the contexts)."""
-        self.t = 0
-        self.levels_now = [self.target] * len(self.layers)
-        self.level_history = []            # (step, levels) of every allocation
-        self.miss_sum = [0.0] * len(self.layers)
-        self.n_probes = 0
-        self._pending = None               # step of a probe whose curves are not applied yet
-        self._publish(self.levels_now, fill_probe=True)
+    def reset_budgets(self, stream=None):
+        """Uniform target levels, no probe history (on the current stream):
+        call with a reset of the layers, and after set_requests (the budgets
+        follow the contexts)."""
+        bts = [lay.batch(lay.n_pages) for lay in self.layers]
+        api.spin_stack_reset_budgets(self.stack, [lay.cfg for lay in self.layers], bts,
+                                     main_stream=stream)
 
-    def _publish(self, levels, fill_probe=False):
-        """Level table -> per-layer budgets, on the side stream (before its plans).
-        The fill reads the layers' ctx_len, written on the main stream."""
-        self.publish_event.synchronize()       # the previous copy out of level_host ran
-        self.level_host.copy_(torch.tensor(levels, dtype=torch.int32))
-        self.side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(self.side):
-            self.level_table.copy_(self.level_host, non_blocking=True)
-            for l, lay in enumerate(self.layers):
-                bt = lay.batch(lay.n_pages)
-                api.spin_budget_fill(lay.cfg, bt, self.level_table[l:l + 1], self.levels,
-                                     self.budget[l], stream=self.side)
-                if fill_probe:
-                    api.spin_budget_fill(lay.cfg, bt, self.probe_table, self.levels,
-                                         self.probe_budget[l], stream=self.side)
-        self.publish_event.record(self.side)
-
-    def _apply_probe(self):
-        """Host side of a probe: miss curves -> new levels (see class docstring)."""
-        self.probe_event.synchronize()
-        cov = self.covered_host.to(torch.int64).sum(dim=(1, 2)).numpy()     # [L, levels+1]
-        tot = self.kprime_host.to(torch.int64).sum(dim=(1, 2)).numpy()      # [L]
-        if self.policy == "minimax":
-            new = api.spin_budget_allocate("minimax", self.levels, self.target, covered=cov,
-                                           total=tot)
-        else:
-            for l in range(len(self.layers)):
-                g = self.levels_now[l]
-                self.miss_sum[l] += 0.0 if tot[l] == 0 else float(tot[l] - cov[l][g]) / float(tot[l])
-            self.n_probes += 1
-            new = api.spin_budget_allocate("proportional", self.levels, self.target,
-                                           running_miss=[m / self.n_probes for m in self.miss_sum])
-        self.levels_now = list(new)
-        self.level_history.append((self.t, list(new)))
-        self._publish(self.levels_now)
+    def levels_now(self):
+        """The layers' current budget levels (reads the device table: a host
+        synchronisation, for inspection only)."""
+        return self.level_table.cpu().tolist()
 
     def commit(self, n_valid=None, stream=None):
         """The deferred EMA updates of the last step: layer l replays its rows
@@ -246,22 +213,9 @@ class SpinStack:
     def step(self, qs, ws, k_pages, k_scales, page_tables, n_valid=None, budgets=None,
              stream=None, n_layers=None, defer_ema: bool = False):
         """One decode step of the first n_layers layers (default: all).
-        defer_ema: the EMA updates wait for commit() (speculative decoding)."""
+        defer_ema: the EMA updates wait for commit() (speculative decoding).
+        With a budget policy the stack chooses the budgets (`budgets` unused)."""
         n = len(self.layers) if n_layers is None else n_layers
-        probe = False
-        if self.policy is not None:
-            assert not defer_ema
-            assert budgets is None and n == len(self.layers)
-            if self._pending is not None and self.t >= self._pending + 2:
-                self._apply_probe()
-                self._pending = None
-            probe = self.t > 0 and self.t % self.P == 0
-            src = self.probe_budget if probe else self.budget
-            budgets = [src[l] for l in range(n)]
-        if self.policy is not None and self.one_stream:
-            # the budget table is written on the side stream; on one stream
-            # the plans run on main and must see it
-            (torch.cuda.current_stream() if stream is None else stream).wait_stream(self.side)
         cfgs, bts, ios = [], [], []
         for l, lay in enumerate(self.layers[:n]):
             bts.append(lay.batch(k_pages[l].shape[0]))
@@ -276,18 +230,4 @@ class SpinStack:
         self._order_next = False
         if defer_ema:
             self._deferred = (cfgs, bts, ios)
-        if probe:
-            st = torch.cuda.current_stream() if stream is None else stream
-            for l, lay in enumerate(self.layers):
-                api.spin_miss_curve(lay.cfg, bts[l], lay.S, lay.topk_idx, self.levels,
-                                    self.covered[l], self.kprime[l], stream=st)
-            with torch.cuda.stream(st):
-                self.covered_host.copy_(self.covered, non_blocking=True)
-                self.kprime_host.copy_(self.kprime, non_blocking=True)
-            self.probe_event.record(st)
-            self._pending = self.t
-            # the next plans overwrite S: order them after the curves
-            self._order_next = True
-        if self.policy is not None:
-            self.t += 1
         return [lay.topk_idx for lay in self.layers[:n]]

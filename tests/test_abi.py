@@ -51,7 +51,7 @@ def test_struct_layouts_match_header(tmp_path):
     if cc is None:
         pytest.skip("no C compiler")
     structs = {"spin_config": _lib.SpinConfig, "spin_batch": _lib.SpinBatch,
-               "spin_step_io": _lib.SpinStepIO}
+               "spin_step_io": _lib.SpinStepIO, "spin_budget_policy": _lib.SpinBudgetPolicy}
     lines = ['#include "spin.h"', "#include <stdio.h>", "#include <stddef.h>", "int main(void) {"]
     for cname, ct in structs.items():
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')

@@ -83,10 +83,12 @@ def test_budget_fill_parity():
 @pytest.mark.parametrize("policy,one_stream", [("minimax", False), ("proportional", False),
                                                ("proportional", True)])
 def test_stack_budgets_match_oracle_reference(policy, one_stream):
-    """SpinStack with probes every 3 steps against sequential spin_step layers
-    whose budgets come from the oracle: oracle miss curves of the same probe
-    outputs, oracle allocation, applied from the second step after the probe."""
-    banner(f"stack budgets {policy}")
+    """SpinStack with probes every 3 steps, the policy run by the library
+    (curves, allocation and budgets on the device, no host round trip),
+    against sequential spin_step layers whose budgets come from the oracle:
+    oracle miss curves of the same probe outputs, oracle allocation, applied
+    from the step after the probe."""
+    banner(f"stack budgets {policy} one_stream={one_stream}")
     from sparse_attention_indexer_spin_amd import SpinStack
     L, P, levels, sp = 3, 3, 100, 4000
     w = G.WORKLOADS["fp8_256k_ragged_8l"].scaled(batch=4, layers=L, n_slots=64 * 120 + 9,
@@ -98,22 +100,9 @@ def test_stack_budgets_match_oracle_reference(policy, one_stream):
     stack = SpinStack(stk, budget_policy=policy, probe_period=P, levels=levels,
                       one_stream=one_stream)
     target = (10000 - sp) // 100
-    ref_levels, history, pending, miss_sum, n_probes = [target] * L, [], None, [0.0] * L, 0
+    ref_levels, history, miss_sum, n_probes = [target] * L, [], [0.0] * L, 0
     Bs = [O.n_blocks(int(c)) for c in lis[0].ctx]
-    ref_cov = None
     for s in range(w.steps):
-        if pending is not None and s >= pending + 2:
-            cov, tot = ref_cov
-            if policy == "minimax":
-                ref_levels = OB.allocate_minimax(cov, tot, target, levels)
-            else:
-                for l in range(L):
-                    miss_sum[l] += 0.0 if tot[l] == 0 else (tot[l] - cov[l][ref_levels[l]]) / tot[l]
-                n_probes += 1
-                ref_levels = OB.allocate_proportional([m / n_probes for m in miss_sum], target,
-                                                      levels)
-            history.append((s, list(ref_levels)))
-            pending = None
         probe = s > 0 and s % P == 0
         qs = [li.q[s].to(DEV).contiguous() for li in lis]
         ws = [li.weights.to(DEV) for li in lis]
@@ -128,25 +117,71 @@ def test_stack_budgets_match_oracle_reference(policy, one_stream):
             for a, b in ((seq[l].topk_idx, stk[l].topk_idx), (seq[l].V, stk[l].V),
                          (seq[l].D, stk[l].D), (seq[l].row_code, stk[l].row_code)):
                 assert torch.equal(a, b), f"step {s} layer {l}"
-        if probe:
-            cov, tot = [], []
+        if not probe:
+            continue
+        cov, tot = [], []
+        for l in range(L):
+            S, top = seq[l].S.cpu().numpy(), seq[l].topk_idx.cpu().numpy()
+            c_l, t_l = np.zeros(levels + 1, dtype=np.int64), 0
+            for r in range(w.batch):
+                c, k = OB.miss_curve(S[r, 0, :Bs[r]], top[r, 0], int(lis[l].ctx[r]), w.topk,
+                                     w.explore_bp, levels)
+                c_l += np.asarray(c)
+                t_l += k
+                assert stk_cov_row(stack, l, r) == c, (s, l, r)
+            cov.append(c_l.tolist())
+            tot.append(t_l)
+        if policy == "minimax":
+            ref_levels = OB.allocate_minimax(cov, tot, target, levels)
+        else:
             for l in range(L):
-                S, top = seq[l].S.cpu().numpy(), seq[l].topk_idx.cpu().numpy()
-                c_l, t_l = np.zeros(levels + 1, dtype=np.int64), 0
-                for r in range(w.batch):
-                    c, k = OB.miss_curve(S[r, 0, :Bs[r]], top[r, 0], int(lis[l].ctx[r]), w.topk,
-                                         w.explore_bp, levels)
-                    c_l += np.asarray(c)
-                    t_l += k
-                    assert stk_cov_row(stack, l, r) == c, (s, l, r)
-                cov.append(c_l.tolist())
-                tot.append(t_l)
-            ref_cov, pending = (cov, tot), s
-    assert [h[1] for h in stack.level_history] == [h[1] for h in history]
-    assert [h[0] for h in stack.level_history] == [h[0] for h in history]
+                miss_sum[l] += 0.0 if tot[l] == 0 else (tot[l] - cov[l][ref_levels[l]]) / tot[l]
+            n_probes += 1
+            ref_levels = OB.allocate_proportional([m / n_probes for m in miss_sum], target,
+                                                  levels)
+        assert stack.levels_now() == list(ref_levels), s
+        history.append((s, list(ref_levels)))
     assert len(history) >= 2
     for lay in seq + stk:
         assert int(lay.err.item()) == 0
+
+
+@pytest.mark.parametrize("policy", ["minimax", "proportional"])
+@pytest.mark.parametrize("L,rows_total,levels", [(1, 5, 100), (3, 24, 100), (8, 50, 4),
+                                                  (70, 7, 100)])
+def test_budget_update_matches_oracle(policy, L, rows_total, levels):
+    """spin_budget_update through the C ABI on random monotone curves (zero
+    totals and ties included), three probes in a row (the proportional rule
+    carries its running miss rates in the device state): the levels equal the
+    oracle allocation every time."""
+    banner(f"budget update {policy} L={L} rows={rows_total} levels={levels}")
+    from sparse_attention_indexer_spin_amd import api as A
+    rng = np.random.default_rng(L * 7 + rows_total)
+    target = levels * 3 // 5
+    state = torch.zeros(A.spin_budget_state_bytes(L, levels), dtype=torch.uint8, device=DEV)
+    table = torch.full((L,), target, dtype=torch.int32, device=DEV)
+    ref_levels, miss_sum = [target] * L, [0.0] * L
+    for probe in range(3):
+        kp = rng.integers(0, 300, (L, rows_total)).astype(np.int32)
+        kp[0, :] = 0 if L > 2 and probe == 1 else kp[0, :]       # a layer with no top-K slots
+        inc = rng.integers(0, 3, (L, rows_total, levels + 1))
+        cov = np.minimum(np.cumsum(inc, axis=2), kp[:, :, None]).astype(np.int32)
+        cov[:, :, -1] = kp                                       # the top level covers all
+        A.spin_budget_update(policy, levels, target, torch.from_numpy(cov).to(DEV),
+                             torch.from_numpy(kp).to(DEV), state, table)
+        torch.cuda.synchronize()
+        c_l = cov.astype(np.int64).sum(axis=1)
+        t_l = kp.astype(np.int64).sum(axis=1)
+        if policy == "minimax":
+            ref_levels = OB.allocate_minimax(c_l.tolist(), t_l.tolist(), target, levels)
+        else:
+            for l in range(L):
+                miss_sum[l] += 0.0 if t_l[l] == 0 else \
+                    float(t_l[l] - c_l[l][ref_levels[l]]) / float(t_l[l])
+            ref_levels = OB.allocate_proportional([m / (probe + 1) for m in miss_sum], target,
+                                                  levels)
+        assert table.cpu().tolist() == list(ref_levels), probe
+        assert sum(ref_levels) == L * target
 
 
 def stk_cov_row(stack, l, r):

@@ -191,10 +191,8 @@ def test_full_size_stack_with_budgets(one_stream):
     target = (10000 - sp) // 100
     Bs = [O.n_blocks(int(c)) for c in ctx]
     levels_now = [target] * w.layers
-    want_levels = None                       # allocation from the first probe's curves
+    checked = False
     for s in range(n_steps):
-        if stack.level_history and stack.level_history[-1][0] == s:
-            levels_now = stack.level_history[-1][1]
         probe = s > 0 and s % P == 0
         for l in range(w.layers):
             bud = [B if probe else OB.level_budget(B, w.topk, levels_now[l], levels) for B in Bs]
@@ -208,20 +206,26 @@ def test_full_size_stack_with_budgets(one_stream):
             for a, b in ((seq[l].topk_idx, stk[l].topk_idx), (seq[l].V, stk[l].V),
                          (seq[l].D, stk[l].D), (seq[l].sel, stk[l].sel)):
                 assert torch.equal(a, b), f"step {s} layer {l}"
-        if probe and want_levels is None:
-            cov = stack.covered.cpu().numpy()
-            kp = stack.kprime.cpu().numpy()
+        if not probe:
+            continue
+        cov = stack.covered.cpu().numpy()
+        kp = stack.kprime.cpu().numpy()
+        if not checked:
             for l in (0, w.layers - 1):
                 S, top = stk[l].S.cpu().numpy(), stk[l].topk_idx.cpu().numpy()
                 for r in _sample_requests(w.batch):
                     want, wk = OB.miss_curve(S[r, 0, :Bs[r]], top[r, 0], int(ctx[r]), w.topk,
                                              w.explore_bp, levels)
                     assert cov[l, r, 0].tolist() == want and kp[l, r, 0] == wk, (s, l, r)
-            tot = kp.astype(np.int64).sum(axis=(1, 2))
-            c = cov.astype(np.int64).sum(axis=(1, 2))
-            miss = [0.0 if tot[l] == 0 else float(tot[l] - c[l][levels_now[l]]) / float(tot[l])
-                    for l in range(w.layers)]
+            checked = True
+        tot = kp.astype(np.int64).sum(axis=(1, 2))
+        c = cov.astype(np.int64).sum(axis=(1, 2))
+        miss = [0.0 if tot[l] == 0 else float(tot[l] - c[l][levels_now[l]]) / float(tot[l])
+                for l in range(w.layers)]
+        if s == P:
             want_levels = OB.allocate_proportional(miss, target, levels)
-    assert stack.level_history[0] == (P + 2, want_levels)
+            assert stack.levels_now() == list(want_levels)
+        levels_now = stack.levels_now()
+    assert checked
     for lay in seq + stk:
         assert int(lay.err.item()) == 0
