@@ -684,25 +684,30 @@ template <>
 struct PageRegs<0> {
   static constexpr int kRegs = 8;
   static constexpr int64_t kBytes = 8192;
-  // WL: register 2 st + b holds slots 16 st + 8 b + (l & 7), chunk (l >> 4) + 4 l3
+  // WL: register 2 st + b holds slots 16 st + 8 b + (l & 7), chunk (l >> 4) + 4 l3.
+  // idle: the same instructions, every lane at the page's first 16 bytes (one
+  // line per instruction): a worker's loads past its last page keep the
+  // loop's load counts, and so its waits, the same without moving a page.
   template <bool WL>
   __device__ static __forceinline__ void load(const ScoreParams& p, int page, v4u (&b)[8],
-                                              float& sc) {
+                                              float& sc, bool idle = false) {
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
     const uint8_t* page_base = reinterpret_cast<const uint8_t*>(p.kp) + (int64_t)page * kBytes;
+    const int step = idle ? 0 : 1;
     if constexpr (WL) {
-      const uint8_t* base = page_base + (lane & 7) * 128 + ((lane >> 3) & 1) * 64 + g * 16;
+      const uint8_t* base =
+          page_base + step * ((lane & 7) * 128 + ((lane >> 3) & 1) * 64 + g * 16);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) b[i] = load16_nt(base + i * 1024);
+      for (int i = 0; i < 8; ++i) b[i] = load16_nt(base + step * i * 1024);
     } else {
-      const uint8_t* base = page_base + n * 128 + 16 * g;
+      const uint8_t* base = page_base + step * (n * 128 + 16 * g);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        b[2 * st] = *reinterpret_cast<const v4u*>(base + st * 2048);
-        b[2 * st + 1] = *reinterpret_cast<const v4u*>(base + st * 2048 + 64);
+        b[2 * st] = *reinterpret_cast<const v4u*>(base + step * st * 2048);
+        b[2 * st + 1] = *reinterpret_cast<const v4u*>(base + step * (st * 2048 + 64));
       }
     }
-    sc = p.ks[(int64_t)page * 64 + lane];
+    sc = p.ks[(int64_t)page * 64 + step * lane];
   }
   template <bool WL, class Q>
   __device__ static __forceinline__ float tile(const Q& q, v4u (&b)[8], int st) {
@@ -721,21 +726,23 @@ struct PageRegs<1> {
   // 128 k1 + 64 l3 + 16 (l >> 4) of the slot (after the swap: k-step 2 k1 + b)
   template <bool WL>
   __device__ static __forceinline__ void load(const ScoreParams& p, int page, v4u (&b)[16],
-                                              float& sc) {
+                                              float& sc, bool idle = false) {
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
     const uint8_t* page_base = reinterpret_cast<const uint8_t*>(p.kp) + (int64_t)page * kBytes;
+    const int step = idle ? 0 : 1;  // as PageRegs<0>
     if constexpr (WL) {
-      const uint8_t* base = page_base + (lane & 7) * 256 + ((lane >> 3) & 1) * 64 + g * 16;
+      const uint8_t* base =
+          page_base + step * ((lane & 7) * 256 + ((lane >> 3) & 1) * 64 + g * 16);
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        b[i] = load16_nt(base + (i >> 2) * 4096 + (i & 1) * 2048 + ((i >> 1) & 1) * 128);
+        b[i] = load16_nt(base + step * ((i >> 2) * 4096 + (i & 1) * 2048 + ((i >> 1) & 1) * 128));
     } else {
-      const uint8_t* base = page_base + n * 256 + 16 * g;
+      const uint8_t* base = page_base + step * (n * 256 + 16 * g);
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          b[4 * st + ks] = *reinterpret_cast<const v4u*>(base + st * 4096 + ks * 64);
+          b[4 * st + ks] = *reinterpret_cast<const v4u*>(base + step * (st * 4096 + ks * 64));
     }
     sc = 1.0f;
   }
@@ -762,11 +769,15 @@ struct PageRegs<1> {
 // requests.
 // ---------------------------------------------------------------------------
 
-// The row's top-K threshold hint (0 without a sink), as a scalar: reading
-// it into an SGPR completes its load here, so the page loop does not wait
-// for every outstanding load (the pages in flight) at its first use.
-__device__ __forceinline__ uint32_t row_hint(const ScoreParams& p, int rowid) {
-  return p.sink.hint ? __builtin_amdgcn_readfirstlane(p.sink.hint[rowid]) : 0u;
+// The row's top-K threshold hint (0 without a sink).  hint_fetch issues its
+// load and hint_use moves it into an SGPR, which waits for it: a worker
+// fetches its first row's hint before its descriptors, whose wait then
+// covers it, so that the page loop does not wait for the pages in flight.
+__device__ __forceinline__ uint32_t hint_fetch(const ScoreParams& p, int rowid) {
+  return p.sink.hint ? p.sink.hint[rowid] : 0u;
+}
+__device__ __forceinline__ uint32_t hint_use(uint32_t h) {
+  return __builtin_amdgcn_readfirstlane(h);
 }
 
 // The worker's current candidate run (see CandSink): row, first block, the
@@ -775,9 +786,14 @@ struct CandRun {
   int rowid = -1, k0 = 0, knext = 0, cnt = 0;
 };
 
+// The run's counts: rs.cnt at its first block, 0 at the others, in one
+// coalesced store per 64 blocks (per-page stores of 4 bytes each went to HBM
+// as partial lines amid the page stream).
 __device__ __forceinline__ void run_flush(const ScoreParams& p, const CandRun& rs) {
-  if (p.sink.hint && rs.rowid >= 0 && (threadIdx.x & 63) == 0)
-    p.sink.pcnt[(int64_t)rs.rowid * p.sink.pcnt_ld + rs.k0] = rs.cnt;
+  if (!p.sink.hint || rs.rowid < 0) return;
+  int32_t* pc = p.sink.pcnt + (int64_t)rs.rowid * p.sink.pcnt_ld + rs.k0;
+  const int n = rs.knext - rs.k0;
+  for (int i = threadIdx.x & 63; i < n; i += 64) pc[i] = i == 0 ? rs.cnt : 0;
 }
 
 // A scored page: the 4 lane groups' partial sums become slot l's total in
@@ -809,7 +825,6 @@ __device__ __forceinline__ void emit_page(const ScoreParams& p, const float (&pa
     if (pass)
       p.sink.cand[(int64_t)rowid * p.sink.cand_ld + (int64_t)rs.k0 * 64 + rs.cnt + pos] =
           make_uint2(key, (uint32_t)slot);
-    if (lane == 0 && d.k != rs.k0) p.sink.pcnt[(int64_t)rowid * p.sink.pcnt_ld + d.k] = 0;
     rs.cnt += __popcll(m);
   }
 }
@@ -853,11 +868,12 @@ struct ZQueue {
 template <int KT, int NS, int QB, int P, bool Span, bool WL, class Cur>
 __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd,
                                           v4u (&kb)[P][PageRegs<KT>::kRegs], float (&sc)[P],
-                                          QFull<KT, NS>& Q, int lo, int hi, int q_req, int row) {
+                                          QFull<KT, NS>& Q, int lo, int hi, int q_req, int row,
+                                          uint32_t hint_raw) {
   using PR = PageRegs<KT>;
   const int lane = threadIdx.x & 63;
   int rowid = q_req * p.rows + row;
-  uint32_t hint = row_hint(p, rowid);
+  uint32_t hint = hint_use(hint_raw);
   int bad = 0;
   CandRun rs;
   ZQueue zq;  // one row, runs inside one request: z stores queued
@@ -866,15 +882,15 @@ __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd
     for (int u = 0; u < P; ++u) {
       const int cur = it + u;
       if (cur >= hi) break;
-      // refill: page cur + P - 1 (the last page again past the end: an L2 hit)
+      // refill: page cur + P - 1 (past the end an idle load of the last page)
       PR::template load<WL>(p, dd.get(p, min(cur + P - 1, hi - 1)).page,
-                            kb[(u + P - 1) % P], sc[(u + P - 1) % P]);
+                            kb[(u + P - 1) % P], sc[(u + P - 1) % P], cur + P - 1 >= hi);
       const Desc d = db.get(p, cur);
       if (Span && d.r != q_req) {
         q_req = d.r;
         rowid = q_req * p.rows + row;
         Q.load(p, QB, rowid);
-        hint = row_hint(p, rowid);
+        hint = hint_use(hint_fetch(p, rowid));
       }
       float part[4];
 #pragma unroll
@@ -900,7 +916,8 @@ __device__ __forceinline__ void first_pages(const ScoreParams& p, Cur& dd,
                                             int lo, int hi) {
 #pragma unroll
   for (int u = 0; u < P - 1; ++u)
-    PageRegs<KT>::template load<WL>(p, dd.get(p, min(lo + u, hi - 1)).page, kb[u], sc[u]);
+    PageRegs<KT>::template load<WL>(p, dd.get(p, min(lo + u, hi - 1)).page, kb[u], sc[u],
+                                    lo + u >= hi);
 }
 
 // One worker with its own query: descriptors first, then the first page, then
@@ -913,10 +930,11 @@ __device__ __forceinline__ void score_pages(const ScoreParams& p, Cur& db, int l
   v4u kb[P][PageRegs<KT>::kRegs];
   float sc[P];
   first_pages<KT, P, WL>(p, dd, kb, sc, lo, hi);
+  const uint32_t hint = hint_fetch(p, q_req * p.rows + row);  // the query's wait covers it
   QFull<KT, NS> Q;
   Q.fetch(p, QB, q_req * p.rows + row);
   Q.convert(p, QB, q_req * p.rows + row);
-  page_loop<KT, NS, QB, P, Span, WL>(p, db, dd, kb, sc, Q, lo, hi, q_req, row);
+  page_loop<KT, NS, QB, P, Span, WL>(p, db, dd, kb, sc, Q, lo, hi, q_req, row, hint);
 }
 
 enum { kRunWave = 0, kRunTable = 1, kRunSpan = 2 };
@@ -951,6 +969,8 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
     // wave w stages head tile w of every row k: the query loads go out first
     // (the descriptor wait covers them), the first page next, and the
     // conversion then runs while the page is in flight
+    // the row's hint first: the descriptor wait below covers it
+    const uint32_t hint = hint_fetch(p, run.r * p.rows + row);
     QFull<KT, NS> S;
     constexpr int kRowsMax = WL ? 1 : SPIN_MAX_ROWS;  // WL: one row
 #pragma unroll
@@ -981,7 +1001,7 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
     if (!active) return;
     QFull<KT, NS> Q;
     Q.from_lds(lds, wstage, row);
-    page_loop<KT, NS, QB, P, false, WL>(p, db, dd, kb, sc, Q, lo, hi, run.r, row);
+    page_loop<KT, NS, QB, P, false, WL>(p, db, dd, kb, sc, Q, lo, hi, run.r, row, hint);
   } else {
     int n_ne;
     const ItemTable tb = build_items(p, pre_dyn, tmp, pre_dyn + p.R + 1, &n_ne);
