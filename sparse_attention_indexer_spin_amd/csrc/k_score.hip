@@ -781,19 +781,30 @@ __device__ __forceinline__ uint32_t hint_use(uint32_t h) {
 }
 
 // The worker's current candidate run (see CandSink): row, first block, the
-// block expected next and the candidates so far (wave-uniform).
+// block expected next and the candidates so far (wave-uniform), and the last
+// qn of them not yet stored, one per lane (lanes 0 .. qn - 1, in order).
+// Stored page by page, the candidates cost ~1.4 us of the in-step launch:
+// each page with a candidate wrote its few 8-byte pairs as a partial line.
+// Queued, they leave in 512-byte stores, one per 64 candidates.
 struct CandRun {
-  int rowid = -1, k0 = 0, knext = 0, cnt = 0;
+  int rowid = -1, k0 = 0, knext = 0, cnt = 0, qn = 0;
+  uint32_t qkey = 0, qslot = 0;
 };
 
-// The run's counts: rs.cnt at its first block, 0 at the others, in one
-// coalesced store per 64 blocks (per-page stores of 4 bytes each went to HBM
-// as partial lines amid the page stream).
+__device__ __forceinline__ uint2* run_cand(const ScoreParams& p, const CandRun& rs) {
+  return p.sink.cand + (int64_t)rs.rowid * p.sink.cand_ld + (int64_t)rs.k0 * 64;
+}
+
+// The run's queued candidates, and its counts: rs.cnt at its first block, 0
+// at the others, in one coalesced store per 64 blocks (per-page stores of 4
+// bytes each went to HBM as partial lines amid the page stream).
 __device__ __forceinline__ void run_flush(const ScoreParams& p, const CandRun& rs) {
   if (!p.sink.hint || rs.rowid < 0) return;
+  const int lane = threadIdx.x & 63;
+  if (lane < rs.qn) run_cand(p, rs)[rs.cnt - rs.qn + lane] = make_uint2(rs.qkey, rs.qslot);
   int32_t* pc = p.sink.pcnt + (int64_t)rs.rowid * p.sink.pcnt_ld + rs.k0;
   const int n = rs.knext - rs.k0;
-  for (int i = threadIdx.x & 63; i < n; i += 64) pc[i] = i == 0 ? rs.cnt : 0;
+  for (int i = lane; i < n; i += 64) pc[i] = i == 0 ? rs.cnt : 0;
 }
 
 // A scored page: the 4 lane groups' partial sums become slot l's total in
@@ -813,19 +824,40 @@ __device__ __forceinline__ void emit_page(const ScoreParams& p, const float (&pa
     const uint32_t key = float_key(zv);
     const bool pass = slot < d.N && key >= hint;
     const uint64_t m = __ballot(pass);
-    const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
     if (rowid != rs.rowid || d.k != rs.knext) {  // a new run
       run_flush(p, rs);
       rs.rowid = rowid;
       rs.k0 = d.k;
       rs.cnt = 0;
+      rs.qn = 0;
     }
     rs.knext = d.k + 1;
-    if (pass)
-      p.sink.cand[(int64_t)rowid * p.sink.cand_ld + (int64_t)rs.k0 * 64 + rs.cnt + pos] =
-          make_uint2(key, (uint32_t)slot);
-    rs.cnt += __popcll(m);
+    const int c = __popcll(m);
+    if (c > 0) {  // (uniform)
+      // candidate i of the page goes to queue lane (qn + i) mod 64 and the
+      // other lanes to the rest, a permutation: a forward lane permute
+      const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      const int dst = (pass ? rs.qn + pos : rs.qn + c + (lane - pos)) & 63;
+      const uint32_t nkey = (uint32_t)__builtin_amdgcn_ds_permute(dst * 4, (int)key);
+      const uint32_t nslot = (uint32_t)__builtin_amdgcn_ds_permute(dst * 4, slot);
+      const int nq = rs.qn + c;
+      if (lane >= rs.qn && lane < nq) {
+        rs.qkey = nkey;
+        rs.qslot = nslot;
+      }
+      if (nq >= 64) {  // full: 64 in order, then the rest of the page's
+        run_cand(p, rs)[rs.cnt - rs.qn + lane] = make_uint2(rs.qkey, rs.qslot);
+        if (lane < nq - 64) {
+          rs.qkey = nkey;
+          rs.qslot = nslot;
+        }
+        rs.qn = nq - 64;
+      } else {
+        rs.qn = nq;
+      }
+      rs.cnt += c;
+    }
   }
 }
 

@@ -55,28 +55,37 @@ __device__ __forceinline__ float pool_block_wave(float zhat, bool valid, int n_v
   return s / (float)cnt;
 }
 
-// One wave's 8 blocks j0 .. j0+7 (j0 < B) of one (request, row).
-__device__ __forceinline__ void predict_wave(int combine, int pooling, int N, int B, int q,
-                                             int j0, const float* __restrict__ Vr,
+// Prediction of NB blocks j0 .. j0 + NB - 1 (j0 < B) of one (request, row)
+// by one wave, lane = slot: predict_load issues the loads, predict_reduce
+// pools and stores the block scores.
+template <int NB>
+__device__ __forceinline__ void predict_load(int N, int B, int q, int j0,
+                                             const float* __restrict__ Vr,
                                              const float* __restrict__ Dr,
-                                             const float* __restrict__ vmax_r,
-                                             float* __restrict__ Srow) {
+                                             const float* __restrict__ vmax_r, float (&vv)[NB],
+                                             float (&dd)[NB], float& vm) {
+  static_assert(NB <= 64, "one V max per lane");
   const int lane = threadIdx.x & 63;
   // with the V block maxima (max combine), every block but the last reads
   // its V max (lane b holds block j0 + b's) instead of its 64 V values
-  const float vm = vmax_r && lane < kPredBlocksPerWave && j0 + lane < B - 1 ? vmax_r[j0 + lane]
-                                                                             : -INFINITY;
-  float vv[kPredBlocksPerWave], dd[kPredBlocksPerWave];
+  vm = vmax_r && lane < NB && j0 + lane < B - 1 ? vmax_r[j0 + lane] : -INFINITY;
 #pragma unroll
-  for (int b = 0; b < kPredBlocksPerWave; ++b) {
+  for (int b = 0; b < NB; ++b) {
     const int i = (j0 + b) * SPIN_BLOCK + lane;
     const bool ok = i < N;
     const bool cached = vmax_r && j0 + b < B - 1;
     vv[b] = ok && !cached ? Vr[i] : -INFINITY;
     dd[b] = ok ? Dr[q - i] : 0.0f;
   }
+}
+
+template <int NB>
+__device__ __forceinline__ void predict_reduce(int combine, int pooling, int N, int B, int j0,
+                                               const float (&vv)[NB], const float (&dd)[NB],
+                                               float vm, float* __restrict__ Srow) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int b = 0; b < kPredBlocksPerWave; ++b) {
+  for (int b = 0; b < NB; ++b) {
     const int j = j0 + b;
     const int i = j * SPIN_BLOCK + lane;
     const float zhat =
@@ -88,6 +97,17 @@ __device__ __forceinline__ void predict_wave(int combine, int pooling, int N, in
             : pool_block_wave(zhat, i < N, min(SPIN_BLOCK, N - j * SPIN_BLOCK), pooling);
     if (lane == 0 && j < B) Srow[j] = m + 0.0f;
   }
+}
+
+// One wave's 8 blocks j0 .. j0+7 (j0 < B) of one (request, row).
+__device__ __forceinline__ void predict_wave(int combine, int pooling, int N, int B, int q,
+                                             int j0, const float* __restrict__ Vr,
+                                             const float* __restrict__ Dr,
+                                             const float* __restrict__ vmax_r,
+                                             float* __restrict__ Srow) {
+  float vv[kPredBlocksPerWave], dd[kPredBlocksPerWave], vm;
+  predict_load<kPredBlocksPerWave>(N, B, q, j0, Vr, Dr, vmax_r, vv, dd, vm);
+  predict_reduce<kPredBlocksPerWave>(combine, pooling, N, B, j0, vv, dd, vm, Srow);
 }
 
 // ---------------------------------------------------------------------------
