@@ -111,13 +111,29 @@ enum { SPIN_DERR_CTX = 1,   /* ctx_len < 1, > 64*max_blocks or > v_ld        */
  *    pooling flag's rule over its valid slots), three fp32 roundings per
  *    update, rows replayed in order; prediction S[j] = C(V[j], D[floor(q /
  *    64) - j]).  v_max does not apply.
+ *  - SPIN_PREDICT_AHEAD (an execution choice; results are unchanged, bit for
+ *    bit): the EMA update of a whole step (spin_step, spin_step_finish,
+ *    spin_stack_step, spin_stack_commit) also computes, from the state it has
+ *    just written, the block scores the next step's prediction (Eq. 1, Eq. 2)
+ *    would, at that step's position q + A (A = the counter advance), into
+ *    io->S, and records (step, q + A, ctx_len) per request in io->s_tag.  The
+ *    next step's prediction then skips every request whose tag matches its
+ *    step counter, q_pos and ctx_len, so the prediction reads no V or D of its
+ *    own; any other request is predicted as usual.  One verifier row: with
+ *    several the flag changes nothing (the EMA runs as without it and the
+ *    next step predicts).  Requires block reduction A1 and io->s_tag.  Between such steps V, D, v_max and S must change only
+ *    through these calls (or spin_reset_state, which zeroes the step counter
+ *    and so invalidates every tag): a caller that edits them otherwise sets
+ *    the affected tags to -1.  The step workspace grows by 4 R max_blocks
+ *    bytes (spin_workspace_bytes).
  */
 enum {
   SPIN_POOL_MAX = 0, SPIN_POOL_TOP4 = 1, SPIN_POOL_MEAN = 2, SPIN_POOL_MASK = 3,
   SPIN_MTP_ROW0_MASK = 4, SPIN_MTP_ROW0_UPDATE = 8, SPIN_EXPLORE_PER_ROW = 16,
   SPIN_EXPLORE_AGE = 32, SPIN_EXPLORE_STALENESS = 64, SPIN_EXPLORE_POLICY_MASK = 96,
   SPIN_REDUCE_A0 = 128, SPIN_REDUCE_A2 = 256, SPIN_REDUCE_MASK = 384,
-  SPIN_FLAGS_ALL = 511
+  SPIN_PREDICT_AHEAD = 512,
+  SPIN_FLAGS_ALL = 1023
 };
 
 /* Method parameters, passed by host pointer and copied by value. */
@@ -285,6 +301,9 @@ typedef struct spin_step_io {
   void* workspace; size_t workspace_bytes;
   int32_t* last_obs;                    /* optional i32 [R][max_blocks]: see
                                            spin_select_blocks                 */
+  int32_t* s_tag;                       /* with SPIN_PREDICT_AHEAD: i32 [R][4],
+                                           caller-owned, -1 before the first
+                                           step (none predicted ahead)        */
 } spin_step_io;
 
 /*

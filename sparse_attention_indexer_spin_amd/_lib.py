@@ -33,6 +33,7 @@ SPIN_POOL_MAX, SPIN_POOL_TOP4, SPIN_POOL_MEAN = 0, 1, 2
 SPIN_MTP_ROW0_MASK, SPIN_MTP_ROW0_UPDATE, SPIN_EXPLORE_PER_ROW = 4, 8, 16
 SPIN_EXPLORE_AGE, SPIN_EXPLORE_STALENESS = 32, 64
 SPIN_REDUCE_A0, SPIN_REDUCE_A2 = 128, 256
+SPIN_PREDICT_AHEAD = 512
 
 
 class SpinConfig(C.Structure):
@@ -57,7 +58,8 @@ class SpinStepIO(C.Structure):
                 ("row_code", C.c_void_p), ("sel", C.c_void_p), ("n_sel", C.c_void_p),
                 ("z", C.c_void_p), ("z_ld", C.c_int64), ("topk_idx", C.c_void_p),
                 ("q_pos_mut", C.c_void_p), ("step_mut", C.c_void_p), ("workspace", C.c_void_p),
-                ("workspace_bytes", C.c_size_t), ("last_obs", C.c_void_p)]
+                ("workspace_bytes", C.c_size_t), ("last_obs", C.c_void_p),
+                ("s_tag", C.c_void_p)]
 
 
 class SpinBudgetPolicy(C.Structure):

@@ -45,12 +45,14 @@ def config(*, topk: int, sparsity_bp: int, explore_bp: int = 500, ema_alpha: flo
            n_heads: int = 64, head_dim: int = 128, block_size: int = 64, pooling: str = "max",
            mtp_row0_mask: bool = False, mtp_row0_update: bool = False,
            explore_per_row: bool = False, explore: str = "random",
-           reduction: str = "A1") -> L.SpinConfig:
-    """spin_config; the keyword variants map to spin_config.flags (defaults: the paper's)."""
+           reduction: str = "A1", predict_ahead: bool = False) -> L.SpinConfig:
+    """spin_config; the keyword variants map to spin_config.flags (defaults: the paper's).
+    predict_ahead (SPIN_PREDICT_AHEAD) changes where the prediction runs, not its results."""
     flags = (_POOL[pooling] | (L.SPIN_MTP_ROW0_MASK if mtp_row0_mask else 0)
              | (L.SPIN_MTP_ROW0_UPDATE if mtp_row0_update else 0)
              | (L.SPIN_EXPLORE_PER_ROW if explore_per_row else 0)
-             | _EXPLORE[explore] | _REDUCE[reduction])
+             | _EXPLORE[explore] | _REDUCE[reduction]
+             | (L.SPIN_PREDICT_AHEAD if predict_ahead else 0))
     return L.SpinConfig(n_heads=n_heads, head_dim=head_dim, block_size=block_size, topk=topk,
                         sparsity_bp=sparsity_bp, explore_bp=explore_bp, ema_alpha=ema_alpha,
                         combine=L.SPIN_COMBINE_SUM if combine == "sum" else L.SPIN_COMBINE_MAX,
@@ -124,7 +126,7 @@ def spin_reset_state(V, D, step, stream=None, v_max=None):
 
 def step_io(*, V, D, q, w, k_pages, k_scale, page_table, S, row_code, sel, n_sel, z, topk_idx,
             budget=None, n_valid=None, q_pos_mut=None, step_mut=None, workspace=None,
-            v_max=None, last_obs=None):
+            v_max=None, last_obs=None, s_tag=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return L.SpinStepIO(V=_p(V), v_ld=_ld(V), D=_p(D), d_ld=_ld(D), v_max=_p(v_max), q=_p(q),
                         w=_p(w),
@@ -133,7 +135,7 @@ def step_io(*, V, D, q, w, k_pages, k_scale, page_table, S, row_code, sel, n_sel
                         row_code=_p(row_code), sel=_p(sel), n_sel=_p(n_sel), z=_p(z),
                         z_ld=_ld(z), topk_idx=_p(topk_idx), q_pos_mut=_p(q_pos_mut),
                         step_mut=_p(step_mut), workspace=_p(workspace), workspace_bytes=ws_bytes,
-                        last_obs=_p(last_obs))
+                        last_obs=_p(last_obs), s_tag=_p(s_tag))
 
 
 def spin_step(cfg, bt, io, defer_ema: bool = False, stream=None):

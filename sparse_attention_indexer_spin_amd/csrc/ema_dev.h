@@ -3,6 +3,7 @@
 // shared by the EMA kernel and the kernel that runs it beside the top-K.
 #pragma once
 #include "spin_dev.h"
+#include "plan_dev.h"
 
 namespace spin {
 
@@ -248,6 +249,178 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
 // One wave: selected blocks k0 .. k0 + kEmaBlocksPerWave - 1 of request r.
 __device__ __forceinline__ void ema_wave(const EmaArgs& A, int r, int k0, bool advance) {
   ema_blocks<kEmaBlocksPerWave>(A, r, k0, k0 + kEmaBlocksPerWave, advance);
+}
+
+
+// ---------------------------------------------------------------------------
+// The EMA update of a whole step fused with the next step's prediction
+// (SPIN_PREDICT_AHEAD, block reduction A1, one verifier row): the block scores
+// the next step would predict from the updated V and D at its position
+// q' = q + A (A = the step's counter advance, 0 or 1), written to S beside a
+// tag (step, q', N) that lets that step skip its own prediction.  Work goes
+// by block j, selected or not, one wave per block, lane l for slot
+// i = 64 j + l:
+//  * V[i]: the update where block j is selected (and the row counts);
+//  * D at offset q' - i, owned by lane l for i < N + A: its update at this
+//    step comes from slot i - A, in block j or (lane 0, A = 1) the last slot
+//    of block j - 1.  The owned offsets [q' - N - A + 1, q'] contain every
+//    offset the step updates, [q - N + 1, q + L - 1], each once, and the next
+//    step's prediction of block j reads exactly block j's, so no wave reads
+//    what another writes.  (With several rows the next step's row r would
+//    also read r offsets of block j - 1's range, written by another wave:
+//    there the flag leaves the EMA as it is and the next step predicts.)
+// The predicted scores are those of predict_block_scores on the updated
+// state: the same pooling code, on the same fp32 values.
+// ---------------------------------------------------------------------------
+struct EmaPredArgs {
+  EmaArgs e;            // the EMA's (qpos: the step's q positions; rows == 1)
+  const int32_t* inv;   // [R][max_blocks]: position of block j in sel, -1 if not selected
+  int combine, pooling;
+  float* S;             // [R][max_blocks]: the next step's block scores
+  int32_t* tag;         // [R][4]: step, q', N the scores are for (-1: none)
+};
+
+// Where a whole step's EMA also puts the next step's block scores
+// (SPIN_PREDICT_AHEAD): the step's inverse block map, S and the tags.
+struct Ahead {
+  const int32_t* inv;
+  float* S;
+  int32_t* tag;
+};
+
+inline EmaPredArgs ema_pred_args(const spin_config& c, const EmaArgs& e, const Ahead* a) {
+  return EmaPredArgs{e, a ? a->inv : nullptr, c.combine, c.flags & SPIN_POOL_MASK,
+                     a ? a->S : nullptr, a ? a->tag : nullptr};
+}
+
+// Request r's blocks [w nb / n, (w + 1) nb / n) for worker w of n, nb the
+// blocks whose lanes own offsets; `advance`: this thread also advances r's
+// counters and writes its tag.  The blocks' positions in sel come from one
+// vector load per 63 blocks (lane l: block base + l), and CH blocks' loads
+// are issued together, two such chunks in flight: a chunk's loads depend on
+// no load of its own, so a wave waits about one memory round per chunk.
+template <int CH>
+__device__ __forceinline__ void ema_predict_blocks(const EmaPredArgs& P, int r, int w, int n,
+                                                   bool advance) {
+  const EmaArgs& E = P.e;
+  const int lane = threadIdx.x & 63;
+  const int max_blocks = E.max_blocks;
+  const int N = E.ctx[r], q = E.qpos[r];
+  const int adv = E.n_valid ? E.n_valid[r] : 1;
+  const int A = adv < 0 ? 0 : (adv > 1 ? 1 : adv);
+  const int q1 = q + A;
+  const bool bad = request_error(N, q, 1, max_blocks, E.v_ld, E.d_ld) != 0;
+  const bool pred = !bad && A == adv && E.step_out &&
+                    request_error(N, q1, 1, max_blocks, E.v_ld, E.d_ld) == 0;
+  if (advance) {
+    int st = 0;
+    if (E.qpos_out) E.qpos_out[r] = q + adv;
+    if (E.step_out) {
+      st = E.step_out[r] + 1;
+      E.step_out[r] = st;
+    }
+    if (P.tag) {
+      int32_t* t = P.tag + 4 * (int64_t)r;
+      t[0] = pred ? st : -1;
+      t[1] = q1;
+      t[2] = N;
+      t[3] = 0;
+    }
+  }
+  if (bad) return;
+  const bool upd = (E.row0_only ? 1 : A) > 0;  // the row counts
+  const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  const int nb = (N + A + SPIN_BLOCK - 1) / SPIN_BLOCK;
+  const int j0 = (int)((int64_t)w * nb / n), j1 = (int)((int64_t)(w + 1) * nb / n);
+  if (j0 >= j1) return;
+  const float a = E.alpha, b = __fsub_rn(1.0f, E.alpha);
+  const float* zb = E.z + (int64_t)r * E.z_ld;
+  const int32_t* ir = P.inv + (int64_t)r * max_blocks;
+  float* Vr = E.V + (int64_t)r * E.v_ld;
+  float* Dr = E.D + (int64_t)r * E.d_ld;
+  const int64_t dcap = E.d_ld > 0 ? E.d_ld : INT64_MAX;
+  struct Chunk {
+    float v[CH], d[CH], zv[CH], zd[CH];
+    bool md[CH];
+    int kj[CH];
+  };
+  // lane l of pos: the position of block base + l (-1 past B), base = the
+  // segment's first block - 1; the window is fixed within a segment, so the
+  // chunk loads below wait for no earlier load
+  int base = 0, pos = 0, s1 = j0;
+  // Every load is unconditional, lanes without an element reading element 0
+  // of the same array: loads under branches made the compiler wait for all
+  // outstanding loads where the branches join, the next chunk's too.
+  const auto load = [&](Chunk& C, int jc) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int j = jc + u;
+      const bool on = j < s1;
+      C.kj[u] = on ? __builtin_amdgcn_readlane(pos, j - base) : -1;
+      const int kjm = on ? __builtin_amdgcn_readlane(pos, j - 1 - base) : -1;
+      const int i = j * SPIN_BLOCK + lane;
+      const bool vin = on && i < N;
+      const bool zin = upd && C.kj[u] >= 0 && i < N;
+      const bool own = on && i < N + A;
+      const int64_t o = (int64_t)q1 - i;
+      const bool din = own && o < dcap;
+      const int s = i - A;  // the slot whose score updates offset q' - i
+      const int kk = (s >= 0 && s < N) ? ((s >> 6) == j ? C.kj[u] : kjm) : -1;
+      C.md[u] = upd && own && kk >= 0;
+      const float vx = Vr[vin ? i : 0];
+      const float zx = zb[zin ? (int64_t)C.kj[u] * 64 + lane : 0];
+      const float dx = Dr[din ? o : 0];
+      const float zy = zb[C.md[u] ? (int64_t)kk * 64 + (s & 63) : 0];
+      C.v[u] = vin ? vx : 0.0f;
+      C.zv[u] = zin ? zx : 0.0f;
+      C.d[u] = din ? dx : 0.0f;
+      C.zd[u] = C.md[u] ? zy : 0.0f;
+    }
+  };
+  const auto finish = [&](Chunk& C, int jc) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int j = jc + u;
+      if (j >= s1) break;
+      const int i = j * SPIN_BLOCK + lane;
+      if (upd && C.kj[u] >= 0) {
+        C.v[u] = ema_step(C.v[u], C.zv[u], a, b);
+        if (i < N) Vr[i] = C.v[u];
+        if (E.vmax) ema_vmax(E, r, j, i < N, C.v[u]);
+      }
+      if (C.md[u]) {
+        C.d[u] = ema_step(C.d[u], C.zd[u], a, b);
+        Dr[q1 - i] = C.d[u];
+      }
+      if (!pred || j >= B) continue;
+      const float zhat =
+          P.combine == SPIN_COMBINE_SUM ? __fadd_rn(C.v[u], C.d[u]) : fmaxf(C.v[u], C.d[u]);
+      const float m = P.pooling == SPIN_POOL_MAX
+                          ? wave_max_f32(i < N ? zhat : -INFINITY)
+                          : pool_block_wave(zhat, i < N, min(SPIN_BLOCK, N - j * SPIN_BLOCK),
+                                            P.pooling);
+      if (lane == 0) P.S[(int64_t)r * max_blocks + j] = m + 0.0f;
+    }
+  };
+  // segments of up to 63 blocks, each with its window of positions
+  for (int sg = j0; sg < j1; sg += 63) {
+    s1 = min(j1, sg + 63);
+    base = sg - 1;
+    {
+      const int jj = base + lane;
+      const int px = ir[jj >= 0 && jj < B ? jj : 0];
+      pos = jj >= 0 && jj < B ? px : -1;
+    }
+    Chunk c0, c1;
+    load(c0, sg);
+    for (int jc = sg; jc < s1; jc += 2 * CH) {
+      if (jc + CH < s1) load(c1, jc + CH);
+      finish(c0, jc);
+      if (jc + CH >= s1) break;
+      if (jc + 2 * CH < s1) load(c0, jc + 2 * CH);
+      finish(c1, jc + CH);
+    }
+  }
 }
 
 }  // namespace spin

@@ -102,14 +102,31 @@ __global__ __launch_bounds__(256) void k_ema(EmaArgs A) {
   ema_wave(A, r, k0, blockIdx.x == 0 && threadIdx.x == 0);
 }
 
+// The EMA update and the next step's block scores (SPIN_PREDICT_AHEAD, one
+// row): wave w of each request's n takes blocks [w nb / n, (w + 1) nb / n).
+__global__ __launch_bounds__(256) void k_ema_predict(EmaPredArgs P) {
+  const int r = blockIdx.y;
+  const int n = (int)gridDim.x * 4, w = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  ema_predict_blocks<4>(P, r, w, n, blockIdx.x == 0 && threadIdx.x == 0);
+}
+
 hipError_t launch_ema(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                       const int32_t* sel, const int32_t* n_sel, const int32_t* n_valid, float* V,
                       int64_t v_ld, float* D, int64_t d_ld, float* vmax, hipStream_t st,
-                      const int32_t* qpos_snap, int32_t* qpos_out, int32_t* step_out) {
-  dim3 grid((b.max_blocks + 4 * kEmaBlocksPerWave - 1) / (4 * kEmaBlocksPerWave), b.batch);
+                      const int32_t* qpos_snap, int32_t* qpos_out, int32_t* step_out,
+                      const Ahead* ahead) {
   const EmaArgs A{c.ema_alpha, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap ? qpos_snap : b.q_pos,
                   n_valid, z, z_ld, sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out, vmax,
                   (c.flags & SPIN_MTP_ROW0_UPDATE) != 0};
+  if (ahead) {
+    // every block (and the one past the last, whose first lanes hold the
+    // offset of the slot just beyond the context), 4 blocks per wave
+    if (b.n_rows != 1) return hipErrorInvalidValue;
+    dim3 grid((b.max_blocks + 1 + 15) / 16, b.batch);
+    hipLaunchKernelGGL(k_ema_predict, grid, dim3(256), 0, st, ema_pred_args(c, A, ahead));
+    return hipGetLastError();
+  }
+  dim3 grid((b.max_blocks + 4 * kEmaBlocksPerWave - 1) / (4 * kEmaBlocksPerWave), b.batch);
   hipLaunchKernelGGL(k_ema, grid, dim3(256), 0, st, A);
   return hipGetLastError();
 }

@@ -71,7 +71,9 @@ __global__ __launch_bounds__(256) void k_predict_rows(int combine, int pooling, 
                                                       const float* __restrict__ D, int64_t d_ld,
                                                       const float* __restrict__ vmax,
                                                       float* __restrict__ S, int32_t* err,
-                                                      int32_t* __restrict__ qpos_snap) {
+                                                      int32_t* __restrict__ qpos_snap,
+                                                      const int32_t* __restrict__ step,
+                                                      const int32_t* __restrict__ tag) {
   const int r = blockIdx.z;
   const int N = ctx[r], q0 = qpos[r];
   if (qpos_snap && blockIdx.x == 0 && threadIdx.x == 0) qpos_snap[r] = q0;
@@ -80,6 +82,7 @@ __global__ __launch_bounds__(256) void k_predict_rows(int combine, int pooling, 
     if (blockIdx.x == 0 && threadIdx.x == 0) raise_error(err, e);
     return;
   }
+  if (predicted_ahead(tag, step, r, q0, N)) return;
   const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
   const int j0 = (blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * kPredBlocksPerWave;
   if (j0 >= B) return;
@@ -97,7 +100,9 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int pooling, int r
                                                  const float* __restrict__ D, int64_t d_ld,
                                                  const float* __restrict__ vmax,
                                                  float* __restrict__ S, int32_t* err,
-                                                 int32_t* __restrict__ qpos_snap) {
+                                                 int32_t* __restrict__ qpos_snap,
+                                                 const int32_t* __restrict__ step,
+                                                 const int32_t* __restrict__ tag) {
   const int r = blockIdx.z, row = blockIdx.y;
   const int N = ctx[r], q0 = qpos[r];
   // a whole step keeps the step's query position here for the fused EMA +
@@ -108,6 +113,7 @@ __global__ __launch_bounds__(256) void k_predict(int combine, int pooling, int r
     if (row == 0 && blockIdx.x == 0 && threadIdx.x == 0) raise_error(err, e);
     return;
   }
+  if (predicted_ahead(tag, step, r, q0, N)) return;
   const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
   const int j0 = (blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * kPredBlocksPerWave;
   if (j0 >= B) return;
@@ -122,7 +128,7 @@ template <int EPT>
 __device__ __forceinline__ void union_row(int rows, int n_use, int max_blocks, int r, int B,
                                           const uint8_t* __restrict__ code,
                                           int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
-                                          int* sh, int32_t* last_obs, int t) {
+                                          int* sh, int32_t* last_obs, int t, int32_t* inv) {
   const int j0 = threadIdx.x * EPT;
   uint32_t any = 0u;
   for (int row = 0; row < n_use; ++row) {  // the first n_use rows' masks
@@ -131,7 +137,8 @@ __device__ __forceinline__ void union_row(int rows, int n_use, int max_blocks, i
     for (int e = 0; e < EPT; ++e)
       if (j0 + e < B && crow[j0 + e] != SPIN_CODE_SKIP) any |= 1u << e;
   }
-  compact_blocks<EPT>(any, max_blocks, sel + (int64_t)r * max_blocks, n_sel + r, sh);
+  compact_blocks<EPT>(any, max_blocks, sel + (int64_t)r * max_blocks, n_sel + r, sh,
+                      inv ? inv + (int64_t)r * max_blocks : nullptr);
   record_observed<EPT>(last_obs ? last_obs + (int64_t)r * max_blocks : nullptr, j0, B, any, t);
 }
 
@@ -158,13 +165,13 @@ __global__ __launch_bounds__(kSelThreads) void k_union(int rows, int n_use, int 
                                                        const uint8_t* __restrict__ code,
                                                        int32_t* __restrict__ sel,
                                                        int32_t* __restrict__ n_sel,
-                                                       int32_t* last_obs) {
+                                                       int32_t* last_obs, int32_t* inv) {
   __shared__ int sh[32];
   const int r = blockIdx.x;
   const int N = ctx[r];
   const bool bad = request_error(N, qpos[r], rows, max_blocks, 0, 0) != 0;
   const int B = bad ? 0 : (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
-  union_row<EPT>(rows, n_use, max_blocks, r, B, code, sel, n_sel, sh, last_obs, step[r]);
+  union_row<EPT>(rows, n_use, max_blocks, r, B, code, sel, n_sel, sh, last_obs, step[r], inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -328,22 +335,22 @@ static bool vmax_usable(const spin_config& c) {
 template <int ROWS>
 static void predict_rows_t(const spin_config& c, const spin_batch& b, const float* V,
                            int64_t v_ld, const float* D, int64_t d_ld, const float* vmax,
-                           float* S, hipStream_t st, int32_t* qpos_snap) {
+                           float* S, hipStream_t st, int32_t* qpos_snap, const int32_t* tag) {
   dim3 grid((b.max_blocks + 4 * kPredBlocksPerWave - 1) / (4 * kPredBlocksPerWave), 1, b.batch);
   const int pooling = c.flags & SPIN_POOL_MASK;
   hipLaunchKernelGGL(k_predict_rows<ROWS>, grid, dim3(256), 0, st, c.combine, pooling,
                      b.max_blocks, b.ctx_len, b.q_pos, V, v_ld, D, d_ld,
-                     vmax_usable(c) ? vmax : nullptr, S, b.err, qpos_snap);
+                     vmax_usable(c) ? vmax : nullptr, S, b.err, qpos_snap, b.step, tag);
 }
 
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
                           const float* D, int64_t d_ld, const float* vmax, float* S,
-                          hipStream_t st, int32_t* qpos_snap) {
+                          hipStream_t st, int32_t* qpos_snap, const int32_t* tag) {
   if (b.n_rows > 1) {  // every row from one load of V and D
     switch (b.n_rows) {
-      case 2: predict_rows_t<2>(c, b, V, v_ld, D, d_ld, vmax, S, st, qpos_snap); break;
-      case 3: predict_rows_t<3>(c, b, V, v_ld, D, d_ld, vmax, S, st, qpos_snap); break;
-      default: predict_rows_t<4>(c, b, V, v_ld, D, d_ld, vmax, S, st, qpos_snap); break;
+      case 2: predict_rows_t<2>(c, b, V, v_ld, D, d_ld, vmax, S, st, qpos_snap, tag); break;
+      case 3: predict_rows_t<3>(c, b, V, v_ld, D, d_ld, vmax, S, st, qpos_snap, tag); break;
+      default: predict_rows_t<4>(c, b, V, v_ld, D, d_ld, vmax, S, st, qpos_snap, tag); break;
     }
     return hipGetLastError();
   }
@@ -351,12 +358,13 @@ hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float
             b.batch);
   hipLaunchKernelGGL(k_predict, grid, dim3(256), 0, st, c.combine, c.flags & SPIN_POOL_MASK,
                      b.n_rows, b.max_blocks, b.ctx_len, b.q_pos, V, v_ld, D, d_ld,
-                     vmax_usable(c) ? vmax : nullptr, S, b.err, qpos_snap);
+                     vmax_usable(c) ? vmax : nullptr, S, b.err, qpos_snap, b.step, tag);
   return hipGetLastError();
 }
 
 static SelectArgs select_args(const spin_config& c, const spin_batch& b, uint8_t* code,
-                              int32_t* sel, int32_t* n_sel, int32_t* last_obs) {
+                              int32_t* sel, int32_t* n_sel, int32_t* last_obs,
+                              int32_t* inv = nullptr) {
   const int pol = c.flags & SPIN_EXPLORE_POLICY_MASK;
   return SelectArgs{c.topk, c.sparsity_bp, c.explore_bp, c.layer,
                     (c.flags & SPIN_EXPLORE_PER_ROW) != 0,
@@ -365,16 +373,17 @@ static SelectArgs select_args(const spin_config& c, const spin_batch& b, uint8_t
                     pol == SPIN_EXPLORE_AGE ? kExploreAge
                                             : pol == SPIN_EXPLORE_STALENESS ? kExploreStaleness
                                                                             : kExploreRandom,
-                    last_obs};
+                    last_obs, inv};
 }
 
 PredictPlan predict_plan(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
                          const float* D, int64_t d_ld, const float* vmax, float* S,
-                         int32_t* qpos_snap) {
+                         int32_t* qpos_snap, const int32_t* tag) {
   const int per_req = (b.max_blocks + kPredBlocksPerWg - 1) / kPredBlocksPerWg;
   return PredictPlan{PredictArgs{c.combine, c.flags & SPIN_POOL_MASK, b.max_blocks, per_req,
                                  b.ctx_len, b.q_pos, V, v_ld, D, d_ld,
-                                 vmax_usable(c) ? vmax : nullptr, S, b.err, qpos_snap},
+                                 vmax_usable(c) ? vmax : nullptr, S, b.err, qpos_snap, b.step,
+                                 tag},
                      b.batch * per_req};
 }
 
@@ -387,10 +396,11 @@ static int select_ept(int max_blocks) {
 template <int EPT>
 static void select_t(const spin_config& c, const spin_batch& b, const float* S,
                      const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                     int32_t* last_obs, hipStream_t st) {
+                     int32_t* last_obs, hipStream_t st, int32_t* inv) {
   const int compact = b.n_rows == 1;
   hipLaunchKernelGGL(k_select<EPT>, dim3(b.n_rows, b.batch), dim3(kSelectThreads), 0, st,
-                     select_args(c, b, code, sel, n_sel, last_obs), b.ctx_len, b.q_pos, b.step,
+                     select_args(c, b, code, sel, n_sel, last_obs, inv), b.ctx_len, b.q_pos,
+                     b.step,
                      b.req_id, S, budget, compact);
 }
 
@@ -406,40 +416,41 @@ static void a0_select_t(const spin_config& c, const spin_batch& b, const float* 
 
 template <int EPT>
 static void union_t(const spin_config& c, const spin_batch& b, uint8_t* code, int32_t* sel,
-                    int32_t* n_sel, int32_t* last_obs, hipStream_t st) {
+                    int32_t* n_sel, int32_t* last_obs, hipStream_t st, int32_t* inv) {
   // row-0 sharing scores row 0's mask alone
   const int n_use = (c.flags & SPIN_MTP_ROW0_MASK) ? 1 : b.n_rows;
   hipLaunchKernelGGL(k_union<EPT>, dim3(b.batch), dim3(kSelThreads), 0, st, b.n_rows, n_use,
-                     b.max_blocks, b.ctx_len, b.q_pos, b.step, code, sel, n_sel, last_obs);
+                     b.max_blocks, b.ctx_len, b.q_pos, b.step, code, sel, n_sel, last_obs, inv);
 }
 
 static void launch_union(const spin_config& c, const spin_batch& b, uint8_t* code, int32_t* sel,
-                         int32_t* n_sel, int32_t* last_obs, hipStream_t st) {
+                         int32_t* n_sel, int32_t* last_obs, hipStream_t st,
+                         int32_t* inv = nullptr) {
   const int eu = (b.max_blocks + kSelThreads - 1) / kSelThreads;
-  if (eu <= 1) union_t<1>(c, b, code, sel, n_sel, last_obs, st);
-  else if (eu <= 2) union_t<2>(c, b, code, sel, n_sel, last_obs, st);
-  else if (eu <= 4) union_t<4>(c, b, code, sel, n_sel, last_obs, st);
-  else union_t<8>(c, b, code, sel, n_sel, last_obs, st);
+  if (eu <= 1) union_t<1>(c, b, code, sel, n_sel, last_obs, st, inv);
+  else if (eu <= 2) union_t<2>(c, b, code, sel, n_sel, last_obs, st, inv);
+  else if (eu <= 4) union_t<4>(c, b, code, sel, n_sel, last_obs, st, inv);
+  else union_t<8>(c, b, code, sel, n_sel, last_obs, st, inv);
 }
 
 SelectPlan select_plan(const spin_config& c, const spin_batch& b, const float* S,
                        const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                       int32_t* last_obs) {
-  return SelectPlan{select_args(c, b, code, sel, n_sel, last_obs),
+                       int32_t* last_obs, int32_t* inv) {
+  return SelectPlan{select_args(c, b, code, sel, n_sel, last_obs, inv),
                     SelectInputs{b.ctx_len, b.q_pos, b.step, b.req_id, S, budget}, b.batch,
                     select_ept(b.max_blocks)};
 }
 
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                         int32_t* last_obs, hipStream_t st) {
+                         int32_t* last_obs, hipStream_t st, int32_t* inv) {
   switch (select_ept(b.max_blocks)) {
-    case 1: select_t<1>(c, b, S, budget, code, sel, n_sel, last_obs, st); break;
-    case 2: select_t<2>(c, b, S, budget, code, sel, n_sel, last_obs, st); break;
-    case 4: select_t<4>(c, b, S, budget, code, sel, n_sel, last_obs, st); break;
-    default: select_t<8>(c, b, S, budget, code, sel, n_sel, last_obs, st); break;
+    case 1: select_t<1>(c, b, S, budget, code, sel, n_sel, last_obs, st, inv); break;
+    case 2: select_t<2>(c, b, S, budget, code, sel, n_sel, last_obs, st, inv); break;
+    case 4: select_t<4>(c, b, S, budget, code, sel, n_sel, last_obs, st, inv); break;
+    default: select_t<8>(c, b, S, budget, code, sel, n_sel, last_obs, st, inv); break;
   }
-  if (b.n_rows > 1) launch_union(c, b, code, sel, n_sel, last_obs, st);  // the rows' masks
+  if (b.n_rows > 1) launch_union(c, b, code, sel, n_sel, last_obs, st, inv);  // the rows' masks
   return hipGetLastError();
 }
 

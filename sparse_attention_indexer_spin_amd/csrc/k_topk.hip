@@ -350,7 +350,7 @@ struct PagesShared {
   uint32_t tmpu[32];
 };
 
-__device__ void topk_pages_row(int rowid, int K, int rows, int max_blocks,
+__device__ __forceinline__ void topk_pages_row(int rowid, int K, int rows, int max_blocks,
                                const int32_t* __restrict__ ctx, const int32_t* __restrict__ qpos,
                                const float* __restrict__ z, int64_t z_ld,
                                const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
@@ -469,6 +469,9 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select_pages(
 // blocks whose loads an EMA wave issues together (two such chunks are in
 // flight; 16 made the 1,024-thread kernel spill)
 constexpr int kEmaChunk = 6;
+// blocks whose loads a wave of the fused EMA + next-step prediction issues
+// together
+constexpr int kAheadChunk = 4;
 
 // SEPT > 0: the last `sel_wgs` workgroups select the blocks of another layer
 // (one verifier row, SEPT blocks per thread), one request each.
@@ -477,8 +480,9 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_ema(
     int K, int rows, int max_blocks, const int32_t* __restrict__ ctx,
     const int32_t* __restrict__ qpos, const float* __restrict__ z, int64_t z_ld,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
-    int32_t* __restrict__ out, TopkWs ws, int rows_total, EmaArgs A, int ema_x,
+    int32_t* __restrict__ out, TopkWs ws, int rows_total, EmaPredArgs PA, int ema_x,
     SelectArgs sa, SelectInputs si, int sel_wgs) {
+  const EmaArgs& A = PA.e;
   __shared__ __align__(16) PagesShared L;
   if constexpr (SEPT > 0) {
     const int s0 = (int)gridDim.x - sel_wgs;
@@ -497,6 +501,10 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_ema(
   const int e = blockIdx.x - rows_total, r = e / ema_x, bx = e % ema_x;
   constexpr int kWaves = kSelThreads / 64;
   const int n_waves = ema_x * kWaves, w = bx * kWaves + (int)(threadIdx.x >> 6);
+  if (PA.S) {  // SPIN_PREDICT_AHEAD (one row): every block, and the next step's scores
+    ema_predict_blocks<kAheadChunk>(PA, r, w, n_waves, w == 0 && threadIdx.x == 0);
+    return;
+  }
   const int ns = clamp_nsel(A.n_sel[r], A.max_blocks);
   const int k0 = (int)((int64_t)w * ns / n_waves), k1 = (int)((int64_t)(w + 1) * ns / n_waves);
   ema_blocks<kEmaChunk>(A, r, k0, k1, w == 0 && threadIdx.x == 0);
@@ -508,13 +516,14 @@ size_t topk_workspace_bytes(const spin_config&, int R, int rows, int max_blocks)
 
 size_t step_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks) {
   return (size_t)align256((int64_t)topk_workspace_bytes(c, R, rows, max_blocks)) +
-         (size_t)align256(4LL * R);
+         (size_t)align256(4LL * R) +
+         ((c.flags & SPIN_PREDICT_AHEAD) ? (size_t)align256(4LL * R * max_blocks) : 0);
 }
 
 template <int SEPT>
 static void topk_ema_t(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                        const int32_t* sel, const int32_t* n_sel, int32_t* out, const TopkWs& ws,
-                       const EmaArgs& A, const SelectArgs& sa, const SelectInputs& si,
+                       const EmaPredArgs& A, const SelectArgs& sa, const SelectInputs& si,
                        int sel_wgs, hipStream_t st, bool ema) {
   const int rows_total = b.batch * b.n_rows;
   constexpr int per_block = (kSelThreads / 64) * kEmaChunk;
@@ -526,7 +535,7 @@ static void topk_ema_t(const spin_config& c, const spin_batch& b, const float* z
   const int ema_x = ema ? max(1, min(most, free_cus / max(1, b.batch))) : 0;
   hipLaunchKernelGGL(k_topk_ema<SEPT>, dim3(rows_total + ema_x * b.batch + sel_wgs),
                      dim3(kSelThreads), 0, st, c.topk, b.n_rows, b.max_blocks, b.ctx_len,
-                     A.qpos, z, z_ld, sel, n_sel, out, ws, rows_total, A, ema_x, sa, si,
+                     A.e.qpos, z, z_ld, sel, n_sel, out, ws, rows_total, A, ema_x, sa, si,
                      sel_wgs);
 }
 
@@ -535,12 +544,14 @@ hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const floa
                            void* wsp, const int32_t* n_valid, float* V, int64_t v_ld, float* D,
                            int64_t d_ld, float* vmax, const int32_t* qpos_snap,
                            int32_t* qpos_out, int32_t* step_out, hipStream_t st,
-                           const SelectPlan* next, bool ema) {
+                           const SelectPlan* next, bool ema, const Ahead* ahead) {
   const int rows_total = b.batch * b.n_rows;
   const TopkWs ws = carve(wsp, rows_total, b.max_blocks);
-  const EmaArgs A{c.ema_alpha, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap, n_valid, z, z_ld,
-                  sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out, vmax,
-                  (c.flags & SPIN_MTP_ROW0_UPDATE) != 0};
+  const EmaPredArgs A = ema_pred_args(
+      c, EmaArgs{c.ema_alpha, b.n_rows, b.max_blocks, b.ctx_len, qpos_snap, n_valid, z, z_ld,
+                 sel, n_sel, V, v_ld, D, d_ld, qpos_out, step_out, vmax,
+                 (c.flags & SPIN_MTP_ROW0_UPDATE) != 0},
+      ahead);
   if (!next) {
     topk_ema_t<0>(c, b, z, z_ld, sel, n_sel, out, ws, A, SelectArgs{}, SelectInputs{}, 0, st,
                   true);

@@ -129,6 +129,7 @@ struct SelectArgs {
   int32_t* n_sel;  // [R]
   int policy;          // kExplore*
   int32_t* last_obs;   // optional [R][max_blocks]: step of each block's last observation
+  int32_t* inv;        // optional [R][max_blocks]: each block's position in sel, -1 if none
 };
 
 // Exploration key of block j (larger = taken first; ties: lower block) under
@@ -237,7 +238,8 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int r, int row, 
     if (j0 + e < B) crow[j0 + e] = c[e];
   if (compact) {
     compact_blocks<EPT, kSelectThreads>(chosen, a.max_blocks, a.sel + (int64_t)r * a.max_blocks,
-                                        a.n_sel + r, L.sh);
+                                        a.n_sel + r, L.sh,
+                                        a.inv ? a.inv + (int64_t)r * a.max_blocks : nullptr);
     // the union is this row's mask: its blocks are observed at step t
     record_observed<EPT>(a.last_obs ? a.last_obs + (int64_t)r * a.max_blocks : nullptr, j0, B,
                          chosen, t);
@@ -267,7 +269,18 @@ struct PredictArgs {
   float* S;            // [R][max_blocks]
   int32_t* err;
   int32_t* qpos_snap;  // optional: the step's q positions
+  const int32_t* step;  // with tag: the step counters
+  const int32_t* tag;   // optional [R][4]: scores already predicted (predicted_ahead)
 };
+
+// Request r's block scores for (step[r], q, N) already sit in S: the last
+// EMA update predicted them (SPIN_PREDICT_AHEAD) and wrote the tag.
+__device__ __forceinline__ bool predicted_ahead(const int32_t* tag, const int32_t* step, int r,
+                                                int q, int N) {
+  if (!tag || !step) return false;
+  const int32_t* t = tag + 4 * (int64_t)r;
+  return t[0] >= 0 && t[0] == step[r] && t[1] == q && t[2] == N;
+}
 
 __device__ __forceinline__ void predict_wg(const PredictArgs& a, int w) {
   const int r = w / a.per_req, bx = w % a.per_req;
@@ -278,6 +291,7 @@ __device__ __forceinline__ void predict_wg(const PredictArgs& a, int w) {
     if (bx == 0 && threadIdx.x == 0) raise_error(a.err, e);
     return;
   }
+  if (predicted_ahead(a.tag, a.step, r, q0, N)) return;
   const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
   const int wave = threadIdx.x >> 6;
   for (int g = 0; g < kPredGroups; ++g) {

@@ -57,6 +57,8 @@ spin_status check_config(const char* fn, const spin_config* c) {
     return fail(SPIN_E_SHAPE, "%s: unknown flags 0x%x", fn, c->flags);
   if ((c->flags & SPIN_EXPLORE_PER_ROW) && (c->layer < 0 || c->layer >= 65536))
     return fail(SPIN_E_SHAPE, "%s: per-row exploration needs 0 <= layer < 65536", fn);
+  if ((c->flags & SPIN_PREDICT_AHEAD) && (c->flags & SPIN_REDUCE_MASK) != 0)
+    return fail(SPIN_E_SHAPE, "%s: SPIN_PREDICT_AHEAD needs block reduction A1", fn);
   return SPIN_OK;
 }
 
@@ -326,6 +328,7 @@ spin_status check_step(const char* fn, const spin_config* cfg, const spin_batch*
   if (!io->workspace || io->workspace_bytes < need)
     return fail(SPIN_E_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
   if (explore_needs_obs(*cfg)) SPIN_REQUIRE(io->last_obs);
+  if (cfg->flags & SPIN_PREDICT_AHEAD) SPIN_REQUIRE(io->s_tag);
   return SPIN_OK;
 }
 
@@ -334,6 +337,30 @@ int32_t* step_qsnap(const spin_config& c, const spin_batch& b, const spin_step_i
   const size_t topk_bytes = spin::topk_workspace_bytes(c, b.batch, b.n_rows, b.max_blocks);
   return reinterpret_cast<int32_t*>(static_cast<char*>(io.workspace) +
                                     ((topk_bytes + 255) & ~size_t(255)));
+}
+
+bool ahead_on(const spin_config& c) { return (c.flags & SPIN_PREDICT_AHEAD) != 0; }
+
+// With SPIN_PREDICT_AHEAD: each block's position in sel, written by the
+// step's selection for its EMA, after the snapshot (256-B aligned).
+int32_t* step_inv(const spin_config& c, const spin_batch& b, const spin_step_io& io) {
+  if (!ahead_on(c)) return nullptr;
+  const size_t snap = (size_t)4 * b.batch;
+  return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(step_qsnap(c, b, io)) +
+                                    ((snap + 255) & ~size_t(255)));
+}
+
+const int32_t* step_tag(const spin_config& c, const spin_step_io& io) {
+  return ahead_on(c) ? io.s_tag : nullptr;
+}
+
+// The step's EMA also predicts the next step's block scores (one verifier
+// row), or nullptr.
+const spin::Ahead* step_ahead(const spin_config& c, const spin_batch& b, const spin_step_io& io,
+                              spin::Ahead& buf) {
+  if (!ahead_on(c) || b.n_rows != 1) return nullptr;
+  buf = spin::Ahead{step_inv(c, b, io), io.S, io.s_tag};
+  return &buf;
 }
 
 // Predict + select (+ union), arguments already checked.
@@ -345,7 +372,7 @@ spin_status issue_plan(const spin_config& c, const spin_batch& b, const spin_ste
                           "spin_step/predict(A2)"));
   } else {
     SPIN_CHECK(hip_status(spin::launch_predict(c, b, io.V, io.v_ld, io.D, io.d_ld, io.v_max,
-                                               io.S, st, step_qsnap(c, b, io)),
+                                               io.S, st, step_qsnap(c, b, io), step_tag(c, io)),
                           "spin_step/predict"));
   }
   if (reduce_a0(c)) {
@@ -362,7 +389,7 @@ spin_status issue_plan(const spin_config& c, const spin_batch& b, const spin_ste
                       "spin_step/select(A0)");
   }
   return hip_status(spin::launch_select(c, b, io.S, io.budget, io.row_code, io.sel, io.n_sel,
-                                        io.last_obs, st),
+                                        io.last_obs, st, step_inv(c, b, io)),
                     "spin_step/select");
 }
 
@@ -387,11 +414,13 @@ spin_status issue_finish(const spin_config& c, const spin_batch& b, const spin_s
                                           io.step_mut),
                       "spin_step/ema+advance(A2)");
   }
+  spin::Ahead abuf;
+  const spin::Ahead* ahead = step_ahead(c, b, io, abuf);
   if (prefilter && !defer_ema)  // top-K beside the EMA update, one launch
     return hip_status(spin::launch_topk_ema(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.topk_idx,
                                             io.workspace, io.n_valid, io.V, io.v_ld, io.D,
                                             io.d_ld, io.v_max, qsnap, io.q_pos_mut, io.step_mut,
-                                            st),
+                                            st, nullptr, true, ahead),
                       "spin_step/topk+ema");
   SPIN_CHECK(hip_status(spin::launch_topk(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.topk_idx,
                                           io.workspace, io.workspace_bytes, st, prefilter),
@@ -402,7 +431,7 @@ spin_status issue_finish(const spin_config& c, const spin_batch& b, const spin_s
   // cannot race with its reads
   return hip_status(spin::launch_ema(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.n_valid, io.V,
                                      io.v_ld, io.D, io.d_ld, io.v_max, st, qsnap, io.q_pos_mut,
-                                     io.step_mut),
+                                     io.step_mut, ahead),
                     "spin_step/ema+advance");
 }
 
@@ -416,10 +445,14 @@ spin_status issue_finish_with_plan(const spin_config& c, const spin_batch& b,
                                    const spin_batch& nb, const spin_step_io& nio,
                                    int32_t defer_ema, hipStream_t st) {
   const spin::CandSink sink = spin::topk_sink(io.workspace, b.batch, b.n_rows, b.max_blocks);
-  const spin::PredictPlan pp = spin::predict_plan(nc, nb, nio.V, nio.v_ld, nio.D, nio.d_ld,
-                                                  nio.v_max, nio.S, step_qsnap(nc, nb, nio));
+  const spin::PredictPlan pp =
+      spin::predict_plan(nc, nb, nio.V, nio.v_ld, nio.D, nio.d_ld, nio.v_max, nio.S,
+                         step_qsnap(nc, nb, nio), step_tag(nc, nio));
   const spin::SelectPlan sp = spin::select_plan(nc, nb, nio.S, nio.budget, nio.row_code,
-                                                nio.sel, nio.n_sel, nio.last_obs);
+                                                nio.sel, nio.n_sel, nio.last_obs,
+                                                step_inv(nc, nb, nio));
+  spin::Ahead abuf;
+  const spin::Ahead* ahead = step_ahead(c, b, io, abuf);
   SPIN_CHECK(hip_status(spin::launch_score(c, b, io.q, io.w, io.k_pages, io.k_scale,
                                            io.page_table, io.pt_ld, io.sel, io.n_sel, io.z,
                                            io.z_ld, st, &sink, &pp),
@@ -427,7 +460,7 @@ spin_status issue_finish_with_plan(const spin_config& c, const spin_batch& b,
   return hip_status(spin::launch_topk_ema(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.topk_idx,
                                           io.workspace, io.n_valid, io.V, io.v_ld, io.D,
                                           io.d_ld, io.v_max, step_qsnap(c, b, io),
-                                          io.q_pos_mut, io.step_mut, st, &sp, !defer_ema),
+                                          io.q_pos_mut, io.step_mut, st, &sp, !defer_ema, ahead),
                     "spin_stack_step/topk+ema+select");
 }
 
@@ -440,9 +473,10 @@ spin_status issue_ema(const spin_config& c, const spin_batch& b, const spin_step
                                           io.v_ld, io.D, io.d_ld, st, step_qsnap(c, b, io),
                                           io.q_pos_mut, io.step_mut),
                       "spin_stack_step/ema+advance(A2)");
+  spin::Ahead abuf;
   return hip_status(spin::launch_ema(c, b, io.z, io.z_ld, io.sel, io.n_sel, io.n_valid, io.V,
                                      io.v_ld, io.D, io.d_ld, io.v_max, st, step_qsnap(c, b, io),
-                                     io.q_pos_mut, io.step_mut),
+                                     io.q_pos_mut, io.step_mut, step_ahead(c, b, io, abuf)),
                     "spin_stack_step/ema+advance");
 }
 
@@ -690,6 +724,13 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
   std::vector<spin_step_io> own(ios, ios + n_layers);
   for (int l = 0; l < n_layers; ++l)
     own[l].budget = probe ? P.probe_budget : P.budget + (int64_t)l * R;
+  // the miss curves read the probe's own block scores: its EMA must not
+  // replace them with the next step's (SPIN_PREDICT_AHEAD), so the probe runs
+  // without the flag (its layers' next step then predicts as usual)
+  std::vector<spin_config> pc(cfgs, cfgs + n_layers);
+  if (probe)
+    for (auto& c : pc) c.flags &= ~SPIN_PREDICT_AHEAD;
+  cfgs = pc.data();
   SPIN_CHECK(stack_step_impl(stack, n_layers, cfgs, bts, own.data(),
                              order_after_main || stack->order_side, 0, main_stream, side_stream,
                              ema_stream));

@@ -303,14 +303,22 @@ __device__ uint32_t block_select_top(const uint32_t (&key)[EPT], uint32_t elig, 
 }
 
 // Write the ascending list of flagged blocks; pad with -1 to max_blocks.
+// inv_row (optional): each block's position in the list, -1 if not flagged.
 template <int EPT, int NT = kSelThreads>
 __device__ void compact_blocks(uint32_t flag, int max_blocks, int32_t* sel_row, int32_t* n_sel_r,
-                               int* sh) {
+                               int* sh, int32_t* inv_row = nullptr) {
   int tot;
   int pos = block_excl_scan<NT>(__popc(flag), sh, &tot);
 #pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    if (flag >> e & 1u) sel_row[pos++] = threadIdx.x * EPT + e;
+  for (int e = 0; e < EPT; ++e) {
+    const int j = threadIdx.x * EPT + e;
+    if (flag >> e & 1u) {
+      if (inv_row) inv_row[j] = pos;
+      sel_row[pos++] = j;
+    } else if (inv_row && j < max_blocks) {
+      inv_row[j] = -1;
+    }
+  }
   for (int i = tot + threadIdx.x; i < max_blocks; i += NT) sel_row[i] = -1;
   if (threadIdx.x == 0) *n_sel_r = tot;
 }

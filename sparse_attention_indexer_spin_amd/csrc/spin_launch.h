@@ -4,6 +4,7 @@
 
 #include "spin.h"
 #include "plan_dev.h"
+#include "ema_dev.h"
 
 namespace spin {
 
@@ -23,10 +24,13 @@ struct CandSink {
 
 // vmax (optional, [R][max_blocks]): the V block maxima (max combine only).
 // qpos_snap (optional, [R]): predict records the step's q_pos there; the
-// fused EMA + advance of a whole step reads it instead of q_pos.
+// fused EMA + advance of a whole step reads it instead of q_pos.  tag
+// (optional, [R][4]): requests whose scores the last EMA predicted ahead are
+// skipped (their snapshot is still recorded).
 hipError_t launch_predict(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
                           const float* D, int64_t d_ld, const float* vmax, float* S,
-                          hipStream_t st, int32_t* qpos_snap = nullptr);
+                          hipStream_t st, int32_t* qpos_snap = nullptr,
+                          const int32_t* tag = nullptr);
 // A layer's plan (one verifier row) run inside another layer's launches:
 // its prediction by the last workgroups of a score launch, its selection by
 // the last workgroups of a top-K + EMA launch.
@@ -39,18 +43,21 @@ struct SelectPlan {
   SelectInputs in;
   int requests, ept;
 };
+// tag (optional): skip the requests whose scores were predicted ahead.
 PredictPlan predict_plan(const spin_config& c, const spin_batch& b, const float* V, int64_t v_ld,
                          const float* D, int64_t d_ld, const float* vmax, float* S,
-                         int32_t* qpos_snap);
+                         int32_t* qpos_snap, const int32_t* tag = nullptr);
 // last_obs (optional, [R][max_blocks]): the step of each block's last
 // observation, read by the age / staleness exploration policies and set to
 // the step for every block of the union.
+// inv (optional, [R][max_blocks]): each block's position in sel, -1 if not
+// selected (what the predict-ahead EMA reads).
 SelectPlan select_plan(const spin_config& c, const spin_batch& b, const float* S,
                        const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                       int32_t* last_obs);
+                       int32_t* last_obs, int32_t* inv = nullptr);
 hipError_t launch_select(const spin_config& c, const spin_batch& b, const float* S,
                          const int32_t* budget, uint8_t* code, int32_t* sel, int32_t* n_sel,
-                         int32_t* last_obs, hipStream_t st);
+                         int32_t* last_obs, hipStream_t st, int32_t* inv = nullptr);
 // Block reduction A2: block scores from block-level states.
 hipError_t launch_predict_a2(const spin_config& c, const spin_batch& b, const float* V,
                              int64_t v_ld, const float* D, int64_t d_ld, float* S,
@@ -89,19 +96,22 @@ hipError_t launch_topk_ema(const spin_config& c, const spin_batch& b, const floa
                            void* ws, const int32_t* n_valid, float* V, int64_t v_ld, float* D,
                            int64_t d_ld, float* vmax, const int32_t* qpos_snap,
                            int32_t* qpos_out, int32_t* step_out, hipStream_t st,
-                           const SelectPlan* next = nullptr, bool ema = true);
+                           const SelectPlan* next = nullptr, bool ema = true,
+                           const Ahead* ahead = nullptr);
 // The candidate sink inside a top-K workspace.
 CandSink topk_sink(void* ws, int R, int rows, int max_blocks);
 size_t topk_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks);
 // A whole step's workspace: the top-K region, then the step's q_pos snapshot.
 size_t step_workspace_bytes(const spin_config& c, int R, int rows, int max_blocks);
 // With qpos_snap, q positions come from the snapshot and the kernel also
-// advances qpos_out / step_out (each optional) like launch_advance.
+// advances qpos_out / step_out (each optional) like launch_advance.  With
+// `ahead` (A1), every block's EMA update and the next step's block scores
+// (SPIN_PREDICT_AHEAD).
 hipError_t launch_ema(const spin_config& c, const spin_batch& b, const float* z, int64_t z_ld,
                       const int32_t* sel, const int32_t* n_sel, const int32_t* n_valid, float* V,
                       int64_t v_ld, float* D, int64_t d_ld, float* vmax, hipStream_t st,
                       const int32_t* qpos_snap = nullptr, int32_t* qpos_out = nullptr,
-                      int32_t* step_out = nullptr);
+                      int32_t* step_out = nullptr, const Ahead* ahead = nullptr);
 hipError_t launch_advance(int R, int rows, const int32_t* n_valid, int32_t* qpos, int32_t* step,
                           hipStream_t st);
 hipError_t launch_reset(int R, float* V, int64_t v_ld, float* D, int64_t d_ld, int64_t vmax_ld,

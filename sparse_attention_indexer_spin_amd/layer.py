@@ -18,14 +18,20 @@ class SpinLayer:
                  n_rows: int = 1, explore_bp: int = 500, ema_alpha: float = 0.9,
                  combine: str = "max", key_dtype=torch.uint8, q_dtype=torch.bfloat16,
                  layer: int = 0, seed: int = 0x5350494E, device="cuda", vmax_cache: bool = False,
-                 **variants):
+                 predict_ahead: bool = False, **variants):
         """`variants`: the design variants of api.config (pooling, mtp_row0_mask,
         mtp_row0_update, explore_per_row, explore, reduction); the paper's
-        defaults without them."""
+        defaults without them.  predict_ahead: each step's EMA update also
+        predicts the next step's block scores (SPIN_PREDICT_AHEAD; one
+        verifier row, block reduction A1), the same scores the next step's own
+        prediction would compute.  Off by default: the update then walks every
+        block instead of the selected ones, and inside the top-K launch that
+        costs about what the skipped prediction saves."""
         self.R, self.rows, self.max_blocks, self.K = batch, n_rows, max_blocks, topk
         self.cfg = api.config(topk=topk, sparsity_bp=sparsity_bp, explore_bp=explore_bp,
                               ema_alpha=ema_alpha, combine=combine, key_dtype=key_dtype,
-                              q_dtype=q_dtype, layer=layer, seed=seed, **variants)
+                              q_dtype=q_dtype, layer=layer, seed=seed,
+                              predict_ahead=predict_ahead, **variants)
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         n_cap = 64 * max_blocks
@@ -41,6 +47,9 @@ class SpinLayer:
         # the step at which each block was last scored (exploration by block
         # age / staleness), kept by every step's selection
         self.last_obs = torch.zeros(batch, max_blocks, **i32)
+        # per request: the (step, q position, context) S was predicted ahead
+        # for by the last EMA update, -1 when none
+        self.s_tag = torch.full((batch, 4), -1, **i32) if predict_ahead else None
         self.row_code = torch.zeros(batch, n_rows, max_blocks, dtype=torch.uint8, device=dev)
         self.sel = torch.full((batch, max_blocks), -1, **i32)
         self.n_sel = torch.zeros(batch, **i32)
@@ -63,6 +72,8 @@ class SpinLayer:
         self.q_pos.copy_(q_pos.to(torch.int32))
         if req_id is not None:
             self.req_id.copy_(req_id.to(torch.int32))
+        if self.s_tag is not None:
+            self.s_tag.fill_(-1)
         self._bt = None
 
     def reset(self, stream=None):
@@ -70,6 +81,8 @@ class SpinLayer:
         st = torch.cuda.current_stream() if stream is None else stream
         with torch.cuda.stream(st):
             self.last_obs.zero_()
+            if self.s_tag is not None:
+                self.s_tag.fill_(-1)
 
     def batch(self, n_pages: int):
         if self._bt is None or self.n_pages != n_pages:
@@ -85,7 +98,8 @@ class SpinLayer:
                            page_table=page_table, S=self.S, row_code=self.row_code, sel=self.sel,
                            n_sel=self.n_sel, z=self.z, topk_idx=self.topk_idx, budget=budget,
                            n_valid=n_valid, q_pos_mut=self.q_pos, step_mut=self.step_ctr,
-                           workspace=self.workspace, v_max=self.v_max, last_obs=self.last_obs)
+                           workspace=self.workspace, v_max=self.v_max, last_obs=self.last_obs,
+                           s_tag=self.s_tag)
 
     def step(self, q, w, k_pages, k_scale, page_table, n_valid=None, budget=None,
              defer_ema: bool = False, stream=None):

@@ -149,3 +149,27 @@ def test_stack_host_validation_without_gpu(lib):
     assert lib.spin_stack_step(None, 1, None, None, None, 0, 0, None, None, None) == 1
     assert lib.spin_stack_commit(None, 1, None, None, None, None) == 1
     lib.spin_stack_destroy(None)  # a no-op
+
+
+def test_predict_ahead_host_validation(lib):
+    """SPIN_PREDICT_AHEAD: block reduction A1 only, io->s_tag required, and the
+    step workspace grows by the inverse block map (4 R max_blocks bytes)."""
+    from sparse_attention_indexer_spin_amd import _lib
+    bt = _lib.SpinBatch(batch=2, n_rows=1, max_blocks=16, n_pages=32, ctx_len=1, q_pos=1,
+                        step=1, req_id=1, err=None)
+    for red in ("A0", "A2"):
+        bad = _cfg(reduction=red, predict_ahead=True)
+        assert lib.spin_select_blocks(C.byref(bad), C.byref(bt), 1, None, 1, 1, 1, 1, None) == 2
+    cfg, plain = _cfg(predict_ahead=True), _cfg()
+    ws = lib.spin_workspace_bytes(C.byref(cfg), 2, 1, 16)
+    ws0 = lib.spin_workspace_bytes(C.byref(plain), 2, 1, 16)
+    assert ws - ws0 == 256  # 4 x 2 x 16 = 128 bytes, 256-byte aligned
+    assert lib.spin_workspace_bytes(C.byref(cfg), 32, 1, 2048) - \
+        lib.spin_workspace_bytes(C.byref(plain), 32, 1, 2048) == 4 * 32 * 2048
+    # every other argument valid (host checks only): a missing tag array is refused
+    io = _lib.SpinStepIO(V=1, v_ld=1024, D=1, d_ld=4096, v_max=None, q=1, w=1, k_pages=1,
+                         k_scale=1, page_table=1, pt_ld=16, budget=None, n_valid=None, S=1,
+                         row_code=1, sel=1, n_sel=1, z=1, z_ld=1024, topk_idx=1, q_pos_mut=1,
+                         step_mut=1, workspace=1, workspace_bytes=ws, last_obs=None, s_tag=None)
+    assert lib.spin_step(C.byref(cfg), C.byref(bt), C.byref(io), 0, None) == 1
+    assert "s_tag" in lib.spin_last_error().decode()

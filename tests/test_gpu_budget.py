@@ -95,7 +95,10 @@ def test_stack_budgets_match_oracle_reference(policy, one_stream):
                                                  n_slots_min=3000, steps=11, topk=256)
     lis = [build_layer(w, layer=l) for l in range(L)]
     keys = [device_keys(li) for li in lis]
-    seq = [make_layer(li, sp) for li in lis]
+    # the reference miss curves read each step's own block scores from S, so
+    # the sequential layers do not predict ahead (the stack's probe steps do
+    # not either)
+    seq = [make_layer(li, sp, predict_ahead=False) for li in lis]
     stk = [make_layer(li, sp) for li in lis]
     stack = SpinStack(stk, budget_policy=policy, probe_period=P, levels=levels,
                       one_stream=one_stream)

@@ -41,9 +41,11 @@ def test_step_predict_select_matches_stages(rows, R, n_max, n_min, mb, bad):
                                  topk=256)
     li = build_layer(w)
     cap = mb or w.max_blocks
+    # (S after the step is the step's own prediction: without predicting ahead)
     lay = SpinLayer(batch=R, max_blocks=cap, d_cap=G.d_capacity(w, w.steps), topk=w.topk,
                     sparsity_bp=4000, n_rows=rows, explore_bp=w.explore_bp, ema_alpha=w.alpha,
-                    key_dtype=torch.uint8, q_dtype=torch.bfloat16, device=DEV)
+                    key_dtype=torch.uint8, q_dtype=torch.bfloat16, device=DEV,
+                    predict_ahead=False)
     ctx = li.ctx.clone()
     if bad is not None:
         ctx[bad] = 64 * cap + 1                   # beyond the block capacity
