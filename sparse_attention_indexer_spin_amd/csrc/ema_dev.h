@@ -105,23 +105,30 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
     // one observation per slot: V[i] and D[q - i] from row 0, CH blocks'
     // loads at a time, two chunks in flight: chunk c + 1's loads go out
     // before chunk c's stores, so a wave's writes overlap its next reads
-    // (different blocks touch disjoint V and D elements)
+    // (different blocks touch disjoint V and D elements).  The block ids
+    // come one per lane from one load per 64 blocks, and every load is
+    // unconditional (lanes without an element read element 0): a block id
+    // moved to a scalar right after its load, or loads under branches, made
+    // the compiler wait for every outstanding load, the other chunk's too.
     struct Chunk {
       float vv[CH], dd[CH], zz[CH];
       int ii[CH], jj[CH];
     };
+    int sg = k0, s1 = k1, ids = -1;
     const auto load = [&](Chunk& C, int kb) {
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
         const int k = kb + u;
-        const int j = k < k1 ? __builtin_amdgcn_readfirstlane(sr[k]) : -1;  // uniform
+        const int j = k < s1 ? __builtin_amdgcn_readlane(ids, k - sg) : -1;  // uniform
         const int i = j * 64 + lane;
-        const bool ok = k < k1 && j >= 0 && j < max_blocks && i < N;
-        C.jj[u] = k < k1 && j >= 0 && j < max_blocks ? j : -1;
+        const bool ok = k < s1 && j >= 0 && j < max_blocks && i < N;
+        C.jj[u] = k < s1 && j >= 0 && j < max_blocks ? j : -1;
         C.ii[u] = ok ? i : -1;
-        C.vv[u] = ok ? Vr[i] : 0.0f;
-        C.dd[u] = ok ? Dr[q - i] : 0.0f;
-        C.zz[u] = ok ? zb[(int64_t)k * 64 + lane] : 0.0f;
+        const float vx = Vr[ok ? i : 0], dx = Dr[ok ? q - i : 0];
+        const float zx = zb[ok ? (int64_t)k * 64 + lane : 0];
+        C.vv[u] = ok ? vx : 0.0f;
+        C.dd[u] = ok ? dx : 0.0f;
+        C.zz[u] = ok ? zx : 0.0f;
       }
     };
     const auto finish = [&](const Chunk& C) {
@@ -137,14 +144,22 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
         if (A.vmax && C.jj[u] >= 0) ema_vmax(A, r, C.jj[u], C.ii[u] >= 0, vn);
       }
     };
-    Chunk c0, c1;
-    load(c0, k0);
-    for (int kb = k0; kb < k1; kb += 2 * CH) {
-      if (kb + CH < k1) load(c1, kb + CH);
-      finish(c0);
-      if (kb + CH >= k1) break;
-      if (kb + 2 * CH < k1) load(c0, kb + 2 * CH);
-      finish(c1);
+    for (; sg < k1; sg += 64) {
+      s1 = min(k1, sg + 64);
+      {
+        const int kk = sg + lane;
+        const int idx = sr[kk < s1 ? kk : sg];
+        ids = kk < s1 ? idx : -1;
+      }
+      Chunk c0, c1;
+      load(c0, sg);
+      for (int kb = sg; kb < s1; kb += 2 * CH) {
+        if (kb + CH < s1) load(c1, kb + CH);
+        finish(c0);
+        if (kb + CH >= s1) break;
+        if (kb + 2 * CH < s1) load(c0, kb + 2 * CH);
+        finish(c1);
+      }
     }
     return;
   }
