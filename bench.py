@@ -9,11 +9,14 @@ each launched through the C ABI on the current stream, inputs resident in HBM.
 
 Prints one JSON line.  `value` = indexer keys scored per second of whole-step
 time (one spin_step call per step).  By default (`--cache rotate`) the bench
-steps 4 independent copies of the workload (own key pages, EMA state and
+steps 8 independent copies of the workload (own key pages, EMA state and
 buffers; the same data) round robin back to back, as the layers of a model
-run: when a copy steps again, the other copies have streamed 3 x its pages
-(~1 GB) through the L2s and the 256 MB MALL, so its pages come from HBM, and
-no host sync or event sits between steps.  The two other protocols are
+run: when a copy steps again, the other copies have streamed 7 x its pages
+(~2.4 GB) and 7 x its ~51 MB of EMA state and step buffers through the L2s and
+the 256 MB MALL, so its pages and its state come from HBM, and no host sync or
+event sits between steps.  (The page loads are non-temporal; with 4 copies
+the state of all copies, ~205 MB, stays in the MALL, which a model with tens
+of layers does not allow.)  The two other protocols are
 reported beside it: `cold` times each step alone after a 1 GiB read (adds the
 event and launch latency of an isolated step), `warm` steps one copy back to
 back (the MALL keeps part of the previous step's pages).  `roofline` is the
@@ -22,7 +25,7 @@ score kernel's algorithmic HBM bytes per launch / its mean launch duration
 the step's stream, on the last timed step's selection) against 8 TB/s, with
 `traffic` taken from the committed FETCH_SIZE/WRITE_SIZE summary when it was
 measured on the current kernel source.  `cpu_baseline` times the CPU oracle
-on whole requests of the same workload for about 15 s.
+on whole requests of the same workload for about 10 s.
 """
 from __future__ import annotations
 
@@ -63,7 +66,9 @@ def parse():
                          "back to back (each step's pages were evicted by the others, as between "
                          "the layers of a model); cold: a 1 GiB read before every timed step and "
                          "stage launch, each timed alone; warm: one copy back to back")
-    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--copies", type=int, default=8,
+                    help="rotate: copies of the workload; at 8 the other copies' EMA state and "
+                         "buffers (~360 MB) also evict a copy's own from the 256 MB MALL")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-max-requests", type=int, default=32)
@@ -398,7 +403,7 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
     """`copies` independent copies of the workload -- own key pages (same data),
     EMA state and buffers -- stepped round robin back to back, as the layers of
     a model run: by the time a copy steps again, the others have streamed
-    (copies - 1) x its pages through the L2s and the 256 MB MALL, and no host
+    (copies - 1) x its pages and state through the L2s and the 256 MB MALL, and no host
     sync or event sits between two steps.  Per-step time = total / (steps x
     copies).  Stage timing likewise: each stage launched round robin over the
     copies, reps x copies launches between two events."""

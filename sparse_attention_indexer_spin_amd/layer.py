@@ -17,7 +17,8 @@ class SpinLayer:
     def __init__(self, *, batch: int, max_blocks: int, d_cap: int, topk: int, sparsity_bp: int,
                  n_rows: int = 1, explore_bp: int = 500, ema_alpha: float = 0.9,
                  combine: str = "max", key_dtype=torch.uint8, q_dtype=torch.bfloat16,
-                 layer: int = 0, seed: int = 0x5350494E, device="cuda", vmax_cache: bool = False,
+                 layer: int = 0, seed: int = 0x5350494E, device="cuda",
+                 vmax_cache: Optional[bool] = None,
                  predict_ahead: bool = False, **variants):
         """`variants`: the design variants of api.config (pooling, mtp_row0_mask,
         mtp_row0_update, explore_per_row, explore, reduction); the paper's
@@ -38,9 +39,13 @@ class SpinLayer:
         self.V = torch.zeros(batch, n_cap, dtype=torch.float32, device=dev)
         self.D = torch.zeros(batch, d_cap, dtype=torch.float32, device=dev)
         # optional block maxima of V: predict then reads one float per block
-        # instead of 64 (max combine), kept by reset, the EMA update and every
-        # step.  Off by default: the predict kernel is latency-bound, so the
-        # bytes it saves buy less than the upkeep costs the EMA update.
+        # instead of 64, kept by reset, the EMA update and every step.  By
+        # default on where it applies (max combine, max pooling, block
+        # reduction A1): with the state in HBM, halving the prediction's bytes
+        # saves more than the upkeep costs the EMA update.
+        if vmax_cache is None:
+            vmax_cache = (combine == "max" and variants.get("pooling", "max") == "max"
+                          and variants.get("reduction", "A1") == "A1")
         self.v_max = torch.zeros(batch, max_blocks, dtype=torch.float32, device=dev) \
             if vmax_cache else None
         self.S = torch.zeros(batch, n_rows, max_blocks, dtype=torch.float32, device=dev)
