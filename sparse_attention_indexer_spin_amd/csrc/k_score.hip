@@ -532,10 +532,9 @@ struct QFull<0, NS> {  // fp8 keys: NS E4M3 terms per query value
       for (int i = 0; i < 4; ++i) wq[t][i] = ws[64 * slot + 16 * t + 4 * g + i];
   }
 
-  // this lane's ReLU-weighted sum over its 16 heads for the 16 slots whose
-  // key bytes are in kf (MFMA B operand)
-  __device__ __forceinline__ float dot(const v8i& kf) const {
-    v4f acc[4];
+  // the 16 heads x 16 slots of each head tile for the slots whose key bytes
+  // are in kf (MFMA B operand): NS terms accumulated per tile
+  __device__ __forceinline__ void mma(const v8i& kf, v4f (&acc)[4]) const {
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -544,12 +543,29 @@ struct QFull<0, NS> {  // fp8 keys: NS E4M3 terms per query value
       for (int t = 0; t < 4; ++t)
         acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(part[sp][t], kf, acc[t], 0, 0, 0,
                                                                   127, 0, 127);
+  }
+  // One term of head tile t of staged row `slot`, as from_lds() reads it.
+  __device__ static __forceinline__ v8i lds_part(const unsigned char* lds, int slot, int sp,
+                                                 int t) {
+    const int lane = threadIdx.x & 63;
+    const v4u* qs = reinterpret_cast<const v4u*>(lds + slot * kStageBytes);
+    const v4u a = qs[((sp * 4 + t) * 2 + 0) * 64 + lane], b = qs[((sp * 4 + t) * 2 + 1) * 64 + lane];
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  }
+
+  // this lane's ReLU-weighted sum over its 16 heads of those tiles
+  __device__ __forceinline__ float epi(const v4f (&acc)[4]) const {
     float s = 0.0f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) s = fmaf(wq[t][i], relu(acc[t][i]), s);
     return s;
+  }
+  __device__ __forceinline__ float dot(const v8i& kf) const {
+    v4f acc[4];
+    mma(kf, acc);
+    return epi(acc);
   }
 };
 
@@ -712,9 +728,40 @@ struct PageRegs<0> {
   template <bool WL, class Q>
   __device__ static __forceinline__ float tile(const Q& q, v4u (&b)[8], int st) {
     if constexpr (WL) swap_pair(b[2 * st], b[2 * st + 1]);
+    return q.dot(operand(b, st));
+  }
+  __device__ static __forceinline__ v8i operand(const v4u (&b)[8], int st) {
     const v4u a = b[2 * st], c = b[2 * st + 1];
-    return q.dot(v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z,
-                     (int)c.w});
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
+  }
+  // The page's 4 sub-tiles with several rows (half-line layout), software
+  // pipelined: sub-tile st + 1's MFMAs go out before sub-tile st's epilogue,
+  // whose accumulators are then complete, so the epilogue's VALU work runs
+  // beside matrix-core work instead of waiting for it.
+  template <class Q>
+  __device__ static __forceinline__ void tiles(const Q& q, const v4u (&b)[8], float (&part)[4]) {
+    v4f a0[4], a1[4], a2[4], a3[4];
+    q.mma(operand(b, 0), a0);
+    q.mma(operand(b, 1), a1);
+    __builtin_amdgcn_sched_barrier(0);
+    part[0] = q.epi(a0);
+    q.mma(operand(b, 2), a2);
+    interleave();
+    part[1] = q.epi(a1);
+    q.mma(operand(b, 3), a3);
+    interleave();
+    part[2] = q.epi(a2);
+    part[3] = q.epi(a3);
+  }
+  // the scheduling region so far: its 2 NS x 4 MFMAs each followed by 4 VALU
+  // instructions (the other sub-tile's epilogue), then a hard boundary
+  __device__ static __forceinline__ void interleave() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 };
 
@@ -925,8 +972,12 @@ __device__ __forceinline__ void page_loop(const ScoreParams& p, Cur& db, Cur& dd
         hint = hint_use(hint_fetch(p, rowid));
       }
       float part[4];
+      if constexpr (KT == 0 && !WL) {
+        PR::tiles(Q, kb[u], part);
+      } else {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) part[st] = PR::template tile<WL>(Q, kb[u], st);
+        for (int st = 0; st < 4; ++st) part[st] = PR::template tile<WL>(Q, kb[u], st);
+      }
       if constexpr (WL && !Span) {
         float zv;
         emit_page(p, part, KT == 0 ? sc[u] : 1.0f, d, rowid, hint, bad, rs, &zv);
@@ -1055,6 +1106,171 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Several verifier rows, fp8 keys, at most 64 requests: every wave is a stream
+// of its own and scores each page of its run for all ROWS rows, so a page is
+// loaded once instead of once per row (half-line loads in the MFMA layout: no
+// lane swap, and the kernel is bound by the matrix cores and the VALU, not by
+// HBM).  The workgroup stages every row's converted query in LDS; the wave
+// walks (row, head tile) steps, each the NS x 4 MFMAs of one head tile over
+// the page's 4 sub-tiles, reading that tile's query terms and head weights
+// from LDS one step ahead.  A step's MFMAs run beside the previous step's
+// epilogue (ReLU and weighted head sum, accumulated per sub-tile in the same
+// order as QFull::epi), whose accumulators are complete by then, so the
+// matrix cores and the VALU work side by side.  Per accumulator the MFMA
+// order (term 0, then 1, ...) and per slot the epilogue order (head tile,
+// then head) are those of k_score_wave: the scores are the same bits.
+// ---------------------------------------------------------------------------
+// Waves per workgroup.  Two query terms: 12, with the 4 rows' staged queries
+// (64 KB of LDS) one workgroup per CU and three waves per SIMD (at most 168
+// registers), which hide more of each other's stalls than two.  Three terms
+// (fp32 queries) do not fit 168 registers: 8 waves, two per SIMD.
+template <int NS>
+constexpr int rows_waves() { return NS == 2 ? 12 : 8; }
+
+template <int NS, int ROWS>
+struct RowsPage {
+  const unsigned char* lds;
+  const float* ws;
+  v8i qa[2][NS];  // query terms of a step (double-buffered)
+  v4f wv[2];      // its head weights (4 per lane)
+  v4f acc[2][4];  // per sub-tile accumulators of a step (double-buffered)
+  float s[4];     // the current row's partial sums per sub-tile
+
+  __device__ __forceinline__ void fetch(int k, int b) {
+    const int r = k >> 2, t = k & 3, g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) qa[b][sp] = QFull<0, NS>::lds_part(lds, r, sp, t);
+    wv[b] = *reinterpret_cast<const v4f*>(ws + 64 * r + 16 * t + 4 * g);
+  }
+  __device__ __forceinline__ void mma(const v8i (&kf)[4], int b) {
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp)
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        acc[b][st] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            qa[b][sp], kf[st], sp == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : acc[b][st], 0, 0, 0, 127,
+            0, 127);
+  }
+  __device__ __forceinline__ void epi(int k, int b) {
+    const bool first = (k & 3) == 0;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      float v = first ? 0.0f : s[st];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v = fmaf(wv[b][i], relu(acc[b][st][i]), v);
+      s[st] = v;
+    }
+  }
+};
+
+template <int NS, int ROWS>
+__device__ __forceinline__ void score_rows_page(const ScoreParams& p, const v8i (&kf)[4], float sc,
+                                                const Desc& d, int req, RowsPage<NS, ROWS>& R,
+                                                const uint32_t (&hint)[ROWS], int& bad,
+                                                CandRun (&rs)[ROWS]) {
+  constexpr int S = ROWS * 4;  // steps: (row, head tile)
+  R.fetch(0, 0);
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const int b = k & 1;
+    R.mma(kf, b);
+    if (k > 0) R.epi(k - 1, b ^ 1);
+    // (after the epilogue in program order: it reads the buffer's weights)
+    if (k + 1 < S) R.fetch(k + 1, b ^ 1);
+    // each of the step's 4 NS MFMAs followed by a share of the epilogue's 32
+    // VALU instructions
+#pragma unroll
+    for (int i = 0; i < 4 * NS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, (32 + 4 * NS - 1) / (4 * NS), 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (k > 0 && ((k - 1) & 3) == 3) {  // row (k - 1) / 4 complete
+      const int r = (k - 1) >> 2;
+      emit_page(p, R.s, sc, d, req * ROWS + r, hint[r], bad, rs[r]);
+    }
+  }
+  R.epi(S - 1, (S - 1) & 1);
+  emit_page(p, R.s, sc, d, req * ROWS + ROWS - 1, hint[ROWS - 1], bad, rs[ROWS - 1]);
+}
+
+
+template <int NS, int QB, int ROWS>
+__global__ __launch_bounds__(64 * rows_waves<NS>()) void k_score_rows(ScoreParams p) {
+  constexpr int P = 2;  // pages in flight per wave
+  extern __shared__ int pre_dyn[];
+  const int gx = (int)gridDim.x - p.plan_wgs;  // scoring workgroups
+  if ((int)blockIdx.x >= gx) {  // the plan role: no barrier, no LDS
+    if (threadIdx.x < 256) predict_wg(p.plan, (int)blockIdx.x - gx);
+    return;
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const Run run = wave_run(p, blockIdx.x, gx);
+  if (run.lo >= run.hi) return;  // the whole workgroup: no barrier follows
+  const int nb = run.hi - run.lo;
+  constexpr int W = rows_waves<NS>();
+  const int lo = __builtin_amdgcn_readfirstlane(run.lo + wave * nb / W);
+  const int hi = __builtin_amdgcn_readfirstlane(run.lo + (wave + 1) * nb / W);
+  const bool active = __builtin_amdgcn_readfirstlane(lo < hi ? 1 : 0) != 0;
+  unsigned char* lds = reinterpret_cast<unsigned char*>(pre_dyn);
+  __shared__ __align__(16) float wstage[SPIN_MAX_ROWS * 64];  // head weights of each row
+  uint32_t hraw[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) hraw[r] = hint_fetch(p, run.r * ROWS + r);
+  // wave w < 4 stages head tile w of every row (as k_score_wave)
+  QFull<0, NS> S;
+  const bool stager = wave < 4;
+  if (stager)
+#pragma unroll
+    for (int k = 0; k < ROWS; ++k) S.stage_fetch(p, QB, run.r * ROWS + k, wave, k);
+  RunCursor db, dd;
+  v4u kb[P][8];
+  float sc[P];
+  if (active) {
+    db.r = run.r;
+    db.N = run.N;
+    db.hi = hi;
+    db.init(p, lo);  // its wait completes the query loads too
+    dd = db;
+    first_pages<0, P, false>(p, dd, kb, sc, lo, hi);
+    if (stager)
+#pragma unroll
+      for (int k = 0; k < ROWS; ++k) S.stage_put(QB, wave, k, lds, wstage, k);
+  } else if (stager) {
+#pragma unroll
+    for (int k = 0; k < ROWS; ++k) S.stage_put(QB, wave, k, lds, wstage, k);
+  }
+  __syncthreads();
+  if (!active) return;
+  uint32_t hint[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) hint[r] = hint_use(hraw[r]);
+  RowsPage<NS, ROWS> R;
+  R.lds = lds;
+  R.ws = wstage;
+  int bad = 0;
+  CandRun rs[ROWS];
+  for (int it = lo; it < hi; it += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int cur = it + u;
+      if (cur >= hi) break;
+      // refill: page cur + P - 1 (past the end an idle load of the last page)
+      PageRegs<0>::load<false>(p, dd.get(p, min(cur + P - 1, hi - 1)).page,
+                               kb[(u + P - 1) % P], sc[(u + P - 1) % P], cur + P - 1 >= hi);
+      const Desc d = db.get(p, cur);
+      v8i kf[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) kf[st] = PageRegs<0>::operand(kb[u], st);
+      score_rows_page<NS, ROWS>(p, kf, sc[u], d, run.r, R, hint, bad, rs);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) run_flush(p, rs[r]);
+  if (bad && lane == 0) raise_error(p.err, SPIN_DERR_PAGE);
+}
+
+// ---------------------------------------------------------------------------
 // fp32 keys and queries: one thread per slot, fp32 FMA accumulation over the
 // 128 dims, then the ReLU-weighted head sum.  Query and weights in LDS.
 // ---------------------------------------------------------------------------
@@ -1125,10 +1341,34 @@ static void launch_wave_l(const ScoreParams& p, hipStream_t st) {
   hipLaunchKernelGGL(span, dim3(g2 + p.plan_wgs), dim3(256), dyn, st, p);
 }
 
+// k_score_rows for fp8 keys with several rows and at most 64 requests, when
+// its workgroups fit; false otherwise.
+template <int NS, int QB, int ROWS>
+static bool launch_rows_n(const ScoreParams& p, hipStream_t st) {
+  const size_t stage = (size_t)ROWS * QFull<0, NS>::kStageBytes;
+  const auto k = k_score_rows<NS, QB, ROWS>;
+  const int g = min(resident_workgroups((const void*)k, 64 * rows_waves<NS>(), stage),
+                    p.R * p.max_blocks);
+  if (g < p.R || !lds_fits((const void*)k, stage)) return false;
+  hipLaunchKernelGGL(k, dim3(g + p.plan_wgs), dim3(64 * rows_waves<NS>()), stage, st, p);
+  return true;
+}
+
 template <int KT, int NS, int QB>
 static void launch_wave(const ScoreParams& p, hipStream_t st) {
-  if (p.rows == 1) launch_wave_l<KT, NS, QB, true>(p, st);
-  else launch_wave_l<KT, NS, QB, false>(p, st);
+  if (p.rows == 1) {
+    launch_wave_l<KT, NS, QB, true>(p, st);
+    return;
+  }
+  if constexpr (KT == 0) {
+    if (p.R <= 64) {
+      const bool done = p.rows == 2 ? launch_rows_n<NS, QB, 2>(p, st)
+                        : p.rows == 3 ? launch_rows_n<NS, QB, 3>(p, st)
+                                      : launch_rows_n<NS, QB, 4>(p, st);
+      if (done) return;
+    }
+  }
+  launch_wave_l<KT, NS, QB, false>(p, st);
 }
 
 bool score_filters(const spin_config& c, const spin_batch&) {

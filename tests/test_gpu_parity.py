@@ -199,7 +199,7 @@ def _small(key, q, rows=1, integer=False, N=(4096 + 200, 3000)):
 @pytest.mark.parametrize("key,q", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "bf16"),
                                    ("fp8", "f32")])
 @pytest.mark.parametrize("integer", [False, True])
-@pytest.mark.parametrize("rows", [1, 4])
+@pytest.mark.parametrize("rows", [1, 2, 3, 4])
 def test_score_parity(key, q, integer, rows):
     banner(f"score key={key} q={q} integer={integer} rows={rows}")
     A = api()
@@ -254,43 +254,77 @@ def test_score_parity(key, q, integer, rows):
     assert int(keep["err"].item()) == 0
 
 
-def test_score_parity_more_requests_than_waves():
+@pytest.mark.parametrize("rows", [1, 3])
+def test_score_parity_more_requests_than_waves(rows):
     """3,000 short requests: more requests than the fp8 kernel has waves, so a
-    wave's range crosses requests and the query is reloaded inside the loop."""
-    banner("score: more requests than waves")
+    wave's range crosses requests and the query is reloaded inside the loop
+    (with several rows, the per-row-wave kernel's path for many requests)."""
+    banner(f"score: more requests than waves, rows={rows}")
     A = api()
-    li = _small("fp8", "bf16", N=tuple(64 + (r * 37) % 200 for r in range(3000)))
+    li = _small("fp8", "bf16", rows=rows, N=tuple(64 + (r * 37) % 200 for r in range(3000)))
     w = li.w
     R, mb = w.batch, w.max_blocks
     sel, n_sel = G.make_selection(R, torch.tensor([O.n_blocks(int(c)) for c in li.ctx]), mb,
                                   0.5, seed=7)
     pages, scale, pt = device_keys(li)
-    bt, keep = _batch(li.ctx.numpy(), li.pos[0].numpy(), [1] * R, 1, mb, n_pages=pages.shape[0])
+    bt, keep = _batch(li.ctx.numpy(), li.pos[0].numpy(), [1] * R, rows, mb,
+                      n_pages=pages.shape[0])
     cfg = A.config(topk=512, sparsity_bp=4000, key_dtype=pages.dtype, q_dtype=torch.bfloat16)
-    z = torch.full((R, 1, 64 * mb), -3.0, device=DEV)
+    z = torch.full((R, rows, 64 * mb), -3.0, device=DEV)
     A.spin_sparse_index_score(cfg, bt, li.q[1].to(DEV).contiguous(), li.weights.to(DEV), pages,
                               scale, pt, sel.to(DEV), n_sel.to(DEV), z)
     z = z.cpu().numpy()
     np_pages, np_scale = li.np_pages(), li.keys.scale.numpy()
     q_all = li.np_q(1)
-    for r in range(R):
+    for r in range(0, R, 7 if rows > 1 else 1):
         N = int(li.ctx[r])
         blocks = sel[r, :int(n_sel[r])].numpy()
         slots = O.union_slots(blocks, N)
         keys = O.gather_keys(np_pages, li.keys.page_table[r].numpy(), slots, "fp8", np_scale)
-        qd = O.decode_q(q_all[r], "bf16")[0]
-        want = O.index_scores(qd, li.weights[r, 0].numpy(), keys)
         comp = np.searchsorted(blocks, slots // 64) * 64 + slots % 64
-        ok, worst = z_close(z[r, 0, comp], want, TOL["fp8"])
-        assert ok, (r, worst)
         phys = li.keys.page_table[r].numpy()[slots // 64]
         unscaled = O.gather_keys(np_pages, li.keys.page_table[r].numpy(), slots, "fp8",
                                  np.ones_like(np_scale))
-        b = score_bound(qd, li.weights[r, 0].numpy(), unscaled,
-                        np_scale[phys, slots % 64].astype(np.float64), "fp8", "bf16")
-        ok, worst = check_bound(z[r, 0, comp], want, b)
-        assert ok, ("bound", r, worst)
+        for row in range(rows):
+            qd = O.decode_q(q_all[r], "bf16")[row]
+            want = O.index_scores(qd, li.weights[r, row].numpy(), keys)
+            ok, worst = z_close(z[r, row, comp], want, TOL["fp8"])
+            assert ok, (r, row, worst)
+            b = score_bound(qd, li.weights[r, row].numpy(), unscaled,
+                            np_scale[phys, slots % 64].astype(np.float64), "fp8", "bf16")
+            ok, worst = check_bound(z[r, row, comp], want, b)
+            assert ok, ("bound", r, row, worst)
     assert int(keep["err"].item()) == 0
+
+
+@pytest.mark.parametrize("rows", [2, 4])
+def test_score_rows_kernels_agree(rows):
+    """Several verifier rows: the kernel that scores a page for all rows in one
+    wave (at most 64 requests) and the one with a wave per row (used past 64
+    requests) make the same arithmetic in the same order, so the first 40
+    requests of a 70-request batch score the same bits either way."""
+    banner(f"score: all-rows and per-row-wave kernels agree, rows={rows}")
+    A = api()
+    li = _small("fp8", "bf16", rows=rows, N=tuple(700 + (r * 997) % 9000 for r in range(70)))
+    w = li.w
+    R, mb = w.batch, w.max_blocks
+    sel, n_sel = G.make_selection(R, torch.tensor([O.n_blocks(int(c)) for c in li.ctx]), mb,
+                                  0.5, seed=11)
+    pages, scale, pt = device_keys(li)
+    q, wts = li.q[1].to(DEV).contiguous(), li.weights.to(DEV)
+    cfg = A.config(topk=512, sparsity_bp=4000, key_dtype=pages.dtype, q_dtype=torch.bfloat16)
+    zs = []
+    for n in (R, 40):
+        bt, keep = _batch(li.ctx.numpy()[:n], li.pos[0].numpy()[:n], [1] * n, rows, mb,
+                          n_pages=pages.shape[0])
+        z = torch.full((n, rows, 64 * mb), -3.0, device=DEV)
+        A.spin_sparse_index_score(cfg, bt, q[:n].contiguous(), wts[:n].contiguous(), pages, scale,
+                                  pt[:n].contiguous(), sel[:n].to(DEV).contiguous(),
+                                  n_sel[:n].to(DEV).contiguous(), z)
+        torch.cuda.synchronize()
+        assert int(keep["err"].item()) == 0
+        zs.append(z[:40].cpu())
+    assert torch.equal(zs[0], zs[1])
 
 
 # ---------------------------------------------------------------------------
