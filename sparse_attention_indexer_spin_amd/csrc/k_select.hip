@@ -39,6 +39,37 @@ __device__ __forceinline__ void predict_wave_rows(int combine, int pooling, int 
     vv[b] = ok && !cached ? Vr[i] : -INFINITY;
     dd[b] = ok ? Dr[q0 - i] : 0.0f;
   }
+  if (pooling == SPIN_POOL_MAX) {
+    // every (row, block) maximum at once: a reduce-scatter over the wave
+    // instead of ROWS x 8 wave reductions (the kernel is bound by VALU issue)
+    constexpr int NV = ROWS * kPredBlocksPerWave <= 16 ? 16 : 32;
+    constexpr int SH = NV == 16 ? 2 : 1;  // lane l holds value l >> SH
+    float x[NV];
+#pragma unroll
+    for (int b = 0; b < kPredBlocksPerWave; ++b) {
+      const int i = (j0 + b) * SPIN_BLOCK + lane;
+      const float before = b == 0 ? dprev : dd[b > 0 ? b - 1 : 0];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        float d = dd[b];
+        if (r > 0) {
+          const int src = (lane - r) & 63;
+          const float xs = __shfl(dd[b], src), ys = __shfl(before, src);
+          d = lane >= r ? xs : ys;
+        }
+        const float zhat = combine == SPIN_COMBINE_SUM ? __fadd_rn(vv[b], d) : fmaxf(vv[b], d);
+        x[r * kPredBlocksPerWave + b] = i < N ? zhat : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int k = ROWS * kPredBlocksPerWave; k < NV; ++k) x[k] = -INFINITY;
+    float m = wave_max_scatter<NV>(x);
+    const int idx = lane >> SH, r = idx / kPredBlocksPerWave, j = j0 + idx % kPredBlocksPerWave;
+    if (vmax_r && j < B - 1) m = fmaxf(m, vmax_r[j]);
+    if ((lane & ((1 << SH) - 1)) == 0 && r < ROWS && j < B)
+      S0[(int64_t)r * max_blocks + j] = m + 0.0f;
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < kPredBlocksPerWave; ++b) {
     const int j = j0 + b;

@@ -84,6 +84,23 @@ __device__ __forceinline__ void predict_reduce(int combine, int pooling, int N, 
                                                const float (&vv)[NB], const float (&dd)[NB],
                                                float vm, float* __restrict__ Srow) {
   const int lane = threadIdx.x & 63;
+  if (pooling == SPIN_POOL_MAX && (NB & (NB - 1)) == 0) {
+    // all NB block maxima at once (wave_max_scatter), lane l holding block
+    // j0 + (l >> (6 - log2 NB)); its V max comes from the lane that loaded it
+    constexpr int LG = NB == 1 ? 0 : NB == 2 ? 1 : NB == 4 ? 2 : NB == 8 ? 3 : NB == 16 ? 4 : 5;
+    float x[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int i = (j0 + b) * SPIN_BLOCK + lane;
+      const float zhat =
+          combine == SPIN_COMBINE_SUM ? __fadd_rn(vv[b], dd[b]) : fmaxf(vv[b], dd[b]);
+      x[b] = i < N ? zhat : -INFINITY;
+    }
+    const int b = lane >> (6 - LG), j = j0 + b;
+    const float m = fmaxf(wave_max_scatter<NB>(x), __shfl(vm, b, 64));
+    if ((lane & ((1 << (6 - LG)) - 1)) == 0 && j < B) Srow[j] = m + 0.0f;
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int j = j0 + b;
@@ -99,15 +116,17 @@ __device__ __forceinline__ void predict_reduce(int combine, int pooling, int N, 
   }
 }
 
-// One wave's 8 blocks j0 .. j0+7 (j0 < B) of one (request, row).
+// One wave's NB blocks j0 .. j0 + NB - 1 (j0 < B) of one (request, row),
+// every load in flight before the reductions.
+template <int NB = kPredBlocksPerWave>
 __device__ __forceinline__ void predict_wave(int combine, int pooling, int N, int B, int q,
                                              int j0, const float* __restrict__ Vr,
                                              const float* __restrict__ Dr,
                                              const float* __restrict__ vmax_r,
                                              float* __restrict__ Srow) {
-  float vv[kPredBlocksPerWave], dd[kPredBlocksPerWave], vm;
-  predict_load<kPredBlocksPerWave>(N, B, q, j0, Vr, Dr, vmax_r, vv, dd, vm);
-  predict_reduce<kPredBlocksPerWave>(combine, pooling, N, B, j0, vv, dd, vm, Srow);
+  float vv[NB], dd[NB], vm;
+  predict_load<NB>(N, B, q, j0, Vr, Dr, vmax_r, vv, dd, vm);
+  predict_reduce<NB>(combine, pooling, N, B, j0, vv, dd, vm, Srow);
 }
 
 // ---------------------------------------------------------------------------
@@ -251,11 +270,16 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int r, int row, 
 // top-K + EMA launch), one verifier row.
 // ---------------------------------------------------------------------------
 // Prediction: workgroup w of n covers request w / per_req, blocks
-// [32 kPredGroups (w % per_req), + 32 kPredGroups): 4 waves x kPredGroups
-// groups of 8 blocks.  One group per workgroup (as k_predict) beat 2 and 4:
-// the many small workgroups fill the CUs the scoring workgroups leave.
-constexpr int kPredGroups = 1;
-constexpr int kPredBlocksPerWg = 4 * kPredGroups * kPredBlocksPerWave;
+// [64 (w % per_req), + 64): 16 per wave.  These workgroups run as the scoring
+// workgroups leave their CUs, two per CU (the kernel's registers), so the
+// tail is bound by how fast a workgroup turns its loads into block scores:
+// with one wave reduction per block most of it went into the reductions
+// (workgroup timestamps: ~10 us of tail after the last scoring workgroup);
+// the reduce-scatter over all of a wave's blocks (wave_max_scatter) took the
+// one-stream stack from 93.3 to 89.5 us per layer-step, and 16 blocks per
+// wave instead of 8 another ~0.6 us (32: no further gain).
+constexpr int kTailPredBlocksPerWave = 16;
+constexpr int kPredBlocksPerWg = 4 * kTailPredBlocksPerWave;
 
 struct PredictArgs {
   int combine, pooling, max_blocks, per_req;  // per_req: workgroups per request
@@ -294,14 +318,12 @@ __device__ __forceinline__ void predict_wg(const PredictArgs& a, int w) {
   if (predicted_ahead(a.tag, a.step, r, q0, N)) return;
   const int B = (N + SPIN_BLOCK - 1) / SPIN_BLOCK;
   const int wave = threadIdx.x >> 6;
-  for (int g = 0; g < kPredGroups; ++g) {
-    const int j0 = ((bx * kPredGroups + g) * 4 + wave) * kPredBlocksPerWave;
-    if (j0 >= B) return;
-    predict_wave(a.combine, a.pooling, N, B, q0, j0, a.V + (int64_t)r * a.v_ld,
-                 a.D + (int64_t)r * a.d_ld,
-                 a.vmax ? a.vmax + (int64_t)r * a.max_blocks : nullptr,
-                 a.S + (int64_t)r * a.max_blocks);
-  }
+  const int j0 = (bx * 4 + wave) * kTailPredBlocksPerWave;
+  if (j0 >= B) return;
+  predict_wave<kTailPredBlocksPerWave>(a.combine, a.pooling, N, B, q0, j0,
+                                       a.V + (int64_t)r * a.v_ld, a.D + (int64_t)r * a.d_ld,
+                                       a.vmax ? a.vmax + (int64_t)r * a.max_blocks : nullptr,
+                                       a.S + (int64_t)r * a.max_blocks);
 }
 
 // Selection of request r (one row, compacted): the whole workgroup of

@@ -96,6 +96,74 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   });
   return __int_as_float(__builtin_amdgcn_readlane(s, 63));
 }
+// Maxima of NB values per lane over all 64 lanes at once (NB a power of two,
+// at most 32), a reduce-scatter: lane l returns the max of value
+// l >> (6 - log2 NB) over the wave.  Each step halves the values a lane holds:
+// for lane bits 5 and 4 one permlane swap exchanges the halves of a pair of
+// registers between partner lanes, so the lanes with the bit clear keep value
+// k and the others value k + h, with no selects; for lane bits 3 .. 0 a DPP
+// move brings the partner's value.  Lane bits left once one value remains
+// are plain butterfly steps.  The max of a set does not depend on the order
+// it is taken in.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// value of lane l ^ 2^b for b < 4 (within a row of 16 lanes)
+template <int B>
+__device__ __forceinline__ float xor_lane_low(float v) {
+  if constexpr (B == 3) return dpp_f<0x128>(v);  // row_ror:8
+  if constexpr (B == 2) {
+    const bool up = (threadIdx.x >> 2) & 1;
+    const float dn = dpp_f<0x104>(v), upv = dpp_f<0x114>(v);  // row_shl:4, row_shr:4
+    return up ? upv : dn;
+  }
+  if constexpr (B == 1) return dpp_f<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+  return dpp_f<0xB1>(v);                        // quad_perm [1, 0, 3, 2]
+}
+template <int NB, int B>
+__device__ __forceinline__ void scatter_step(float (&x)[NB], int h) {
+  if constexpr (B >= 4) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k >= h) break;
+      const auto s = B == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x[k]),
+                                                               __float_as_uint(x[k + h]), false,
+                                                               false)
+                            : __builtin_amdgcn_permlane16_swap(__float_as_uint(x[k]),
+                                                               __float_as_uint(x[k + h]), false,
+                                                               false);
+      x[k] = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+    }
+  } else {
+    const bool up = (threadIdx.x >> B) & 1;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k >= h) break;
+      const float keep = up ? x[k + h] : x[k], send = up ? x[k] : x[k + h];
+      x[k] = fmaxf(keep, xor_lane_low<B>(send));
+    }
+  }
+}
+template <int NB>
+__device__ __forceinline__ float wave_max_scatter(float (&x)[NB]) {
+  static_assert(NB >= 1 && NB <= 32 && (NB & (NB - 1)) == 0, "a power of two up to 32");
+  constexpr int LG = NB == 1 ? 0 : NB == 2 ? 1 : NB == 4 ? 2 : NB == 8 ? 3 : NB == 16 ? 4 : 5;
+  if constexpr (LG >= 1) scatter_step<NB, 5>(x, NB / 2);
+  if constexpr (LG >= 2) scatter_step<NB, 4>(x, NB / 4);
+  if constexpr (LG >= 3) scatter_step<NB, 3>(x, NB / 8);
+  if constexpr (LG >= 4) scatter_step<NB, 2>(x, NB / 16);
+  if constexpr (LG >= 5) scatter_step<NB, 1>(x, NB / 32);
+  float m = x[0];
+  if constexpr (LG < 1) m = fmaxf(m, __shfl_xor(m, 32, 64));
+  if constexpr (LG < 2) m = fmaxf(m, __shfl_xor(m, 16, 64));
+  if constexpr (LG < 3) m = fmaxf(m, xor_lane_low<3>(m));
+  if constexpr (LG < 4) m = fmaxf(m, xor_lane_low<2>(m));
+  if constexpr (LG < 5) m = fmaxf(m, xor_lane_low<1>(m));
+  m = fmaxf(m, xor_lane_low<0>(m));
+  return m;
+}
+
 __device__ __forceinline__ int wave_sum_i32(int v) {
   return __builtin_amdgcn_readlane(dpp_incl_scan(v, 0, [](int a, int b) { return a + b; }), 63);
 }
