@@ -134,8 +134,10 @@ class Evictor:
 
 def _timed_us(fn, reps: int, stream, evict=None) -> float:
     """Mean duration of `fn` over `reps` launches (HIP events on `stream`):
-    back to back, or each one after `evict` (outside its events)."""
-    fn()
+    back to back, or each one after `evict` (outside its events), after
+    reps / 4 untimed calls."""
+    for _ in range(max(1, reps // 4)):
+        fn()
     torch.cuda.synchronize()
     if evict is None:
         e0 = torch.cuda.Event(enable_timing=True)
@@ -524,11 +526,11 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
             fns = [make(c, lays[c], bts[c]) for c in range(copies)]
             return lambda: [f() for f in fns]
 
+        # the score stages first, on the last step's own selection and query: the
+        # candidate filter then compares against the hint that step's top-K left
+        # (after the predict and select stages the selection is the next step's,
+        # the hint no longer fits it and the candidate count is not a step's)
         st = {
-            "predict": per_copy(lambda c, lay, bt: lambda: api.spin_predict_blocks(
-                lay.cfg, bt, lay.V, lay.D, lay.S, v_max=lay.v_max)),
-            "select": per_copy(lambda c, lay, bt: lambda: api.spin_select_blocks(
-                lay.cfg, bt, lay.S, lay.row_code, lay.sel, lay.n_sel)),
             # the kernel spin_step runs (it also filters the top-K candidates)
             "score": per_copy(lambda c, lay, bt: lambda: api.spin_sparse_index_score(
                 lay.cfg, bt, q, inp.weights, pages[c], scales[c], pt, lay.sel, lay.n_sel,
@@ -541,6 +543,10 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
             "ema": per_copy(lambda c, lay, bt: lambda: api.spin_ema_update(
                 lay.cfg, bt, lay.z, lay.sel, lay.n_sel, lay.V, lay.D, n_valid=last_nv,
                 v_max=lay.v_max)),
+            "predict": per_copy(lambda c, lay, bt: lambda: api.spin_predict_blocks(
+                lay.cfg, bt, lay.V, lay.D, lay.S, v_max=lay.v_max)),
+            "select": per_copy(lambda c, lay, bt: lambda: api.spin_select_blocks(
+                lay.cfg, bt, lay.S, lay.row_code, lay.sel, lay.n_sel)),
         }
         out["stage_us"] = {k: _timed_us(f, stage_reps, stream) / copies for k, f in st.items()}
         for lay in lays:
