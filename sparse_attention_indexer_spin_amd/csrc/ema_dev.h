@@ -201,43 +201,37 @@ __device__ __forceinline__ void ema_blocks(const EmaArgs& A, int r, int k0, int 
               lane < L - 1;
       kn[u] = next_sel ? k + 1 : -1;
       const int i = j * 64 + lane;
-      vV[u] = 0.0f;
-      dM[u] = 0.0f;
-      dE[u] = 0.0f;
+      // every load unconditional, lanes without an element reading element
+      // 0 of the same array (rows past L read row 0): loads under branches
+      // made the compiler wait for all outstanding loads where they joined
+      const bool on = jj[u] >= 0, in = on && i < N;
+      const float vx = Vr[in ? i : 0], dx = Dr[in ? q - i : 0];
+      vV[u] = in ? vx : 0.0f;
+      dM[u] = in ? dx : 0.0f;
       mM[u] = 0u;
       mE[u] = 0u;
 #pragma unroll
       for (int row = 0; row < SPIN_MAX_ROWS; ++row) {
-        zV[u][row] = 0.0f;
-        zM[u][row] = 0.0f;
-        zE[u][row] = 0.0f;
-      }
-      if (jj[u] < 0) continue;
-      if (i < N) {
-        vV[u] = Vr[i];
-        dM[u] = Dr[q - i];
-      }
-#pragma unroll
-      for (int row = 0; row < SPIN_MAX_ROWS; ++row) {
-        if (row >= L) break;
-        if (i < N) zV[u][row] = zb[row * z_ld + (int64_t)k * 64 + lane];
+        const bool rw = row < L;
+        const int64_t ro = (int64_t)(rw ? row : 0) * z_ld;
+        const float zv = zb[ro + (rw && in ? (int64_t)k * 64 + lane : 0)];
+        zV[u][row] = rw && in ? zv : 0.0f;
         // offset q - i, row `row`: slot i + row, in block j or (if selected) j + 1
         const int sm = i + row;
-        if (i < N && sm < N) {
-          const int kk = (sm >> 6) == j ? k : kn[u];
-          if (kk >= 0) {
-            zM[u][row] = zb[row * z_ld + (int64_t)kk * 64 + (sm & 63)];
-            mM[u] |= 1u << row;
-          }
-        }
+        const int kk = (sm >> 6) == j ? k : kn[u];
+        const bool mm = rw && in && sm < N && kk >= 0;
+        const float zm = zb[ro + (mm ? (int64_t)kk * 64 + (sm & 63) : 0)];
+        zM[u][row] = mm ? zm : 0.0f;
+        mM[u] |= mm ? 1u << row : 0u;
         // extension offset q - s0, s0 = 64 j - 1 - lane: slot s0 + row in block j
         const int se = j * 64 - 1 - lane + row;
-        if (pe[u] && se >= j * 64 && se < N) {
-          zE[u][row] = zb[row * z_ld + (int64_t)k * 64 + (se & 63)];
-          mE[u] |= 1u << row;
-        }
+        const bool me = rw && on && pe[u] && se >= j * 64 && se < N;
+        const float ze = zb[ro + (me ? (int64_t)k * 64 + (se & 63) : 0)];
+        zE[u][row] = me ? ze : 0.0f;
+        mE[u] |= me ? 1u << row : 0u;
       }
-      if (mE[u]) dE[u] = Dr[q - (j * 64 - 1 - lane)];
+      const float dex = Dr[mE[u] ? q - (j * 64 - 1 - lane) : 0];
+      dE[u] = mE[u] ? dex : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < CR; ++u) {

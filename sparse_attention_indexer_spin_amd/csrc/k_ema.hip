@@ -96,10 +96,14 @@ hipError_t launch_ema_a2(const spin_config& c, const spin_batch& b, const float*
   return hipGetLastError();
 }
 
+// BPW blocks per wave: kEmaBlocksPerWave with one row; with several rows a
+// wave's blocks are one chunk of the several-row update (kEmaChunkRows), whose
+// loads are unconditional, so a wave's last chunk should not be a partial one.
+template <int BPW>
 __global__ __launch_bounds__(256) void k_ema(EmaArgs A) {
   const int r = blockIdx.y;
-  const int k0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kEmaBlocksPerWave;
-  ema_wave(A, r, k0, blockIdx.x == 0 && threadIdx.x == 0);
+  const int k0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * BPW;
+  ema_blocks<BPW>(A, r, k0, k0 + BPW, blockIdx.x == 0 && threadIdx.x == 0);
 }
 
 // The EMA update and the next step's block scores (SPIN_PREDICT_AHEAD, one
@@ -126,8 +130,15 @@ hipError_t launch_ema(const spin_config& c, const spin_batch& b, const float* z,
     hipLaunchKernelGGL(k_ema_predict, grid, dim3(256), 0, st, ema_pred_args(c, A, ahead));
     return hipGetLastError();
   }
-  dim3 grid((b.max_blocks + 4 * kEmaBlocksPerWave - 1) / (4 * kEmaBlocksPerWave), b.batch);
-  hipLaunchKernelGGL(k_ema, grid, dim3(256), 0, st, A);
+  if (b.n_rows > 1 && !A.row0_only) {
+    constexpr int W = kEmaChunkRows;
+    dim3 grid((b.max_blocks + 4 * W - 1) / (4 * W), b.batch);
+    hipLaunchKernelGGL(k_ema<W>, grid, dim3(256), 0, st, A);
+  } else {
+    constexpr int W = kEmaBlocksPerWave;
+    dim3 grid((b.max_blocks + 4 * W - 1) / (4 * W), b.batch);
+    hipLaunchKernelGGL(k_ema<W>, grid, dim3(256), 0, st, A);
+  }
   return hipGetLastError();
 }
 
