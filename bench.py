@@ -61,6 +61,9 @@ def parse():
                     help="skip the fixed-cost section (the sparsity sweep with its fits)")
     ap.add_argument("--sweep-runs", type=int, default=3)
     ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--runs", type=int, default=3,
+                    help="rotate: timed runs of the steps (each from a reset) and of the stage "
+                         "loop; the line reports their median and spread")
     ap.add_argument("--cache", choices=["rotate", "cold", "warm"], default="rotate",
                     help="rotate: step --copies independent copies of the workload round robin "
                          "back to back (each step's pages were evicted by the others, as between "
@@ -132,12 +135,25 @@ class Evictor:
         self.buf.sum()
 
 
+# Untimed calls before a stage is timed back to back.  When the load changes
+# (say from latency-bound launches to the HBM-bound score kernel) the chip's
+# power management takes ~15-20 ms to settle: the score launch then runs
+# ~60.5 us for two rounds over the copies, 63-71 us for the next ~20 rounds
+# and ~60.5 us again from ~15 ms on.  Timing starts after the transient.
+WARM_MS = 25.0
+
+
 def _timed_us(fn, reps: int, stream, evict=None) -> float:
     """Mean duration of `fn` over `reps` launches (HIP events on `stream`):
-    back to back, or each one after `evict` (outside its events), after
-    reps / 4 untimed calls."""
-    for _ in range(max(1, reps // 4)):
+    back to back, after untimed calls for WARM_MS of device time (and at
+    least reps / 4 of them), or each one after `evict` (outside its events),
+    after reps / 4 untimed calls."""
+    n, t_end = 0, time.perf_counter() + (WARM_MS * 1e-3 if evict is None else 0.0)
+    while n < max(1, reps // 4) or time.perf_counter() < t_end:
         fn()
+        n += 1
+        if n % 4 == 0:  # keep the host within a few calls of the device
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     if evict is None:
         e0 = torch.cuda.Event(enable_timing=True)
@@ -401,14 +417,15 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
 
 
 def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_reps: int,
-               copies: int):
+               copies: int, runs: int = 3):
     """`copies` independent copies of the workload -- own key pages (same data),
     EMA state and buffers -- stepped round robin back to back, as the layers of
     a model run: by the time a copy steps again, the others have streamed
     (copies - 1) x its pages and state through the L2s and the 256 MB MALL, and no host
     sync or event sits between two steps.  Per-step time = total / (steps x
-    copies).  Stage timing likewise: each stage launched round robin over the
-    copies, reps x copies launches between two events."""
+    copies), the median over `runs` runs, each from a reset.  Stage timing
+    likewise: each stage launched round robin over the copies, reps x copies
+    launches between two events, the median over `runs` loops."""
     from sparse_attention_indexer_spin_amd import SpinLayer, api
     w = inp.w
     pages = [inp.keys.pages] + [inp.keys.pages.clone() for _ in range(copies - 1)]
@@ -432,19 +449,26 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
     ios = [[lay.make_io(inp.q[s], inp.weights, pages[c], scales[c], pt, n_valid=nv[s])
             for s in range(warmup + steps)] for c, lay in enumerate(lays)]
     stream = torch.cuda.current_stream()
-    for s in range(warmup):
-        for c in range(copies):
-            api.spin_step(lays[c].cfg, bts[c], ios[c][s])
-    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for s in range(warmup, warmup + steps):
-        for c in range(copies):
-            api.spin_step(lays[c].cfg, bts[c], ios[c][s])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
+    run_ms = []
+    for run in range(runs):
+        if run:
+            for lay in lays:
+                lay.set_requests(inp.ctx.cuda(), inp.pos[0].cuda())
+                lay.reset()
+        for s in range(warmup):
+            for c in range(copies):
+                api.spin_step(lays[c].cfg, bts[c], ios[c][s])
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for s in range(warmup, warmup + steps):
+            for c in range(copies):
+                api.spin_step(lays[c].cfg, bts[c], ios[c][s])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        run_ms.append(t0.elapsed_time(t1))
+    total_ms = float(np.median(run_ms))
     for lay in lays:
         assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
     for lay in lays[1:]:
@@ -453,7 +477,8 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
     ctx = lays[0].ctx_len.cpu().numpy().astype(np.int64)
     keys = int(np.minimum(n_sel * 64, ctx).sum()) * w.rows
     out = dict(total_ms=total_ms, ms_per_step=total_ms / (steps * copies), keys_per_step=keys,
-               n_sel=int(n_sel.sum()))
+               n_sel=int(n_sel.sum()),
+               ms_per_step_runs=[t / (steps * copies) for t in run_ms])
     # the same copies as the layers of one model through the multi-layer
     # schedule (plans on a side stream), from fresh state: per-layer step time
     from sparse_attention_indexer_spin_amd import SpinStack
@@ -548,7 +573,25 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
             "select": per_copy(lambda c, lay, bt: lambda: api.spin_select_blocks(
                 lay.cfg, bt, lay.S, lay.row_code, lay.sel, lay.n_sel)),
         }
-        out["stage_us"] = {k: _timed_us(f, stage_reps, stream) / copies for k, f in st.items()}
+        # every loop starts from the state the last step left (its selection,
+        # the top-K hints and candidates in the workspace): the predict and
+        # select stages of a loop leave the next step's selection behind
+        snap = [(lay.sel.clone(), lay.n_sel.clone(),
+                 None if lay.workspace is None else lay.workspace.clone()) for lay in lays]
+
+        def stage_loop():
+            for lay, (s_sel, s_n, s_ws) in zip(lays, snap):
+                lay.sel.copy_(s_sel)
+                lay.n_sel.copy_(s_n)
+                if s_ws is not None:
+                    lay.workspace.copy_(s_ws)
+            return {k: _timed_us(f, stage_reps, stream) / copies for k, f in st.items()}
+
+        loops = [stage_loop() for _ in range(max(1, runs))]
+        del snap
+        out["stage_us"] = {k: float(np.median([lp[k] for lp in loops])) for k in st}
+        out["stage_us_spread"] = {k: [min(lp[k] for lp in loops), max(lp[k] for lp in loops)]
+                                  for k in st}
         for lay in lays:
             assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
     return out
@@ -900,7 +943,8 @@ def main():
     if args.cache != "cold":
         refs["cold"] = run_gpu(inp, sp, args.steps, args.warmup, evict=evictor)
     if args.cache == "rotate":
-        res = run_rotate(inp, sp, args.steps, args.warmup, args.stage_reps, args.copies)
+        res = run_rotate(inp, sp, args.steps, args.warmup, args.stage_reps, args.copies,
+                         args.runs)
     else:
         res = run_gpu(inp, sp, args.steps, args.warmup, stage_reps=args.stage_reps,
                       evict=evictor if args.cache == "cold" else None)
@@ -921,6 +965,7 @@ def main():
                    "sparsity_bp": sp, "explore_bp": w.explore_bp, "key_dtype": w.key_dtype,
                    "q_dtype": w.q_dtype},
         "us_per_step_layer": res["ms_per_step"] * 1e3,
+        "us_per_step_layer_runs": [t * 1e3 for t in res.get("ms_per_step_runs", [])] or None,
         "cache": {"mode": args.cache,
                   "how": {"rotate": f"{args.copies} independent copies of the workload (own "
                                     "pages and state) stepped round robin back to back",
@@ -932,6 +977,7 @@ def main():
         "graph_us_per_step_layer": (res["graph_ms_per_step"] * 1e3
                                     if "graph_ms_per_step" in res else None),
         "stage_us": res["stage_us"],
+        "stage_us_spread": res.get("stage_us_spread"),
         "keys_scored_per_step": keys_row,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
@@ -949,7 +995,10 @@ def main():
         hbm = out["roofline"]
         out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": FP8_MFMA_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": tflops / FP8_MFMA_PEAK_TFLOPS,
-                           "traffic": hbm["traffic"], "kernel": hbm["kernel"],
+                           "traffic": hbm["traffic"],
+                           # 2-4 rows and at most 64 requests: the all-rows kernel
+                           "kernel": ("spin::k_score_rows" if w.batch <= 64
+                                      else hbm["kernel"]),
                            "algorithmic_flops_per_launch": flops,
                            "algorithmic_bytes_per_launch": score_bytes, "launch_us": score_us,
                            "hbm_achieved_gbs": achieved, "hbm_frac": achieved / HBM_PEAK_GBS}
