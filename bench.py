@@ -143,11 +143,12 @@ class Evictor:
 WARM_MS = 25.0
 
 
-def _timed_us(fn, reps: int, stream, evict=None) -> float:
+def _timed_us(fn, reps: int, stream, evict=None, warm_log=None) -> float:
     """Mean duration of `fn` over `reps` launches (HIP events on `stream`):
     back to back, after untimed calls for WARM_MS of device time (and at
     least reps / 4 of them), or each one after `evict` (outside its events),
-    after reps / 4 untimed calls."""
+    after reps / 4 untimed calls.  `warm_log` (a list) receives the number
+    of untimed calls, which locates the timed launches in a kernel trace."""
     n, t_end = 0, time.perf_counter() + (WARM_MS * 1e-3 if evict is None else 0.0)
     while n < max(1, reps // 4) or time.perf_counter() < t_end:
         fn()
@@ -155,6 +156,8 @@ def _timed_us(fn, reps: int, stream, evict=None) -> float:
         if n % 4 == 0:  # keep the host within a few calls of the device
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    if warm_log is not None:
+        warm_log.append(n)
     if evict is None:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -585,10 +588,14 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
                 lay.n_sel.copy_(s_n)
                 if s_ws is not None:
                     lay.workspace.copy_(s_ws)
-            return {k: _timed_us(f, stage_reps, stream) / copies for k, f in st.items()}
+            return {k: _timed_us(f, stage_reps, stream, warm_log=warm[k]) / copies
+                    for k, f in st.items()}
 
+        warm = {k: [] for k in st}
         loops = [stage_loop() for _ in range(max(1, runs))]
         del snap
+        # untimed calls (rounds over the copies) before each loop's timed ones
+        out["stage_warm_rounds"] = warm
         out["stage_us"] = {k: float(np.median([lp[k] for lp in loops])) for k in st}
         out["stage_us_spread"] = {k: [min(lp[k] for lp in loops), max(lp[k] for lp in loops)]
                                   for k in st}
@@ -978,6 +985,7 @@ def main():
                                     if "graph_ms_per_step" in res else None),
         "stage_us": res["stage_us"],
         "stage_us_spread": res.get("stage_us_spread"),
+        "stage_warm_rounds": res.get("stage_warm_rounds"),
         "keys_scored_per_step": keys_row,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
