@@ -33,6 +33,9 @@ Readings where the pages are silent (each is listed in the design doc):
     parts, then one more level to the largest fractional parts (ties: lower
     layer) until the sum is T.  The running miss rate of a layer is the mean
     of its miss rates at the levels it ran at, over the probes so far.
+  * Drift: the table is re-sized when some layer's miss rate at some level
+    moved by more than a threshold since the curves of the last publication
+    (BudgetPolicy); a zero threshold re-sizes at every probe.
 """
 from __future__ import annotations
 
@@ -142,3 +145,57 @@ def allocate_proportional(miss, target_level: int, levels: int):
             g[l] += 1
             left -= 1
     return g
+
+
+def miss_rates(covered_l, total_l):
+    """One layer's miss rate at every level, in binary64: (K' - covered[g]) / K'
+    (0 for a layer without top-K slots)."""
+    t = int(total_l)
+    return [0.0 if t == 0 else float(t - int(c)) / float(t) for c in covered_l]
+
+
+class BudgetPolicy:
+    """The policy across probes (the pages: a background computation re-sizes
+    the budgets whenever the miss curves drift and publishes them to a table).
+
+    Reading: at every probe,
+      * the proportional rule adds each layer's miss rate at the level it ran
+        at to its running sum (the probe count grows by one);
+      * the levels are re-sized and published when drift_bp == 0, at the
+        first probe, or when some layer's miss rate at some level differs by
+        more than drift_bp / 10000 from the curves of the last publication;
+        otherwise the table keeps its levels.  The published curves become
+        the new reference.
+    Minimax re-sizes from the probe's curves, proportional from the running
+    means."""
+
+    def __init__(self, policy: str, n_layers: int, levels: int, target_level: int,
+                 drift_bp: int = 0):
+        assert policy in ("minimax", "proportional") and 0 <= drift_bp <= 10000
+        self.policy, self.L, self.levels = policy, int(n_layers), int(levels)
+        self.target, self.drift_bp = int(target_level), int(drift_bp)
+        self.level_now = [self.target] * self.L
+        self.miss_sum = [0.0] * self.L
+        self.n_probes = 0
+        self.ref = None
+
+    def probe(self, covered, total):
+        """covered: [L][levels + 1] ints, total: [L] ints (summed over the
+        layer's requests and rows).  Returns (levels, published)."""
+        cur = [miss_rates(covered[l], total[l]) for l in range(self.L)]
+        if self.policy == "proportional":
+            self.n_probes += 1
+            for l in range(self.L):
+                self.miss_sum[l] += cur[l][self.level_now[l]]
+        publish = self.drift_bp == 0 or self.ref is None
+        if not publish:
+            drift = max(abs(a - b) for l in range(self.L) for a, b in zip(cur[l], self.ref[l]))
+            publish = drift > self.drift_bp / 10000
+        if publish:
+            if self.policy == "minimax":
+                self.level_now = allocate_minimax(covered, total, self.target, self.levels)
+            else:
+                self.level_now = allocate_proportional(
+                    [m / self.n_probes for m in self.miss_sum], self.target, self.levels)
+            self.ref = cur
+        return list(self.level_now), publish

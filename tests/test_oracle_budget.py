@@ -114,3 +114,53 @@ def test_proportional_properties():
         # harder layers never get fewer levels (up to the one-level rounding)
         order = np.argsort(miss)
         assert all(g[order[i]] <= g[order[i + 1]] + 1 for i in range(L - 1))
+
+
+# Curves of the drift example (2 layers, 4 levels, K' = 10 each): the miss
+# rates at levels 0..4 written out, then the covered counts they come from.
+_P1 = ([0, 4, 7, 9, 10], [0, 2, 5, 8, 10])    # miss [1 .6 .3 .1 0], [1 .8 .5 .2 0]
+_P2 = ([0, 5, 7, 9, 10], [0, 2, 4, 8, 10])    # miss [1 .5 .3 .1 0], [1 .8 .6 .2 0]
+_P3 = ([0, 1, 2, 10, 10], [0, 2, 4, 8, 10])   # miss [1 .9 .8  0 0], [1 .8 .6 .2 0]
+
+
+def test_budget_policy_drift_gate_minimax_hand_example():
+    """Minimax on the hand-worked curves above (greedy raises, ties to the
+    lower layer): probe 1 gives [2, 2]; probe 2 alone would give [1, 3] but
+    moves no miss rate by more than 0.1, so a 0.15 threshold keeps [2, 2];
+    probe 3 moves layer 0 by 0.5 at level 2 and is published: [3, 1].  With
+    no threshold every probe is published."""
+    gated = OB.BudgetPolicy("minimax", 2, 4, 2, drift_bp=1500)
+    every = OB.BudgetPolicy("minimax", 2, 4, 2, drift_bp=0)
+    want_gated = [([2, 2], True), ([2, 2], False), ([3, 1], True)]
+    want_every = [([2, 2], True), ([1, 3], True), ([3, 1], True)]
+    for cov, wg, we in zip((_P1, _P2, _P3), want_gated, want_every):
+        assert gated.probe(list(cov), [10, 10]) == wg
+        assert every.probe(list(cov), [10, 10]) == we
+
+
+def test_budget_policy_drift_gate_keeps_the_running_means():
+    """Proportional: a gated probe still adds each layer's miss rate at its
+    current level to the running sums.  Probe 1 at the target levels [2, 2]
+    adds (.3, .5) and publishes shares 4 * (.301, .501) / .802 = (1.50, 2.50)
+    -> [1, 2] plus the larger fraction -> [2, 2]; probe 2 adds (.3, .6),
+    drifts 0.1 and is not published."""
+    pol = OB.BudgetPolicy("proportional", 2, 4, 2, drift_bp=1500)
+    assert pol.probe(list(_P1), [10, 10]) == ([2, 2], True)
+    assert pol.probe(list(_P2), [10, 10]) == ([2, 2], False)
+    assert pol.n_probes == 2
+    assert pol.miss_sum == pytest.approx([0.6, 1.1], abs=1e-15)
+    assert pol.ref == [OB.miss_rates(c, 10) for c in _P1]
+
+
+def test_budget_policy_full_threshold_publishes_only_the_first_probe():
+    """Miss rates lie in [0, 1], so no drift exceeds a threshold of 10000 bp."""
+    rng = np.random.default_rng(3)
+    pol = OB.BudgetPolicy("minimax", 3, 8, 5, drift_bp=10000)
+    for k in range(6):
+        tot = rng.integers(1, 50, 3)
+        cov = [np.minimum(np.cumsum(rng.integers(0, 5, 9)), t).tolist() for t in tot]
+        for l in range(3):
+            cov[l][-1] = int(tot[l])
+        levels, published = pol.probe(cov, tot.tolist())
+        assert published == (k == 0)
+        assert sum(levels) == 15
