@@ -85,6 +85,10 @@ def parse():
                          "--probe-period steps (the multi-layer workload states the "
                          "proportional rule), timed beside the uniform runs")
     ap.add_argument("--probe-period", type=int, default=8)
+    ap.add_argument("--budget-drift-bp", type=int, default=0,
+                    help="--stack with budgets: re-size the levels only when a layer's miss "
+                         "curve moved by more than this many basis points since the last "
+                         "re-sizing (0: at every probe)")
     ap.add_argument("--stack-layers", type=int, default=8,
                     help="--stack on a one-layer workload: that many independent layers of it")
     ap.add_argument("--miss-eval", action="store_true",
@@ -269,7 +273,7 @@ class StackInputs:
 
 def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict=None,
               policy: str = "none", probe_period: int = 8,
-              modes=("seq", "stack", "ema_stream", "one_stream")):
+              modes=("seq", "stack", "ema_stream", "one_stream"), drift_bp: int = 0):
     """Whole decode steps of every layer: (a) one spin_step per layer in layer
     order on the current stream, (b) one spin_stack_step (plans on a side
     stream).  Each mode on its own layer states from the same reset; each timed
@@ -348,7 +352,8 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
         # the same schedule with per-layer budgets and dense probe steps; the
         # effective sparsity counts every selected block of every step
         bud_layers = layers()
-        bstack = SpinStack(bud_layers, budget_policy=policy, probe_period=probe_period)
+        bstack = SpinStack(bud_layers, budget_policy=policy, probe_period=probe_period,
+                           budget_drift_bp=drift_bp)
         sel_blocks = []
 
         def budget_step(s):
@@ -374,7 +379,7 @@ def run_stack(inp: StackInputs, sparsity_bp: int, steps: int, warmup: int, evict
         ms_budget = sum(a.elapsed_time(b) for a, b in ev) / steps
         total_blocks = w.layers * int(sum(-(-int(c) // 64) for c in inp.ctx))
         chosen = float(torch.stack(sel_blocks).sum().item()) / steps
-        budget = {"policy": policy, "probe_period": probe_period,
+        budget = {"policy": policy, "probe_period": probe_period, "drift_bp": drift_bp,
                   "us_per_step": ms_budget * 1e3,
                   "us_per_step_layer": ms_budget * 1e3 / w.layers,
                   "effective_block_sparsity": 1.0 - chosen / total_blocks,
@@ -1057,7 +1062,7 @@ def main_stack(args, w: G.Workload, sp: int):
         print(json.dumps({"workload": w.name, "cache": args.cache, "stack_sweep": sw}))
         return
     res = run_stack(inp, sp, args.steps, args.warmup, evict, args.budget_policy,
-                    args.probe_period)
+                    args.probe_period, drift_bp=args.budget_drift_bp)
     score_bytes = algorithmic_score_bytes(w, res["keys_layer0"], res["n_sel_layer0"])
     achieved = score_bytes / (res["score_us_layer0"] * 1e-6) / 1e9
     out = {

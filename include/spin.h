@@ -470,7 +470,7 @@ spin_status spin_budget_allocate(int32_t policy, int32_t n_layers, int32_t level
  * The per-layer budget policy run by a spin_stack itself (blog, "Per-layer
  * block budgets": a dense probe every P steps measures each layer's miss
  * curve, and the budgets are re-sized at a fixed total and published to a
- * device-side table).  With a policy set, spin_stack_step
+ * device-side table whenever the curves drift).  With a policy set, spin_stack_step
  *   - counts its calls since spin_stack_reset_budgets; call t = P, 2P, ... is
  *     a probe: every layer selects every block (probe_budget);
  *   - otherwise layer l selects with budget[l] (its level in level_table[l],
@@ -478,8 +478,11 @@ spin_status spin_budget_allocate(int32_t policy, int32_t n_layers, int32_t level
  *   - after a probe call's finishes, on the main stream: each layer's miss
  *     curve (spin_miss_curve into covered / kprime), then one device kernel
  *     that sums the curves over requests and rows, updates the running miss
- *     rates (state) and writes the new levels into level_table -- the same
- *     arithmetic as spin_budget_allocate -- then each layer's budget fill.
+ *     rates (state) and, unless drift_bp > 0 and no layer's miss rate at any
+ *     level moved by more than drift_bp / 10000 since the curves of the last
+ *     publication (the first probe always publishes), writes the new levels
+ *     into level_table -- the same arithmetic as spin_budget_allocate -- then
+ *     each layer's budget fill.
  *     The next call selects with them; nothing waits for the host.
  * Every layer of the stack takes part (n_layers of the stack), with the same
  * batch and n_rows; defer_ema is not available with a policy.  Buffers are
@@ -497,6 +500,7 @@ typedef struct spin_budget_policy {
   int32_t probe_period;  /* P >= 1                                                  */
   int32_t levels;        /* divides 10000                                           */
   int32_t target_level;  /* 0 .. levels; the level sum is n_layers * target_level  */
+  int32_t drift_bp;      /* 0 .. 10000: publish only past this drift (0: always)    */
   int32_t* level_table;
   int32_t* budget;
   int32_t* probe_budget;
@@ -514,13 +518,17 @@ size_t spin_budget_state_bytes(int32_t n_layers, int32_t levels);
  *   SPIN_BUDGET_PROPORTIONAL: each layer's miss rate at its current level
  *     (level_table on entry) added to its running sum in `state`, the probe
  *     count incremented, and the proportional allocation of the running means;
- * new levels into level_table.  state (spin_budget_state_bytes()) must be
- * zero before the first probe.  No host synchronisation.
+ * new levels into level_table, which is left as it is when drift_bp > 0 and
+ * no miss rate of any layer at any level moved by more than drift_bp / 10000
+ * from the curves of the last call that wrote it (the first call always
+ * writes; the running miss rates advance either way).  state
+ * (spin_budget_state_bytes()) must be zero before the first probe.  No host
+ * synchronisation.  drift_bp outside [0, 10000]: SPIN_E_SHAPE.
  */
 spin_status spin_budget_update(int32_t policy, int32_t n_layers, int32_t levels,
-                               int32_t target_level, int32_t rows_total, const int32_t* covered,
-                               const int32_t* kprime, void* state, int32_t* level_table,
-                               void* stream);
+                               int32_t target_level, int32_t drift_bp, int32_t rows_total,
+                               const int32_t* covered, const int32_t* kprime, void* state,
+                               int32_t* level_table, void* stream);
 spin_status spin_stack_set_budget_policy(spin_stack* stack, const spin_budget_policy* policy);
 spin_status spin_stack_reset_budgets(spin_stack* stack, int32_t n_layers, const spin_config* cfgs,
                                      const spin_batch* bts, void* main_stream);

@@ -64,7 +64,8 @@ class SpinStepIO(C.Structure):
 
 class SpinBudgetPolicy(C.Structure):
     _fields_ = [("policy", C.c_int32), ("probe_period", C.c_int32), ("levels", C.c_int32),
-                ("target_level", C.c_int32), ("level_table", C.c_void_p), ("budget", C.c_void_p),
+                ("target_level", C.c_int32), ("drift_bp", C.c_int32),
+                ("level_table", C.c_void_p), ("budget", C.c_void_p),
                 ("probe_budget", C.c_void_p), ("covered", C.c_void_p), ("kprime", C.c_void_p),
                 ("state", C.c_void_p)]
 
@@ -103,7 +104,7 @@ def load() -> C.CDLL:
         "spin_budget_allocate": [I32, I32, I32, I32, P, P, P, P],
         "spin_stack_set_budget_policy": [P, C.POINTER(SpinBudgetPolicy)],
         "spin_stack_reset_budgets": [P, I32, cfg, bt, P],
-        "spin_budget_update": [I32, I32, I32, I32, I32, P, P, P, P, P],
+        "spin_budget_update": [I32, I32, I32, I32, I32, I32, P, P, P, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)

@@ -243,15 +243,17 @@ def spin_budget_state_bytes(n_layers: int, levels: int) -> int:
 def spin_stack_set_budget_policy(stack: Stack, policy: Optional[str], probe_period: int = 8,
                                  levels: int = 100, target_level: int = 0, level_table=None,
                                  budget=None, probe_budget=None, covered=None, kprime=None,
-                                 state=None):
+                                 state=None, drift_bp: int = 0):
     """The stack runs per-layer budgets itself (policy "minimax" or
-    "proportional"; None clears it).  Buffers: see include/spin.h."""
+    "proportional"; None clears it; drift_bp > 0 publishes new levels only
+    past that drift of the miss curves).  Buffers: see include/spin.h."""
     if policy is None:
         L.check(L.load().spin_stack_set_budget_policy(stack.handle, None))
         return
     code = {"minimax": L.SPIN_BUDGET_MINIMAX, "proportional": L.SPIN_BUDGET_PROPORTIONAL}[policy]
     p = L.SpinBudgetPolicy(policy=code, probe_period=probe_period, levels=levels,
-                           target_level=target_level, level_table=_p(level_table),
+                           target_level=target_level, drift_bp=drift_bp,
+                           level_table=_p(level_table),
                            budget=_p(budget), probe_budget=_p(probe_budget), covered=_p(covered),
                            kprime=_p(kprime), state=_p(state))
     L.check(L.load().spin_stack_set_budget_policy(stack.handle, C.byref(p)))
@@ -264,12 +266,13 @@ def spin_stack_reset_budgets(stack: Stack, cfgs, bts, main_stream=None):
 
 
 def spin_budget_update(policy: str, levels: int, target_level: int, covered, kprime, state,
-                       level_table, stream=None):
+                       level_table, stream=None, drift_bp: int = 0):
     """One probe's allocation on the device.  covered: i32 [L, rows_total,
-    levels + 1], kprime: i32 [L, rows_total] (device tensors)."""
+    levels + 1], kprime: i32 [L, rows_total] (device tensors); with
+    drift_bp > 0 level_table changes only past that drift of the curves."""
     code = {"minimax": L.SPIN_BUDGET_MINIMAX, "proportional": L.SPIN_BUDGET_PROPORTIONAL}[policy]
     n_layers = level_table.numel()
     rows_total = kprime.numel() // n_layers
-    L.check(L.load().spin_budget_update(code, n_layers, levels, target_level, rows_total,
+    L.check(L.load().spin_budget_update(code, n_layers, levels, target_level, drift_bp, rows_total,
                                         _p(covered), _p(kprime), _p(state), _p(level_table),
                                         _stream(stream)))

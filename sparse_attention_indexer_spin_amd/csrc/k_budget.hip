@@ -174,14 +174,21 @@ hipError_t launch_budget_fill(const spin_config& c, const spin_batch& b, const i
 // layer's curves over its requests and rows, update the running miss rates
 // (proportional rule), re-size the layers' levels into the level table.  The
 // same arithmetic as the host allocation below, so both give the same levels.
+// With a drift threshold the new levels are published only when some
+// layer's miss rate at some level moved by more than drift_bp / 10000 since
+// the curves of the last publication (the first probe always publishes); the
+// running miss rates advance at every probe.
 // State (caller-owned, budget_state_bytes()): f64 miss sums [L], f64 probe
-// count, i64 curve sums [L][levels + 1], i64 valid top-K totals [L].
+// count, i64 curve sums [L][levels + 1], i64 valid top-K totals [L], f64 miss
+// rates of the last publication [L][levels + 1], f64 flag "published once".
 // ---------------------------------------------------------------------------
 struct BudgetState {
   double* miss_sum;
   double* n_probes;
   int64_t* cov;
   int64_t* tot;
+  double* ref;
+  double* has_ref;
 };
 
 __host__ __device__ inline BudgetState budget_state(void* p, int L, int levels) {
@@ -191,12 +198,21 @@ __host__ __device__ inline BudgetState budget_state(void* p, int L, int levels) 
   s.n_probes = s.miss_sum + L;
   s.cov = reinterpret_cast<int64_t*>(s.n_probes + 1);
   s.tot = s.cov + (int64_t)L * (levels + 1);
+  s.ref = reinterpret_cast<double*>(s.tot + L);
+  s.has_ref = s.ref + (int64_t)L * (levels + 1);
   return s;
 }
 
 size_t budget_state_bytes(int L, int levels) {
-  const size_t n = 8 * ((size_t)L + 1 + (size_t)L * (levels + 1) + (size_t)L);
+  const size_t W = (size_t)levels + 1;
+  const size_t n = 8 * ((size_t)L + 1 + (size_t)L * W + (size_t)L + (size_t)L * W + 1);
   return (n + 255) & ~size_t(255);
+}
+
+// Layer l's miss rate at level g from the summed curves (binary64).
+__device__ __forceinline__ double state_miss(const BudgetState& st, int W, int i) {
+  const int64_t t = st.tot[i / W], c = st.cov[i];
+  return t == 0 ? 0.0 : (double)(t - c) / (double)t;
 }
 
 // lane-held (miss numerator, denominator, layer) candidates; the wave's
@@ -218,7 +234,8 @@ constexpr int kBudgetLanes = 64;
 constexpr int kBudgetMaxPerLane = (SPIN_MAX_LAYERS + kBudgetLanes - 1) / kBudgetLanes;
 
 __global__ __launch_bounds__(256) void k_budget_update(int policy, int L, int levels, int target,
-                                                       int RR, const int32_t* __restrict__ cov,
+                                                       int drift_bp, int RR,
+                                                       const int32_t* __restrict__ cov,
                                                        const int32_t* __restrict__ kp,
                                                        void* state, int32_t* level_table) {
   const BudgetState st = budget_state(state, L, levels);
@@ -235,9 +252,34 @@ __global__ __launch_bounds__(256) void k_budget_update(int policy, int L, int le
     st.tot[l] = s;
   }
   __syncthreads();
+  // the drift since the last publication: the largest change of any miss rate
+  __shared__ double wave_drift[256 / 64];
+  __shared__ int publish_s;
+  const bool gate = drift_bp > 0 && *st.has_ref != 0.0;
+  if (gate) {
+    double d = 0.0;
+    for (int i = threadIdx.x; i < L * W; i += blockDim.x)
+      d = fmax(d, fabs(state_miss(st, W, i) - st.ref[i]));
+    for (int m = 32; m > 0; m >>= 1) d = fmax(d, __shfl_xor(d, m));
+    if ((threadIdx.x & 63) == 0) wave_drift[threadIdx.x >> 6] = d;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double d = 0.0;
+    if (gate)
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) d = fmax(d, wave_drift[w]);
+    publish_s = !gate || d > (double)drift_bp / 10000.0;
+  }
+  __syncthreads();
+  const bool publish = publish_s != 0;
+  if (publish) {  // these curves become the reference (read above, before the barrier)
+    for (int i = threadIdx.x; i < L * W; i += blockDim.x) st.ref[i] = state_miss(st, W, i);
+    if (threadIdx.x == 0) *st.has_ref = 1.0;
+  }
   if (threadIdx.x >= kBudgetLanes) return;
   const int lane = threadIdx.x;
   if (policy == SPIN_BUDGET_MINIMAX) {
+    if (!publish) return;
     // raise the layer of the largest miss rate by one level, from all zero
     int g[kBudgetMaxPerLane];
 #pragma unroll
@@ -293,6 +335,7 @@ __global__ __launch_bounds__(256) void k_budget_update(int policy, int L, int le
     fixed[l] = -1;
     share[l] = 0.0;
   }
+  if (!publish) return;
   const int64_t T = (int64_t)L * target;
   for (;;) {
     int64_t rem = T;
@@ -335,11 +378,11 @@ __global__ __launch_bounds__(256) void k_budget_update(int policy, int L, int le
   for (int l = 0; l < L; ++l) level_table[l] = gl[l];
 }
 
-hipError_t launch_budget_update(int policy, int L, int levels, int target, int RR,
+hipError_t launch_budget_update(int policy, int L, int levels, int target, int drift_bp, int RR,
                                 const int32_t* covered, const int32_t* kprime, void* state,
                                 int32_t* level_table, hipStream_t st) {
-  hipLaunchKernelGGL(k_budget_update, dim3(1), dim3(256), 0, st, policy, L, levels, target, RR,
-                     covered, kprime, state, level_table);
+  hipLaunchKernelGGL(k_budget_update, dim3(1), dim3(256), 0, st, policy, L, levels, target,
+                     drift_bp, RR, covered, kprime, state, level_table);
   return hipGetLastError();
 }
 
@@ -353,7 +396,10 @@ __global__ void k_budget_reset(int L, int levels, int target, int R, void* state
     st.miss_sum[i] = 0.0;
   }
   for (int i = threadIdx.x; i < R; i += blockDim.x) probe_budget[i] = SPIN_MAX_BLOCKS;
-  if (threadIdx.x == 0) *st.n_probes = 0.0;
+  if (threadIdx.x == 0) {
+    *st.n_probes = 0.0;
+    *st.has_ref = 0.0;
+  }
 }
 
 hipError_t launch_budget_reset(int L, int levels, int target, int R, void* state,

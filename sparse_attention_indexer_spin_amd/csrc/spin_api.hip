@@ -746,8 +746,8 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
                                                   P.covered + (int64_t)l * R * rows * W,
                                                   P.kprime + (int64_t)l * R * rows, mst),
                           "spin_stack_step/miss curve"));
-  SPIN_CHECK(spin_budget_update(P.policy, n_layers, P.levels, P.target_level, R * rows,
-                                P.covered, P.kprime, P.state, P.level_table, mst));
+  SPIN_CHECK(spin_budget_update(P.policy, n_layers, P.levels, P.target_level, P.drift_bp,
+                                R * rows, P.covered, P.kprime, P.state, P.level_table, mst));
   for (int l = 0; l < n_layers; ++l)
     SPIN_CHECK(hip_status(spin::launch_budget_fill(cfgs[l], bts[l], P.level_table + l, P.levels,
                                                    P.budget + (int64_t)l * R, mst),
@@ -757,9 +757,9 @@ spin_status spin_stack_step(spin_stack* stack, int32_t n_layers, const spin_conf
 }
 
 spin_status spin_budget_update(int32_t policy, int32_t n_layers, int32_t levels,
-                               int32_t target_level, int32_t rows_total, const int32_t* covered,
-                               const int32_t* kprime, void* state, int32_t* level_table,
-                               void* stream) {
+                               int32_t target_level, int32_t drift_bp, int32_t rows_total,
+                               const int32_t* covered, const int32_t* kprime, void* state,
+                               int32_t* level_table, void* stream) {
   const char* fn = "spin_budget_update";
   SPIN_CHECK(check_levels(fn, levels));
   if (policy != SPIN_BUDGET_MINIMAX && policy != SPIN_BUDGET_PROPORTIONAL)
@@ -768,14 +768,16 @@ spin_status spin_budget_update(int32_t policy, int32_t n_layers, int32_t levels,
     return fail(SPIN_E_SHAPE, "%s: n_layers %d outside [1, %d]", fn, n_layers, SPIN_MAX_LAYERS);
   if (target_level < 0 || target_level > levels)
     return fail(SPIN_E_SHAPE, "%s: target_level %d outside [0, %d]", fn, target_level, levels);
+  if (drift_bp < 0 || drift_bp > 10000)
+    return fail(SPIN_E_SHAPE, "%s: drift_bp %d outside [0, 10000]", fn, drift_bp);
   if (rows_total < 0 || rows_total > SPIN_MAX_BATCH * SPIN_MAX_ROWS)
     return fail(SPIN_E_SHAPE, "%s: rows_total %d", fn, rows_total);
   SPIN_REQUIRE(covered);
   SPIN_REQUIRE(kprime);
   SPIN_REQUIRE(state);
   SPIN_REQUIRE(level_table);
-  return hip_status(spin::launch_budget_update(policy, n_layers, levels, target_level, rows_total,
-                                               covered, kprime, state, level_table,
+  return hip_status(spin::launch_budget_update(policy, n_layers, levels, target_level, drift_bp,
+                                               rows_total, covered, kprime, state, level_table,
                                                (hipStream_t)stream), fn);
 }
 
@@ -798,6 +800,8 @@ spin_status spin_stack_set_budget_policy(spin_stack* stack, const spin_budget_po
   if (P.probe_period < 1) return fail(SPIN_E_SHAPE, "%s: probe_period < 1", fn);
   if (P.target_level < 0 || P.target_level > P.levels)
     return fail(SPIN_E_SHAPE, "%s: target_level outside [0, levels]", fn);
+  if (P.drift_bp < 0 || P.drift_bp > 10000)
+    return fail(SPIN_E_SHAPE, "%s: drift_bp outside [0, 10000]", fn);
   if (!P.level_table || !P.budget || !P.probe_budget || !P.covered || !P.kprime || !P.state)
     return fail(SPIN_E_NULL, "%s: a policy buffer is NULL", fn);
   stack->policy = P;

@@ -125,8 +125,9 @@ hipError_t launch_miss_curve(const spin_config& c, const spin_batch& b, const fl
 hipError_t launch_budget_fill(const spin_config& c, const spin_batch& b, const int32_t* level,
                               int levels, int32_t* budget, hipStream_t st);
 // After a probe step: the layers' curves summed, the running miss rates and
-// the new levels, all on the device (state: budget_state_bytes()).
-hipError_t launch_budget_update(int policy, int L, int levels, int target, int RR,
+// the new levels (published when the curves drifted by more than drift_bp,
+// always with drift_bp 0), all on the device (state: budget_state_bytes()).
+hipError_t launch_budget_update(int policy, int L, int levels, int target, int drift_bp, int RR,
                                 const int32_t* covered, const int32_t* kprime, void* state,
                                 int32_t* level_table, hipStream_t st);
 hipError_t launch_budget_reset(int L, int levels, int target, int R, void* state,

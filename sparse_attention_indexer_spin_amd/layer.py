@@ -136,11 +136,14 @@ class SpinStack:
     dense probe step measures the layers' miss curves, and a device kernel
     re-sizes the levels (their sum stays n_layers x the target level of the
     layers' sparsity) into the device-side level table and the layers'
-    budgets, used from the next step on.  This object only owns the buffers.
-    Until the first probe every layer runs at the target level."""
+    budgets, used from the next step on; with `budget_drift_bp` > 0 only
+    when some layer's miss curve moved by more than that many basis points
+    since the last re-sizing.  This object only owns the buffers.  Until the
+    first probe every layer runs at the target level."""
 
     def __init__(self, layers, device="cuda", budget_policy=None, probe_period: int = 8,
-                 levels: int = 100, ema_stream: bool = False, one_stream: bool = False):
+                 levels: int = 100, ema_stream: bool = False, one_stream: bool = False,
+                 budget_drift_bp: int = 0):
         self.layers = list(layers)
         # one_stream: every layer's plan inside the previous layer's score and
         # top-K + EMA launches on the main stream (no side stream, no events)
@@ -178,7 +181,7 @@ class SpinStack:
                 self.stack, budget_policy, probe_period=probe_period, levels=levels,
                 target_level=self.target, level_table=self.level_table, budget=self.budget,
                 probe_budget=self.probe_budget, covered=self.covered, kprime=self.kprime,
-                state=self.state)
+                state=self.state, drift_bp=budget_drift_bp)
             self.reset_budgets()
 
     # -- budgets -------------------------------------------------------------

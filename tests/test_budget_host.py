@@ -62,3 +62,8 @@ def test_allocation_argument_errors(api):
     tot = (C.c_int64 * 2)(2, 3)
     assert lib.spin_budget_allocate(0, 2, 2, 1, cov, tot, None, out) == 2
     assert lib.spin_budget_allocate(1, 2, 100, 10, None, None, miss, out) == 0
+    # the device update refuses a drift threshold outside [0, 10000] before
+    # it touches any buffer
+    for drift in (-1, 10001):
+        assert lib.spin_budget_update(1, 2, 100, 10, drift, 4, None, None, None, None,
+                                      None) == 2

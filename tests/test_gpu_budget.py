@@ -80,15 +80,17 @@ def test_budget_fill_parity():
             assert out.cpu().tolist() == want, (levels, g)
 
 
-@pytest.mark.parametrize("policy,one_stream", [("minimax", False), ("proportional", False),
-                                               ("proportional", True)])
-def test_stack_budgets_match_oracle_reference(policy, one_stream):
+@pytest.mark.parametrize("policy,one_stream,drift_bp", [("minimax", False, 0),
+                                                        ("proportional", False, 0),
+                                                        ("proportional", True, 0),
+                                                        ("minimax", True, 300)])
+def test_stack_budgets_match_oracle_reference(policy, one_stream, drift_bp):
     """SpinStack with probes every 3 steps, the policy run by the library
     (curves, allocation and budgets on the device, no host round trip),
     against sequential spin_step layers whose budgets come from the oracle:
     oracle miss curves of the same probe outputs, oracle allocation, applied
     from the step after the probe."""
-    banner(f"stack budgets {policy} one_stream={one_stream}")
+    banner(f"stack budgets {policy} one_stream={one_stream} drift_bp={drift_bp}")
     from sparse_attention_indexer_spin_amd import SpinStack
     L, P, levels, sp = 3, 3, 100, 4000
     w = G.WORKLOADS["fp8_256k_ragged_8l"].scaled(batch=4, layers=L, n_slots=64 * 120 + 9,
@@ -101,9 +103,10 @@ def test_stack_budgets_match_oracle_reference(policy, one_stream):
     seq = [make_layer(li, sp, predict_ahead=False) for li in lis]
     stk = [make_layer(li, sp) for li in lis]
     stack = SpinStack(stk, budget_policy=policy, probe_period=P, levels=levels,
-                      one_stream=one_stream)
+                      one_stream=one_stream, budget_drift_bp=drift_bp)
     target = (10000 - sp) // 100
-    ref_levels, history, miss_sum, n_probes = [target] * L, [], [0.0] * L, 0
+    ref_levels, history = [target] * L, []
+    ref = OB.BudgetPolicy(policy, L, levels, target, drift_bp=drift_bp)
     Bs = [O.n_blocks(int(c)) for c in lis[0].ctx]
     for s in range(w.steps):
         probe = s > 0 and s % P == 0
@@ -134,14 +137,7 @@ def test_stack_budgets_match_oracle_reference(policy, one_stream):
                 assert stk_cov_row(stack, l, r) == c, (s, l, r)
             cov.append(c_l.tolist())
             tot.append(t_l)
-        if policy == "minimax":
-            ref_levels = OB.allocate_minimax(cov, tot, target, levels)
-        else:
-            for l in range(L):
-                miss_sum[l] += 0.0 if tot[l] == 0 else (tot[l] - cov[l][ref_levels[l]]) / tot[l]
-            n_probes += 1
-            ref_levels = OB.allocate_proportional([m / n_probes for m in miss_sum], target,
-                                                  levels)
+        ref_levels, _ = ref.probe(cov, tot)
         assert stack.levels_now() == list(ref_levels), s
         history.append((s, list(ref_levels)))
     assert len(history) >= 2
@@ -163,7 +159,7 @@ def test_budget_update_matches_oracle(policy, L, rows_total, levels):
     target = levels * 3 // 5
     state = torch.zeros(A.spin_budget_state_bytes(L, levels), dtype=torch.uint8, device=DEV)
     table = torch.full((L,), target, dtype=torch.int32, device=DEV)
-    ref_levels, miss_sum = [target] * L, [0.0] * L
+    ref = OB.BudgetPolicy(policy, L, levels, target)
     for probe in range(3):
         kp = rng.integers(0, 300, (L, rows_total)).astype(np.int32)
         kp[0, :] = 0 if L > 2 and probe == 1 else kp[0, :]       # a layer with no top-K slots
@@ -175,16 +171,60 @@ def test_budget_update_matches_oracle(policy, L, rows_total, levels):
         torch.cuda.synchronize()
         c_l = cov.astype(np.int64).sum(axis=1)
         t_l = kp.astype(np.int64).sum(axis=1)
-        if policy == "minimax":
-            ref_levels = OB.allocate_minimax(c_l.tolist(), t_l.tolist(), target, levels)
-        else:
-            for l in range(L):
-                miss_sum[l] += 0.0 if t_l[l] == 0 else \
-                    float(t_l[l] - c_l[l][ref_levels[l]]) / float(t_l[l])
-            ref_levels = OB.allocate_proportional([m / (probe + 1) for m in miss_sum], target,
-                                                  levels)
-        assert table.cpu().tolist() == list(ref_levels), probe
+        ref_levels, published = ref.probe(c_l.tolist(), t_l.tolist())
+        assert published
+        assert table.cpu().tolist() == ref_levels, probe
         assert sum(ref_levels) == L * target
+
+
+@pytest.mark.parametrize("policy", ["minimax", "proportional"])
+@pytest.mark.parametrize("L,levels,drift_bp", [(3, 100, 400), (8, 20, 1500), (40, 100, 250)])
+def test_budget_update_drift_gate_matches_oracle(policy, L, levels, drift_bp):
+    """With a drift threshold: eight probes whose curves move a little (at
+    most half the threshold per level since the last large move) or, every
+    third probe, a lot; the device publishes exactly when the oracle policy
+    does, its level table equals the oracle's after every probe, and the
+    running miss rates keep advancing across the probes it does not publish."""
+    banner(f"budget drift gate {policy} L={L} levels={levels} drift={drift_bp}")
+    from sparse_attention_indexer_spin_amd import api as A
+    rng = np.random.default_rng(L * 31 + levels + drift_bp)
+    rows_total = 6
+    target = levels // 2
+    state = torch.zeros(A.spin_budget_state_bytes(L, levels), dtype=torch.uint8, device=DEV)
+    table = torch.full((L,), target, dtype=torch.int32, device=DEV)
+    ref = OB.BudgetPolicy(policy, L, levels, target, drift_bp=drift_bp)
+    tot = rng.integers(1000, 3000, L).astype(np.int64)     # a layer's top-K slots
+
+    def curves():  # monotone from anywhere in [0, K'] up to K' at the top level
+        c = np.sort(rng.integers(0, tot[:, None] + 1, (L, levels + 1)), axis=1)
+        c[:, -1] = tot
+        return c
+
+    summed = curves()
+    flags = []
+    for probe in range(8):
+        if probe % 3 == 2:
+            summed = curves()                                # a large move
+        else:
+            # a small one: every miss rate moves by at most a quarter of the
+            # threshold (the raised prefix maximum keeps the curve monotone)
+            step = np.floor(tot * drift_bp / 40000.0).astype(np.int64)
+            new = np.clip(summed + rng.integers(-1, 2, summed.shape) * step[:, None], 0,
+                          tot[:, None])
+            new[:, -1] = tot
+            summed = np.maximum.accumulate(new, axis=1)
+        # one row of each layer carries the layer's curve, the others are empty
+        cov = np.zeros((L, rows_total, levels + 1), dtype=np.int32)
+        kp = np.zeros((L, rows_total), dtype=np.int32)
+        cov[:, 0, :] = summed
+        kp[:, 0] = tot
+        A.spin_budget_update(policy, levels, target, torch.from_numpy(cov).to(DEV),
+                             torch.from_numpy(kp).to(DEV), state, table, drift_bp=drift_bp)
+        torch.cuda.synchronize()
+        ref_levels, published = ref.probe(summed.tolist(), tot.tolist())
+        flags.append(published)
+        assert table.cpu().tolist() == ref_levels, probe
+    assert flags[0] and not all(flags) and sum(flags) >= 2, flags
 
 
 def stk_cov_row(stack, l, r):
