@@ -517,7 +517,8 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
         out["stack_ms_per_step"] = t0.elapsed_time(t1) / (steps * copies)
     del slays, stack
     if w.rows == 1:
-        # one spin_step per copy captured in a HIP graph, replayed round robin
+        # the round of spin_steps over the copies captured in one HIP graph (as
+        # a model captures its layers' decode step) and replayed
         gl = []
         for c in range(copies):
             lay = SpinLayer(batch=w.batch, max_blocks=w.max_blocks,
@@ -534,23 +535,20 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
             for c in range(copies):
                 gl[c].step(inp.q[s], inp.weights, pages[c], scales[c], pt)
         torch.cuda.synchronize()
-        graphs = []
-        for c in range(copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in range(copies):
                 gl[c].step(inp.q[warmup], inp.weights, pages[c], scales[c], pt)
-            graphs.append(g)
         torch.cuda.synchronize()
         t0.record(stream)
         for s in range(steps):
-            for g in graphs:
-                g.replay()
+            graph.replay()
         t1.record(stream)
         torch.cuda.synchronize()
         for lay in gl:
             assert int(lay.err.item()) == 0, f"device error word {int(lay.err.item())}"
         out["graph_ms_per_step"] = t0.elapsed_time(t1) / (steps * copies)
-        del graphs, gl
+        del graph, gl
     if stage_reps:
         q = inp.q[warmup + steps - 1]
         last_nv = nv[-1]
