@@ -528,11 +528,16 @@ static void topk_ema_t(const spin_config& c, const spin_batch& b, const float* z
   const int rows_total = b.batch * b.n_rows;
   constexpr int per_block = (kSelThreads / 64) * kEmaChunk;
   const int most = (b.max_blocks + per_block - 1) / per_block;
-  const int free_cus =
-      resident_workgroups((const void*)k_topk_ema<SEPT>, kSelThreads) - rows_total - sel_wgs;
+  const int resident = resident_workgroups((const void*)k_topk_ema<SEPT>, kSelThreads);
+  // With one row the EMA workgroups fill the CUs the selects leave free.  With
+  // several rows the selects hold many CUs (a workgroup per request and row)
+  // and the EMA has several rows of work per block: it gets workgroups for
+  // every CU, and those beyond the free ones start where a select workgroup
+  // has finished.
+  const int ema_cus = b.n_rows > 1 ? resident - sel_wgs : resident - rows_total - sel_wgs;
   // no EMA workgroups when the update is deferred (the launch is then the
   // top-K and, with SEPT > 0, the next layer's selection)
-  const int ema_x = ema ? max(1, min(most, free_cus / max(1, b.batch))) : 0;
+  const int ema_x = ema ? max(1, min(most, ema_cus / max(1, b.batch))) : 0;
   hipLaunchKernelGGL(k_topk_ema<SEPT>, dim3(rows_total + ema_x * b.batch + sel_wgs),
                      dim3(kSelThreads), 0, st, c.topk, b.n_rows, b.max_blocks, b.ctx_len,
                      A.e.qpos, z, z_ld, sel, n_sel, out, ws, rows_total, A, ema_x, sa, si,
