@@ -287,11 +287,11 @@ __device__ __forceinline__ float xor32(float v) {
 __device__ __forceinline__ float reduce_scatter4(const float (&p)[4]) {
   const int g = (threadIdx.x & 63) >> 4;
   const bool odd = g & 1;
-  // round 1 (partner g ^ 1): keep sub-tiles with bit0 == g & 1
+  // first exchange (partner g ^ 1): keep sub-tiles with bit0 == g & 1
   const float send0 = odd ? p[0] : p[1], send1 = odd ? p[2] : p[3];
   const float keep0 = odd ? p[1] : p[0], keep1 = odd ? p[3] : p[2];
   const float a0 = keep0 + xor16(send0), a1 = keep1 + xor16(send1);
-  // round 2 (partner g ^ 2): keep the sub-tile with bit1 == g >> 1
+  // second exchange (partner g ^ 2): keep the sub-tile with bit1 == g >> 1
   const bool hi = g >> 1;
   const float send = hi ? a0 : a1, keep = hi ? a1 : a0;
   return keep + xor32(send);
