@@ -1022,6 +1022,19 @@ __device__ __forceinline__ void score_pages(const ScoreParams& p, Cur& db, int l
 
 enum { kRunWave = 0, kRunTable = 1, kRunSpan = 2 };
 
+// Worker of scoring workgroup b of g.  Workgroups go to the 8 XCDs round
+// robin (b on XCD b % 8); each XCD takes a contiguous range of workers, so
+// the workgroups of a request share one XCD's L2 (its query, block list and
+// page-table entries, and the lines of z at run boundaries).  A bijection of
+// [0, g) whatever the placement.  Used by the one-row kernel (its score
+// launch 0.1-0.7 us shorter); the all-rows kernel gained nothing from it.
+__device__ __forceinline__ int xcd_worker(int b, int g) {
+  const int x = b & 7, i = b >> 3;
+  int pre = 0;
+  for (int y = 0; y < x; ++y) pre += (g - y + 7) >> 3;
+  return pre + i;
+}
+
 // WL: whole-line page loads (one verifier row; see PageRegs)
 template <int KT, int NS, int QB, int P, int Mode, bool WL>
 __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
@@ -1040,7 +1053,7 @@ __global__ __launch_bounds__(256) void k_score_wave(ScoreParams p) {
     // Teams of workgroups: a workgroup's streams split its request-aligned
     // run, found by each wave on its own (no table), and share the request's
     // query rows through LDS, each wave converting rows of the 16-head tiles.
-    const Run run = wave_run(p, blockIdx.x, gx);
+    const Run run = wave_run(p, xcd_worker(blockIdx.x, gx), gx);
     if (run.lo >= run.hi) return;  // the whole workgroup: no barrier follows
     const int s = wave / p.rows, nb = run.hi - run.lo;
     const int lo = __builtin_amdgcn_readfirstlane(run.lo + s * nb / spw);
