@@ -579,6 +579,14 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
             "select": per_copy(lambda c, lay, bt: lambda: api.spin_select_blocks(
                 lay.cfg, bt, lay.S, lay.row_code, lay.sel, lay.n_sel)),
         }
+        # the score launch's pages (the last step's selection), for the HBM
+        # read probe timed beside the stages
+        probe_ids = []
+        for lay in lays:
+            kk = torch.arange(w.max_blocks, device=lay.sel.device)
+            mask = kk[None, :] < lay.n_sel.long()[:, None]
+            probe_ids.append(pt.long().gather(1, lay.sel.long().clamp(min=0))[mask]
+                             .to(torch.int32).contiguous())
         # every loop starts from the state the last step left (its selection,
         # the top-K hints and candidates in the workspace): the predict and
         # select stages of a loop leave the next step's selection behind
@@ -599,6 +607,18 @@ def run_rotate(inp: Inputs, sparsity_bp: int, steps: int, warmup: int, stage_rep
         del snap
         # untimed calls (rounds over the copies) before each loop's timed ones
         out["stage_warm_rounds"] = warm
+        if w.key_dtype == "fp8":
+            # a plain read of the same pages with the score kernel's loads
+            # (include/spin_probe.h): the practical ceiling of the score launch
+            from sparse_attention_indexer_spin_amd import _lib as LIB
+            sink = torch.zeros(LIB.SPIN_READ_PROBE_SINK_WORDS, dtype=torch.int32,
+                               device=pages[0].device)
+            probe = per_copy(lambda c, lay, bt: lambda: api.spin_read_pages(
+                pages[c], probe_ids[c], sink))
+            pr = [_timed_us(probe, stage_reps, stream) / copies for _ in range(max(1, runs))]
+            out["page_read_us"] = float(np.median(pr))
+            out["page_read_us_spread"] = [min(pr), max(pr)]
+            out["page_read_bytes"] = 8192.0 * sum(int(x.numel()) for x in probe_ids) / copies
         out["stage_us"] = {k: float(np.median([lp[k] for lp in loops])) for k in st}
         out["stage_us_spread"] = {k: [min(lp[k] for lp in loops), max(lp[k] for lp in loops)]
                                   for k in st}
@@ -989,6 +1009,16 @@ def main():
         "stage_us": res["stage_us"],
         "stage_us_spread": res.get("stage_us_spread"),
         "stage_warm_rounds": res.get("stage_warm_rounds"),
+        "page_read_probe": ({
+            "how": "the score launch's pages read with its loads and nothing else "
+                   "(spin_read_pages), timed like the stages",
+            "us": res["page_read_us"], "us_spread": res["page_read_us_spread"],
+            "key_bytes": res["page_read_bytes"],
+            "gbs": res["page_read_bytes"] / (res["page_read_us"] * 1e-6) / 1e9,
+            "frac_of_peak": res["page_read_bytes"] / (res["page_read_us"] * 1e-6) / 1e9
+            / HBM_PEAK_GBS,
+            "score_launch_over_read": res["stage_us"]["score"] / res["page_read_us"]}
+            if "page_read_us" in res else None),
         "keys_scored_per_step": keys_row,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,

@@ -26,7 +26,9 @@ EXPORTS = ["spin_predict_blocks", "spin_select_blocks", "spin_sparse_index_score
            "spin_stack_create", "spin_stack_destroy", "spin_stack_step", "spin_miss_curve",
            "spin_budget_fill", "spin_budget_allocate", "spin_step_noalloc", "spin_stack_commit",
            "spin_budget_state_bytes", "spin_stack_set_budget_policy", "spin_stack_reset_budgets",
-           "spin_budget_update"]
+           "spin_budget_update", "spin_read_pages"]
+SPIN_READ_PROBE_WAVES = 2048
+SPIN_READ_PROBE_SINK_WORDS = SPIN_READ_PROBE_WAVES * 64
 SPIN_NOALLOC_WORKSPACE_BYTES = 160 * 1024 * 1024
 SPIN_BUDGET_MINIMAX, SPIN_BUDGET_PROPORTIONAL = 0, 1
 SPIN_POOL_MAX, SPIN_POOL_TOP4, SPIN_POOL_MEAN = 0, 1, 2
@@ -105,6 +107,7 @@ def load() -> C.CDLL:
         "spin_stack_set_budget_policy": [P, C.POINTER(SpinBudgetPolicy)],
         "spin_stack_reset_budgets": [P, I32, cfg, bt, P],
         "spin_budget_update": [I32, I32, I32, I32, I32, I32, P, P, P, P, P],
+        "spin_read_pages": [P, I64, P, I32, P, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)

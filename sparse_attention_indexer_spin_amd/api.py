@@ -276,3 +276,14 @@ def spin_budget_update(policy: str, levels: int, target_level: int, covered, kpr
     L.check(L.load().spin_budget_update(code, n_layers, levels, target_level, drift_bp, rows_total,
                                         _p(covered), _p(kprime), _p(state), _p(level_table),
                                         _stream(stream)))
+
+
+def spin_read_pages(k_pages, page_ids, sink, stream=None):
+    """The HBM read probe of include/spin_probe.h (measurement only): reads
+    the listed 8 KB pages of k_pages with the fp8 score kernel's loads.
+    page_ids: i32 device tensor; sink: u32/i32 device tensor of
+    SPIN_READ_PROBE_SINK_WORDS words."""
+    assert sink.numel() >= L.SPIN_READ_PROBE_SINK_WORDS and k_pages.element_size() == 1
+    n_pages = k_pages.numel() // 8192
+    L.check(L.load().spin_read_pages(_p(k_pages), n_pages, _p(page_ids), page_ids.numel(),
+                                     _p(sink), _stream(stream)))

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libspin.so")
 ARCH = os.environ.get("SPIN_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["spin_api.hip", "k_select.hip", "k_score.hip", "k_topk.hip", "k_ema.hip",
-           "k_budget.hip"]
+           "k_budget.hip", "k_probe.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "spin_launch.h"
+#include "spin_probe.h"
 
 namespace {
 
@@ -160,6 +161,17 @@ bool lds_fits(const void* kernel, size_t dyn_lds) {
 extern "C" {
 
 const char* spin_last_error(void) { return g_err; }
+
+spin_status spin_read_pages(const void* k_pages, int64_t n_pages, const int32_t* page_ids,
+                            int32_t n_ids, uint32_t* sink, void* stream) {
+  const char* fn = "spin_read_pages";
+  if (!k_pages || !page_ids || !sink) return fail(SPIN_E_NULL, "%s: NULL buffer", fn);
+  if (n_ids < 0 || n_pages < 1)
+    return fail(SPIN_E_SHAPE, "%s: n_ids %d, n_pages %lld", fn, n_ids, (long long)n_pages);
+  if (n_ids == 0) return SPIN_OK;
+  return hip_status(spin::launch_read_pages(k_pages, n_pages, page_ids, n_ids, sink,
+                                            (hipStream_t)stream), fn);
+}
 
 size_t spin_workspace_bytes(const spin_config* cfg, int32_t batch, int32_t n_rows,
                             int32_t max_blocks) {

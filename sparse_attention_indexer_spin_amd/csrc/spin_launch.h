@@ -137,6 +137,10 @@ void allocate_minimax(int L, int levels, int target, const int64_t* covered,
                       const int64_t* total, int32_t* out);
 void allocate_proportional(int L, int levels, int target, const double* miss, int32_t* out);
 
+// The HBM read probe of include/spin_probe.h.
+hipError_t launch_read_pages(const void* kp, int64_t n_pages, const int32_t* ids, int n,
+                             uint32_t* sink, hipStream_t st);
+
 // Number of workgroups of `threads` threads of `kernel` resident at once on
 // the current device (occupancy x compute units), cached per kernel.
 int resident_workgroups(const void* kernel, int threads, size_t dyn_lds = 0);

@@ -9,12 +9,16 @@ import pytest
 from tests.conftest import ROOT
 
 HEADER = os.path.join(ROOT, "include", "spin.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(spin_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(spin_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -173,3 +177,14 @@ def test_predict_ahead_host_validation(lib):
                          step_mut=1, workspace=1, workspace_bytes=ws, last_obs=None, s_tag=None)
     assert lib.spin_step(C.byref(cfg), C.byref(bt), C.byref(io), 0, None) == 1
     assert "s_tag" in lib.spin_last_error().decode()
+
+
+def test_read_probe_argument_checks(lib):
+    """The read probe refuses NULL buffers and negative counts before any
+    device work, and launches nothing for an empty list."""
+    import ctypes as C
+    dummy = C.c_void_p(256)
+    assert lib.spin_read_pages(None, 1, dummy, 1, dummy, None) == 1          # SPIN_E_NULL
+    assert lib.spin_read_pages(dummy, 1, dummy, -1, dummy, None) == 2        # SPIN_E_SHAPE
+    assert lib.spin_read_pages(dummy, 0, dummy, 1, dummy, None) == 2
+    assert lib.spin_read_pages(dummy, 4, dummy, 0, dummy, None) == 0         # nothing to read
