@@ -10,8 +10,6 @@ namespace spin {
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-namespace {
-
 __device__ __forceinline__ void probe_load(const uint8_t* kp, int64_t n_pages, int id,
                                            v4u (&b)[8]) {
   const int lane = threadIdx.x & 63;
@@ -60,8 +58,6 @@ __global__ __launch_bounds__(256) void k_read_pages(const uint8_t* __restrict__ 
   }
   sink[(int64_t)w * 64 + lane] = acc;
 }
-
-}  // namespace
 
 hipError_t launch_read_pages(const void* kp, int64_t n_pages, const int32_t* ids, int n,
                              uint32_t* sink, hipStream_t st) {
